@@ -1,0 +1,220 @@
+"""CPU oracle: plain float64 definitions of what the block-sparse path computes.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, the smoke check and the benchmark's
+CPU-baseline leg import this package; the product path never does. It shares no
+code with the HIP library: geometry, masses, selection, masked attention, FP8
+quantization and the structured mask are each written here from their definitions
+(``fpsa_oracle.c``), over raster-ordered tokens.
+
+Parity pins (tests/test_oracle_pins.py) tie each function to something other than
+itself: closed forms, invariants, brute force on tiny inputs, textbook softmax
+attention computed by a library routine, and the published e4m3 code table.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fpsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_vp = ctypes.c_void_p
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, OpenMP over independent rows)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            L = ctypes.CDLL(_LIB_PATH)
+            L.orc_num_blocks.restype = ctypes.c_int64
+            L.orc_num_blocks.argtypes = [ctypes.c_int] * 6
+            L.orc_token_blocks.restype = None
+            L.orc_token_blocks.argtypes = [ctypes.c_int] * 6 + [_i32p, _vp]
+            L.orc_dense_attention.restype = None
+            L.orc_dense_attention.argtypes = [_f32p, _f32p, _f32p] + [ctypes.c_int] * 4 + [
+                ctypes.c_double, _vp, ctypes.c_int, _f64p]
+            L.orc_block_mass.restype = None
+            L.orc_block_mass.argtypes = [_f32p, _f32p] + [ctypes.c_int] * 4 + [
+                _i32p, ctypes.c_int, ctypes.c_double, _vp, ctypes.c_int, _f64p]
+            L.orc_mass_key.restype = ctypes.c_uint64
+            L.orc_mass_key.argtypes = [ctypes.c_float]
+            L.orc_select_blocks.restype = ctypes.c_int64
+            L.orc_select_blocks.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                                            ctypes.c_uint32, _i32p, _i32p]
+            L.orc_cut_margin.restype = None
+            L.orc_cut_margin.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, _f64p]
+            L.orc_masked_attention.restype = None
+            L.orc_masked_attention.argtypes = [_f32p, _f32p, _f32p] + [ctypes.c_int] * 4 + [
+                _i32p, ctypes.c_int, ctypes.c_double, _i32p, _i32p, _vp, ctypes.c_int, _f64p, _i32p]
+            L.orc_e4m3_decode.restype = ctypes.c_double
+            L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+            L.orc_e4m3_encode.restype = ctypes.c_uint8
+            L.orc_e4m3_encode.argtypes = [ctypes.c_double]
+            L.orc_fp8_tile_quantize.restype = None
+            L.orc_fp8_tile_quantize.argtypes = [_f32p] + [ctypes.c_int] * 4 + [_i32p, ctypes.c_int, _f32p, _f32p]
+            L.orc_structured_mask.restype = ctypes.c_int64
+            L.orc_structured_mask.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p]
+            _lib = L
+    return _lib
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _opt_i32(a):
+    """(pointer, count, keepalive) for an optional int32 index list."""
+    if a is None:
+        return None, 0, None
+    arr = _c(a, np.int32)
+    return arr.ctypes.data_as(ctypes.c_void_p), len(arr), arr
+
+
+# --------------------------------------------------------------------------- geometry
+
+def num_blocks(grid, tile) -> int:
+    return int(lib().orc_num_blocks(*grid, *tile))
+
+
+def token_blocks(grid, tile):
+    """(block_of[N] int32, slot_of[N] int64) for the raster tokens of ``grid``."""
+    T, Hg, Wg = grid
+    N = T * Hg * Wg
+    blk = np.empty(N, np.int32)
+    slot = np.empty(N, np.int64)
+    lib().orc_token_blocks(*grid, *tile, blk, slot.ctypes.data_as(ctypes.c_void_p))
+    return blk, slot
+
+
+def block_sizes(grid, tile):
+    """Number of real tokens in every block."""
+    blk, _ = token_blocks(grid, tile)
+    return np.bincount(blk, minlength=num_blocks(grid, tile))
+
+
+# --------------------------------------------------------------------------- attention
+
+def dense_attention(q, k, v, scale, queries=None):
+    """Full softmax attention; q, k, v raster [B, N, H, D]. Rows not in ``queries`` are 0."""
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    B, N, H, D = q.shape
+    out = np.zeros((B, N, H, D), np.float64)
+    p, n, keep = _opt_i32(queries)
+    lib().orc_dense_attention(q, k, v, B, N, H, D, float(scale), p, n, out)
+    return out
+
+
+def block_mass(q, k, grid, tile, scale, qblocks=None):
+    """Block masses [B, H, nsel, nb] float64 (rows for ``qblocks``, default all)."""
+    q, k = _c(q, np.float32), _c(k, np.float32)
+    B, N, H, D = q.shape
+    blk, _ = token_blocks(grid, tile)
+    nb = num_blocks(grid, tile)
+    p, n, keep = _opt_i32(qblocks)
+    count = n if qblocks is not None else nb
+    out = np.empty((B, H, count, nb), np.float64)
+    lib().orc_block_mass(q, k, B, N, H, D, blk, nb, float(scale), p, n, out)
+    return out
+
+
+def mass_key(m: float) -> int:
+    return int(lib().orc_mass_key(float(m)))
+
+
+def select_blocks(mass, thr_num=99, thr_den=100):
+    """CSR (row_ptr[R+1], col_idx[nnz]) of the retained-mass selection of float32 rows."""
+    m = _c(mass, np.float32)
+    nb = m.shape[-1]
+    m2 = m.reshape(-1, nb)
+    R = m2.shape[0]
+    row_ptr = np.zeros(R + 1, np.int32)
+    col_idx = np.zeros(max(R * nb, 1), np.int32)
+    nnz = lib().orc_select_blocks(m2, R, nb, thr_num, thr_den, row_ptr, col_idx)
+    return row_ptr, col_idx[:nnz].copy()
+
+
+def cut_margin(mass64, p=0.99):
+    m = _c(mass64, np.float64)
+    nb = m.shape[-1]
+    m2 = m.reshape(-1, nb)
+    out = np.empty(m2.shape[0], np.float64)
+    lib().orc_cut_margin(m2, m2.shape[0], nb, float(p), out)
+    return out
+
+
+def masked_attention(q, k, v, grid, tile, scale, row_ptr, col_idx, qblocks=None):
+    """Masked attention for the requested query blocks.
+
+    Returns (out [B, H, nsel, 64, D] float64, token_of [B, H, nsel, 64] int32): row e
+    of a block is its e-th real token in raster order (token_of = -1 past the end).
+    """
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    B, N, H, D = q.shape
+    blk, _ = token_blocks(grid, tile)
+    nb = num_blocks(grid, tile)
+    p, n, keep = _opt_i32(qblocks)
+    count = n if qblocks is not None else nb
+    out = np.empty((B, H, count, 64, D), np.float64)
+    tok = np.empty((B, H, count, 64), np.int32)
+    rp = _c(row_ptr, np.int32)
+    ci = _c(col_idx, np.int32)
+    if ci.size == 0:
+        ci = np.zeros(1, np.int32)
+    lib().orc_masked_attention(q, k, v, B, N, H, D, blk, nb, float(scale), rp, ci, p, n, out, tok)
+    return out, tok
+
+
+# --------------------------------------------------------------------------- fp8
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().orc_e4m3_decode(int(code) & 0xFF))
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().orc_e4m3_encode(float(x)))
+
+
+def fp8_tile_quantize(x, grid, tile):
+    """(xhat [B, N, H, D] float32, scales [B, H, nb] float32) of per-tile e4m3 quantization."""
+    x = _c(x, np.float32)
+    B, N, H, D = x.shape
+    blk, _ = token_blocks(grid, tile)
+    nb = num_blocks(grid, tile)
+    xhat = np.empty_like(x)
+    scales = np.empty((B, H, nb), np.float32)
+    lib().orc_fp8_tile_quantize(x, B, N, H, D, blk, nb, xhat, scales)
+    return xhat, scales
+
+
+# --------------------------------------------------------------------------- structured mask
+
+def structured_mask(gh, gw, copies=1):
+    nb = gh * gw
+    row_ptr = np.zeros(copies * nb + 1, np.int32)
+    # each row keeps at most 3x3 + one row + one column of groups
+    cap = copies * nb * (gw + gh + 9)
+    col_idx = np.zeros(cap, np.int32)
+    nnz = lib().orc_structured_mask(gh, gw, copies, row_ptr, col_idx)
+    return row_ptr, col_idx[:nnz].copy()

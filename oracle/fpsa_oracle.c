@@ -1,0 +1,413 @@
+/*
+ * CPU oracle for block-sparse attention with retained-mass block selection.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library. The product path never calls it.
+ *
+ * Plain, slow, obviously correct: every score, exponential and sum is taken in
+ * double precision, loops follow the definitions one token at a time, and tokens
+ * stay in raster order: block membership comes from the tile formula, never from
+ * a permuted layout. Parallelism: OpenMP over independent (batch, head, q-block)
+ * rows only, which does not change any arithmetic.
+ *
+ * Sources: the retained-mass rule, per-head / per-query-block selection and frozen
+ * reuse follow [LoSA: Near-Lossless Sparse Attention for Training-Free Video
+ * Diffusion Acceleration, Abstract]; the 3D tile as the unit of both sparsity and
+ * quantization follows [FPSAttention: Training-Aware FP8 and Sparsity Co-Design for
+ * Fast Video Diffusion, Abstract]; the group-shared structured key set follows
+ * [Grouping First, Attending Smartly: Training-Free Acceleration for Diffusion
+ * Transformers, Abstract].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------- */
+/* Geometry                                                                   */
+/* ------------------------------------------------------------------------- */
+
+/* Number of tiles along one axis: the grid is padded up to a tile multiple. */
+static int64_t tiles_along(int64_t g, int64_t tile) { return (g + tile - 1) / tile; }
+
+int64_t orc_num_blocks(int T, int Hg, int Wg, int tt, int th, int tw) {
+    if (T <= 0 || Hg <= 0 || Wg <= 0 || tt <= 0 || th <= 0 || tw <= 0) return -1;
+    return tiles_along(T, tt) * tiles_along(Hg, th) * tiles_along(Wg, tw);
+}
+
+/*
+ * For every raster token n = (t*Hg + h)*Wg + w: its block id (tiles numbered in
+ * raster order over the tile grid) and its slot in the tiled sequence, i.e.
+ * 64*block + the token's raster position inside its tile.
+ */
+void orc_token_blocks(int T, int Hg, int Wg, int tt, int th, int tw,
+                      int32_t* block_of, int64_t* slot_of) {
+    int64_t nh = tiles_along(Hg, th), nw = tiles_along(Wg, tw);
+    int64_t tile_tokens = (int64_t)tt * th * tw;
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < Hg; ++h)
+            for (int w = 0; w < Wg; ++w) {
+                int64_t n = ((int64_t)t * Hg + h) * Wg + w;
+                int64_t blk = ((int64_t)(t / tt) * nh + (h / th)) * nw + (w / tw);
+                int64_t within = ((int64_t)(t % tt) * th + (h % th)) * tw + (w % tw);
+                block_of[n] = (int32_t)blk;
+                if (slot_of) slot_of[n] = blk * tile_tokens + within;
+            }
+}
+
+/* Raster index of element (b, n, h, d) in a [B, N, H, D] array. */
+#define RIX(b, n, h, d) ((((int64_t)(b) * N + (n)) * H + (h)) * D + (d))
+
+static double dot_scaled(const float* q, const float* k, int D, double scale) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += (double)q[d] * (double)k[d];
+    return s * scale;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Dense softmax attention (the reference every sparse result reduces to)    */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * out[b,n,h,:] = sum_j softmax_j(scale * q_n . k_j) v_j over all N keys, for the
+ * queries listed in `queries` (all N when queries == NULL). out is [B, N, H, D].
+ */
+void orc_dense_attention(const float* q, const float* k, const float* v,
+                         int B, int N, int H, int D, double scale,
+                         const int32_t* queries, int nq, double* out) {
+    int count = queries ? nq : N;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int qi = 0; qi < count; ++qi) {
+                int i = queries ? queries[qi] : qi;
+                double* s = (double*)malloc(sizeof(double) * (size_t)N);
+                double m = -INFINITY;
+                for (int j = 0; j < N; ++j) {
+                    s[j] = dot_scaled(q + RIX(b, i, h, 0), k + RIX(b, j, h, 0), D, scale);
+                    if (s[j] > m) m = s[j];
+                }
+                double z = 0.0;
+                for (int j = 0; j < N; ++j) z += exp(s[j] - m);
+                double* o = out + RIX(b, i, h, 0);
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                for (int j = 0; j < N; ++j) {
+                    double p = exp(s[j] - m) / z;
+                    const float* vj = v + RIX(b, j, h, 0);
+                    for (int d = 0; d < D; ++d) o[d] += p * (double)vj[d];
+                }
+                free(s);
+            }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Block attention masses (the exact dense measurement step)                  */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * mass[b,h,r,kb] for each requested query block qb = qblocks[r] (all nb blocks
+ * when qblocks == NULL): the softmax probability that the real queries of qb put
+ * on the real keys of kb, summed over those keys and averaged over those queries.
+ * Each row therefore sums to one. Padding tokens do not exist in raster order, so
+ * they carry no mass. mass is [B, H, nsel, nb] float64.
+ */
+void orc_block_mass(const float* q, const float* k, int B, int N, int H, int D,
+                    const int32_t* block_of, int nb, double scale,
+                    const int32_t* qblocks, int nsel, double* mass) {
+    int count = qblocks ? nsel : nb;
+    int64_t* cnt = (int64_t*)calloc((size_t)nb, sizeof(int64_t));
+    for (int n = 0; n < N; ++n) cnt[block_of[n]]++;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int r = 0; r < count; ++r) {
+                int qb = qblocks ? qblocks[r] : r;
+                double* row = mass + (((int64_t)b * H + h) * count + r) * nb;
+                for (int kb = 0; kb < nb; ++kb) row[kb] = 0.0;
+                double* s = (double*)malloc(sizeof(double) * (size_t)N);
+                for (int i = 0; i < N; ++i) {
+                    if (block_of[i] != qb) continue;
+                    double m = -INFINITY;
+                    for (int j = 0; j < N; ++j) {
+                        s[j] = dot_scaled(q + RIX(b, i, h, 0), k + RIX(b, j, h, 0), D, scale);
+                        if (s[j] > m) m = s[j];
+                    }
+                    double z = 0.0;
+                    for (int j = 0; j < N; ++j) z += exp(s[j] - m);
+                    for (int j = 0; j < N; ++j) row[block_of[j]] += exp(s[j] - m) / z;
+                }
+                if (cnt[qb] > 0)
+                    for (int kb = 0; kb < nb; ++kb) row[kb] /= (double)cnt[qb];
+                free(s);
+            }
+    free(cnt);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Retained-mass selection                                                    */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Fixed-point key of a mass: floor(m * 2^40) after clamping m to [0, 1] (NaN -> 0).
+ * For a float32 m in [0, 1] the product is an exact power-of-two shift, so the key
+ * is exact and identical wherever it is computed.
+ */
+uint64_t orc_mass_key(float m) {
+    if (!(m > 0.0f)) return 0;          /* zero, negative, NaN */
+    if (m >= 1.0f) return (uint64_t)1 << 40;
+    return (uint64_t)floor((double)m * 1099511627776.0);
+}
+
+typedef struct { uint64_t key; int32_t idx; } ranked;
+
+/* Larger key first; equal keys: lower block index first. */
+static int rank_order(const void* a, const void* b) {
+    const ranked* x = (const ranked*)a;
+    const ranked* y = (const ranked*)b;
+    if (x->key != y->key) return x->key > y->key ? -1 : 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx ? 1 : 0);
+}
+
+static int ascending_int(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+/*
+ * For each of the R rows of mass [R, nb]: rank blocks by mass (ties to the lower
+ * index), and keep the shortest leading run of that ranking whose summed mass
+ * reaches thr_num/thr_den of the row total; the comparison is den*kept >= num*total
+ * on the fixed-point keys. A row with zero total keeps nothing. Kept indices are
+ * written in ascending order: row r occupies col_idx[row_ptr[r] .. row_ptr[r+1]).
+ * col_idx must hold R*nb entries. Returns the number of kept pairs.
+ */
+int64_t orc_select_blocks(const float* mass, int64_t R, int nb, uint32_t thr_num, uint32_t thr_den,
+                          int32_t* row_ptr, int32_t* col_idx) {
+    ranked* order = (ranked*)malloc(sizeof(ranked) * (size_t)nb);
+    int64_t nnz = 0;
+    row_ptr[0] = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        const float* row = mass + r * nb;
+        uint64_t total = 0;
+        for (int k = 0; k < nb; ++k) {
+            order[k].key = orc_mass_key(row[k]);
+            order[k].idx = k;
+            total += order[k].key;
+        }
+        qsort(order, (size_t)nb, sizeof(ranked), rank_order);
+        int keep = 0;
+        uint64_t kept = 0;
+        while (keep < nb && (uint64_t)thr_den * kept < (uint64_t)thr_num * total) {
+            kept += order[keep].key;
+            keep++;
+        }
+        /* total == 0 (or thr_num == 0): the loop never runs and nothing is kept. */
+        int32_t* out = col_idx + nnz;
+        for (int i = 0; i < keep; ++i) out[i] = order[i].idx;
+        qsort(out, (size_t)keep, sizeof(int32_t), ascending_int);
+        nnz += keep;
+        row_ptr[r + 1] = (int32_t)nnz;
+    }
+    free(order);
+    return nnz;
+}
+
+/*
+ * How close each row's cut is to flipping, in real (float64) arithmetic on float64
+ * masses: the smallest of (kept - p*total), (p*total - kept_without_last) and the
+ * mass gap between the last kept block and the first dropped one, in the ranking of
+ * the float64 masses. A row whose margin is below the error of a computed mass may
+ * legitimately select differently.
+ */
+typedef struct { double val; int32_t idx; } ranked64;
+
+/* Larger mass first; equal masses: lower block index first. */
+static int rank_order64(const void* a, const void* b) {
+    const ranked64* x = (const ranked64*)a;
+    const ranked64* y = (const ranked64*)b;
+    if (x->val != y->val) return x->val > y->val ? -1 : 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx ? 1 : 0);
+}
+
+void orc_cut_margin(const double* mass, int64_t R, int nb, double p, double* margin) {
+    ranked64* order = (ranked64*)malloc(sizeof(ranked64) * (size_t)nb);
+    for (int64_t r = 0; r < R; ++r) {
+        const double* row = mass + r * nb;
+        double total = 0.0;
+        for (int k = 0; k < nb; ++k) {
+            order[k].val = row[k];
+            order[k].idx = k;
+            total += row[k];
+        }
+        qsort(order, (size_t)nb, sizeof(ranked64), rank_order64);
+        double target = p * total, c = 0.0, prev = 0.0;
+        int keep = 0;
+        while (keep < nb && c < target) { prev = c; c += order[keep].val; keep++; }
+        double m = INFINITY;
+        if (keep > 0) {
+            if (c - target < m) m = c - target;
+            if (target - prev < m) m = target - prev;
+            if (keep < nb && order[keep - 1].val - order[keep].val < m)
+                m = order[keep - 1].val - order[keep].val;
+        }
+        margin[r] = m;
+    }
+    free(order);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Masked (block-sparse) attention                                            */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * For each requested query block qb = qblocks[r] of each (b, h): every real query
+ * i of qb attends to the real keys of the blocks kept for row (b*H + h)*nb + qb of
+ * the CSR, with the softmax renormalised over exactly those keys. A query whose
+ * allowed set is empty gets a zero output. Output rows are written to
+ * out[b, h, r, e, :] for the e-th real token of qb in raster order (e < 64), and
+ * token_of[b, h, r, e] holds that token's raster index (-1 past the last token).
+ * out is [B, H, nsel, 64, D] float64.
+ */
+void orc_masked_attention(const float* q, const float* k, const float* v,
+                          int B, int N, int H, int D, const int32_t* block_of, int nb, double scale,
+                          const int32_t* row_ptr, const int32_t* col_idx,
+                          const int32_t* qblocks, int nsel, double* out, int32_t* token_of) {
+    int count = qblocks ? nsel : nb;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int r = 0; r < count; ++r) {
+                int qb = qblocks ? qblocks[r] : r;
+                int64_t row = ((int64_t)b * H + h) * nb + qb;
+                char* allowed = (char*)calloc((size_t)nb, 1);
+                for (int32_t e = row_ptr[row]; e < row_ptr[row + 1]; ++e) allowed[col_idx[e]] = 1;
+                double* s = (double*)malloc(sizeof(double) * (size_t)N);
+                int64_t base = (((int64_t)b * H + h) * count + r) * 64;
+                for (int e = 0; e < 64; ++e) {
+                    token_of[base + e] = -1;
+                    for (int d = 0; d < D; ++d) out[(base + e) * D + d] = 0.0;
+                }
+                int e = 0;
+                for (int i = 0; i < N && e < 64; ++i) {
+                    if (block_of[i] != qb) continue;
+                    token_of[base + e] = i;
+                    double* o = out + (base + e) * D;
+                    double m = -INFINITY;
+                    for (int j = 0; j < N; ++j) {
+                        if (!allowed[block_of[j]]) continue;
+                        s[j] = dot_scaled(q + RIX(b, i, h, 0), k + RIX(b, j, h, 0), D, scale);
+                        if (s[j] > m) m = s[j];
+                    }
+                    if (m != -INFINITY) {
+                        double z = 0.0;
+                        for (int j = 0; j < N; ++j)
+                            if (allowed[block_of[j]]) z += exp(s[j] - m);
+                        for (int j = 0; j < N; ++j) {
+                            if (!allowed[block_of[j]]) continue;
+                            double p = exp(s[j] - m) / z;
+                            const float* vj = v + RIX(b, j, h, 0);
+                            for (int d = 0; d < D; ++d) o[d] += p * (double)vj[d];
+                        }
+                    }
+                    e++;
+                }
+                free(s);
+                free(allowed);
+            }
+}
+
+/* ------------------------------------------------------------------------- */
+/* FP8 e4m3 (OCP "e4m3fn") per-tile quantization, simulated                   */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Value of an 8-bit e4m3fn code: 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); the all-ones pattern
+ * S.1111.111 is NaN and there is no infinity, so the largest finite value is 448.
+ */
+double orc_e4m3_decode(uint8_t code) {
+    int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp((double)m / 8.0, -6);
+    else mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/*
+ * Nearest finite e4m3fn code to x (ties to the even code, i.e. the one whose
+ * mantissa LSB is zero), found by comparing against every finite magnitude; values
+ * beyond 448 therefore saturate to 448. NaN maps to the NaN code.
+ */
+uint8_t orc_e4m3_encode(double x) {
+    if (isnan(x)) return 0x7F;
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x);
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c < 0x7F; ++c) {            /* 0x00 .. 0x7E: all finite magnitudes */
+        double err = fabs(orc_e4m3_decode((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/*
+ * Per (b, h, block): a = max |x| over the block's real tokens and all D channels,
+ * scale = float32(a / 448) (1 when a == 0), and every element becomes
+ * decode(encode(float32(x / scale))) * scale, stored as float32 (a relative
+ * rounding of at most 2^-24 on top of the quantization). x and xhat are
+ * [B, N, H, D]; scales is [B, H, nb] float32.
+ */
+void orc_fp8_tile_quantize(const float* x, int B, int N, int H, int D,
+                           const int32_t* block_of, int nb, float* xhat, float* scales) {
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            float* sc = scales + ((int64_t)b * H + h) * nb;
+            for (int blk = 0; blk < nb; ++blk) sc[blk] = 0.0f;
+            for (int n = 0; n < N; ++n)
+                for (int d = 0; d < D; ++d) {
+                    float a = fabsf(x[RIX(b, n, h, d)]);
+                    if (a > sc[block_of[n]]) sc[block_of[n]] = a;
+                }
+            for (int blk = 0; blk < nb; ++blk) sc[blk] = sc[blk] > 0.0f ? sc[blk] / 448.0f : 1.0f;
+            for (int n = 0; n < N; ++n)
+                for (int d = 0; d < D; ++d) {
+                    float s = sc[block_of[n]];
+                    float y = x[RIX(b, n, h, d)] / s;
+                    xhat[RIX(b, n, h, d)] = (float)(orc_e4m3_decode(orc_e4m3_encode((double)y)) * (double)s);
+                }
+        }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Structured (group-shared) mask                                             */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * On a 2D grid of gh x gw token groups (block id = row*gw + col): query group
+ * (r, c) may attend key group (r2, c2) when it is in the 3x3 neighbourhood
+ * (|r-r2| <= 1 and |c-c2| <= 1, clipped at the border, itself included), or in the
+ * same group-row (r2 == r), or in the same group-column (c2 == c). Rows are
+ * replicated for `copies` (batch*head) copies; indices ascending. A row has at
+ * most gh + gw + 9 entries, so col_idx must hold copies * gh*gw * (gh + gw + 9).
+ * Returns the number of pairs.
+ */
+int64_t orc_structured_mask(int gh, int gw, int copies, int32_t* row_ptr, int32_t* col_idx) {
+    int64_t nb = (int64_t)gh * gw, nnz = 0;
+    row_ptr[0] = 0;
+    for (int cp = 0; cp < copies; ++cp)
+        for (int64_t qb = 0; qb < nb; ++qb) {
+            int r = (int)(qb / gw), c = (int)(qb % gw);
+            for (int64_t kb = 0; kb < nb; ++kb) {
+                int r2 = (int)(kb / gw), c2 = (int)(kb % gw);
+                int near = abs(r - r2) <= 1 && abs(c - c2) <= 1;
+                if (near || r2 == r || c2 == c) col_idx[nnz++] = (int32_t)kb;
+            }
+            row_ptr[(int64_t)cp * nb + qb + 1] = (int32_t)nnz;
+        }
+    return nnz;
+}

@@ -1,0 +1,364 @@
+"""Pins for the CPU oracle: each function is tied to something other than itself.
+
+Sources of truth used here: closed forms worked out by hand, invariants of the
+definitions, brute-force enumeration on tiny inputs, textbook softmax attention
+computed by a library routine (torch's scaled_dot_product_attention in float64),
+and the published OCP 8-bit floating-point (e4m3fn) code table.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_attention_reorder_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+# --------------------------------------------------------------------------- geometry
+
+def test_block_counts_of_the_workload_grids():
+    # tiles per axis worked out by hand: ceil(21/4)=6, ceil(30/4)=8, 52/4=13 -> 624 ...
+    assert O.num_blocks((4, 8, 8), (4, 4, 4)) == 4
+    assert O.num_blocks((21, 30, 52), (4, 4, 4)) == 6 * 8 * 13
+    assert O.num_blocks((21, 45, 80), (4, 4, 4)) == 6 * 12 * 20
+    assert O.num_blocks((33, 45, 80), (4, 4, 4)) == 9 * 12 * 20
+    assert O.num_blocks((1, 512, 512), (1, 8, 8)) == 64 * 64
+    assert O.num_blocks((0, 4, 4), (4, 4, 4)) < 0
+
+
+def test_token_slots_hand_values():
+    blk, slot = O.token_blocks((21, 30, 52), (4, 4, 4))
+    # token (t=5, h=7, w=50): tile (1, 1, 12) -> block (1*8 + 1)*13 + 12 = 129,
+    # position inside the tile (1, 3, 2) -> (1*4 + 3)*4 + 2 = 30
+    n = (5 * 30 + 7) * 52 + 50
+    assert blk[n] == 129 and slot[n] == 129 * 64 + 30
+    # first and last token
+    assert blk[0] == 0 and slot[0] == 0
+    n = 21 * 30 * 52 - 1             # (20, 29, 51): tile (5, 7, 12) -> 5*104+7*13+12 = 623
+    assert blk[n] == 623 and slot[n] == 623 * 64 + (0 * 4 + 1) * 4 + 3
+    # 2D image groups: token (h=9, w=17) -> group (1, 2) = 66, inside (1, 1) -> 9
+    blk, slot = O.token_blocks((1, 512, 512), (1, 8, 8))
+    n = 9 * 512 + 17
+    assert blk[n] == 66 and slot[n] == 66 * 64 + 9
+
+
+def test_token_slots_are_a_bijection_onto_real_slots():
+    for grid in [(5, 6, 4), (21, 30, 52), (4, 8, 8), (7, 9, 13)]:
+        blk, slot = O.token_blocks(grid, (4, 4, 4))
+        assert len(np.unique(slot)) == len(slot)
+        assert np.all(slot // 64 == blk)
+        assert slot.min() >= 0 and slot.max() < 64 * O.num_blocks(grid, (4, 4, 4))
+
+
+def test_block_sizes_ragged_hand_values():
+    # grid 5x6x4 with 4^3 tiles: t-tiles hold 4 and 1 frames, h-tiles 4 and 2 rows
+    sizes = O.block_sizes((5, 6, 4), (4, 4, 4))
+    assert sizes.tolist() == [64, 32, 16, 8]
+    # smallest blocks of the video workloads: 480p 1*2*4, 720p 1*1*4
+    assert O.block_sizes((21, 30, 52), (4, 4, 4)).min() == 8
+    assert O.block_sizes((21, 45, 80), (4, 4, 4)).min() == 4
+    assert O.block_sizes((21, 30, 52), (4, 4, 4)).sum() == 21 * 30 * 52
+
+
+# --------------------------------------------------------------------------- dense attention
+
+def _rand_qkv(B, N, H, D, seed):
+    g = np.random.default_rng(seed)
+    return [g.standard_normal((B, N, H, D)).astype(np.float32) for _ in range(3)]
+
+
+def _torch_sdpa(q, k, v, scale):
+    # library routine, float64, [B, H, N, D] layout
+    t = lambda a: torch.from_numpy(a.astype(np.float64)).permute(0, 2, 1, 3)
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def test_dense_attention_matches_library_softmax_attention():
+    q, k, v = _rand_qkv(2, 70, 3, 16, 1)
+    ref = _torch_sdpa(q, k, v, 0.25)
+    got = O.dense_attention(q, k, v, 0.25)
+    assert np.abs(got - ref).max() < 1e-12
+
+
+def test_dense_attention_zero_query_is_mean_of_values():
+    q, k, v = _rand_qkv(1, 50, 2, 8, 2)
+    q[:] = 0
+    got = O.dense_attention(q, k, v, 0.3)
+    assert np.abs(got - v.astype(np.float64).mean(axis=1, keepdims=True)).max() < 1e-12
+
+
+# --------------------------------------------------------------------------- block masses
+
+def test_mass_rows_sum_to_one_on_a_ragged_grid():
+    grid, tile = (5, 6, 7), (4, 4, 4)
+    N = 5 * 6 * 7
+    q, k, _ = _rand_qkv(1, N, 2, 16, 3)
+    M = O.block_mass(q * 2, k * 2, grid, tile, 0.25)
+    assert np.abs(M.sum(-1) - 1).max() < 1e-12
+    assert M.min() >= 0
+
+
+def test_mass_zero_query_is_key_count_share():
+    grid, tile = (5, 6, 4), (4, 4, 4)
+    q, k, _ = _rand_qkv(1, 120, 1, 8, 4)
+    q[:] = 0
+    M = O.block_mass(q, k, grid, tile, 1.0)
+    want = np.array([64, 32, 16, 8]) / 120.0
+    assert np.abs(M[0, 0] - want).max() < 1e-13
+
+
+def test_mass_single_block_is_one():
+    q, k, _ = _rand_qkv(1, 64, 2, 8, 5)
+    M = O.block_mass(q, k, (4, 4, 4), (4, 4, 4), 0.5)
+    assert M.shape == (1, 2, 1, 1) and np.abs(M - 1).max() < 1e-13
+
+
+def test_mass_closed_form_with_blockwise_constant_scores():
+    # every query = alpha*e0, every key of block b = beta_b*e0, so the score of any
+    # query against block b is scale*alpha*beta_b and the mass of b is
+    # c(b) e^{s_b} / sum_b' c(b') e^{s_b'} for every query block.
+    grid, tile = (5, 6, 4), (4, 4, 4)
+    sizes = np.array([64, 32, 16, 8], dtype=np.float64)
+    blk, _ = O.token_blocks(grid, tile)
+    beta = np.array([0.5, -1.0, 2.0, 1.25])
+    q = np.zeros((1, 120, 1, 8), np.float32); q[..., 0] = 1.5
+    k = np.zeros((1, 120, 1, 8), np.float32); k[0, :, 0, 0] = beta[blk]
+    scale = 0.75
+    s = scale * 1.5 * beta
+    want = sizes * np.exp(s) / np.sum(sizes * np.exp(s))
+    M = O.block_mass(q, k, grid, tile, scale)
+    for qb in range(4):
+        assert np.abs(M[0, 0, qb] - want).max() < 1e-13
+
+
+def test_mass_subset_rows_equal_full_rows():
+    grid, tile = (4, 8, 12), (4, 4, 4)
+    q, k, _ = _rand_qkv(1, 4 * 8 * 12, 2, 16, 6)
+    full = O.block_mass(q, k, grid, tile, 0.3)
+    part = O.block_mass(q, k, grid, tile, 0.3, qblocks=[5, 0, 3])
+    assert np.array_equal(part, full[:, :, [5, 0, 3]])
+
+
+def test_mass_follows_swapped_key_blocks():
+    # swapping the keys of two equal-sized blocks swaps their mass columns
+    grid, tile = (4, 8, 8), (4, 4, 4)
+    q, k, _ = _rand_qkv(1, 256, 1, 16, 7)
+    blk, _ = O.token_blocks(grid, tile)
+    a, b = np.where(blk == 1)[0], np.where(blk == 2)[0]
+    k2 = k.copy(); k2[:, a], k2[:, b] = k[:, b], k[:, a]
+    M, M2 = O.block_mass(q, k, grid, tile, 0.3), O.block_mass(q, k2, grid, tile, 0.3)
+    assert np.abs(M2[..., [0, 2, 1, 3]] - M).max() < 1e-14
+
+
+# --------------------------------------------------------------------------- selection
+
+def test_mass_key_exact_values():
+    assert O.mass_key(0.5) == 2 ** 39
+    assert O.mass_key(1.0) == 2 ** 40
+    assert O.mass_key(3.0) == 2 ** 40
+    assert O.mass_key(2.0 ** -40) == 1
+    assert O.mass_key(2.0 ** -41) == 0
+    assert O.mass_key(0.0) == 0 and O.mass_key(-0.25) == 0 and O.mass_key(float("nan")) == 0
+    m = float(np.float32(0.1))
+    assert O.mass_key(m) == math.floor(m * 2 ** 40)
+
+
+def _csr_rows(rp, ci):
+    return [ci[rp[r]:rp[r + 1]].tolist() for r in range(len(rp) - 1)]
+
+
+def test_selection_hand_examples():
+    row = np.array([[1 / 2, 1 / 4, 1 / 8, 1 / 16, 1 / 32, 1 / 32]], np.float32)
+    assert _csr_rows(*O.select_blocks(row, 99, 100)) == [[0, 1, 2, 3, 4, 5]]
+    assert _csr_rows(*O.select_blocks(row, 1, 2)) == [[0]]          # exactly half: >= holds
+    assert _csr_rows(*O.select_blocks(row, 3, 4)) == [[0, 1]]
+    assert _csr_rows(*O.select_blocks(row, 15, 16)) == [[0, 1, 2, 3]]
+    # ties go to the lower block index
+    row = np.full((1, 4), 0.25, np.float32)
+    assert _csr_rows(*O.select_blocks(row, 1, 2)) == [[0, 1]]
+    row = np.array([[0.1, 0.3, 0.3, 0.3]], np.float32)
+    assert _csr_rows(*O.select_blocks(row, 1, 2)) == [[1, 2]]
+    # all-zero row keeps nothing; so does a zero threshold
+    assert _csr_rows(*O.select_blocks(np.zeros((1, 5), np.float32))) == [[]]
+    assert _csr_rows(*O.select_blocks(np.ones((1, 3), np.float32) / 3, 0, 100)) == [[]]
+    # kept indices come out ascending even when the ranking is not
+    row = np.array([[0.05, 0.6, 0.05, 0.3]], np.float32)
+    assert _csr_rows(*O.select_blocks(row, 9, 10)) == [[1, 3]]
+
+
+def _brute_force_select(row, num, den):
+    keys = [math.floor(float(x) * 2 ** 40) if x > 0 else 0 for x in row]
+    keys = [min(kk, 2 ** 40) for kk in keys]
+    S = sum(keys)
+    nb = len(row)
+    for size in range(0, nb + 1):
+        best = None
+        for sub in itertools.combinations(range(nb), size):
+            c = sum(keys[i] for i in sub)
+            if den * c >= num * S:
+                cand = (-c, list(sub))
+                if best is None or cand < best:
+                    best = cand
+        if best is not None:
+            return best[1]
+    raise AssertionError("unreachable")
+
+
+@pytest.mark.parametrize("nb,num,den", [(4, 99, 100), (8, 99, 100), (10, 9, 10), (12, 99, 100), (9, 1, 2)])
+def test_selection_equals_brute_force(nb, num, den):
+    rows = synth.random_mass_rows(24 if nb <= 10 else 6, nb, seed=nb * 7 + num, tie_frac=0.3, zero_frac=0.1)
+    # add rows with heavy exact ties
+    rows = np.concatenate([rows, np.full((1, nb), 1.0 / nb, np.float32)])
+    got = _csr_rows(*O.select_blocks(rows, num, den))
+    for r in range(rows.shape[0]):
+        assert got[r] == _brute_force_select(rows[r], num, den), r
+
+
+def test_selection_is_minimal_and_rank_consistent():
+    rows = synth.random_mass_rows(300, 97, seed=11)
+    rp, ci = O.select_blocks(rows)
+    for r in range(rows.shape[0]):
+        keys = np.array([O.mass_key(x) for x in rows[r]], dtype=object)
+        kept = ci[rp[r]:rp[r + 1]]
+        S, C = int(keys.sum()), int(keys[kept].sum())
+        assert 100 * C >= 99 * S
+        if len(kept):
+            weakest = min(kept, key=lambda i: (keys[i], -i))
+            assert 100 * (C - int(keys[weakest])) < 99 * S
+        dropped = np.setdiff1d(np.arange(rows.shape[1]), kept)
+        for d in dropped:
+            for kk in kept:
+                assert (keys[kk] > keys[d]) or (keys[kk] == keys[d] and kk < d)
+
+
+def test_cut_margin_of_dyadic_row():
+    # masses 0.5, 0.3, 0.2 at p = 0.75: keep 2, c = 0.8, prev = 0.5, gap 0.1
+    m = O.cut_margin(np.array([[0.5, 0.3, 0.2]]), 0.75)
+    assert abs(m[0] - 0.05) < 1e-15
+
+
+# --------------------------------------------------------------------------- masked attention
+
+def test_all_blocks_mask_equals_dense_attention():
+    grid, tile = (5, 6, 7), (4, 4, 4)
+    N, nb = 210, O.num_blocks(grid, tile)
+    q, k, v = _rand_qkv(1, N, 2, 16, 8)
+    rp = np.arange(0, 2 * nb * nb + 1, nb, dtype=np.int32)
+    ci = np.tile(np.arange(nb, dtype=np.int32), 2 * nb)
+    out, tok = O.masked_attention(q, k, v, grid, tile, 0.25, rp, ci)
+    dense = _torch_sdpa(q, k, v, 0.25)
+    for h in range(2):
+        for qb in range(nb):
+            t = tok[0, h, qb]
+            t = t[t >= 0]
+            assert np.abs(out[0, h, qb, :len(t)] - dense[0, t, h]).max() < 1e-12
+
+
+def test_single_kept_block_is_attention_within_that_block():
+    grid, tile = (4, 8, 8), (4, 4, 4)
+    q, k, v = _rand_qkv(1, 256, 1, 16, 9)
+    blk, _ = O.token_blocks(grid, tile)
+    rp = np.array([0, 1, 2, 2, 3], np.int32)           # qb0->{2}, qb1->{0}, qb2->{}, qb3->{3}
+    ci = np.array([2, 0, 3], np.int32)
+    out, tok = O.masked_attention(q, k, v, grid, tile, 0.4, rp, ci)
+    for qb, kb in [(0, 2), (1, 0), (3, 3)]:
+        qs, ks = np.where(blk == qb)[0], np.where(blk == kb)[0]
+        ref = _torch_sdpa(q[:, qs], k[:, ks], v[:, ks], 0.4)
+        assert np.array_equal(tok[0, 0, qb], qs)
+        assert np.abs(out[0, 0, qb] - ref[0, :, 0]).max() < 1e-12
+    assert np.all(out[0, 0, 2] == 0)                   # empty row: zero output
+
+
+def test_masked_attention_constant_values_give_constant_output():
+    grid, tile = (5, 6, 7), (4, 4, 4)
+    q, k, v = _rand_qkv(1, 210, 1, 8, 10)
+    v[:] = 0.375
+    nb = O.num_blocks(grid, tile)
+    rows = synth.random_mass_rows(nb, nb, seed=3)
+    rp, ci = O.select_blocks(rows, 1, 2)
+    out, tok = O.masked_attention(q, k, v, grid, tile, 0.3, rp, ci)
+    for qb in range(nb):
+        n = int((tok[0, 0, qb] >= 0).sum())
+        expect = 0.375 if rp[qb + 1] > rp[qb] else 0.0
+        assert np.abs(out[0, 0, qb, :n] - expect).max() < 1e-14
+
+
+# --------------------------------------------------------------------------- fp8 e4m3
+
+def test_e4m3_code_table():
+    # OCP 8-bit floating point spec, E4M3 (bias 7, no infinities, S.1111.111 = NaN)
+    assert O.e4m3_decode(0x00) == 0.0 and math.copysign(1, O.e4m3_decode(0x80)) < 0
+    assert O.e4m3_decode(0x01) == 2.0 ** -9                   # smallest subnormal
+    assert O.e4m3_decode(0x07) == 7 * 2.0 ** -9               # largest subnormal
+    assert O.e4m3_decode(0x08) == 2.0 ** -6                   # smallest normal
+    assert O.e4m3_decode(0x38) == 1.0
+    assert O.e4m3_decode(0x39) == 1.125
+    assert O.e4m3_decode(0x40) == 2.0 and O.e4m3_decode(0x44) == 3.0
+    assert O.e4m3_decode(0x7E) == 448.0 and O.e4m3_decode(0xFE) == -448.0
+    assert O.e4m3_decode(0x78) == 256.0
+    assert math.isnan(O.e4m3_decode(0x7F)) and math.isnan(O.e4m3_decode(0xFF))
+    mags = [O.e4m3_decode(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(mags, mags[1:]))
+    assert len([c for c in range(256) if math.isnan(O.e4m3_decode(c))]) == 2
+
+
+def test_e4m3_encode_roundtrip_rne_and_saturation():
+    for c in list(range(0x7F)) + list(range(0x81, 0xFF)):
+        assert O.e4m3_encode(O.e4m3_decode(c)) == c
+    assert O.e4m3_encode(1.0625) == 0x38      # midpoint 1 / 1.125 -> even code
+    assert O.e4m3_encode(1.1875) == 0x3A      # midpoint 1.125 / 1.25 -> even code
+    assert O.e4m3_encode(1.0626) == 0x39
+    assert O.e4m3_encode(2.0 ** -10) == 0x00  # half the smallest subnormal -> even (zero)
+    assert O.e4m3_encode(3 * 2.0 ** -10) == 0x02
+    assert O.e4m3_encode(449.0) == 0x7E and O.e4m3_encode(464.0) == 0x7E
+    assert O.e4m3_encode(1e9) == 0x7E and O.e4m3_encode(-1e9) == 0xFE
+    assert O.e4m3_encode(-3.0) == 0xC4
+
+
+def test_fp8_tile_quantize_scales_and_error():
+    grid, tile = (5, 6, 4), (4, 4, 4)
+    x = _rand_qkv(1, 120, 2, 16, 12)[0]
+    blk, _ = O.token_blocks(grid, tile)
+    x[0, blk == 2, 1, :] = 0.0                               # an all-zero tile
+    xhat, sc = O.fp8_tile_quantize(x, grid, tile)
+    for h in range(2):
+        for b in range(4):
+            sel = x[0, blk == b, h, :]
+            if np.all(sel == 0):
+                assert sc[0, h, b] == 1.0
+                continue
+            amax = np.float32(np.abs(sel).max())
+            assert sc[0, h, b] == np.float32(amax / np.float32(448.0))
+            xs = xhat[0, blk == b, h, :]
+            # the largest element lands on 448 * scale; e4m3 relative step <= 2^-3 for normals
+            assert np.isclose(np.abs(xs).max(), 448.0 * sc[0, h, b], rtol=1e-6)
+            big = np.abs(sel) > 2.0 ** -6 * sc[0, h, b]
+            assert np.all(np.abs(xs[big] - sel[big]) <= 2.0 ** -4 * np.abs(sel[big]) * 1.0001)
+
+
+# --------------------------------------------------------------------------- structured mask
+
+def test_structured_mask_counts_by_hand():
+    # interior group: its row (64) + its column (64) - itself + 4 diagonal neighbours = 131;
+    # border groups lose 2 diagonals (129), corners lose 3 (128)
+    rp, ci = O.structured_mask(64, 64)
+    counts = np.diff(rp)
+    assert len(ci) == 4 * 128 + 4 * 62 * 129 + 62 * 62 * 131 == 536068
+    vals, freq = np.unique(counts, return_counts=True)
+    assert dict(zip(vals.tolist(), freq.tolist())) == {128: 4, 129: 248, 131: 3844}
+
+
+def test_structured_mask_small_grid_by_enumeration():
+    rp, ci = O.structured_mask(3, 4)
+    rows = _csr_rows(rp, ci)
+    # group (1, 1) = id 5: everything in row 1, column 1, and the 3x3 around it
+    assert rows[5] == [0, 1, 2, 4, 5, 6, 7, 8, 9, 10]
+    # corner (0, 0): row 0, column 0, and (1, 1)
+    assert rows[0] == [0, 1, 2, 3, 4, 5, 8]
+    rp2, ci2 = O.structured_mask(3, 4, copies=2)
+    assert _csr_rows(rp2, ci2) == rows + rows
