@@ -1,0 +1,216 @@
+"""Benchmark of the whole block-sparse hot path on one MI355X.
+
+One step = tile Q, K (rows) and V (VT) -> dense block-mass pass -> 99 % retained-mass
+selection -> block-sparse forward over the kept blocks -> untile O, on the
+Wan2.1-1.3B-shaped 480p workload (grid 21x30x52, 12 heads, head size 128, bf16,
+synthetic seeded inputs already resident in HBM).
+
+Prints one JSON line. `value` is kept-block TFLOP per step (nnz * 4 * 64 * 64 * D,
+the MFMA work of the sparse forward) divided by the whole step time; per-kernel
+times come from HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "fp8": 5000.0}          # dense MFMA, TFLOP/s
+HBM_PEAK = 8000.0                                # GB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="wan480p")
+    p.add_argument("--cpu-sample", type=int, default=24,
+                   help="query blocks of head 0 the oracle runs for the CPU baseline (0: skip)")
+    p.add_argument("--kernels-only", action="store_true", help="skip the CPU baseline")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_reorder_amd import synth
+    from block_sparse_attention_reorder_amd.pipeline import BlockSparseAttention
+    from block_sparse_attention_reorder_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = synth.make_qkv(w.grid, w.B, w.H, w.D, w.amp, w.sigma, w.seed, bf16=True)
+    qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
+    bsa = BlockSparseAttention(w.grid, w.tile, w.B, w.H, w.D, device=dev)
+
+    qt = torch.empty(bsa.tiled_shape(), dtype=torch.bfloat16, device=dev)
+    kt = torch.empty_like(qt)
+    vt = torch.empty_like(qt)
+    ot = torch.empty_like(qt)
+    o = torch.empty((w.B, bsa.N, w.H, w.D), dtype=torch.bfloat16, device=dev)
+    mass = torch.empty((w.B, w.H, bsa.nb, bsa.nb), dtype=torch.float32, device=dev)
+    csr = bsa.new_csr()
+    ws = bsa.workspace()
+    stream = torch.cuda.current_stream()
+
+    stages = ["tile_qkv", "block_mass", "select", "sparse_fwd", "untile"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bsa.tile_rows(qd, qt)
+        bsa.tile_rows(kd, kt)
+        bsa.tile_vt(vd, vt)
+        if ev is not None:
+            ev[1].record(stream)
+        bsa.block_mass(qt, kt, mass=mass)
+        if ev is not None:
+            ev[2].record(stream)
+        bsa.select(mass, 99, 100, csr=csr, workspace=ws)
+        if ev is not None:
+            ev[3].record(stream)
+        bsa.forward(qt, kt, vt, csr, out=ot)
+        if ev is not None:
+            ev[4].record(stream)
+        bsa.untile(ot, out=o)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nnz = int(csr.row_ptr[-1].item())
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    per = {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
+           for j, s in enumerate(stages)}
+    assert int(csr.row_ptr[-1].item()) == nnz
+
+    D, H, B = w.D, w.H, w.B
+    kept_flop = nnz * 4.0 * 64 * 64 * D
+    mass_flop = 4.0 * bsa.npad * bsa.npad * D * H * B
+    eff_flop = 4.0 * bsa.N * bsa.N * D * H * B           # dense-equivalent over real tokens
+    tile_bytes = 3 * (B * bsa.N * H * D * 2 + B * H * bsa.npad * D * 2)
+    untile_bytes = B * H * bsa.npad * D * 2 + B * bsa.N * H * D * 2
+    select_bytes = 4 * bsa.R * bsa.nb * 2 + 4 * (bsa.R + 1) + 4 * nnz   # mass read twice
+    kernels = {
+        "sparse_fwd": {"bound": "mfma", "ms": per["sparse_fwd"], "achieved": kept_flop / per["sparse_fwd"] / 1e9,
+                       "peak": PEAK["bf16"], "unit": "TFLOP/s", "work_per_unit": "4*64*64*D FLOP per kept block pair",
+                       "units": nnz},
+        "block_mass": {"bound": "mfma", "ms": per["block_mass"], "achieved": mass_flop / per["block_mass"] / 1e9,
+                       "peak": PEAK["bf16"], "unit": "TFLOP/s", "work_per_unit": "2 passes * 2*64*64*D FLOP per block pair",
+                       "units": bsa.R * bsa.nb},
+        "tile_qkv": {"bound": "hbm", "ms": per["tile_qkv"], "achieved": tile_bytes / per["tile_qkv"] / 1e6,
+                     "peak": HBM_PEAK, "unit": "GB/s", "work_per_unit": "D*2 bytes read + D*2 written per token-head",
+                     "units": 3 * B * H * bsa.npad},
+        "select": {"bound": "hbm", "ms": per["select"], "achieved": select_bytes / per["select"] / 1e6,
+                   "peak": HBM_PEAK, "unit": "GB/s", "work_per_unit": "2*nb*4 bytes read per row + CSR written",
+                   "units": bsa.R},
+        "untile": {"bound": "hbm", "ms": per["untile"], "achieved": untile_bytes / per["untile"] / 1e6,
+                   "peak": HBM_PEAK, "unit": "GB/s", "work_per_unit": "D*2 bytes read + D*2 written per token-head",
+                   "units": B * H * bsa.npad},
+    }
+    for kk in kernels.values():
+        kk["frac"] = kk["achieved"] / kk["peak"]
+    dominant = max(kernels, key=lambda n: kernels[n]["ms"])
+    dk = kernels[dominant]
+    roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": round(dk["achieved"], 2),
+                "peak": dk["peak"], "unit": dk["unit"], "frac": round(dk["frac"], 4),
+                "traffic": None}
+
+    cpu = None
+    if args.cpu_sample > 0 and not args.kernels_only:
+        cpu = cpu_baseline(w, q, k, v, bsa, args.cpu_sample)
+
+    out = {
+        "metric": "block-sparse attn ms/call + kept-block TFLOP/s (% MFMA peak), Wan-1.3B 480p shape",
+        "value": round(kept_flop / ms_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded sinusoidal positional features + N(0,1) noise, bf16",
+        "config": {"workload": f"{w.name}: {w.note}", "grid": list(w.grid), "tile": list(w.tile),
+                   "batch": w.B, "heads": w.H, "head_dim": w.D, "threshold": "99/100",
+                   "nb": bsa.nb, "kept_pairs": nnz, "density": round(nnz / (bsa.R * bsa.nb), 4)},
+        "sparse_fwd_ms_per_call": round(per["sparse_fwd"], 4),
+        "sparse_fwd_kept_tflops": round(kernels["sparse_fwd"]["achieved"], 2),
+        "sparse_fwd_frac_of_bf16_peak": round(kernels["sparse_fwd"]["frac"], 4),
+        "sparse_fwd_effective_tflops": round(eff_flop / per["sparse_fwd"] / 1e9, 2),
+        "stage_ms": {s: round(x, 4) for s, x in per.items()},
+        "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in d.items()}
+                    for n, d in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(w, q, k, v, bsa, nsample):
+    """The oracle, as it stands, on a bounded sample: mass pass, selection and masked
+    attention for `nsample` query blocks of head 0 (first, last and seeded others).
+    Reported in the same unit as `value`: kept-block FLOP of the sampled rows over the
+    oracle's time for those rows."""
+    import numpy as np
+
+    import oracle as O
+
+    rng = np.random.default_rng(12345)
+    nb = bsa.nb
+    picks = sorted(set([0, nb - 1] + rng.choice(nb, size=max(0, nsample - 2), replace=False).tolist()))[:nsample]
+    q0, k0, v0 = (np.ascontiguousarray(x[:, :, :1, :]) for x in (q, k, v))
+    t0 = time.perf_counter()
+    m = O.block_mass(q0, k0, w.grid, w.tile, bsa.scale, qblocks=picks)
+    t1 = time.perf_counter()
+    rows = m.reshape(len(picks), nb).astype(np.float32)
+    rp_s, ci_s = O.select_blocks(rows)
+    t2 = time.perf_counter()
+    # expand the sampled rows into a CSR over all rows of head 0 (others empty)
+    rp = np.zeros(nb + 1, np.int32)
+    counts = np.zeros(nb, np.int64)
+    for i, qb in enumerate(picks):
+        counts[qb] = rp_s[i + 1] - rp_s[i]
+    rp[1:] = np.cumsum(counts)
+    ci = ci_s if len(ci_s) else np.zeros(1, np.int32)        # picks are ascending
+    O.masked_attention(q0, k0, v0, w.grid, w.tile, bsa.scale, rp, ci, qblocks=picks)
+    t3 = time.perf_counter()
+    kept = int(len(ci_s))
+    flop = kept * 4.0 * 64 * 64 * w.D
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(flop / (t3 - t0) / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(picks)} query blocks of head 0 of {w.name} (first, last, seeded others): "
+                      f"float64 mass pass {t1 - t0:.2f} s, selection {t2 - t1:.3f} s, masked attention "
+                      f"{t3 - t2:.2f} s; {kept} kept pairs",
+            "seconds": round(t3 - t0, 3)}
+
+
+if __name__ == "__main__":
+    main()

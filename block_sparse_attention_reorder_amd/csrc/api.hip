@@ -1,0 +1,179 @@
+// C ABI of the block-sparse attention library (declared in include/fpsa.h).
+// Every argument is checked on the host before anything is enqueued; kernels are
+// launched asynchronously on the caller's stream and launch errors come back as
+// FPSA_ERR_HIP. No device memory is allocated and no state is kept between calls.
+#include <hip/hip_runtime.h>
+
+#include "../../include/fpsa.h"
+#include "fpsa_internal.h"
+
+using fpsa::Geom;
+
+namespace {
+
+bool make_geom(const fpsa_grid* g, Geom* out) {
+    if (g == nullptr) return false;
+    if (g->t <= 0 || g->h <= 0 || g->w <= 0) return false;
+    if (g->tile_t <= 0 || g->tile_h <= 0 || g->tile_w <= 0) return false;
+    if ((long)g->tile_t * g->tile_h * g->tile_w != fpsa::kBlock) return false;
+    Geom r;
+    r.T = g->t; r.Hg = g->h; r.Wg = g->w;
+    r.tt = g->tile_t; r.th = g->tile_h; r.tw = g->tile_w;
+    r.nt = (g->t + g->tile_t - 1) / g->tile_t;
+    r.nh = (g->h + g->tile_h - 1) / g->tile_h;
+    r.nw = (g->w + g->tile_w - 1) / g->tile_w;
+    long nb = (long)r.nt * r.nh * r.nw;
+    if (nb > (1L << 24)) return false;                  // keeps 64*nb and grid sizes in range
+    r.nb = (int)nb;
+    *out = r;
+    return true;
+}
+
+int32_t hip_status() {
+    return hipGetLastError() == hipSuccess ? FPSA_OK : FPSA_ERR_HIP;
+}
+
+bool dims_ok(int32_t B, int32_t H) { return B >= 1 && H >= 1 && B <= 65535 && H <= 65535; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t fpsa_version(void) { return 100; }
+
+int32_t fpsa_num_blocks(const fpsa_grid* g) {
+    Geom geo;
+    if (!make_geom(g, &geo)) return -1;
+    return geo.nb;
+}
+
+const char* fpsa_status_string(int32_t s) {
+    switch (s) {
+        case FPSA_OK: return "ok";
+        case FPSA_ERR_INVALID_ARG: return "invalid argument";
+        case FPSA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case FPSA_ERR_CAPACITY: return "output capacity too small";
+        case FPSA_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+size_t fpsa_select_workspace_bytes(int64_t R, int32_t nb) {
+    if (R <= 0 || nb <= 0) return 0;
+    return fpsa::select_workspace_bytes((long)R);
+}
+
+int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t dst_dtype,
+                          int32_t dst_layout, float* dst_scale, int32_t B, int32_t H, int32_t D,
+                          const fpsa_grid* g, int32_t inverse, void* stream) {
+    Geom geo;
+    if (!make_geom(g, &geo) || !dims_ok(B, H)) return FPSA_ERR_INVALID_ARG;
+    if (src == nullptr || dst == nullptr) return FPSA_ERR_INVALID_ARG;
+    if (inverse != 0 && inverse != 1) return FPSA_ERR_INVALID_ARG;
+    if (dst_layout != FPSA_LAYOUT_ROWS && dst_layout != FPSA_LAYOUT_VT) return FPSA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    const long N = (long)g->t * g->h * g->w;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (inverse) {
+        if (src_dtype != FPSA_BF16 || dst_layout != FPSA_LAYOUT_ROWS) return FPSA_ERR_UNSUPPORTED;
+        if (dst_dtype != FPSA_F32 && dst_dtype != FPSA_BF16) return FPSA_ERR_UNSUPPORTED;
+        if (dst_scale != nullptr) return FPSA_ERR_INVALID_ARG;
+        fpsa::launch_tile_inverse(src, dst, dst_dtype == FPSA_F32 ? 0 : 1, geo, N, B, H, D, st);
+        return hip_status();
+    }
+    if (src_dtype != FPSA_F32 && src_dtype != FPSA_BF16) return FPSA_ERR_UNSUPPORTED;
+    int mode;
+    if (dst_dtype == FPSA_BF16) {
+        if (dst_scale != nullptr) return FPSA_ERR_INVALID_ARG;
+        mode = dst_layout == FPSA_LAYOUT_VT ? 1 : 0;
+    } else if (dst_dtype == FPSA_FP8_E4M3) {
+        if (dst_scale == nullptr) return FPSA_ERR_INVALID_ARG;
+        if (dst_layout != FPSA_LAYOUT_ROWS) return FPSA_ERR_UNSUPPORTED;
+        mode = 2;
+    } else {
+        return FPSA_ERR_UNSUPPORTED;
+    }
+    fpsa::launch_tile_forward(src, src_dtype == FPSA_F32 ? 0 : 1, dst, mode, dst_scale, geo, N, B, H,
+                              D, st);
+    return hip_status();
+}
+
+int32_t fpsa_block_mass(const void* q_tiled, const void* k_tiled, int32_t B, int32_t H, int32_t D,
+                        const fpsa_grid* g, float softmax_scale, float* mass, float* lse,
+                        void* stream) {
+    Geom geo;
+    if (!make_geom(g, &geo) || !dims_ok(B, H)) return FPSA_ERR_INVALID_ARG;
+    if (q_tiled == nullptr || k_tiled == nullptr || mass == nullptr) return FPSA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return FPSA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    if (geo.nb > FPSA_MAX_SELECT_BLOCKS) return FPSA_ERR_UNSUPPORTED;
+    if ((long)B * H * geo.nb > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
+    fpsa::launch_block_mass(q_tiled, k_tiled, B, H, D, geo, softmax_scale, mass, lse,
+                            static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_select_blocks(const float* mass, int64_t R, int32_t nb, uint32_t thr_num,
+                           uint32_t thr_den, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t col_capacity, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (mass == nullptr || row_ptr == nullptr || col_idx == nullptr || workspace == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (R <= 0 || R > (1L << 24) || nb <= 0) return FPSA_ERR_INVALID_ARG;
+    if (nb > FPSA_MAX_SELECT_BLOCKS) return FPSA_ERR_UNSUPPORTED;
+    if (thr_den < 1 || thr_den > 1000 || thr_num > thr_den) return FPSA_ERR_INVALID_ARG;
+    if ((int64_t)R * nb > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;   // nnz must fit int32
+    if (col_capacity < (int64_t)R * nb) return FPSA_ERR_CAPACITY;
+    if (workspace_bytes < fpsa::select_workspace_bytes((long)R)) return FPSA_ERR_CAPACITY;
+    fpsa::launch_select(mass, (long)R, nb, thr_num, thr_den, row_ptr, col_idx, workspace,
+                        static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_structured_mask(const fpsa_grid* g, int32_t copies, int32_t* row_ptr,
+                             int32_t* col_idx, int64_t col_capacity, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    Geom geo;
+    if (!make_geom(g, &geo)) return FPSA_ERR_INVALID_ARG;
+    if (copies < 1 || row_ptr == nullptr || col_idx == nullptr || workspace == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (geo.nt != 1) return FPSA_ERR_UNSUPPORTED;          // a 2D grid of groups only
+    const int64_t R = (int64_t)copies * geo.nb;
+    if (R > (1L << 24)) return FPSA_ERR_UNSUPPORTED;
+    const int64_t need = R * (int64_t)(geo.nh + geo.nw + 9);
+    if (need > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    if (col_capacity < need) return FPSA_ERR_CAPACITY;
+    if (workspace_bytes < fpsa::select_workspace_bytes((long)R)) return FPSA_ERR_CAPACITY;
+    fpsa::launch_structured(geo, copies, row_ptr, col_idx, workspace,
+                            static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t qk_dtype,
+                             const float* q_scale, const float* k_scale, const int32_t* row_ptr,
+                             const int32_t* col_idx, int32_t B, int32_t H, int32_t D,
+                             const fpsa_grid* g, float softmax_scale, void* o, float* lse,
+                             void* stream) {
+    Geom geo;
+    if (!make_geom(g, &geo) || !dims_ok(B, H)) return FPSA_ERR_INVALID_ARG;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FPSA_ERR_INVALID_ARG;
+    if (row_ptr == nullptr || col_idx == nullptr) return FPSA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return FPSA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    if ((long)B * H * geo.nb > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
+    int fp8;
+    if (qk_dtype == FPSA_BF16) {
+        if (q_scale != nullptr || k_scale != nullptr) return FPSA_ERR_INVALID_ARG;
+        fp8 = 0;
+    } else if (qk_dtype == FPSA_FP8_E4M3) {
+        if (q_scale == nullptr || k_scale == nullptr) return FPSA_ERR_INVALID_ARG;
+        fp8 = 1;
+    } else {
+        return FPSA_ERR_UNSUPPORTED;
+    }
+    fpsa::launch_sparse_attn(q, k, v, fp8, q_scale, k_scale, row_ptr, col_idx, B, H, D, geo,
+                             softmax_scale, o, lse, static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+}  // extern "C"

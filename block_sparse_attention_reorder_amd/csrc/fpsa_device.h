@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 kernels: geometry of the tiled token
+// layout, vector types for MFMA operands, and wave-wide reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fpsa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
+constexpr int kBlock = 64;                       // tokens per tile (block)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Tile geometry of a token grid. Blocks are numbered in raster order over the
+// tile grid; slots inside a block follow the raster order of the tile.
+struct Geom {
+    int T, Hg, Wg;          // token grid
+    int tt, th, tw;         // tile shape (product 64)
+    int nt, nh, nw;         // tiles per axis
+    int nb;                 // blocks
+
+    // Raster token index of (block, slot), or -1 for a padding slot.
+    __host__ __device__ inline long token(int blk, int e) const {
+        int bt = blk / (nh * nw), r = blk - bt * (nh * nw);
+        int bh = r / nw, bw = r - bh * nw;
+        int et = e / (th * tw), r2 = e - et * (th * tw);
+        int eh = r2 / tw, ew = r2 - eh * tw;
+        int t = bt * tt + et, h = bh * th + eh, w = bw * tw + ew;
+        if (t >= T || h >= Hg || w >= Wg) return -1;
+        return ((long)t * Hg + h) * Wg + w;
+    }
+    __host__ __device__ inline bool valid(int blk, int e) const { return token(blk, e) >= 0; }
+    // Number of real tokens in a block.
+    __host__ __device__ inline int count(int blk) const {
+        int bt = blk / (nh * nw), r = blk - bt * (nh * nw);
+        int bh = r / nw, bw = r - bh * nw;
+        int ct = min(tt, T - bt * tt), ch = min(th, Hg - bh * th), cw = min(tw, Wg - bw * tw);
+        return ct * ch * cw;
+    }
+    __host__ __device__ inline bool full(int blk) const { return count(blk) == kBlock; }
+};
+
+// 64-bit mask of the real slots of a block (bit e set when slot e holds a token).
+// Every lane of the wave must call it; lane e tests slot e.
+__device__ inline uint64_t block_valid_mask(const Geom& g, int blk) {
+    int lane = threadIdx.x & 63;
+    return __ballot(g.valid(blk, lane));
+}
+
+__device__ inline float wave_max32(float x) {  // combine the two 32-lane halves
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ inline float wave_add32(float x) { return x + __shfl_xor(x, 32); }
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+__device__ inline uint64_t wave_sum_u64(uint64_t x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor((unsigned long long)x, o);
+    return x;
+}
+
+__device__ inline float bf16_to_f32(__bf16 x) { return (float)x; }
+
+// Pack 8 floats into 8 bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ inline bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                     float a6, float a7) {
+    bf16x8 r;
+    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+    return r;
+}
+
+// Which slot of a 16-slot run feeds operand position j of the P*V product: the
+// score accumulator of a 32x32 MFMA hands lane half h the rows 4h..4h+3 and
+// 8+4h..8+4h+3 of each 16-row run, and operand position 8h + j must hold them.
+__host__ __device__ inline int vt_slot_of_position(int pos) {
+    int run = pos & ~15, p = pos & 15;
+    int h = p >> 3, j = p & 7;
+    return run + 4 * h + (j & 3) + 8 * (j >> 2);
+}
+
+}  // namespace fpsa

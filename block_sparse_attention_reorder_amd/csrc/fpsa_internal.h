@@ -1,0 +1,34 @@
+// Kernel launchers behind the C ABI (host side). Arguments are validated by the
+// caller in api.hip before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fpsa_device.h"
+
+namespace fpsa {
+
+void launch_tile_forward(const void* src, int src_dt, void* dst, int mode, float* scale,
+                         const Geom& g, long N, int B, int H, int D, hipStream_t st);
+void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, long N, int B,
+                         int H, int D, hipStream_t st);
+
+void launch_block_mass(const void* q, const void* k, int B, int H, int D, const Geom& g,
+                       float scale, float* mass, float* lse, hipStream_t st);
+
+// Workspace layout for selection: per row a kept count (int32) and the cut key
+// (uint64) with the number of tied keys kept (int32).
+size_t select_workspace_bytes(long R);
+void launch_select(const float* mass, long R, int nb, uint32_t num, uint32_t den, int32_t* row_ptr,
+                   int32_t* col_idx, void* ws, hipStream_t st);
+void launch_structured(const Geom& g, int copies, int32_t* row_ptr, int32_t* col_idx, void* ws,
+                       hipStream_t st);
+
+void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, const float* q_scale,
+                        const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
+                        int B, int H, int D, const Geom& g, float scale, void* o, float* lse,
+                        hipStream_t st);
+
+}  // namespace fpsa

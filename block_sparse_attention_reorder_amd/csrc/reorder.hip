@@ -1,0 +1,206 @@
+// Token permutation between raster order and 64-token tiles, with the FP8 e4m3
+// per-tile quantization folded into the same pass (one tile = one sparsity block =
+// one quantization group, [FPSAttention: Training-Aware FP8 and Sparsity Co-Design
+// for Fast Video Diffusion, Abstract]).
+//
+// One workgroup per (block, head, batch) moves 64 x D values. Both sides are
+// contiguous: a source token row is H*D elements with this head's D in the middle,
+// a destination block is 64*D contiguous elements, so every access is a 16-byte
+// vector load or store. HBM-bound by construction.
+#include "fpsa_device.h"
+#include "fpsa_internal.h"
+
+namespace fpsa {
+
+// Nearest-even OCP e4m3fn encoding of a finite float, saturating to +-448.
+__device__ inline uint32_t encode_e4m3(float y) {
+    uint32_t bits = __float_as_uint(y);
+    uint32_t sign = (bits >> 24) & 0x80u;
+    float a = fabsf(y);
+    if (!(a == a)) return 0x7Fu;                        // NaN
+    if (a > 448.0f) return sign | 0x7Eu;                // beyond the largest finite: saturate
+    if (a < 0.015625f) {                                // below 2^-6: subnormal step 2^-9
+        float q = rintf(a * 512.0f);                    // exact scaling; rint rounds to even
+        return sign | (uint32_t)q;                      // q == 8 is code 0x08 = 2^-6
+    }
+    uint32_t ab = __float_as_uint(a);
+    int e = (int)((ab >> 23) & 0xFF) - 127;             // -6 .. 8
+    uint32_t man = ab & 0x7FFFFFu;
+    uint32_t keep = man >> 20, rest = man & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep++;
+    if (keep == 8u) { keep = 0; e++; }
+    return sign | ((uint32_t)(e + 7) << 3) | keep;      // a <= 448 keeps this <= 0x7E
+}
+
+template <typename SrcT>
+__device__ inline void load8(const SrcT* p, float* v);
+
+template <>
+__device__ inline void load8<__bf16>(const __bf16* p, float* v) {
+    bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+}
+
+template <>
+__device__ inline void load8<float>(const float* p, float* v) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+
+// MODE 0: bf16 tiled rows; MODE 1: bf16 tiled VT; MODE 2: e4m3 tiled rows + scale.
+template <typename SrcT, int D, int MODE>
+__global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ src,
+                                                      void* __restrict__ dst,
+                                                      float* __restrict__ scale_out, Geom g,
+                                                      long N, int H) {
+    constexpr int kChunks = kBlock * D / 8;             // 8-element chunks per block
+    constexpr int kPerThread = kChunks / 256;
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const long bh = (long)b * H + h;
+
+    float v[kPerThread][8];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        int c = tid + 256 * i;
+        int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
+        long n = g.token(blk, e);
+        if (n >= 0) {
+            load8<SrcT>(src + (((long)b * N + n) * H + h) * D + d0, v[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+        }
+    }
+
+    if constexpr (MODE == 0) {
+        __bf16* out = reinterpret_cast<__bf16*>(dst) + (bh * g.nb + blk) * (long)(kBlock * D);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            int c = tid + 256 * i;
+            *reinterpret_cast<bf16x8*>(out + (long)c * 8) =
+                pack_bf16x8(v[i][0], v[i][1], v[i][2], v[i][3], v[i][4], v[i][5], v[i][6], v[i][7]);
+        }
+    } else if constexpr (MODE == 1) {
+        // Stage the block as bf16 [slot][d] in LDS, then emit [d][position] rows.
+        __shared__ __bf16 tile[kBlock][D + 8];
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            int c = tid + 256 * i;
+            int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
+            *reinterpret_cast<bf16x8*>(&tile[e][d0]) =
+                pack_bf16x8(v[i][0], v[i][1], v[i][2], v[i][3], v[i][4], v[i][5], v[i][6], v[i][7]);
+        }
+        __syncthreads();
+        __bf16* out = reinterpret_cast<__bf16*>(dst) + (bh * g.nb + blk) * (long)(kBlock * D);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            int c = tid + 256 * i;                       // chunk of 8 positions of one d
+            int d = c / (kBlock / 8), p0 = (c % (kBlock / 8)) * 8;
+            bf16x8 r;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[j] = tile[vt_slot_of_position(p0 + j)][d];
+            *reinterpret_cast<bf16x8*>(out + (long)d * kBlock + p0) = r;
+        }
+    } else {
+        // FP8: scale = float32(amax / 448) over the whole 64 x D tile.
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        __shared__ float wmax[4];
+        if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        const float s = amax > 0.0f ? amax / 448.0f : 1.0f;   // IEEE division
+        if (tid == 0) scale_out[bh * g.nb + blk] = s;
+        uint8_t* out = reinterpret_cast<uint8_t*>(dst) + (bh * g.nb + blk) * (long)(kBlock * D);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            int c = tid + 256 * i;
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo |= encode_e4m3(v[i][j] / s) << (8 * j);
+                hi |= encode_e4m3(v[i][4 + j] / s) << (8 * j);
+            }
+            i32x2 w;
+            w[0] = (int)lo;
+            w[1] = (int)hi;
+            *reinterpret_cast<i32x2*>(out + (long)c * 8) = w;
+        }
+    }
+}
+
+template <typename DstT, int D>
+__global__ __launch_bounds__(256) void k_tile_inverse(const __bf16* __restrict__ src,
+                                                      DstT* __restrict__ dst, Geom g, long N,
+                                                      int H) {
+    constexpr int kChunks = kBlock * D / 8;
+    constexpr int kPerThread = kChunks / 256;
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const long bh = (long)b * H + h;
+    const __bf16* in = src + (bh * g.nb + blk) * (long)(kBlock * D);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        int c = threadIdx.x + 256 * i;
+        int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
+        long n = g.token(blk, e);
+        if (n < 0) continue;
+        bf16x8 x = *reinterpret_cast<const bf16x8*>(in + (long)c * 8);
+        DstT* o = dst + (((long)b * N + n) * H + h) * D + d0;
+        if constexpr (sizeof(DstT) == 2) {
+            *reinterpret_cast<bf16x8*>(o) = x;
+        } else {
+            f32x4 a, bq;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { a[j] = (float)x[j]; bq[j] = (float)x[4 + j]; }
+            *reinterpret_cast<f32x4*>(o) = a;
+            *reinterpret_cast<f32x4*>(o + 4) = bq;
+        }
+    }
+}
+
+template <int D>
+static void launch_forward(const void* src, int src_dt, void* dst, int mode, float* scale,
+                           const Geom& g, long N, int B, int H, hipStream_t st) {
+    dim3 grid(g.nb, H, B);
+    if (src_dt == 0) {
+        const float* s = static_cast<const float*>(src);
+        if (mode == 0) k_tile_forward<float, D, 0><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        else if (mode == 1) k_tile_forward<float, D, 1><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        else k_tile_forward<float, D, 2><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+    } else {
+        const __bf16* s = static_cast<const __bf16*>(src);
+        if (mode == 0) k_tile_forward<__bf16, D, 0><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        else if (mode == 1) k_tile_forward<__bf16, D, 1><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        else k_tile_forward<__bf16, D, 2><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+    }
+}
+
+void launch_tile_forward(const void* src, int src_dt, void* dst, int mode, float* scale,
+                         const Geom& g, long N, int B, int H, int D, hipStream_t st) {
+    if (D == 128) launch_forward<128>(src, src_dt, dst, mode, scale, g, N, B, H, st);
+    else launch_forward<64>(src, src_dt, dst, mode, scale, g, N, B, H, st);
+}
+
+void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, long N, int B,
+                         int H, int D, hipStream_t st) {
+    dim3 grid(g.nb, H, B);
+    const __bf16* s = static_cast<const __bf16*>(src);
+    if (D == 128) {
+        if (dst_dt == 0) k_tile_inverse<float, 128><<<grid, 256, 0, st>>>(s, (float*)dst, g, N, H);
+        else k_tile_inverse<__bf16, 128><<<grid, 256, 0, st>>>(s, (__bf16*)dst, g, N, H);
+    } else {
+        if (dst_dt == 0) k_tile_inverse<float, 64><<<grid, 256, 0, st>>>(s, (float*)dst, g, N, H);
+        else k_tile_inverse<__bf16, 64><<<grid, 256, 0, st>>>(s, (__bf16*)dst, g, N, H);
+    }
+}
+
+}  // namespace fpsa

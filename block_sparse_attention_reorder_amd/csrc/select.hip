@@ -1,0 +1,247 @@
+// Retained-mass block selection: for each (head, query block) row of block masses,
+// keep the smallest set of key blocks whose mass reaches the threshold (99 %),
+// ranking by mass and breaking ties toward the lower block index [LoSA:
+// Near-Lossless Sparse Attention for Training-Free Video Diffusion Acceleration,
+// Abstract]. Also builds the fixed group-shared structured mask [Grouping First,
+// Attending Smartly: Training-Free Acceleration for Diffusion Transformers,
+// Abstract] into the same CSR form.
+//
+// Arithmetic is on integer keys floor(m * 2^40), so the cut is exact and
+// reproducible. The kept set is the top of the ranking up to the cut key v*:
+// every key above v*, plus the lowest-indexed keys equal to v* that are still
+// needed. v* is the largest key value v for which the keys >= v already reach the
+// threshold; it is found bit by bit (41 wave-wide sums) instead of by sorting,
+// which gives the same set as sort + prefix sum + cut. One wavefront per row; the
+// ascending output order falls out of ballot prefix counts over index order.
+#include "fpsa_device.h"
+#include "fpsa_internal.h"
+
+namespace fpsa {
+
+constexpr int kSelWaves = 4;               // rows per workgroup (one wave each)
+constexpr size_t kSelLdsBytes = 64 * 1024; // keys of all rows of a workgroup live in LDS
+
+// Rows (waves) per workgroup of the counting kernel so that their keys fit in LDS.
+static int select_waves(int nb) {
+    int w = (int)(kSelLdsBytes / ((size_t)nb * 8));
+    return w < 1 ? 1 : (w > kSelWaves ? kSelWaves : w);
+}
+
+__device__ inline uint64_t mass_key(float m) {
+    if (!(m > 0.0f)) return 0;             // zero, negative, NaN
+    if (m >= 1.0f) return 1ull << 40;
+    // m < 1: m * 2^40 is an exact exponent shift of a 24-bit significand < 2^40.
+    return (uint64_t)(double)(m * 1099511627776.0f);
+}
+
+__device__ inline uint64_t lanemask_lt() {
+    int lane = threadIdx.x & 63;
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Per row: kept count, cut key and how many keys equal to the cut key are kept.
+// Dynamic LDS: (blockDim.x / 64) * nb keys.
+__global__ __launch_bounds__(64 * kSelWaves) void k_select_count(const float* __restrict__ mass,
+                                                                 long R, int nb, uint32_t num,
+                                                                 uint32_t den,
+                                                                 int32_t* __restrict__ count,
+                                                                 uint64_t* __restrict__ cut,
+                                                                 int32_t* __restrict__ ties) {
+    extern __shared__ uint64_t keys[];
+    const int waves = blockDim.x >> 6;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long r = (long)blockIdx.x * waves + w;
+    if (r >= R) return;
+    const float* row = mass + r * nb;
+    uint64_t* kk = keys + (size_t)w * nb;
+    uint64_t part = 0;
+    for (int i = lane; i < nb; i += 64) {
+        uint64_t key = mass_key(row[i]);
+        kk[i] = key;
+        part += key;
+    }
+    const uint64_t S = wave_sum_u64(part);
+    int kept = 0;
+    uint64_t vstar = 0;
+    int nties = 0;
+    if (S > 0 && num > 0) {
+        const uint64_t target = (uint64_t)num * S;     // <= 1000 * 2^52
+        uint64_t v = 0;
+        for (int bit = 40; bit >= 0; --bit) {
+            uint64_t cand = v | (1ull << bit);
+            uint64_t c = 0;
+            for (int i = lane; i < nb; i += 64) {
+                uint64_t key = kk[i];
+                c += key >= cand ? key : 0;
+            }
+            c = wave_sum_u64(c);
+            if ((uint64_t)den * c >= target) v = cand;
+        }
+        // v >= 1 here: all positive keys sum to S and den >= num.
+        uint64_t cgt = 0;
+        int ngt = 0;
+        for (int i = lane; i < nb; i += 64) {
+            uint64_t key = kk[i];
+            if (key > v) { cgt += key; ngt++; }
+        }
+        cgt = wave_sum_u64(cgt);
+        for (int o = 32; o >= 1; o >>= 1) ngt += __shfl_xor(ngt, o);
+        // den*cgt < target by maximality of v; the tied keys needed, each worth v:
+        const uint64_t need = target - (uint64_t)den * cgt;
+        const uint64_t per = (uint64_t)den * v;
+        nties = (int)((need + per - 1) / per);
+        kept = ngt + nties;
+        vstar = v;
+    }
+    if (lane == 0) {
+        count[r] = kept;
+        cut[r] = vstar;
+        ties[r] = nties;
+    }
+}
+
+// Exclusive scan of per-row counts into row_ptr[R + 1] with a single workgroup.
+__global__ __launch_bounds__(1024) void k_scan_counts(const int32_t* __restrict__ count, long R,
+                                                      int32_t* __restrict__ row_ptr) {
+    __shared__ int32_t wsum[16];
+    const int tid = threadIdx.x;
+    const long per = (R + 1023) / 1024;
+    const long lo = min((long)tid * per, R), hi = min(lo + per, R);
+    int32_t local = 0;
+    for (long i = lo; i < hi; ++i) local += count[i];
+    // inclusive scan of `local` across the workgroup
+    int lane = tid & 63, w = tid >> 6;
+    int32_t x = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int32_t before = 0;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    int32_t run = before + x - local;            // exclusive prefix of this thread's chunk
+    for (long i = lo; i < hi; ++i) {
+        row_ptr[i] = run;
+        run += count[i];
+    }
+    if (tid == 1023) {
+        int32_t total = 0;
+        for (int i = 0; i < 16; ++i) total += wsum[i];
+        row_ptr[R] = total;
+    }
+}
+
+// Write kept indices of each row in ascending order.
+__global__ __launch_bounds__(64 * kSelWaves) void k_select_fill(const float* __restrict__ mass,
+                                                                long R, int nb,
+                                                                const uint64_t* __restrict__ cut,
+                                                                const int32_t* __restrict__ ties,
+                                                                const int32_t* __restrict__ row_ptr,
+                                                                int32_t* __restrict__ col_idx) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long r = (long)blockIdx.x * kSelWaves + w;
+    if (r >= R) return;
+    const float* row = mass + r * nb;
+    const uint64_t v = cut[r];
+    const int need_ties = ties[r];
+    int32_t* out = col_idx + row_ptr[r];
+    if (row_ptr[r + 1] == row_ptr[r]) return;
+    const uint64_t lt = lanemask_lt();
+    int tie_base = 0, out_base = 0;
+    for (int i0 = 0; i0 < nb; i0 += 64) {
+        int i = i0 + lane;
+        uint64_t key = i < nb ? mass_key(row[i]) : 0;
+        bool tie = i < nb && key == v;
+        uint64_t tmask = __ballot(tie);
+        int tie_rank = tie_base + __popcll(tmask & lt);
+        bool keep = i < nb && (key > v || (tie && tie_rank < need_ties));
+        uint64_t kmask = __ballot(keep);
+        if (keep) out[out_base + __popcll(kmask & lt)] = i;
+        tie_base += __popcll(tmask);
+        out_base += __popcll(kmask);
+    }
+}
+
+size_t select_workspace_bytes(long R) {
+    // count int32 [R] | ties int32 [R] | cut uint64 [R], each 256-byte aligned
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return up((size_t)R * 4) * 2 + up((size_t)R * 8);
+}
+
+static void carve(void* ws, long R, int32_t** count, int32_t** ties, uint64_t** cut) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    char* p = static_cast<char*>(ws);
+    *count = reinterpret_cast<int32_t*>(p);
+    *ties = reinterpret_cast<int32_t*>(p + up((size_t)R * 4));
+    *cut = reinterpret_cast<uint64_t*>(p + 2 * up((size_t)R * 4));
+}
+
+void launch_select(const float* mass, long R, int nb, uint32_t num, uint32_t den, int32_t* row_ptr,
+                   int32_t* col_idx, void* ws, hipStream_t st) {
+    int32_t *count, *ties;
+    uint64_t* cut;
+    carve(ws, R, &count, &ties, &cut);
+    const int cw = select_waves(nb);
+    unsigned cblocks = (unsigned)((R + cw - 1) / cw);
+    k_select_count<<<cblocks, 64 * cw, (size_t)cw * nb * 8, st>>>(mass, R, nb, num, den, count, cut,
+                                                                  ties);
+    unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
+    k_scan_counts<<<1, 1024, 0, st>>>(count, R, row_ptr);
+    k_select_fill<<<blocks, 64 * kSelWaves, 0, st>>>(mass, R, nb, cut, ties, row_ptr, col_idx);
+}
+
+// ---------------------------------------------------------------- structured mask
+
+__device__ inline bool structured_keep(int qb, int kb, int nw) {
+    int r = qb / nw, c = qb - r * nw, r2 = kb / nw, c2 = kb - r2 * nw;
+    return (abs(r - r2) <= 1 && abs(c - c2) <= 1) || r2 == r || c2 == c;
+}
+
+__global__ __launch_bounds__(64 * kSelWaves) void k_structured_count(int nb, int nw, long R,
+                                                                     int32_t* __restrict__ count) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long r = (long)blockIdx.x * kSelWaves + w;
+    if (r >= R) return;
+    const int qb = (int)(r % nb);
+    int n = 0;
+    for (int i0 = 0; i0 < nb; i0 += 64) {
+        int kb = i0 + lane;
+        n += __popcll(__ballot(kb < nb && structured_keep(qb, kb, nw)));
+    }
+    if (lane == 0) count[r] = n;
+}
+
+__global__ __launch_bounds__(64 * kSelWaves) void k_structured_fill(int nb, int nw, long R,
+                                                                    const int32_t* __restrict__ row_ptr,
+                                                                    int32_t* __restrict__ col_idx) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long r = (long)blockIdx.x * kSelWaves + w;
+    if (r >= R) return;
+    const int qb = (int)(r % nb);
+    int32_t* out = col_idx + row_ptr[r];
+    const uint64_t lt = lanemask_lt();
+    int base = 0;
+    for (int i0 = 0; i0 < nb; i0 += 64) {
+        int kb = i0 + lane;
+        bool keep = kb < nb && structured_keep(qb, kb, nw);
+        uint64_t m = __ballot(keep);
+        if (keep) out[base + __popcll(m & lt)] = kb;
+        base += __popcll(m);
+    }
+}
+
+void launch_structured(const Geom& g, int copies, int32_t* row_ptr, int32_t* col_idx, void* ws,
+                       hipStream_t st) {
+    long R = (long)copies * g.nb;
+    int32_t *count, *ties;
+    uint64_t* cut;
+    carve(ws, R, &count, &ties, &cut);
+    unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
+    k_structured_count<<<blocks, 64 * kSelWaves, 0, st>>>(g.nb, g.nw, R, count);
+    k_scan_counts<<<1, 1024, 0, st>>>(count, R, row_ptr);
+    k_structured_fill<<<blocks, 64 * kSelWaves, 0, st>>>(g.nb, g.nw, R, row_ptr, col_idx);
+}
+
+}  // namespace fpsa

@@ -1,0 +1,173 @@
+"""Thin ctypes binding of libfpsa.so (include/fpsa.h): argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU (PyTorch provides
+device memory and streams), checks dtype/shape/contiguity, and passes raw device
+pointers plus the current HIP stream to the C ABI. Every computation runs in the
+library's HIP kernels; there is no fallback. A non-OK status raises FpsaError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfpsa.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP = 0, 1, 2, 3, 4
+F32, BF16, FP8_E4M3 = 0, 1, 2
+LAYOUT_ROWS, LAYOUT_VT = 0, 1
+MAX_SELECT_BLOCKS = 4096
+
+EXPORTED = [
+    "fpsa_num_blocks", "fpsa_status_string", "fpsa_version", "fpsa_select_workspace_bytes",
+    "fpsa_tile_reorder", "fpsa_block_mass", "fpsa_select_blocks", "fpsa_structured_mask",
+    "fpsa_sparse_attn_fwd",
+]
+
+
+class FpsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class Grid(ctypes.Structure):
+    _fields_ = [("t", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32),
+                ("tile_t", ctypes.c_int32), ("tile_h", ctypes.c_int32), ("tile_w", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, grid, tile) -> "Grid":
+        return cls(*[int(x) for x in grid], *[int(x) for x in tile])
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library; raise if it was never built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_reorder_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+        gp = ctypes.POINTER(Grid)
+        L.fpsa_num_blocks.restype = i32
+        L.fpsa_num_blocks.argtypes = [gp]
+        L.fpsa_status_string.restype = ctypes.c_char_p
+        L.fpsa_status_string.argtypes = [i32]
+        L.fpsa_version.restype = i32
+        L.fpsa_version.argtypes = []
+        L.fpsa_select_workspace_bytes.restype = ctypes.c_size_t
+        L.fpsa_select_workspace_bytes.argtypes = [i64, i32]
+        L.fpsa_tile_reorder.restype = i32
+        L.fpsa_tile_reorder.argtypes = [vp, i32, vp, i32, i32, vp, i32, i32, i32, gp, i32, vp]
+        L.fpsa_block_mass.restype = i32
+        L.fpsa_block_mass.argtypes = [vp, vp, i32, i32, i32, gp, f32, vp, vp, vp]
+        L.fpsa_select_blocks.restype = i32
+        L.fpsa_select_blocks.argtypes = [vp, i64, i32, u32, u32, vp, vp, i64, vp, ctypes.c_size_t, vp]
+        L.fpsa_structured_mask.restype = i32
+        L.fpsa_structured_mask.argtypes = [gp, i32, vp, vp, i64, vp, ctypes.c_size_t, vp]
+        L.fpsa_sparse_attn_fwd.restype = i32
+        L.fpsa_sparse_attn_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, gp, f32,
+                                           vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().fpsa_status_string(int(s)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise FpsaError(status, what)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: FP8_E4M3, torch.float8_e4m3fn: FP8_E4M3}
+
+
+# --------------------------------------------------------------------------- host-only
+
+def num_blocks(grid, tile) -> int:
+    g = Grid.of(grid, tile)
+    return int(lib().fpsa_num_blocks(ctypes.byref(g)))
+
+
+def select_workspace_bytes(R: int, nb: int) -> int:
+    return int(lib().fpsa_select_workspace_bytes(int(R), int(nb)))
+
+
+def version() -> int:
+    return int(lib().fpsa_version())
+
+
+# --------------------------------------------------------------------------- device calls
+
+def tile_reorder(src, dst, grid, tile, B, H, D, *, inverse=False, layout=LAYOUT_ROWS,
+                 dst_scale=None, stream=None) -> None:
+    """fpsa_tile_reorder; dtypes are taken from the tensors (uint8 = e4m3 bytes)."""
+    g = Grid.of(grid, tile)
+    s = lib().fpsa_tile_reorder(_ptr(src), _DT[src.dtype], _ptr(dst), _DT[dst.dtype], int(layout),
+                                _ptr(dst_scale), int(B), int(H), int(D), ctypes.byref(g),
+                                1 if inverse else 0, _stream(stream))
+    _check(s, "fpsa_tile_reorder")
+
+
+def block_mass(q_tiled, k_tiled, grid, tile, B, H, D, softmax_scale, mass, lse=None, stream=None) -> None:
+    if q_tiled.dtype != torch.bfloat16 or k_tiled.dtype != torch.bfloat16:
+        raise ValueError("block_mass takes bf16 tiled Q and K")
+    if mass.dtype != torch.float32 or (lse is not None and lse.dtype != torch.float32):
+        raise ValueError("mass and lse are float32")
+    g = Grid.of(grid, tile)
+    s = lib().fpsa_block_mass(_ptr(q_tiled), _ptr(k_tiled), int(B), int(H), int(D), ctypes.byref(g),
+                              float(softmax_scale), _ptr(mass), _ptr(lse), _stream(stream))
+    _check(s, "fpsa_block_mass")
+
+
+def select_blocks(mass, R, nb, thr_num, thr_den, row_ptr, col_idx, workspace, stream=None) -> None:
+    if mass.dtype != torch.float32 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("mass float32, row_ptr/col_idx int32")
+    s = lib().fpsa_select_blocks(_ptr(mass), int(R), int(nb), int(thr_num), int(thr_den), _ptr(row_ptr),
+                                 _ptr(col_idx), int(col_idx.numel()), _ptr(workspace),
+                                 int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(s, "fpsa_select_blocks")
+
+
+def structured_mask(grid, tile, copies, row_ptr, col_idx, workspace, stream=None) -> None:
+    g = Grid.of(grid, tile)
+    s = lib().fpsa_structured_mask(ctypes.byref(g), int(copies), _ptr(row_ptr), _ptr(col_idx),
+                                   int(col_idx.numel()), _ptr(workspace),
+                                   int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(s, "fpsa_structured_mask")
+
+
+def sparse_attn_fwd(q, k, v, row_ptr, col_idx, grid, tile, B, H, D, softmax_scale, o, *,
+                    q_scale=None, k_scale=None, lse=None, stream=None) -> None:
+    qk_dt = _DT[q.dtype]
+    if _DT[k.dtype] != qk_dt or v.dtype != torch.bfloat16 or o.dtype != torch.bfloat16:
+        raise ValueError("q/k same dtype (bf16 or e4m3 bytes), v and o bf16")
+    g = Grid.of(grid, tile)
+    s = lib().fpsa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), qk_dt, _ptr(q_scale), _ptr(k_scale),
+                                   _ptr(row_ptr), _ptr(col_idx), int(B), int(H), int(D), ctypes.byref(g),
+                                   float(softmax_scale), _ptr(o), _ptr(lse), _stream(stream))
+    _check(s, "fpsa_sparse_attn_fwd")

@@ -1,0 +1,122 @@
+"""The whole hot path on one GPU, as calls into libfpsa.
+
+    raster Q, K, V --tile--> tiled Q, K (rows) and V (VT)
+        --block_mass--> M[B, H, nb, nb] --select_blocks (99 %)--> frozen CSR
+        --sparse_attn_fwd--> tiled O --tile (inverse)--> raster O
+
+The measurement and selection happen once; the CSR is then reused for every later
+call [LoSA: Near-Lossless Sparse Attention for Training-Free Video Diffusion
+Acceleration, Abstract]. A fixed structured CSR can stand in for the measured one
+[Grouping First, Attending Smartly: Training-Free Acceleration for Diffusion
+Transformers, Abstract]. This module only allocates device buffers (torch) and
+sequences the library calls; all arithmetic runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import fpsa
+
+
+@dataclass
+class Csr:
+    row_ptr: torch.Tensor      # int32 [R + 1]
+    col_idx: torch.Tensor      # int32 [capacity]; the first row_ptr[R] entries are used
+
+    def nnz(self) -> int:
+        return int(self.row_ptr[-1].item())
+
+
+class BlockSparseAttention:
+    """Buffers and calls for one geometry (grid, tile, B, H, D) on one device."""
+
+    def __init__(self, grid, tile, B, H, D, device="cuda", softmax_scale=None):
+        self.grid, self.tile = tuple(grid), tuple(tile)
+        self.B, self.H, self.D = int(B), int(H), int(D)
+        self.device = torch.device(device)
+        self.nb = fpsa.num_blocks(self.grid, self.tile)
+        if self.nb <= 0:
+            raise ValueError(f"invalid grid {grid} / tile {tile}")
+        self.N = self.grid[0] * self.grid[1] * self.grid[2]
+        self.npad = 64 * self.nb
+        self.R = self.B * self.H * self.nb
+        self.scale = float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(self.D)
+
+    # ------------------------------------------------------------------ layout
+    def tiled_shape(self):
+        return (self.B, self.H, self.npad, self.D)
+
+    def tile_rows(self, x, out=None, stream=None):
+        """raster [B, N, H, D] (f32/bf16) -> tiled rows bf16."""
+        out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device) if out is None else out
+        fpsa.tile_reorder(x, out, self.grid, self.tile, self.B, self.H, self.D, stream=stream)
+        return out
+
+    def tile_vt(self, x, out=None, stream=None):
+        """raster [B, N, H, D] -> tiled VT bf16 (value operand layout)."""
+        out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device) if out is None else out
+        fpsa.tile_reorder(x, out, self.grid, self.tile, self.B, self.H, self.D, layout=fpsa.LAYOUT_VT,
+                          stream=stream)
+        return out
+
+    def tile_fp8(self, x, out=None, scale=None, stream=None):
+        """raster [B, N, H, D] -> tiled e4m3 bytes + per-tile float32 scales [B, H, nb]."""
+        out = torch.empty(self.tiled_shape(), dtype=torch.uint8, device=self.device) if out is None else out
+        scale = torch.empty((self.B, self.H, self.nb), dtype=torch.float32, device=self.device) if scale is None else scale
+        fpsa.tile_reorder(x, out, self.grid, self.tile, self.B, self.H, self.D, dst_scale=scale, stream=stream)
+        return out, scale
+
+    def untile(self, o_tiled, dtype=torch.bfloat16, out=None, stream=None):
+        """tiled rows bf16 -> raster [B, N, H, D] of dtype (real tokens only)."""
+        out = torch.empty((self.B, self.N, self.H, self.D), dtype=dtype, device=self.device) if out is None else out
+        fpsa.tile_reorder(o_tiled, out, self.grid, self.tile, self.B, self.H, self.D, inverse=True, stream=stream)
+        return out
+
+    # ------------------------------------------------------------------ selection
+    def block_mass(self, qt, kt, mass=None, lse=None, want_lse=False, stream=None):
+        mass = torch.empty((self.B, self.H, self.nb, self.nb), dtype=torch.float32, device=self.device) if mass is None else mass
+        if want_lse and lse is None:
+            lse = torch.empty((self.B, self.H, self.npad), dtype=torch.float32, device=self.device)
+        fpsa.block_mass(qt, kt, self.grid, self.tile, self.B, self.H, self.D, self.scale, mass, lse, stream=stream)
+        return (mass, lse) if want_lse else mass
+
+    def new_csr(self, capacity=None) -> Csr:
+        cap = self.R * self.nb if capacity is None else int(capacity)
+        return Csr(torch.empty(self.R + 1, dtype=torch.int32, device=self.device),
+                   torch.empty(cap, dtype=torch.int32, device=self.device))
+
+    def workspace(self, rows=None):
+        n = fpsa.select_workspace_bytes(self.R if rows is None else rows, self.nb)
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+
+    def select(self, mass, thr_num=99, thr_den=100, csr=None, workspace=None, stream=None) -> Csr:
+        csr = self.new_csr() if csr is None else csr
+        ws = self.workspace() if workspace is None else workspace
+        fpsa.select_blocks(mass, self.R, self.nb, thr_num, thr_den, csr.row_ptr, csr.col_idx, ws, stream=stream)
+        return csr
+
+    def structured(self, stream=None) -> Csr:
+        nh = -(-self.grid[1] // self.tile[1])
+        nw = -(-self.grid[2] // self.tile[2])
+        csr = self.new_csr(capacity=self.R * (nh + nw + 9))
+        ws = self.workspace()
+        fpsa.structured_mask(self.grid, self.tile, self.B * self.H, csr.row_ptr, csr.col_idx, ws, stream=stream)
+        return csr
+
+    # ------------------------------------------------------------------ attention
+    def forward(self, qt, kt, vt, csr: Csr, q_scale=None, k_scale=None, out=None, lse=None, stream=None):
+        out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device) if out is None else out
+        fpsa.sparse_attn_fwd(qt, kt, vt, csr.row_ptr, csr.col_idx, self.grid, self.tile, self.B, self.H,
+                             self.D, self.scale, out, q_scale=q_scale, k_scale=k_scale, lse=lse, stream=stream)
+        return out
+
+    def run(self, q, k, v, thr_num=99, thr_den=100, out_dtype=torch.bfloat16):
+        """Full path on raster Q, K, V: returns (raster O, CSR, masses)."""
+        qt, kt, vt = self.tile_rows(q), self.tile_rows(k), self.tile_vt(v)
+        mass = self.block_mass(qt, kt)
+        csr = self.select(mass, thr_num, thr_den)
+        ot = self.forward(qt, kt, vt, csr)
+        return self.untile(ot, out_dtype), csr, mass

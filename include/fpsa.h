@@ -1,0 +1,192 @@
+/*
+ * fpsa.h - block-sparse attention over 3D-tiled token sequences, for AMD MI355X (gfx950).
+ *
+ * The method: tokens of a video latent (or image) are grouped into 64-token tiles,
+ * which serve both as the unit of sparsity and the unit of FP8 quantization
+ * [FPSAttention: Training-Aware FP8 and Sparsity Co-Design for Fast Video Diffusion,
+ * Abstract]. One dense step measures the exact softmax attention mass between every
+ * query tile and key tile; for each head and query tile the smallest set of key
+ * tiles holding 99 % of that mass is kept, and those frozen indices drive every
+ * later step [LoSA: Near-Lossless Sparse Attention for Training-Free Video
+ * Diffusion Acceleration, Abstract]. Attention then visits only kept tiles with an
+ * online softmax (FlashAttention style). A fixed structured key set shared by each
+ * query group (neighbouring groups plus the group's row and column) can replace the
+ * measured selection [Grouping First, Attending Smartly: Training-Free Acceleration
+ * for Diffusion Transformers, Abstract].
+ *
+ * Conventions for every call:
+ *   - Data pointers are DEVICE pointers owned by the caller, except `g`, which is a
+ *     host pointer. `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *   - No call allocates device memory, synchronises the device or keeps state
+ *     between calls; work is enqueued on `stream` and the status reports only
+ *     argument validation (done on the host before any launch) and launch errors.
+ *   - Buffers are contiguous, 16-byte aligned and must not overlap unless stated.
+ *   - Status codes: FPSA_OK, FPSA_ERR_INVALID_ARG (bad shape, pointer or value),
+ *     FPSA_ERR_UNSUPPORTED (valid but not implemented: head size, dtype combination,
+ *     grid kind), FPSA_ERR_CAPACITY (an output buffer is declared too small),
+ *     FPSA_ERR_HIP (the HIP runtime rejected a launch). Nothing is enqueued when a
+ *     call returns anything but FPSA_OK, except for FPSA_ERR_HIP, where earlier
+ *     kernels of the same call may have been enqueued.
+ *
+ * Geometry. A grid of T x Hg x Wg tokens (T = 1 for an image) in raster order
+ * n = (t*Hg + h)*Wg + w is cut into tiles of tile_t x tile_h x tile_w = 64 tokens;
+ * each axis is padded up to a multiple of its tile size. Tiles (blocks) are
+ * numbered in raster order over the tile grid, nb = ceil(T/tile_t) *
+ * ceil(Hg/tile_h) * ceil(Wg/tile_w), and inside a tile the 64 slots follow the
+ * raster order of the tile's positions. Slots outside the grid are padding: their
+ * tiled rows are zero, padding keys receive no attention and padding queries
+ * produce zero output. Npad = 64 * nb.
+ *
+ * Tensor layouts (B = batch, H = heads, D = head size in {64, 128}):
+ *   raster      [B, N, H, D]            N = T*Hg*Wg
+ *   tiled rows  [B, H, Npad, D]         row 64*blk + slot
+ *   tiled VT    [B, H, nb, D, 64]       per block, D-major; within each run of 16
+ *                                       keys the order is slots 0-3, 8-11, 4-7, 12-15
+ *                                       (the operand order of the P*V matrix product)
+ *   CSR         row_ptr[R + 1], col_idx[nnz] int32; R = B*H*nb rows, row
+ *               (b*H + h)*nb + qb; each row's key blocks ascending.
+ */
+#ifndef FPSA_H
+#define FPSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FPSA_OK = 0,
+    FPSA_ERR_INVALID_ARG = 1,
+    FPSA_ERR_UNSUPPORTED = 2,
+    FPSA_ERR_CAPACITY = 3,
+    FPSA_ERR_HIP = 4
+} fpsa_status;
+
+typedef enum { FPSA_F32 = 0, FPSA_BF16 = 1, FPSA_FP8_E4M3 = 2 } fpsa_dtype;
+
+typedef enum { FPSA_LAYOUT_ROWS = 0, FPSA_LAYOUT_VT = 1 } fpsa_layout;
+
+typedef struct {
+    int32_t t, h, w;                 /* token grid (t = 1 for an image) */
+    int32_t tile_t, tile_h, tile_w;  /* tile shape, product must be 64 */
+} fpsa_grid;
+
+/* Largest block count accepted by fpsa_block_mass and fpsa_select_blocks. */
+#define FPSA_MAX_SELECT_BLOCKS 4096
+
+/* Number of 64-token blocks of the grid; negative if the grid or tile is invalid.
+   Host-only. */
+int32_t fpsa_num_blocks(const fpsa_grid* g);
+
+/* Static, NUL-terminated description of a status code. Host-only. */
+const char* fpsa_status_string(int32_t status);
+
+/* Library version as major*10000 + minor*100 + patch. Host-only. */
+int32_t fpsa_version(void);
+
+/* Device scratch bytes fpsa_select_blocks needs for R rows of nb blocks. Host-only. */
+size_t fpsa_select_workspace_bytes(int64_t R, int32_t nb);
+
+/*
+ * Permute tokens between raster order and the tiled layout (the unified tile
+ * granularity of [FPSAttention ..., Abstract]).
+ *
+ * Forward (inverse = 0): src raster [B, N, H, D] of src_dtype (F32 or BF16) ->
+ *   dst tiled of dst_dtype:
+ *     BF16, layout ROWS: tiled rows, values rounded to nearest even;
+ *     BF16, layout VT:   tiled VT (the value operand of fpsa_sparse_attn_fwd);
+ *     FP8_E4M3, layout ROWS: tiled rows of OCP e4m3fn bytes plus dst_scale
+ *       [B, H, nb] float32: per (b, h, block) the scale is float32(amax / 448) over
+ *       the block's 64 x D values (1 when amax = 0) and each byte is the
+ *       nearest-even e4m3fn encoding of float32(x / scale), saturated to +-448.
+ *   Padding slots are written as zero.
+ * Inverse (inverse = 1): src tiled rows BF16 -> dst raster of dst_dtype (F32 or
+ *   BF16); only real tokens are written; layout must be ROWS, dst_scale NULL.
+ * dst_scale must be non-NULL exactly when dst_dtype is FP8_E4M3.
+ */
+int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t dst_dtype,
+                          int32_t dst_layout, float* dst_scale, int32_t B, int32_t H, int32_t D,
+                          const fpsa_grid* g, int32_t inverse, void* stream);
+
+/*
+ * Exact dense block attention mass (the one dense measurement step of [LoSA ...,
+ * Abstract]).
+ *
+ * q_tiled, k_tiled: tiled rows BF16. For each (b, h) and query block qb,
+ *   mass[b, h, qb, kb] = (1 / c(qb)) * sum over real queries i of qb and real keys j
+ *   of kb of softmax_j(softmax_scale * q_i . k_j), the softmax running over all real
+ *   keys and c(qb) the number of real queries in qb. Each row sums to 1.
+ * mass: [B, H, nb, nb] float32. lse: [B, H, Npad] float32 natural-log log-sum-exp of
+ *   each real query's scaled scores (padding rows get 0), or NULL.
+ * nb must not exceed FPSA_MAX_SELECT_BLOCKS.
+ */
+int32_t fpsa_block_mass(const void* q_tiled, const void* k_tiled, int32_t B, int32_t H, int32_t D,
+                        const fpsa_grid* g, float softmax_scale, float* mass, float* lse,
+                        void* stream);
+
+/*
+ * Retained-mass block selection ([LoSA ..., Abstract]: per head and query block,
+ * the smallest key-block set meeting the threshold).
+ *
+ * For each of the R rows of mass [R, nb] float32: key_k = floor(clamp(m_k, 0, 1) *
+ * 2^40) (NaN -> 0) as an integer; blocks are ranked by key, larger first, equal keys
+ * by lower index; the row keeps the shortest leading run of the ranking whose key
+ * sum C satisfies thr_den * C >= thr_num * S, S the row's key sum (nothing when
+ * S = 0). Kept indices are written ascending; row_ptr gets the exclusive prefix
+ * sum of the kept counts (row_ptr[R] = nnz). The result is exact and deterministic.
+ * Requires 0 <= thr_num <= thr_den, 1 <= thr_den <= 1000, 1 <= nb <=
+ * FPSA_MAX_SELECT_BLOCKS, R <= 2^24, col_capacity >= R * nb (FPSA_ERR_CAPACITY
+ * otherwise), workspace_bytes >= fpsa_select_workspace_bytes(R, nb).
+ */
+int32_t fpsa_select_blocks(const float* mass, int64_t R, int32_t nb, uint32_t thr_num,
+                           uint32_t thr_den, int32_t* row_ptr, int32_t* col_idx,
+                           int64_t col_capacity, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Structured group-shared mask ([Grouping First, Attending Smartly ..., Abstract]).
+ *
+ * Only for 2D grids (t = 1, tile_t = 1): the blocks form an nh x nw grid of token
+ * groups. Query group (r, c) keeps key group (r2, c2) when |r - r2| <= 1 and
+ * |c - c2| <= 1 (clipped at the border, itself included), or r2 = r, or c2 = c.
+ * The same rows are written for each of `copies` (= B*H) copies, so the CSR has
+ * R = copies * nb rows. col_capacity must be >= copies * nb * (nh + nw + 9);
+ * workspace_bytes >= fpsa_select_workspace_bytes(copies * nb, nb).
+ */
+int32_t fpsa_structured_mask(const fpsa_grid* g, int32_t copies, int32_t* row_ptr,
+                             int32_t* col_idx, int64_t col_capacity, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse attention forward with an online softmax over the kept blocks.
+ *
+ * q, k: tiled rows, BF16 when qk_dtype = FPSA_BF16, or FP8_E4M3 bytes with
+ *   q_scale / k_scale [B, H, nb] float32 (as produced by fpsa_tile_reorder) when
+ *   qk_dtype = FPSA_FP8_E4M3; scales must be NULL for BF16.
+ * v: tiled VT, BF16.
+ * row_ptr / col_idx: CSR with R = B*H*nb rows; key-block indices outside [0, nb)
+ *   are skipped.
+ * For each real query i of block qb of row r: o_i = sum_j p_ij v_j over the real
+ *   keys j of the kept blocks, p the softmax of softmax_scale * q_i . k_j over
+ *   exactly those keys (FP8: the scores use the decoded values, q8 * k8 * q_scale *
+ *   k_scale). Queries with no kept key, and padding rows, get o = 0. The kept blocks
+ *   are visited in CSR order; probabilities are rounded to BF16 for the P*V
+ *   product, which accumulates in float32, and the softmax denominator is the sum
+ *   of those rounded probabilities.
+ * o: tiled rows BF16 [B, H, Npad, D]. lse: [B, H, Npad] float32 natural-log
+ *   log-sum-exp over the visited keys, taken from the same rounded probabilities
+ *   that normalise o (-inf for a query with none; 0 for padding), or NULL.
+ */
+int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t qk_dtype,
+                             const float* q_scale, const float* k_scale, const int32_t* row_ptr,
+                             const int32_t* col_idx, int32_t B, int32_t H, int32_t D,
+                             const fpsa_grid* g, float softmax_scale, void* o, float* lse,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FPSA_H */

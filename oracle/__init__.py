@@ -29,6 +29,7 @@ _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
 _vp = ctypes.c_void_p
 
 
@@ -74,6 +75,8 @@ def lib():
             L.orc_e4m3_encode.argtypes = [ctypes.c_double]
             L.orc_fp8_tile_quantize.restype = None
             L.orc_fp8_tile_quantize.argtypes = [_f32p] + [ctypes.c_int] * 4 + [_i32p, ctypes.c_int, _f32p, _f32p]
+            L.orc_fp8_tile_codes.restype = None
+            L.orc_fp8_tile_codes.argtypes = [_f32p] + [ctypes.c_int] * 4 + [_i32p, ctypes.c_int, _u8p, _f32p]
             L.orc_structured_mask.restype = ctypes.c_int64
             L.orc_structured_mask.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p]
             _lib = L
@@ -206,6 +209,18 @@ def fp8_tile_quantize(x, grid, tile):
     scales = np.empty((B, H, nb), np.float32)
     lib().orc_fp8_tile_quantize(x, B, N, H, D, blk, nb, xhat, scales)
     return xhat, scales
+
+
+def fp8_tile_codes(x, grid, tile):
+    """(codes [B, N, H, D] uint8 raster, scales [B, H, nb] float32) of per-tile e4m3 quantization."""
+    x = _c(x, np.float32)
+    B, N, H, D = x.shape
+    blk, _ = token_blocks(grid, tile)
+    nb = num_blocks(grid, tile)
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty((B, H, nb), np.float32)
+    lib().orc_fp8_tile_codes(x, B, N, H, D, blk, nb, codes, scales)
+    return codes, scales
 
 
 # --------------------------------------------------------------------------- structured mask

@@ -411,3 +411,27 @@ int64_t orc_structured_mask(int gh, int gw, int copies, int32_t* row_ptr, int32_
         }
     return nnz;
 }
+
+/*
+ * The same per-tile quantization as orc_fp8_tile_quantize, returning the e4m3fn
+ * codes themselves: codes [B, N, H, D] (raster) and scales [B, H, nb].
+ */
+void orc_fp8_tile_codes(const float* x, int B, int N, int H, int D,
+                        const int32_t* block_of, int nb, uint8_t* codes, float* scales) {
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            float* sc = scales + ((int64_t)b * H + h) * nb;
+            for (int blk = 0; blk < nb; ++blk) sc[blk] = 0.0f;
+            for (int n = 0; n < N; ++n)
+                for (int d = 0; d < D; ++d) {
+                    float a = fabsf(x[RIX(b, n, h, d)]);
+                    if (a > sc[block_of[n]]) sc[block_of[n]] = a;
+                }
+            for (int blk = 0; blk < nb; ++blk) sc[blk] = sc[blk] > 0.0f ? sc[blk] / 448.0f : 1.0f;
+            for (int n = 0; n < N; ++n)
+                for (int d = 0; d < D; ++d) {
+                    float y = x[RIX(b, n, h, d)] / sc[block_of[n]];
+                    codes[RIX(b, n, h, d)] = orc_e4m3_encode((double)y);
+                }
+        }
+}

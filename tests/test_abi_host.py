@@ -1,0 +1,145 @@
+"""Host-only checks of the C ABI: the library loads, exports every function that
+include/fpsa.h declares, and rejects bad arguments on the host before any launch.
+No call here reaches the GPU (every device call made is one that must fail
+validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_reorder_amd import fpsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fpsa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fpsa.LIB_PATH):
+        from block_sparse_attention_reorder_amd import build
+        build.build(verbose=False)
+    return fpsa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fpsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_calls():
+    names = declared_functions()
+    for n in ["fpsa_tile_reorder", "fpsa_block_mass", "fpsa_select_blocks", "fpsa_sparse_attn_fwd",
+              "fpsa_structured_mask", "fpsa_num_blocks", "fpsa_status_string",
+              "fpsa_select_workspace_bytes", "fpsa_version"]:
+        assert n in names
+    assert sorted(fpsa.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_num_blocks_and_strings(L):
+    assert fpsa.num_blocks((21, 30, 52), (4, 4, 4)) == 624
+    assert fpsa.num_blocks((21, 45, 80), (4, 4, 4)) == 1440
+    assert fpsa.num_blocks((33, 45, 80), (4, 4, 4)) == 2160
+    assert fpsa.num_blocks((1, 512, 512), (1, 8, 8)) == 4096
+    assert fpsa.num_blocks((4, 8, 8), (4, 4, 4)) == 4
+    assert fpsa.num_blocks((4, 8, 8), (4, 4, 2)) < 0          # tile product 32
+    assert fpsa.num_blocks((0, 8, 8), (4, 4, 4)) < 0
+    assert fpsa.status_string(fpsa.OK) == "ok"
+    assert fpsa.status_string(fpsa.ERR_CAPACITY) == "output capacity too small"
+    assert fpsa.status_string(99) == "unknown status"
+    assert fpsa.version() >= 100
+
+
+def test_select_workspace_bytes(L):
+    assert fpsa.select_workspace_bytes(0, 10) == 0
+    n = fpsa.select_workspace_bytes(7488, 624)
+    assert n >= 7488 * 16 and n % 256 == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call below fails validation
+
+
+def grid(t=4, h=8, w=8, tt=4, th=4, tw=4):
+    return ctypes.byref(fpsa.Grid(t, h, w, tt, th, tw))
+
+
+def test_tile_reorder_validation(L):
+    f = L.fpsa_tile_reorder
+    ok_args = dict(src=FAKE, sdt=fpsa.BF16, dst=FAKE, ddt=fpsa.BF16, lay=0, sc=None, B=1, H=1, D=64, g=grid(), inv=0)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return f(a["src"], a["sdt"], a["dst"], a["ddt"], a["lay"], a["sc"], a["B"], a["H"], a["D"], a["g"], a["inv"], None)
+
+    assert call(src=None) == fpsa.ERR_INVALID_ARG
+    assert call(dst=None) == fpsa.ERR_INVALID_ARG
+    assert call(g=grid(tw=2)) == fpsa.ERR_INVALID_ARG
+    assert call(g=None) == fpsa.ERR_INVALID_ARG
+    assert call(B=0) == fpsa.ERR_INVALID_ARG
+    assert call(H=-1) == fpsa.ERR_INVALID_ARG
+    assert call(D=96) == fpsa.ERR_UNSUPPORTED
+    assert call(inv=2) == fpsa.ERR_INVALID_ARG
+    assert call(lay=7) == fpsa.ERR_INVALID_ARG
+    assert call(ddt=fpsa.FP8_E4M3) == fpsa.ERR_INVALID_ARG            # fp8 needs a scale buffer
+    assert call(ddt=fpsa.FP8_E4M3, sc=FAKE, lay=fpsa.LAYOUT_VT) == fpsa.ERR_UNSUPPORTED
+    assert call(sc=FAKE) == fpsa.ERR_INVALID_ARG                       # bf16 takes no scale
+    assert call(sdt=fpsa.FP8_E4M3) == fpsa.ERR_UNSUPPORTED
+    assert call(inv=1, sdt=fpsa.F32) == fpsa.ERR_UNSUPPORTED
+    assert call(inv=1, lay=fpsa.LAYOUT_VT) == fpsa.ERR_UNSUPPORTED
+    assert call(inv=1, ddt=fpsa.FP8_E4M3) == fpsa.ERR_UNSUPPORTED
+
+
+def test_block_mass_validation(L):
+    f = L.fpsa_block_mass
+    assert f(None, FAKE, 1, 1, 64, grid(), 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.125, None, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.0, FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, grid(), float("nan"), FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 32, grid(), 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
+    # 4097 blocks: beyond the selection limit
+    assert f(FAKE, FAKE, 1, 1, 64, grid(1, 8, 4097 * 8, 1, 8, 8), 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
+
+
+def test_select_blocks_validation(L):
+    f = L.fpsa_select_blocks
+    ws = fpsa.select_workspace_bytes(10, 8)
+    assert f(None, 10, 8, 99, 100, FAKE, FAKE, 80, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 0, 8, 99, 100, FAKE, FAKE, 80, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 0, 99, 100, FAKE, FAKE, 80, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 8, 101, 100, FAKE, FAKE, 80, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 8, 0, 0, FAKE, FAKE, 80, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 8, 99, 1001, FAKE, FAKE, 80, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 8, 99, 100, FAKE, FAKE, 79, FAKE, ws, None) == fpsa.ERR_CAPACITY
+    assert f(FAKE, 10, 8, 99, 100, FAKE, FAKE, 80, FAKE, ws - 1, None) == fpsa.ERR_CAPACITY
+    assert f(FAKE, 10, 4097, 99, 100, FAKE, FAKE, 10 * 4097, FAKE, ws, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, 10, 8, 99, 100, None, FAKE, 80, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+
+
+def test_structured_mask_validation(L):
+    f = L.fpsa_structured_mask
+    g2 = grid(1, 64, 64, 1, 8, 8)
+    ws = fpsa.select_workspace_bytes(64, 64)
+    assert f(grid(8, 8, 8), 1, FAKE, FAKE, 10 ** 6, FAKE, ws, None) == fpsa.ERR_UNSUPPORTED   # 2 tiles in t
+    assert f(g2, 0, FAKE, FAKE, 10 ** 6, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(g2, 1, FAKE, FAKE, 64 * 25 - 1, FAKE, ws, None) == fpsa.ERR_CAPACITY
+    assert f(g2, 1, FAKE, FAKE, 64 * 25, FAKE, 0, None) == fpsa.ERR_CAPACITY
+    assert f(g2, 1, None, FAKE, 64 * 25, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+
+
+def test_sparse_attn_validation(L):
+    f = L.fpsa_sparse_attn_fwd
+    g = grid()
+    assert f(None, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, FAKE, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.FP8_E4M3, None, FAKE, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.F32, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, None, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 80, g, 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, -1.0, FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, None, None, None) == fpsa.ERR_INVALID_ARG

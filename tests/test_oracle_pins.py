@@ -362,3 +362,15 @@ def test_structured_mask_small_grid_by_enumeration():
     assert rows[0] == [0, 1, 2, 3, 4, 5, 8]
     rp2, ci2 = O.structured_mask(3, 4, copies=2)
     assert _csr_rows(rp2, ci2) == rows + rows
+
+
+def test_fp8_tile_codes_decode_to_quantized_values():
+    grid, tile = (5, 6, 4), (4, 4, 4)
+    x = _rand_qkv(1, 120, 2, 16, 13)[0] * 7
+    codes, sc = O.fp8_tile_codes(x, grid, tile)
+    xhat, sc2 = O.fp8_tile_quantize(x, grid, tile)
+    blk, _ = O.token_blocks(grid, tile)
+    assert np.array_equal(sc, sc2)
+    dec = np.vectorize(O.e4m3_decode)(codes)
+    s = sc[0][:, blk].T[None, :, :, None]                 # [1, N, H, 1]
+    assert np.array_equal((dec * s).astype(np.float32), xhat)

@@ -1,0 +1,297 @@
+"""GPU parity of every step of the hot path against the CPU oracle, at sizes the
+oracle finishes in seconds (several tiles, ragged tails). All calls go through the
+C ABI of libfpsa.so."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_attention_reorder_amd import fpsa, synth
+from block_sparse_attention_reorder_amd.pipeline import BlockSparseAttention, Csr
+
+from parity_util import (BF16_MAX_ABS, BF16_MEAN_ABS, compare_selection, csr_to_numpy, dev,
+                         expected_tiled_rows, inputs, output_errors, rows_to_vt, value_scale)
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [((4, 8, 8), 1, 64), ((5, 6, 7), 2, 128), ((9, 10, 13), 3, 64), ((6, 9, 14), 2, 128)]
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy()
+
+
+# --------------------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("grid,H,D", RAGGED)
+@pytest.mark.parametrize("src_dtype", [torch.bfloat16, torch.float32])
+def test_tile_rows_bitexact(grid, H, D, src_dtype):
+    tile = (4, 4, 4)
+    x = inputs(grid, 1, H, D, bf16=(src_dtype == torch.bfloat16), seed=3)[0]
+    bsa = BlockSparseAttention(grid, tile, 1, H, D)
+    got = bsa.tile_rows(dev(x, src_dtype))
+    want = torch.from_numpy(expected_tiled_rows(x, grid, tile)).to(torch.bfloat16)
+    assert np.array_equal(_bits(got), want.view(torch.int16).numpy())
+
+
+@pytest.mark.parametrize("grid,H,D", RAGGED)
+def test_tile_vt_bitexact(grid, H, D):
+    tile = (4, 4, 4)
+    x = inputs(grid, 2, H, D, seed=4)[2]
+    bsa = BlockSparseAttention(grid, tile, 2, H, D)
+    got = bsa.tile_vt(dev(x, torch.bfloat16)).cpu().float().numpy()
+    want = rows_to_vt(expected_tiled_rows(x, grid, tile), bsa.nb)
+    assert np.array_equal(got.reshape(want.shape), want)
+
+
+@pytest.mark.parametrize("grid,H,D", RAGGED)
+@pytest.mark.parametrize("src_dtype", [torch.bfloat16, torch.float32])
+def test_tile_fp8_bitexact(grid, H, D, src_dtype):
+    tile = (4, 4, 4)
+    x = inputs(grid, 1, H, D, amp=2.0, bf16=(src_dtype == torch.bfloat16), seed=5)[0]
+    x[0, :7, 0, :] = 0.0                      # a block with leading zero rows
+    if H > 1:
+        x[0, :, 1, :] *= 1e-3                 # small values: subnormal e4m3 codes
+    if src_dtype == torch.bfloat16:
+        x = synth.to_bf16_values(x)           # both sides see the same bf16 values
+    bsa = BlockSparseAttention(grid, tile, 1, H, D)
+    codes, scales = bsa.tile_fp8(dev(x, src_dtype))
+    want_codes, want_scales = O.fp8_tile_codes(x, grid, tile)
+    _, slot = O.token_blocks(grid, tile)
+    tiled = np.zeros((1, H, bsa.npad, D), np.uint8)
+    tiled[:, :, slot, :] = np.transpose(want_codes, (0, 2, 1, 3))
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
+    assert np.array_equal(codes.cpu().numpy(), tiled)
+
+
+def test_tile_fp8_all_zero_tile_has_unit_scale():
+    grid, tile = (4, 8, 8), (4, 4, 4)
+    x = np.zeros((1, 256, 1, 64), np.float32)
+    x[0, 200, 0, 3] = 1.5
+    bsa = BlockSparseAttention(grid, tile, 1, 1, 64)
+    codes, scales = bsa.tile_fp8(dev(x, torch.bfloat16))
+    _, want_scales = O.fp8_tile_codes(x, grid, tile)
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
+    assert (want_scales == 1.0).sum() == 3
+
+
+@pytest.mark.parametrize("grid,H,D", RAGGED)
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_tile_inverse_roundtrip(grid, H, D, out_dtype):
+    tile = (4, 4, 4)
+    x = inputs(grid, 2, H, D, seed=6)[1]
+    bsa = BlockSparseAttention(grid, tile, 2, H, D)
+    t = bsa.tile_rows(dev(x, torch.bfloat16))
+    back = bsa.untile(t, out_dtype)
+    assert np.array_equal(back.float().cpu().numpy(), x)
+
+
+# --------------------------------------------------------------------------- selection
+
+def _gpu_select(mass_np, num, den):
+    R, nb = mass_np.shape
+    m = dev(mass_np, torch.float32)
+    rp = torch.empty(R + 1, dtype=torch.int32, device="cuda")
+    ci = torch.full((R * nb,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(fpsa.select_workspace_bytes(R, nb), dtype=torch.uint8, device="cuda")
+    fpsa.select_blocks(m, R, nb, num, den, rp, ci, ws)
+    return csr_to_numpy(rp, ci)
+
+
+@pytest.mark.parametrize("R,nb", [(5, 1), (40, 3), (64, 64), (64, 65), (300, 200), (500, 624),
+                                  (40, 2160), (12, 4096)])
+@pytest.mark.parametrize("num,den", [(99, 100), (1, 2), (9, 10), (1000, 1000), (0, 7)])
+def test_select_bitexact_on_seeded_masses(R, nb, num, den):
+    m = synth.random_mass_rows(R, nb, seed=R * 31 + nb, tie_frac=0.2, zero_frac=0.1)
+    m[0] = 0.0                                          # empty row
+    if R > 2:
+        m[1] = 1.0 / nb                                  # all ties
+    if R > 3:
+        m[2, : min(nb, 5)] = [2.0, -1.0, np.nan, 0.5, np.inf][: min(nb, 5)]   # clamp rules
+    rp, ci = _gpu_select(m, num, den)
+    rp_o, ci_o = O.select_blocks(m, num, den)
+    assert np.array_equal(rp, rp_o)
+    assert np.array_equal(ci, ci_o)
+
+
+@pytest.mark.parametrize("gh,gw,copies", [(3, 4, 2), (1, 5, 1), (7, 1, 3), (64, 64, 2)])
+def test_structured_mask_bitexact(gh, gw, copies):
+    grid, tile = (1, 8 * gh, 8 * gw), (1, 8, 8)
+    bsa = BlockSparseAttention(grid, tile, 1, copies, 128)
+    csr = bsa.structured()
+    rp, ci = csr_to_numpy(csr.row_ptr, csr.col_idx)
+    rp_o, ci_o = O.structured_mask(gh, gw, copies)
+    assert np.array_equal(rp, rp_o) and np.array_equal(ci, ci_o)
+
+
+# --------------------------------------------------------------------------- block masses
+
+MASS_CASES = [((4, 8, 8), 1, 64, 0.5), ((5, 6, 7), 2, 128, 1.0), ((9, 10, 13), 2, 64, 2.0),
+              ((8, 8, 8), 1, 128, 4.0), ((4, 12, 16), 2, 128, 3.0), ((6, 9, 14), 1, 128, 1.5)]
+
+
+@pytest.mark.parametrize("grid,H,D,amp", MASS_CASES)
+def test_block_mass_matches_oracle(grid, H, D, amp):
+    tile = (4, 4, 4)
+    q, k, _ = inputs(grid, 1, H, D, amp=amp, seed=7)
+    bsa = BlockSparseAttention(grid, tile, 1, H, D)
+    qt, kt = bsa.tile_rows(dev(q, torch.bfloat16)), bsa.tile_rows(dev(k, torch.bfloat16))
+    mass, lse = bsa.block_mass(qt, kt, want_lse=True)
+    mg = mass.cpu().numpy().astype(np.float64)
+    mo = O.block_mass(q, k, grid, tile, bsa.scale)
+    assert np.abs(mg.sum(-1) - 1).max() < 1e-5
+    big = mo >= 1e-6
+    rel = np.abs(mg - mo)[big] / mo[big]
+    assert rel.max() < 2e-5, rel.max()
+    assert np.abs(mg - mo).max() < 1e-6
+    # lse of every real query against a float64 library logsumexp
+    _, slot = O.token_blocks(grid, tile)
+    s = np.einsum("nhd,mhd->hnm", q[0].astype(np.float64), k[0].astype(np.float64)) * bsa.scale
+    want = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy()          # [H, N]
+    got = lse.cpu().numpy()[0][:, slot]
+    assert np.abs(got - want).max() < 2e-5
+
+
+# --------------------------------------------------------------------------- attention
+
+def _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=False):
+    bsa = BlockSparseAttention(grid, tile, 1, H, D)
+    vt = bsa.tile_vt(dev(v, torch.bfloat16))
+    csr = Csr(dev(rp, torch.int32), dev(ci if len(ci) else np.zeros(1, np.int32), torch.int32))
+    lse = torch.empty((1, H, bsa.npad), dtype=torch.float32, device="cuda")
+    if fp8:
+        qt, qs = bsa.tile_fp8(dev(q, torch.bfloat16))
+        kt, ks = bsa.tile_fp8(dev(k, torch.bfloat16))
+        ot = bsa.forward(qt, kt, vt, csr, q_scale=qs, k_scale=ks, lse=lse)
+    else:
+        qt, kt = bsa.tile_rows(dev(q, torch.bfloat16)), bsa.tile_rows(dev(k, torch.bfloat16))
+        ot = bsa.forward(qt, kt, vt, csr, lse=lse)
+    return bsa, ot, bsa.untile(ot, torch.float32).cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("grid,H,D", RAGGED)
+def test_all_blocks_forward_equals_dense_attention(grid, H, D):
+    tile = (4, 4, 4)
+    q, k, v = inputs(grid, 1, H, D, seed=8)
+    nb = O.num_blocks(grid, tile)
+    R = H * nb
+    rp = np.arange(0, R * nb + 1, nb, dtype=np.int32)
+    ci = np.tile(np.arange(nb, dtype=np.int32), R)
+    bsa, ot, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    dense = O.dense_attention(q, k, v, bsa.scale)
+    err = np.abs(o.astype(np.float64) - dense)
+    assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS, (err.max(), err.mean())
+    # padding rows of the tiled output are zero
+    _, slot = O.token_blocks(grid, tile)
+    pad = np.setdiff1d(np.arange(bsa.npad), slot)
+    assert np.all(ot.float().cpu().numpy()[:, :, pad, :] == 0)
+
+
+@pytest.mark.parametrize("grid,H,D", RAGGED)
+@pytest.mark.parametrize("num,den", [(1, 2), (99, 100)])
+def test_sparse_forward_matches_masked_oracle(grid, H, D, num, den):
+    tile = (4, 4, 4)
+    q, k, v = inputs(grid, 1, H, D, amp=1.5, seed=9)
+    nb = O.num_blocks(grid, tile)
+    m = synth.random_mass_rows(H * nb, nb, seed=nb + H, tie_frac=0.1, zero_frac=0.2)
+    m[0] = 0.0                                      # one query block with no kept key
+    rp, ci = O.select_blocks(m, num, den)
+    bsa, ot, o, lse = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci)
+    mx, mean = output_errors(o, out, tok)
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    # the empty row: zero output, lse = -inf
+    t0 = tok[0, 0, 0][tok[0, 0, 0] >= 0]
+    assert np.all(o[0, t0, 0, :] == 0)
+    _, slot = O.token_blocks(grid, tile)
+    assert np.all(np.isneginf(lse[0, 0, slot[t0]]))
+    # lse of the other rows against a float64 library logsumexp over allowed keys; the
+    # kernel's lse is that of the bf16-rounded probabilities that normalise O, which
+    # moves it by up to about 2^-9 relative in the sum
+    blk, _ = O.token_blocks(grid, tile)
+    rows = [r for r in range(1, H * nb, max(1, H * nb // 7)) if rp[r + 1] > rp[r]]
+    for r in rows:
+        h, qb = divmod(r, nb)
+        keys = np.where(np.isin(blk, ci[rp[r]:rp[r + 1]]))[0]
+        qs = np.where(blk == qb)[0]
+        s = q[0, qs, h].astype(np.float64) @ k[0, keys, h].astype(np.float64).T * bsa.scale
+        want = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy()
+        assert np.abs(lse[0, h, slot[qs]] - want).max() < 2e-3
+
+
+def test_forward_skips_out_of_range_blocks():
+    grid, tile, H, D = (5, 6, 7), (4, 4, 4), 1, 64
+    q, k, v = inputs(grid, 1, H, D, seed=10)
+    nb = O.num_blocks(grid, tile)
+    rp = np.array([0, 3, 4, 4, 6, 6, 6, 6, 7][: nb + 1], np.int32)
+    ci_bad = np.array([1, 99, 5, -1, 2, 7, nb], np.int32)
+    ci_ok = np.array([1, 5, 2, 7], np.int32)
+    rp_ok = np.array([0, 2, 2, 2, 4, 4, 4, 4, 4][: nb + 1], np.int32)
+    _, _, o_bad, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci_bad)
+    _, _, o_ok, _ = _run_forward(q, k, v, grid, tile, H, D, rp_ok, ci_ok)
+    assert np.array_equal(o_bad, o_ok)
+
+
+@pytest.mark.parametrize("grid,H,D", [((5, 6, 7), 2, 128), ((9, 10, 13), 1, 128), ((4, 8, 8), 2, 64)])
+def test_fp8_forward(grid, H, D):
+    """FP8 Q/K: parity with the oracle's simulation of the same per-tile e4m3
+    quantization, at the bf16 tolerances. Against unquantized attention the error is
+    the quantization's own, which the oracle measures by itself (simulated vs
+    unquantized); the GPU may exceed that by no more than the bf16 bound."""
+    tile = (4, 4, 4)
+    q, k, v = inputs(grid, 1, H, D, amp=1.0, seed=11)
+    nb = O.num_blocks(grid, tile)
+    m = synth.random_mass_rows(H * nb, nb, seed=5)
+    rp, ci = O.select_blocks(m, 9, 10)
+    bsa, _, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=True)
+    qh, _ = O.fp8_tile_quantize(q, grid, tile)
+    kh, _ = O.fp8_tile_quantize(k, grid, tile)
+    out_s, tok_s = O.masked_attention(qh, kh, v, grid, tile, bsa.scale, rp, ci)
+    mx_s, mean_s = output_errors(o, out_s, tok_s)
+    assert mx_s <= BF16_MAX_ABS and mean_s <= BF16_MEAN_ABS, (mx_s, mean_s)
+    out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci)
+    mx, _ = output_errors(o, out, tok)
+    quant = max(np.abs(a - b).max() for a, b in zip(out_s, out))
+    assert mx <= quant + BF16_MAX_ABS, (mx, quant)
+
+
+# --------------------------------------------------------------------------- end to end
+
+E2E = [("tiny", (4, 8, 8), 1, 64, 0.5, False), ("sharp-8", (8, 8, 8), 1, 128, 4.0, True),
+       ("sharp-12", (4, 12, 16), 2, 128, 3.0, True), ("ragged", (6, 9, 14), 2, 128, 1.0, True)]
+
+
+@pytest.mark.parametrize("name,grid,H,D,amp,bf16", E2E)
+def test_end_to_end(name, grid, H, D, amp, bf16):
+    tile = (4, 4, 4)
+    q, k, v = inputs(grid, 1, H, D, amp=amp, bf16=bf16, seed=0)
+    src_dt = torch.bfloat16 if bf16 else torch.float32
+    bsa = BlockSparseAttention(grid, tile, 1, H, D)
+    o, csr, mass = bsa.run(dev(q, src_dt), dev(k, src_dt), dev(v, src_dt), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    mo = O.block_mass(q, k, grid, tile, bsa.scale)
+    rp_o, ci_o = O.select_blocks(mo.astype(np.float32))
+    rp, ci = csr_to_numpy(csr.row_ptr, csr.col_idx)
+    mg = mass.cpu().numpy()
+    n_diff, n_bad = compare_selection(rp, ci, rp_o, ci_o, mo, mg)
+    assert n_bad == 0, f"{n_diff} rows differ, {n_bad} not certified fragile"
+    if n_diff == 0:
+        out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp_o, ci_o)
+        mx, mean = output_errors(o.cpu().numpy(), out, tok)
+        vs = value_scale(v)
+        assert mx <= BF16_MAX_ABS * vs and mean <= BF16_MEAN_ABS * vs, (mx, mean, vs)
+    if name.startswith("sharp"):
+        assert len(ci_o) < (H * bsa.nb) * bsa.nb          # the cut actually drops blocks
+
+
+def test_repeat_runs_are_bitwise_identical():
+    grid, tile, H, D = (6, 9, 14), (4, 4, 4), 2, 128
+    q, k, v = inputs(grid, 1, H, D, amp=2.0, seed=12)
+    bsa = BlockSparseAttention(grid, tile, 1, H, D)
+    a = bsa.run(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16))
+    b = bsa.run(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16))
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].row_ptr, b[1].row_ptr)
+    assert torch.equal(a[2], b[2])
