@@ -1,6 +1,6 @@
 """Benchmark of the whole block-sparse hot path on one MI355X.
 
-One step = tile Q, K (rows) and V (VT) -> dense block-mass pass -> 99 % retained-mass
+One step = tile Q, K (QK operand layout) and V (VT) -> dense block-mass pass -> 99 % retained-mass
 selection -> block-sparse forward over the kept blocks -> untile O, on the
 Wan2.1-1.3B-shaped 480p workload (grid 21x30x52, 12 heads, head size 128, bf16,
 synthetic seeded inputs already resident in HBM).
@@ -73,8 +73,8 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        bsa.tile_rows(qd, qt)
-        bsa.tile_rows(kd, kt)
+        bsa.tile_qk(qd, qt)
+        bsa.tile_qk(kd, kt)
         bsa.tile_vt(vd, vt)
         if ev is not None:
             ev[1].record(stream)

@@ -70,7 +70,8 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
     if (!make_geom(g, &geo) || !dims_ok(B, H)) return FPSA_ERR_INVALID_ARG;
     if (src == nullptr || dst == nullptr) return FPSA_ERR_INVALID_ARG;
     if (inverse != 0 && inverse != 1) return FPSA_ERR_INVALID_ARG;
-    if (dst_layout != FPSA_LAYOUT_ROWS && dst_layout != FPSA_LAYOUT_VT) return FPSA_ERR_INVALID_ARG;
+    if (dst_layout != FPSA_LAYOUT_ROWS && dst_layout != FPSA_LAYOUT_VT && dst_layout != FPSA_LAYOUT_QK)
+        return FPSA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
     const long N = (long)g->t * g->h * g->w;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -82,19 +83,19 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
         return hip_status();
     }
     if (src_dtype != FPSA_F32 && src_dtype != FPSA_BF16) return FPSA_ERR_UNSUPPORTED;
-    int mode;
+    int fp8;
     if (dst_dtype == FPSA_BF16) {
         if (dst_scale != nullptr) return FPSA_ERR_INVALID_ARG;
-        mode = dst_layout == FPSA_LAYOUT_VT ? 1 : 0;
+        fp8 = 0;
     } else if (dst_dtype == FPSA_FP8_E4M3) {
         if (dst_scale == nullptr) return FPSA_ERR_INVALID_ARG;
-        if (dst_layout != FPSA_LAYOUT_ROWS) return FPSA_ERR_UNSUPPORTED;
-        mode = 2;
+        if (dst_layout == FPSA_LAYOUT_VT) return FPSA_ERR_UNSUPPORTED;
+        fp8 = 1;
     } else {
         return FPSA_ERR_UNSUPPORTED;
     }
-    fpsa::launch_tile_forward(src, src_dtype == FPSA_F32 ? 0 : 1, dst, mode, dst_scale, geo, N, B, H,
-                              D, st);
+    fpsa::launch_tile_forward(src, src_dtype == FPSA_F32 ? 0 : 1, dst, fp8, dst_layout, dst_scale, geo,
+                              N, B, H, D, st);
     return hip_status();
 }
 

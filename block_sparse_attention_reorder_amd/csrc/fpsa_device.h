@@ -55,6 +55,32 @@ __device__ inline uint64_t block_valid_mask(const Geom& g, int blk) {
     return __ballot(g.valid(blk, lane));
 }
 
+// Fast per-block validity for kernels that visit many blocks: the in-tile position
+// of this lane's slot is decomposed once, and only blocks on a ragged edge of the
+// grid (last tile of an axis the tile does not divide) need a ballot.
+struct SlotMask {
+    int et, eh, ew;                 // in-tile coordinates of slot (lane)
+    bool rt, rh, rw;                // axis is ragged (grid not a multiple of the tile)
+    __device__ inline void init(const Geom& g, int lane) {
+        int plane = g.th * g.tw;
+        et = lane / plane;
+        eh = (lane - et * plane) / g.tw;
+        ew = lane - et * plane - eh * g.tw;
+        rt = g.T % g.tt != 0;
+        rh = g.Hg % g.th != 0;
+        rw = g.Wg % g.tw != 0;
+    }
+    // All-ones for an interior block; otherwise the ballot of the real slots.
+    __device__ inline uint64_t mask(const Geom& g, int blk) const {
+        int plane = g.nh * g.nw;
+        int bt = blk / plane, r = blk - bt * plane;
+        int bh = r / g.nw, bw = r - bh * g.nw;
+        bool edge = (rt && bt == g.nt - 1) || (rh && bh == g.nh - 1) || (rw && bw == g.nw - 1);
+        if (!edge) return ~0ull;
+        return __ballot(bt * g.tt + et < g.T && bh * g.th + eh < g.Hg && bw * g.tw + ew < g.Wg);
+    }
+};
+
 __device__ inline float wave_max32(float x) {  // combine the two 32-lane halves
     return fmaxf(x, __shfl_xor(x, 32));
 }

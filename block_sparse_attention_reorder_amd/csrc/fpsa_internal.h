@@ -10,7 +10,8 @@
 
 namespace fpsa {
 
-void launch_tile_forward(const void* src, int src_dt, void* dst, int mode, float* scale,
+// layout: 0 rows, 1 VT, 2 QK (fpsa_layout values)
+void launch_tile_forward(const void* src, int src_dt, void* dst, int fp8, int layout, float* scale,
                          const Geom& g, long N, int B, int H, int D, hipStream_t st);
 void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, long N, int B,
                          int H, int D, hipStream_t st);

@@ -24,17 +24,19 @@ __device__ inline long xcd_row_mass(long nwg) {
     return (i % 8) * (full / 8) + i / 8;
 }
 
+// Scores of one key block against this wave's 32 queries; K in the QK tiled layout
+// (each wave-wide operand load is one contiguous kilobyte).
 template <int D>
-__device__ inline void tile_scores(const __bf16* __restrict__ k, long krow0, int col, int half,
+__device__ inline void tile_scores(const __bf16* __restrict__ k, long krow0, int lane,
                                    const bf16x8* qop, f32x16* s) {
+    const __bf16* kp = k + krow0 * D + 8 * lane;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
-        const __bf16* kp = k + (krow0 + 32 * kt + col) * D;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * st + 8 * half);
+            bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + (kt * (D / 16) + st) * 512);
             s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], s[kt], 0, 0, 0);
         }
     }
@@ -55,18 +57,20 @@ __global__ __launch_bounds__(128) void k_block_mass(const __bf16* __restrict__ q
     const long npad = (long)g.nb * kBlock;
     const long qrow = bh * npad + (long)qb * kBlock + 32 * w + col;
     const bool qvalid = g.valid(qb, 32 * w + col);
+    SlotMask sm;
+    sm.init(g, lane);
 
     bf16x8 qop[D / 16];
-    const __bf16* qp = q + qrow * D;
+    const __bf16* qp = q + (bh * npad + (long)qb * kBlock) * D + 8 * lane;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * half);
+    for (int s = 0; s < D / 16; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(qp + (w * (D / 16) + s) * 512);
 
     // Pass 1: running max and sum of exp2 over all real keys.
     float m = -INFINITY, l = 0.0f;
     for (int kb = 0; kb < g.nb; ++kb) {
         f32x16 s[2];
-        tile_scores<D>(k, bh * npad + (long)kb * kBlock, col, half, qop, s);
-        const uint64_t vmask = block_valid_mask(g, kb);
+        tile_scores<D>(k, bh * npad + (long)kb * kBlock, lane, qop, s);
+        const uint64_t vmask = sm.mask(g, kb);
         const bool full = vmask == ~0ull;
         float mloc = -INFINITY;
 #pragma unroll
@@ -99,8 +103,8 @@ __global__ __launch_bounds__(128) void k_block_mass(const __bf16* __restrict__ q
     // Pass 2: probabilities against the final lse, summed per 64x64 tile.
     for (int kb = 0; kb < g.nb; ++kb) {
         f32x16 s[2];
-        tile_scores<D>(k, bh * npad + (long)kb * kBlock, col, half, qop, s);
-        const uint64_t vmask = block_valid_mask(g, kb);
+        tile_scores<D>(k, bh * npad + (long)kb * kBlock, lane, qop, s);
+        const uint64_t vmask = sm.mask(g, kb);
         const bool full = vmask == ~0ull;
         float ps = 0.0f;
 #pragma unroll

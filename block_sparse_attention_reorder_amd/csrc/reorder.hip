@@ -50,21 +50,52 @@ __device__ inline void load8<float>(const float* p, float* v) {
     for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
 }
 
-// MODE 0: bf16 tiled rows; MODE 1: bf16 tiled VT; MODE 2: e4m3 tiled rows + scale.
-template <typename SrcT, int D, int MODE>
+// Output layouts (see include/fpsa.h): rows, QK operand order, VT operand order.
+enum { kRows = 0, kVT = 1, kQK = 2 };
+
+// Where output chunk `oc` (16 bytes) of a block comes from: slot and first channel,
+// for a layout whose 16-byte chunks each hold consecutive channels of one slot.
+template <int D, int ESIZE, int LAYOUT>
+__device__ inline void chunk_source(int oc, int& e, int& d0) {
+    constexpr int kPer = 16 / ESIZE;                     // elements per chunk
+    if constexpr (LAYOUT == kRows) {
+        e = oc / (D / kPer);
+        d0 = (oc % (D / kPer)) * kPer;
+    } else if constexpr (ESIZE == 2) {                   // QK, bf16: units of 8 channels
+        int col = oc & 31, half = (oc >> 5) & 1, rest = oc >> 6;
+        int st = rest % (D / 16), kt = rest / (D / 16);
+        e = 32 * kt + col;
+        d0 = 16 * st + 8 * half;
+    } else {                                             // QK, e4m3: units of 32 channels, two chunks each
+        int part = oc & 1, u = oc >> 1;
+        int col = u & 31, half = (u >> 5) & 1, rest = u >> 6;
+        int st = rest % (D / 64), kt = rest / (D / 64);
+        e = 32 * kt + col;
+        d0 = 64 * st + 32 * half + 16 * part;
+    }
+}
+
+// One workgroup per (block, head, batch). Phase 1 reads the block's 64 token rows
+// in raster order (coalesced), converts (and for e4m3 computes the tile scale and
+// encodes) into an LDS tile; phase 2 writes the block in the requested layout as
+// contiguous 16-byte chunks.
+template <typename SrcT, int D, bool FP8, int LAYOUT>
 __global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ src,
                                                       void* __restrict__ dst,
                                                       float* __restrict__ scale_out, Geom g,
                                                       long N, int H) {
-    constexpr int kChunks = kBlock * D / 8;             // 8-element chunks per block
-    constexpr int kPerThread = kChunks / 256;
+    constexpr int kIn = kBlock * D / 8;                 // 8-element input chunks
+    constexpr int kInPerThread = kIn / 256;
+    constexpr int ESIZE = FP8 ? 1 : 2;
+    constexpr int kRowBytes = D * ESIZE + 16;           // padded LDS row
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * kRowBytes];
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const long bh = (long)b * H + h;
 
-    float v[kPerThread][8];
+    float v[kInPerThread][8];
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
+    for (int i = 0; i < kInPerThread; ++i) {
         int c = tid + 256 * i;
         int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
         long n = g.token(blk, e);
@@ -76,40 +107,10 @@ __global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ s
         }
     }
 
-    if constexpr (MODE == 0) {
-        __bf16* out = reinterpret_cast<__bf16*>(dst) + (bh * g.nb + blk) * (long)(kBlock * D);
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            int c = tid + 256 * i;
-            *reinterpret_cast<bf16x8*>(out + (long)c * 8) =
-                pack_bf16x8(v[i][0], v[i][1], v[i][2], v[i][3], v[i][4], v[i][5], v[i][6], v[i][7]);
-        }
-    } else if constexpr (MODE == 1) {
-        // Stage the block as bf16 [slot][d] in LDS, then emit [d][position] rows.
-        __shared__ __bf16 tile[kBlock][D + 8];
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            int c = tid + 256 * i;
-            int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
-            *reinterpret_cast<bf16x8*>(&tile[e][d0]) =
-                pack_bf16x8(v[i][0], v[i][1], v[i][2], v[i][3], v[i][4], v[i][5], v[i][6], v[i][7]);
-        }
-        __syncthreads();
-        __bf16* out = reinterpret_cast<__bf16*>(dst) + (bh * g.nb + blk) * (long)(kBlock * D);
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            int c = tid + 256 * i;                       // chunk of 8 positions of one d
-            int d = c / (kBlock / 8), p0 = (c % (kBlock / 8)) * 8;
-            bf16x8 r;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) r[j] = tile[vt_slot_of_position(p0 + j)][d];
-            *reinterpret_cast<bf16x8*>(out + (long)d * kBlock + p0) = r;
-        }
-    } else {
-        // FP8: scale = float32(amax / 448) over the whole 64 x D tile.
+    if constexpr (FP8) {
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i)
+        for (int i = 0; i < kInPerThread; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
 #pragma unroll
@@ -120,21 +121,53 @@ __global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ s
         amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
         const float s = amax > 0.0f ? amax / 448.0f : 1.0f;   // IEEE division
         if (tid == 0) scale_out[bh * g.nb + blk] = s;
-        uint8_t* out = reinterpret_cast<uint8_t*>(dst) + (bh * g.nb + blk) * (long)(kBlock * D);
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
+        for (int i = 0; i < kInPerThread; ++i) {
             int c = tid + 256 * i;
+            int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 lo |= encode_e4m3(v[i][j] / s) << (8 * j);
                 hi |= encode_e4m3(v[i][4 + j] / s) << (8 * j);
             }
-            i32x2 w;
-            w[0] = (int)lo;
-            w[1] = (int)hi;
-            *reinterpret_cast<i32x2*>(out + (long)c * 8) = w;
+            i32x2 w2;
+            w2[0] = (int)lo;
+            w2[1] = (int)hi;
+            *reinterpret_cast<i32x2*>(tile + e * kRowBytes + d0) = w2;
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kInPerThread; ++i) {
+            int c = tid + 256 * i;
+            int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
+            *reinterpret_cast<bf16x8*>(tile + e * kRowBytes + 2 * d0) =
+                pack_bf16x8(v[i][0], v[i][1], v[i][2], v[i][3], v[i][4], v[i][5], v[i][6], v[i][7]);
+        }
+    }
+    __syncthreads();
+
+    constexpr int kOut = kBlock * D * ESIZE / 16;       // 16-byte output chunks
+    uint8_t* out = reinterpret_cast<uint8_t*>(dst) + (bh * g.nb + blk) * (long)(kBlock * D * ESIZE);
+#pragma unroll
+    for (int i = 0; i < kOut / 256; ++i) {
+        int oc = tid + 256 * i;
+        i32x4 val;
+        if constexpr (LAYOUT == kVT) {
+            // chunk = 8 positions of one channel: ((t*4 + cc)*2 + half)*32 + col
+            int col = oc & 31, half = (oc >> 5) & 1, cc = (oc >> 6) & 3, t = oc >> 8;
+            int d = 32 * t + col, p0 = 16 * cc + 8 * half;
+            bf16x8 r;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                r[j] = *reinterpret_cast<const __bf16*>(tile + vt_slot_of_position(p0 + j) * kRowBytes + 2 * d);
+            val = *reinterpret_cast<i32x4*>(&r);
+        } else {
+            int e, d0;
+            chunk_source<D, ESIZE, LAYOUT>(oc, e, d0);
+            val = *reinterpret_cast<const i32x4*>(tile + e * kRowBytes + d0 * ESIZE);
+        }
+        *reinterpret_cast<i32x4*>(out + (long)oc * 16) = val;
     }
 }
 
@@ -167,27 +200,31 @@ __global__ __launch_bounds__(256) void k_tile_inverse(const __bf16* __restrict__
     }
 }
 
-template <int D>
-static void launch_forward(const void* src, int src_dt, void* dst, int mode, float* scale,
-                           const Geom& g, long N, int B, int H, hipStream_t st) {
+template <typename SrcT, int D>
+static void launch_forward_t(const SrcT* s, void* dst, bool fp8, int layout, float* scale,
+                             const Geom& g, long N, int B, int H, hipStream_t st) {
     dim3 grid(g.nb, H, B);
-    if (src_dt == 0) {
-        const float* s = static_cast<const float*>(src);
-        if (mode == 0) k_tile_forward<float, D, 0><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
-        else if (mode == 1) k_tile_forward<float, D, 1><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
-        else k_tile_forward<float, D, 2><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+    if (fp8) {
+        if (layout == kQK) k_tile_forward<SrcT, D, true, kQK><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        else k_tile_forward<SrcT, D, true, kRows><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
     } else {
-        const __bf16* s = static_cast<const __bf16*>(src);
-        if (mode == 0) k_tile_forward<__bf16, D, 0><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
-        else if (mode == 1) k_tile_forward<__bf16, D, 1><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
-        else k_tile_forward<__bf16, D, 2><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        if (layout == kQK) k_tile_forward<SrcT, D, false, kQK><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        else if (layout == kVT) k_tile_forward<SrcT, D, false, kVT><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        else k_tile_forward<SrcT, D, false, kRows><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
     }
 }
 
-void launch_tile_forward(const void* src, int src_dt, void* dst, int mode, float* scale,
+void launch_tile_forward(const void* src, int src_dt, void* dst, int fp8, int layout, float* scale,
                          const Geom& g, long N, int B, int H, int D, hipStream_t st) {
-    if (D == 128) launch_forward<128>(src, src_dt, dst, mode, scale, g, N, B, H, st);
-    else launch_forward<64>(src, src_dt, dst, mode, scale, g, N, B, H, st);
+    if (src_dt == 0) {
+        const float* s = static_cast<const float*>(src);
+        if (D == 128) launch_forward_t<float, 128>(s, dst, fp8, layout, scale, g, N, B, H, st);
+        else launch_forward_t<float, 64>(s, dst, fp8, layout, scale, g, N, B, H, st);
+    } else {
+        const __bf16* s = static_cast<const __bf16*>(src);
+        if (D == 128) launch_forward_t<__bf16, 128>(s, dst, fp8, layout, scale, g, N, B, H, st);
+        else launch_forward_t<__bf16, 64>(s, dst, fp8, layout, scale, g, N, B, H, st);
+    }
 }
 
 void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, long N, int B,

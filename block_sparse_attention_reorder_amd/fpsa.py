@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libfpsa.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3 = 0, 1, 2
-LAYOUT_ROWS, LAYOUT_VT = 0, 1
+LAYOUT_ROWS, LAYOUT_VT, LAYOUT_QK = 0, 1, 2
 MAX_SELECT_BLOCKS = 4096
 
 EXPORTED = [

@@ -1,6 +1,6 @@
 """The whole hot path on one GPU, as calls into libfpsa.
 
-    raster Q, K, V --tile--> tiled Q, K (rows) and V (VT)
+    raster Q, K, V --tile--> tiled Q, K (QK operand layout) and V (VT)
         --block_mass--> M[B, H, nb, nb] --select_blocks (99 %)--> frozen CSR
         --sparse_attn_fwd--> tiled O --tile (inverse)--> raster O
 
@@ -55,6 +55,13 @@ class BlockSparseAttention:
         fpsa.tile_reorder(x, out, self.grid, self.tile, self.B, self.H, self.D, stream=stream)
         return out
 
+    def tile_qk(self, x, out=None, stream=None):
+        """raster [B, N, H, D] (f32/bf16) -> tiled QK operand layout bf16 (for Q and K)."""
+        out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device) if out is None else out
+        fpsa.tile_reorder(x, out, self.grid, self.tile, self.B, self.H, self.D, layout=fpsa.LAYOUT_QK,
+                          stream=stream)
+        return out
+
     def tile_vt(self, x, out=None, stream=None):
         """raster [B, N, H, D] -> tiled VT bf16 (value operand layout)."""
         out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device) if out is None else out
@@ -62,11 +69,13 @@ class BlockSparseAttention:
                           stream=stream)
         return out
 
-    def tile_fp8(self, x, out=None, scale=None, stream=None):
-        """raster [B, N, H, D] -> tiled e4m3 bytes + per-tile float32 scales [B, H, nb]."""
+    def tile_fp8(self, x, out=None, scale=None, layout=fpsa.LAYOUT_QK, stream=None):
+        """raster [B, N, H, D] -> tiled e4m3 bytes (QK layout by default) + per-tile
+        float32 scales [B, H, nb]."""
         out = torch.empty(self.tiled_shape(), dtype=torch.uint8, device=self.device) if out is None else out
         scale = torch.empty((self.B, self.H, self.nb), dtype=torch.float32, device=self.device) if scale is None else scale
-        fpsa.tile_reorder(x, out, self.grid, self.tile, self.B, self.H, self.D, dst_scale=scale, stream=stream)
+        fpsa.tile_reorder(x, out, self.grid, self.tile, self.B, self.H, self.D, layout=layout, dst_scale=scale,
+                          stream=stream)
         return out, scale
 
     def untile(self, o_tiled, dtype=torch.bfloat16, out=None, stream=None):
@@ -115,7 +124,7 @@ class BlockSparseAttention:
 
     def run(self, q, k, v, thr_num=99, thr_den=100, out_dtype=torch.bfloat16):
         """Full path on raster Q, K, V: returns (raster O, CSR, masses)."""
-        qt, kt, vt = self.tile_rows(q), self.tile_rows(k), self.tile_vt(v)
+        qt, kt, vt = self.tile_qk(q), self.tile_qk(k), self.tile_vt(v)
         mass = self.block_mass(qt, kt)
         csr = self.select(mass, thr_num, thr_den)
         ot = self.forward(qt, kt, vt, csr)

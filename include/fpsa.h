@@ -37,12 +37,23 @@
  * tiled rows are zero, padding keys receive no attention and padding queries
  * produce zero output. Npad = 64 * nb.
  *
- * Tensor layouts (B = batch, H = heads, D = head size in {64, 128}):
+ * Tensor layouts (B = batch, H = heads, D = head size in {64, 128}). Every tiled
+ * layout holds one contiguous 64*D-element block per (b, h, blk), blocks in order;
+ * they differ only in how the 64 slots x D channels of a block are arranged:
  *   raster      [B, N, H, D]            N = T*Hg*Wg
- *   tiled rows  [B, H, Npad, D]         row 64*blk + slot
- *   tiled VT    [B, H, nb, D, 64]       per block, D-major; within each run of 16
- *                                       keys the order is slots 0-3, 8-11, 4-7, 12-15
- *                                       (the operand order of the P*V matrix product)
+ *   tiled rows  [B, H, Npad, D]         element (slot e, channel d) at e*D + d
+ *   tiled QK    (bf16) element (e, d) at
+ *                 ((((e/32)*(D/16) + d/16)*2 + (d/8)%2)*32 + e%32)*8 + d%8
+ *               (e4m3) element (e, d) at
+ *                 ((((e/32)*(D/64) + d/64)*2 + (d/32)%2)*32 + e%32)*32 + d%32
+ *               i.e. the order in which the 64 lanes of a wavefront hold a 32-row
+ *               operand of one 32x32 matrix-core step, so that each wave-wide load
+ *               reads one contiguous kilobyte; used for Q and K.
+ *   tiled VT    (bf16) with p the position of slot e inside its run of 16 slots
+ *               (slots 0-3, 8-11, 4-7, 12-15 of each run take positions 0-15) and
+ *               P = 16*(e/16) + p, element (e, d) at
+ *                 ((((d/32)*4 + P/16)*2 + (P/8)%2)*32 + d%32)*8 + P%8
+ *               i.e. the value operand of the P*V product in lane order; used for V.
  *   CSR         row_ptr[R + 1], col_idx[nnz] int32; R = B*H*nb rows, row
  *               (b*H + h)*nb + qb; each row's key blocks ascending.
  */
@@ -66,7 +77,7 @@ typedef enum {
 
 typedef enum { FPSA_F32 = 0, FPSA_BF16 = 1, FPSA_FP8_E4M3 = 2 } fpsa_dtype;
 
-typedef enum { FPSA_LAYOUT_ROWS = 0, FPSA_LAYOUT_VT = 1 } fpsa_layout;
+typedef enum { FPSA_LAYOUT_ROWS = 0, FPSA_LAYOUT_VT = 1, FPSA_LAYOUT_QK = 2 } fpsa_layout;
 
 typedef struct {
     int32_t t, h, w;                 /* token grid (t = 1 for an image) */
@@ -94,13 +105,12 @@ size_t fpsa_select_workspace_bytes(int64_t R, int32_t nb);
  * granularity of [FPSAttention ..., Abstract]).
  *
  * Forward (inverse = 0): src raster [B, N, H, D] of src_dtype (F32 or BF16) ->
- *   dst tiled of dst_dtype:
- *     BF16, layout ROWS: tiled rows, values rounded to nearest even;
- *     BF16, layout VT:   tiled VT (the value operand of fpsa_sparse_attn_fwd);
- *     FP8_E4M3, layout ROWS: tiled rows of OCP e4m3fn bytes plus dst_scale
- *       [B, H, nb] float32: per (b, h, block) the scale is float32(amax / 448) over
- *       the block's 64 x D values (1 when amax = 0) and each byte is the
- *       nearest-even e4m3fn encoding of float32(x / scale), saturated to +-448.
+ *   dst tiled of dst_dtype in dst_layout:
+ *     BF16 in ROWS, QK or VT: values rounded to nearest even;
+ *     FP8_E4M3 in ROWS or QK: OCP e4m3fn bytes plus dst_scale [B, H, nb] float32:
+ *       per (b, h, block) the scale is float32(amax / 448) over the block's 64 x D
+ *       values (1 when amax = 0) and each byte is the nearest-even e4m3fn encoding
+ *       of float32(x / scale), saturated to +-448.
  *   Padding slots are written as zero.
  * Inverse (inverse = 1): src tiled rows BF16 -> dst raster of dst_dtype (F32 or
  *   BF16); only real tokens are written; layout must be ROWS, dst_scale NULL.
@@ -114,7 +124,7 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
  * Exact dense block attention mass (the one dense measurement step of [LoSA ...,
  * Abstract]).
  *
- * q_tiled, k_tiled: tiled rows BF16. For each (b, h) and query block qb,
+ * q_tiled, k_tiled: tiled QK layout, BF16. For each (b, h) and query block qb,
  *   mass[b, h, qb, kb] = (1 / c(qb)) * sum over real queries i of qb and real keys j
  *   of kb of softmax_j(softmax_scale * q_i . k_j), the softmax running over all real
  *   keys and c(qb) the number of real queries in qb. Each row sums to 1.
@@ -162,9 +172,9 @@ int32_t fpsa_structured_mask(const fpsa_grid* g, int32_t copies, int32_t* row_pt
 /*
  * Block-sparse attention forward with an online softmax over the kept blocks.
  *
- * q, k: tiled rows, BF16 when qk_dtype = FPSA_BF16, or FP8_E4M3 bytes with
- *   q_scale / k_scale [B, H, nb] float32 (as produced by fpsa_tile_reorder) when
- *   qk_dtype = FPSA_FP8_E4M3; scales must be NULL for BF16.
+ * q, k: tiled QK layout, BF16 when qk_dtype = FPSA_BF16, or FP8_E4M3 bytes with
+ *   q_scale / k_scale [B, H, nb] float32, positive (as produced by
+ *   fpsa_tile_reorder) when qk_dtype = FPSA_FP8_E4M3; scales must be NULL for BF16.
  * v: tiled VT, BF16.
  * row_ptr / col_idx: CSR with R = B*H*nb rows; key-block indices outside [0, nb)
  *   are skipped.

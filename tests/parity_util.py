@@ -45,11 +45,36 @@ def expected_tiled_rows(x, grid, tile):
 
 
 def rows_to_vt(rows, nb):
-    """tiled rows [B, H, Npad, D] -> VT [B, H, nb, D, 64] following the header's order."""
+    """tiled rows [B, H, Npad, D] -> VT layout, flat per block, following the header:
+    element (e, d) at ((((d/32)*4 + P/16)*2 + (P/8)%2)*32 + d%32)*8 + P%8, where P is
+    the position of slot e (runs of 16 ordered slots 0-3, 8-11, 4-7, 12-15)."""
     B, H, _, D = rows.shape
     blocks = rows.reshape(B, H, nb, 64, D)
-    order = np.array([16 * (p // 16) + VT_RUN_ORDER[p % 16] for p in range(64)])
-    return np.ascontiguousarray(np.transpose(blocks[:, :, :, order, :], (0, 1, 2, 4, 3)))
+    out = np.zeros((B, H, nb, 64 * D), rows.dtype)
+    pos_of_slot = np.zeros(64, np.int64)
+    for P in range(64):
+        pos_of_slot[16 * (P // 16) + VT_RUN_ORDER[P % 16]] = P
+    e = np.arange(64)[:, None]
+    d = np.arange(D)[None, :]
+    P = pos_of_slot[e]
+    off = ((((d // 32) * 4 + P // 16) * 2 + (P // 8) % 2) * 32 + d % 32) * 8 + P % 8
+    out[:, :, :, off.ravel()] = blocks.reshape(B, H, nb, 64 * D)
+    return out
+
+
+def rows_to_qk(rows, nb, esize=2):
+    """tiled rows [B, H, Npad, D] -> QK layout, flat per block, following the header."""
+    B, H, _, D = rows.shape
+    blocks = rows.reshape(B, H, nb, 64, D)
+    out = np.zeros((B, H, nb, 64 * D), rows.dtype)
+    e = np.arange(64)[:, None]
+    d = np.arange(D)[None, :]
+    if esize == 2:
+        off = ((((e // 32) * (D // 16) + d // 16) * 2 + (d // 8) % 2) * 32 + e % 32) * 8 + d % 8
+    else:
+        off = ((((e // 32) * (D // 64) + d // 64) * 2 + (d // 32) % 2) * 32 + e % 32) * 32 + d % 32
+    out[:, :, :, off.ravel()] = blocks.reshape(B, H, nb, 64 * D)
+    return out
 
 
 def csr_to_numpy(row_ptr, col_idx):

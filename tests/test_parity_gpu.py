@@ -12,7 +12,8 @@ from block_sparse_attention_reorder_amd import fpsa, synth
 from block_sparse_attention_reorder_amd.pipeline import BlockSparseAttention, Csr
 
 from parity_util import (BF16_MAX_ABS, BF16_MEAN_ABS, compare_selection, csr_to_numpy, dev,
-                         expected_tiled_rows, inputs, output_errors, rows_to_vt, value_scale)
+                         expected_tiled_rows, inputs, output_errors, rows_to_qk, rows_to_vt,
+                         value_scale)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +49,18 @@ def test_tile_vt_bitexact(grid, H, D):
 
 @pytest.mark.parametrize("grid,H,D", RAGGED)
 @pytest.mark.parametrize("src_dtype", [torch.bfloat16, torch.float32])
+def test_tile_qk_bitexact(grid, H, D, src_dtype):
+    tile = (4, 4, 4)
+    x = inputs(grid, 2, H, D, bf16=(src_dtype == torch.bfloat16), seed=14)[0]
+    bsa = BlockSparseAttention(grid, tile, 2, H, D)
+    got = bsa.tile_qk(dev(x, src_dtype)).view(torch.int16).cpu().numpy()
+    rows = torch.from_numpy(expected_tiled_rows(x, grid, tile)).to(torch.bfloat16).view(torch.int16).numpy()
+    want = rows_to_qk(rows, bsa.nb, esize=2)
+    assert np.array_equal(got.reshape(want.shape), want)
+
+
+@pytest.mark.parametrize("grid,H,D", RAGGED)
+@pytest.mark.parametrize("src_dtype", [torch.bfloat16, torch.float32])
 def test_tile_fp8_bitexact(grid, H, D, src_dtype):
     tile = (4, 4, 4)
     x = inputs(grid, 1, H, D, amp=2.0, bf16=(src_dtype == torch.bfloat16), seed=5)[0]
@@ -57,13 +70,17 @@ def test_tile_fp8_bitexact(grid, H, D, src_dtype):
     if src_dtype == torch.bfloat16:
         x = synth.to_bf16_values(x)           # both sides see the same bf16 values
     bsa = BlockSparseAttention(grid, tile, 1, H, D)
-    codes, scales = bsa.tile_fp8(dev(x, src_dtype))
     want_codes, want_scales = O.fp8_tile_codes(x, grid, tile)
     _, slot = O.token_blocks(grid, tile)
     tiled = np.zeros((1, H, bsa.npad, D), np.uint8)
     tiled[:, :, slot, :] = np.transpose(want_codes, (0, 2, 1, 3))
+    codes, scales = bsa.tile_fp8(dev(x, src_dtype), layout=fpsa.LAYOUT_ROWS)
     assert np.array_equal(scales.cpu().numpy(), want_scales)
     assert np.array_equal(codes.cpu().numpy(), tiled)
+    codes, scales = bsa.tile_fp8(dev(x, src_dtype), layout=fpsa.LAYOUT_QK)
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
+    want = rows_to_qk(tiled, bsa.nb, esize=1)
+    assert np.array_equal(codes.cpu().numpy().reshape(want.shape), want)
 
 
 def test_tile_fp8_all_zero_tile_has_unit_scale():
@@ -137,7 +154,7 @@ def test_block_mass_matches_oracle(grid, H, D, amp):
     tile = (4, 4, 4)
     q, k, _ = inputs(grid, 1, H, D, amp=amp, seed=7)
     bsa = BlockSparseAttention(grid, tile, 1, H, D)
-    qt, kt = bsa.tile_rows(dev(q, torch.bfloat16)), bsa.tile_rows(dev(k, torch.bfloat16))
+    qt, kt = bsa.tile_qk(dev(q, torch.bfloat16)), bsa.tile_qk(dev(k, torch.bfloat16))
     mass, lse = bsa.block_mass(qt, kt, want_lse=True)
     mg = mass.cpu().numpy().astype(np.float64)
     mo = O.block_mass(q, k, grid, tile, bsa.scale)
@@ -166,7 +183,7 @@ def _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=False):
         kt, ks = bsa.tile_fp8(dev(k, torch.bfloat16))
         ot = bsa.forward(qt, kt, vt, csr, q_scale=qs, k_scale=ks, lse=lse)
     else:
-        qt, kt = bsa.tile_rows(dev(q, torch.bfloat16)), bsa.tile_rows(dev(k, torch.bfloat16))
+        qt, kt = bsa.tile_qk(dev(q, torch.bfloat16)), bsa.tile_qk(dev(k, torch.bfloat16))
         ot = bsa.forward(qt, kt, vt, csr, lse=lse)
     return bsa, ot, bsa.untile(ot, torch.float32).cpu().numpy(), lse.cpu().numpy()
 
