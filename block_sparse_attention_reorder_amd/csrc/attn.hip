@@ -4,20 +4,25 @@
 // indices of the retained-mass selection [LoSA: Near-Lossless Sparse Attention for
 // Training-Free Video Diffusion Acceleration, Abstract].
 //
-// gfx950 mapping. A workgroup owns one query block (64 rows) of one (batch, head);
-// each of its two waves owns 32 query rows and walks the block's CSR list. Scores
-// are formed transposed, S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16 (or
+// gfx950 mapping. A workgroup of four waves owns one query block (64 rows) of one
+// (batch, head) and walks the block's CSR list. Wave w takes query rows
+// 32*(w & 1) .. +31 and key rows 32*(w >> 1) .. +31 of every kept block, so each
+// wave holds a 32-query x 32-key score tile, a 32 x D output accumulator and the
+// matching K and V halves: small enough for two waves per SIMD, which lets one
+// wave's softmax overlap the other's matrix products. The two key halves of a
+// query row carry separate online-softmax states that are merged once at the end
+// through LDS.
+//
+// Scores are formed transposed, S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16 (or
 // v_mfma_f32_32x32x64_f8f6f4 on e4m3 Q/K): in the 32x32 accumulator a lane holds
 // one query column, so the softmax row reductions are in-lane plus one swap of the
 // two 32-lane halves, and the output O^T = V^T * P^T keeps one query per lane too,
-// making the rescale a per-lane scalar. The accumulator of S already sits in the
-// B-operand order of the P*V product once V is stored in the VT layout, so P never
-// leaves registers. Q and K come in the QK tiled layout and V in the VT layout,
-// both stored in lane order, so every operand load is one contiguous kilobyte per
-// wave straight from HBM/L2 into registers; no LDS is used. K of the next kept block is
-// loaded while the current block is computed (two register buffers).
-// Workgroups are remapped so that each XCD gets a contiguous range of rows (same
-// heads), which keeps the shared K/V tiles in that XCD's L2.
+// making the rescale a per-lane scalar. The S accumulator already sits in the
+// B-operand order of the P*V product, so P never leaves registers. Q and K come in
+// the QK tiled layout and V in the VT layout, both stored in lane order, so each
+// operand load is one contiguous kilobyte per wave straight from HBM/L2 into
+// registers. Workgroups are remapped so that each XCD gets a contiguous range of
+// rows (same heads), which keeps the shared K/V tiles in that XCD's L2.
 //
 // Softmax details: scores stay raw until the exponent, exp2(s * c - m) with c the
 // scale times log2(e) (times the two FP8 tile scales), so one FMA per element;
@@ -40,212 +45,207 @@ __device__ inline long xcd_row(long nwg) {
 }
 
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr int kAttnThreads = 256;
 
+// K operand of one 32-key half: bf16 (D/16 steps of 8 values) or e4m3 (D/64 steps
+// of 32 bytes) per lane.
 template <int D, bool FP8>
-struct KOperand {
-    // per key-tile (2) and d-step: bf16x8 (bf16) or i32x8 (e4m3)
-    bf16x8 b[FP8 ? 1 : 2][D / 16];
-    i32x8 f[FP8 ? 2 : 1][FP8 ? D / 64 : 1];
+struct KHalf {
+    bf16x8 b[FP8 ? 1 : D / 16];
+    i32x8 f[FP8 ? D / 64 : 1];
 };
 
-// Operand loads from the QK / VT tiled layouts: for every (tile, step) the 64 lanes
-// read one contiguous kilobyte (bf16) or two (e4m3), lane l at offset 16*l or 32*l.
+// Operand loads from the QK / VT tiled layouts: each (tile, step) is one contiguous
+// kilobyte (bf16) or two (e4m3) across the wave, lane l at 16*l or 32*l bytes.
 template <int D, bool FP8>
-__device__ inline void load_k(KOperand<D, FP8>& k, const void* kv, long krow0, int lane) {
+__device__ inline void load_khalf(KHalf<D, FP8>& k, const void* base, long row0, int kt, int lane) {
+    if constexpr (FP8) {
+        const uint8_t* p = static_cast<const uint8_t*>(base) + row0 * D + 32 * lane;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-        if constexpr (FP8) {
-            const uint8_t* p = static_cast<const uint8_t*>(kv) + krow0 * D + 32 * lane;
+        for (int st = 0; st < D / 64; ++st)
+            k.f[st] = *reinterpret_cast<const i32x8*>(p + (kt * (D / 64) + st) * 2048);
+    } else {
+        const __bf16* p = static_cast<const __bf16*>(base) + row0 * D + 8 * lane;
 #pragma unroll
-            for (int st = 0; st < D / 64; ++st)
-                k.f[kt][st] = *reinterpret_cast<const i32x8*>(p + (kt * (D / 64) + st) * 2048);
-        } else {
-            const __bf16* p = static_cast<const __bf16*>(kv) + krow0 * D + 8 * lane;
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st)
-                k.b[kt][st] = *reinterpret_cast<const bf16x8*>(p + (kt * (D / 16) + st) * 512);
-        }
+        for (int st = 0; st < D / 16; ++st)
+            k.b[st] = *reinterpret_cast<const bf16x8*>(p + (kt * (D / 16) + st) * 512);
     }
 }
 
+// V^T operand for the two 16-key chunks of key half kh: v[t][c] covers channels
+// 32t..32t+31 and operand positions 16*(2*kh + c) .. +15 of the block.
 template <int D>
-__device__ inline void load_v(bf16x8 (&v)[D / 32][4], const __bf16* vb, int lane) {
+__device__ inline void load_vhalf(bf16x8 (&v)[D / 32][2], const __bf16* vb, int kh, int lane) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-            v[t][cc] = *reinterpret_cast<const bf16x8*>(vb + (t * 4 + cc) * 512 + 8 * lane);
+        for (int c = 0; c < 2; ++c)
+            v[t][c] = *reinterpret_cast<const bf16x8*>(vb + (t * 4 + 2 * kh + c) * 512 + 8 * lane);
 }
 
 template <int D, bool FP8>
-struct AttnState {
-    f32x16 acc[D / 32];
-    float m, l;
-};
+__global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
+    const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long R,
+    float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse) {
+    constexpr int kDT = D / 32;
+    __shared__ float xch[2][kDT * 16 + 2][64];      // key-half 1 -> key-half 0 merge
 
-template <int D, bool FP8>
-__device__ inline void attend_block(AttnState<D, FP8>& st, const KOperand<D, FP8>& k,
-                                    const bf16x8 (&v)[D / 32][4], const bf16x8* qop,
-                                    const i32x8* qop8, float c, uint64_t vmask, int half) {
-    f32x16 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
-        if constexpr (FP8) {
-#pragma unroll
-            for (int j = 0; j < D / 64; ++j)
-                s[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k.f[kt][j], qop8[j], s[kt], 0, 0, 0, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int j = 0; j < D / 16; ++j)
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.b[kt][j], qop[j], s[kt], 0, 0, 0);
-        }
-    }
-    if (vmask != ~0ull) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                int key = 32 * kt + 8 * (i >> 2) + 4 * half + (i & 3);
-                if (!((vmask >> key) & 1ull)) s[kt][i] = -INFINITY;
-            }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-    const float mloc = wave_max32(mx) * c;          // c > 0
-    const bool grow = mloc > st.m + kRescaleSlack;
-    if (__ballot(grow)) {
-        const float mnew = grow ? mloc : st.m;
-        const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);   // 0 when m = -inf
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st.acc[t][i] *= alpha;
-        st.l *= alpha;
-        st.m = mnew;
-    }
-    const float mref = st.m == -INFINITY ? 0.0f : st.m;
-    bf16x8 pb[4];
-    float rs = 0.0f;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-        const int kt = cc >> 1, b0 = 8 * (cc & 1);
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            bf16x2 pr;
-            pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][b0 + j], c, -mref));
-            pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][b0 + j + 1], c, -mref));
-            pb[cc][j] = pr[0];
-            pb[cc][j + 1] = pr[1];
-            rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
-        }
-    }
-    st.l += wave_add32(rs);
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-            st.acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[t][cc], pb[cc], st.acc[t], 0, 0, 0);
-}
-
-template <int D, bool FP8>
-__global__ __launch_bounds__(128) void k_sparse_attn(const void* __restrict__ qv,
-                                                     const void* __restrict__ kv,
-                                                     const __bf16* __restrict__ vt,
-                                                     const float* __restrict__ q_scale,
-                                                     const float* __restrict__ k_scale,
-                                                     const int32_t* __restrict__ row_ptr,
-                                                     const int32_t* __restrict__ col_idx, Geom g,
-                                                     long R, float scale_log2, __bf16* __restrict__ o,
-                                                     float* __restrict__ lse) {
     const long r = xcd_row(R);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int qh = w & 1, kh = w >> 1;
     const int col = lane & 31, half = lane >> 5;
     const long bh = r / g.nb;
     const int qb = (int)(r - bh * g.nb);
     const long npad = (long)g.nb * kBlock;
-    const long qrow = bh * npad + (long)qb * kBlock + 32 * w + col;   // this lane's query row
+    const long qblk0 = bh * npad + (long)qb * kBlock;
     SlotMask sm;
     sm.init(g, lane);
 
-    // Q operand (B of S^T = K * Q^T): lane holds 8 (bf16) or 32 (e4m3) d-values.
-    bf16x8 qop[FP8 ? 1 : D / 16];
-    i32x8 qop8[FP8 ? D / 64 : 1];
-    const long qblk0 = bh * npad + (long)qb * kBlock;                  // first row of the block
-    if constexpr (FP8) {
-        const uint8_t* q8 = static_cast<const uint8_t*>(qv) + qblk0 * D + 32 * lane;
-#pragma unroll
-        for (int s = 0; s < D / 64; ++s) qop8[s] = *reinterpret_cast<const i32x8*>(q8 + (w * (D / 64) + s) * 2048);
-    } else {
-        const __bf16* q = static_cast<const __bf16*>(qv) + qblk0 * D + 8 * lane;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) qop[s] = *reinterpret_cast<const bf16x8*>(q + (w * (D / 16) + s) * 512);
-    }
+    // Q operand (B of S^T = K * Q^T) for query rows 32*qh .. +31.
+    KHalf<D, FP8> q;
+    load_khalf<D, FP8>(q, qv, qblk0, qh, lane);
     const float cq = FP8 ? scale_log2 * q_scale[r] : scale_log2;
 
-    AttnState<D, FP8> st;
+    f32x16 acc[kDT];
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
+    for (int t = 0; t < kDT; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st.acc[t][i] = 0.0f;
-    st.m = -INFINITY;
-    st.l = 0.0f;
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+    float m = -INFINITY, l = 0.0f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
     const __bf16* vbase = vt + bh * (long)g.nb * (kBlock * D);
     const long kbase = bh * npad;
-    auto clamp_kb = [&](int e) {
-        int kb = col_idx[e];
+    // The CSR list is read 64 entries at a time into one VGPR (lane j holds entry
+    // base + j) and single entries are picked with v_readlane, so no iteration
+    // waits on a scalar load.
+    int batch_base = e0;
+    int batch = e0 + lane < e1 ? col_idx[e0 + lane] : -1;
+    auto block_at = [&](int e) {
+        if (e >= e1) return -1;
+        if (e - batch_base >= 64) {
+            batch_base += 64;
+            batch = batch_base + lane < e1 ? col_idx[batch_base + lane] : -1;
+        }
+        int kb = __builtin_amdgcn_readlane(batch, e - batch_base);
         return (kb < 0 || kb >= g.nb) ? -1 : kb;
     };
 
-    // K of the next kept block is prefetched one block ahead (two register buffers);
-    // V of the current block is issued before its scores are formed, so its latency
-    // hides behind the QK^T product and the softmax.
-    KOperand<D, FP8> ka, kb2;
-    bf16x8 vv[D / 32][4];
-    int kbA = e0 < e1 ? clamp_kb(e0) : -1;
-    load_k<D, FP8>(ka, kv, kbase + (long)(kbA < 0 ? 0 : kbA) * kBlock, lane);
-    for (int e = e0; e < e1; e += 2) {
-        int kbB = e + 1 < e1 ? clamp_kb(e + 1) : -1;
-        load_v<D>(vv, vbase + (long)(kbA < 0 ? 0 : kbA) * (kBlock * D), lane);
-        load_k<D, FP8>(kb2, kv, kbase + (long)(kbB < 0 ? 0 : kbB) * kBlock, lane);
-        if (kbA >= 0) {
-            const float c = FP8 ? cq * k_scale[bh * g.nb + kbA] : cq;
-            attend_block<D, FP8>(st, ka, vv, qop, qop8, c, sm.mask(g, kbA), half);
+    KHalf<D, FP8> k;
+    bf16x8 v[kDT][2];
+    int kb = block_at(e0);
+    load_khalf<D, FP8>(k, kv, kbase + (long)(kb < 0 ? 0 : kb) * kBlock, kh, lane);
+    for (int e = e0; e < e1; ++e) {
+        const int kbn = block_at(e + 1);
+        load_vhalf<D>(v, vbase + (long)(kb < 0 ? 0 : kb) * (kBlock * D), kh, lane);
+        f32x16 s;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+        if constexpr (FP8) {
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j)
+                s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k.f[j], q.f[j], s, 0, 0, 0, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.b[j], q.b[j], s, 0, 0, 0);
         }
-        if (e + 1 >= e1) break;
-        kbA = e + 2 < e1 ? clamp_kb(e + 2) : -1;
-        load_v<D>(vv, vbase + (long)(kbB < 0 ? 0 : kbB) * (kBlock * D), lane);
-        load_k<D, FP8>(ka, kv, kbase + (long)(kbA < 0 ? 0 : kbA) * kBlock, lane);
-        if (kbB >= 0) {
-            const float c = FP8 ? cq * k_scale[bh * g.nb + kbB] : cq;
-            attend_block<D, FP8>(st, kb2, vv, qop, qop8, c, sm.mask(g, kbB), half);
+        // K of the next kept block streams in while this block's softmax and P*V run
+        load_khalf<D, FP8>(k, kv, kbase + (long)(kbn < 0 ? 0 : kbn) * kBlock, kh, lane);
+        if (kb >= 0) {
+            const float c = FP8 ? cq * k_scale[bh * g.nb + kb] : cq;
+            const uint64_t vmask = sm.mask(g, kb);
+            if (vmask != ~0ull) {
+                // bit 8*(i/4) + i%4 of m32 tells whether element i's key is real
+                const uint32_t m32 = (uint32_t)(vmask >> (32 * kh + 4 * half));
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (!(m32 & (1u << (8 * (i >> 2) + (i & 3))))) s[i] = -INFINITY;
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+            const float mloc = wave_max32(mx) * c;          // c > 0
+            const bool grow = mloc > m + kRescaleSlack;
+            if (__ballot(grow)) {
+                const float mnew = grow ? mloc : m;
+                const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // 0 when m = -inf
+#pragma unroll
+                for (int t = 0; t < kDT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+                l *= alpha;
+                m = mnew;
+            }
+            const float mref = m == -INFINITY ? 0.0f : m;
+            bf16x8 pb[2];
+            float rs = 0.0f;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    bf16x2 pr;
+                    pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * cc + j], c, -mref));
+                    pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * cc + j + 1], c, -mref));
+                    pb[cc][j] = pr[0];
+                    pb[cc][j + 1] = pr[1];
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+                }
+            l += wave_add32(rs);
+#pragma unroll
+            for (int t = 0; t < kDT; ++t)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc)
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[t][cc], pb[cc], acc[t], 0, 0, 0);
         }
+        kb = kbn;
     }
 
-    const bool qvalid = g.valid(qb, 32 * w + col);
-    const float inv = (qvalid && st.l > 0.0f) ? 1.0f / st.l : 0.0f;
-    __bf16* orow = o + qrow * D;
+    // Merge the two key halves of each query row: wave (qh, 1) hands its state to
+    // wave (qh, 0), which rescales both to the larger reference and finishes.
+    if (kh == 1) {
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xch[qh][t * 16 + i][lane] = acc[t][i];
+        xch[qh][kDT * 16][lane] = m;
+        xch[qh][kDT * 16 + 1][lane] = l;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    {
+        const float m1 = xch[qh][kDT * 16][lane], l1 = xch[qh][kDT * 16 + 1][lane];
+        const float mm = fmaxf(m, m1);
+        const float mref = mm == -INFINITY ? 0.0f : mm;
+        const float a0 = __builtin_amdgcn_exp2f(m - mref), a1 = __builtin_amdgcn_exp2f(m1 - mref);
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[t][i] = acc[t][i] * a0 + xch[qh][t * 16 + i][lane] * a1;
+        l = l * a0 + l1 * a1;
+        m = mm;
+    }
+
+    const int qslot = 32 * qh + col;
+    const bool qvalid = g.valid(qb, qslot);
+    const float inv = (qvalid && l > 0.0f) ? 1.0f / l : 0.0f;
+    __bf16* orow = o + (qblk0 + qslot) * D;
     typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
+    for (int t = 0; t < kDT; ++t)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             bf16x4 v4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(st.acc[t][4 * g4 + j] * inv);
+            for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(acc[t][4 * g4 + j] * inv);
             *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g4 + 4 * half) = v4;
         }
     if (lse != nullptr && half == 0) {
         float val = 0.0f;
-        if (qvalid) val = st.l > 0.0f ? (st.m + __builtin_amdgcn_logf(st.l)) * kLn2 : -INFINITY;
-        lse[qrow] = val;
+        if (qvalid) val = l > 0.0f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+        lse[qblk0 + qslot] = val;
     }
 }
 
@@ -257,7 +257,7 @@ void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, co
     const float sl2 = scale * kLog2e;
     const __bf16* vt = static_cast<const __bf16*>(v);
     __bf16* out = static_cast<__bf16*>(o);
-    dim3 grid((unsigned)R), block(128);
+    dim3 grid((unsigned)R), block(kAttnThreads);
     if (D == 128) {
         if (fp8) k_sparse_attn<128, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse);
         else k_sparse_attn<128, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse);

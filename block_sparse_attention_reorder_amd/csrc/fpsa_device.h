@@ -81,10 +81,19 @@ struct SlotMask {
     }
 };
 
-__device__ inline float wave_max32(float x) {  // combine the two 32-lane halves
-    return fmaxf(x, __shfl_xor(x, 32));
+// Combine lane l with lane l ^ 32 (the two 32-lane halves of the wave) with one
+// v_permlane32_swap: with both operands holding x, the two results hold x of this
+// lane and of its partner half.
+__device__ inline float wave_max32(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ inline float wave_add32(float x) { return x + __shfl_xor(x, 32); }
+__device__ inline float wave_add32(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline float wave_sum(float x) {
 #pragma unroll

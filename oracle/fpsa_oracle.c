@@ -339,14 +339,21 @@ double orc_e4m3_decode(uint8_t code) {
  * mantissa LSB is zero), found by comparing against every finite magnitude; values
  * beyond 448 therefore saturate to 448. NaN maps to the NaN code.
  */
+static double e4m3_magnitude[0x7F];             /* decode of codes 0x00 .. 0x7E */
+static int e4m3_table_ready = 0;
+
 uint8_t orc_e4m3_encode(double x) {
+    if (!e4m3_table_ready) {
+        for (int c = 0; c < 0x7F; ++c) e4m3_magnitude[c] = orc_e4m3_decode((uint8_t)c);
+        e4m3_table_ready = 1;
+    }
     if (isnan(x)) return 0x7F;
     uint8_t sign = signbit(x) ? 0x80 : 0x00;
     double a = fabs(x);
     int best = 0;
     double best_err = INFINITY;
     for (int c = 0; c < 0x7F; ++c) {            /* 0x00 .. 0x7E: all finite magnitudes */
-        double err = fabs(orc_e4m3_decode((uint8_t)c) - a);
+        double err = fabs(e4m3_magnitude[c] - a);
         if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
             best = c;
             best_err = err;
