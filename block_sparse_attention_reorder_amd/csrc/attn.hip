@@ -161,8 +161,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
                 // bit 8*(i/4) + i%4 of m32 tells whether element i's key is real
                 const uint32_t m32 = (uint32_t)(vmask >> (32 * kh + 4 * half));
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (!(m32 & (1u << (8 * (i >> 2) + (i & 3))))) s[i] = -INFINITY;
+                for (int i = 0; i < 16; ++i) s[i] += mask_bias(m32, 8 * (i >> 2) + (i & 3));
             }
             float mx = s[0];
 #pragma unroll

@@ -84,6 +84,13 @@ struct SlotMask {
 // Combine lane l with lane l ^ 32 (the two 32-lane halves of the wave) with one
 // v_permlane32_swap: with both operands holding x, the two results hold x of this
 // lane and of its partner half.
+// 0.0f when bit `pos` of m is set, -inf otherwise (an additive score mask that
+// needs no compare/select).
+__device__ inline float mask_bias(uint32_t m, int pos) {
+    const uint32_t off = ((m >> pos) & 1u) ^ 1u;        // 1 for a padding key
+    return __uint_as_float((0u - off) & 0xFF800000u);
+}
+
 __device__ inline float wave_max32(float x) {
     const unsigned u = __float_as_uint(x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);

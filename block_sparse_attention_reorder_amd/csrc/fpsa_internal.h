@@ -16,8 +16,12 @@ void launch_tile_forward(const void* src, int src_dt, void* dst, int fp8, int la
 void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, long N, int B,
                          int H, int D, hipStream_t st);
 
+// Workspace of the mass pass: nb * 64 floats per query-block row in flight; rows
+// are processed in launches of as many rows as the workspace holds.
+size_t mass_workspace_bytes_per_row(int nb);
 void launch_block_mass(const void* q, const void* k, int B, int H, int D, const Geom& g,
-                       float scale, float* mass, float* lse, hipStream_t st);
+                       float scale, float* mass, float* lse, void* ws, size_t ws_bytes,
+                       hipStream_t st);
 
 // Workspace layout for selection: per row a kept count (int32) and the cut key
 // (uint64) with the number of tied keys kept (int32).

@@ -22,6 +22,7 @@ MAX_SELECT_BLOCKS = 4096
 
 EXPORTED = [
     "fpsa_num_blocks", "fpsa_status_string", "fpsa_version", "fpsa_select_workspace_bytes",
+    "fpsa_mass_workspace_bytes",
     "fpsa_tile_reorder", "fpsa_block_mass", "fpsa_select_blocks", "fpsa_structured_mask",
     "fpsa_sparse_attn_fwd",
 ]
@@ -66,7 +67,9 @@ def lib() -> ctypes.CDLL:
         L.fpsa_tile_reorder.restype = i32
         L.fpsa_tile_reorder.argtypes = [vp, i32, vp, i32, i32, vp, i32, i32, i32, gp, i32, vp]
         L.fpsa_block_mass.restype = i32
-        L.fpsa_block_mass.argtypes = [vp, vp, i32, i32, i32, gp, f32, vp, vp, vp]
+        L.fpsa_block_mass.argtypes = [vp, vp, i32, i32, i32, gp, f32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.fpsa_mass_workspace_bytes.restype = ctypes.c_size_t
+        L.fpsa_mass_workspace_bytes.argtypes = [i32, i32, gp]
         L.fpsa_select_blocks.restype = i32
         L.fpsa_select_blocks.argtypes = [vp, i64, i32, u32, u32, vp, vp, i64, vp, ctypes.c_size_t, vp]
         L.fpsa_structured_mask.restype = i32
@@ -117,6 +120,11 @@ def select_workspace_bytes(R: int, nb: int) -> int:
     return int(lib().fpsa_select_workspace_bytes(int(R), int(nb)))
 
 
+def mass_workspace_bytes(B: int, H: int, grid, tile) -> int:
+    g = Grid.of(grid, tile)
+    return int(lib().fpsa_mass_workspace_bytes(int(B), int(H), ctypes.byref(g)))
+
+
 def version() -> int:
     return int(lib().fpsa_version())
 
@@ -133,14 +141,16 @@ def tile_reorder(src, dst, grid, tile, B, H, D, *, inverse=False, layout=LAYOUT_
     _check(s, "fpsa_tile_reorder")
 
 
-def block_mass(q_tiled, k_tiled, grid, tile, B, H, D, softmax_scale, mass, lse=None, stream=None) -> None:
+def block_mass(q_tiled, k_tiled, grid, tile, B, H, D, softmax_scale, mass, workspace, lse=None,
+               stream=None) -> None:
     if q_tiled.dtype != torch.bfloat16 or k_tiled.dtype != torch.bfloat16:
         raise ValueError("block_mass takes bf16 tiled Q and K")
     if mass.dtype != torch.float32 or (lse is not None and lse.dtype != torch.float32):
         raise ValueError("mass and lse are float32")
     g = Grid.of(grid, tile)
     s = lib().fpsa_block_mass(_ptr(q_tiled), _ptr(k_tiled), int(B), int(H), int(D), ctypes.byref(g),
-                              float(softmax_scale), _ptr(mass), _ptr(lse), _stream(stream))
+                              float(softmax_scale), _ptr(mass), _ptr(lse), _ptr(workspace),
+                              int(workspace.numel() * workspace.element_size()), _stream(stream))
     _check(s, "fpsa_block_mass")
 
 

@@ -85,11 +85,21 @@ class BlockSparseAttention:
         return out
 
     # ------------------------------------------------------------------ selection
-    def block_mass(self, qt, kt, mass=None, lse=None, want_lse=False, stream=None):
+    def mass_workspace(self, max_bytes=None):
+        """Scratch for the mass pass: enough for one launch, or at most max_bytes
+        (then the pass runs in several launches)."""
+        n = fpsa.mass_workspace_bytes(self.B, self.H, self.grid, self.tile)
+        if max_bytes is not None:
+            n = min(n, int(max_bytes))
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def block_mass(self, qt, kt, mass=None, lse=None, want_lse=False, workspace=None, stream=None):
         mass = torch.empty((self.B, self.H, self.nb, self.nb), dtype=torch.float32, device=self.device) if mass is None else mass
         if want_lse and lse is None:
             lse = torch.empty((self.B, self.H, self.npad), dtype=torch.float32, device=self.device)
-        fpsa.block_mass(qt, kt, self.grid, self.tile, self.B, self.H, self.D, self.scale, mass, lse, stream=stream)
+        ws = self.mass_workspace() if workspace is None else workspace
+        fpsa.block_mass(qt, kt, self.grid, self.tile, self.B, self.H, self.D, self.scale, mass, ws, lse,
+                        stream=stream)
         return (mass, lse) if want_lse else mass
 
     def new_csr(self, capacity=None) -> Csr:

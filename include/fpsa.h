@@ -130,11 +130,20 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
  *   keys and c(qb) the number of real queries in qb. Each row sums to 1.
  * mass: [B, H, nb, nb] float32. lse: [B, H, Npad] float32 natural-log log-sum-exp of
  *   each real query's scaled scores (padding rows get 0), or NULL.
- * nb must not exceed FPSA_MAX_SELECT_BLOCKS.
+ * workspace: device scratch of workspace_bytes, at least nb*64*4 bytes (one query
+ *   block); fpsa_mass_workspace_bytes gives the size that lets one launch cover all
+ *   B*H*nb query blocks. With less, the call issues several launches, each covering
+ *   as many query blocks as fit. Contents on return are unspecified.
+ * nb must not exceed FPSA_MAX_SELECT_BLOCKS; FPSA_ERR_CAPACITY if the workspace
+ *   holds less than one query block.
  */
 int32_t fpsa_block_mass(const void* q_tiled, const void* k_tiled, int32_t B, int32_t H, int32_t D,
                         const fpsa_grid* g, float softmax_scale, float* mass, float* lse,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for fpsa_block_mass to run in one launch (B*H*nb*nb*64*4);
+   0 for an invalid grid. Host-only. */
+size_t fpsa_mass_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g);
 
 /*
  * Retained-mass block selection ([LoSA ..., Abstract]: per head and query block,

@@ -97,13 +97,21 @@ def test_tile_reorder_validation(L):
 
 def test_block_mass_validation(L):
     f = L.fpsa_block_mass
-    assert f(None, FAKE, 1, 1, 64, grid(), 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.125, None, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.0, FAKE, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, 1, 1, 64, grid(), float("nan"), FAKE, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, 1, 1, 32, grid(), 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
+    ws = 4 * 64 * 4                                    # one query block of a 4-block grid
+    assert f(None, FAKE, 1, 1, 64, grid(), 0.125, FAKE, None, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.125, None, None, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.125, FAKE, None, None, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.0, FAKE, None, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, grid(), float("nan"), FAKE, None, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 32, grid(), 0.125, FAKE, None, FAKE, ws, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.125, FAKE, None, FAKE, ws - 1, None) == fpsa.ERR_CAPACITY
     # 4097 blocks: beyond the selection limit
-    assert f(FAKE, FAKE, 1, 1, 64, grid(1, 8, 4097 * 8, 1, 8, 8), 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 1, 1, 64, grid(1, 8, 4097 * 8, 1, 8, 8), 0.125, FAKE, None, FAKE, 1 << 30, None) == fpsa.ERR_UNSUPPORTED
+
+
+def test_mass_workspace_bytes(L):
+    assert fpsa.mass_workspace_bytes(1, 12, (21, 30, 52), (4, 4, 4)) == 12 * 624 * 624 * 64 * 4
+    assert fpsa.mass_workspace_bytes(1, 1, (4, 8, 8), (4, 4, 2)) == 0
 
 
 def test_select_blocks_validation(L):

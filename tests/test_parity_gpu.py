@@ -168,7 +168,12 @@ def test_block_mass_matches_oracle(grid, H, D, amp):
     s = np.einsum("nhd,mhd->hnm", q[0].astype(np.float64), k[0].astype(np.float64)) * bsa.scale
     want = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy()          # [H, N]
     got = lse.cpu().numpy()[0][:, slot]
-    assert np.abs(got - want).max() < 2e-5
+    # float32 carries lse ~ 100 to about 8e-6: allow a few units in the last place
+    assert np.all(np.abs(got - want) <= 4e-7 * np.abs(want) + 2e-6)
+    # a workspace of three query blocks runs the pass in several launches; every
+    # row is computed the same way, so the result is bit-identical
+    mass3 = bsa.block_mass(qt, kt, workspace=bsa.mass_workspace(max_bytes=3 * bsa.nb * 64 * 4))
+    assert torch.equal(mass3, mass)
 
 
 # --------------------------------------------------------------------------- attention
