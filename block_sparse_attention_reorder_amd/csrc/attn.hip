@@ -5,13 +5,16 @@
 // Training-Free Video Diffusion Acceleration, Abstract].
 //
 // gfx950 mapping. A workgroup of four waves owns one query block (64 rows) of one
-// (batch, head) and walks the block's CSR list. Wave w takes query rows
-// 32*(w & 1) .. +31 and key rows 32*(w >> 1) .. +31 of every kept block, so each
-// wave holds a 32-query x 32-key score tile, a 32 x D output accumulator and the
-// matching K and V halves: small enough for two waves per SIMD, which lets one
-// wave's softmax overlap the other's matrix products. The two key halves of a
-// query row carry separate online-softmax states that are merged once at the end
-// through LDS.
+// (batch, head) and walks the block's CSR list. The K and V tiles of each kept
+// block (32 KB in bf16) are copied once per workgroup into LDS with direct
+// global-to-LDS loads (global_load_lds_dwordx4, each wave moving eight contiguous
+// kilobytes), double-buffered so that the copy of the next kept block overlaps the
+// current one; one barrier per block. Wave w takes query rows 32*(w & 1) .. +31 and
+// key rows 32*(w >> 1) .. +31 of every block, so each wave holds a 32-query x 32-key
+// score tile, a 32 x D output accumulator and the matching K and V halves read from
+// LDS: small enough for two waves per SIMD, which lets one wave's softmax overlap
+// the other's matrix products. The two key halves of a query row carry separate
+// online-softmax states that are merged once at the end through LDS.
 //
 // Scores are formed transposed, S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16 (or
 // v_mfma_f32_32x32x64_f8f6f4 on e4m3 Q/K): in the 32x32 accumulator a lane holds
@@ -19,10 +22,11 @@
 // two 32-lane halves, and the output O^T = V^T * P^T keeps one query per lane too,
 // making the rescale a per-lane scalar. The S accumulator already sits in the
 // B-operand order of the P*V product, so P never leaves registers. Q and K come in
-// the QK tiled layout and V in the VT layout, both stored in lane order, so each
-// operand load is one contiguous kilobyte per wave straight from HBM/L2 into
-// registers. Workgroups are remapped so that each XCD gets a contiguous range of
-// rows (same heads), which keeps the shared K/V tiles in that XCD's L2.
+// the QK tiled layout and V in the VT layout, both stored in lane order, so every
+// copy is a contiguous kilobyte and every LDS operand read is a conflict-free
+// 16-byte-per-lane ds_read_b128. Workgroups are remapped so that each XCD gets a
+// contiguous range of rows (same heads), which keeps the shared K/V tiles in that
+// XCD's L2.
 //
 // Softmax details: scores stay raw until the exponent, exp2(s * c - m) with c the
 // scale times log2(e) (times the two FP8 tile scales), so one FMA per element;
@@ -83,6 +87,29 @@ __device__ inline void load_vhalf(bf16x8 (&v)[D / 32][2], const __bf16* vb, int 
             v[t][c] = *reinterpret_cast<const bf16x8*>(vb + (t * 4 + 2 * kh + c) * 512 + 8 * lane);
 }
 
+// LDS operand reads: the same lane-order kilobytes the global layouts hold.
+template <int D, bool FP8>
+__device__ inline void lds_khalf(KHalf<D, FP8>& k, const uint8_t* st, int kh, int lane) {
+    if constexpr (FP8) {
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j)
+            k.f[j] = *reinterpret_cast<const i32x8*>(st + (kh * (D / 64) + j) * 2048 + 32 * lane);
+    } else {
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+            k.b[j] = *reinterpret_cast<const bf16x8*>(st + (kh * (D / 16) + j) * 1024 + 16 * lane);
+    }
+}
+
+template <int D>
+__device__ inline void lds_vhalf(bf16x8 (&v)[D / 32][2], const uint8_t* st, int kh, int lane) {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            v[t][c] = *reinterpret_cast<const bf16x8*>(st + (t * 4 + 2 * kh + c) * 1024 + 16 * lane);
+}
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
@@ -90,7 +117,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long R,
     float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse) {
     constexpr int kDT = D / 32;
-    __shared__ float xch[2][kDT * 16 + 2][64];      // key-half 1 -> key-half 0 merge
+    constexpr int kKBytes = kBlock * D * (FP8 ? 1 : 2);   // K tile of one block
+    constexpr int kVBytes = kBlock * D * 2;               // V tile of one block
+    constexpr int kStage = kKBytes + kVBytes;
+    constexpr int kChunksPerWave = kStage / 1024 / 4;
+    static_assert(kStage % 4096 == 0, "a stage splits into whole kilobytes per wave");
+    static_assert(2 * (kDT * 16 + 2) * 64 * 4 <= 2 * kStage, "merge buffer fits in the stages");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
 
     const long r = xcd_row(R);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -117,8 +150,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
-    const __bf16* vbase = vt + bh * (long)g.nb * (kBlock * D);
-    const long kbase = bh * npad;
+    const uint8_t* kbytes = static_cast<const uint8_t*>(kv) + bh * npad * D * (FP8 ? 1 : 2);
+    const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(vt) + bh * (long)g.nb * kVBytes;
     // The CSR list is read 64 entries at a time into one VGPR (lane j holds entry
     // base + j) and single entries are picked with v_readlane, so no iteration
     // waits on a scalar load.
@@ -133,28 +166,46 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
         int kb = __builtin_amdgcn_readlane(batch, e - batch_base);
         return (kb < 0 || kb >= g.nb) ? -1 : kb;
     };
+    // Copy block kb's K and V tiles into stage `st`: this wave moves kilobytes
+    // kChunksPerWave*w .. +kChunksPerWave-1 of the stage, lane l carrying 16 bytes.
+    auto copy_block = [&](int kb, int st) {
+        const int b = kb < 0 ? 0 : kb;
+#pragma unroll
+        for (int j = 0; j < kChunksPerWave; ++j) {
+            const int c = kChunksPerWave * w + j;
+            const uint8_t* src = c * 1024 < kKBytes ? kbytes + (long)b * kKBytes + c * 1024
+                                                    : vbytes + (long)b * kVBytes + (c * 1024 - kKBytes);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(src + 16 * lane),
+                (__attribute__((address_space(3))) void*)(lds + st * kStage + c * 1024), 16, 0, 0);
+        }
+    };
 
+    int kb = block_at(e0);
+    if (e0 < e1) copy_block(kb, 0);
     KHalf<D, FP8> k;
     bf16x8 v[kDT][2];
-    int kb = block_at(e0);
-    load_khalf<D, FP8>(k, kv, kbase + (long)(kb < 0 ? 0 : kb) * kBlock, kh, lane);
     for (int e = e0; e < e1; ++e) {
+        const int stage = (e - e0) & 1;
         const int kbn = block_at(e + 1);
-        load_vhalf<D>(v, vbase + (long)(kb < 0 ? 0 : kb) * (kBlock * D), kh, lane);
-        f32x16 s;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.0f;
-        if constexpr (FP8) {
-#pragma unroll
-            for (int j = 0; j < D / 64; ++j)
-                s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k.f[j], q.f[j], s, 0, 0, 0, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int j = 0; j < D / 16; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.b[j], q.b[j], s, 0, 0, 0);
-        }
-        // K of the next kept block streams in while this block's softmax and P*V run
-        load_khalf<D, FP8>(k, kv, kbase + (long)(kbn < 0 ? 0 : kbn) * kBlock, kh, lane);
+        // this block's copy has landed for every wave, and every wave is done with
+        // the other stage (read in the previous iteration)
+        __syncthreads();
+        lds_khalf<D, FP8>(k, lds + stage * kStage, kh, lane);
+        lds_vhalf<D>(v, lds + stage * kStage + kKBytes, kh, lane);
+        if (e + 1 < e1) copy_block(kbn, stage ^ 1);
         if (kb >= 0) {
+            f32x16 s;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+            if constexpr (FP8) {
+#pragma unroll
+                for (int j = 0; j < D / 64; ++j)
+                    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k.f[j], q.f[j], s, 0, 0, 0, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int j = 0; j < D / 16; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.b[j], q.b[j], s, 0, 0, 0);
+            }
             const float c = FP8 ? cq * k_scale[bh * g.nb + kb] : cq;
             const uint64_t vmask = sm.mask(g, kb);
             if (vmask != ~0ull) {
@@ -203,26 +254,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     }
 
     // Merge the two key halves of each query row: wave (qh, 1) hands its state to
-    // wave (qh, 0), which rescales both to the larger reference and finishes.
+    // wave (qh, 0) through the (now idle) stage memory; wave (qh, 0) rescales both
+    // to the larger reference and finishes.
+    __syncthreads();
+    float* xch = reinterpret_cast<float*>(lds) + qh * (kDT * 16 + 2) * 64;
     if (kh == 1) {
 #pragma unroll
         for (int t = 0; t < kDT; ++t)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) xch[qh][t * 16 + i][lane] = acc[t][i];
-        xch[qh][kDT * 16][lane] = m;
-        xch[qh][kDT * 16 + 1][lane] = l;
+            for (int i = 0; i < 16; ++i) xch[(t * 16 + i) * 64 + lane] = acc[t][i];
+        xch[(kDT * 16) * 64 + lane] = m;
+        xch[(kDT * 16 + 1) * 64 + lane] = l;
     }
     __syncthreads();
     if (kh == 1) return;
     {
-        const float m1 = xch[qh][kDT * 16][lane], l1 = xch[qh][kDT * 16 + 1][lane];
+        const float m1 = xch[(kDT * 16) * 64 + lane], l1 = xch[(kDT * 16 + 1) * 64 + lane];
         const float mm = fmaxf(m, m1);
         const float mref = mm == -INFINITY ? 0.0f : mm;
         const float a0 = __builtin_amdgcn_exp2f(m - mref), a1 = __builtin_amdgcn_exp2f(m1 - mref);
 #pragma unroll
         for (int t = 0; t < kDT; ++t)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[t][i] = acc[t][i] * a0 + xch[qh][t * 16 + i][lane] * a1;
+            for (int i = 0; i < 16; ++i) acc[t][i] = acc[t][i] * a0 + xch[(t * 16 + i) * 64 + lane] * a1;
         l = l * a0 + l1 * a1;
         m = mm;
     }
