@@ -7,9 +7,9 @@
 // gfx950 mapping. A workgroup of four waves owns one query block (64 rows) of one
 // (batch, head) and walks the block's CSR list. The K and V tiles of each kept
 // block (32 KB in bf16) are copied once per workgroup into LDS with direct
-// global-to-LDS loads (global_load_lds_dwordx4, each wave moving eight contiguous
-// kilobytes), double-buffered so that the copy of the next kept block overlaps the
-// current one; one barrier per block. Wave w takes query rows 32*(w & 1) .. +31 and
+// global-to-LDS loads (global_load_lds_dwordx4, each wave moving a quarter of each
+// tile in contiguous kilobytes) into two-slot K and V rings, K two blocks and V one
+// block ahead of use, so the copies overlap the computation; one barrier per block. Wave w takes query rows 32*(w & 1) .. +31 and
 // key rows 32*(w >> 1) .. +31 of every block, so each wave holds a 32-query x 32-key
 // score tile, a 32 x D output accumulator and the matching K and V halves read from
 // LDS: small enough for two waves per SIMD, which lets one wave's softmax overlap
@@ -119,11 +119,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     constexpr int kDT = D / 32;
     constexpr int kKBytes = kBlock * D * (FP8 ? 1 : 2);   // K tile of one block
     constexpr int kVBytes = kBlock * D * 2;               // V tile of one block
-    constexpr int kStage = kKBytes + kVBytes;
-    constexpr int kChunksPerWave = kStage / 1024 / 4;
-    static_assert(kStage % 4096 == 0, "a stage splits into whole kilobytes per wave");
-    static_assert(2 * (kDT * 16 + 2) * 64 * 4 <= 2 * kStage, "merge buffer fits in the stages");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+    constexpr int kKChunks = kKBytes / 1024 / 4;          // kilobytes per wave per copy
+    constexpr int kVChunks = kVBytes / 1024 / 4;
+    static_assert(kKBytes % 4096 == 0 && kVBytes % 4096 == 0, "copies split into whole kilobytes");
+    static_assert(2 * (kDT * 16 + 2) * 64 * 4 <= 2 * (kKBytes + kVBytes), "merge buffer fits");
+    // LDS: K ring [K0 | K1] then V ring [V0 | V1]
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kKBytes + kVBytes)];
+    uint8_t* const kring = lds;
+    uint8_t* const vring = lds + 2 * kKBytes;
 
     const long r = xcd_row(R);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -166,57 +169,93 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
         int kb = __builtin_amdgcn_readlane(batch, e - batch_base);
         return (kb < 0 || kb >= g.nb) ? -1 : kb;
     };
-    // Copy block kb's K and V tiles into stage `st`: this wave moves kilobytes
-    // kChunksPerWave*w .. +kChunksPerWave-1 of the stage, lane l carrying 16 bytes.
-    auto copy_block = [&](int kb, int st) {
-        const int b = kb < 0 ? 0 : kb;
+    // Copy the K (or V) tile of block kb into ring slot `slot`: this wave moves
+    // its share of contiguous kilobytes, lane l carrying 16 bytes each.
+    auto copy_k = [&](int kb, int slot) {
+        const uint8_t* src = kbytes + (long)(kb < 0 ? 0 : kb) * kKBytes;
 #pragma unroll
-        for (int j = 0; j < kChunksPerWave; ++j) {
-            const int c = kChunksPerWave * w + j;
-            const uint8_t* src = c * 1024 < kKBytes ? kbytes + (long)b * kKBytes + c * 1024
-                                                    : vbytes + (long)b * kVBytes + (c * 1024 - kKBytes);
+        for (int j = 0; j < kKChunks; ++j) {
+            const int c = kKChunks * w + j;
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(src + 16 * lane),
-                (__attribute__((address_space(3))) void*)(lds + st * kStage + c * 1024), 16, 0, 0);
+                (const __attribute__((address_space(1))) void*)(src + c * 1024 + 16 * lane),
+                (__attribute__((address_space(3))) void*)(kring + slot * kKBytes + c * 1024), 16, 0, 0);
+        }
+    };
+    auto copy_v = [&](int kb, int slot) {
+        const uint8_t* src = vbytes + (long)(kb < 0 ? 0 : kb) * kVBytes;
+#pragma unroll
+        for (int j = 0; j < kVChunks; ++j) {
+            const int c = kVChunks * w + j;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(src + c * 1024 + 16 * lane),
+                (__attribute__((address_space(3))) void*)(vring + slot * kVBytes + c * 1024), 16, 0, 0);
         }
     };
 
-    int kb = block_at(e0);
-    if (e0 < e1) copy_block(kb, 0);
+    // Software pipeline across kept blocks. Iteration j holds the scores of block j
+    // (issued one iteration earlier); after the barrier it reads K of block j+1 and
+    // V of block j from LDS, starts the copies of K(j+2) (over K(j)) and V(j+1)
+    // (over V(j-1)), both read by every wave before this barrier, issues the QK^T
+    // products of block j+1, and only then runs the softmax and P*V of block j, so
+    // the matrix pipe works on block j+1 while the vector ALUs work on block j.
+    const int n = e1 - e0;
     KHalf<D, FP8> k;
     bf16x8 v[kDT][2];
-    for (int e = e0; e < e1; ++e) {
-        const int stage = (e - e0) & 1;
-        const int kbn = block_at(e + 1);
-        // this block's copy has landed for every wave, and every wave is done with
-        // the other stage (read in the previous iteration)
+    f32x16 s, sn;
+    int kb = -1, kbn = -1;
+    auto scores = [&](f32x16& out) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) out[i] = 0.0f;
+        if constexpr (FP8) {
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j)
+                out = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k.f[j], q.f[j], out, 0, 0, 0, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.b[j], q.b[j], out, 0, 0, 0);
+        }
+    };
+    if (n > 0) {
+        kb = block_at(e0);
+        copy_k(kb, 0);
+        copy_v(kb, 0);
+        if (n > 1) {
+            kbn = block_at(e0 + 1);
+            copy_k(kbn, 1);
+        }
+        __syncthreads();                              // K(0), V(0), K(1) landed
+        lds_khalf<D, FP8>(k, kring, kh, lane);
+        scores(s);
+    }
+    for (int j = 0; j < n; ++j) {
+        const int kb2 = block_at(e0 + j + 2);
+        // K(j+1) and V(j) landed; every wave is done with iteration j-1's reads
         __syncthreads();
-        lds_khalf<D, FP8>(k, lds + stage * kStage, kh, lane);
-        lds_vhalf<D>(v, lds + stage * kStage + kKBytes, kh, lane);
-        if (e + 1 < e1) copy_block(kbn, stage ^ 1);
-        if (kb >= 0) {
-            f32x16 s;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = 0.0f;
-            if constexpr (FP8) {
-#pragma unroll
-                for (int j = 0; j < D / 64; ++j)
-                    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k.f[j], q.f[j], s, 0, 0, 0, 0, 0, 0);
-            } else {
-#pragma unroll
-                for (int j = 0; j < D / 16; ++j) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.b[j], q.b[j], s, 0, 0, 0);
-            }
-            const float c = FP8 ? cq * k_scale[bh * g.nb + kb] : cq;
-            const uint64_t vmask = sm.mask(g, kb);
+        lds_vhalf<D>(v, vring + (j & 1) * kVBytes, kh, lane);
+        if (j + 1 < n) {
+            lds_khalf<D, FP8>(k, kring + ((j + 1) & 1) * kKBytes, kh, lane);
+            copy_v(kbn, (j + 1) & 1);
+            if (j + 2 < n) copy_k(kb2, j & 1);
+            scores(sn);
+        }
+        {
+            // An entry outside [0, nb) is processed as a block with no real key: all
+            // its scores are masked, so it adds nothing. Every iteration takes the
+            // same path, and the scores are always read an iteration after their
+            // products were issued.
+            const float c = FP8 ? cq * k_scale[bh * g.nb + (kb < 0 ? 0 : kb)] : cq;
+            const uint64_t vmask = kb >= 0 ? sm.mask(g, kb) : 0ull;
             if (vmask != ~0ull) {
                 // bit 8*(i/4) + i%4 of m32 tells whether element i's key is real
                 const uint32_t m32 = (uint32_t)(vmask >> (32 * kh + 4 * half));
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[i] += mask_bias(m32, 8 * (i >> 2) + (i & 3));
             }
-            float mx = s[0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+            float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+            float mx2 = fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]));
+            float mx3 = fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11]));
+            float mx4 = fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]));
+            mx = fmaxf(fmaxf(mx, mx2), fmaxf(mx3, mx4));
             const float mloc = wave_max32(mx) * c;          // c > 0
             const bool grow = mloc > m + kRescaleSlack;
             if (__ballot(grow)) {
@@ -231,26 +270,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
             }
             const float mref = m == -INFINITY ? 0.0f : m;
             bf16x8 pb[2];
-            float rs = 0.0f;
+            float rs0 = 0.0f, rs1 = 0.0f;
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-                for (int j = 0; j < 8; j += 2) {
+                for (int jj = 0; jj < 8; jj += 2) {
                     bf16x2 pr;
-                    pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * cc + j], c, -mref));
-                    pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * cc + j + 1], c, -mref));
-                    pb[cc][j] = pr[0];
-                    pb[cc][j + 1] = pr[1];
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+                    pr[0] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * cc + jj], c, -mref));
+                    pr[1] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * cc + jj + 1], c, -mref));
+                    pb[cc][jj] = pr[0];
+                    pb[cc][jj + 1] = pr[1];
+                    if (cc == 0) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs0, false);
+                    else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs1, false);
                 }
-            l += wave_add32(rs);
+            l += wave_add32(rs0 + rs1);
 #pragma unroll
             for (int t = 0; t < kDT; ++t)
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc)
                     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[t][cc], pb[cc], acc[t], 0, 0, 0);
         }
+        s = sn;
         kb = kbn;
+        kbn = kb2;
     }
 
     // Merge the two key halves of each query row: wave (qh, 1) hands its state to

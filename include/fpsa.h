@@ -186,7 +186,7 @@ int32_t fpsa_structured_mask(const fpsa_grid* g, int32_t copies, int32_t* row_pt
  *   fpsa_tile_reorder) when qk_dtype = FPSA_FP8_E4M3; scales must be NULL for BF16.
  * v: tiled VT, BF16.
  * row_ptr / col_idx: CSR with R = B*H*nb rows; key-block indices outside [0, nb)
- *   are skipped.
+ *   contribute nothing (they are treated as blocks without real keys).
  * For each real query i of block qb of row r: o_i = sum_j p_ij v_j over the real
  *   keys j of the kept blocks, p the softmax of softmax_scale * q_i . k_j over
  *   exactly those keys (FP8: the scores use the decoded values, q8 * k8 * q_scale *
