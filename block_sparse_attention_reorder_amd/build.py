@@ -25,9 +25,16 @@ FLAGS = [
 ]
 
 
+# The attention and mass kernels never see NaN scores (padding is -inf and every
+# -inf case is guarded), so they are built without IEEE NaN-quieting; otherwise each
+# max over MFMA results starts with a canonicalising v_max_f32 x, x, x.
+NO_NAN_SOURCES = {"attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+                  "mass.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src: str, build_dir: str) -> str:
     obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *NO_NAN_SOURCES.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -4,7 +4,7 @@
 // FPSA_ERR_HIP. No device memory is allocated and no state is kept between calls.
 #include <hip/hip_runtime.h>
 
-#include "../../include/fpsa.h"
+#include "fpsa.h"
 #include "fpsa_internal.h"
 
 using fpsa::Geom;
