@@ -12,8 +12,8 @@ times come from HIP events recorded on the stream the kernels run on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -23,17 +23,52 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16": 2500.0, "fp8": 5000.0}          # dense MFMA, TFLOP/s
 HBM_PEAK = 8000.0                                # GB/s
+CSRC = os.path.join(ROOT, "block_sparse_attention_reorder_amd", "csrc")
+# sources each timed kernel is built from (its counters go stale when they change)
+KERNEL_SOURCES = {
+    "sparse_fwd": ["attn.hip", "fpsa_device.h"],
+    "block_mass": ["mass.hip", "fpsa_device.h"],
+    "tile_qkv": ["reorder.hip", "fpsa_device.h"],
+    "untile": ["reorder.hip", "fpsa_device.h"],
+    "select": ["select.hip", "fpsa_device.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the same counter on a plain copy of known size), or None when the
+    kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get("kernels", {}).get(kernel)
+    if not e or e.get("source_sha256") != source_hash(kernel):
+        return None
+    return int(e["hbm_bytes_per_launch"])
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="wan480p")
-    p.add_argument("--cpu-sample", type=int, default=24,
+    p.add_argument("--cpu-sample", type=int, default=624,
                    help="query blocks of head 0 the oracle runs for the CPU baseline (0: skip)")
     p.add_argument("--kernels-only", action="store_true", help="skip the CPU baseline")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="after timing, run one plain 256 MiB device copy (reference for counter runs)")
     return p.parse_args()
 
 
@@ -135,11 +170,19 @@ def main():
     }
     for kk in kernels.values():
         kk["frac"] = kk["achieved"] / kk["peak"]
+    for name, kk in kernels.items():
+        kk["traffic"] = measured_traffic(name)
     dominant = max(kernels, key=lambda n: kernels[n]["ms"])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": round(dk["achieved"], 2),
                 "peak": dk["peak"], "unit": dk["unit"], "frac": round(dk["frac"], 4),
-                "traffic": None}
+                "traffic": dk["traffic"]}
+
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
     cpu = None
     if args.cpu_sample > 0 and not args.kernels_only:
