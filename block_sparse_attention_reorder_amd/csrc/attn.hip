@@ -48,6 +48,17 @@ __device__ inline long xcd_row(long nwg) {
     return (i % 8) * (full / 8) + i / 8;
 }
 
+// Direct global-to-LDS copies are counted by vmcnt, and __syncthreads() alone only
+// waits for LDS instructions (lgkmcnt), so a barrier that hands copied tiles to the
+// other waves must first drain this wave's copies. s_waitcnt immediate on gfx9-family
+// targets: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]; this asks
+// for vmcnt = 0 and leaves the other counters at their maximum (no wait).
+constexpr short kWaitVmcnt0 = 0x0F70;
+__device__ inline void copies_landed_barrier() {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+}
+
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr int kAttnThreads = 256;
 
@@ -223,14 +234,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
             kbn = block_at(e0 + 1);
             copy_k(kbn, 1);
         }
-        __syncthreads();                              // K(0), V(0), K(1) landed
+        copies_landed_barrier();                      // K(0), V(0), K(1) landed
         lds_khalf<D, FP8>(k, kring, kh, lane);
         scores(s);
     }
     for (int j = 0; j < n; ++j) {
         const int kb2 = block_at(e0 + j + 2);
         // K(j+1) and V(j) landed; every wave is done with iteration j-1's reads
-        __syncthreads();
+        copies_landed_barrier();
         lds_vhalf<D>(v, vring + (j & 1) * kVBytes, kh, lane);
         if (j + 1 < n) {
             lds_khalf<D, FP8>(k, kring + ((j + 1) & 1) * kKBytes, kh, lane);
