@@ -102,7 +102,7 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
 size_t fpsa_mass_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g) {
     Geom geo;
     if (!make_geom(g, &geo) || !dims_ok(B, H)) return 0;
-    return fpsa::mass_workspace_bytes_per_row(geo.nb) * (size_t)B * H * geo.nb;
+    return fpsa::mass_workspace_bytes_all(B, H, geo.nb);
 }
 
 int32_t fpsa_block_mass(const void* q_tiled, const void* k_tiled, int32_t B, int32_t H, int32_t D,
@@ -116,7 +116,7 @@ int32_t fpsa_block_mass(const void* q_tiled, const void* k_tiled, int32_t B, int
     if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
     if (geo.nb > FPSA_MAX_SELECT_BLOCKS) return FPSA_ERR_UNSUPPORTED;
     if ((long)B * H * geo.nb > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
-    if (workspace_bytes < fpsa::mass_workspace_bytes_per_row(geo.nb)) return FPSA_ERR_CAPACITY;
+    if (workspace_bytes < fpsa::mass_workspace_bytes_min(geo.nb)) return FPSA_ERR_CAPACITY;
     fpsa::launch_block_mass(q_tiled, k_tiled, B, H, D, geo, softmax_scale, mass, lse, workspace,
                             workspace_bytes, static_cast<hipStream_t>(stream));
     return hip_status();

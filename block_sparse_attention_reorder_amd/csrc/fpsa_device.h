@@ -81,9 +81,6 @@ struct SlotMask {
     }
 };
 
-// Combine lane l with lane l ^ 32 (the two 32-lane halves of the wave) with one
-// v_permlane32_swap: with both operands holding x, the two results hold x of this
-// lane and of its partner half.
 // 0.0f when bit `pos` of m is set, -inf otherwise (an additive score mask that
 // needs no compare/select).
 __device__ inline float mask_bias(uint32_t m, int pos) {
@@ -91,6 +88,46 @@ __device__ inline float mask_bias(uint32_t m, int pos) {
     return __uint_as_float((0u - off) & 0xFF800000u);
 }
 
+// x when bit `pos` of m is set, -inf otherwise: one bitfield extract (0 or all
+// ones) and one bitfield insert.
+__device__ inline float keep_or_neg_inf(float x, uint32_t m, int pos) {
+    const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)m, pos, 1);
+    return __uint_as_float((__float_as_uint(x) & sel) | (0xFF800000u & ~sel));
+}
+
+// Block validity for kernels that read each kept block's index once per 64 blocks:
+// the block's edge code (bit a set when the block is the last, partial tile along
+// a ragged axis a = t, h, w) travels with its index, and the real slots of an edge
+// block follow from this lane's precomputed in-tile bounds without any division.
+struct EdgeSlots {
+    int ok;   // bit a: this lane's slot lies inside the partial last tile along axis a
+    __device__ inline void init(const Geom& g, int lane) {
+        const int plane = g.th * g.tw;
+        const int et = lane / plane, eh = (lane - et * plane) / g.tw, ew = lane - et * plane - eh * g.tw;
+        ok = (et < g.T - (g.nt - 1) * g.tt ? 1 : 0) | (eh < g.Hg - (g.nh - 1) * g.th ? 2 : 0) |
+             (ew < g.Wg - (g.nw - 1) * g.tw ? 4 : 0);
+    }
+    // Ballot of the real slots of a block with edge code `code` (uniform).
+    __device__ inline uint64_t mask(int code) const { return __ballot(((ok | ~code) & 7) == 7); }
+};
+
+// Index word of a kept block: the block index in bits 0..23 and its edge code in
+// bits 24..26; -1 for an entry outside [0, nb).
+constexpr int kEdgeShift = 24;
+constexpr int kBlockIdMask = (1 << kEdgeShift) - 1;
+__device__ inline int block_info(const Geom& g, int kb) {
+    if (kb < 0 || kb >= g.nb) return -1;
+    const int plane = g.nh * g.nw;
+    const int bt = kb / plane, rr = kb - bt * plane;
+    const int bh = rr / g.nw, bw = rr - bh * g.nw;
+    const int code = ((bt + 1) * g.tt > g.T ? 1 : 0) | ((bh + 1) * g.th > g.Hg ? 2 : 0) |
+                     ((bw + 1) * g.tw > g.Wg ? 4 : 0);
+    return kb | (code << kEdgeShift);
+}
+
+// Combine lane l with lane l ^ 32 (the two 32-lane halves of the wave) with one
+// v_permlane32_swap: with both operands holding x, the two results hold x of this
+// lane and of its partner half.
 __device__ inline float wave_max32(float x) {
     const unsigned u = __float_as_uint(x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);

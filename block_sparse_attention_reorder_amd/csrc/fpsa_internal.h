@@ -19,6 +19,10 @@ void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, 
 // Workspace of the mass pass: nb * 64 floats per query-block row in flight; rows
 // are processed in launches of as many rows as the workspace holds.
 size_t mass_workspace_bytes_per_row(int nb);
+// The mass pass takes query blocks in pairs: the smallest workspace holds one pair,
+// the full one every pair of every (batch, head).
+size_t mass_workspace_bytes_min(int nb);
+size_t mass_workspace_bytes_all(int B, int H, int nb);
 void launch_block_mass(const void* q, const void* k, int B, int H, int D, const Geom& g,
                        float scale, float* mass, float* lse, void* ws, size_t ws_bytes,
                        hipStream_t st);

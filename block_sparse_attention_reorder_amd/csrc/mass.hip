@@ -12,177 +12,270 @@
 // quantity as summing every probability, with one exponential per score instead
 // of two passes over QK^T.
 //
-// A workgroup of four waves owns one query block; wave w visits the key blocks
-// kb = w (mod 4), each against all 64 queries, so every K byte is loaded by exactly
-// one wave. Scores use the transposed MFMA form of the sparse forward (S^T = K * Q^T
-// with v_mfma_f32_32x32x16_bf16): a lane holds 32 of a query's 64 block scores, so
-// the block max and sum are in-lane plus one swap of the wave halves. After the
-// sweep the four online states merge through LDS and each thread turns the
-// workspace column of one key block into its mass (a fixed-order sum over the 64
-// queries, so results are reproducible).
-#include "fpsa_device.h"
+// gfx950 mapping. The pass is dense, so two query blocks (2i, 2i+1 of one head)
+// share every key tile: a workgroup of four waves owns both, wave w taking query
+// rows 32*(w & 1) .. +31 of block 2i + (w >> 1) against all 64 keys of each key
+// block. The K tile of each block is copied once per workgroup into a two-slot LDS
+// ring with direct global-to-LDS loads; every wave reads it in the lane order of the MFMA
+// operand (QK tiled layout). Scores use the transposed MFMA form of the sparse
+// forward (S^T = K * Q^T, v_mfma_f32_32x32x16_bf16), so a lane holds 32 of its
+// query's 64 block scores and the block sums are in-lane plus one swap of the wave
+// halves. The products of block j+1 are issued between the exponentials of block j
+// (software pipeline, hand-ordered issue).
+//
+// Exponent reference. Instead of a per-block maximum, each query keeps a lazy
+// reference m: the block's terms 2^(t - m) are summed directly, and only when a sum
+// exceeds 2^64 (or m is still -inf) is the block redone with m raised to the block
+// maximum. Terms far below m underflow to 0; such a block's mass is below 2^-120 of
+// the row's. After the sweep the workgroup's threads turn each workspace column
+// into a mass with a fixed-order sum over the 64 queries (reproducible results).
+#include "attn_common.h"
 #include "fpsa_internal.h"
 
 namespace fpsa {
 
-__device__ inline long xcd_row_mass(long nwg) {
-    long i = blockIdx.x;
-    long full = nwg - nwg % 8;
-    if (i >= full) return i;
-    return (i % 8) * (full / 8) + i / 8;
-}
-
 constexpr int kMassThreads = 256;
+constexpr float kMassSumLimit = 18446744073709551616.0f;   // 2^64
 
 template <int D>
 __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __restrict__ q,
                                                                 const __bf16* __restrict__ k,
-                                                                Geom g, long r_begin, long r_count,
+                                                                Geom g, long p_begin, long p_count,
                                                                 float scale_log2,
                                                                 float* __restrict__ mass,
                                                                 float* __restrict__ lse,
                                                                 float* __restrict__ ws) {
-    __shared__ float ml[4][2][64];                 // [wave][m | l][query]
-    __shared__ float lse_q[64];
-    const long r = r_begin + xcd_row_mass(r_count);
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int kKBytes = kBlock * D * 2;                  // K tile of one block
+    constexpr int kKChunks = kKBytes / 1024 / 4;             // kilobytes per wave per copy
+    static_assert(kKBytes % 4096 == 0, "copies split into whole kilobytes");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kKBytes];
+    __shared__ float lse_q[2][64];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qh = w & 1, sel = w >> 1;
     const int col = lane & 31, half = lane >> 5;
-    const long bh = r / g.nb;
-    const int qb = (int)(r - bh * g.nb);
+    const long p = p_begin + xcd_row(p_count);
+    const int ph = (g.nb + 1) >> 1;                          // pairs per (batch, head)
+    const long bh = p / ph;
+    const int qbA = 2 * (int)(p - bh * ph);
+    const int qb = qbA + sel;                                // this wave's query block
+    const bool hasrow = qb < g.nb;                           // uniform per wave
     const long npad = (long)g.nb * kBlock;
     const long qblk0 = bh * npad + (long)qb * kBlock;
-    float* wrow = ws + (r - r_begin) * (long)g.nb * kBlock;   // [nb][64] block lse of each query
-    SlotMask sm;
-    sm.init(g, lane);
+    // workspace [pair slot][sel][nb][64]: block log-sum-exp of each query
+    float* wrow = ws + ((p - p_begin) * 2 + sel) * (long)g.nb * kBlock;
+    EdgeSlots edge;
+    edge.init(g, lane);
 
-    bf16x8 qop[2][D / 16];
-    const __bf16* qp = q + qblk0 * D + 8 * lane;
+    KHalf<D, false> qop;
+    if (hasrow) {
+        load_khalf<D, false>(qop, q, qblk0, qh, lane);
+    } else {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+        for (int j = 0; j < D / 16; ++j)
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st)
-            qop[qt][st] = *reinterpret_cast<const bf16x8*>(qp + (qt * (D / 16) + st) * 512);
+            for (int e = 0; e < 8; ++e) qop.b[j][e] = (__bf16)0.0f;
+    }
 
-    // K of a block is loaded one visit ahead (register double buffer), so the
-    // product of this block never waits on memory.
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
-    const __bf16* kbase = k + bh * npad * D + 8 * lane;
-    bf16x8 kcur[2][D / 16], knext[2][D / 16];
-    auto load_block = [&](bf16x8 (&dst)[2][D / 16], int kb) {
-        const __bf16* kp = kbase + (long)(kb < g.nb ? kb : 0) * kBlock * D;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st)
-                dst[kt][st] = *reinterpret_cast<const bf16x8*>(kp + (kt * (D / 16) + st) * 512);
+    const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(k) + bh * npad * D * 2;
+    const int lane16 = 16 * lane;
+    auto copy_k = [&](int kb, int slot) {
+        copy_to_lds<kKChunks>(kbytes + (long)(kb < g.nb ? kb : 0) * kKBytes + kKChunks * w * 1024,
+                              lds + slot * kKBytes + kKChunks * w * 1024, lane16);
     };
-    load_block(kcur, w);
-    for (int kb = w; kb < g.nb; kb += 4) {
-        load_block(knext, kb + 4);
-        f32x16 s[2][2];                            // [key tile][query tile]
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[kt][qt][i] = 0.0f;
-#pragma unroll
-                for (int st = 0; st < D / 16; ++st)
-                    s[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[kt][st], qop[qt][st], s[kt][qt], 0, 0, 0);
+
+    // Edge code of block kb (bit a: last, partial tile along a ragged axis), kept
+    // incrementally as kb walks the blocks in raster order.
+    const int rag = (g.T % g.tt ? 1 : 0) | (g.Hg % g.th ? 2 : 0) | (g.Wg % g.tw ? 4 : 0);
+    int bt = 0, bhh = 0, bw = 0;
+    auto edge_code = [&]() {
+        return ((bt == g.nt - 1 ? 1 : 0) | (bhh == g.nh - 1 ? 2 : 0) | (bw == g.nw - 1 ? 4 : 0)) & rag;
+    };
+    auto next_coords = [&]() {
+        if (++bw == g.nw) {
+            bw = 0;
+            if (++bhh == g.nh) {
+                bhh = 0;
+                ++bt;
             }
+        }
+    };
+
+    float m = -INFINITY, l = 0.0f;                           // this lane's query: lazy reference, sum
+    KHalf<D, false> k0, k1;                                  // key tiles 0 and 1 of the next block
+    f32x16 sa[2], sb[2];                                     // scores [key tile] of two blocks
+
+    // Sum of 2^(t - m) over this wave's 64 keys of a block (both lanes of a query
+    // hold it after the half swap).
+    auto block_sum = [&](const f32x16 (&s)[2], float nref) {
+        float a = 0.0f, b = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            a += __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][i], scale_log2, nref));
+            b += __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][i], scale_log2, nref));
+        }
+        return wave_add32(a + b);
+    };
+    // Finish block kb: redo the sum with a raised reference when needed, record
+    // L = m + log2(sum) and accumulate the row sum. `sum` is the sum formed in the
+    // main section; the scores s already have their padding keys masked.
+    auto finish = [&](const f32x16 (&s)[2], int kb, float sum) {
+        if (__ballot(!(sum <= kMassSumLimit) || m == -INFINITY)) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+            const float mb = wave_max32(mx) * scale_log2;   // a block always has a real key
+            const float mnew = fmaxf(m, mb);
+            l *= __builtin_amdgcn_exp2f(m - mnew);          // 0 while m = -inf
+            m = mnew;
+            sum = block_sum(s, -m);
+        }
+        l += sum;
+        if (hasrow && half == 0) wrow[(long)kb * kBlock + 32 * qh + col] = m + __builtin_amdgcn_logf(sum);
+    };
+
+    // Main section of block j (scores s) with the products of block j+1 (into sn), in
+    // hand-chosen issue order: K(j+1) is read from LDS, K(j+2) copied into the slot
+    // K(j) used (after the reads: a read issued after a copy that might write the
+    // same bytes has to wait for it), then each product of block j+1 is followed by
+    // exponentials of block j. Returns the sum of block j's terms against the
+    // current reference.
+    auto main_ordered = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2], bool masked, uint64_t vm) {
+        const float nref = m == -INFINITY ? 0.0f : -m;
+        uint32_t m32[2] = {0u, 0u};
+        if (masked) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) m32[kt] = (uint32_t)(vm >> (32 * kt + 4 * half));
+        }
+        const uint8_t* kst = lds + ((j + 1) & 1) * kKBytes;
+        lds_khalf<D, false>(k0, kst, 0, lane);
+        lds_khalf<D, false>(k1, kst, 1, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        copy_k(j + 2, j & 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) kcur[kt][st] = knext[kt][st];
-        const uint64_t vmask = sm.mask(g, kb);
-        if (vmask != ~0ull) {
+            for (int i = 0; i < 16; ++i) sn[kt][i] = 0.0f;
+        // 2 * D/16 products of block j+1; the 32 exponentials of block j spread over them
+        constexpr int kProducts = 2 * (D / 16);
+        constexpr int kPerProduct = (32 + kProducts - 1) / kProducts;
+        float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const uint32_t m32 = (uint32_t)(vmask >> (32 * kt + 4 * half));
+        for (int pi = 0; pi < kProducts; ++pi) {
+            const int kt = pi & 1, st = pi >> 1;
+            if (kt == 0) sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0.b[st], qop.b[st], sn[0], 0, 0, 0);
+            else sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1.b[st], qop.b[st], sn[1], 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float bias = mask_bias(m32, 8 * (i >> 2) + (i & 3));
-                    s[kt][0][i] += bias;
-                    s[kt][1][i] += bias;
+            for (int e = 0; e < kPerProduct; ++e) {
+                const int i = pi * kPerProduct + e;
+                if (i < 32) {
+                    if (masked) s[i >> 4][i & 15] = keep_or_neg_inf(s[i >> 4][i & 15], m32[i >> 4],
+                                                                    8 * ((i & 15) >> 2) + (i & 3));
+                    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 4][i & 15], scale_log2, nref));
+                    if (i & 1) acc1 += t;
+                    else acc0 += t;
                 }
             }
+            pin(acc0);
+            pin(acc1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        float lb[2];
+        return wave_add32(acc0 + acc1);
+    };
+
+    const int nb = g.nb;
+    // prologue: K(0), K(1) in flight, K(0) read, products of block 0
+    copy_k(0, 0);
+    copy_k(1, 1);
+    copies_landed_barrier();
+    {
+        lds_khalf<D, false>(k0, lds, 0, lane);
+        lds_khalf<D, false>(k1, lds, 1, lane);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            float mx = s[0][qt][0];
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int i = 0; i < 16; ++i) sa[kt][i] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][qt][i]);
-            const float mb = wave_max32(mx) * scale_log2;     // block max (base 2); a block always has a real key
-            float sum = 0.0f;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][i], scale_log2, -mb));
-            sum = wave_add32(sum);                            // >= 1: the max term is 2^0
-            lb[qt] = mb + __builtin_amdgcn_logf(sum);         // v_log_f32 is log2
-            const float mnew = fmaxf(m[qt], mb);
-            l[qt] = l[qt] * __builtin_amdgcn_exp2f(m[qt] - mnew) + sum * __builtin_amdgcn_exp2f(mb - mnew);
-            m[qt] = mnew;
+        for (int st = 0; st < D / 16; ++st) {
+            sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0.b[st], qop.b[st], sa[0], 0, 0, 0);
+            sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1.b[st], qop.b[st], sa[1], 0, 0, 0);
         }
-        // query 32*half + col of this block: lanes of half h store query tile h
-        wrow[(long)kb * kBlock + lane] = half ? lb[1] : lb[0];
     }
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-        if (half == qt) {
-            ml[w][0][32 * qt + col] = m[qt];
-            ml[w][1][32 * qt + col] = l[qt];
-        }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int qi = threadIdx.x;
-        float mm = ml[0][0][qi];
-#pragma unroll
-        for (int j = 1; j < 4; ++j) mm = fmaxf(mm, ml[j][0][qi]);
-        float ll = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ll += ml[j][1][qi] == 0.0f ? 0.0f : ml[j][1][qi] * __builtin_amdgcn_exp2f(ml[j][0][qi] - mm);
-        const bool valid = g.valid(qb, qi);
-        const float l2 = mm + __builtin_amdgcn_logf(ll);
-        if (lse != nullptr) lse[qblk0 + qi] = valid ? l2 * kLn2 : 0.0f;
-        lse_q[qi] = valid ? l2 : INFINITY;          // padding queries contribute 2^-inf = 0
+    auto step = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2]) {
+        const int code = edge_code();
+        // K(j+1) landed; every wave is done reading K(j) (its slot is refilled below)
+        copies_landed_barrier();
+        // two straight-line versions of the main section: edge blocks mask their
+        // padding keys before the exponentials
+        float sum;
+        if (code == 0) sum = main_ordered(j, s, sn, false, ~0ull);
+        else sum = main_ordered(j, s, sn, true, edge.mask(code));
+        finish(s, j, sum);
+        next_coords();
+    };
+    for (int j = 0; j < nb; j += 2) {
+        step(j, sa, sb);
+        if (j + 1 < nb) step(j + 1, sb, sa);
     }
+
+    // Row log-sum-exp (base 2) of each query; padding queries take +inf so that
+    // they add 2^-inf = 0 to every mass.
+    const int qslot = 32 * qh + col;
+    const bool qvalid = hasrow && g.valid(qb, qslot);
+    const float l2 = m + __builtin_amdgcn_logf(l);
+    if (half == 0) {
+        lse_q[sel][qslot] = qvalid ? l2 : INFINITY;
+        if (hasrow && lse != nullptr) lse[qblk0 + qslot] = qvalid ? l2 * kLn2 : 0.0f;
+    }
+    // the workspace rows written above are read back by other threads below
     __syncthreads();
-    const float inv = 1.0f / (float)g.count(qb);
-    float* out = mass + r * g.nb;
-    for (int kb = threadIdx.x; kb < g.nb; kb += kMassThreads) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(wrow + (long)kb * kBlock);
-        float acc = 0.0f;
+    {
+        const int s2 = threadIdx.x >> 7, t = threadIdx.x & 127;   // threads 0-127: block 2i, 128-255: 2i+1
+        if (qbA + s2 < nb) {
+            const float* wr = ws + ((p - p_begin) * 2 + s2) * (long)nb * kBlock;
+            const float inv = 1.0f / (float)g.count(qbA + s2);
+            float* out = mass + (bh * nb + qbA + s2) * (long)nb;
+            for (int kb = t; kb < nb; kb += 128) {
+                const f32x4* src = reinterpret_cast<const f32x4*>(wr + (long)kb * kBlock);
+                float acc = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const f32x4 v4 = src[j];
+                for (int j = 0; j < 16; ++j) {
+                    const f32x4 v4 = src[j];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc += __builtin_amdgcn_exp2f(v4[t] - lse_q[4 * j + t]);
+                    for (int e = 0; e < 4; ++e) acc += __builtin_amdgcn_exp2f(v4[e] - lse_q[s2][4 * j + e]);
+                }
+                out[kb] = acc * inv;
+            }
         }
-        out[kb] = acc * inv;
     }
 }
 
 size_t mass_workspace_bytes_per_row(int nb) { return (size_t)nb * kBlock * sizeof(float); }
 
+size_t mass_workspace_bytes_min(int nb) { return 2 * mass_workspace_bytes_per_row(nb); }
+
+size_t mass_workspace_bytes_all(int B, int H, int nb) {
+    return mass_workspace_bytes_min(nb) * (size_t)B * H * ((nb + 1) / 2);
+}
+
 void launch_block_mass(const void* q, const void* k, int B, int H, int D, const Geom& g,
                        float scale, float* mass, float* lse, void* ws, size_t ws_bytes,
                        hipStream_t st) {
-    const long R = (long)B * H * g.nb;
+    const long P = (long)B * H * ((g.nb + 1) / 2);              // query-block pairs
     const float sl2 = scale * kLog2e;
     const __bf16* qb = static_cast<const __bf16*>(q);
     const __bf16* kb = static_cast<const __bf16*>(k);
-    const long chunk = (long)(ws_bytes / mass_workspace_bytes_per_row(g.nb));   // >= 1, checked by the caller
-    for (long r0 = 0; r0 < R; r0 += chunk) {
-        const long n = R - r0 < chunk ? R - r0 : chunk;
+    const long chunk = (long)(ws_bytes / mass_workspace_bytes_min(g.nb));   // >= 1, checked by the caller
+    for (long p0 = 0; p0 < P; p0 += chunk) {
+        const long n = P - p0 < chunk ? P - p0 : chunk;
         if (D == 128)
-            k_block_mass<128><<<(unsigned)n, kMassThreads, 0, st>>>(qb, kb, g, r0, n, sl2, mass, lse, (float*)ws);
+            k_block_mass<128><<<(unsigned)n, kMassThreads, 0, st>>>(qb, kb, g, p0, n, sl2, mass, lse, (float*)ws);
         else
-            k_block_mass<64><<<(unsigned)n, kMassThreads, 0, st>>>(qb, kb, g, r0, n, sl2, mass, lse, (float*)ws);
+            k_block_mass<64><<<(unsigned)n, kMassThreads, 0, st>>>(qb, kb, g, p0, n, sl2, mass, lse, (float*)ws);
     }
 }
 

@@ -130,19 +130,20 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
  *   keys and c(qb) the number of real queries in qb. Each row sums to 1.
  * mass: [B, H, nb, nb] float32. lse: [B, H, Npad] float32 natural-log log-sum-exp of
  *   each real query's scaled scores (padding rows get 0), or NULL.
- * workspace: device scratch of workspace_bytes, at least nb*64*4 bytes (one query
- *   block); fpsa_mass_workspace_bytes gives the size that lets one launch cover all
- *   B*H*nb query blocks. With less, the call issues several launches, each covering
- *   as many query blocks as fit. Contents on return are unspecified.
+ * workspace: device scratch of workspace_bytes, at least 2*nb*64*4 bytes (the
+ *   pass takes query blocks in pairs, 2i and 2i+1 of a head, and keeps nb*64 floats
+ *   per query block); fpsa_mass_workspace_bytes gives the size that lets one launch
+ *   cover every pair. With less, the call issues several launches, each covering as
+ *   many pairs as fit. Contents on return are unspecified.
  * nb must not exceed FPSA_MAX_SELECT_BLOCKS; FPSA_ERR_CAPACITY if the workspace
- *   holds less than one query block.
+ *   holds less than one pair.
  */
 int32_t fpsa_block_mass(const void* q_tiled, const void* k_tiled, int32_t B, int32_t H, int32_t D,
                         const fpsa_grid* g, float softmax_scale, float* mass, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes for fpsa_block_mass to run in one launch (B*H*nb*nb*64*4);
-   0 for an invalid grid. Host-only. */
+/* Workspace bytes for fpsa_block_mass to run in one launch
+   (B*H*ceil(nb/2) pairs * 2*nb*64*4); 0 for an invalid grid. Host-only. */
 size_t fpsa_mass_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g);
 
 /*

@@ -97,7 +97,7 @@ def test_tile_reorder_validation(L):
 
 def test_block_mass_validation(L):
     f = L.fpsa_block_mass
-    ws = 4 * 64 * 4                                    # one query block of a 4-block grid
+    ws = 2 * 4 * 64 * 4                                # one pair of query blocks of a 4-block grid
     assert f(None, FAKE, 1, 1, 64, grid(), 0.125, FAKE, None, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
     assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.125, None, None, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
     assert f(FAKE, FAKE, 1, 1, 64, grid(), 0.125, FAKE, None, None, ws, None) == fpsa.ERR_INVALID_ARG
@@ -111,6 +111,8 @@ def test_block_mass_validation(L):
 
 def test_mass_workspace_bytes(L):
     assert fpsa.mass_workspace_bytes(1, 12, (21, 30, 52), (4, 4, 4)) == 12 * 624 * 624 * 64 * 4
+    # 3 blocks: two pairs (the second holds one query block), 2 * 3 * 64 floats each
+    assert fpsa.mass_workspace_bytes(2, 1, (4, 4, 12), (4, 4, 4)) == 2 * 2 * (2 * 3 * 64 * 4)
     assert fpsa.mass_workspace_bytes(1, 1, (4, 8, 8), (4, 4, 2)) == 0
 
 

@@ -170,8 +170,8 @@ def test_block_mass_matches_oracle(grid, H, D, amp):
     got = lse.cpu().numpy()[0][:, slot]
     # float32 carries lse ~ 100 to about 8e-6: allow a few units in the last place
     assert np.all(np.abs(got - want) <= 4e-7 * np.abs(want) + 2e-6)
-    # a workspace of three query blocks runs the pass in several launches; every
-    # row is computed the same way, so the result is bit-identical
+    # a workspace of three query blocks (one pair) runs the pass in several launches;
+    # every row is computed the same way, so the result is bit-identical
     mass3 = bsa.block_mass(qt, kt, workspace=bsa.mass_workspace(max_bytes=3 * bsa.nb * 64 * 4))
     assert torch.equal(mass3, mass)
 
