@@ -26,8 +26,8 @@ HBM_PEAK = 8000.0                                # GB/s
 CSRC = os.path.join(ROOT, "block_sparse_attention_reorder_amd", "csrc")
 # sources each timed kernel is built from (its counters go stale when they change)
 KERNEL_SOURCES = {
-    "sparse_fwd": ["attn.hip", "fpsa_device.h"],
-    "block_mass": ["mass.hip", "fpsa_device.h"],
+    "sparse_fwd": ["attn.hip", "attn_common.h", "fpsa_device.h"],
+    "block_mass": ["mass.hip", "attn_common.h", "fpsa_device.h"],
     "tile_qkv": ["reorder.hip", "fpsa_device.h"],
     "untile": ["reorder.hip", "fpsa_device.h"],
     "select": ["select.hip", "fpsa_device.h"],
