@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, the smoke check and the benchmark's
 CPU-baseline leg import this package; the product path never does. It shares no
 code with the HIP library: geometry, masses, selection, masked attention, FP8
-quantization and the structured mask are each written here from their definitions
+quantization, the structured mask, the retained-mass monitor and the fixed
+diagonal / multi-diagonal / stripe patterns are each written here from their definitions
 (``fpsa_oracle.c``), over raster-ordered tokens.
 
 Parity pins (tests/test_oracle_pins.py) tie each function to something other than
@@ -79,6 +80,10 @@ def lib():
             L.orc_fp8_tile_codes.argtypes = [_f32p] + [ctypes.c_int] * 4 + [_i32p, ctypes.c_int, _u8p, _f32p]
             L.orc_structured_mask.restype = ctypes.c_int64
             L.orc_structured_mask.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p]
+            L.orc_retained_mass.restype = None
+            L.orc_retained_mass.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, _i32p, _i32p, _f64p]
+            L.orc_pattern_mask.restype = ctypes.c_int64
+            L.orc_pattern_mask.argtypes = [ctypes.c_int] * 3 + [_i32p, _i32p, _i32p]
             _lib = L
     return _lib
 
@@ -232,4 +237,27 @@ def structured_mask(gh, gw, copies=1):
     cap = copies * nb * (gw + gh + 9)
     col_idx = np.zeros(cap, np.int32)
     nnz = lib().orc_structured_mask(gh, gw, copies, row_ptr, col_idx)
+    return row_ptr, col_idx[:nnz].copy()
+
+
+# --------------------------------------------------------------------------- monitor and patterns
+
+def retained_mass(mass, row_ptr, col_idx):
+    """Per row: the sum of the row's block masses (rows x nb, any leading shape)
+    over the distinct in-range indices its CSR row lists, in float64."""
+    m = _c(mass, np.float32)
+    nb = m.shape[-1]
+    m = m.reshape(-1, nb)
+    ci = _c(col_idx, np.int32) if len(col_idx) else np.zeros(1, np.int32)
+    out = np.zeros(m.shape[0], np.float64)
+    lib().orc_retained_mass(m, m.shape[0], nb, _c(row_ptr, np.int32), ci, out)
+    return out
+
+
+def pattern_mask(nb, B, H, patterns):
+    """CSR of the per-head fixed patterns; patterns: H tuples (band, period, stripe, dense)."""
+    pat = np.ascontiguousarray(np.asarray(patterns, np.int32).reshape(H, 4))
+    row_ptr = np.zeros(B * H * nb + 1, np.int32)
+    col_idx = np.zeros(max(B * H * nb * nb, 1), np.int32)
+    nnz = lib().orc_pattern_mask(nb, B, H, pat, row_ptr, col_idx)
     return row_ptr, col_idx[:nnz].copy()

@@ -16,7 +16,9 @@
  * quantization follows [FPSAttention: Training-Aware FP8 and Sparsity Co-Design for
  * Fast Video Diffusion, Abstract]; the group-shared structured key set follows
  * [Grouping First, Attending Smartly: Training-Free Acceleration for Diffusion
- * Transformers, Abstract].
+ * Transformers, Abstract]; the diagonal, multi-diagonal and vertical-stripe patterns
+ * follow [Sparse-vDiT: Unleashing the Power of Sparse Attention to Accelerate Video
+ * Diffusion Transformers, Abstract].
  */
 #include <math.h>
 #include <stdint.h>
@@ -441,4 +443,79 @@ void orc_fp8_tile_codes(const float* x, int B, int N, int H, int D,
                     codes[RIX(b, n, h, d)] = orc_e4m3_encode((double)y);
                 }
         }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Retained mass of a frozen block set                                        */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * The fraction of a row's attention mass that a block set keeps: for row r,
+ * out[r] = sum of mass[r, kb] over the distinct indices kb in [0, nb) that the row
+ * lists (the block masses of a later step measured on the support frozen at the
+ * dense step; the support's stability across steps is the observation the frozen
+ * indices rest on [LoSA: Near-Lossless Sparse Attention for Training-Free Video
+ * Diffusion Acceleration, Abstract]). Float64 sum in ascending kb order.
+ */
+void orc_retained_mass(const float* mass, int64_t R, int nb, const int32_t* row_ptr,
+                       const int32_t* col_idx, double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        char* seen = (char*)calloc((size_t)nb, 1);
+        for (int32_t e = row_ptr[r]; e < row_ptr[r + 1]; ++e)
+            if (col_idx[e] >= 0 && col_idx[e] < nb) seen[col_idx[e]] = 1;
+        double s = 0.0;
+        for (int kb = 0; kb < nb; ++kb)
+            if (seen[kb]) s += (double)mass[r * (int64_t)nb + kb];
+        out[r] = s;
+        free(seen);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Fixed sparsity patterns (diagonal, multi-diagonal, vertical stripes)       */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * The three recurring patterns named for video DiT attention maps [Sparse-vDiT:
+ * Unleashing the Power of Sparse Attention to Accelerate Video Diffusion
+ * Transformers, Abstract], read on the sequence of 64-token blocks (raster tile order):
+ *   diagonal:        key block kb with |kb - qb| <= band;
+ *   multi-diagonal:  the same band repeated every `period` blocks, i.e. the distance
+ *                    from kb - qb to the nearest multiple of period is <= band;
+ *   vertical stripe: every query block keeps the key blocks kb < stripe;
+ *   dense:           every key block.
+ * A head's pattern is the union of the parts it enables (band < 0: no band;
+ * period <= 0: no repeat; stripe <= 0: no stripe). pattern[h] = {band, period,
+ * stripe, dense}; rows (b*H + h)*nb + qb; indices ascending. Returns the number of
+ * pairs; col_idx must hold them.
+ */
+static int pattern_keep(const int32_t* p, int qb, int kb) {
+    int band = p[0], period = p[1], stripe = p[2], dense = p[3];
+    if (dense) return 1;
+    if (kb < stripe) return 1;
+    if (band >= 0) {
+        int d = kb - qb;
+        if (abs(d) <= band) return 1;
+        if (period > 0) {
+            int m = ((d % period) + period) % period;
+            int dist = m < period - m ? m : period - m;
+            if (dist <= band) return 1;
+        }
+    }
+    return 0;
+}
+
+int64_t orc_pattern_mask(int nb, int B, int H, const int32_t* pattern, int32_t* row_ptr,
+                         int32_t* col_idx) {
+    int64_t nnz = 0;
+    row_ptr[0] = 0;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int qb = 0; qb < nb; ++qb) {
+                for (int kb = 0; kb < nb; ++kb)
+                    if (pattern_keep(pattern + 4 * h, qb, kb)) col_idx[nnz++] = kb;
+                row_ptr[((int64_t)b * H + h) * nb + qb + 1] = (int32_t)nnz;
+            }
+    return nnz;
 }

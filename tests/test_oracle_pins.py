@@ -374,3 +374,97 @@ def test_fp8_tile_codes_decode_to_quantized_values():
     dec = np.vectorize(O.e4m3_decode)(codes)
     s = sc[0][:, blk].T[None, :, :, None]                 # [1, N, H, 1]
     assert np.array_equal((dec * s).astype(np.float32), xhat)
+
+
+# --------------------------------------------------------------------------- retained-mass monitor
+
+def test_retained_mass_hand_values_and_degenerate_rows():
+    m = np.array([[0.5, 0.25, 0.125, 0.125],
+                  [0.1, 0.2, 0.3, 0.4],
+                  [1.0, 0.0, 0.0, 0.0]], np.float32)
+    rp = np.array([0, 2, 2, 6], np.int32)
+    # row 0 keeps {0, 2}; row 1 keeps nothing; row 2 lists 3 twice, -1 and 4 (out of range)
+    ci = np.array([2, 0, 3, 3, -1, 4], np.int32)
+    out = O.retained_mass(m, rp, ci)
+    assert out.tolist() == [0.625, 0.0, 0.0]
+    # leading shapes flatten to rows
+    out2 = O.retained_mass(m.reshape(1, 3, 4), rp, ci)
+    assert out2.tolist() == out.tolist()
+
+
+def test_retained_mass_of_full_rows_is_one_and_of_selection_clears_threshold():
+    grid, tile = (5, 6, 7), (4, 4, 4)
+    nb = O.num_blocks(grid, tile)
+    q, k, _ = _rand_qkv(1, 210, 2, 16, 21)
+    mass = O.block_mass(q, k, grid, tile, 0.25).reshape(-1, nb)
+    full_rp = np.arange(0, mass.shape[0] * nb + 1, nb, dtype=np.int32)
+    full_ci = np.tile(np.arange(nb, dtype=np.int32), mass.shape[0])
+    assert np.abs(O.retained_mass(mass, full_rp, full_ci) - 1.0).max() < 1e-6
+    # the 99 % selection of the same step keeps at least 99 % of each row's
+    # (float32-stored) mass, up to the selection's 2^-40 key quantum per block
+    rp, ci = O.select_blocks(mass)
+    kept = O.retained_mass(mass, rp, ci)
+    tot = mass.astype(np.float64).sum(axis=1)
+    assert np.all(kept >= 0.99 * tot - nb * 2.0 ** -40)
+    # and dropping its smallest kept block falls below
+    for r in range(mass.shape[0]):
+        row = ci[rp[r]:rp[r + 1]]
+        w = min(row, key=lambda i: (mass[r, i], -i))
+        assert kept[r] - mass[r, w] < 0.99 * tot[r] + nb * 2.0 ** -40
+
+
+# --------------------------------------------------------------------------- fixed patterns
+
+def test_pattern_mask_counts_by_closed_form():
+    nb = 37
+    # diagonal band w: row qb keeps min(qb+w, nb-1) - max(qb-w, 0) + 1 blocks;
+    # in total nb(2w+1) - w(w+1)
+    for w in (0, 1, 3):
+        rp, ci = O.pattern_mask(nb, 1, 1, [(w, 0, 0, 0)])
+        assert len(ci) == nb * (2 * w + 1) - w * (w + 1)
+        assert np.diff(rp).tolist() == [min(q + w, nb - 1) - max(q - w, 0) + 1 for q in range(nb)]
+    # vertical stripe s alone: every row keeps exactly blocks 0..s-1
+    rp, ci = O.pattern_mask(nb, 1, 1, [(-1, 0, 5, 0)])
+    assert _csr_rows(rp, ci) == [list(range(5))] * nb
+    # dense: all nb
+    rp, ci = O.pattern_mask(nb, 1, 1, [(-1, 0, 0, 1)])
+    assert _csr_rows(rp, ci) == [list(range(nb))] * nb
+    # nothing enabled: every row empty
+    rp, ci = O.pattern_mask(nb, 1, 1, [(-1, 0, 0, 0)])
+    assert len(ci) == 0 and np.all(rp == 0)
+
+
+def test_pattern_mask_multi_diagonal_is_residue_classes():
+    # band 0, period p dividing nb: row qb keeps exactly the blocks congruent to qb mod p
+    nb, p = 48, 12
+    rows = _csr_rows(*O.pattern_mask(nb, 1, 1, [(0, p, 0, 0)]))
+    for q in range(nb):
+        assert rows[q] == [k for k in range(q % p, nb, p)]
+    # band w < p/2: 2w+1 residues around qb, so (2w+1) nb/p blocks per row
+    rows = _csr_rows(*O.pattern_mask(nb, 1, 1, [(2, p, 0, 0)]))
+    for q in range(nb):
+        res = {(q + d) % p for d in range(-2, 3)}
+        assert rows[q] == [k for k in range(nb) if k % p in res]
+        assert len(rows[q]) == 5 * nb // p
+
+
+def test_pattern_mask_heads_batches_and_union():
+    nb = 20
+    parts = [(1, 0, 0, 0), (-1, 0, 3, 0), (0, 5, 0, 0)]
+    union = (1, 5, 3, 0)
+    single = [_csr_rows(*O.pattern_mask(nb, 1, 1, [p])) for p in parts]
+    both = _csr_rows(*O.pattern_mask(nb, 1, 1, [union]))
+    for q in range(nb):
+        assert both[q] == sorted(set(single[0][q]) | set(single[1][q]) | set(
+            k for k in range(nb) if min((k - q) % 5, (q - k) % 5) <= 1))
+    # rows are laid out (b, h, qb) with each head's own pattern
+    rp, ci = O.pattern_mask(nb, 2, 3, parts)
+    rows = _csr_rows(rp, ci)
+    for b in range(2):
+        for h in range(3):
+            assert rows[(b * 3 + h) * nb:(b * 3 + h + 1) * nb] == single[h]
+    # band patterns are symmetric: kb in row qb iff qb in row kb
+    sym = _csr_rows(*O.pattern_mask(nb, 1, 1, [(2, 7, 0, 0)]))
+    for q in range(nb):
+        for k in sym[q]:
+            assert q in sym[k]
