@@ -158,6 +158,35 @@ int32_t fpsa_structured_mask(const fpsa_grid* g, int32_t copies, int32_t* row_pt
     return hip_status();
 }
 
+int32_t fpsa_pattern_mask(const fpsa_grid* g, int32_t B, int32_t H, const int32_t* patterns,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    Geom geo;
+    if (!make_geom(g, &geo) || !dims_ok(B, H)) return FPSA_ERR_INVALID_ARG;
+    if (patterns == nullptr || row_ptr == nullptr || col_idx == nullptr || workspace == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    const int64_t R = (int64_t)B * H * geo.nb;
+    if (R > (1L << 24)) return FPSA_ERR_UNSUPPORTED;
+    const int64_t need = R * (int64_t)geo.nb;
+    if (need > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    if (col_capacity < need) return FPSA_ERR_CAPACITY;
+    if (workspace_bytes < fpsa::select_workspace_bytes((long)R)) return FPSA_ERR_CAPACITY;
+    fpsa::launch_pattern(geo.nb, B, H, patterns, row_ptr, col_idx, workspace,
+                         static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_retained_mass(const float* mass, int64_t R, int32_t nb, const int32_t* row_ptr,
+                           const int32_t* col_idx, float* retained, void* stream) {
+    if (mass == nullptr || row_ptr == nullptr || col_idx == nullptr || retained == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (R <= 0 || R > (1L << 24) || nb <= 0) return FPSA_ERR_INVALID_ARG;
+    if (nb > FPSA_MAX_SELECT_BLOCKS) return FPSA_ERR_UNSUPPORTED;
+    fpsa::launch_retained_mass(mass, (long)R, nb, row_ptr, col_idx, retained,
+                               static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
 int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t qk_dtype,
                              const float* q_scale, const float* k_scale, const int32_t* row_ptr,
                              const int32_t* col_idx, int32_t B, int32_t H, int32_t D,

@@ -34,6 +34,10 @@ void launch_select(const float* mass, long R, int nb, uint32_t num, uint32_t den
                    int32_t* col_idx, void* ws, hipStream_t st);
 void launch_structured(const Geom& g, int copies, int32_t* row_ptr, int32_t* col_idx, void* ws,
                        hipStream_t st);
+void launch_pattern(int nb, int B, int H, const int32_t* patterns, int32_t* row_ptr,
+                    int32_t* col_idx, void* ws, hipStream_t st);
+void launch_retained_mass(const float* mass, long R, int nb, const int32_t* row_ptr,
+                          const int32_t* col_idx, float* out, hipStream_t st);
 
 void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, const float* q_scale,
                         const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,

@@ -2,9 +2,9 @@
 // keep the smallest set of key blocks whose mass reaches the threshold (99 %),
 // ranking by mass and breaking ties toward the lower block index [LoSA:
 // Near-Lossless Sparse Attention for Training-Free Video Diffusion Acceleration,
-// Abstract]. Also builds the fixed group-shared structured mask [Grouping First,
-// Attending Smartly: Training-Free Acceleration for Diffusion Transformers,
-// Abstract] into the same CSR form.
+// Abstract]. Also builds fixed masks into the same CSR form (the group-shared
+// structured mask and per-head diagonal / multi-diagonal / stripe patterns) and
+// measures how much of a later step's mass a frozen CSR retains.
 //
 // Arithmetic is on integer keys floor(m * 2^40), so the cut is exact and
 // reproducible. The kept set is the top of the ranking up to the cut key v*:
@@ -192,56 +192,163 @@ void launch_select(const float* mass, long R, int nb, uint32_t num, uint32_t den
     k_select_fill<<<blocks, 64 * kSelWaves, 0, st>>>(mass, R, nb, cut, ties, row_ptr, col_idx);
 }
 
-// ---------------------------------------------------------------- structured mask
+// ---------------------------------------------------------------- rule-built masks
+//
+// A fixed mask is a per-row predicate keep(kb); one count kernel, the scan, and one
+// fill kernel turn it into the CSR. Rows are (b*H + h)*nb + qb, one wave each;
+// ballots over 64 consecutive kb give the ascending order directly.
 
-__device__ inline bool structured_keep(int qb, int kb, int nw) {
-    int r = qb / nw, c = qb - r * nw, r2 = kb / nw, c2 = kb - r2 * nw;
-    return (abs(r - r2) <= 1 && abs(c - c2) <= 1) || r2 == r || c2 == c;
-}
+// Group-shared structured mask [Grouping First, Attending Smartly: Training-Free
+// Acceleration for Diffusion Transformers, Abstract]: blocks form an nh x nw grid of
+// groups; a query group keeps its 3x3 neighbourhood, its whole row and its whole
+// column of groups.
+struct StructuredRule {
+    int nb, nw;
+    struct Row {
+        int r, c, nw;
+        __device__ bool keep(int kb) const {
+            int r2 = kb / nw, c2 = kb - r2 * nw;
+            return (abs(r - r2) <= 1 && abs(c - c2) <= 1) || r2 == r || c2 == c;
+        }
+    };
+    __device__ Row row(long r) const {
+        int qb = (int)(r % nb);
+        return Row{qb / nw, qb % nw, nw};
+    }
+};
 
-__global__ __launch_bounds__(64 * kSelWaves) void k_structured_count(int nb, int nw, long R,
-                                                                     int32_t* __restrict__ count) {
+// Per-head fixed patterns [Sparse-vDiT: Unleashing the Power of Sparse Attention to
+// Accelerate Video Diffusion Transformers, Abstract] on the raster sequence of
+// blocks: a diagonal band |kb - qb| <= band; the band repeated every `period` blocks
+// (multi-diagonal); the first `stripe` blocks for every query (vertical stripe); or
+// everything (dense). A head keeps the union of what it enables.
+struct PatternRule {
+    int nb, H;
+    const int32_t* pat;                    // [H][4]: band, period, stripe, dense
+    struct Row {
+        int qb, band, period, stripe, dense;
+        __device__ bool keep(int kb) const {
+            if (dense || kb < stripe) return true;
+            if (band < 0) return false;
+            const int d = kb - qb;
+            if (abs(d) <= band) return true;
+            if (period <= 0) return false;
+            int m = d % period;
+            if (m < 0) m += period;
+            return min(m, period - m) <= band;
+        }
+    };
+    __device__ Row row(long r) const {
+        const int qb = (int)(r % nb);
+        const int32_t* p = pat + 4 * (int)((r / nb) % H);
+        return Row{qb, p[0], p[1], p[2], p[3] != 0};
+    }
+};
+
+template <class Rule>
+__global__ __launch_bounds__(64 * kSelWaves) void k_rule_count(Rule rule, int nb, long R,
+                                                               int32_t* __restrict__ count) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const long r = (long)blockIdx.x * kSelWaves + w;
     if (r >= R) return;
-    const int qb = (int)(r % nb);
+    const auto row = rule.row(r);
     int n = 0;
     for (int i0 = 0; i0 < nb; i0 += 64) {
         int kb = i0 + lane;
-        n += __popcll(__ballot(kb < nb && structured_keep(qb, kb, nw)));
+        n += __popcll(__ballot(kb < nb && row.keep(kb)));
     }
     if (lane == 0) count[r] = n;
 }
 
-__global__ __launch_bounds__(64 * kSelWaves) void k_structured_fill(int nb, int nw, long R,
-                                                                    const int32_t* __restrict__ row_ptr,
-                                                                    int32_t* __restrict__ col_idx) {
+template <class Rule>
+__global__ __launch_bounds__(64 * kSelWaves) void k_rule_fill(Rule rule, int nb, long R,
+                                                              const int32_t* __restrict__ row_ptr,
+                                                              int32_t* __restrict__ col_idx) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const long r = (long)blockIdx.x * kSelWaves + w;
     if (r >= R) return;
-    const int qb = (int)(r % nb);
+    const auto row = rule.row(r);
     int32_t* out = col_idx + row_ptr[r];
     const uint64_t lt = lanemask_lt();
     int base = 0;
     for (int i0 = 0; i0 < nb; i0 += 64) {
         int kb = i0 + lane;
-        bool keep = kb < nb && structured_keep(qb, kb, nw);
+        bool keep = kb < nb && row.keep(kb);
         uint64_t m = __ballot(keep);
         if (keep) out[base + __popcll(m & lt)] = kb;
         base += __popcll(m);
     }
 }
 
-void launch_structured(const Geom& g, int copies, int32_t* row_ptr, int32_t* col_idx, void* ws,
-                       hipStream_t st) {
-    long R = (long)copies * g.nb;
+template <class Rule>
+static void launch_rule(const Rule& rule, int nb, long R, int32_t* row_ptr, int32_t* col_idx,
+                        void* ws, hipStream_t st) {
     int32_t *count, *ties;
     uint64_t* cut;
     carve(ws, R, &count, &ties, &cut);
     unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
-    k_structured_count<<<blocks, 64 * kSelWaves, 0, st>>>(g.nb, g.nw, R, count);
+    k_rule_count<<<blocks, 64 * kSelWaves, 0, st>>>(rule, nb, R, count);
     k_scan_counts<<<1, 1024, 0, st>>>(count, R, row_ptr);
-    k_structured_fill<<<blocks, 64 * kSelWaves, 0, st>>>(g.nb, g.nw, R, row_ptr, col_idx);
+    k_rule_fill<<<blocks, 64 * kSelWaves, 0, st>>>(rule, nb, R, row_ptr, col_idx);
+}
+
+void launch_structured(const Geom& g, int copies, int32_t* row_ptr, int32_t* col_idx, void* ws,
+                       hipStream_t st) {
+    launch_rule(StructuredRule{g.nb, g.nw}, g.nb, (long)copies * g.nb, row_ptr, col_idx, ws, st);
+}
+
+void launch_pattern(int nb, int B, int H, const int32_t* patterns, int32_t* row_ptr,
+                    int32_t* col_idx, void* ws, hipStream_t st) {
+    launch_rule(PatternRule{nb, H, patterns}, nb, (long)B * H * nb, row_ptr, col_idx, ws, st);
+}
+
+// ---------------------------------------------------------------- retained-mass monitor
+//
+// The share of each row's block mass that a frozen block set still holds at a later
+// step: sum of mass[r, kb] over the distinct in-range kb that CSR row r lists. The
+// frozen indices rest on the support staying put across steps [LoSA: Near-Lossless
+// Sparse Attention for Training-Free Video Diffusion Acceleration, Abstract]; this
+// measures how much of the new mass they cover. One wave per row: the row's indices
+// are marked in an LDS bitmap (duplicates collapse), then the dense mass row is read
+// once, coalesced, and the marked entries are summed in float64 (lane-strided
+// partial sums, then a fixed butterfly: deterministic).
+
+__global__ __launch_bounds__(64 * kSelWaves) void k_retained_mass(const float* __restrict__ mass,
+                                                                  long R, int nb,
+                                                                  const int32_t* __restrict__ row_ptr,
+                                                                  const int32_t* __restrict__ col_idx,
+                                                                  float* __restrict__ out) {
+    extern __shared__ uint32_t marks[];    // kSelWaves bitmaps of ceil(nb / 32) words
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int words = (nb + 31) >> 5;
+    uint32_t* my = marks + w * words;
+    const long r = (long)blockIdx.x * kSelWaves + w;
+    const bool live = r < R;
+    for (int i = lane; i < words; i += 64) my[i] = 0;
+    __syncthreads();
+    if (live) {
+        const int32_t e1 = row_ptr[r + 1];
+        for (int32_t e = row_ptr[r] + lane; e < e1; e += 64) {
+            const int kb = col_idx[e];
+            if ((unsigned)kb < (unsigned)nb) atomicOr(&my[kb >> 5], 1u << (kb & 31));
+        }
+    }
+    __syncthreads();
+    if (!live) return;
+    const float* row = mass + r * nb;
+    double s = 0.0;
+    for (int kb = lane; kb < nb; kb += 64)
+        if ((my[kb >> 5] >> (kb & 31)) & 1u) s += (double)row[kb];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) out[r] = (float)s;
+}
+
+void launch_retained_mass(const float* mass, long R, int nb, const int32_t* row_ptr,
+                          const int32_t* col_idx, float* out, hipStream_t st) {
+    unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
+    size_t lds = (size_t)kSelWaves * ((nb + 31) / 32) * 4;
+    k_retained_mass<<<blocks, 64 * kSelWaves, lds, st>>>(mass, R, nb, row_ptr, col_idx, out);
 }
 
 }  // namespace fpsa

@@ -24,7 +24,7 @@ EXPORTED = [
     "fpsa_num_blocks", "fpsa_status_string", "fpsa_version", "fpsa_select_workspace_bytes",
     "fpsa_mass_workspace_bytes",
     "fpsa_tile_reorder", "fpsa_block_mass", "fpsa_select_blocks", "fpsa_structured_mask",
-    "fpsa_sparse_attn_fwd",
+    "fpsa_pattern_mask", "fpsa_retained_mass", "fpsa_sparse_attn_fwd",
 ]
 
 
@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.fpsa_structured_mask.restype = i32
         L.fpsa_structured_mask.argtypes = [gp, i32, vp, vp, i64, vp, ctypes.c_size_t, vp]
         L.fpsa_sparse_attn_fwd.restype = i32
+        L.fpsa_pattern_mask.restype = i32
+        L.fpsa_pattern_mask.argtypes = [gp, i32, i32, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
+        L.fpsa_retained_mass.restype = i32
+        L.fpsa_retained_mass.argtypes = [vp, i64, i32, vp, vp, vp, vp]
         L.fpsa_sparse_attn_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, gp, f32,
                                            vp, vp, vp]
         _lib = L
@@ -169,6 +173,29 @@ def structured_mask(grid, tile, copies, row_ptr, col_idx, workspace, stream=None
                                    int(col_idx.numel()), _ptr(workspace),
                                    int(workspace.numel() * workspace.element_size()), _stream(stream))
     _check(s, "fpsa_structured_mask")
+
+
+def pattern_mask(grid, tile, B, H, patterns, row_ptr, col_idx, workspace, stream=None) -> None:
+    """patterns: int32 device tensor [H, 4] = (band, period, stripe, dense) per head."""
+    if patterns.dtype != torch.int32 or tuple(patterns.shape) != (int(H), 4) or not patterns.is_contiguous():
+        raise ValueError("patterns must be a contiguous int32 [H, 4] tensor")
+    g = Grid.of(grid, tile)
+    s = lib().fpsa_pattern_mask(ctypes.byref(g), int(B), int(H), _ptr(patterns), _ptr(row_ptr),
+                                _ptr(col_idx), int(col_idx.numel()), _ptr(workspace),
+                                int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(s, "fpsa_pattern_mask")
+
+
+def retained_mass(mass, R, nb, row_ptr, col_idx, out, stream=None) -> None:
+    if mass.dtype != torch.float32 or out.dtype != torch.float32:
+        raise ValueError("mass and out float32")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr/col_idx int32")
+    if mass.numel() < int(R) * int(nb) or out.numel() < int(R) or row_ptr.numel() < int(R) + 1:
+        raise ValueError("mass [R, nb], out [R] and row_ptr [R + 1] are too small")
+    s = lib().fpsa_retained_mass(_ptr(mass), int(R), int(nb), _ptr(row_ptr), _ptr(col_idx), _ptr(out),
+                                 _stream(stream))
+    _check(s, "fpsa_retained_mass")
 
 
 def sparse_attn_fwd(q, k, v, row_ptr, col_idx, grid, tile, B, H, D, softmax_scale, o, *,

@@ -8,7 +8,10 @@ The measurement and selection happen once; the CSR is then reused for every late
 call [LoSA: Near-Lossless Sparse Attention for Training-Free Video Diffusion
 Acceleration, Abstract]. A fixed structured CSR can stand in for the measured one
 [Grouping First, Attending Smartly: Training-Free Acceleration for Diffusion
-Transformers, Abstract]. This module only allocates device buffers (torch) and
+Transformers, Abstract], and so can fixed per-head diagonal / multi-diagonal /
+stripe patterns [Sparse-vDiT: Unleashing the Power of Sparse Attention to Accelerate
+Video Diffusion Transformers, Abstract]; `retained_mass` reports how much of a
+later step's mass the frozen CSR still covers. This module only allocates device buffers (torch) and
 sequences the library calls; all arithmetic runs in the HIP kernels.
 """
 from __future__ import annotations
@@ -124,6 +127,28 @@ class BlockSparseAttention:
         ws = self.workspace()
         fpsa.structured_mask(self.grid, self.tile, self.B * self.H, csr.row_ptr, csr.col_idx, ws, stream=stream)
         return csr
+
+    def frame_period(self) -> int:
+        """Blocks per tile-grid time slice (nh * nw): the block offset between a
+        tile and the tile at the same spatial place one time slice later, the
+        natural period of a multi-diagonal pattern on video grids."""
+        return (-(-self.grid[1] // self.tile[1])) * (-(-self.grid[2] // self.tile[2]))
+
+    def pattern(self, patterns, stream=None) -> Csr:
+        """CSR of fixed per-head patterns: H tuples (band, period, stripe, dense)
+        or an int32 [H, 4] tensor; every head shares the one CSR (one forward launch)."""
+        pat = torch.as_tensor(patterns, dtype=torch.int32).reshape(self.H, 4).contiguous().to(self.device)
+        csr = self.new_csr()
+        fpsa.pattern_mask(self.grid, self.tile, self.B, self.H, pat, csr.row_ptr, csr.col_idx,
+                          self.workspace(), stream=stream)
+        return csr
+
+    def retained_mass(self, mass, csr: Csr, out=None, stream=None):
+        """Share of each row's block mass [B, H, nb, nb] held by the CSR's blocks
+        (the frozen indices' coverage at a later step): float32 [B, H, nb]."""
+        out = torch.empty((self.B, self.H, self.nb), dtype=torch.float32, device=self.device) if out is None else out
+        fpsa.retained_mass(mass, self.R, self.nb, csr.row_ptr, csr.col_idx, out, stream=stream)
+        return out
 
     # ------------------------------------------------------------------ attention
     def forward(self, qt, kt, vt, csr: Csr, q_scale=None, k_scale=None, out=None, lse=None, stream=None):

@@ -12,7 +12,10 @@
  * online softmax (FlashAttention style). A fixed structured key set shared by each
  * query group (neighbouring groups plus the group's row and column) can replace the
  * measured selection [Grouping First, Attending Smartly: Training-Free Acceleration
- * for Diffusion Transformers, Abstract].
+ * for Diffusion Transformers, Abstract], as can fixed per-head diagonal,
+ * multi-diagonal and vertical-stripe patterns [Sparse-vDiT: Unleashing the Power of
+ * Sparse Attention to Accelerate Video Diffusion Transformers, Abstract]. A monitor
+ * reports how much of a later step's mass the frozen indices still retain.
  *
  * Conventions for every call:
  *   - Data pointers are DEVICE pointers owned by the caller, except `g`, which is a
@@ -178,6 +181,43 @@ int32_t fpsa_select_blocks(const float* mass, int64_t R, int32_t nb, uint32_t th
 int32_t fpsa_structured_mask(const fpsa_grid* g, int32_t copies, int32_t* row_ptr,
                              int32_t* col_idx, int64_t col_capacity, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * Fixed per-head patterns ([Sparse-vDiT: Unleashing the Power of Sparse Attention to
+ * Accelerate Video Diffusion Transformers, Abstract]: diagonal, multi-diagonal and
+ * vertical-stripe structures, chosen per head).
+ *
+ * patterns: DEVICE int32 [H][4], head h = {band, period, stripe, dense}. On the
+ * raster sequence of blocks, query block qb of head h keeps key block kb when
+ *   dense != 0, or kb < stripe (vertical stripe), or band >= 0 and either
+ *   |kb - qb| <= band (diagonal) or period > 0 and the distance from kb - qb to the
+ *   nearest multiple of period is <= band (multi-diagonal).
+ * Any int32 values are accepted (band < 0, period <= 0, stripe <= 0 disable their
+ * part); a head with nothing enabled gets empty rows, which the forward answers
+ * with zero output (a skipped head). Rows (b*H + h)*nb + qb, indices ascending;
+ * R = B*H*nb. All heads share one CSR, so one forward launch serves every pattern.
+ * Requires R <= 2^24, R * nb < 2^31, col_capacity >= R * nb (FPSA_ERR_CAPACITY
+ * otherwise), workspace_bytes >= fpsa_select_workspace_bytes(R, nb).
+ */
+int32_t fpsa_pattern_mask(const fpsa_grid* g, int32_t B, int32_t H, const int32_t* patterns,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Retained-mass monitor for frozen indices ([LoSA ..., Abstract]: the kept support
+ * is taken as stable across denoising steps; this measures how much of a later
+ * step's mass it still covers).
+ *
+ * mass: [R, nb] float32 block masses (e.g. fpsa_block_mass of a later step, R =
+ * B*H*nb). row_ptr / col_idx: a CSR with R rows (e.g. the frozen selection).
+ * retained[r] = sum of mass[r, kb] over the DISTINCT indices kb in [0, nb) listed by
+ * row r (repeats count once, out-of-range indices are ignored, an empty row gives
+ * 0), summed in float64 and rounded once to float32. The CSR must be well formed:
+ * 0 <= row_ptr[r] <= row_ptr[r + 1] and col_idx holding row_ptr[R] entries.
+ * Requires 1 <= R <= 2^24, 1 <= nb <= FPSA_MAX_SELECT_BLOCKS. Deterministic.
+ */
+int32_t fpsa_retained_mass(const float* mass, int64_t R, int32_t nb, const int32_t* row_ptr,
+                           const int32_t* col_idx, float* retained, void* stream);
 
 /*
  * Block-sparse attention forward with an online softmax over the kept blocks.

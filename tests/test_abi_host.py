@@ -153,3 +153,26 @@ def test_sparse_attn_validation(L):
     assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 80, g, 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, -1.0, FAKE, None, None) == fpsa.ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, None, None, None) == fpsa.ERR_INVALID_ARG
+
+
+def test_pattern_mask_validation(L):
+    f = L.fpsa_pattern_mask
+    g = grid()                                          # 4 blocks
+    R = 2 * 3 * 4
+    ws = fpsa.select_workspace_bytes(R, 4)
+    assert f(g, 0, 3, FAKE, FAKE, FAKE, R * 4, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(g, 2, 3, None, FAKE, FAKE, R * 4, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(g, 2, 3, FAKE, FAKE, None, R * 4, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(g, 2, 3, FAKE, FAKE, FAKE, R * 4 - 1, FAKE, ws, None) == fpsa.ERR_CAPACITY
+    assert f(g, 2, 3, FAKE, FAKE, FAKE, R * 4, FAKE, ws - 1, None) == fpsa.ERR_CAPACITY
+    assert f(grid(tw=2), 2, 3, FAKE, FAKE, FAKE, R * 4, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+
+
+def test_retained_mass_validation(L):
+    f = L.fpsa_retained_mass
+    assert f(None, 10, 8, FAKE, FAKE, FAKE, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 8, FAKE, FAKE, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 0, 8, FAKE, FAKE, FAKE, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, (1 << 24) + 1, 8, FAKE, FAKE, FAKE, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 0, FAKE, FAKE, FAKE, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 4097, FAKE, FAKE, FAKE, None) == fpsa.ERR_UNSUPPORTED

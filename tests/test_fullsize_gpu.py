@@ -214,6 +214,44 @@ def test_hunyuan_frozen_mask_reuse_sampled():
         del qs_, ks_, vs_, r2
 
 
+def test_hunyuan_retained_mass_monitor():
+    """The frozen step-0 CSR measured against the block masses of later calls:
+    every row of step 0 keeps at least 99 % of its own mass (a property at any
+    size); at steps 1 and 10 sampled rows match the oracle's masses summed over the
+    oracle's own step-0 selection, within the mass pass's per-entry error."""
+    w = WORKLOADS["hunyuan720p"]
+    bsa = BlockSparseAttention(w.grid, w.tile, w.B, w.H, w.D)
+    h = 3
+    blocks = _sample_blocks(bsa.nb, 3, seed=3)
+    csr, rp_o, ci_o, same = None, None, None, None
+    for step in (0, 1, 10):
+        q, k, _ = synth.make_qkv(w.grid, w.B, w.H, w.D, w.amp, w.sigma_at(step), step, bf16=True)
+        qt = bsa.tile_qk(torch.from_numpy(q).to("cuda").to(torch.bfloat16))
+        kt = bsa.tile_qk(torch.from_numpy(k).to("cuda").to(torch.bfloat16))
+        mass = bsa.block_mass(qt, kt)
+        mo = O.block_mass(_head(q, h), _head(k, h), w.grid, w.tile, bsa.scale, qblocks=blocks)[0, 0]
+        if step == 0:
+            csr = bsa.select(mass)
+            rp_o, ci_o = O.select_blocks(mo.astype(np.float32))
+            rp_g, ci_g = csr_to_numpy(csr.row_ptr, csr.col_idx)
+            same = [np.array_equal(ci_g[rp_g[h * bsa.nb + b]:rp_g[h * bsa.nb + b + 1]],
+                                   ci_o[rp_o[i]:rp_o[i + 1]]) for i, b in enumerate(blocks)]
+        kept = bsa.retained_mass(mass, csr)
+        if step == 0:
+            tot = mass.double().sum(-1)
+            assert bool((kept.double() >= 0.99 * tot - 1e-6).all())
+        want = O.retained_mass(mo, rp_o, ci_o)
+        got = kept[0, h].cpu().numpy()[blocks]
+        for i in range(len(blocks)):
+            if same[i]:
+                n = rp_o[i + 1] - rp_o[i]
+                assert abs(got[i] - want[i]) <= n * 1e-6 + 1e-6, (step, blocks[i], got[i], want[i])
+        allk = kept.cpu().numpy()
+        print(f"step {step}: retained mass min {allk.min():.4f} mean {allk.mean():.4f}")
+        assert allk.min() >= 0 and allk.max() <= 1 + 1e-5
+        del q, k, qt, kt, mass
+
+
 def test_structured_mask_full_8192_sampled():
     """The fixed group-shared mask on an 8192x8192 image (512x512 tokens, 8x8
     groups): CSR bit-exact against the oracle for every row, outputs of sampled

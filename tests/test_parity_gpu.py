@@ -143,6 +143,85 @@ def test_structured_mask_bitexact(gh, gw, copies):
     assert np.array_equal(rp, rp_o) and np.array_equal(ci, ci_o)
 
 
+def _periods(grid, tile):
+    return (-(-grid[1] // tile[1])) * (-(-grid[2] // tile[2]))
+
+
+def _patterns(period):
+    # diagonal; multi-diagonal at the time-slice period; both plus a stripe; stripe
+    # only; dense; nothing (a skipped head); saturating / disabled extremes; period 1
+    return [(1, 0, 0, 0), (0, period, 0, 0), (1, period, 2, 0), (-1, 0, 3, 0), (-1, 0, 0, 1),
+            (-1, 0, 0, 0), (2 ** 31 - 1, -5, -3, 0), (0, 1, 0, 0), (2, 7, 2 ** 31 - 1, 0)]
+
+
+@pytest.mark.parametrize("grid,B", [((5, 6, 7), 2), ((9, 10, 13), 1), ((21, 30, 52), 1)])
+def test_pattern_mask_bitexact(grid, B):
+    tile = (4, 4, 4)
+    pats = _patterns(_periods(grid, tile))
+    H = len(pats)
+    bsa = BlockSparseAttention(grid, tile, B, H, 64)
+    csr = bsa.pattern(pats)
+    rp, ci = csr_to_numpy(csr.row_ptr, csr.col_idx)
+    rp_o, ci_o = O.pattern_mask(bsa.nb, B, H, pats)
+    assert np.array_equal(rp, rp_o) and np.array_equal(ci, ci_o)
+
+
+def test_pattern_forward_matches_masked_oracle():
+    grid, tile, H, D = (9, 10, 13), (4, 4, 4), 4, 128
+    per = _periods(grid, tile)
+    pats = [(1, 0, 0, 0), (0, per, 1, 0), (-1, 0, 0, 0), (-1, 0, 2, 0)]
+    q, k, v = inputs(grid, 1, H, D, amp=1.5, seed=31)
+    bsa = BlockSparseAttention(grid, tile, 1, H, D)
+    csr = bsa.pattern(pats)
+    qt, kt = bsa.tile_qk(dev(q, torch.bfloat16)), bsa.tile_qk(dev(k, torch.bfloat16))
+    vt = bsa.tile_vt(dev(v, torch.bfloat16))
+    o = bsa.untile(bsa.forward(qt, kt, vt, csr), torch.float32).cpu().numpy()
+    rp_o, ci_o = O.pattern_mask(bsa.nb, 1, H, pats)
+    out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp_o, ci_o)
+    mx, mean = output_errors(o, out, tok)
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    assert np.all(o[:, :, 2, :] == 0)                   # the skipped head
+
+
+def _ragged_csr(R, nb, seed):
+    """Seeded CSR rows in any order with repeats and out-of-range indices."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for r in range(R):
+        n = int(rng.integers(0, min(2 * nb, 300) + 1)) if r % 5 else 0
+        idx = rng.integers(-3, nb + 3, size=n)
+        rows.append(idx.astype(np.int32))
+    rp = np.zeros(R + 1, np.int32)
+    rp[1:] = np.cumsum([len(x) for x in rows])
+    return rp, (np.concatenate(rows) if rp[-1] else np.zeros(0, np.int32))
+
+
+def _gpu_retained(m, rp, ci):
+    R, nb = m.shape
+    out = torch.full((R,), float("nan"), dtype=torch.float32, device="cuda")
+    fpsa.retained_mass(dev(m, torch.float32), R, nb, dev(rp, torch.int32),
+                       dev(ci if len(ci) else np.zeros(1, np.int32), torch.int32), out)
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("R,nb", [(1, 1), (7, 5), (64, 64), (301, 200), (1000, 624), (33, 4096)])
+def test_retained_mass_matches_oracle(R, nb):
+    m = synth.random_mass_rows(R, nb, seed=R + 3 * nb, tie_frac=0.2, zero_frac=0.1)
+    # float64 sums in another order round to the same float32, or to a neighbour
+    for rp, ci in (_ragged_csr(R, nb, R * nb), O.select_blocks(m)):
+        got = _gpu_retained(m, rp, ci)
+        want = O.retained_mass(m, rp, ci).astype(np.float32)
+        assert np.all(np.abs(got - want) <= np.spacing(want)), np.abs(got - want).max()
+    # every block: the row total; an empty row: exactly 0
+    rp = np.arange(0, R * nb + 1, nb, dtype=np.int32)
+    ci = np.tile(np.arange(nb, dtype=np.int32), R)
+    got = _gpu_retained(m, rp, ci)
+    want = O.retained_mass(m, rp, ci).astype(np.float32)
+    assert np.all(np.abs(got - want) <= np.spacing(want))
+    got = _gpu_retained(m, np.zeros(R + 1, np.int32), np.zeros(0, np.int32))
+    assert np.all(got == 0)
+
+
 # --------------------------------------------------------------------------- block masses
 
 MASS_CASES = [((4, 8, 8), 1, 64, 0.5), ((5, 6, 7), 2, 128, 1.0), ((9, 10, 13), 2, 64, 2.0),
