@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE ONLY. Only ``tests/``, the smoke check and the benchmark's
 CPU-baseline leg import this package; the product path never does. It shares no
 code with the HIP library: geometry, masses, selection, masked attention, FP8
-quantization, the structured mask, the retained-mass monitor and the fixed
-diagonal / multi-diagonal / stripe patterns are each written here from their definitions
+quantization, the structured mask, the retained-mass monitor, the fixed
+diagonal / multi-diagonal / stripe patterns, the gradients of masked attention and the
+block-CSR transpose are each written here from their definitions
 (``fpsa_oracle.c``), over raster-ordered tokens.
 
 Parity pins (tests/test_oracle_pins.py) tie each function to something other than
@@ -83,6 +84,14 @@ def lib():
             L.orc_retained_mass.restype = None
             L.orc_retained_mass.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int, _i32p, _i32p, _f64p]
             L.orc_pattern_mask.restype = ctypes.c_int64
+            L.orc_masked_attention_bwd.restype = None
+            L.orc_masked_attention_bwd.argtypes = [_f32p] * 4 + [ctypes.c_int] * 4 + [
+                _i32p, ctypes.c_int, ctypes.c_double, _i32p, _i32p, _f64p, _f64p, _f64p]
+            L.orc_masked_attention_bwd_dq.restype = None
+            L.orc_masked_attention_bwd_dq.argtypes = [_f32p] * 4 + [ctypes.c_int] * 4 + [
+                _i32p, ctypes.c_int, ctypes.c_double, _i32p, _i32p, _i32p, ctypes.c_int, _f64p, _i32p]
+            L.orc_csr_transpose.restype = ctypes.c_int64
+            L.orc_csr_transpose.argtypes = [_i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p]
             L.orc_pattern_mask.argtypes = [ctypes.c_int] * 3 + [_i32p, _i32p, _i32p]
             _lib = L
     return _lib
@@ -261,3 +270,45 @@ def pattern_mask(nb, B, H, patterns):
     col_idx = np.zeros(max(B * H * nb * nb, 1), np.int32)
     nnz = lib().orc_pattern_mask(nb, B, H, pat, row_ptr, col_idx)
     return row_ptr, col_idx[:nnz].copy()
+
+
+# --------------------------------------------------------------------------- backward
+
+def masked_attention_bwd(q, k, v, dout, grid, tile, scale, row_ptr, col_idx):
+    """(dq, dk, dv), raster [B, N, H, D] float64: gradients of masked attention for
+    the upstream gradient dout."""
+    q, k, v, g = (_c(x, np.float32) for x in (q, k, v, dout))
+    B, N, H, D = q.shape
+    blk, _ = token_blocks(grid, tile)
+    nb = num_blocks(grid, tile)
+    dq, dk, dv = (np.empty((B, N, H, D), np.float64) for _ in range(3))
+    ci = _c(col_idx, np.int32) if len(col_idx) else np.zeros(1, np.int32)
+    lib().orc_masked_attention_bwd(q, k, v, g, B, N, H, D, blk, nb, float(scale),
+                                   _c(row_ptr, np.int32), ci, dq, dk, dv)
+    return dq, dk, dv
+
+
+def masked_attention_bwd_dq(q, k, v, dout, grid, tile, scale, row_ptr, col_idx, qblocks):
+    """(dq [B, H, nsel, 64, D] float64, token_of [B, H, nsel, 64]) for the listed
+    query blocks, rows ordered as in masked_attention."""
+    q, k, v, g = (_c(x, np.float32) for x in (q, k, v, dout))
+    B, N, H, D = q.shape
+    blk, _ = token_blocks(grid, tile)
+    nb = num_blocks(grid, tile)
+    qb = _c(qblocks, np.int32)
+    dq = np.empty((B, H, len(qb), 64, D), np.float64)
+    tok = np.empty((B, H, len(qb), 64), np.int32)
+    ci = _c(col_idx, np.int32) if len(col_idx) else np.zeros(1, np.int32)
+    lib().orc_masked_attention_bwd_dq(q, k, v, g, B, N, H, D, blk, nb, float(scale),
+                                      _c(row_ptr, np.int32), ci, qb, len(qb), dq, tok)
+    return dq, tok
+
+
+def csr_transpose(row_ptr, col_idx, B, H, nb):
+    """(col_ptr [B*H*nb + 1], row_idx [nnz]): per (b, h) the query blocks keeping each key block."""
+    R = B * H * nb
+    col_ptr = np.zeros(R + 1, np.int32)
+    row_idx = np.zeros(max(len(col_idx), 1), np.int32)
+    ci = _c(col_idx, np.int32) if len(col_idx) else np.zeros(1, np.int32)
+    nnz = lib().orc_csr_transpose(_c(row_ptr, np.int32), ci, B, H, nb, col_ptr, row_idx)
+    return col_ptr, row_idx[:nnz].copy()

@@ -519,3 +519,163 @@ int64_t orc_pattern_mask(int nb, int B, int H, const int32_t* pattern, int32_t* 
             }
     return nnz;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Gradients of masked attention                                              */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Backward of the masked attention above for a loss whose gradient with respect
+ * to o_i is dout_i, written from the chain rule (the kernel is FlashAttention
+ * style, and training through the same tiles is what the FP8 and sparsity
+ * co-design is for [FPSAttention: Training-Aware FP8 and Sparsity Co-Design for
+ * Fast Video Diffusion, Abstract]). With s_ij = scale q_i . k_j and p_ij the
+ * softmax of s_i over the allowed keys A_i of query i:
+ *   dv_j  = sum_i p_ij dout_i                    (o_i = sum_j p_ij v_j)
+ *   dp_ij = dout_i . v_j
+ *   ds_ij = p_ij (dp_ij - sum_j' p_ij' dp_ij')   (softmax Jacobian)
+ *   dq_i  = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i.
+ * Queries with an empty A_i contribute nothing. One query at a time; per (b, h) the
+ * key gradients accumulate over queries in raster order.
+ *
+ * The per-query step writes dq_i into dq_row and, when dk / dv are given, adds the
+ * query's contributions to the key gradients of the (b, h) slice.
+ */
+static void bwd_one_query(const float* q, const float* k, const float* v, const float* dout,
+                          int N, int H, int D, int b, int h, int i, const int32_t* block_of,
+                          const char* allowed, double scale, double* s, double* dp,
+                          double* dq_row, double* dk, double* dv) {
+    const float* qi = q + RIX(b, i, h, 0);
+    const float* gi = dout + RIX(b, i, h, 0);
+    for (int d = 0; d < D; ++d) dq_row[d] = 0.0;
+    double m = -INFINITY;
+    for (int j = 0; j < N; ++j) {
+        if (!allowed[block_of[j]]) continue;
+        s[j] = dot_scaled(qi, k + RIX(b, j, h, 0), D, scale);
+        if (s[j] > m) m = s[j];
+    }
+    if (m == -INFINITY) return;
+    double z = 0.0;
+    for (int j = 0; j < N; ++j)
+        if (allowed[block_of[j]]) z += exp(s[j] - m);
+    double delta = 0.0;
+    for (int j = 0; j < N; ++j) {
+        if (!allowed[block_of[j]]) continue;
+        s[j] = exp(s[j] - m) / z;                       /* s now holds p_ij */
+        const float* vj = v + RIX(b, j, h, 0);
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc += (double)gi[d] * (double)vj[d];
+        dp[j] = acc;
+        delta += s[j] * acc;
+    }
+    for (int j = 0; j < N; ++j) {
+        if (!allowed[block_of[j]]) continue;
+        const double p = s[j], ds = p * (dp[j] - delta);
+        const float* kj = k + RIX(b, j, h, 0);
+        for (int d = 0; d < D; ++d) dq_row[d] += scale * ds * (double)kj[d];
+        if (dk) {
+            double* dkj = dk + RIX(b, j, h, 0);
+            double* dvj = dv + RIX(b, j, h, 0);
+            for (int d = 0; d < D; ++d) {
+                dkj[d] += scale * ds * (double)qi[d];
+                dvj[d] += p * (double)gi[d];
+            }
+        }
+    }
+}
+
+/* Full gradients, raster [B, N, H, D] float64 each. */
+void orc_masked_attention_bwd(const float* q, const float* k, const float* v, const float* dout,
+                              int B, int N, int H, int D, const int32_t* block_of, int nb,
+                              double scale, const int32_t* row_ptr, const int32_t* col_idx,
+                              double* dq, double* dk, double* dv) {
+    memset(dq, 0, sizeof(double) * (size_t)B * N * H * D);
+    memset(dk, 0, sizeof(double) * (size_t)B * N * H * D);
+    memset(dv, 0, sizeof(double) * (size_t)B * N * H * D);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            char* allowed = (char*)malloc((size_t)nb);
+            double* s = (double*)malloc(sizeof(double) * (size_t)N);
+            double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+            for (int i = 0; i < N; ++i) {
+                const int64_t row = ((int64_t)b * H + h) * nb + block_of[i];
+                memset(allowed, 0, (size_t)nb);
+                for (int32_t e = row_ptr[row]; e < row_ptr[row + 1]; ++e)
+                    if (col_idx[e] >= 0 && col_idx[e] < nb) allowed[col_idx[e]] = 1;
+                bwd_one_query(q, k, v, dout, N, H, D, b, h, i, block_of, allowed, scale, s, dp,
+                              dq + RIX(b, i, h, 0), dk, dv);
+            }
+            free(dp);
+            free(s);
+            free(allowed);
+        }
+}
+
+/*
+ * Query gradients only, for the requested query blocks (the key gradients of a
+ * block need every query that keeps it, so sampled checks take dq). Layout as in
+ * orc_masked_attention: dq_out [B, H, nsel, 64, D], token_of [B, H, nsel, 64].
+ */
+void orc_masked_attention_bwd_dq(const float* q, const float* k, const float* v, const float* dout,
+                                 int B, int N, int H, int D, const int32_t* block_of, int nb,
+                                 double scale, const int32_t* row_ptr, const int32_t* col_idx,
+                                 const int32_t* qblocks, int nsel, double* dq_out,
+                                 int32_t* token_of) {
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int r = 0; r < nsel; ++r) {
+                const int qb = qblocks[r];
+                const int64_t row = ((int64_t)b * H + h) * nb + qb;
+                char* allowed = (char*)calloc((size_t)nb, 1);
+                for (int32_t e = row_ptr[row]; e < row_ptr[row + 1]; ++e)
+                    if (col_idx[e] >= 0 && col_idx[e] < nb) allowed[col_idx[e]] = 1;
+                double* s = (double*)malloc(sizeof(double) * (size_t)N);
+                double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+                const int64_t base = (((int64_t)b * H + h) * nsel + r) * 64;
+                for (int e = 0; e < 64; ++e) {
+                    token_of[base + e] = -1;
+                    for (int d = 0; d < D; ++d) dq_out[(base + e) * D + d] = 0.0;
+                }
+                int e = 0;
+                for (int i = 0; i < N && e < 64; ++i) {
+                    if (block_of[i] != qb) continue;
+                    token_of[base + e] = i;
+                    bwd_one_query(q, k, v, dout, N, H, D, b, h, i, block_of, allowed, scale, s, dp,
+                                  dq_out + (base + e) * D, NULL, NULL);
+                    e++;
+                }
+                free(dp);
+                free(s);
+                free(allowed);
+            }
+}
+
+/*
+ * Transpose of a block CSR per (b, h): for each key block kb, the query blocks whose
+ * row keeps it, ascending (the column view the key-gradient pass walks). Out-of-range
+ * indices are dropped and repeats collapse. col_ptr [B*H*nb + 1], row_idx [nnz].
+ * Returns nnz.
+ */
+int64_t orc_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int B, int H, int nb,
+                          int32_t* col_ptr, int32_t* row_idx) {
+    int64_t nnz = 0;
+    char* keep = (char*)malloc((size_t)nb * (size_t)nb);
+    col_ptr[0] = 0;
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        memset(keep, 0, (size_t)nb * (size_t)nb);
+        for (int qb = 0; qb < nb; ++qb) {
+            const int64_t row = bh * nb + qb;
+            for (int32_t e = row_ptr[row]; e < row_ptr[row + 1]; ++e)
+                if (col_idx[e] >= 0 && col_idx[e] < nb) keep[(size_t)col_idx[e] * nb + qb] = 1;
+        }
+        for (int kb = 0; kb < nb; ++kb) {
+            for (int qb = 0; qb < nb; ++qb)
+                if (keep[(size_t)kb * nb + qb]) row_idx[nnz++] = qb;
+            col_ptr[bh * nb + kb + 1] = (int32_t)nnz;
+        }
+    }
+    free(keep);
+    return nnz;
+}

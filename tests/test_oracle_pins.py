@@ -468,3 +468,115 @@ def test_pattern_mask_heads_batches_and_union():
     for q in range(nb):
         for k in sym[q]:
             assert q in sym[k]
+
+
+# --------------------------------------------------------------------------- backward
+
+def _token_mask(grid, tile, H, rp, ci):
+    """[H, N, N] bool: query i may attend key j (key block kept by i's block row)."""
+    blk, _ = O.token_blocks(grid, tile)
+    nb = O.num_blocks(grid, tile)
+    keep = np.zeros((H, nb, nb), bool)
+    for h in range(H):
+        for qb in range(nb):
+            keep[h, qb, ci[rp[h * nb + qb]:rp[h * nb + qb + 1]]] = True
+    return keep[:, blk][:, :, blk]
+
+
+def _torch_grads(q, k, v, g, scale, mask):
+    # library autograd through masked softmax attention, float64, [B, H, N, D]
+    t = lambda a: torch.from_numpy(a.astype(np.float64)).permute(0, 2, 1, 3).clone().requires_grad_(True)
+    tq, tk, tv = t(q), t(k), t(v)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask)[None],
+                                                         scale=scale)
+    o.backward(torch.from_numpy(g.astype(np.float64)).permute(0, 2, 1, 3))
+    back = lambda x: x.grad.permute(0, 2, 1, 3).numpy()
+    return back(tq), back(tk), back(tv)
+
+
+def test_backward_matches_library_autograd():
+    grid, tile, H, D = (5, 6, 7), (4, 4, 4), 2, 16
+    nb = O.num_blocks(grid, tile)
+    q, k, v = _rand_qkv(1, 210, H, D, 41)
+    g = _rand_qkv(1, 210, H, D, 42)[0]
+    rows = synth.random_mass_rows(H * nb, nb, seed=5)
+    rp, ci = O.select_blocks(rows, 1, 2)
+    dq, dk, dv = O.masked_attention_bwd(q, k, v, g, grid, tile, 0.3, rp, ci)
+    rq, rk, rv = _torch_grads(q, k, v, g, 0.3, _token_mask(grid, tile, H, rp, ci))
+    for a, b in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.abs(a - b).max() < 1e-11
+
+
+def test_backward_matches_finite_differences_of_the_forward_oracle():
+    grid, tile, H, D = (4, 8, 8), (4, 4, 4), 1, 8
+    nb = O.num_blocks(grid, tile)
+    q, k, v = _rand_qkv(1, 256, H, D, 43)
+    g = _rand_qkv(1, 256, H, D, 44)[0]
+    rp = np.array([0, 2, 3, 3, 5], np.int32)            # block 2 keeps nothing
+    ci = np.array([0, 3, 1, 2, 3], np.int32)
+    dq, dk, dv = O.masked_attention_bwd(q, k, v, g, grid, tile, 0.5, rp, ci)
+    blk, _ = O.token_blocks(grid, tile)
+
+    def loss(q_, k_, v_):
+        out, tok = O.masked_attention(q_, k_, v_, grid, tile, 0.5, rp, ci)
+        tot = 0.0
+        for qb in range(nb):
+            t = tok[0, 0, qb][tok[0, 0, qb] >= 0]
+            tot += float(np.sum(out[0, 0, qb, :len(t)] * g[0, t, 0].astype(np.float64)))
+        return tot
+
+    rng = np.random.default_rng(0)
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(4):
+            n, d = int(rng.integers(0, 256)), int(rng.integers(0, D))
+            plus, minus = [x.copy() for x in (q, k, v)], [x.copy() for x in (q, k, v)]
+            plus[which][0, n, 0, d] += np.float32(1e-3)
+            minus[which][0, n, 0, d] -= np.float32(1e-3)
+            step = float(plus[which][0, n, 0, d]) - float(minus[which][0, n, 0, d])
+            fd = (loss(*plus) - loss(*minus)) / step
+            assert abs(fd - grad[0, n, 0, d]) < 1e-5 * max(1.0, abs(fd)), (which, n, d, fd, grad[0, n, 0, d])
+    # queries of the block with no kept key get no gradient; nothing flows to its keys from them
+    assert np.all(dq[0, blk == 2] == 0)
+
+
+def test_backward_sums_over_keys():
+    # sum_j ds_ij = 0 for every query, so the key gradients sum to zero; the value
+    # gradients sum to the upstream gradients of the queries that attend anything
+    grid, tile, H, D = (9, 10, 13), (4, 4, 4), 2, 16
+    nb = O.num_blocks(grid, tile)
+    N = 9 * 10 * 13
+    q, k, v = _rand_qkv(1, N, H, D, 45)
+    g = _rand_qkv(1, N, H, D, 46)[0]
+    rows = synth.random_mass_rows(H * nb, nb, seed=6)
+    rows[3] = 0.0                                       # one empty row
+    rp, ci = O.select_blocks(rows, 9, 10)
+    dq, dk, dv = O.masked_attention_bwd(q, k, v, g, grid, tile, 0.25, rp, ci)
+    blk, _ = O.token_blocks(grid, tile)
+    assert np.abs(dk.sum(axis=1)).max() < 1e-10
+    for h in range(H):
+        live = np.diff(rp)[h * nb + blk] > 0
+        want = g[0, live, h].astype(np.float64).sum(axis=0)
+        assert np.abs(dv[0, :, h].sum(axis=0) - want).max() < 1e-9
+    # the sampled query-gradient routine gives the same rows
+    sel = [0, 3, nb - 1]
+    dqs, tok = O.masked_attention_bwd_dq(q, k, v, g, grid, tile, 0.25, rp, ci, sel)
+    for h in range(H):
+        for r in range(len(sel)):
+            t = tok[0, h, r][tok[0, h, r] >= 0]
+            assert np.array_equal(dqs[0, h, r, :len(t)], dq[0, t, h])
+
+
+def test_csr_transpose_hand_example_and_round_trip():
+    # 1 batch, 2 heads, 3 blocks
+    rp = np.array([0, 2, 3, 3, 4, 7, 8], np.int32)
+    ci = np.array([0, 2, 2, 1, 0, 1, 2, 1], np.int32)
+    cp, ri = O.csr_transpose(rp, ci, 1, 2, 3)
+    assert _csr_rows(cp, ri) == [[0], [], [0, 1], [1], [0, 1, 2], [1]]
+    rows = synth.random_mass_rows(3 * 40, 40, seed=8)
+    rp, ci = O.select_blocks(rows, 1, 2)
+    cp, ri = O.csr_transpose(rp, ci, 1, 3, 40)
+    rp2, ci2 = O.csr_transpose(cp, ri, 1, 3, 40)
+    assert np.array_equal(rp2, rp) and np.array_equal(ci2, ci)
+    # out-of-range entries dropped, repeats collapse
+    cp, ri = O.csr_transpose(np.array([0, 4, 4], np.int32), np.array([1, 1, -1, 5], np.int32), 1, 1, 2)
+    assert _csr_rows(cp, ri) == [[], [0]]
