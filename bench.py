@@ -178,6 +178,8 @@ def main():
                 "peak": dk["peak"], "unit": dk["unit"], "frac": round(dk["frac"], 4),
                 "traffic": dk["traffic"]}
 
+    extras = next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, max(3, args.steps // 4))
+
     if args.calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -212,9 +214,58 @@ def main():
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                     for n, d in kernels.items()},
         "roofline": roofline,
+        "next_rows": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def _timed(fn, stream, reps):
+    import torch
+    fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        fn()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, reps):
+    """Timings of the rows beyond the headline path on the same inputs, after the
+    timed region: the retained-mass monitor over the step's masses and CSR, and
+    fixed per-head patterns (mask build and the forward over them)."""
+    import torch
+    kept = torch.empty((w.B, w.H, bsa.nb), dtype=torch.float32, device=qt.device)
+    nnz = int(csr.row_ptr[-1].item())
+    t_mon = _timed(lambda: bsa.retained_mass(mass, csr, out=kept), stream, reps)
+    mon_bytes = bsa.R * bsa.nb * 4 + (bsa.R + 1) * 4 + nnz * 4 + bsa.R * 4
+    per = bsa.frame_period()
+    cycle = [(2, 0, 0, 0), (1, per, 0, 0), (-1, 0, 8, 0), (1, per, 4, 0)]
+    pats = [cycle[h % len(cycle)] for h in range(w.H)]
+    pcsr = bsa.pattern(pats)
+    ws = bsa.workspace()
+    patt = torch.as_tensor(pats, dtype=torch.int32).to(qt.device)
+    from block_sparse_attention_reorder_amd import fpsa
+    t_build = _timed(lambda: fpsa.pattern_mask(bsa.grid, bsa.tile, bsa.B, bsa.H, patt, pcsr.row_ptr,
+                                               pcsr.col_idx, ws), stream, reps)
+    pnnz = int(pcsr.row_ptr[-1].item())
+    t_pf = _timed(lambda: bsa.forward(qt, kt, vt, pcsr, out=ot), stream, reps)
+    pflop = pnnz * 4.0 * 64 * 64 * w.D
+    return {
+        "retained_mass": {"ms": round(t_mon, 4), "bound": "hbm",
+                          "achieved_GBps": round(mon_bytes / t_mon / 1e6, 1),
+                          "frac": round(mon_bytes / t_mon / 1e6 / HBM_PEAK, 4),
+                          "work_per_unit": "nb*4 bytes of masses + CSR entries per row",
+                          "min": round(float(kept.min()), 5), "mean": round(float(kept.mean()), 5)},
+        "pattern_mask": {"ms_build": round(t_build, 4), "patterns": "per head, cycling diagonal band 2; "
+                         "multi-diagonal band 1 period nh*nw; stripe 8; multi-diagonal + stripe 4",
+                         "kept_pairs": pnnz, "density": round(pnnz / (bsa.R * bsa.nb), 4),
+                         "fwd_ms": round(t_pf, 4), "fwd_kept_tflops": round(pflop / t_pf / 1e9, 2),
+                         "fwd_frac_of_bf16_peak": round(pflop / t_pf / 1e9 / PEAK["bf16"], 4)},
+    }
 
 
 def cpu_baseline(w, q, k, v, bsa, nsample):

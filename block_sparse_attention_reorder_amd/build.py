@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfpsa.so")
-SOURCES = ["api.hip", "reorder.hip", "mass.hip", "select.hip", "attn.hip"]
+SOURCES = ["api.hip", "reorder.hip", "mass.hip", "select.hip", "attn.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

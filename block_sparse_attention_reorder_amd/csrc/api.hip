@@ -99,6 +99,17 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
     return hip_status();
 }
 
+size_t fpsa_transpose_workspace_bytes(int64_t R, int32_t nb) {
+    if (R <= 0 || nb <= 0 || R > (1L << 24)) return 0;
+    return fpsa::transpose_workspace_bytes((long)R, nb);
+}
+
+size_t fpsa_bwd_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g) {
+    Geom geo;
+    if (!make_geom(g, &geo) || !dims_ok(B, H)) return 0;
+    return fpsa::bwd_workspace_bytes(B, H, geo.nb);
+}
+
 size_t fpsa_mass_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g) {
     Geom geo;
     if (!make_geom(g, &geo) || !dims_ok(B, H)) return 0;
@@ -191,7 +202,7 @@ int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_
                              const float* q_scale, const float* k_scale, const int32_t* row_ptr,
                              const int32_t* col_idx, int32_t B, int32_t H, int32_t D,
                              const fpsa_grid* g, float softmax_scale, void* o, float* lse,
-                             void* stream) {
+                             float* o_f32, void* stream) {
     Geom geo;
     if (!make_geom(g, &geo) || !dims_ok(B, H)) return FPSA_ERR_INVALID_ARG;
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return FPSA_ERR_INVALID_ARG;
@@ -210,7 +221,50 @@ int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_
         return FPSA_ERR_UNSUPPORTED;
     }
     fpsa::launch_sparse_attn(q, k, v, fp8, q_scale, k_scale, row_ptr, col_idx, B, H, D, geo,
-                             softmax_scale, o, lse, static_cast<hipStream_t>(stream));
+                             softmax_scale, o, lse, o_f32, static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int32_t B, int32_t H,
+                           int32_t nb, int32_t* col_ptr, int32_t* row_idx, int64_t capacity,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (row_ptr == nullptr || col_idx == nullptr || col_ptr == nullptr || row_idx == nullptr ||
+        workspace == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (!dims_ok(B, H) || nb <= 0) return FPSA_ERR_INVALID_ARG;
+    const int64_t R = (int64_t)B * H * nb;
+    if (R > (1L << 24)) return FPSA_ERR_UNSUPPORTED;
+    if (R * nb > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    if (capacity < R * nb) return FPSA_ERR_CAPACITY;
+    if (workspace_bytes < fpsa::transpose_workspace_bytes((long)R, nb)) return FPSA_ERR_CAPACITY;
+    fpsa::launch_csr_transpose(row_ptr, col_idx, (long)R, nb, col_ptr, row_idx, workspace,
+                               static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                             int32_t o_dtype, const void* dout, const float* lse, const int32_t* row_ptr,
+                             const int32_t* col_idx, const int32_t* col_ptr,
+                             const int32_t* row_idx, int32_t B, int32_t H, int32_t D,
+                             const fpsa_grid* g, float softmax_scale, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    Geom geo;
+    if (!make_geom(g, &geo) || !dims_ok(B, H)) return FPSA_ERR_INVALID_ARG;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || dout == nullptr ||
+        lse == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (row_ptr == nullptr || col_idx == nullptr || col_ptr == nullptr || row_idx == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return FPSA_ERR_INVALID_ARG;
+    if (o_dtype != FPSA_BF16 && o_dtype != FPSA_F32) return FPSA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    if ((long)B * H * geo.nb > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
+    if (workspace_bytes < fpsa::bwd_workspace_bytes(B, H, geo.nb)) return FPSA_ERR_CAPACITY;
+    fpsa::launch_sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, B, H, D,
+                                 geo, softmax_scale, o_dtype == FPSA_F32, dq, dk, dv, workspace,
+                                 static_cast<hipStream_t>(stream));
     return hip_status();
 }
 

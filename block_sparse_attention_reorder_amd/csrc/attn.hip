@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long R,
-    float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse) {
+    float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o32) {
     constexpr int kDT = D / 32;
     constexpr int kKBytes = kBlock * D * (FP8 ? 1 : 2);   // K tile of one block
     constexpr int kVBytes = kBlock * D * 2;               // V tile of one block
@@ -170,12 +170,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
 
     // The last iteration's copies target the memory the merge uses: drain them.
     copies_landed_barrier();
-    merge_and_store<D>(reinterpret_cast<float*>(lds), qh, kh, lane, acc, m, l, true, g, qb, qblk0, o, lse);
+    merge_and_store<D>(reinterpret_cast<float*>(lds), qh, kh, lane, acc, m, l, true, g, qb, qblk0, o, lse, o32);
 }
 
 void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, const float* q_scale,
                         const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
-                        int B, int H, int D, const Geom& g, float scale, void* o, float* lse,
+                        int B, int H, int D, const Geom& g, float scale, void* o, float* lse, float* o32,
                         hipStream_t st) {
     const long R = (long)B * H * g.nb;
     const float sl2 = scale * kLog2e;
@@ -183,11 +183,11 @@ void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, co
     __bf16* out = static_cast<__bf16*>(o);
     dim3 grid((unsigned)R), block(kAttnThreads);
     if (D == 128) {
-        if (fp8) k_sparse_attn<128, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse);
-        else k_sparse_attn<128, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse);
+        if (fp8) k_sparse_attn<128, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32);
+        else k_sparse_attn<128, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32);
     } else {
-        if (fp8) k_sparse_attn<64, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse);
-        else k_sparse_attn<64, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse);
+        if (fp8) k_sparse_attn<64, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32);
+        else k_sparse_attn<64, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32);
     }
 }
 

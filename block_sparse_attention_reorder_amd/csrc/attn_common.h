@@ -320,7 +320,8 @@ __device__ __attribute__((always_inline)) inline void block_main_bf16_d128(
 template <int D>
 __device__ __attribute__((always_inline)) inline void merge_and_store(
     float* xch_base, int qh, int kh, int lane, f32x16 (&acc)[D / 32], float m, float l, bool store,
-    const Geom& g, int qb, long qblk0, __bf16* __restrict__ o, float* __restrict__ lse) {
+    const Geom& g, int qb, long qblk0, __bf16* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ o32) {
     constexpr int kDT = D / 32;
     float* xch = xch_base + qh * (kDT * 16 + 2) * 64;
     if (kh == 1) {
@@ -359,6 +360,18 @@ __device__ __attribute__((always_inline)) inline void merge_and_store(
             for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(acc[t][4 * g4 + j] * inv);
             *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g4 + 4 * half) = v4;
         }
+    if (o32 != nullptr) {
+        float* frow = o32 + (qblk0 + qslot) * D;
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 v4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v4[j] = acc[t][4 * g4 + j] * inv;
+                *reinterpret_cast<f32x4*>(frow + 32 * t + 8 * g4 + 4 * half) = v4;
+            }
+    }
     if (lse != nullptr && half == 0) {
         float val = 0.0f;
         if (qvalid) val = l > 0.0f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;

@@ -1,0 +1,403 @@
+// Block-sparse attention backward over a frozen block CSR (bf16 operands, float32
+// accumulation): the gradients of the FlashAttention-style forward, which is what
+// training through the same 64-token tiles needs [FPSAttention: Training-Aware FP8
+// and Sparsity Co-Design for Fast Video Diffusion, Abstract].
+//
+// With s = scale q.k, p = exp(s - lse) (lse from the forward), dp = dO.v and
+// delta = dO.O per query:
+//   dV_j = sum_i p_ij dO_i,  dS_ij = p_ij (dp_ij - delta_i),
+//   dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j.
+// Three kernels, no atomics (deterministic):
+//   k_bwd_prep  per query slot: delta = dO.O (O in bf16 or, more accurately, the
+//               forward's float32 copy) and lse in base 2 (+inf for padding or
+//               a query without keys, so its probabilities are exactly 0);
+//   k_bwd_dkdv  one workgroup per key block, walking the query blocks that keep it
+//               (the transposed CSR); dK and dV stay in registers;
+//   k_bwd_dq    one workgroup per query block, walking its kept key blocks.
+// Every operand comes from the QK tiled layout. Products whose reduction runs over
+// tokens (P^T dO, dS^T Q, dS K) need the tile transposed - channel per lane, tokens
+// along the operand - which the gfx950 transposing LDS read (ds_read_b64_tr_b16)
+// delivers from the same LDS copy: within each 16-lane group, output lane i element
+// j is element i%4 of input lane 4j + i/4. Each wave owns a 32 x 32 (query, key)
+// sub-tile of every block pair; the two partial sums of each output half are added
+// through LDS at the end.
+#include "attn_common.h"
+#include "fpsa_internal.h"
+
+namespace fpsa {
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Byte offset of element (token e, channel d) inside a bf16 QK tile (include/fpsa.h).
+template <int D>
+__device__ inline int qk_off(int e, int d) {
+    return 2 * (((((e >> 5) * (D / 16) + (d >> 4)) * 2 + ((d >> 3) & 1)) * 32 + (e & 31)) * 8 + (d & 7));
+}
+
+// Offset of this lane's 8-byte source for a transposing read of the QK tile that
+// gives each lane of a 16-lane group g one channel (16*(g%2) + lane%16 of a 32-channel
+// tile) and four consecutive tokens, starting at token t0 + 4*(g/2): input lane a
+// supplies token t0 + 4*(g/2) + a/4, channels 4*(a%4) .. +3. Tokens t0 + 8 .. follow
+// at +128 bytes, the next 16 tokens at +256, the next 32-channel tile at +2048.
+template <int D>
+__device__ inline int tr_base(int t0, int lane) {
+    const int g = lane >> 4, a = lane & 15;
+    return qk_off<D>(t0 + 4 * (g >> 1) + (a >> 2), 16 * (g & 1) + 4 * (a & 3));
+}
+
+// Operand of 8 tokens in position order (t0..t0+3, then t0+8..t0+11 of the lane's
+// half) for one channel per lane.
+__device__ inline bf16x8 tr_operand(const uint8_t* tile, int off) {
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off));
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off + 128));
+    const s16x8 z = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, z);
+}
+
+// ---------------------------------------------------------------- preprocessing
+
+template <int D, class OT>
+__global__ __launch_bounds__(256) void k_bwd_prep(const OT* __restrict__ o,
+                                                  const __bf16* __restrict__ dout,
+                                                  const float* __restrict__ lse, Geom g,
+                                                  float* __restrict__ lse2, float* __restrict__ delta) {
+    const long blk = blockIdx.x;                   // (b*H + h)*nb + qb
+    const int qb = (int)(blk % g.nb);
+    const int e = threadIdx.x >> 2, part = threadIdx.x & 3;
+    const OT* ot = o + blk * 64 * D;
+    const uint8_t* gt = reinterpret_cast<const uint8_t*>(dout + blk * 64 * D);
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+        const int d0 = 8 * (part + 4 * j);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(gt + qk_off<D>(e, d0));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc += (float)ot[e * D + d0 + t] * (float)b[t];
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (part == 0) {
+        const long i = blk * 64 + e;
+        const float L = lse[i];
+        const bool live = g.valid(qb, e) && L > -INFINITY;
+        lse2[i] = live ? L * kLog2e : INFINITY;
+        delta[i] = live ? acc : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
+    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, Geom g, float c,
+    float scale, __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
+    constexpr int kTile = 64 * D * 2;
+    constexpr int kSlot = 2 * kTile + 512;        // Q tile, dO tile, lse2[64], delta[64]
+    constexpr int kCh = kTile / (256 * 16);       // 16-byte pieces per thread per tile
+    constexpr int kDT = D / 32;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlot];
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hb = lane >> 5;
+    const int kh = w & 1, qh = w >> 1;
+    const long col = xcd_row(gridDim.x);
+    const long bh = col / g.nb;
+    const int kb = (int)(col - bh * g.nb);
+    const long npad = 64L * g.nb;
+
+    KHalf<D, false> kf, vf;                        // B operands: key (lane % 32) of half kh
+    load_khalf<D, false>(kf, k, col * 64, kh, lane);
+    load_khalf<D, false>(vf, v, col * 64, kh, lane);
+    const bool kvalid = g.valid(kb, 32 * kh + (lane & 31));
+    const int trb = tr_base<D>(32 * qh, lane);
+
+    f32x16 accv[kDT], acck[kDT];
+#pragma unroll
+    for (int t = 0; t < kDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) accv[t][i] = acck[t][i] = 0.0f;
+
+    const int e0 = col_ptr[col], n = col_ptr[col + 1] - e0;
+    i32x4 rq[kCh], rg[kCh];
+    float rl = 0.0f;
+    auto fetch = [&](int qbk) {
+        const long base = (bh * g.nb + qbk) * 64;
+        const i32x4* qs = reinterpret_cast<const i32x4*>(q + base * D);
+        const i32x4* gs = reinterpret_cast<const i32x4*>(dout + base * D);
+#pragma unroll
+        for (int j = 0; j < kCh; ++j) {
+            rq[j] = qs[tid + 256 * j];
+            rg[j] = gs[tid + 256 * j];
+        }
+        if (tid < 64) rl = lse2[base + tid];
+        else if (tid < 128) rl = delta[base + tid - 64];
+    };
+    auto stash = [&](int s) {
+        uint8_t* dst = lds + s * kSlot;
+#pragma unroll
+        for (int j = 0; j < kCh; ++j) {
+            *reinterpret_cast<i32x4*>(dst + (tid + 256 * j) * 16) = rq[j];
+            *reinterpret_cast<i32x4*>(dst + kTile + (tid + 256 * j) * 16) = rg[j];
+        }
+        if (tid < 128) reinterpret_cast<float*>(dst + 2 * kTile)[tid] = rl;
+    };
+    auto qb_at = [&](int j) {
+        const int x = row_idx[e0 + j];
+        return (x >= 0 && x < g.nb) ? x : -1;
+    };
+
+    int qcur = n > 0 ? qb_at(0) : -1;
+    if (qcur >= 0) {
+        fetch(qcur);
+        stash(0);
+    }
+    for (int j = 0; j < n; ++j) {
+        __syncthreads();
+        const int qnext = j + 1 < n ? qb_at(j + 1) : -1;
+        if (qnext >= 0) fetch(qnext);
+        if (qcur >= 0) {
+            const uint8_t* sq = lds + (j & 1) * kSlot;
+            const uint8_t* sg = sq + kTile;
+            const float* sl = reinterpret_cast<const float*>(sq + 2 * kTile);
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                const int off = (qh * (D / 16) + st) * 1024 + 16 * lane;
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sq + off),
+                                                            kf.b[st], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sg + off),
+                                                             vf.b[st], dp, 0, 0, 0);
+            }
+            // element i: query 32*qh + 8*(i/4) + 4*hb + i%4, key 32*kh + lane%32
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 L0 = *reinterpret_cast<const f32x4*>(sl + 32 * qh + 16 * ks + 4 * hb);
+                const f32x4 L1 = *reinterpret_cast<const f32x4*>(sl + 32 * qh + 16 * ks + 8 + 4 * hb);
+                const f32x4 G0 = *reinterpret_cast<const f32x4*>(sl + 64 + 32 * qh + 16 * ks + 4 * hb);
+                const f32x4 G1 = *reinterpret_cast<const f32x4*>(sl + 64 + 32 * qh + 16 * ks + 8 + 4 * hb);
+                float p[8], ds[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int i = 8 * ks + t;
+                    const float lq = t < 4 ? L0[t] : L1[t - 4];
+                    const float gq = t < 4 ? G0[t] : G1[t - 4];
+                    const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq)) : 0.0f;
+                    p[t] = pp;
+                    ds[t] = pp * (dp[i] - gq);
+                }
+                const bf16x8 pa = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+                const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+                for (int t = 0; t < kDT; ++t) {
+                    const int off = trb + t * 2048 + ks * 256;
+                    accv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_operand(sg, off), accv[t], 0, 0, 0);
+                    acck[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(sq, off), acck[t], 0, 0, 0);
+                }
+            }
+        }
+        if (qnext >= 0) stash((j + 1) & 1);
+        qcur = qnext;
+    }
+    __syncthreads();
+
+    // add the two query halves' partial sums; element i of tile t: key 32*kh +
+    // 8*(i/4) + 4*hb + i%4, channel 32*t + lane%32
+    float* xch = reinterpret_cast<float*>(lds) + kh * (2 * kDT * 16 * 64);
+    if (qh == 1) {
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                xch[((0 * kDT + t) * 16 + i) * 64 + lane] = accv[t][i];
+                xch[((1 * kDT + t) * 16 + i) * 64 + lane] = acck[t][i];
+            }
+    }
+    __syncthreads();
+    if (qh == 0) {
+        const long row0 = bh * npad + 64L * kb + 32 * kh;
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const long r = row0 + 8 * (i >> 2) + 4 * hb + (i & 3);
+                const int ch = 32 * t + (lane & 31);
+                dv[r * D + ch] = (__bf16)(accv[t][i] + xch[((0 * kDT + t) * 16 + i) * 64 + lane]);
+                dk[r * D + ch] = (__bf16)(scale * (acck[t][i] + xch[((1 * kDT + t) * 16 + i) * 64 + lane]));
+            }
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void k_bwd_dq(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, float c,
+    float scale, __bf16* __restrict__ dq) {
+    constexpr int kTile = 64 * D * 2;
+    constexpr int kSlot = 2 * kTile;              // K tile, V tile
+    constexpr int kCh = kTile / (256 * 16);
+    constexpr int kDT = D / 32;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlot];
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hb = lane >> 5;
+    const int qh = w & 1, kh = w >> 1;
+    const long row = xcd_row(gridDim.x);
+    const long bh = row / g.nb;
+    const long npad = 64L * g.nb;
+
+    KHalf<D, false> qf, gf;                        // B operands: query (lane % 32) of half qh
+    load_khalf<D, false>(qf, q, row * 64, qh, lane);
+    load_khalf<D, false>(gf, dout, row * 64, qh, lane);
+    const float lq = lse2[row * 64 + 32 * qh + (lane & 31)];
+    const float gq = delta[row * 64 + 32 * qh + (lane & 31)];
+    const int trb = tr_base<D>(32 * kh, lane);
+    EdgeSlots edge;
+    edge.init(g, lane);
+
+    f32x16 acc[kDT];
+#pragma unroll
+    for (int t = 0; t < kDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+
+    const int e0 = row_ptr[row], n = row_ptr[row + 1] - e0;
+    i32x4 rk[kCh], rv[kCh];
+    auto fetch = [&](int kbk) {
+        const long base = (bh * g.nb + kbk) * 64 * D;
+        const i32x4* ks = reinterpret_cast<const i32x4*>(k + base);
+        const i32x4* vs = reinterpret_cast<const i32x4*>(v + base);
+#pragma unroll
+        for (int j = 0; j < kCh; ++j) {
+            rk[j] = ks[tid + 256 * j];
+            rv[j] = vs[tid + 256 * j];
+        }
+    };
+    auto stash = [&](int s) {
+        uint8_t* dst = lds + s * kSlot;
+#pragma unroll
+        for (int j = 0; j < kCh; ++j) {
+            *reinterpret_cast<i32x4*>(dst + (tid + 256 * j) * 16) = rk[j];
+            *reinterpret_cast<i32x4*>(dst + kTile + (tid + 256 * j) * 16) = rv[j];
+        }
+    };
+
+    int icur = n > 0 ? block_info(g, col_idx[e0]) : -1;
+    if (icur >= 0) {
+        fetch(icur & kBlockIdMask);
+        stash(0);
+    }
+    for (int j = 0; j < n; ++j) {
+        __syncthreads();
+        const int inext = j + 1 < n ? block_info(g, col_idx[e0 + j + 1]) : -1;
+        if (inext >= 0) fetch(inext & kBlockIdMask);
+        if (icur >= 0) {
+            const uint8_t* sk = lds + (j & 1) * kSlot;
+            const uint8_t* sv = sk + kTile;
+            const int code = icur >> kEdgeShift;
+            const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
+            const uint32_t m32 = (uint32_t)(vm >> (32 * kh + 4 * hb));
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                const int off = (kh * (D / 16) + st) * 1024 + 16 * lane;
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sk + off),
+                                                            qf.b[st], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sv + off),
+                                                             gf.b[st], dp, 0, 0, 0);
+            }
+            // element i: key 32*kh + 8*(i/4) + 4*hb + i%4, query 32*qh + lane%32
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                float ds[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int i = 8 * ks + t;
+                    const float x = keep_or_neg_inf(s[i], m32, 8 * (i >> 2) + (i & 3));
+                    const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lq));
+                    ds[t] = pp * (dp[i] - gq);
+                }
+                const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+                for (int t = 0; t < kDT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(sk, trb + t * 2048 + ks * 256),
+                                                                     acc[t], 0, 0, 0);
+            }
+        }
+        if (inext >= 0) stash((j + 1) & 1);
+        icur = inext;
+    }
+    __syncthreads();
+
+    // add the two key halves; element i of tile t: query 32*qh + 8*(i/4) + 4*hb +
+    // i%4, channel 32*t + lane%32
+    float* xch = reinterpret_cast<float*>(lds) + qh * (kDT * 16 * 64);
+    if (kh == 1) {
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xch[(t * 16 + i) * 64 + lane] = acc[t][i];
+    }
+    __syncthreads();
+    if (kh == 0) {
+        const long row0 = row * 64 + 32 * qh;
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const long r = row0 + 8 * (i >> 2) + 4 * hb + (i & 3);
+                dq[r * D + 32 * t + (lane & 31)] = (__bf16)(scale * (acc[t][i] + xch[(t * 16 + i) * 64 + lane]));
+            }
+    }
+    (void)npad;
+}
+
+// ---------------------------------------------------------------- host
+
+size_t bwd_workspace_bytes(int B, int H, int nb) { return 2 * (size_t)B * H * nb * 64 * sizeof(float); }
+
+template <int D>
+static void launch_bwd_d(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                         const int32_t* col_ptr, const int32_t* row_idx, int B, int H, const Geom& g,
+                         float scale, int o_f32, void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
+    const long rows = (long)B * H * g.nb;
+    float* lse2 = static_cast<float*>(ws);
+    float* delta = lse2 + rows * 64;
+    const float c = scale * kLog2e;
+    auto bq = static_cast<const __bf16*>(q);
+    auto bk = static_cast<const __bf16*>(k);
+    auto bv = static_cast<const __bf16*>(v);
+    auto bg = static_cast<const __bf16*>(dout);
+    if (o_f32)
+        k_bwd_prep<D, float><<<(unsigned)rows, 256, 0, st>>>(static_cast<const float*>(o), bg, lse, g, lse2, delta);
+    else
+        k_bwd_prep<D, __bf16><<<(unsigned)rows, 256, 0, st>>>(static_cast<const __bf16*>(o), bg, lse, g, lse2, delta);
+    k_bwd_dkdv<D><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, col_ptr, row_idx, g, c, scale,
+                                                  static_cast<__bf16*>(dk), static_cast<__bf16*>(dv));
+    k_bwd_dq<D><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, g, c, scale,
+                                                static_cast<__bf16*>(dq));
+}
+
+void launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, const int32_t* row_ptr,
+                            const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,
+                            int B, int H, int D, const Geom& g, float scale, int o_f32, void* dq,
+                            void* dk, void* dv, void* ws, hipStream_t st) {
+    if (D == 128)
+        launch_bwd_d<128>(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, B, H, g, scale, o_f32, dq,
+                          dk, dv, ws, st);
+    else
+        launch_bwd_d<64>(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, B, H, g, scale, o_f32, dq,
+                         dk, dv, ws, st);
+}
+
+}  // namespace fpsa

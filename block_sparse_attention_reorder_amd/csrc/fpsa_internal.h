@@ -39,9 +39,22 @@ void launch_pattern(int nb, int B, int H, const int32_t* patterns, int32_t* row_
 void launch_retained_mass(const float* mass, long R, int nb, const int32_t* row_ptr,
                           const int32_t* col_idx, float* out, hipStream_t st);
 
+// CSR transpose: a bitmap of R * ceil(nb/32) words and R column counts.
+size_t transpose_workspace_bytes(long R, int nb);
+void launch_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, long R, int nb,
+                          int32_t* col_ptr, int32_t* row_idx, void* ws, hipStream_t st);
+
+// Backward: lse in base 2 and delta = dO.O per query slot (2 floats per slot).
+size_t bwd_workspace_bytes(int B, int H, int nb);
+void launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, const int32_t* row_ptr,
+                            const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,
+                            int B, int H, int D, const Geom& g, float scale, int o_f32, void* dq,
+                            void* dk, void* dv, void* ws, hipStream_t st);
+
 void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, const float* q_scale,
                         const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                         int B, int H, int D, const Geom& g, float scale, void* o, float* lse,
-                        hipStream_t st);
+                        float* o32, hipStream_t st);
 
 }  // namespace fpsa

@@ -351,4 +351,94 @@ void launch_retained_mass(const float* mass, long R, int nb, const int32_t* row_
     k_retained_mass<<<blocks, 64 * kSelWaves, lds, st>>>(mass, R, nb, row_ptr, col_idx, out);
 }
 
+// ---------------------------------------------------------------- CSR transpose
+//
+// For each (b, h) and key block kb, the query blocks whose row keeps kb, ascending:
+// the column view the key-gradient pass walks. The rows are first marked in a bitmap
+// (one bit per (row, kb); repeats collapse, out-of-range indices are dropped), then a
+// wave per column counts and writes its query blocks in index order from ballots, so
+// the result is deterministic.
+
+__global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, long n) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(64 * kSelWaves) void k_csr_bitmap(const int32_t* __restrict__ row_ptr,
+                                                               const int32_t* __restrict__ col_idx,
+                                                               long R, int nb, int words,
+                                                               uint32_t* __restrict__ bits) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long r = (long)blockIdx.x * kSelWaves + w;
+    if (r >= R) return;
+    uint32_t* row = bits + r * words;
+    const int32_t e1 = row_ptr[r + 1];
+    for (int32_t e = row_ptr[r] + lane; e < e1; e += 64) {
+        const int kb = col_idx[e];
+        if ((unsigned)kb < (unsigned)nb) atomicOr(&row[kb >> 5], 1u << (kb & 31));
+    }
+}
+
+// bit (qb, kb) of head slice bh
+__device__ inline bool csr_bit(const uint32_t* bits, long bh, int nb, int words, int qb, int kb) {
+    return (bits[(bh * nb + qb) * words + (kb >> 5)] >> (kb & 31)) & 1u;
+}
+
+__global__ __launch_bounds__(64 * kSelWaves) void k_col_count(const uint32_t* __restrict__ bits, int nb,
+                                                              int words, long C,
+                                                              int32_t* __restrict__ count) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long c = (long)blockIdx.x * kSelWaves + w;
+    if (c >= C) return;
+    const long bh = c / nb;
+    const int kb = (int)(c - bh * nb);
+    int n = 0;
+    for (int q0 = 0; q0 < nb; q0 += 64) {
+        const int qb = q0 + lane;
+        n += __popcll(__ballot(qb < nb && csr_bit(bits, bh, nb, words, qb, kb)));
+    }
+    if (lane == 0) count[c] = n;
+}
+
+__global__ __launch_bounds__(64 * kSelWaves) void k_col_fill(const uint32_t* __restrict__ bits, int nb,
+                                                             int words, long C,
+                                                             const int32_t* __restrict__ col_ptr,
+                                                             int32_t* __restrict__ row_idx) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long c = (long)blockIdx.x * kSelWaves + w;
+    if (c >= C) return;
+    const long bh = c / nb;
+    const int kb = (int)(c - bh * nb);
+    int32_t* out = row_idx + col_ptr[c];
+    const uint64_t lt = lanemask_lt();
+    int base = 0;
+    for (int q0 = 0; q0 < nb; q0 += 64) {
+        const int qb = q0 + lane;
+        const bool keep = qb < nb && csr_bit(bits, bh, nb, words, qb, kb);
+        const uint64_t m = __ballot(keep);
+        if (keep) out[base + __popcll(m & lt)] = qb;
+        base += __popcll(m);
+    }
+}
+
+size_t transpose_workspace_bytes(long R, int nb) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return up((size_t)R * ((nb + 31) / 32) * 4) + up((size_t)R * 4);
+}
+
+void launch_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, long R, int nb,
+                          int32_t* col_ptr, int32_t* row_idx, void* ws, hipStream_t st) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const int words = (nb + 31) / 32;
+    uint32_t* bits = static_cast<uint32_t*>(ws);
+    int32_t* count = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + up((size_t)R * words * 4));
+    const long nbits = R * words;
+    const unsigned fill_blocks = (unsigned)min((nbits + 255) / 256, 65536L);
+    k_fill_zero<<<fill_blocks, 256, 0, st>>>(bits, nbits);
+    const unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
+    k_csr_bitmap<<<blocks, 64 * kSelWaves, 0, st>>>(row_ptr, col_idx, R, nb, words, bits);
+    k_col_count<<<blocks, 64 * kSelWaves, 0, st>>>(bits, nb, words, R, count);
+    k_scan_counts<<<1, 1024, 0, st>>>(count, R, col_ptr);
+    k_col_fill<<<blocks, 64 * kSelWaves, 0, st>>>(bits, nb, words, R, col_ptr, row_idx);
+}
+
 }  // namespace fpsa

@@ -25,6 +25,8 @@ EXPORTED = [
     "fpsa_mass_workspace_bytes",
     "fpsa_tile_reorder", "fpsa_block_mass", "fpsa_select_blocks", "fpsa_structured_mask",
     "fpsa_pattern_mask", "fpsa_retained_mass", "fpsa_sparse_attn_fwd",
+    "fpsa_csr_transpose", "fpsa_transpose_workspace_bytes", "fpsa_sparse_attn_bwd",
+    "fpsa_bwd_workspace_bytes",
 ]
 
 
@@ -79,8 +81,17 @@ def lib() -> ctypes.CDLL:
         L.fpsa_pattern_mask.argtypes = [gp, i32, i32, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
         L.fpsa_retained_mass.restype = i32
         L.fpsa_retained_mass.argtypes = [vp, i64, i32, vp, vp, vp, vp]
+        L.fpsa_csr_transpose.restype = i32
+        L.fpsa_csr_transpose.argtypes = [vp, vp, i32, i32, i32, vp, vp, i64, vp, ctypes.c_size_t, vp]
+        L.fpsa_transpose_workspace_bytes.restype = ctypes.c_size_t
+        L.fpsa_transpose_workspace_bytes.argtypes = [i64, i32]
+        L.fpsa_sparse_attn_bwd.restype = i32
+        L.fpsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, gp, f32,
+                                           vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.fpsa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fpsa_bwd_workspace_bytes.argtypes = [i32, i32, gp]
         L.fpsa_sparse_attn_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, gp, f32,
-                                           vp, vp, vp]
+                                           vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -198,13 +209,52 @@ def retained_mass(mass, R, nb, row_ptr, col_idx, out, stream=None) -> None:
     _check(s, "fpsa_retained_mass")
 
 
+def transpose_workspace_bytes(R: int, nb: int) -> int:
+    return int(lib().fpsa_transpose_workspace_bytes(int(R), int(nb)))
+
+
+def bwd_workspace_bytes(B: int, H: int, grid, tile) -> int:
+    g = Grid.of(grid, tile)
+    return int(lib().fpsa_bwd_workspace_bytes(int(B), int(H), ctypes.byref(g)))
+
+
+def csr_transpose(row_ptr, col_idx, B, H, nb, col_ptr, row_idx, workspace, stream=None) -> None:
+    for t in (row_ptr, col_idx, col_ptr, row_idx):
+        if t.dtype != torch.int32:
+            raise ValueError("CSR arrays are int32")
+    s = lib().fpsa_csr_transpose(_ptr(row_ptr), _ptr(col_idx), int(B), int(H), int(nb), _ptr(col_ptr),
+                                 _ptr(row_idx), int(row_idx.numel()), _ptr(workspace),
+                                 int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(s, "fpsa_csr_transpose")
+
+
+def sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, grid, tile, B, H, D,
+                    softmax_scale, dq, dk, dv, workspace, stream=None) -> None:
+    for t in (q, k, v, dout, dq, dk, dv):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("q, k, v, dout and the gradients are bf16")
+    if o.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("o is bf16 or float32")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse float32")
+    g = Grid.of(grid, tile)
+    s = lib().fpsa_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DT[o.dtype], _ptr(dout), _ptr(lse), _ptr(row_ptr),
+                                   _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx), int(B), int(H), int(D),
+                                   ctypes.byref(g), float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                   _stream(stream))
+    _check(s, "fpsa_sparse_attn_bwd")
+
+
 def sparse_attn_fwd(q, k, v, row_ptr, col_idx, grid, tile, B, H, D, softmax_scale, o, *,
-                    q_scale=None, k_scale=None, lse=None, stream=None) -> None:
+                    q_scale=None, k_scale=None, lse=None, o_f32=None, stream=None) -> None:
     qk_dt = _DT[q.dtype]
     if _DT[k.dtype] != qk_dt or v.dtype != torch.bfloat16 or o.dtype != torch.bfloat16:
         raise ValueError("q/k same dtype (bf16 or e4m3 bytes), v and o bf16")
+    if o_f32 is not None and o_f32.dtype != torch.float32:
+        raise ValueError("o_f32 float32")
     g = Grid.of(grid, tile)
     s = lib().fpsa_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), qk_dt, _ptr(q_scale), _ptr(k_scale),
                                    _ptr(row_ptr), _ptr(col_idx), int(B), int(H), int(D), ctypes.byref(g),
-                                   float(softmax_scale), _ptr(o), _ptr(lse), _stream(stream))
+                                   float(softmax_scale), _ptr(o), _ptr(lse), _ptr(o_f32), _stream(stream))
     _check(s, "fpsa_sparse_attn_fwd")

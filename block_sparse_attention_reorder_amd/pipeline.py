@@ -151,11 +151,41 @@ class BlockSparseAttention:
         return out
 
     # ------------------------------------------------------------------ attention
-    def forward(self, qt, kt, vt, csr: Csr, q_scale=None, k_scale=None, out=None, lse=None, stream=None):
+    def forward(self, qt, kt, vt, csr: Csr, q_scale=None, k_scale=None, out=None, lse=None, out_f32=None,
+                stream=None):
+        """Tiled bf16 output; optionally lse and a float32 copy of the output (both
+        for the backward)."""
         out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device) if out is None else out
         fpsa.sparse_attn_fwd(qt, kt, vt, csr.row_ptr, csr.col_idx, self.grid, self.tile, self.B, self.H,
-                             self.D, self.scale, out, q_scale=q_scale, k_scale=k_scale, lse=lse, stream=stream)
+                             self.D, self.scale, out, q_scale=q_scale, k_scale=k_scale, lse=lse, o_f32=out_f32,
+                             stream=stream)
         return out
+
+    # ------------------------------------------------------------------ backward
+    def transpose(self, csr: Csr, stream=None) -> Csr:
+        """Column view of a CSR (per key block, the query blocks keeping it), the
+        index lists the key-gradient pass walks."""
+        csc = self.new_csr()
+        ws = torch.empty(max(fpsa.transpose_workspace_bytes(self.R, self.nb), 1), dtype=torch.uint8,
+                         device=self.device)
+        fpsa.csr_transpose(csr.row_ptr, csr.col_idx, self.B, self.H, self.nb, csc.row_ptr, csc.col_idx, ws,
+                           stream=stream)
+        return csc
+
+    def backward(self, qt, kt, vqk, ot, gt, lse, csr: Csr, csc: Csr, grads=None, workspace=None, stream=None):
+        """Gradients (dq, dk, dv) in tiled rows bf16 from Q, K, V and dO in the QK
+        layout, the forward's tiled output (bf16, or its float32 copy for a more
+        accurate delta) and lse, the CSR and its transpose."""
+        if grads is None:
+            grads = tuple(torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device)
+                          for _ in range(3))
+        ws = workspace
+        if ws is None:
+            ws = torch.empty(fpsa.bwd_workspace_bytes(self.B, self.H, self.grid, self.tile), dtype=torch.uint8,
+                             device=self.device)
+        fpsa.sparse_attn_bwd(qt, kt, vqk, ot, gt, lse, csr.row_ptr, csr.col_idx, csc.row_ptr, csc.col_idx,
+                             self.grid, self.tile, self.B, self.H, self.D, self.scale, *grads, ws, stream=stream)
+        return grads
 
     def run(self, q, k, v, thr_num=99, thr_den=100, out_dtype=torch.bfloat16):
         """Full path on raster Q, K, V: returns (raster O, CSR, masses)."""

@@ -15,7 +15,8 @@
  * for Diffusion Transformers, Abstract], as can fixed per-head diagonal,
  * multi-diagonal and vertical-stripe patterns [Sparse-vDiT: Unleashing the Power of
  * Sparse Attention to Accelerate Video Diffusion Transformers, Abstract]. A monitor
- * reports how much of a later step's mass the frozen indices still retain.
+ * reports how much of a later step's mass the frozen indices still retain, and a
+ * backward pass gives the gradients over the same blocks.
  *
  * Conventions for every call:
  *   - Data pointers are DEVICE pointers owned by the caller, except `g`, which is a
@@ -238,12 +239,65 @@ int32_t fpsa_retained_mass(const float* mass, int64_t R, int32_t nb, const int32
  * o: tiled rows BF16 [B, H, Npad, D]. lse: [B, H, Npad] float32 natural-log
  *   log-sum-exp over the visited keys, taken from the same rounded probabilities
  *   that normalise o (-inf for a query with none; 0 for padding), or NULL.
+ * o_f32: NULL, or tiled rows float32 [B, H, Npad, D] receiving o before its BF16
+ *   rounding (the backward's delta = dO.o is then free of that rounding).
  */
 int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t qk_dtype,
                              const float* q_scale, const float* k_scale, const int32_t* row_ptr,
                              const int32_t* col_idx, int32_t B, int32_t H, int32_t D,
                              const fpsa_grid* g, float softmax_scale, void* o, float* lse,
-                             void* stream);
+                             float* o_f32, void* stream);
+
+/*
+ * Transpose of a block CSR, per (b, h): for key block kb of head slice (b, h), the
+ * query blocks qb whose row (b*H + h)*nb + qb keeps kb, ascending - the column view
+ * the key-gradient pass of fpsa_sparse_attn_bwd walks.
+ *
+ * row_ptr / col_idx: CSR with R = B*H*nb rows (out-of-range indices are dropped,
+ * repeats collapse). col_ptr [R + 1] (column (b*H + h)*nb + kb), row_idx [nnz].
+ * Requires R <= 2^24, R * nb < 2^31, capacity >= R * nb (FPSA_ERR_CAPACITY
+ * otherwise), workspace_bytes >= fpsa_transpose_workspace_bytes(R, nb).
+ * Deterministic.
+ */
+int32_t fpsa_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int32_t B, int32_t H,
+                           int32_t nb, int32_t* col_ptr, int32_t* row_idx, int64_t capacity,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for fpsa_csr_transpose (a bitmap of R x nb bits and R counts);
+   0 for R <= 0 or nb <= 0. Host-only. */
+size_t fpsa_transpose_workspace_bytes(int64_t R, int32_t nb);
+
+/*
+ * Block-sparse attention backward over the same CSR as the forward (the gradients
+ * that training through the sparse, tiled kernel needs [FPSAttention ...,
+ * Abstract]).
+ *
+ * q, k, v, dout: tiled QK layout, BF16 (V and the upstream gradient dO in the QK
+ *   layout too, not VT). o: the forward's output in tiled rows, BF16 (o_dtype =
+ *   FPSA_BF16) or its float32 copy o_f32 (o_dtype = FPSA_F32, more accurate delta).
+ *   lse: the forward's lse [B, H, Npad] (natural log). row_ptr / col_idx: the forward's CSR;
+ *   col_ptr / row_idx: its transpose (fpsa_csr_transpose).
+ * With p_ij = exp(softmax_scale q_i.k_j - lse_i) over the kept keys j of query i
+ * and delta_i = dO_i.o_i:
+ *   dv_j = sum_i p_ij dO_i,  ds_ij = p_ij (dO_i.v_j - delta_i),
+ *   dk_j = softmax_scale sum_i ds_ij q_i,  dq_i = softmax_scale sum_j ds_ij k_j,
+ * products in BF16 with float32 accumulation (p and ds are rounded to BF16 for the
+ * matrix products). Padding rows and queries whose lse is -inf contribute nothing
+ * and get zero gradients; so do key blocks no row keeps.
+ * dq, dk, dv: tiled rows BF16 [B, H, Npad, D], fully written.
+ * workspace_bytes >= fpsa_bwd_workspace_bytes(B, H, g) (two floats per query slot).
+ * Deterministic: no atomics, fixed summation order.
+ */
+int32_t fpsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                             int32_t o_dtype, const void* dout, const float* lse, const int32_t* row_ptr,
+                             const int32_t* col_idx, const int32_t* col_ptr,
+                             const int32_t* row_idx, int32_t B, int32_t H, int32_t D,
+                             const fpsa_grid* g, float softmax_scale, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for fpsa_sparse_attn_bwd (B*H*Npad*8); 0 for an invalid grid.
+   Host-only. */
+size_t fpsa_bwd_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g);
 
 #ifdef __cplusplus
 }

@@ -86,10 +86,10 @@ def lib():
             L.orc_pattern_mask.restype = ctypes.c_int64
             L.orc_masked_attention_bwd.restype = None
             L.orc_masked_attention_bwd.argtypes = [_f32p] * 4 + [ctypes.c_int] * 4 + [
-                _i32p, ctypes.c_int, ctypes.c_double, _i32p, _i32p, _f64p, _f64p, _f64p]
+                _i32p, ctypes.c_int, ctypes.c_double, _i32p, _i32p, _f64p, _f64p, _f64p, _vp, _vp, _vp]
             L.orc_masked_attention_bwd_dq.restype = None
             L.orc_masked_attention_bwd_dq.argtypes = [_f32p] * 4 + [ctypes.c_int] * 4 + [
-                _i32p, ctypes.c_int, ctypes.c_double, _i32p, _i32p, _i32p, ctypes.c_int, _f64p, _i32p]
+                _i32p, ctypes.c_int, ctypes.c_double, _i32p, _i32p, _i32p, ctypes.c_int, _f64p, _vp, _i32p]
             L.orc_csr_transpose.restype = ctypes.c_int64
             L.orc_csr_transpose.argtypes = [_i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p]
             L.orc_pattern_mask.argtypes = [ctypes.c_int] * 3 + [_i32p, _i32p, _i32p]
@@ -274,34 +274,41 @@ def pattern_mask(nb, B, H, patterns):
 
 # --------------------------------------------------------------------------- backward
 
-def masked_attention_bwd(q, k, v, dout, grid, tile, scale, row_ptr, col_idx):
+def masked_attention_bwd(q, k, v, dout, grid, tile, scale, row_ptr, col_idx, magnitudes=False):
     """(dq, dk, dv), raster [B, N, H, D] float64: gradients of masked attention for
-    the upstream gradient dout."""
+    the upstream gradient dout; with magnitudes=True also (mq, mk, mv), the sums of
+    the absolute values of the terms of each gradient element."""
     q, k, v, g = (_c(x, np.float32) for x in (q, k, v, dout))
     B, N, H, D = q.shape
     blk, _ = token_blocks(grid, tile)
     nb = num_blocks(grid, tile)
-    dq, dk, dv = (np.empty((B, N, H, D), np.float64) for _ in range(3))
+    n = 6 if magnitudes else 3
+    arrs = [np.empty((B, N, H, D), np.float64) for _ in range(n)]
+    ptrs = [a.ctypes.data for a in arrs[3:]] if magnitudes else [None, None, None]
     ci = _c(col_idx, np.int32) if len(col_idx) else np.zeros(1, np.int32)
     lib().orc_masked_attention_bwd(q, k, v, g, B, N, H, D, blk, nb, float(scale),
-                                   _c(row_ptr, np.int32), ci, dq, dk, dv)
-    return dq, dk, dv
+                                   _c(row_ptr, np.int32), ci, arrs[0], arrs[1], arrs[2], *ptrs)
+    return tuple(arrs)
 
 
-def masked_attention_bwd_dq(q, k, v, dout, grid, tile, scale, row_ptr, col_idx, qblocks):
+def masked_attention_bwd_dq(q, k, v, dout, grid, tile, scale, row_ptr, col_idx, qblocks,
+                            magnitudes=False):
     """(dq [B, H, nsel, 64, D] float64, token_of [B, H, nsel, 64]) for the listed
-    query blocks, rows ordered as in masked_attention."""
+    query blocks, rows ordered as in masked_attention; with magnitudes=True,
+    (dq, mq, token_of)."""
     q, k, v, g = (_c(x, np.float32) for x in (q, k, v, dout))
     B, N, H, D = q.shape
     blk, _ = token_blocks(grid, tile)
     nb = num_blocks(grid, tile)
     qb = _c(qblocks, np.int32)
     dq = np.empty((B, H, len(qb), 64, D), np.float64)
+    mq = np.empty_like(dq) if magnitudes else None
     tok = np.empty((B, H, len(qb), 64), np.int32)
     ci = _c(col_idx, np.int32) if len(col_idx) else np.zeros(1, np.int32)
     lib().orc_masked_attention_bwd_dq(q, k, v, g, B, N, H, D, blk, nb, float(scale),
-                                      _c(row_ptr, np.int32), ci, qb, len(qb), dq, tok)
-    return dq, tok
+                                      _c(row_ptr, np.int32), ci, qb, len(qb), dq,
+                                      mq.ctypes.data if magnitudes else None, tok)
+    return (dq, mq, tok) if magnitudes else (dq, tok)
 
 
 def csr_transpose(row_ptr, col_idx, B, H, nb):

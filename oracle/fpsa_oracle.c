@@ -544,10 +544,13 @@ int64_t orc_pattern_mask(int nb, int B, int H, const int32_t* pattern, int32_t* 
 static void bwd_one_query(const float* q, const float* k, const float* v, const float* dout,
                           int N, int H, int D, int b, int h, int i, const int32_t* block_of,
                           const char* allowed, double scale, double* s, double* dp,
-                          double* dq_row, double* dk, double* dv) {
+                          double* dq_row, double* dk, double* dv, double* mq_row, double* mk,
+                          double* mv) {
     const float* qi = q + RIX(b, i, h, 0);
     const float* gi = dout + RIX(b, i, h, 0);
     for (int d = 0; d < D; ++d) dq_row[d] = 0.0;
+    if (mq_row)
+        for (int d = 0; d < D; ++d) mq_row[d] = 0.0;
     double m = -INFINITY;
     for (int j = 0; j < N; ++j) {
         if (!allowed[block_of[j]]) continue;
@@ -568,9 +571,21 @@ static void bwd_one_query(const float* q, const float* k, const float* v, const 
         dp[j] = acc;
         delta += s[j] * acc;
     }
+    /* a_i = sum_d |dout_id| sum_j p_ij |v_jd|: how far rounding the output o_i (or
+       the probabilities forming it) can move delta_i, per unit of relative error */
+    double a_i = 0.0;
+    if (mq_row) {
+        for (int d = 0; d < D; ++d) {
+            double w = 0.0;
+            for (int j = 0; j < N; ++j)
+                if (allowed[block_of[j]]) w += s[j] * fabs((double)v[RIX(b, j, h, d)]);
+            a_i += fabs((double)gi[d]) * w;
+        }
+    }
     for (int j = 0; j < N; ++j) {
         if (!allowed[block_of[j]]) continue;
         const double p = s[j], ds = p * (dp[j] - delta);
+        const double mag = fabs(ds) + 0.25 * p * a_i;
         const float* kj = k + RIX(b, j, h, 0);
         for (int d = 0; d < D; ++d) dq_row[d] += scale * ds * (double)kj[d];
         if (dk) {
@@ -581,17 +596,41 @@ static void bwd_one_query(const float* q, const float* k, const float* v, const 
                 dvj[d] += p * (double)gi[d];
             }
         }
+        if (mq_row) {
+            for (int d = 0; d < D; ++d) mq_row[d] += scale * mag * fabs((double)kj[d]);
+            if (mk) {
+                double* mkj = mk + RIX(b, j, h, 0);
+                double* mvj = mv + RIX(b, j, h, 0);
+                for (int d = 0; d < D; ++d) {
+                    mkj[d] += scale * mag * fabs((double)qi[d]);
+                    mvj[d] += p * fabs((double)gi[d]);
+                }
+            }
+        }
     }
 }
 
-/* Full gradients, raster [B, N, H, D] float64 each. */
+/*
+ * Full gradients, raster [B, N, H, D] float64 each. When mq is given, mq / mk / mv
+ * receive magnitude sums that bound each gradient element and scale how far
+ * rounding can move it: with delta_i = sum_j p_ij dp_ij, a_i = sum_d |dout_id|
+ * sum_j p_ij |v_jd| (rounding the probabilities that form o_i, or o_i itself, by a
+ * relative eps moves delta_i by at most about eps a_i) and m_ij = |ds_ij| +
+ * p_ij a_i / 4, mq = scale sum_j m_ij |k_jd|, mk = scale sum_i m_ij |q_id| and
+ * mv = sum_i p_ij |dout_id|.
+ */
 void orc_masked_attention_bwd(const float* q, const float* k, const float* v, const float* dout,
                               int B, int N, int H, int D, const int32_t* block_of, int nb,
                               double scale, const int32_t* row_ptr, const int32_t* col_idx,
-                              double* dq, double* dk, double* dv) {
+                              double* dq, double* dk, double* dv, double* mq, double* mk,
+                              double* mv) {
     memset(dq, 0, sizeof(double) * (size_t)B * N * H * D);
     memset(dk, 0, sizeof(double) * (size_t)B * N * H * D);
     memset(dv, 0, sizeof(double) * (size_t)B * N * H * D);
+    if (mq) {
+        memset(mk, 0, sizeof(double) * (size_t)B * N * H * D);
+        memset(mv, 0, sizeof(double) * (size_t)B * N * H * D);
+    }
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < H; ++h) {
@@ -604,7 +643,8 @@ void orc_masked_attention_bwd(const float* q, const float* k, const float* v, co
                 for (int32_t e = row_ptr[row]; e < row_ptr[row + 1]; ++e)
                     if (col_idx[e] >= 0 && col_idx[e] < nb) allowed[col_idx[e]] = 1;
                 bwd_one_query(q, k, v, dout, N, H, D, b, h, i, block_of, allowed, scale, s, dp,
-                              dq + RIX(b, i, h, 0), dk, dv);
+                              dq + RIX(b, i, h, 0), dk, dv, mq ? mq + RIX(b, i, h, 0) : NULL, mk,
+                              mv);
             }
             free(dp);
             free(s);
@@ -615,13 +655,14 @@ void orc_masked_attention_bwd(const float* q, const float* k, const float* v, co
 /*
  * Query gradients only, for the requested query blocks (the key gradients of a
  * block need every query that keeps it, so sampled checks take dq). Layout as in
- * orc_masked_attention: dq_out [B, H, nsel, 64, D], token_of [B, H, nsel, 64].
+ * orc_masked_attention: dq_out [B, H, nsel, 64, D], token_of [B, H, nsel, 64];
+ * mq_out (optional, same layout) receives the term magnitudes as above.
  */
 void orc_masked_attention_bwd_dq(const float* q, const float* k, const float* v, const float* dout,
                                  int B, int N, int H, int D, const int32_t* block_of, int nb,
                                  double scale, const int32_t* row_ptr, const int32_t* col_idx,
                                  const int32_t* qblocks, int nsel, double* dq_out,
-                                 int32_t* token_of) {
+                                 double* mq_out, int32_t* token_of) {
 #pragma omp parallel for collapse(3) schedule(dynamic)
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < H; ++h)
@@ -637,13 +678,16 @@ void orc_masked_attention_bwd_dq(const float* q, const float* k, const float* v,
                 for (int e = 0; e < 64; ++e) {
                     token_of[base + e] = -1;
                     for (int d = 0; d < D; ++d) dq_out[(base + e) * D + d] = 0.0;
+                    if (mq_out)
+                        for (int d = 0; d < D; ++d) mq_out[(base + e) * D + d] = 0.0;
                 }
                 int e = 0;
                 for (int i = 0; i < N && e < 64; ++i) {
                     if (block_of[i] != qb) continue;
                     token_of[base + e] = i;
                     bwd_one_query(q, k, v, dout, N, H, D, b, h, i, block_of, allowed, scale, s, dp,
-                                  dq_out + (base + e) * D, NULL, NULL);
+                                  dq_out + (base + e) * D, NULL, NULL,
+                                  mq_out ? mq_out + (base + e) * D : NULL, NULL, NULL);
                     e++;
                 }
                 free(dp);

@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_the_expected_calls():
     names = declared_functions()
     for n in ["fpsa_tile_reorder", "fpsa_block_mass", "fpsa_select_blocks", "fpsa_sparse_attn_fwd",
+              "fpsa_pattern_mask", "fpsa_retained_mass", "fpsa_csr_transpose", "fpsa_sparse_attn_bwd",
               "fpsa_structured_mask", "fpsa_num_blocks", "fpsa_status_string",
               "fpsa_select_workspace_bytes", "fpsa_version"]:
         assert n in names
@@ -145,14 +146,14 @@ def test_structured_mask_validation(L):
 def test_sparse_attn_validation(L):
     f = L.fpsa_sparse_attn_fwd
     g = grid()
-    assert f(None, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, fpsa.BF16, FAKE, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, fpsa.FP8_E4M3, None, FAKE, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, fpsa.F32, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
-    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, None, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 80, g, 0.125, FAKE, None, None) == fpsa.ERR_UNSUPPORTED
-    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, -1.0, FAKE, None, None) == fpsa.ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, None, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(None, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, FAKE, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.FP8_E4M3, None, FAKE, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.F32, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, None, FAKE, 1, 1, 64, g, 0.125, FAKE, None, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 80, g, 0.125, FAKE, None, None, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, -1.0, FAKE, None, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, None, None, None, None) == fpsa.ERR_INVALID_ARG
 
 
 def test_pattern_mask_validation(L):
@@ -176,3 +177,42 @@ def test_retained_mass_validation(L):
     assert f(FAKE, (1 << 24) + 1, 8, FAKE, FAKE, FAKE, None) == fpsa.ERR_INVALID_ARG
     assert f(FAKE, 10, 0, FAKE, FAKE, FAKE, None) == fpsa.ERR_INVALID_ARG
     assert f(FAKE, 10, 4097, FAKE, FAKE, FAKE, None) == fpsa.ERR_UNSUPPORTED
+
+
+def test_csr_transpose_validation(L):
+    f = L.fpsa_csr_transpose
+    ws = fpsa.transpose_workspace_bytes(2 * 3 * 4, 4)
+    assert ws >= 24 * 4 and fpsa.transpose_workspace_bytes(0, 4) == 0
+    cap = 2 * 3 * 4 * 4
+    assert f(None, FAKE, 2, 3, 4, FAKE, FAKE, cap, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 2, 3, 4, None, FAKE, cap, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 0, 3, 4, FAKE, FAKE, cap, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 2, 3, 0, FAKE, FAKE, cap, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 2, 3, 4, FAKE, FAKE, cap - 1, FAKE, ws, None) == fpsa.ERR_CAPACITY
+    assert f(FAKE, FAKE, 2, 3, 4, FAKE, FAKE, cap, FAKE, ws - 1, None) == fpsa.ERR_CAPACITY
+    assert f(FAKE, FAKE, 2, 3, 4, FAKE, FAKE, cap, None, ws, None) == fpsa.ERR_INVALID_ARG
+
+
+def test_sparse_attn_bwd_validation(L):
+    f = L.fpsa_sparse_attn_bwd
+    g = grid()
+    ws = fpsa.bwd_workspace_bytes(1, 2, (4, 8, 8), (4, 4, 4))
+    assert ws == 2 * 2 * 4 * 64 * 4
+    assert fpsa.bwd_workspace_bytes(1, 2, (4, 8, 8), (4, 4, 2)) == 0
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, odt=fpsa.BF16, g_=FAKE, lse=FAKE, rp=FAKE, ci=FAKE, cp=FAKE, ri=FAKE,
+                 B=1, H=2, D=128, grid=g, sc=0.1, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["odt"], a["g_"], a["lse"], a["rp"], a["ci"], a["cp"], a["ri"], a["B"], a["H"],
+                 a["D"], a["grid"], a["sc"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], None)
+
+    for name in ("q", "k", "v", "o", "g_", "lse", "rp", "ci", "cp", "ri", "dq", "dk", "dv", "ws"):
+        assert call(**{name: None}) == fpsa.ERR_INVALID_ARG, name
+    assert call(grid=grid(tw=2)) == fpsa.ERR_INVALID_ARG
+    assert call(B=0) == fpsa.ERR_INVALID_ARG
+    assert call(sc=0.0) == fpsa.ERR_INVALID_ARG
+    assert call(sc=float("inf")) == fpsa.ERR_INVALID_ARG
+    assert call(D=96) == fpsa.ERR_UNSUPPORTED
+    assert call(odt=fpsa.FP8_E4M3) == fpsa.ERR_UNSUPPORTED
+    assert call(wsb=ws - 1) == fpsa.ERR_CAPACITY

@@ -580,3 +580,25 @@ def test_csr_transpose_hand_example_and_round_trip():
     # out-of-range entries dropped, repeats collapse
     cp, ri = O.csr_transpose(np.array([0, 4, 4], np.int32), np.array([1, 1, -1, 5], np.int32), 1, 1, 2)
     assert _csr_rows(cp, ri) == [[], [0]]
+
+
+def test_backward_term_magnitudes():
+    # triangle inequality everywhere; equality for dv when every upstream gradient is
+    # non-negative (all its terms p_ij dout_i share a sign)
+    grid, tile, H, D = (5, 6, 7), (4, 4, 4), 2, 16
+    nb = O.num_blocks(grid, tile)
+    q, k, v = _rand_qkv(1, 210, H, D, 47)
+    g = np.abs(_rand_qkv(1, 210, H, D, 48)[0])
+    rp, ci = O.select_blocks(synth.random_mass_rows(H * nb, nb, seed=7), 9, 10)
+    dq, dk, dv, mq, mk, mv = O.masked_attention_bwd(q, k, v, g, grid, tile, 0.25, rp, ci, magnitudes=True)
+    dq2, dk2, dv2 = O.masked_attention_bwd(q, k, v, g, grid, tile, 0.25, rp, ci)
+    assert np.array_equal(dq, dq2) and np.array_equal(dk, dk2) and np.array_equal(dv, dv2)
+    for a, m in ((dq, mq), (dk, mk), (dv, mv)):
+        assert np.all(np.abs(a) <= m * (1 + 1e-12) + 1e-300)
+    assert np.abs(dv - mv).max() < 1e-12
+    sel = [1, nb - 1]
+    dqs, mqs, tok = O.masked_attention_bwd_dq(q, k, v, g, grid, tile, 0.25, rp, ci, sel, magnitudes=True)
+    for h in range(H):
+        for r in range(len(sel)):
+            t = tok[0, h, r][tok[0, h, r] >= 0]
+            assert np.array_equal(mqs[0, h, r, :len(t)], mq[0, t, h])
