@@ -254,6 +254,24 @@ def next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, reps):
     pnnz = int(pcsr.row_ptr[-1].item())
     t_pf = _timed(lambda: bsa.forward(qt, kt, vt, pcsr, out=ot), stream, reps)
     pflop = pnnz * 4.0 * 64 * 64 * w.D
+    # backward over the step's CSR: delta/lse preprocessing, dK/dV per key block,
+    # dQ per query block; the transpose is built once per frozen CSR (timed apart)
+    lse = torch.empty((w.B, w.H, bsa.npad), dtype=torch.float32, device=qt.device)
+    o32 = torch.empty(bsa.tiled_shape(), dtype=torch.float32, device=qt.device)
+    bsa.forward(qt, kt, vt, csr, out=ot, lse=lse, out_f32=o32)
+    vq = torch.empty_like(qt)
+    gt = torch.empty_like(qt)
+    gen = torch.Generator(device=qt.device)
+    gen.manual_seed(7)
+    vq.copy_(torch.randn(qt.shape, generator=gen, device=qt.device, dtype=torch.float32))
+    gt.copy_(torch.randn(qt.shape, generator=gen, device=qt.device, dtype=torch.float32))
+    csc = bsa.transpose(csr)
+    t_tr = _timed(lambda: bsa.transpose(csr), stream, reps)
+    grads = tuple(torch.empty_like(qt) for _ in range(3))
+    bws = torch.empty(fpsa.bwd_workspace_bytes(w.B, w.H, w.grid, w.tile), dtype=torch.uint8, device=qt.device)
+    t_bwd = _timed(lambda: bsa.backward(qt, kt, vq, o32, gt, lse, csr, csc, grads=grads, workspace=bws),
+                   stream, reps)
+    bflop = nnz * 10.0 * 64 * 64 * w.D          # five 64x64xD products per kept pair
     return {
         "retained_mass": {"ms": round(t_mon, 4), "bound": "hbm",
                           "achieved_GBps": round(mon_bytes / t_mon / 1e6, 1),
@@ -265,6 +283,12 @@ def next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, reps):
                          "kept_pairs": pnnz, "density": round(pnnz / (bsa.R * bsa.nb), 4),
                          "fwd_ms": round(t_pf, 4), "fwd_kept_tflops": round(pflop / t_pf / 1e9, 2),
                          "fwd_frac_of_bf16_peak": round(pflop / t_pf / 1e9 / PEAK["bf16"], 4)},
+        "backward": {"ms": round(t_bwd, 4), "kept_pairs": nnz,
+                     "work_per_unit": "10*64*64*D FLOP per kept pair (QK^T, dO V^T, P^T dO, dS^T Q, dS K)",
+                     "tflops": round(bflop / t_bwd / 1e9, 2),
+                     "frac_of_bf16_peak": round(bflop / t_bwd / 1e9 / PEAK["bf16"], 4),
+                     "transpose_ms": round(t_tr, 4),
+                     "inputs": "Q, K from the step; V (QK layout) and dO random normal bf16"},
     }
 
 

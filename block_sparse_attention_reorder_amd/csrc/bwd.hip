@@ -56,6 +56,18 @@ __device__ inline bf16x8 tr_operand(const uint8_t* tile, int off) {
     return __builtin_bit_cast(bf16x8, z);
 }
 
+// Fragments loaded once and reused for every block: an empty asm that rewrites each
+// register keeps the compiler from re-issuing the global loads inside the loop.
+template <int D>
+__device__ __attribute__((always_inline)) inline void keep_resident(KHalf<D, false>& x) {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+        i32x4 r = __builtin_bit_cast(i32x4, x.b[st]);
+        asm volatile("" : "+v"(r));
+        x.b[st] = __builtin_bit_cast(bf16x8, r);
+    }
+}
+
 // ---------------------------------------------------------------- preprocessing
 
 template <int D, class OT>
@@ -111,6 +123,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     KHalf<D, false> kf, vf;                        // B operands: key (lane % 32) of half kh
     load_khalf<D, false>(kf, k, col * 64, kh, lane);
     load_khalf<D, false>(vf, v, col * 64, kh, lane);
+    keep_resident<D>(kf);
+    keep_resident<D>(vf);
     const bool kvalid = g.valid(kb, 32 * kh + (lane & 31));
     const int trb = tr_base<D>(32 * qh, lane);
 
@@ -162,30 +176,55 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
             const uint8_t* sq = lds + (j & 1) * kSlot;
             const uint8_t* sg = sq + kTile;
             const float* sl = reinterpret_cast<const float*>(sq + 2 * kTile);
+            // operand reads first (the S and dP products then issue back to back)
+            bf16x8 qa[D / 16], ga[D / 16];
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                const int off = (qh * (D / 16) + st) * 1024 + 16 * lane;
+                qa[st] = *reinterpret_cast<const bf16x8*>(sq + off);
+                ga[st] = *reinterpret_cast<const bf16x8*>(sg + off);
+            }
+            // lse2 and delta of the rows this lane holds: queries 32*qh + 16*ks +
+            // 8*u + 4*hb + (0..3)
+            f32x4 L[2][2], G[2][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    L[ks][u] = *reinterpret_cast<const f32x4*>(sl + 32 * qh + 16 * ks + 8 * u + 4 * hb);
+                    G[ks][u] = *reinterpret_cast<const f32x4*>(sl + 64 + 32 * qh + 16 * ks + 8 * u + 4 * hb);
+                }
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 s, dp;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
 #pragma unroll
             for (int st = 0; st < D / 16; ++st) {
-                const int off = (qh * (D / 16) + st) * 1024 + 16 * lane;
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sq + off),
-                                                            kf.b[st], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sg + off),
-                                                             vf.b[st], dp, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kf.b[st], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[st], vf.b[st], dp, 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            // transposed operands of the two token-reduction products, read while the
+            // products above drain
+            bf16x8 gtr[2][kDT], qtr[2][kDT];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int t = 0; t < kDT; ++t) {
+                    const int off = trb + t * 2048 + ks * 256;
+                    gtr[ks][t] = tr_operand(sg, off);
+                    qtr[ks][t] = tr_operand(sq, off);
+                }
+            __builtin_amdgcn_sched_barrier(0);
             // element i: query 32*qh + 8*(i/4) + 4*hb + i%4, key 32*kh + lane%32
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 L0 = *reinterpret_cast<const f32x4*>(sl + 32 * qh + 16 * ks + 4 * hb);
-                const f32x4 L1 = *reinterpret_cast<const f32x4*>(sl + 32 * qh + 16 * ks + 8 + 4 * hb);
-                const f32x4 G0 = *reinterpret_cast<const f32x4*>(sl + 64 + 32 * qh + 16 * ks + 4 * hb);
-                const f32x4 G1 = *reinterpret_cast<const f32x4*>(sl + 64 + 32 * qh + 16 * ks + 8 + 4 * hb);
                 float p[8], ds[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const int i = 8 * ks + t;
-                    const float lq = t < 4 ? L0[t] : L1[t - 4];
-                    const float gq = t < 4 ? G0[t] : G1[t - 4];
+                    const float lq = L[ks][t >> 2][t & 3];
+                    const float gq = G[ks][t >> 2][t & 3];
                     const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq)) : 0.0f;
                     p[t] = pp;
                     ds[t] = pp * (dp[i] - gq);
@@ -194,9 +233,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
                 const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
 #pragma unroll
                 for (int t = 0; t < kDT; ++t) {
-                    const int off = trb + t * 2048 + ks * 256;
-                    accv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_operand(sg, off), accv[t], 0, 0, 0);
-                    acck[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(sq, off), acck[t], 0, 0, 0);
+                    accv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, gtr[ks][t], accv[t], 0, 0, 0);
+                    acck[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qtr[ks][t], acck[t], 0, 0, 0);
                 }
             }
         }
@@ -255,6 +293,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
     KHalf<D, false> qf, gf;                        // B operands: query (lane % 32) of half qh
     load_khalf<D, false>(qf, q, row * 64, qh, lane);
     load_khalf<D, false>(gf, dout, row * 64, qh, lane);
+    keep_resident<D>(qf);
+    keep_resident<D>(gf);
     const float lq = lse2[row * 64 + 32 * qh + (lane & 31)];
     const float gq = delta[row * 64 + 32 * qh + (lane & 31)];
     const int trb = tr_base<D>(32 * kh, lane);
@@ -303,17 +343,29 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
             const int code = icur >> kEdgeShift;
             const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
             const uint32_t m32 = (uint32_t)(vm >> (32 * kh + 4 * hb));
+            bf16x8 ka[D / 16], va[D / 16];
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                const int off = (kh * (D / 16) + st) * 1024 + 16 * lane;
+                ka[st] = *reinterpret_cast<const bf16x8*>(sk + off);
+                va[st] = *reinterpret_cast<const bf16x8*>(sv + off);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 s, dp;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
 #pragma unroll
             for (int st = 0; st < D / 16; ++st) {
-                const int off = (kh * (D / 16) + st) * 1024 + 16 * lane;
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sk + off),
-                                                            qf.b[st], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(sv + off),
-                                                             gf.b[st], dp, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf.b[st], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st], gf.b[st], dp, 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 ktr[2][kDT];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int t = 0; t < kDT; ++t) ktr[ks][t] = tr_operand(sk, trb + t * 2048 + ks * 256);
+            __builtin_amdgcn_sched_barrier(0);
             // element i: key 32*kh + 8*(i/4) + 4*hb + i%4, query 32*qh + lane%32
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -328,8 +380,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
                 const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
 #pragma unroll
                 for (int t = 0; t < kDT; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(sk, trb + t * 2048 + ks * 256),
-                                                                     acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, ktr[ks][t], acc[t], 0, 0, 0);
             }
         }
         if (inext >= 0) stash((j + 1) & 1);
