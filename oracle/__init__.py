@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY. Only ``tests/``, the smoke check and the benchmark's
 CPU-baseline leg import this package; the product path never does. It shares no
 code with the HIP library: geometry, masses, selection, masked attention, FP8
 quantization, the structured mask, the retained-mass monitor, the fixed
-diagonal / multi-diagonal / stripe patterns, the gradients of masked attention and the
-block-CSR transpose are each written here from their definitions
+diagonal / multi-diagonal / stripe patterns, the gradients of masked attention, the
+block-CSR transpose and the k-means semantic permutation (clusters, layout, cluster
+masses, cluster attention) are each written here from their definitions
 (``fpsa_oracle.c``), over raster-ordered tokens.
 
 Parity pins (tests/test_oracle_pins.py) tie each function to something other than
@@ -91,6 +92,18 @@ def lib():
             L.orc_masked_attention_bwd_dq.argtypes = [_f32p] * 4 + [ctypes.c_int] * 4 + [
                 _i32p, ctypes.c_int, ctypes.c_double, _i32p, _i32p, _i32p, ctypes.c_int, _f64p, _vp, _i32p]
             L.orc_csr_transpose.restype = ctypes.c_int64
+            L.orc_kmeans.restype = None
+            L.orc_kmeans.argtypes = [_f32p] + [ctypes.c_int] * 6 + [_i32p, _f64p, _i32p]
+            L.orc_cluster_layout.restype = ctypes.c_int
+            L.orc_cluster_layout.argtypes = [_i32p] + [ctypes.c_int] * 5 + [_i32p, _i32p, _i32p]
+            L.orc_cluster_mass.restype = None
+            L.orc_cluster_mass.argtypes = [_f64p, _i32p, _f64p, _i32p] + [ctypes.c_int] * 5 + [ctypes.c_double, _f64p]
+            L.orc_cluster_blocks.restype = ctypes.c_int64
+            L.orc_cluster_blocks.argtypes = [_i32p] * 4 + [ctypes.c_int] * 5 + [_i32p, _i32p]
+            L.orc_cluster_attention.restype = None
+            L.orc_cluster_attention.argtypes = [_f32p] * 3 + [ctypes.c_int] * 4 + [_i32p, _i32p, ctypes.c_int,
+                                                                                    ctypes.c_int, ctypes.c_double,
+                                                                                    _i32p, _i32p, _f64p]
             L.orc_csr_transpose.argtypes = [_i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p]
             L.orc_pattern_mask.argtypes = [ctypes.c_int] * 3 + [_i32p, _i32p, _i32p]
             _lib = L
@@ -319,3 +332,68 @@ def csr_transpose(row_ptr, col_idx, B, H, nb):
     ci = _c(col_idx, np.int32) if len(col_idx) else np.zeros(1, np.int32)
     nnz = lib().orc_csr_transpose(_c(row_ptr, np.int32), ci, B, H, nb, col_ptr, row_idx)
     return col_ptr, row_idx[:nnz].copy()
+
+
+# --------------------------------------------------------------------------- k-means permutation
+
+def kmeans(x, C, iters):
+    """(assign [B, H, N] int32, centroids [B, H, C, D] float64, counts [B, H, C]) of
+    Lloyd's k-means per (b, h) over x [B, N, H, D]."""
+    x = _c(x, np.float32)
+    B, N, H, D = x.shape
+    assign = np.zeros((B, H, N), np.int32)
+    cent = np.zeros((B, H, C, D), np.float64)
+    count = np.zeros((B, H, C), np.int32)
+    lib().orc_kmeans(x, B, N, H, D, int(C), int(iters), assign, cent, count)
+    return assign, cent, count
+
+
+def blocks_for(N, C):
+    """Blocks per head that any clustering of N tokens into C clusters fits in."""
+    return -(-N // 64) + C
+
+
+def cluster_layout(assign, C, NB):
+    """(slot_token [B, H, NB*64], off [B, H, C+1], blk_count [B, H, NB])."""
+    a = _c(assign, np.int32)
+    B, H, N = a.shape
+    st = np.zeros((B, H, NB * 64), np.int32)
+    off = np.zeros((B, H, C + 1), np.int32)
+    bc = np.zeros((B, H, NB), np.int32)
+    if lib().orc_cluster_layout(a, B, H, N, int(C), int(NB), st, off, bc) != 0:
+        raise ValueError("clusters need more than NB blocks")
+    return st, off, bc
+
+
+def cluster_mass(cq, nq, ck, nk, scale):
+    """est [B, H, Cq, Ck] float64 from centroids and cluster sizes."""
+    cq, ck = _c(cq, np.float64), _c(ck, np.float64)
+    B, H, Cq, D = cq.shape
+    Ck = ck.shape[2]
+    est = np.zeros((B, H, Cq, Ck), np.float64)
+    lib().orc_cluster_mass(cq, _c(nq, np.int32), ck, _c(nk, np.int32), B, H, Cq, Ck, D, float(scale), est)
+    return est
+
+
+def cluster_blocks(crow_ptr, ccol_idx, qoff, koff, NB):
+    """Block CSR (row_ptr [B*H*NB + 1], col_idx) of a cluster CSR."""
+    qoff, koff = _c(qoff, np.int32), _c(koff, np.int32)
+    B, H, Cq1 = qoff.shape
+    Ck = koff.shape[2] - 1
+    row_ptr = np.zeros(B * H * NB + 1, np.int32)
+    col_idx = np.zeros(max(B * H * NB * NB, 1), np.int32)
+    ci = _c(ccol_idx, np.int32) if len(ccol_idx) else np.zeros(1, np.int32)
+    nnz = lib().orc_cluster_blocks(_c(crow_ptr, np.int32), ci, qoff, koff, B, H, Cq1 - 1, Ck, int(NB),
+                                   row_ptr, col_idx)
+    return row_ptr, col_idx[:nnz].copy()
+
+
+def cluster_attention(q, k, v, qassign, kassign, Cq, Ck, scale, crow_ptr, ccol_idx):
+    """Raster output [B, N, H, D] float64 of attention under a cluster selection."""
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    B, N, H, D = q.shape
+    out = np.zeros((B, N, H, D), np.float64)
+    ci = _c(ccol_idx, np.int32) if len(ccol_idx) else np.zeros(1, np.int32)
+    lib().orc_cluster_attention(q, k, v, B, N, H, D, _c(qassign, np.int32), _c(kassign, np.int32), int(Cq),
+                                int(Ck), float(scale), _c(crow_ptr, np.int32), ci, out)
+    return out

@@ -723,3 +723,217 @@ int64_t orc_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int B,
     free(keep);
     return nnz;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Semantic (k-means) permutation                                             */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Tokens clustered by the similarity of their own vectors and reordered so that each
+ * cluster is contiguous, which both sharpens the cluster representation used to find
+ * the critical tokens and packs those tokens densely for the kernel [Sparse
+ * VideoGen2: Accelerate Video Generation with Sparse Attention via Semantic-Aware
+ * Permutation, Abstract]. Lloyd's k-means per (b, h) over the N vectors x[b, :, h, :]:
+ *   start: centroid c = x of token floor(c N / C);
+ *   iters times: assign every token to the nearest centroid (squared Euclidean
+ *   distance summed over channels in order, ties to the lower cluster), then move
+ *   every non-empty cluster's centroid to the mean of its members (summed in token
+ *   order); an empty cluster keeps its centroid.
+ * assign [B, H, N], cent [B, H, C, D] float64, count [B, H, C]: the last assignment
+ * and the centroids and sizes that follow from it.
+ */
+static double sqdist(const float* x, int D, const double* c) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) {
+        const double t = (double)x[d] - c[d];
+        s = s + t * t;
+    }
+    return s;
+}
+
+void orc_kmeans(const float* x, int B, int N, int H, int D, int C, int iters, int32_t* assign,
+                double* cent, int32_t* count) {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const int64_t bh = (int64_t)b * H + h;
+            double* cc = cent + bh * C * D;
+            int32_t* as = assign + bh * N;
+            int32_t* cn = count + bh * C;
+            for (int c = 0; c < C; ++c) {
+                const int64_t t = (int64_t)c * N / C;
+                for (int d = 0; d < D; ++d) cc[(int64_t)c * D + d] = (double)x[RIX(b, t, h, d)];
+            }
+            for (int it = 0; it < iters; ++it) {
+                for (int n = 0; n < N; ++n) {
+                    const float* xn = x + RIX(b, n, h, 0);
+                    int best = 0;
+                    double bd = sqdist(xn, D, cc);
+                    for (int c = 1; c < C; ++c) {
+                        const double dd = sqdist(xn, D, cc + (int64_t)c * D);
+                        if (dd < bd) {
+                            bd = dd;
+                            best = c;
+                        }
+                    }
+                    as[n] = best;
+                }
+                /* member sums, each cluster's members added in token order */
+                double* sum = (double*)calloc((size_t)C * D, sizeof(double));
+                for (int c = 0; c < C; ++c) cn[c] = 0;
+                for (int n = 0; n < N; ++n) {
+                    cn[as[n]]++;
+                    double* sc = sum + (int64_t)as[n] * D;
+                    for (int d = 0; d < D; ++d) sc[d] = sc[d] + (double)x[RIX(b, n, h, d)];
+                }
+                for (int c = 0; c < C; ++c) {
+                    if (cn[c] == 0) continue;
+                    for (int d = 0; d < D; ++d) cc[(int64_t)c * D + d] = sum[(int64_t)c * D + d] / (double)cn[c];
+                }
+                free(sum);
+            }
+        }
+}
+
+/*
+ * Cluster-contiguous block layout of one (b, h): cluster c's members, in token order,
+ * fill blocks off[c] .. off[c+1]-1 (off[c+1] = off[c] + ceil(count_c / 64)), the last
+ * block of a cluster padded. slot_token [B, H, NB*64] holds each slot's token (-1 for
+ * padding), off [B, H, C+1], blk_count [B, H, NB] the real slots of each block (0 for
+ * blocks past off[C]). Returns 0, or -1 if some head needs more than NB blocks.
+ */
+int orc_cluster_layout(const int32_t* assign, int B, int H, int N, int C, int NB,
+                       int32_t* slot_token, int32_t* off, int32_t* blk_count) {
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const int32_t* as = assign + bh * N;
+        int32_t* o = off + bh * (C + 1);
+        int32_t* st = slot_token + bh * (int64_t)NB * 64;
+        int32_t* bc = blk_count + bh * NB;
+        for (int64_t e = 0; e < (int64_t)NB * 64; ++e) st[e] = -1;
+        for (int i = 0; i < NB; ++i) bc[i] = 0;
+        o[0] = 0;
+        for (int c = 0; c < C; ++c) {
+            int cnt = 0;
+            for (int n = 0; n < N; ++n)
+                if (as[n] == c) {
+                    if (o[c] * 64 + cnt >= NB * 64) return -1;
+                    st[(int64_t)o[c] * 64 + cnt] = n;
+                    cnt++;
+                }
+            o[c + 1] = o[c] + (cnt + 63) / 64;
+            if (o[c + 1] > NB) return -1;
+            for (int i = o[c]; i < o[c + 1]; ++i) bc[i] = (cnt - 64 * (i - o[c])) < 64 ? cnt - 64 * (i - o[c]) : 64;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Estimated attention mass between query cluster i and key cluster j, from the
+ * cluster representation: each key cluster stands for count_j keys at its centroid,
+ * so est[i, j] = n_j exp(scale cq_i . ck_j) / sum_j' n_j' exp(scale cq_i . ck_j') over
+ * non-empty key clusters (the dot product summed over channels in order, the
+ * exponent taken relative to the row maximum). Rows of empty query clusters are 0.
+ * est [B, H, Cq, Ck] float64.
+ */
+void orc_cluster_mass(const double* cq, const int32_t* nq, const double* ck, const int32_t* nk,
+                      int B, int H, int Cq, int Ck, int D, double scale, double* est) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
+        for (int i = 0; i < Cq; ++i) {
+            double* row = est + (bh * Cq + i) * Ck;
+            for (int j = 0; j < Ck; ++j) row[j] = 0.0;
+            if (nq[bh * Cq + i] == 0) continue;
+            const double* qi = cq + (bh * Cq + i) * D;
+            double m = -INFINITY;
+            for (int j = 0; j < Ck; ++j) {
+                if (nk[bh * Ck + j] == 0) continue;
+                const double* kj = ck + (bh * Ck + j) * D;
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) s = s + qi[d] * kj[d];
+                row[j] = scale * s;
+                if (row[j] > m) m = row[j];
+            }
+            double z = 0.0;
+            for (int j = 0; j < Ck; ++j) {
+                if (nk[bh * Ck + j] == 0) continue;
+                row[j] = (double)nk[bh * Ck + j] * exp(row[j] - m);
+                z += row[j];
+            }
+            for (int j = 0; j < Ck; ++j) row[j] = nk[bh * Ck + j] ? row[j] / z : 0.0;
+        }
+}
+
+/*
+ * Block CSR of the cluster selection: query block qb of (b, h) lies in query cluster
+ * i when qoff[i] <= qb < qoff[i+1]; it keeps every block of every key cluster j that
+ * cluster row (b*H + h)*Cq + i keeps, i.e. blocks koff[j] .. koff[j+1]-1, in the
+ * row's order. Blocks past qoff[Cq] keep nothing. Rows (b*H + h)*NB + qb. Returns nnz.
+ */
+int64_t orc_cluster_blocks(const int32_t* crow_ptr, const int32_t* ccol_idx, const int32_t* qoff,
+                           const int32_t* koff, int B, int H, int Cq, int Ck, int NB,
+                           int32_t* row_ptr, int32_t* col_idx) {
+    int64_t nnz = 0;
+    row_ptr[0] = 0;
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const int32_t* qo = qoff + bh * (Cq + 1);
+        const int32_t* ko = koff + bh * (Ck + 1);
+        for (int qb = 0; qb < NB; ++qb) {
+            int ci = -1;
+            for (int i = 0; i < Cq; ++i)
+                if (qo[i] <= qb && qb < qo[i + 1]) ci = i;
+            if (ci >= 0) {
+                const int64_t r = bh * Cq + ci;
+                for (int32_t e = crow_ptr[r]; e < crow_ptr[r + 1]; ++e) {
+                    const int j = ccol_idx[e];
+                    for (int kb = ko[j]; kb < ko[j + 1]; ++kb) col_idx[nnz++] = kb;
+                }
+            }
+            row_ptr[bh * NB + qb + 1] = (int32_t)nnz;
+        }
+    }
+    return nnz;
+}
+
+/*
+ * Attention under a cluster selection: query token n of (b, h), in query cluster
+ * qassign[n], attends to the keys whose key cluster the cluster row (b*H + h)*Cq +
+ * qassign[n] keeps, with the softmax over exactly those keys (zero output when
+ * none). out raster [B, N, H, D] float64.
+ */
+void orc_cluster_attention(const float* q, const float* k, const float* v, int B, int N, int H,
+                           int D, const int32_t* qassign, const int32_t* kassign, int Cq, int Ck,
+                           double scale, const int32_t* crow_ptr, const int32_t* ccol_idx,
+                           double* out) {
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int n = 0; n < N; ++n) {
+                const int64_t bh = (int64_t)b * H + h;
+                const int64_t r = bh * Cq + qassign[bh * N + n];
+                char* allowed = (char*)calloc((size_t)Ck, 1);
+                for (int32_t e = crow_ptr[r]; e < crow_ptr[r + 1]; ++e)
+                    if (ccol_idx[e] >= 0 && ccol_idx[e] < Ck) allowed[ccol_idx[e]] = 1;
+                double* o = out + RIX(b, n, h, 0);
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                double* s = (double*)malloc(sizeof(double) * (size_t)N);
+                double m = -INFINITY;
+                for (int j = 0; j < N; ++j) {
+                    if (!allowed[kassign[bh * N + j]]) continue;
+                    s[j] = dot_scaled(q + RIX(b, n, h, 0), k + RIX(b, j, h, 0), D, scale);
+                    if (s[j] > m) m = s[j];
+                }
+                if (m != -INFINITY) {
+                    double z = 0.0;
+                    for (int j = 0; j < N; ++j)
+                        if (allowed[kassign[bh * N + j]]) z += exp(s[j] - m);
+                    for (int j = 0; j < N; ++j) {
+                        if (!allowed[kassign[bh * N + j]]) continue;
+                        const double p = exp(s[j] - m) / z;
+                        for (int d = 0; d < D; ++d) o[d] += p * (double)v[RIX(b, j, h, d)];
+                    }
+                }
+                free(s);
+                free(allowed);
+            }
+}

@@ -602,3 +602,138 @@ def test_backward_term_magnitudes():
         for r in range(len(sel)):
             t = tok[0, h, r][tok[0, h, r] >= 0]
             assert np.array_equal(mqs[0, h, r, :len(t)], mq[0, t, h])
+
+
+# --------------------------------------------------------------------------- k-means permutation
+
+def test_kmeans_recovers_separated_blobs():
+    # C blobs of m consecutive tokens around far-apart centres: the strided start puts
+    # one centroid in each blob, so one step finds the blobs and their means
+    C, m, D, H = 6, 20, 8, 2
+    rng = np.random.default_rng(3)
+    centres = rng.standard_normal((H, C, D)) * 100
+    x = np.zeros((1, C * m, H, D), np.float32)
+    for h in range(H):
+        for c in range(C):
+            x[0, c * m:(c + 1) * m, h] = centres[h, c] + 0.01 * rng.standard_normal((m, D))
+    a, cent, cnt = O.kmeans(x, C, 1)
+    assert np.array_equal(a[0], np.tile(np.repeat(np.arange(C), m), (H, 1)))
+    assert np.all(cnt == m)
+    for h in range(H):
+        for c in range(C):
+            mean = x[0, c * m:(c + 1) * m, h].astype(np.float64).mean(axis=0)
+            assert np.abs(cent[0, h, c] - mean).max() < 1e-9
+
+
+def test_kmeans_hand_example_ties_and_empty_cluster():
+    # start: centroid 0 = token 0, centroid 1 = token 2, both equal to a: every token
+    # is equally far from both and goes to cluster 0; cluster 1 stays empty and keeps
+    # its starting point
+    a_, b_, c_ = [1.0, 2.0], [3.0, -1.0], [0.0, 5.0]
+    x = np.array([[a_, b_, a_, c_]], np.float32)[:, :, None, :]
+    asg, cent, cnt = O.kmeans(x, 2, 1)
+    assert asg[0, 0].tolist() == [0, 0, 0, 0] and cnt[0, 0].tolist() == [4, 0]
+    assert np.allclose(cent[0, 0, 0], np.mean([a_, b_, a_, c_], axis=0), atol=1e-15)
+    assert cent[0, 0, 1].tolist() == a_
+    # second step by hand: centroids (1.25, 2) and (1, 2); a is nearer the second
+    # (0 < 1/16), b the first (12.0625 < 13), c the second (10 < 10.5625)
+    asg, cent, cnt = O.kmeans(x, 2, 2)
+    assert asg[0, 0].tolist() == [1, 0, 1, 1] and cnt[0, 0].tolist() == [1, 3]
+    assert cent[0, 0, 0].tolist() == b_
+    assert np.allclose(cent[0, 0, 1], [2.0 / 3.0, 3.0], atol=1e-15)
+
+
+def test_kmeans_lloyd_properties():
+    x = _rand_qkv(1, 300, 2, 6, 9)[0]
+    objective = []
+    for iters in range(1, 7):
+        a, cent, cnt = O.kmeans(x, 7, iters)
+        for h in range(2):
+            for c in range(7):
+                mem = np.where(a[0, h] == c)[0]
+                assert cnt[0, h, c] == len(mem)
+                if len(mem):
+                    assert np.abs(cent[0, h, c] - x[0, mem, h].astype(np.float64).mean(axis=0)).max() < 1e-12
+        objective.append(sum(np.sum((x[0, :, h].astype(np.float64) - cent[0, h][a[0, h]]) ** 2) for h in range(2)))
+    # Lloyd never increases the within-cluster sum of squares
+    assert all(objective[i + 1] <= objective[i] + 1e-9 for i in range(len(objective) - 1))
+    # after many steps the assignment is a fixed point: every token's nearest centroid
+    a, cent, _ = O.kmeans(x, 7, 60)
+    for h in range(2):
+        d = ((x[0, :, h, None, :].astype(np.float64) - cent[0, h][None]) ** 2).sum(-1)
+        assert np.array_equal(np.argmin(d, axis=1), a[0, h])
+
+
+def test_cluster_layout_closed_forms():
+    rng = np.random.default_rng(4)
+    B, H, N, C = 1, 2, 500, 9
+    assign = rng.integers(0, C, size=(B, H, N)).astype(np.int32)
+    assign[0, 1][assign[0, 1] == 4] = 5                   # an empty cluster
+    NB = O.blocks_for(N, C)
+    st, off, bc = O.cluster_layout(assign, C, NB)
+    for h in range(H):
+        cnt = np.bincount(assign[0, h], minlength=C)
+        assert np.array_equal(np.diff(off[0, h]), -(-cnt // 64))
+        for c in range(C):
+            slots = st[0, h, 64 * off[0, h, c]:64 * off[0, h, c + 1]]
+            assert np.array_equal(slots[:cnt[c]], np.where(assign[0, h] == c)[0])
+            assert np.all(slots[cnt[c]:] == -1)
+            nblk = off[0, h, c + 1] - off[0, h, c]
+            want = [64] * (nblk - 1) + ([cnt[c] - 64 * (nblk - 1)] if nblk else [])
+            assert bc[0, h, off[0, h, c]:off[0, h, c + 1]].tolist() == want
+        assert np.all(bc[0, h, off[0, h, C]:] == 0) and np.all(st[0, h, 64 * off[0, h, C]:] == -1)
+        real = st[0, h][st[0, h] >= 0]
+        assert np.array_equal(np.sort(real), np.arange(N))
+
+
+def test_cluster_mass_closed_forms():
+    rng = np.random.default_rng(5)
+    B, H, Cq, Ck, D = 1, 2, 4, 6, 8
+    cq = rng.standard_normal((B, H, Cq, D))
+    ck = rng.standard_normal((B, H, Ck, D))
+    nq = np.array([[[3, 0, 5, 1], [2, 2, 2, 2]]], np.int32)
+    nk = np.array([[[10, 0, 20, 5, 5, 60], [1, 1, 1, 1, 1, 1]]], np.int32)
+    est = O.cluster_mass(cq, nq, ck, nk, 0.5)
+    assert np.all(est[0, 0, 1] == 0)                       # empty query cluster
+    assert np.all(est[0, 0, :, 1] == 0)                    # empty key cluster
+    live = nq[0] > 0
+    assert np.abs(est[0][live].sum(-1) - 1).max() < 1e-12
+    # zero query centroids: every key cluster scores the same, so its share is its size
+    est0 = O.cluster_mass(np.zeros_like(cq), nq, ck, nk, 0.5)
+    assert np.abs(est0[0, 0, 0] - nk[0, 0] / nk[0, 0].sum()).max() < 1e-15
+    # a single query/key pair of clusters by hand
+    w = nk[0, 1] * np.exp(0.5 * (ck[0, 1] @ cq[0, 1, 2]))
+    assert abs(est[0, 1, 2, 3] - w[3] / w.sum()) < 1e-12
+
+
+def test_cluster_blocks_hand_example():
+    # one head, 2 query clusters over blocks [0, 2) and [2, 3), 3 key clusters over
+    # blocks [0, 1), [1, 1) (empty) and [1, 4); NB = 5
+    qoff = np.array([[[0, 2, 3]]], np.int32)
+    koff = np.array([[[0, 1, 1, 4]]], np.int32)
+    crow = np.array([0, 2, 3], np.int32)
+    ccol = np.array([0, 2, 1], np.int32)
+    rp, ci = O.cluster_blocks(crow, ccol, qoff, koff, 5)
+    assert _csr_rows(rp, ci) == [[0, 1, 2, 3], [0, 1, 2, 3], [], [], []]
+
+
+def test_cluster_attention_all_and_single_cluster():
+    q, k, v = _rand_qkv(1, 120, 2, 16, 12)
+    rng = np.random.default_rng(6)
+    qa = rng.integers(0, 4, size=(1, 2, 120)).astype(np.int32)
+    ka = rng.integers(0, 5, size=(1, 2, 120)).astype(np.int32)
+    # every key cluster kept: dense attention (library routine)
+    crow = np.arange(0, 2 * 4 * 5 + 1, 5, dtype=np.int32)
+    ccol = np.tile(np.arange(5, dtype=np.int32), 8)
+    out = O.cluster_attention(q, k, v, qa, ka, 4, 5, 0.25, crow, ccol)
+    assert np.abs(out - _torch_sdpa(q, k, v, 0.25)).max() < 1e-12
+    # query cluster 2 of head 1 keeps key cluster 3 only; the others keep nothing
+    crow = np.zeros(9, np.int32)
+    crow[4 + 2 + 1:] = 1
+    out = O.cluster_attention(q, k, v, qa, ka, 4, 5, 0.25, crow, np.array([3], np.int32))
+    keys = np.where(ka[0, 1] == 3)[0]
+    qs = np.where(qa[0, 1] == 2)[0]
+    ref = _torch_sdpa(q[:, qs][:, :, 1:2], k[:, keys][:, :, 1:2], v[:, keys][:, :, 1:2], 0.25)
+    assert np.abs(out[0, qs, 1] - ref[0, :, 0]).max() < 1e-12
+    others = np.setdiff1d(np.arange(120), qs)
+    assert np.all(out[0, others, 1] == 0) and np.all(out[0, :, 0] == 0)
