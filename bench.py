@@ -272,6 +272,7 @@ def next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, reps):
     t_bwd = _timed(lambda: bsa.backward(qt, kt, vq, o32, gt, lse, csr, csc, grads=grads, workspace=bws),
                    stream, reps)
     bflop = nnz * 10.0 * 64 * 64 * w.D          # five 64x64xD products per kept pair
+    sem = semantic_row(bsa, w, qt, stream, reps)
     return {
         "retained_mass": {"ms": round(t_mon, 4), "bound": "hbm",
                           "achieved_GBps": round(mon_bytes / t_mon / 1e6, 1),
@@ -289,7 +290,45 @@ def next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, reps):
                      "frac_of_bf16_peak": round(bflop / t_bwd / 1e9 / PEAK["bf16"], 4),
                      "transpose_ms": round(t_tr, 4),
                      "inputs": "Q, K from the step; V (QK layout) and dO random normal bf16"},
+        "semantic_permutation": sem,
     }
+
+
+def semantic_row(bsa, w, qt, stream, reps):
+    """k-means semantic permutation at the same shape: 128 query and 128 key clusters,
+    4 Lloyd steps, top-90 % clusters; per-stage times and the forward over the
+    cluster blocks."""
+    import torch
+    from block_sparse_attention_reorder_amd import fpsa, synth
+    from block_sparse_attention_reorder_amd.pipeline import SemanticSparseAttention
+    q, k, v = synth.make_qkv(w.grid, w.B, w.H, w.D, w.amp, w.sigma, w.seed, bf16=True)
+    qd, kd, vd = (torch.from_numpy(x).to(qt.device).to(torch.bfloat16) for x in (q, k, v))
+    ssa = SemanticSparseAttention(bsa.N, w.B, w.H, w.D, 128, 128, iters=4, device=qt.device)
+    qc, kc = ssa.cluster(qd, 128), ssa.cluster(kd, 128)
+    st = {}
+    st["kmeans_q_and_k"] = _timed(lambda: (ssa.cluster(qd, 128), ssa.cluster(kd, 128)), stream, reps)
+    st["gather_qkv"] = _timed(lambda: (ssa.gather(qd, qc, fpsa.LAYOUT_QK), ssa.gather(kd, kc, fpsa.LAYOUT_QK),
+                                       ssa.gather(vd, kc, fpsa.LAYOUT_VT)), stream, reps)
+    qt2, kt2, vt2 = ssa.gather(qd, qc, fpsa.LAYOUT_QK), ssa.gather(kd, kc, fpsa.LAYOUT_QK), ssa.gather(vd, kc, fpsa.LAYOUT_VT)
+    est = ssa.cluster_mass(qc, kc)
+    ccsr = ssa.select_clusters(est)
+    st["mass_select_blocks"] = _timed(lambda: ssa.block_csr(ssa.select_clusters(ssa.cluster_mass(qc, kc)), qc, kc),
+                                      stream, reps)
+    csr = ssa.block_csr(ccsr, qc, kc)
+    ot = torch.empty(ssa.tiled_shape(), dtype=torch.bfloat16, device=qt.device)
+    st["forward"] = _timed(lambda: ssa.forward(qt2, kt2, vt2, kc, csr, out=ot), stream, reps)
+    st["scatter"] = _timed(lambda: ssa.scatter(ot, qc), stream, reps)
+    nnz = int(csr.row_ptr[-1].item())
+    real_pairs = float((kc.blk_count.double().sum() / 64).item())
+    flop = nnz * 4.0 * 64 * 64 * w.D
+    return {"clusters": [128, 128], "kmeans_steps": 4, "top_p": "90/100",
+            "stage_ms": {kk: round(vv, 4) for kk, vv in st.items()},
+            "total_ms": round(sum(st.values()), 4),
+            "blocks_per_head": ssa.NB, "kept_pairs": nnz,
+            "density_of_padded_pairs": round(nnz / (w.B * w.H * ssa.NB * ssa.NB), 4),
+            "padding_overhead": round(w.B * w.H * ssa.NB / max(real_pairs, 1.0), 4),
+            "fwd_kept_tflops": round(flop / st["forward"] / 1e9, 2),
+            "fwd_frac_of_bf16_peak": round(flop / st["forward"] / 1e9 / PEAK["bf16"], 4)}
 
 
 def cpu_baseline(w, q, k, v, bsa, nsample):

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfpsa.so")
-SOURCES = ["api.hip", "reorder.hip", "mass.hip", "select.hip", "attn.hip", "bwd.hip"]
+SOURCES = ["api.hip", "reorder.hip", "mass.hip", "select.hip", "attn.hip", "bwd.hip", "cluster.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,8 +28,11 @@ FLAGS = [
 # The attention and mass kernels never see NaN scores (padding is -inf and every
 # -inf case is guarded), so they are built without IEEE NaN-quieting; otherwise each
 # max over MFMA results starts with a canonicalising v_max_f32 x, x, x.
+# The k-means kernels reproduce a fixed float64 operation order (no fused
+# multiply-add), so their file is built with contraction off.
 NO_NAN_SOURCES = {"attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
-                  "mass.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+                  "mass.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+                  "cluster.hip": ["-ffp-contract=off"]}
 
 
 def _compile(src: str, build_dir: str) -> str:

@@ -221,7 +221,7 @@ int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_
         return FPSA_ERR_UNSUPPORTED;
     }
     fpsa::launch_sparse_attn(q, k, v, fp8, q_scale, k_scale, row_ptr, col_idx, B, H, D, geo,
-                             softmax_scale, o, lse, o_f32, static_cast<hipStream_t>(stream));
+                             softmax_scale, o, lse, o_f32, nullptr, static_cast<hipStream_t>(stream));
     return hip_status();
 }
 
@@ -265,6 +265,117 @@ int32_t fpsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const 
     fpsa::launch_sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, B, H, D,
                                  geo, softmax_scale, o_dtype == FPSA_F32, dq, dk, dv, workspace,
                                  static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_kmeans(const void* x, int32_t x_dtype, int32_t B, int32_t N, int32_t H, int32_t D,
+                    int32_t C, int32_t iters, int32_t* assign, double* centroids, int32_t* counts,
+                    int32_t* member_off, int32_t* members, void* stream) {
+    if (x == nullptr || assign == nullptr || centroids == nullptr || counts == nullptr ||
+        member_off == nullptr || members == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (!dims_ok(B, H) || N < 1 || C < 1 || C > N || iters < 1 || iters > 1000)
+        return FPSA_ERR_INVALID_ARG;
+    if (x_dtype != FPSA_F32 && x_dtype != FPSA_BF16) return FPSA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    if (C > FPSA_MAX_SELECT_BLOCKS) return FPSA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * N > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    fpsa::launch_kmeans(x, x_dtype == FPSA_F32, B, N, H, D, C, iters, assign, centroids, counts, member_off,
+                        members, static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_cluster_layout(const int32_t* member_off, const int32_t* members, int32_t B, int32_t H,
+                            int32_t N, int32_t C, int32_t NB, int32_t* slot_token, int32_t* blk_off,
+                            int32_t* blk_count, void* stream) {
+    if (member_off == nullptr || members == nullptr || slot_token == nullptr || blk_off == nullptr ||
+        blk_count == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (!dims_ok(B, H) || N < 1 || C < 1 || C > N || NB < 1) return FPSA_ERR_INVALID_ARG;
+    if (C > FPSA_MAX_SELECT_BLOCKS) return FPSA_ERR_UNSUPPORTED;
+    if ((int64_t)NB < ((int64_t)N + 63) / 64 + C) return FPSA_ERR_CAPACITY;
+    if ((int64_t)B * H * NB * 64 > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    fpsa::launch_cluster_layout(member_off, members, B, H, C, NB, slot_token, blk_off, blk_count,
+                                static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_gather_tiles(const void* src, int32_t src_dtype, const int32_t* slot_token, int32_t B,
+                          int32_t N, int32_t H, int32_t D, int32_t NB, int32_t layout, void* dst,
+                          void* stream) {
+    if (src == nullptr || slot_token == nullptr || dst == nullptr) return FPSA_ERR_INVALID_ARG;
+    if (!dims_ok(B, H) || N < 1 || NB < 1) return FPSA_ERR_INVALID_ARG;
+    if (layout != FPSA_LAYOUT_ROWS && layout != FPSA_LAYOUT_VT && layout != FPSA_LAYOUT_QK)
+        return FPSA_ERR_INVALID_ARG;
+    if (src_dtype != FPSA_F32 && src_dtype != FPSA_BF16) return FPSA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    if (NB > 65535 || (int64_t)B * H * NB * 64 > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    fpsa::launch_gather_tiles(src, src_dtype == FPSA_F32 ? 0 : 1, slot_token, NB, dst, layout, N, B, H, D,
+                              static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_scatter_tiles(const void* src, const int32_t* slot_token, int32_t B, int32_t N, int32_t H,
+                           int32_t D, int32_t NB, void* dst, int32_t dst_dtype, void* stream) {
+    if (src == nullptr || slot_token == nullptr || dst == nullptr) return FPSA_ERR_INVALID_ARG;
+    if (!dims_ok(B, H) || N < 1 || NB < 1) return FPSA_ERR_INVALID_ARG;
+    if (dst_dtype != FPSA_F32 && dst_dtype != FPSA_BF16) return FPSA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    if (NB > 65535 || (int64_t)B * H * NB * 64 > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    fpsa::launch_scatter_tiles(src, slot_token, NB, dst, dst_dtype == FPSA_F32 ? 0 : 1, N, B, H, D,
+                               static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_cluster_mass(const double* cq, const int32_t* nq, const double* ck, const int32_t* nk,
+                          int32_t B, int32_t H, int32_t Cq, int32_t Ck, int32_t D, float softmax_scale,
+                          float* est, void* stream) {
+    if (cq == nullptr || nq == nullptr || ck == nullptr || nk == nullptr || est == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (!dims_ok(B, H) || Cq < 1 || Ck < 1) return FPSA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return FPSA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    if (Ck > FPSA_MAX_SELECT_BLOCKS || (int64_t)B * H * Cq > (1L << 24)) return FPSA_ERR_UNSUPPORTED;
+    fpsa::launch_cluster_mass(cq, nq, ck, nk, B, H, Cq, Ck, D, (double)softmax_scale, est,
+                              static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_cluster_blocks(const int32_t* crow_ptr, const int32_t* ccol_idx, const int32_t* qoff,
+                            const int32_t* koff, int32_t B, int32_t H, int32_t Cq, int32_t Ck,
+                            int32_t NB, int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (crow_ptr == nullptr || ccol_idx == nullptr || qoff == nullptr || koff == nullptr ||
+        row_ptr == nullptr || col_idx == nullptr || workspace == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (!dims_ok(B, H) || Cq < 1 || Ck < 1 || NB < 1) return FPSA_ERR_INVALID_ARG;
+    const int64_t R = (int64_t)B * H * NB;
+    if (R > (1L << 24) || R * NB > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    if (capacity < R * NB) return FPSA_ERR_CAPACITY;
+    if (workspace_bytes < (size_t)R * 4) return FPSA_ERR_CAPACITY;
+    fpsa::launch_cluster_blocks(crow_ptr, ccol_idx, qoff, koff, B, H, Cq, Ck, NB, row_ptr, col_idx,
+                                static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
+int32_t fpsa_sparse_attn_fwd_varlen(const void* q, const void* k, const void* v,
+                                    const int32_t* key_counts, const int32_t* row_ptr,
+                                    const int32_t* col_idx, int32_t B, int32_t H, int32_t D,
+                                    int32_t NB, float softmax_scale, void* o, float* lse,
+                                    float* o_f32, void* stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || key_counts == nullptr || row_ptr == nullptr ||
+        col_idx == nullptr || o == nullptr)
+        return FPSA_ERR_INVALID_ARG;
+    if (!dims_ok(B, H) || NB < 1 || NB > (1 << 24)) return FPSA_ERR_INVALID_ARG;
+    if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return FPSA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    if ((long)B * H * NB > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
+    // the blocks as one flat row of 64-token tiles: every slot is a query slot
+    fpsa_grid flat = {1, 1, 64 * NB, 1, 1, 64};
+    Geom geo;
+    if (!make_geom(&flat, &geo)) return FPSA_ERR_INVALID_ARG;
+    fpsa::launch_sparse_attn(q, k, v, 0, nullptr, nullptr, row_ptr, col_idx, B, H, D, geo, softmax_scale, o,
+                             lse, o_f32, key_counts, static_cast<hipStream_t>(stream));
     return hip_status();
 }
 

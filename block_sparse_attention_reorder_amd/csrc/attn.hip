@@ -22,12 +22,15 @@ namespace fpsa {
 
 constexpr int kAttnThreads = 256;
 
-template <int D, bool FP8>
+// CNT: the real keys of each key block are its first kcount[(b*H + h)*nb + kb] slots
+// (blocks of a cluster-contiguous layout) instead of following from the token grid.
+template <int D, bool FP8, bool CNT>
 __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long R,
-    float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o32) {
+    float scale_log2, __bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o32,
+    const int32_t* __restrict__ kcount) {
     constexpr int kDT = D / 32;
     constexpr int kKBytes = kBlock * D * (FP8 ? 1 : 2);   // K tile of one block
     constexpr int kVBytes = kBlock * D * 2;               // V tile of one block
@@ -74,13 +77,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     // edge code) of entries base .. base+63, `raw` the plain indices of the next 64,
     // loaded 64 blocks before they are needed; single entries are picked with
     // v_readlane, so the loop never waits on an index load.
-    int cur = block_info(g, lane < n ? col_idx[e0 + lane] : -1);
+    auto info_of = [&](int x) {
+        if constexpr (CNT) {
+            if (x < 0 || x >= g.nb) return -1;
+            const int c = kcount[bh * g.nb + x];
+            return c >= kBlock ? x : (x | ((kBlock - max(c, 0)) << kEdgeShift));
+        } else {
+            return block_info(g, x);
+        }
+    };
+    int cur = info_of(lane < n ? col_idx[e0 + lane] : -1);
     int raw = 64 + lane < n ? col_idx[e0 + 64 + lane] : -1;
     int base = 0;
     auto info_at = [&](int jj) {          // jj = 0, 1, 2, ... in order
         if (jj - base == 64) {
             base += 64;
-            cur = block_info(g, raw);
+            cur = info_of(raw);
             raw = base + 64 + lane < n ? col_idx[e0 + base + 64 + lane] : -1;
         }
         return __builtin_amdgcn_readlane(cur, jj - base);
@@ -119,7 +131,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
         const float ksc2 = FP8 ? ksc_row[block_of(inf2)] : 1.0f;
         const float c = FP8 ? cq * ksc : cq;
         const int code = inf >> kEdgeShift;           // 0: interior block; < 0: no block
-        const uint64_t vm = code == 0 ? ~0ull : (inf < 0 ? 0ull : edge.mask(code));
+        uint64_t vm;
+        if constexpr (CNT)   // code = 64 - real keys, which are the block's first slots
+            vm = code == 0 ? ~0ull : ((inf < 0 || code >= kBlock) ? 0ull : (~0ull >> code));
+        else
+            vm = code == 0 ? ~0ull : (inf < 0 ? 0ull : edge.mask(code));
         const float nref = softmax_enter<kDT>(s, code == 0, vm, smax, c, kh, half, acc, m, l);
 
         // K(j+1) and V(j) landed; every wave is done with iteration j-1's reads
@@ -176,18 +192,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
 void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, const float* q_scale,
                         const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                         int B, int H, int D, const Geom& g, float scale, void* o, float* lse, float* o32,
-                        hipStream_t st) {
+                        const int32_t* kcount, hipStream_t st) {
     const long R = (long)B * H * g.nb;
     const float sl2 = scale * kLog2e;
     const __bf16* vt = static_cast<const __bf16*>(v);
     __bf16* out = static_cast<__bf16*>(o);
     dim3 grid((unsigned)R), block(kAttnThreads);
     if (D == 128) {
-        if (fp8) k_sparse_attn<128, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32);
-        else k_sparse_attn<128, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32);
+        if (fp8) k_sparse_attn<128, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
+        else if (kcount) k_sparse_attn<128, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, kcount);
+        else k_sparse_attn<128, false, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
     } else {
-        if (fp8) k_sparse_attn<64, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32);
-        else k_sparse_attn<64, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32);
+        if (fp8) k_sparse_attn<64, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
+        else if (kcount) k_sparse_attn<64, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, kcount);
+        else k_sparse_attn<64, false, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
     }
 }
 

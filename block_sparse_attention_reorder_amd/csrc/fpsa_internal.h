@@ -15,6 +15,11 @@ void launch_tile_forward(const void* src, int src_dt, void* dst, int fp8, int la
                          const Geom& g, long N, int B, int H, int D, hipStream_t st);
 void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, long N, int B,
                          int H, int D, hipStream_t st);
+// The same moves driven by an explicit slot map [B*H, nblocks*64] (token or -1).
+void launch_gather_tiles(const void* src, int src_dt, const int32_t* slot_token, int nblocks, void* dst,
+                         int layout, long N, int B, int H, int D, hipStream_t st);
+void launch_scatter_tiles(const void* src, const int32_t* slot_token, int nblocks, void* dst, int dst_dt,
+                          long N, int B, int H, int D, hipStream_t st);
 
 // Workspace of the mass pass: nb * 64 floats per query-block row in flight; rows
 // are processed in launches of as many rows as the workspace holds.
@@ -39,6 +44,20 @@ void launch_pattern(int nb, int B, int H, const int32_t* patterns, int32_t* row_
 void launch_retained_mass(const float* mass, long R, int nb, const int32_t* row_ptr,
                           const int32_t* col_idx, float* out, hipStream_t st);
 
+// Exclusive scan of R counts into out[R + 1] (one workgroup).
+void launch_scan(const int32_t* count, long R, int32_t* out, hipStream_t st);
+
+// k-means semantic permutation (cluster.hip).
+void launch_kmeans(const void* x, int x_f32, int B, int N, int H, int D, int C, int iters, int32_t* assign,
+                   double* cent, int32_t* count, int32_t* off, int32_t* members, hipStream_t st);
+void launch_cluster_layout(const int32_t* off, const int32_t* members, int B, int H, int C, int nblocks,
+                           int32_t* slot_token, int32_t* blk_off, int32_t* blk_count, hipStream_t st);
+void launch_cluster_mass(const double* cq, const int32_t* nq, const double* ck, const int32_t* nk, int B, int H,
+                         int Cq, int Ck, int D, double scale, float* est, hipStream_t st);
+void launch_cluster_blocks(const int32_t* crow_ptr, const int32_t* ccol_idx, const int32_t* qoff,
+                           const int32_t* koff, int B, int H, int Cq, int Ck, int NB, int32_t* row_ptr,
+                           int32_t* col_idx, int32_t* count, hipStream_t st);
+
 // CSR transpose: a bitmap of R * ceil(nb/32) words and R column counts.
 size_t transpose_workspace_bytes(long R, int nb);
 void launch_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, long R, int nb,
@@ -55,6 +74,6 @@ void launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const v
 void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, const float* q_scale,
                         const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                         int B, int H, int D, const Geom& g, float scale, void* o, float* lse,
-                        float* o32, hipStream_t st);
+                        float* o32, const int32_t* kcount, hipStream_t st);
 
 }  // namespace fpsa

@@ -75,14 +75,31 @@ __device__ inline void chunk_source(int oc, int& e, int& d0) {
     }
 }
 
+// Where the tokens of a block come from: the token grid (raster order, tiles in
+// raster order), or an explicit per-(b, h) slot map (-1 for padding), as for the
+// cluster-contiguous layout of the k-means permutation.
+struct GridMap {
+    Geom g;
+    __device__ inline long token(long, int blk, int e) const { return g.token(blk, e); }
+    __host__ __device__ inline int nb() const { return g.nb; }
+};
+struct SlotMap {
+    const int32_t* slot_token;   // [B*H, nblocks*64]
+    int nblocks;
+    __device__ inline long token(long bh, int blk, int e) const {
+        return slot_token[(bh * nblocks + blk) * kBlock + e];
+    }
+    __host__ __device__ inline int nb() const { return nblocks; }
+};
+
 // One workgroup per (block, head, batch). Phase 1 reads the block's 64 token rows
 // in raster order (coalesced), converts (and for e4m3 computes the tile scale and
 // encodes) into an LDS tile; phase 2 writes the block in the requested layout as
 // contiguous 16-byte chunks.
-template <typename SrcT, int D, bool FP8, int LAYOUT>
+template <typename SrcT, int D, bool FP8, int LAYOUT, class Map>
 __global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ src,
                                                       void* __restrict__ dst,
-                                                      float* __restrict__ scale_out, Geom g,
+                                                      float* __restrict__ scale_out, Map map,
                                                       long N, int H) {
     constexpr int kIn = kBlock * D / 8;                 // 8-element input chunks
     constexpr int kInPerThread = kIn / 256;
@@ -98,7 +115,7 @@ __global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ s
     for (int i = 0; i < kInPerThread; ++i) {
         int c = tid + 256 * i;
         int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
-        long n = g.token(blk, e);
+        long n = map.token(bh, blk, e);
         if (n >= 0) {
             load8<SrcT>(src + (((long)b * N + n) * H + h) * D + d0, v[i]);
         } else {
@@ -120,7 +137,7 @@ __global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ s
         __syncthreads();
         amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
         const float s = amax > 0.0f ? amax / 448.0f : 1.0f;   // IEEE division
-        if (tid == 0) scale_out[bh * g.nb + blk] = s;
+        if (tid == 0) scale_out[bh * map.nb() + blk] = s;
 #pragma unroll
         for (int i = 0; i < kInPerThread; ++i) {
             int c = tid + 256 * i;
@@ -148,7 +165,7 @@ __global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ s
     __syncthreads();
 
     constexpr int kOut = kBlock * D * ESIZE / 16;       // 16-byte output chunks
-    uint8_t* out = reinterpret_cast<uint8_t*>(dst) + (bh * g.nb + blk) * (long)(kBlock * D * ESIZE);
+    uint8_t* out = reinterpret_cast<uint8_t*>(dst) + (bh * map.nb() + blk) * (long)(kBlock * D * ESIZE);
 #pragma unroll
     for (int i = 0; i < kOut / 256; ++i) {
         int oc = tid + 256 * i;
@@ -171,20 +188,20 @@ __global__ __launch_bounds__(256) void k_tile_forward(const SrcT* __restrict__ s
     }
 }
 
-template <typename DstT, int D>
+template <typename DstT, int D, class Map>
 __global__ __launch_bounds__(256) void k_tile_inverse(const __bf16* __restrict__ src,
-                                                      DstT* __restrict__ dst, Geom g, long N,
+                                                      DstT* __restrict__ dst, Map map, long N,
                                                       int H) {
     constexpr int kChunks = kBlock * D / 8;
     constexpr int kPerThread = kChunks / 256;
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const long bh = (long)b * H + h;
-    const __bf16* in = src + (bh * g.nb + blk) * (long)(kBlock * D);
+    const __bf16* in = src + (bh * map.nb() + blk) * (long)(kBlock * D);
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
         int c = threadIdx.x + 256 * i;
         int e = c / (D / 8), d0 = (c % (D / 8)) * 8;
-        long n = g.token(blk, e);
+        long n = map.token(bh, blk, e);
         if (n < 0) continue;
         bf16x8 x = *reinterpret_cast<const bf16x8*>(in + (long)c * 8);
         DstT* o = dst + (((long)b * N + n) * H + h) * D + d0;
@@ -200,44 +217,66 @@ __global__ __launch_bounds__(256) void k_tile_inverse(const __bf16* __restrict__
     }
 }
 
-template <typename SrcT, int D>
+template <typename SrcT, int D, class Map>
 static void launch_forward_t(const SrcT* s, void* dst, bool fp8, int layout, float* scale,
-                             const Geom& g, long N, int B, int H, hipStream_t st) {
-    dim3 grid(g.nb, H, B);
+                             const Map& map, long N, int B, int H, hipStream_t st) {
+    dim3 grid(map.nb(), H, B);
     if (fp8) {
-        if (layout == kQK) k_tile_forward<SrcT, D, true, kQK><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
-        else k_tile_forward<SrcT, D, true, kRows><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        if (layout == kQK) k_tile_forward<SrcT, D, true, kQK, Map><<<grid, 256, 0, st>>>(s, dst, scale, map, N, H);
+        else k_tile_forward<SrcT, D, true, kRows, Map><<<grid, 256, 0, st>>>(s, dst, scale, map, N, H);
     } else {
-        if (layout == kQK) k_tile_forward<SrcT, D, false, kQK><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
-        else if (layout == kVT) k_tile_forward<SrcT, D, false, kVT><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
-        else k_tile_forward<SrcT, D, false, kRows><<<grid, 256, 0, st>>>(s, dst, scale, g, N, H);
+        if (layout == kQK) k_tile_forward<SrcT, D, false, kQK, Map><<<grid, 256, 0, st>>>(s, dst, scale, map, N, H);
+        else if (layout == kVT) k_tile_forward<SrcT, D, false, kVT, Map><<<grid, 256, 0, st>>>(s, dst, scale, map, N, H);
+        else k_tile_forward<SrcT, D, false, kRows, Map><<<grid, 256, 0, st>>>(s, dst, scale, map, N, H);
+    }
+}
+
+template <class Map>
+static void launch_forward_map(const void* src, int src_dt, void* dst, int fp8, int layout, float* scale,
+                               const Map& map, long N, int B, int H, int D, hipStream_t st) {
+    if (src_dt == 0) {
+        const float* s = static_cast<const float*>(src);
+        if (D == 128) launch_forward_t<float, 128>(s, dst, fp8, layout, scale, map, N, B, H, st);
+        else launch_forward_t<float, 64>(s, dst, fp8, layout, scale, map, N, B, H, st);
+    } else {
+        const __bf16* s = static_cast<const __bf16*>(src);
+        if (D == 128) launch_forward_t<__bf16, 128>(s, dst, fp8, layout, scale, map, N, B, H, st);
+        else launch_forward_t<__bf16, 64>(s, dst, fp8, layout, scale, map, N, B, H, st);
+    }
+}
+
+template <class Map>
+static void launch_inverse_map(const void* src, void* dst, int dst_dt, const Map& map, long N, int B,
+                               int H, int D, hipStream_t st) {
+    dim3 grid(map.nb(), H, B);
+    const __bf16* s = static_cast<const __bf16*>(src);
+    if (D == 128) {
+        if (dst_dt == 0) k_tile_inverse<float, 128, Map><<<grid, 256, 0, st>>>(s, (float*)dst, map, N, H);
+        else k_tile_inverse<__bf16, 128, Map><<<grid, 256, 0, st>>>(s, (__bf16*)dst, map, N, H);
+    } else {
+        if (dst_dt == 0) k_tile_inverse<float, 64, Map><<<grid, 256, 0, st>>>(s, (float*)dst, map, N, H);
+        else k_tile_inverse<__bf16, 64, Map><<<grid, 256, 0, st>>>(s, (__bf16*)dst, map, N, H);
     }
 }
 
 void launch_tile_forward(const void* src, int src_dt, void* dst, int fp8, int layout, float* scale,
                          const Geom& g, long N, int B, int H, int D, hipStream_t st) {
-    if (src_dt == 0) {
-        const float* s = static_cast<const float*>(src);
-        if (D == 128) launch_forward_t<float, 128>(s, dst, fp8, layout, scale, g, N, B, H, st);
-        else launch_forward_t<float, 64>(s, dst, fp8, layout, scale, g, N, B, H, st);
-    } else {
-        const __bf16* s = static_cast<const __bf16*>(src);
-        if (D == 128) launch_forward_t<__bf16, 128>(s, dst, fp8, layout, scale, g, N, B, H, st);
-        else launch_forward_t<__bf16, 64>(s, dst, fp8, layout, scale, g, N, B, H, st);
-    }
+    launch_forward_map(src, src_dt, dst, fp8, layout, scale, GridMap{g}, N, B, H, D, st);
 }
 
 void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, long N, int B,
                          int H, int D, hipStream_t st) {
-    dim3 grid(g.nb, H, B);
-    const __bf16* s = static_cast<const __bf16*>(src);
-    if (D == 128) {
-        if (dst_dt == 0) k_tile_inverse<float, 128><<<grid, 256, 0, st>>>(s, (float*)dst, g, N, H);
-        else k_tile_inverse<__bf16, 128><<<grid, 256, 0, st>>>(s, (__bf16*)dst, g, N, H);
-    } else {
-        if (dst_dt == 0) k_tile_inverse<float, 64><<<grid, 256, 0, st>>>(s, (float*)dst, g, N, H);
-        else k_tile_inverse<__bf16, 64><<<grid, 256, 0, st>>>(s, (__bf16*)dst, g, N, H);
-    }
+    launch_inverse_map(src, dst, dst_dt, GridMap{g}, N, B, H, D, st);
+}
+
+void launch_gather_tiles(const void* src, int src_dt, const int32_t* slot_token, int nblocks, void* dst,
+                         int layout, long N, int B, int H, int D, hipStream_t st) {
+    launch_forward_map(src, src_dt, dst, 0, layout, nullptr, SlotMap{slot_token, nblocks}, N, B, H, D, st);
+}
+
+void launch_scatter_tiles(const void* src, const int32_t* slot_token, int nblocks, void* dst, int dst_dt,
+                          long N, int B, int H, int D, hipStream_t st) {
+    launch_inverse_map(src, dst, dst_dt, SlotMap{slot_token, nblocks}, N, B, H, D, st);
 }
 
 }  // namespace fpsa

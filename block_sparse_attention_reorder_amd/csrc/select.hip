@@ -420,6 +420,10 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_col_fill(const uint32_t* __r
     }
 }
 
+void launch_scan(const int32_t* count, long R, int32_t* out, hipStream_t st) {
+    k_scan_counts<<<1, 1024, 0, st>>>(count, R, out);
+}
+
 size_t transpose_workspace_bytes(long R, int nb) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return up((size_t)R * ((nb + 31) / 32) * 4) + up((size_t)R * 4);

@@ -26,7 +26,8 @@ EXPORTED = [
     "fpsa_tile_reorder", "fpsa_block_mass", "fpsa_select_blocks", "fpsa_structured_mask",
     "fpsa_pattern_mask", "fpsa_retained_mass", "fpsa_sparse_attn_fwd",
     "fpsa_csr_transpose", "fpsa_transpose_workspace_bytes", "fpsa_sparse_attn_bwd",
-    "fpsa_bwd_workspace_bytes",
+    "fpsa_bwd_workspace_bytes", "fpsa_kmeans", "fpsa_cluster_layout", "fpsa_gather_tiles",
+    "fpsa_scatter_tiles", "fpsa_cluster_mass", "fpsa_cluster_blocks", "fpsa_sparse_attn_fwd_varlen",
 ]
 
 
@@ -90,6 +91,21 @@ def lib() -> ctypes.CDLL:
                                            vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.fpsa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fpsa_bwd_workspace_bytes.argtypes = [i32, i32, gp]
+        L.fpsa_kmeans.restype = i32
+        L.fpsa_kmeans.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.fpsa_cluster_layout.restype = i32
+        L.fpsa_cluster_layout.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+        L.fpsa_gather_tiles.restype = i32
+        L.fpsa_gather_tiles.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+        L.fpsa_scatter_tiles.restype = i32
+        L.fpsa_scatter_tiles.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, i32, vp]
+        L.fpsa_cluster_mass.restype = i32
+        L.fpsa_cluster_mass.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp]
+        L.fpsa_cluster_blocks.restype = i32
+        L.fpsa_cluster_blocks.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i64, vp,
+                                          ctypes.c_size_t, vp]
+        L.fpsa_sparse_attn_fwd_varlen.restype = i32
+        L.fpsa_sparse_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp]
         L.fpsa_sparse_attn_fwd.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, gp, f32,
                                            vp, vp, vp, vp]
         _lib = L
@@ -258,3 +274,77 @@ def sparse_attn_fwd(q, k, v, row_ptr, col_idx, grid, tile, B, H, D, softmax_scal
                                    _ptr(row_ptr), _ptr(col_idx), int(B), int(H), int(D), ctypes.byref(g),
                                    float(softmax_scale), _ptr(o), _ptr(lse), _ptr(o_f32), _stream(stream))
     _check(s, "fpsa_sparse_attn_fwd")
+
+
+# --------------------------------------------------------------------------- k-means permutation
+
+def _i32(*ts):
+    for t in ts:
+        if t.dtype != torch.int32:
+            raise ValueError("index arrays are int32")
+
+
+def kmeans(x, B, N, H, D, C, iters, assign, centroids, counts, member_off, members, stream=None) -> None:
+    _i32(assign, counts, member_off, members)
+    if centroids.dtype != torch.float64:
+        raise ValueError("centroids float64")
+    s = lib().fpsa_kmeans(_ptr(x), _DT[x.dtype], int(B), int(N), int(H), int(D), int(C), int(iters),
+                          _ptr(assign), _ptr(centroids), _ptr(counts), _ptr(member_off), _ptr(members),
+                          _stream(stream))
+    _check(s, "fpsa_kmeans")
+
+
+def cluster_layout(member_off, members, B, H, N, C, NB, slot_token, blk_off, blk_count, stream=None) -> None:
+    _i32(member_off, members, slot_token, blk_off, blk_count)
+    s = lib().fpsa_cluster_layout(_ptr(member_off), _ptr(members), int(B), int(H), int(N), int(C), int(NB),
+                                  _ptr(slot_token), _ptr(blk_off), _ptr(blk_count), _stream(stream))
+    _check(s, "fpsa_cluster_layout")
+
+
+def gather_tiles(src, slot_token, B, N, H, D, NB, layout, dst, stream=None) -> None:
+    _i32(slot_token)
+    if dst.dtype != torch.bfloat16:
+        raise ValueError("gathered tiles are bf16")
+    s = lib().fpsa_gather_tiles(_ptr(src), _DT[src.dtype], _ptr(slot_token), int(B), int(N), int(H), int(D),
+                                int(NB), int(layout), _ptr(dst), _stream(stream))
+    _check(s, "fpsa_gather_tiles")
+
+
+def scatter_tiles(src, slot_token, B, N, H, D, NB, dst, stream=None) -> None:
+    _i32(slot_token)
+    if src.dtype != torch.bfloat16:
+        raise ValueError("tiled rows are bf16")
+    s = lib().fpsa_scatter_tiles(_ptr(src), _ptr(slot_token), int(B), int(N), int(H), int(D), int(NB),
+                                 _ptr(dst), _DT[dst.dtype], _stream(stream))
+    _check(s, "fpsa_scatter_tiles")
+
+
+def cluster_mass(cq, nq, ck, nk, B, H, Cq, Ck, D, softmax_scale, est, stream=None) -> None:
+    _i32(nq, nk)
+    if cq.dtype != torch.float64 or ck.dtype != torch.float64 or est.dtype != torch.float32:
+        raise ValueError("centroids float64, est float32")
+    s = lib().fpsa_cluster_mass(_ptr(cq), _ptr(nq), _ptr(ck), _ptr(nk), int(B), int(H), int(Cq), int(Ck),
+                                int(D), float(softmax_scale), _ptr(est), _stream(stream))
+    _check(s, "fpsa_cluster_mass")
+
+
+def cluster_blocks(crow_ptr, ccol_idx, qoff, koff, B, H, Cq, Ck, NB, row_ptr, col_idx, workspace,
+                   stream=None) -> None:
+    _i32(crow_ptr, ccol_idx, qoff, koff, row_ptr, col_idx)
+    s = lib().fpsa_cluster_blocks(_ptr(crow_ptr), _ptr(ccol_idx), _ptr(qoff), _ptr(koff), int(B), int(H),
+                                  int(Cq), int(Ck), int(NB), _ptr(row_ptr), _ptr(col_idx), int(col_idx.numel()),
+                                  _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                  _stream(stream))
+    _check(s, "fpsa_cluster_blocks")
+
+
+def sparse_attn_fwd_varlen(q, k, v, key_counts, row_ptr, col_idx, B, H, D, NB, softmax_scale, o, *, lse=None,
+                           o_f32=None, stream=None) -> None:
+    _i32(key_counts, row_ptr, col_idx)
+    for t in (q, k, v, o):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("q, k, v and o are bf16")
+    s = lib().fpsa_sparse_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(key_counts), _ptr(row_ptr),
+                                          _ptr(col_idx), int(B), int(H), int(D), int(NB), float(softmax_scale),
+                                          _ptr(o), _ptr(lse), _ptr(o_f32), _stream(stream))
+    _check(s, "fpsa_sparse_attn_fwd_varlen")

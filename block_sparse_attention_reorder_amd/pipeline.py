@@ -194,3 +194,102 @@ class BlockSparseAttention:
         csr = self.select(mass, thr_num, thr_den)
         ot = self.forward(qt, kt, vt, csr)
         return self.untile(ot, out_dtype), csr, mass
+
+
+@dataclass
+class Clusters:
+    """One k-means clustering of the tokens of every (b, h) slice and its block layout."""
+    assign: torch.Tensor        # int32 [B, H, N]
+    centroids: torch.Tensor     # float64 [B, H, C, D]
+    counts: torch.Tensor        # int32 [B, H, C]
+    member_off: torch.Tensor    # int32 [B*H*C + 1]
+    members: torch.Tensor       # int32 [B*H*N]
+    slot_token: torch.Tensor    # int32 [B, H, NB*64]
+    blk_off: torch.Tensor       # int32 [B, H, C+1]
+    blk_count: torch.Tensor     # int32 [B, H, NB]
+
+
+class SemanticSparseAttention:
+    """Attention after a semantic-aware permutation [Sparse VideoGen2: Accelerate
+    Video Generation with Sparse Attention via Semantic-Aware Permutation, Abstract]:
+    per (b, h), k-means over the query vectors (Cq clusters) and over the key vectors
+    (Ck clusters), each cluster laid out in whole 64-token blocks, cluster masses
+    estimated from centroids and sizes, the top-p key clusters kept per query cluster
+    (the same exact cut as the block selection), and the block-sparse forward over the
+    resulting blocks. Everything is recomputed per call (the clustering follows the
+    inputs)."""
+
+    def __init__(self, N, B, H, D, Cq, Ck, iters=8, thr_num=9, thr_den=10, device="cuda", softmax_scale=None):
+        self.N, self.B, self.H, self.D = int(N), int(B), int(H), int(D)
+        self.Cq, self.Ck, self.iters = int(Cq), int(Ck), int(iters)
+        self.thr = (int(thr_num), int(thr_den))
+        self.device = torch.device(device)
+        self.scale = float(softmax_scale) if softmax_scale is not None else 1.0 / math.sqrt(self.D)
+        self.NB = -(-self.N // 64) + max(self.Cq, self.Ck)   # any clustering fits
+
+    def tiled_shape(self):
+        return (self.B, self.H, self.NB * 64, self.D)
+
+    def cluster(self, x, C, stream=None) -> Clusters:
+        B, H, N, D, NB, dev = self.B, self.H, self.N, self.D, self.NB, self.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        c = Clusters(torch.empty((B, H, N), **i32), torch.empty((B, H, C, D), dtype=torch.float64, device=dev),
+                     torch.empty((B, H, C), **i32), torch.empty(B * H * C + 1, **i32), torch.empty(B * H * N, **i32),
+                     torch.empty((B, H, NB * 64), **i32), torch.empty((B, H, C + 1), **i32),
+                     torch.empty((B, H, NB), **i32))
+        fpsa.kmeans(x, B, N, H, D, C, self.iters, c.assign, c.centroids, c.counts, c.member_off, c.members,
+                    stream=stream)
+        fpsa.cluster_layout(c.member_off, c.members, B, H, N, C, NB, c.slot_token, c.blk_off, c.blk_count,
+                            stream=stream)
+        return c
+
+    def gather(self, x, clusters: Clusters, layout, stream=None):
+        out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device)
+        fpsa.gather_tiles(x, clusters.slot_token, self.B, self.N, self.H, self.D, self.NB, layout, out, stream=stream)
+        return out
+
+    def cluster_mass(self, qc: Clusters, kc: Clusters, stream=None):
+        est = torch.empty((self.B, self.H, self.Cq, self.Ck), dtype=torch.float32, device=self.device)
+        fpsa.cluster_mass(qc.centroids, qc.counts, kc.centroids, kc.counts, self.B, self.H, self.Cq, self.Ck,
+                          self.D, self.scale, est, stream=stream)
+        return est
+
+    def select_clusters(self, est, stream=None) -> Csr:
+        R = self.B * self.H * self.Cq
+        csr = Csr(torch.empty(R + 1, dtype=torch.int32, device=self.device),
+                  torch.empty(R * self.Ck, dtype=torch.int32, device=self.device))
+        ws = torch.empty(max(fpsa.select_workspace_bytes(R, self.Ck), 1), dtype=torch.uint8, device=self.device)
+        fpsa.select_blocks(est, R, self.Ck, self.thr[0], self.thr[1], csr.row_ptr, csr.col_idx, ws, stream=stream)
+        return csr
+
+    def block_csr(self, ccsr: Csr, qc: Clusters, kc: Clusters, stream=None) -> Csr:
+        R = self.B * self.H * self.NB
+        csr = Csr(torch.empty(R + 1, dtype=torch.int32, device=self.device),
+                  torch.empty(R * self.NB, dtype=torch.int32, device=self.device))
+        ws = torch.empty(R, dtype=torch.int32, device=self.device)
+        fpsa.cluster_blocks(ccsr.row_ptr, ccsr.col_idx, qc.blk_off, kc.blk_off, self.B, self.H, self.Cq, self.Ck,
+                            self.NB, csr.row_ptr, csr.col_idx, ws, stream=stream)
+        return csr
+
+    def forward(self, qt, kt, vt, kc: Clusters, csr: Csr, out=None, lse=None, stream=None):
+        out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device) if out is None else out
+        fpsa.sparse_attn_fwd_varlen(qt, kt, vt, kc.blk_count, csr.row_ptr, csr.col_idx, self.B, self.H, self.D,
+                                    self.NB, self.scale, out, lse=lse, stream=stream)
+        return out
+
+    def scatter(self, ot, qc: Clusters, dtype=torch.bfloat16, stream=None):
+        out = torch.empty((self.B, self.N, self.H, self.D), dtype=dtype, device=self.device)
+        fpsa.scatter_tiles(ot, qc.slot_token, self.B, self.N, self.H, self.D, self.NB, out, stream=stream)
+        return out
+
+    def run(self, q, k, v, out_dtype=torch.bfloat16, stream=None):
+        """Raster Q, K, V [B, N, H, D] -> (raster O, dict of the intermediate results)."""
+        qc, kc = self.cluster(q, self.Cq, stream), self.cluster(k, self.Ck, stream)
+        qt = self.gather(q, qc, fpsa.LAYOUT_QK, stream)
+        kt = self.gather(k, kc, fpsa.LAYOUT_QK, stream)
+        vt = self.gather(v, kc, fpsa.LAYOUT_VT, stream)
+        est = self.cluster_mass(qc, kc, stream)
+        ccsr = self.select_clusters(est, stream)
+        csr = self.block_csr(ccsr, qc, kc, stream)
+        ot = self.forward(qt, kt, vt, kc, csr, stream=stream)
+        return self.scatter(ot, qc, out_dtype, stream), dict(qc=qc, kc=kc, est=est, ccsr=ccsr, csr=csr, ot=ot)

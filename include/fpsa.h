@@ -16,7 +16,10 @@
  * multi-diagonal and vertical-stripe patterns [Sparse-vDiT: Unleashing the Power of
  * Sparse Attention to Accelerate Video Diffusion Transformers, Abstract]. A monitor
  * reports how much of a later step's mass the frozen indices still retain, and a
- * backward pass gives the gradients over the same blocks.
+ * backward pass gives the gradients over the same blocks. A k-means semantic
+ * permutation with centroid-based top-p cluster selection is the adaptive
+ * alternative [Sparse VideoGen2: Accelerate Video Generation with Sparse Attention
+ * via Semantic-Aware Permutation, Abstract].
  *
  * Conventions for every call:
  *   - Data pointers are DEVICE pointers owned by the caller, except `g`, which is a
@@ -298,6 +301,98 @@ int32_t fpsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const 
 /* Workspace bytes for fpsa_sparse_attn_bwd (B*H*Npad*8); 0 for an invalid grid.
    Host-only. */
 size_t fpsa_bwd_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g);
+
+/*
+ * Semantic-aware permutation ([Sparse VideoGen2: Accelerate Video Generation with
+ * Sparse Attention via Semantic-Aware Permutation, Abstract]): tokens are clustered
+ * by k-means over their own query (or key) vectors, laid out cluster by cluster, and
+ * attention keeps, per query cluster, the key clusters that the centroid-based mass
+ * estimate ranks into the top-p. The calls below give the pieces; the block-sparse
+ * forward over the cluster layout is fpsa_sparse_attn_fwd_varlen.
+ *
+ * fpsa_kmeans: Lloyd's k-means per (b, h) over x[b, :, h, :] (raster [B, N, H, D],
+ * FPSA_BF16 or FPSA_F32), in float64 with a fixed operation order (results are the
+ * same on every run and device):
+ *   start: centroid c = x of token floor(c N / C);
+ *   iters times: assign each token to the centroid at the least squared distance
+ *   (summed over channels in order, no fused multiply-add; ties to the lower
+ *   cluster), then set each non-empty cluster's centroid to the mean of its members
+ *   (summed in token order); an empty cluster keeps its centroid.
+ * Outputs (device): assign [B, H, N]; centroids [B, H, C, D] float64; counts
+ * [B, H, C]; member_off [B*H*C + 1] and members [B*H*N]: the tokens of cluster c of
+ * slice bh, ascending, are members[member_off[bh*C + c] .. member_off[bh*C + c + 1]).
+ * Requires D in {64, 128}, 1 <= C <= min(N, FPSA_MAX_SELECT_BLOCKS), 1 <= iters <=
+ * 1000, B*H*N < 2^31.
+ */
+int32_t fpsa_kmeans(const void* x, int32_t x_dtype, int32_t B, int32_t N, int32_t H, int32_t D,
+                    int32_t C, int32_t iters, int32_t* assign, double* centroids, int32_t* counts,
+                    int32_t* member_off, int32_t* members, void* stream);
+
+/*
+ * Cluster-contiguous block layout: cluster c of slice bh fills blocks
+ * blk_off[bh][c] .. blk_off[bh][c+1]-1 (ceil(count_c / 64) blocks, its members in
+ * token order, the last block padded). slot_token [B, H, NB*64]: the token of each
+ * slot, -1 for padding; blk_off [B, H, C+1]; blk_count [B, H, NB]: the real slots of
+ * each block (a block's real slots are its first ones; 0 past blk_off[bh][C]).
+ * member_off / members as produced by fpsa_kmeans. NB >= ceil(N/64) + C is
+ * required (FPSA_ERR_CAPACITY otherwise): any clustering fits in that many blocks.
+ */
+int32_t fpsa_cluster_layout(const int32_t* member_off, const int32_t* members, int32_t B, int32_t H,
+                            int32_t N, int32_t C, int32_t NB, int32_t* slot_token, int32_t* blk_off,
+                            int32_t* blk_count, void* stream);
+
+/*
+ * Tile moves driven by a slot map instead of the grid: gather raster [B, N, H, D]
+ * (FPSA_BF16 or FPSA_F32) into B*H*NB blocks of layout FPSA_LAYOUT_ROWS, _QK or _VT
+ * (BF16; padding slots zero), and scatter tiled rows (BF16) back to raster
+ * (FPSA_BF16 or FPSA_F32; only slots holding a token are written). slot_token as
+ * from fpsa_cluster_layout; every token must appear at most once per slice.
+ */
+int32_t fpsa_gather_tiles(const void* src, int32_t src_dtype, const int32_t* slot_token, int32_t B,
+                          int32_t N, int32_t H, int32_t D, int32_t NB, int32_t layout, void* dst,
+                          void* stream);
+int32_t fpsa_scatter_tiles(const void* src, const int32_t* slot_token, int32_t B, int32_t N, int32_t H,
+                           int32_t D, int32_t NB, void* dst, int32_t dst_dtype, void* stream);
+
+/*
+ * Cluster-level attention mass from the cluster representation: each key cluster
+ * stands for n_j keys at its centroid, so for query cluster i of slice bh
+ *   est[i, j] = n_j exp(s cq_i . ck_j) / sum_j' n_j' exp(s cq_i . ck_j')
+ * over non-empty key clusters (s = softmax_scale; the dot product in float64 summed
+ * over channels in order), rounded to float32; rows of empty query clusters are 0.
+ * cq [B, H, Cq, D], ck [B, H, Ck, D] float64; nq [B, H, Cq], nk [B, H, Ck];
+ * est [B, H, Cq, Ck] - rows ready for fpsa_select_blocks (R = B*H*Cq, nb = Ck).
+ * Requires D in {64, 128}, 1 <= Cq, 1 <= Ck <= FPSA_MAX_SELECT_BLOCKS.
+ */
+int32_t fpsa_cluster_mass(const double* cq, const int32_t* nq, const double* ck, const int32_t* nk,
+                          int32_t B, int32_t H, int32_t Cq, int32_t Ck, int32_t D, float softmax_scale,
+                          float* est, void* stream);
+
+/*
+ * Block CSR of a cluster selection: query block qb of slice bh lies in query cluster
+ * i when qoff[bh][i] <= qb < qoff[bh][i+1] and keeps every block of every key
+ * cluster j listed in cluster row bh*Cq + i (blocks koff[bh][j] .. koff[bh][j+1]-1),
+ * in the row's order; blocks past qoff[bh][Cq] keep nothing. Rows bh*NB + qb
+ * (R = B*H*NB). qoff [B, H, Cq+1], koff [B, H, Ck+1] as blk_off of
+ * fpsa_cluster_layout. capacity >= R * NB, workspace_bytes >= 4 * R.
+ */
+int32_t fpsa_cluster_blocks(const int32_t* crow_ptr, const int32_t* ccol_idx, const int32_t* qoff,
+                            const int32_t* koff, int32_t B, int32_t H, int32_t Cq, int32_t Ck,
+                            int32_t NB, int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse forward over blocks whose real keys are counted instead of following
+ * from a token grid: block kb of slice bh holds key_counts[bh*NB + kb] real keys in
+ * its first slots (0..64). Otherwise as fpsa_sparse_attn_fwd with BF16 q, k (QK
+ * layout) and v (VT layout) of B*H*NB blocks; every query slot gets an output (the
+ * caller scatters the real ones back); lse and o_f32 optional.
+ */
+int32_t fpsa_sparse_attn_fwd_varlen(const void* q, const void* k, const void* v,
+                                    const int32_t* key_counts, const int32_t* row_ptr,
+                                    const int32_t* col_idx, int32_t B, int32_t H, int32_t D,
+                                    int32_t NB, float softmax_scale, void* o, float* lse,
+                                    float* o_f32, void* stream);
 
 #ifdef __cplusplus
 }

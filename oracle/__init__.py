@@ -103,7 +103,8 @@ def lib():
             L.orc_cluster_attention.restype = None
             L.orc_cluster_attention.argtypes = [_f32p] * 3 + [ctypes.c_int] * 4 + [_i32p, _i32p, ctypes.c_int,
                                                                                     ctypes.c_int, ctypes.c_double,
-                                                                                    _i32p, _i32p, _f64p]
+                                                                                    _i32p, _i32p, _vp, ctypes.c_int,
+                                                                                    _f64p]
             L.orc_csr_transpose.argtypes = [_i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p]
             L.orc_pattern_mask.argtypes = [ctypes.c_int] * 3 + [_i32p, _i32p, _i32p]
             _lib = L
@@ -388,12 +389,15 @@ def cluster_blocks(crow_ptr, ccol_idx, qoff, koff, NB):
     return row_ptr, col_idx[:nnz].copy()
 
 
-def cluster_attention(q, k, v, qassign, kassign, Cq, Ck, scale, crow_ptr, ccol_idx):
-    """Raster output [B, N, H, D] float64 of attention under a cluster selection."""
+def cluster_attention(q, k, v, qassign, kassign, Cq, Ck, scale, crow_ptr, ccol_idx, tokens=None):
+    """Raster output [B, N, H, D] float64 of attention under a cluster selection, or
+    [B, H, len(tokens), D] for the listed query tokens only."""
     q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
     B, N, H, D = q.shape
-    out = np.zeros((B, N, H, D), np.float64)
+    tk = None if tokens is None else _c(tokens, np.int32)
+    out = np.zeros((B, N, H, D) if tk is None else (B, H, len(tk), D), np.float64)
     ci = _c(ccol_idx, np.int32) if len(ccol_idx) else np.zeros(1, np.int32)
     lib().orc_cluster_attention(q, k, v, B, N, H, D, _c(qassign, np.int32), _c(kassign, np.int32), int(Cq),
-                                int(Ck), float(scale), _c(crow_ptr, np.int32), ci, out)
+                                int(Ck), float(scale), _c(crow_ptr, np.int32), ci,
+                                None if tk is None else tk.ctypes.data, 0 if tk is None else len(tk), out)
     return out

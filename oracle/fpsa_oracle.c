@@ -899,22 +899,25 @@ int64_t orc_cluster_blocks(const int32_t* crow_ptr, const int32_t* ccol_idx, con
  * Attention under a cluster selection: query token n of (b, h), in query cluster
  * qassign[n], attends to the keys whose key cluster the cluster row (b*H + h)*Cq +
  * qassign[n] keeps, with the softmax over exactly those keys (zero output when
- * none). out raster [B, N, H, D] float64.
+ * none). With tokens == NULL, out is raster [B, N, H, D] float64; otherwise only the
+ * ntok listed query tokens are computed, into out [B, H, ntok, D].
  */
 void orc_cluster_attention(const float* q, const float* k, const float* v, int B, int N, int H,
                            int D, const int32_t* qassign, const int32_t* kassign, int Cq, int Ck,
                            double scale, const int32_t* crow_ptr, const int32_t* ccol_idx,
-                           double* out) {
+                           const int32_t* tokens, int ntok, double* out) {
+    const int count = tokens ? ntok : N;
 #pragma omp parallel for collapse(3) schedule(dynamic)
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < H; ++h)
-            for (int n = 0; n < N; ++n) {
+            for (int u = 0; u < count; ++u) {
+                const int n = tokens ? tokens[u] : u;
                 const int64_t bh = (int64_t)b * H + h;
                 const int64_t r = bh * Cq + qassign[bh * N + n];
                 char* allowed = (char*)calloc((size_t)Ck, 1);
                 for (int32_t e = crow_ptr[r]; e < crow_ptr[r + 1]; ++e)
                     if (ccol_idx[e] >= 0 && ccol_idx[e] < Ck) allowed[ccol_idx[e]] = 1;
-                double* o = out + RIX(b, n, h, 0);
+                double* o = tokens ? out + (bh * ntok + u) * D : out + RIX(b, n, h, 0);
                 for (int d = 0; d < D; ++d) o[d] = 0.0;
                 double* s = (double*)malloc(sizeof(double) * (size_t)N);
                 double m = -INFINITY;

@@ -216,3 +216,43 @@ def test_sparse_attn_bwd_validation(L):
     assert call(D=96) == fpsa.ERR_UNSUPPORTED
     assert call(odt=fpsa.FP8_E4M3) == fpsa.ERR_UNSUPPORTED
     assert call(wsb=ws - 1) == fpsa.ERR_CAPACITY
+
+
+def test_kmeans_permutation_validation(L):
+    km = L.fpsa_kmeans
+    args = [FAKE, fpsa.BF16, 1, 500, 2, 128, 8, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    def call(i, val, f=km, base=args):
+        a = list(base)
+        a[i] = val
+        return f(*a)
+    assert call(0, None) == fpsa.ERR_INVALID_ARG
+    assert call(1, fpsa.FP8_E4M3) == fpsa.ERR_UNSUPPORTED
+    assert call(3, 0) == fpsa.ERR_INVALID_ARG
+    assert call(5, 96) == fpsa.ERR_UNSUPPORTED
+    assert call(6, 0) == fpsa.ERR_INVALID_ARG
+    assert call(6, 501) == fpsa.ERR_INVALID_ARG                 # more clusters than tokens
+    assert call(7, 0) == fpsa.ERR_INVALID_ARG
+    assert call(12, None) == fpsa.ERR_INVALID_ARG
+    lay = [FAKE, FAKE, 1, 2, 500, 8, 8 + 8, FAKE, FAKE, FAKE, None]   # ceil(500/64) + 8 = 16 blocks
+    assert call(6, 15, L.fpsa_cluster_layout, lay) == fpsa.ERR_CAPACITY
+    assert call(0, None, L.fpsa_cluster_layout, lay) == fpsa.ERR_INVALID_ARG
+    gat = [FAKE, fpsa.BF16, FAKE, 1, 500, 2, 128, 16, fpsa.LAYOUT_QK, FAKE, None]
+    assert call(8, 9, L.fpsa_gather_tiles, gat) == fpsa.ERR_INVALID_ARG
+    assert call(1, fpsa.FP8_E4M3, L.fpsa_gather_tiles, gat) == fpsa.ERR_UNSUPPORTED
+    assert call(2, None, L.fpsa_gather_tiles, gat) == fpsa.ERR_INVALID_ARG
+    sca = [FAKE, FAKE, 1, 500, 2, 128, 16, FAKE, fpsa.F32, None]
+    assert call(8, fpsa.FP8_E4M3, L.fpsa_scatter_tiles, sca) == fpsa.ERR_UNSUPPORTED
+    assert call(6, 0, L.fpsa_scatter_tiles, sca) == fpsa.ERR_INVALID_ARG
+    cm = [FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 8, 128, 0.1, FAKE, None]
+    assert call(9, 0.0, L.fpsa_cluster_mass, cm) == fpsa.ERR_INVALID_ARG
+    assert call(7, 4097, L.fpsa_cluster_mass, cm) == fpsa.ERR_UNSUPPORTED
+    assert call(10, None, L.fpsa_cluster_mass, cm) == fpsa.ERR_INVALID_ARG
+    cb = [FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 8, 16, FAKE, FAKE, 2 * 16 * 16, FAKE, 2 * 16 * 4, None]
+    assert call(11, 2 * 16 * 16 - 1, L.fpsa_cluster_blocks, cb) == fpsa.ERR_CAPACITY
+    assert call(13, 2 * 16 * 4 - 1, L.fpsa_cluster_blocks, cb) == fpsa.ERR_CAPACITY
+    assert call(12, None, L.fpsa_cluster_blocks, cb) == fpsa.ERR_INVALID_ARG
+    fv = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 128, 16, 0.1, FAKE, None, None, None]
+    assert call(3, None, L.fpsa_sparse_attn_fwd_varlen, fv) == fpsa.ERR_INVALID_ARG
+    assert call(8, 80, L.fpsa_sparse_attn_fwd_varlen, fv) == fpsa.ERR_UNSUPPORTED
+    assert call(9, 0, L.fpsa_sparse_attn_fwd_varlen, fv) == fpsa.ERR_INVALID_ARG
+    assert call(10, -1.0, L.fpsa_sparse_attn_fwd_varlen, fv) == fpsa.ERR_INVALID_ARG

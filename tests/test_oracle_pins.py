@@ -737,3 +737,8 @@ def test_cluster_attention_all_and_single_cluster():
     assert np.abs(out[0, qs, 1] - ref[0, :, 0]).max() < 1e-12
     others = np.setdiff1d(np.arange(120), qs)
     assert np.all(out[0, others, 1] == 0) and np.all(out[0, :, 0] == 0)
+    # the token-subset form returns the same rows
+    sel = np.array([qs[0], others[0], 119], np.int32)
+    sub = O.cluster_attention(q, k, v, qa, ka, 4, 5, 0.25, crow, np.array([3], np.int32), tokens=sel)
+    for h in range(2):
+        assert np.array_equal(sub[0, h], out[0, sel, h])
