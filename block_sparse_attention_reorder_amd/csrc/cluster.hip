@@ -7,12 +7,14 @@
 //
 // k-means is Lloyd's algorithm in float64 with a fixed order of every operation:
 // distances summed over channels in order (no fused multiply-add: this file is
-// compiled with contraction off), ties to the lower cluster, member sums in token
-// order. The assignment is therefore the same on every device and run.
+// compiled with contraction off), ties to the lower cluster, member sums in eight
+// interleaved partials combined pairwise. The assignment is therefore the same on
+// every device and run.
 //
 // Kernels: k_km_init (strided starting centroids), k_km_assign (nearest centroid; a
-// lane per token, four waves over interleaved cluster subsets), k_km_count /
-// k_km_fill (member lists in token order, a wave per cluster with ballots),
+// lane per token, token vectors and centroids staged through LDS; cluster sizes by
+// atomic counts), k_km_fill (member lists in token order, a wave per cluster with
+// ballots),
 // k_km_update (centroid = member mean), k_cluster_layout (slot map of the
 // cluster-contiguous blocks), k_cluster_mass (centroid-based cluster masses),
 // k_cblk_count / k_cblk_fill (block CSR of a cluster selection).
@@ -37,43 +39,67 @@ __global__ __launch_bounds__(128) void k_km_init(const T* __restrict__ x, int N,
     cent[(bh * C + c) * D + d] = (double)as_float(x[((b * N + t) * H + h) * D + d]);
 }
 
-// A lane per token of a 64-token tile; wave w scans clusters w, w+4, ... keeping
-// the first strict minimum, and the four candidates are merged on (distance,
-// cluster), which is the sequential scan's answer.
+// A lane per token of a 64-token tile; the tile's vectors sit in LDS (rows padded by
+// one float so that the 64 lanes read 64 different banks) and centroids pass through
+// LDS in chunks of kKmChunk clusters (every lane reads the same centroid value: a
+// broadcast). Within a chunk wave w takes a quarter of the clusters, four at a time so that
+// each converted token value serves four distances. Each wave keeps the first strict
+// minimum of its clusters (visited in increasing order), and the four candidates are
+// merged on (distance, cluster), which is the sequential scan's answer.
+constexpr int kKmChunk = 16;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_km_assign(const T* __restrict__ x, int N, int H, int C,
                                                    const double* __restrict__ cent,
-                                                   int32_t* __restrict__ assign) {
+                                                   int32_t* __restrict__ assign, int32_t* __restrict__ count) {
+    constexpr int kRow = D + 1;
+    __shared__ float xs[64 * kRow];
+    __shared__ double cs[kKmChunk * D];
     __shared__ double bestd[4][64];
     __shared__ int bestc[4][64];
     const long bh = blockIdx.y;
     const long b = bh / H, h = bh % H;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = blockIdx.x * 64 + lane;
-    float xr[D];
-    if (n < N) {
-        const T* row = x + ((b * N + n) * H + h) * D;
-#pragma unroll
-        for (int d = 0; d < D; ++d) xr[d] = as_float(row[d]);
-    } else {
-#pragma unroll
-        for (int d = 0; d < D; ++d) xr[d] = 0.0f;
+    for (int i = tid; i < 64 * D; i += 256) {
+        const int t = i / D, d = i - t * D;
+        const long nn = (long)blockIdx.x * 64 + t;
+        xs[t * kRow + d] = nn < N ? as_float(x[((b * N + nn) * H + h) * D + d]) : 0.0f;
     }
+    const float* xrow = xs + lane * kRow;
     const double* cb = cent + bh * C * D;
     double bd = INFINITY;
     int bc = C;
-    for (int c = w; c < C; c += 4) {
-        const double* cc = cb + (long)c * D;
-        double s = 0.0;
+    for (int c0 = 0; c0 < C; c0 += kKmChunk) {
+        __syncthreads();
+        const long lim = (long)(C - c0) * D;
+        for (int i = tid; i < kKmChunk * D; i += 256) cs[i] = i < lim ? cb[(long)c0 * D + i] : 0.0;
+        __syncthreads();
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const double t = (double)xr[d] - cc[d];
-            s = s + t * t;
-        }
-        if (s < bd) {
-            bd = s;
-            bc = c;
+        for (int g = 0; g < kKmChunk / 16; ++g) {
+            const int cc = (kKmChunk / 4) * w + 4 * g;  // chunk-local cluster of this group
+            if (c0 + cc >= C) break;
+            const double* p = cs + cc * D;
+            double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+#pragma unroll 8
+            for (int d = 0; d < D; ++d) {
+                const double xd = (double)xrow[d];
+                const double t0 = xd - p[d], t1 = xd - p[D + d], t2 = xd - p[2 * D + d], t3 = xd - p[3 * D + d];
+                s0 = s0 + t0 * t0;
+                s1 = s1 + t1 * t1;
+                s2 = s2 + t2 * t2;
+                s3 = s3 + t3 * t3;
+            }
+            const double sv[4] = {s0, s1, s2, s3};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = c0 + cc + u;
+                if (c < C && sv[u] < bd) {
+                    bd = sv[u];
+                    bc = c;
+                }
+            }
         }
     }
     bestd[w][lane] = bd;
@@ -89,28 +115,18 @@ __global__ __launch_bounds__(256) void k_km_assign(const T* __restrict__ x, int 
                 bc = c2;
             }
         }
-        assign[bh * N + n] = bc < C ? bc : 0;
+        const int a = bc < C ? bc : 0;
+        assign[bh * N + n] = a;
+        atomicAdd(&count[bh * C + a], 1);            // sizes only: the order is irrelevant
     }
 }
 
-// Members of cluster c of slice bh (row bh*C + c), counted and written in token
-// order with ballots over the slice's assignment.
-__global__ __launch_bounds__(256) void k_km_count(const int32_t* __restrict__ assign, int N, int C, long rows,
-                                                  int32_t* __restrict__ count) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long r = (long)blockIdx.x * 4 + w;
-    if (r >= rows) return;
-    const long bh = r / C;
-    const int c = (int)(r - bh * C);
-    const int32_t* a = assign + bh * N;
-    int cnt = 0;
-    for (int n0 = 0; n0 < N; n0 += 64) {
-        const int n = n0 + lane;
-        cnt += __popcll(__ballot(n < N && a[n] == c));
-    }
-    if (lane == 0) count[r] = cnt;
+__global__ __launch_bounds__(256) void k_zero_i32(int32_t* __restrict__ p, long n) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0;
 }
 
+// Members of cluster c of slice bh (row bh*C + c), written in token order with
+// ballots over the slice's assignment.
 __global__ __launch_bounds__(256) void k_km_fill(const int32_t* __restrict__ assign, int N, int C, long rows,
                                                  const int32_t* __restrict__ off, int32_t* __restrict__ members) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -131,31 +147,44 @@ __global__ __launch_bounds__(256) void k_km_fill(const int32_t* __restrict__ ass
     }
 }
 
-// Centroid = member mean: a thread per channel adds the members' values in token
-// order (loads fetched 32 at a time, sums strictly sequential).
-template <typename T>
-__global__ __launch_bounds__(128) void k_km_update(const T* __restrict__ x, int N, int H, int D, int C,
-                                                   const int32_t* __restrict__ off,
-                                                   const int32_t* __restrict__ members,
-                                                   double* __restrict__ cent) {
+// Centroid = member mean. The r-th member of a cluster (token order) goes to partial
+// sum r % 8; thread (p, d) adds its partial's members in order (loads fetched 16 at a
+// time), and the eight partials combine as ((p0 + p1) + (p2 + p3)) + ((p4 + p5) +
+// (p6 + p7)). Eight independent chains per channel instead of one.
+constexpr int kKmParts = 8;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kKmParts * D) void k_km_update(const T* __restrict__ x, int N, int H, int C,
+                                                            const int32_t* __restrict__ off,
+                                                            const int32_t* __restrict__ members,
+                                                            double* __restrict__ cent) {
+    __shared__ double part[kKmParts][D];
     const long bh = blockIdx.y;
-    const int c = blockIdx.x, d = threadIdx.x;
-    if (d >= D) return;
+    const int c = blockIdx.x;
+    const int p = threadIdx.x / D, d = threadIdx.x - (threadIdx.x / D) * D;
     const long b = bh / H, h = bh % H;
     const int r0 = off[bh * C + c], r1 = off[bh * C + c + 1];
     if (r1 == r0) return;                        // an empty cluster keeps its centroid
     double s = 0.0;
-    constexpr int kBatch = 32;
-    for (int r = r0; r < r1; r += kBatch) {
+    constexpr int kBatch = 16;
+    for (int r = r0 + p; r < r1; r += kKmParts * kBatch) {
         float v[kBatch];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-            v[i] = r + i < r1 ? as_float(x[((b * N + members[r + i]) * H + h) * D + d]) : 0.0f;
+        for (int i = 0; i < kBatch; ++i) {
+            const int rr = r + kKmParts * i;
+            v[i] = rr < r1 ? as_float(x[((b * N + members[rr]) * H + h) * D + d]) : 0.0f;
+        }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            if (r + i < r1) s = s + (double)v[i];
+            if (r + kKmParts * i < r1) s = s + (double)v[i];
     }
-    cent[(bh * C + c) * D + d] = s / (double)(r1 - r0);
+    part[p][d] = s;
+    __syncthreads();
+    if (p == 0) {
+        const double s01 = part[0][d] + part[1][d], s23 = part[2][d] + part[3][d];
+        const double s45 = part[4][d] + part[5][d], s67 = part[6][d] + part[7][d];
+        cent[(bh * C + c) * D + d] = ((s01 + s23) + (s45 + s67)) / (double)(r1 - r0);
+    }
 }
 
 template <typename T>
@@ -166,13 +195,15 @@ static void kmeans_t(const T* x, int B, int N, int H, int D, int C, int iters, i
     k_km_init<T><<<gc, 128, 0, st>>>(x, N, H, D, C, cent);
     dim3 ga((N + 63) / 64, B * H);
     const unsigned wb = (unsigned)((rows + 3) / 4);
+    const unsigned zb = (unsigned)min((rows + 255) / 256, 4096L);
     for (int it = 0; it < iters; ++it) {
-        if (D == 128) k_km_assign<T, 128><<<ga, 256, 0, st>>>(x, N, H, C, cent, assign);
-        else k_km_assign<T, 64><<<ga, 256, 0, st>>>(x, N, H, C, cent, assign);
-        k_km_count<<<wb, 256, 0, st>>>(assign, N, C, rows, count);
+        k_zero_i32<<<zb, 256, 0, st>>>(count, rows);
+        if (D == 128) k_km_assign<T, 128><<<ga, 256, 0, st>>>(x, N, H, C, cent, assign, count);
+        else k_km_assign<T, 64><<<ga, 256, 0, st>>>(x, N, H, C, cent, assign, count);
         launch_scan(count, rows, off, st);
         k_km_fill<<<wb, 256, 0, st>>>(assign, N, C, rows, off, members);
-        k_km_update<T><<<gc, 128, 0, st>>>(x, N, H, D, C, off, members, cent);
+        if (D == 128) k_km_update<T, 128><<<gc, kKmParts * 128, 0, st>>>(x, N, H, C, off, members, cent);
+        else k_km_update<T, 64><<<gc, kKmParts * 64, 0, st>>>(x, N, H, C, off, members, cent);
     }
 }
 

@@ -317,7 +317,9 @@ size_t fpsa_bwd_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g);
  *   iters times: assign each token to the centroid at the least squared distance
  *   (summed over channels in order, no fused multiply-add; ties to the lower
  *   cluster), then set each non-empty cluster's centroid to the mean of its members
- *   (summed in token order); an empty cluster keeps its centroid.
+ *   (member r, in token order, goes to partial sum r % 8, each partial summed in
+ *   order, the partials combined as ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))); an empty
+ *   cluster keeps its centroid.
  * Outputs (device): assign [B, H, N]; centroids [B, H, C, D] float64; counts
  * [B, H, C]; member_off [B*H*C + 1] and members [B*H*N]: the tokens of cluster c of
  * slice bh, ascending, are members[member_off[bh*C + c] .. member_off[bh*C + c + 1]).

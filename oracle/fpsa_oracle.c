@@ -737,8 +737,9 @@ int64_t orc_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int B,
  *   start: centroid c = x of token floor(c N / C);
  *   iters times: assign every token to the nearest centroid (squared Euclidean
  *   distance summed over channels in order, ties to the lower cluster), then move
- *   every non-empty cluster's centroid to the mean of its members (summed in token
- *   order); an empty cluster keeps its centroid.
+ *   every non-empty cluster's centroid to the mean of its members (eight interleaved
+ *   partial sums in token order, combined pairwise); an empty cluster keeps its
+ *   centroid.
  * assign [B, H, N], cent [B, H, C, D] float64, count [B, H, C]: the last assignment
  * and the centroids and sizes that follow from it.
  */
@@ -778,19 +779,28 @@ void orc_kmeans(const float* x, int B, int N, int H, int D, int C, int iters, in
                     }
                     as[n] = best;
                 }
-                /* member sums, each cluster's members added in token order */
-                double* sum = (double*)calloc((size_t)C * D, sizeof(double));
+                /* member sums: the r-th member of a cluster (token order) is added to
+                   partial sum r % 8, each partial in member order; the partials then
+                   combine as ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)) */
+                double* part = (double*)calloc((size_t)C * 8 * D, sizeof(double));
                 for (int c = 0; c < C; ++c) cn[c] = 0;
                 for (int n = 0; n < N; ++n) {
-                    cn[as[n]]++;
-                    double* sc = sum + (int64_t)as[n] * D;
-                    for (int d = 0; d < D; ++d) sc[d] = sc[d] + (double)x[RIX(b, n, h, d)];
+                    const int c = as[n];
+                    double* pc = part + ((int64_t)c * 8 + cn[c] % 8) * D;
+                    cn[c]++;
+                    for (int d = 0; d < D; ++d) pc[d] = pc[d] + (double)x[RIX(b, n, h, d)];
                 }
                 for (int c = 0; c < C; ++c) {
                     if (cn[c] == 0) continue;
-                    for (int d = 0; d < D; ++d) cc[(int64_t)c * D + d] = sum[(int64_t)c * D + d] / (double)cn[c];
+                    const double* pc = part + (int64_t)c * 8 * D;
+                    for (int d = 0; d < D; ++d) {
+                        const double s01 = pc[d] + pc[D + d], s23 = pc[2 * D + d] + pc[3 * D + d];
+                        const double s45 = pc[4 * D + d] + pc[5 * D + d], s67 = pc[6 * D + d] + pc[7 * D + d];
+                        const double sum = (s01 + s23) + (s45 + s67);
+                        cc[(int64_t)c * D + d] = sum / (double)cn[c];
+                    }
                 }
-                free(sum);
+                free(part);
             }
         }
 }
