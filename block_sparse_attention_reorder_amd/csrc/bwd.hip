@@ -14,6 +14,8 @@
 //   k_bwd_dkdv  one workgroup per key block, walking the query blocks that keep it
 //               (the transposed CSR); dK and dV stay in registers;
 //   k_bwd_dq    one workgroup per query block, walking its kept key blocks.
+// Both walk their blocks through three LDS slots fed from two register staging sets:
+// a block's tiles are loaded two blocks ahead of their use.
 // Every operand comes from the QK tiled layout. Products whose reduction runs over
 // tokens (P^T dO, dS^T Q, dS K) need the tile transposed - channel per lane, tokens
 // along the operand - which the gfx950 transposing LDS read (ds_read_b64_tr_b16)
@@ -21,6 +23,8 @@
 // j is element i%4 of input lane 4j + i/4. Each wave owns a 32 x 32 (query, key)
 // sub-tile of every block pair; the two partial sums of each output half are added
 // through LDS at the end.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "fpsa_internal.h"
 
@@ -109,11 +113,15 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     float scale, __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
     constexpr int kTile = 64 * D * 2;
     constexpr int kSlot = 2 * kTile + 512;        // Q tile, dO tile, lse2[64], delta[64]
-    constexpr int kCh = kTile / (256 * 16);       // 16-byte pieces per thread per tile
     constexpr int kDT = D / 32;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlot];
+    static_assert(2 * kDT * 16 * 64 * 4 <= kSlot, "reduction buffer fits a slot");
+    // three LDS slots
+    __shared__ __attribute__((aligned(16))) uint8_t sl0[kSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t sl1[kSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t sl2[kSlot];
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hb = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kh = w & 1, qh = w >> 1;
     const long col = xcd_row(gridDim.x);
     const long bh = col / g.nb;
@@ -135,117 +143,141 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
         for (int i = 0; i < 16; ++i) accv[t][i] = acck[t][i] = 0.0f;
 
     const int e0 = col_ptr[col], n = col_ptr[col + 1] - e0;
-    i32x4 rq[kCh], rg[kCh];
-    float rl = 0.0f;
-    auto fetch = [&](int qbk) {
-        const long base = (bh * g.nb + qbk) * 64;
+    // query block of entry jj (-1: none or out of range)
+    auto qb_at = [&](int jj) {
+        if (jj >= n) return -1;
+        const int x = __builtin_amdgcn_readfirstlane(row_idx[e0 + jj]);
+        return (x >= 0 && x < g.nb) ? x : -1;
+    };
+    // Two register staging sets: the tiles of block j + 2 are loaded during iteration j
+    // and written to LDS at the end of iteration j + 1, so each load has two blocks of
+    // work to land. A missing block loads block 0.
+    constexpr int kCh = kTile / (256 * 16);       // 16-byte pieces per thread per tile
+    i32x4 rq[2][kCh], rg[2][kCh];
+    float rl[2] = {0.0f, 0.0f};
+    auto fetch = [&](int qbk, auto set) {
+        constexpr int P = decltype(set)::value;
+        const long base = (bh * g.nb + (qbk < 0 ? 0 : qbk)) * 64;
         const i32x4* qs = reinterpret_cast<const i32x4*>(q + base * D);
         const i32x4* gs = reinterpret_cast<const i32x4*>(dout + base * D);
 #pragma unroll
-        for (int j = 0; j < kCh; ++j) {
-            rq[j] = qs[tid + 256 * j];
-            rg[j] = gs[tid + 256 * j];
+        for (int i = 0; i < kCh; ++i) {
+            rq[P][i] = qs[tid + 256 * i];
+            rg[P][i] = gs[tid + 256 * i];
         }
-        if (tid < 64) rl = lse2[base + tid];
-        else if (tid < 128) rl = delta[base + tid - 64];
+        rl[P] = (tid < 64 ? lse2 : delta)[base + (tid & 63)];   // threads >= 128 load unused values
     };
-    auto stash = [&](int s) {
-        uint8_t* dst = lds + s * kSlot;
+    auto stash = [&](auto set, uint8_t* dst) {
+        constexpr int P = decltype(set)::value;
 #pragma unroll
-        for (int j = 0; j < kCh; ++j) {
-            *reinterpret_cast<i32x4*>(dst + (tid + 256 * j) * 16) = rq[j];
-            *reinterpret_cast<i32x4*>(dst + kTile + (tid + 256 * j) * 16) = rg[j];
+        for (int i = 0; i < kCh; ++i) {
+            *reinterpret_cast<i32x4*>(dst + (tid + 256 * i) * 16) = rq[P][i];
+            *reinterpret_cast<i32x4*>(dst + kTile + (tid + 256 * i) * 16) = rg[P][i];
         }
-        if (tid < 128) reinterpret_cast<float*>(dst + 2 * kTile)[tid] = rl;
-    };
-    auto qb_at = [&](int j) {
-        const int x = row_idx[e0 + j];
-        return (x >= 0 && x < g.nb) ? x : -1;
+        if (tid < 128) reinterpret_cast<float*>(dst + 2 * kTile)[tid] = rl[P];
     };
 
-    int qcur = n > 0 ? qb_at(0) : -1;
-    if (qcur >= 0) {
-        fetch(qcur);
-        stash(0);
-    }
-    for (int j = 0; j < n; ++j) {
-        __syncthreads();
-        const int qnext = j + 1 < n ? qb_at(j + 1) : -1;
-        if (qnext >= 0) fetch(qnext);
-        if (qcur >= 0) {
-            const uint8_t* sq = lds + (j & 1) * kSlot;
-            const uint8_t* sg = sq + kTile;
-            const float* sl = reinterpret_cast<const float*>(sq + 2 * kTile);
-            // operand reads first (the S and dP products then issue back to back)
-            bf16x8 qa[D / 16], ga[D / 16];
+    auto compute = [&](const uint8_t* sq) {
+        const uint8_t* sg = sq + kTile;
+        const float* sl = reinterpret_cast<const float*>(sq + 2 * kTile);
+        // operand reads first (the S and dP products then issue back to back)
+        bf16x8 qa[D / 16], ga[D / 16];
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                const int off = (qh * (D / 16) + st) * 1024 + 16 * lane;
-                qa[st] = *reinterpret_cast<const bf16x8*>(sq + off);
-                ga[st] = *reinterpret_cast<const bf16x8*>(sg + off);
+        for (int st = 0; st < D / 16; ++st) {
+            const int off = (qh * (D / 16) + st) * 1024 + 16 * lane;
+            qa[st] = *reinterpret_cast<const bf16x8*>(sq + off);
+            ga[st] = *reinterpret_cast<const bf16x8*>(sg + off);
+        }
+        // lse2 and delta of the rows this lane holds: queries 32*qh + 16*ks +
+        // 8*u + 4*hb + (0..3)
+        f32x4 L[2][2], G[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                L[ks][u] = *reinterpret_cast<const f32x4*>(sl + 32 * qh + 16 * ks + 8 * u + 4 * hb);
+                G[ks][u] = *reinterpret_cast<const f32x4*>(sl + 64 + 32 * qh + 16 * ks + 8 * u + 4 * hb);
             }
-            // lse2 and delta of the rows this lane holds: queries 32*qh + 16*ks +
-            // 8*u + 4*hb + (0..3)
-            f32x4 L[2][2], G[2][2];
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 s, dp;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    L[ks][u] = *reinterpret_cast<const f32x4*>(sl + 32 * qh + 16 * ks + 8 * u + 4 * hb);
-                    G[ks][u] = *reinterpret_cast<const f32x4*>(sl + 64 + 32 * qh + 16 * ks + 8 * u + 4 * hb);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 s, dp;
+        for (int st = 0; st < D / 16; ++st) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kf.b[st], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[st], vf.b[st], dp, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // transposed operands of the two token-reduction products, read while the
+        // products above drain
+        bf16x8 gtr[2][kDT], qtr[2][kDT];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kf.b[st], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[st], vf.b[st], dp, 0, 0, 0);
+            for (int t = 0; t < kDT; ++t) {
+                const int off = trb + t * 2048 + ks * 256;
+                gtr[ks][t] = tr_operand(sg, off);
+                qtr[ks][t] = tr_operand(sq, off);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            // transposed operands of the two token-reduction products, read while the
-            // products above drain
-            bf16x8 gtr[2][kDT], qtr[2][kDT];
+        __builtin_amdgcn_sched_barrier(0);
+        // element i: query 32*qh + 8*(i/4) + 4*hb + i%4, key 32*kh + lane%32
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
+            float p[8], ds[8];
 #pragma unroll
-                for (int t = 0; t < kDT; ++t) {
-                    const int off = trb + t * 2048 + ks * 256;
-                    gtr[ks][t] = tr_operand(sg, off);
-                    qtr[ks][t] = tr_operand(sq, off);
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            // element i: query 32*qh + 8*(i/4) + 4*hb + i%4, key 32*kh + lane%32
+            for (int t = 0; t < 8; ++t) {
+                const int i = 8 * ks + t;
+                const float lq = L[ks][t >> 2][t & 3];
+                const float gq = G[ks][t >> 2][t & 3];
+                const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq)) : 0.0f;
+                p[t] = pp;
+                ds[t] = pp * (dp[i] - gq);
+            }
+            const bf16x8 pa = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float p[8], ds[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int i = 8 * ks + t;
-                    const float lq = L[ks][t >> 2][t & 3];
-                    const float gq = G[ks][t >> 2][t & 3];
-                    const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq)) : 0.0f;
-                    p[t] = pp;
-                    ds[t] = pp * (dp[i] - gq);
-                }
-                const bf16x8 pa = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-                const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-#pragma unroll
-                for (int t = 0; t < kDT; ++t) {
-                    accv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, gtr[ks][t], accv[t], 0, 0, 0);
-                    acck[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qtr[ks][t], acck[t], 0, 0, 0);
-                }
+            for (int t = 0; t < kDT; ++t) {
+                accv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, gtr[ks][t], accv[t], 0, 0, 0);
+                acck[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qtr[ks][t], acck[t], 0, 0, 0);
             }
         }
-        if (qnext >= 0) stash((j + 1) & 1);
-        qcur = qnext;
+    };
+
+    // block j sits in LDS slot j % 3 and passes through staging set j % 2; iteration j
+    // computes it after the barrier, between loading block j + 2 and writing block
+    // j + 1 (loaded an iteration earlier) to its slot, which was last read in
+    // iteration j - 2
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto iter = [&](auto slot, auto set, int jj) {
+        constexpr int S = decltype(slot)::value;
+        uint8_t* cur = S == 0 ? sl0 : (S == 1 ? sl1 : sl2);
+        uint8_t* next = S == 0 ? sl1 : (S == 1 ? sl2 : sl0);
+        __syncthreads();
+        // unconditional (a dummy block past the end) so that the waits before each
+        // stash count exactly one newer set in flight
+        fetch(qb_at(jj + 2), set);
+        if (qb_at(jj) >= 0) compute(cur);
+        stash(std::integral_constant<int, 1 - decltype(set)::value>(), next);
+    };
+    if (n > 0) {
+        fetch(qb_at(0), I0());
+        fetch(qb_at(1), I1());
+        stash(I0(), sl0);
+        for (int jj = 0; jj < n; jj += 6) {
+            iter(std::integral_constant<int, 0>(), I0(), jj);
+            if (jj + 1 < n) iter(std::integral_constant<int, 1>(), I1(), jj + 1);
+            if (jj + 2 < n) iter(std::integral_constant<int, 2>(), I0(), jj + 2);
+            if (jj + 3 < n) iter(std::integral_constant<int, 0>(), I1(), jj + 3);
+            if (jj + 4 < n) iter(std::integral_constant<int, 1>(), I0(), jj + 4);
+            if (jj + 5 < n) iter(std::integral_constant<int, 2>(), I1(), jj + 5);
+        }
     }
     __syncthreads();
 
     // add the two query halves' partial sums; element i of tile t: key 32*kh +
     // 8*(i/4) + 4*hb + i%4, channel 32*t + lane%32
-    float* xch = reinterpret_cast<float*>(lds) + kh * (2 * kDT * 16 * 64);
+    float* xch = reinterpret_cast<float*>(kh == 0 ? sl0 : sl1);
     if (qh == 1) {
 #pragma unroll
         for (int t = 0; t < kDT; ++t)
@@ -280,15 +312,17 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
     float scale, __bf16* __restrict__ dq) {
     constexpr int kTile = 64 * D * 2;
     constexpr int kSlot = 2 * kTile;              // K tile, V tile
-    constexpr int kCh = kTile / (256 * 16);
     constexpr int kDT = D / 32;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlot];
+    static_assert(kDT * 16 * 64 * 4 <= kSlot, "reduction buffer fits a slot");
+    __shared__ __attribute__((aligned(16))) uint8_t sl0[kSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t sl1[kSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t sl2[kSlot];
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, hb = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qh = w & 1, kh = w >> 1;
     const long row = xcd_row(gridDim.x);
     const long bh = row / g.nb;
-    const long npad = 64L * g.nb;
 
     KHalf<D, false> qf, gf;                        // B operands: query (lane % 32) of half qh
     load_khalf<D, false>(qf, q, row * 64, qh, lane);
@@ -308,89 +342,110 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
 
     const int e0 = row_ptr[row], n = row_ptr[row + 1] - e0;
-    i32x4 rk[kCh], rv[kCh];
-    auto fetch = [&](int kbk) {
-        const long base = (bh * g.nb + kbk) * 64 * D;
+    // index word (block and edge code) of entry jj, -1 when none
+    auto info_at = [&](int jj) {
+        if (jj >= n) return -1;
+        return block_info(g, __builtin_amdgcn_readfirstlane(col_idx[e0 + jj]));
+    };
+    // two register staging sets, as in the key-gradient kernel
+    constexpr int kCh = kTile / (256 * 16);
+    i32x4 rk[2][kCh], rv[2][kCh];
+    auto fetch = [&](int info, auto set) {
+        constexpr int P = decltype(set)::value;
+        const long base = (bh * g.nb + (info < 0 ? 0 : (info & kBlockIdMask))) * 64 * D;
         const i32x4* ks = reinterpret_cast<const i32x4*>(k + base);
         const i32x4* vs = reinterpret_cast<const i32x4*>(v + base);
 #pragma unroll
-        for (int j = 0; j < kCh; ++j) {
-            rk[j] = ks[tid + 256 * j];
-            rv[j] = vs[tid + 256 * j];
+        for (int i = 0; i < kCh; ++i) {
+            rk[P][i] = ks[tid + 256 * i];
+            rv[P][i] = vs[tid + 256 * i];
         }
     };
-    auto stash = [&](int s) {
-        uint8_t* dst = lds + s * kSlot;
+    auto stash = [&](auto set, uint8_t* dst) {
+        constexpr int P = decltype(set)::value;
 #pragma unroll
-        for (int j = 0; j < kCh; ++j) {
-            *reinterpret_cast<i32x4*>(dst + (tid + 256 * j) * 16) = rk[j];
-            *reinterpret_cast<i32x4*>(dst + kTile + (tid + 256 * j) * 16) = rv[j];
+        for (int i = 0; i < kCh; ++i) {
+            *reinterpret_cast<i32x4*>(dst + (tid + 256 * i) * 16) = rk[P][i];
+            *reinterpret_cast<i32x4*>(dst + kTile + (tid + 256 * i) * 16) = rv[P][i];
         }
     };
 
-    int icur = n > 0 ? block_info(g, col_idx[e0]) : -1;
-    if (icur >= 0) {
-        fetch(icur & kBlockIdMask);
-        stash(0);
-    }
-    for (int j = 0; j < n; ++j) {
-        __syncthreads();
-        const int inext = j + 1 < n ? block_info(g, col_idx[e0 + j + 1]) : -1;
-        if (inext >= 0) fetch(inext & kBlockIdMask);
-        if (icur >= 0) {
-            const uint8_t* sk = lds + (j & 1) * kSlot;
-            const uint8_t* sv = sk + kTile;
-            const int code = icur >> kEdgeShift;
-            const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
-            const uint32_t m32 = (uint32_t)(vm >> (32 * kh + 4 * hb));
-            bf16x8 ka[D / 16], va[D / 16];
+    auto compute = [&](const uint8_t* sk, int icur) {
+        const uint8_t* sv = sk + kTile;
+        const int code = icur >> kEdgeShift;
+        const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
+        const uint32_t m32 = (uint32_t)(vm >> (32 * kh + 4 * hb));
+        bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                const int off = (kh * (D / 16) + st) * 1024 + 16 * lane;
-                ka[st] = *reinterpret_cast<const bf16x8*>(sk + off);
-                va[st] = *reinterpret_cast<const bf16x8*>(sv + off);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 s, dp;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf.b[st], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st], gf.b[st], dp, 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 ktr[2][kDT];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int t = 0; t < kDT; ++t) ktr[ks][t] = tr_operand(sk, trb + t * 2048 + ks * 256);
-            __builtin_amdgcn_sched_barrier(0);
-            // element i: key 32*kh + 8*(i/4) + 4*hb + i%4, query 32*qh + lane%32
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float ds[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int i = 8 * ks + t;
-                    const float x = keep_or_neg_inf(s[i], m32, 8 * (i >> 2) + (i & 3));
-                    const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lq));
-                    ds[t] = pp * (dp[i] - gq);
-                }
-                const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
-#pragma unroll
-                for (int t = 0; t < kDT; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, ktr[ks][t], acc[t], 0, 0, 0);
-            }
+        for (int st = 0; st < D / 16; ++st) {
+            const int off = (kh * (D / 16) + st) * 1024 + 16 * lane;
+            ka[st] = *reinterpret_cast<const bf16x8*>(sk + off);
+            va[st] = *reinterpret_cast<const bf16x8*>(sv + off);
         }
-        if (inext >= 0) stash((j + 1) & 1);
-        icur = inext;
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 s, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf.b[st], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st], gf.b[st], dp, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 ktr[2][kDT];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int t = 0; t < kDT; ++t) ktr[ks][t] = tr_operand(sk, trb + t * 2048 + ks * 256);
+        __builtin_amdgcn_sched_barrier(0);
+        // element i: key 32*kh + 8*(i/4) + 4*hb + i%4, query 32*qh + lane%32
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            float ds[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int i = 8 * ks + t;
+                const float x = keep_or_neg_inf(s[i], m32, 8 * (i >> 2) + (i & 3));
+                const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lq));
+                ds[t] = pp * (dp[i] - gq);
+            }
+            const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+            for (int t = 0; t < kDT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, ktr[ks][t], acc[t], 0, 0, 0);
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto iter = [&](auto slot, auto set, int jj) {
+        constexpr int S = decltype(slot)::value;
+        uint8_t* cur = S == 0 ? sl0 : (S == 1 ? sl1 : sl2);
+        uint8_t* next = S == 0 ? sl1 : (S == 1 ? sl2 : sl0);
+        __syncthreads();
+        fetch(info_at(jj + 2), set);            // unconditional, as above
+        const int icur = info_at(jj);
+        if (icur >= 0) compute(cur, icur);
+        stash(std::integral_constant<int, 1 - decltype(set)::value>(), next);
+    };
+    if (n > 0) {
+        fetch(info_at(0), I0());
+        fetch(info_at(1), I1());
+        stash(I0(), sl0);
+        for (int jj = 0; jj < n; jj += 6) {
+            iter(std::integral_constant<int, 0>(), I0(), jj);
+            if (jj + 1 < n) iter(std::integral_constant<int, 1>(), I1(), jj + 1);
+            if (jj + 2 < n) iter(std::integral_constant<int, 2>(), I0(), jj + 2);
+            if (jj + 3 < n) iter(std::integral_constant<int, 0>(), I1(), jj + 3);
+            if (jj + 4 < n) iter(std::integral_constant<int, 1>(), I0(), jj + 4);
+            if (jj + 5 < n) iter(std::integral_constant<int, 2>(), I1(), jj + 5);
+        }
     }
     __syncthreads();
 
     // add the two key halves; element i of tile t: query 32*qh + 8*(i/4) + 4*hb +
     // i%4, channel 32*t + lane%32
-    float* xch = reinterpret_cast<float*>(lds) + qh * (kDT * 16 * 64);
+    float* xch = reinterpret_cast<float*>(qh == 0 ? sl0 : sl1);
     if (kh == 1) {
 #pragma unroll
         for (int t = 0; t < kDT; ++t)
@@ -408,7 +463,6 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
                 dq[r * D + 32 * t + (lane & 31)] = (__bf16)(scale * (acc[t][i] + xch[(t * 16 + i) * 64 + lane]));
             }
     }
-    (void)npad;
 }
 
 // ---------------------------------------------------------------- host
