@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
     };
     // Finish block kb: redo the sum with a raised reference when needed, record
     // L = m + log2(sum) and accumulate the row sum. `sum` is the sum formed in the
-    // main section; the scores s already have their padding keys masked.
+    // main section; the padding keys of s already hold -2^100.
     auto finish = [&](const f32x16 (&s)[2], int kb, float sum) {
         if (__ballot(!(sum <= kMassSumLimit) || m == -INFINITY)) {
             float mx = -INFINITY;
@@ -137,29 +137,49 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
         if (hasrow && half == 0) wrow[(long)kb * kBlock + 32 * qh + col] = m + __builtin_amdgcn_logf(sum);
     };
 
-    // Main section of block j (scores s) with the products of block j+1 (into sn), in
-    // hand-chosen issue order: K(j+1) is read from LDS, K(j+2) copied into the slot
-    // K(j) used (after the reads: a read issued after a copy that might write the
-    // same bytes has to wait for it), then each product of block j+1 is followed by
-    // exponentials of block j. Returns the sum of block j's terms against the
-    // current reference.
-    auto main_ordered = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2], bool masked, uint64_t vm) {
-        const float nref = m == -INFINITY ? 0.0f : -m;
-        uint32_t m32[2] = {0u, 0u};
-        if (masked) {
+    // Padding keys of an edge block are excluded inside the products: one extra product
+    // per key tile adds bias(key) * 1 to every query's score, with bias = -2^100 for a
+    // padding key and 0 for a real one (A holds the bias in k slot 0 of the key's row,
+    // B a one in k slot 0 of every query column; all other slots are 0). A real key's
+    // score gains exactly +0, so it is bit-identical to the unbiased product; a padding
+    // key's score becomes -2^100 and its term 2^(t - m) underflows to 0.
+    bf16x8 one_k0;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) m32[kt] = (uint32_t)(vm >> (32 * kt + 4 * half));
+    for (int e = 0; e < 8; ++e) one_k0[e] = (__bf16)0.0f;
+    if (half == 0) one_k0[0] = (__bf16)1.0f;
+    auto key_bias = [&](int code, bf16x8 (&bias)[2]) {
+        const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bias[kt][e] = (__bf16)0.0f;
+            const bool real = (vm >> (32 * kt + col)) & 1ull;
+            if (half == 0 && !real) bias[kt][0] = (__bf16)-0x1p100f;
         }
+    };
+    auto bias_products = [&](f32x16 (&sn)[2], const bf16x8 (&bias)[2]) {
+        f32x16 z;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+        sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias[0], one_k0, z, 0, 0, 0);
+        sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias[1], one_k0, z, 0, 0, 0);
+    };
+
+    // Main section of block j (scores s) with the products of block j+1 (into sn, with
+    // that block's key bias), in hand-chosen issue order: K(j+1) is read from LDS, K(j+2)
+    // copied into the slot K(j) used (after the reads: a read issued after a copy that
+    // might write the same bytes has to wait for it), then each product of block j+1 is
+    // followed by exponentials of block j. Returns the sum of block j's terms against
+    // the current reference.
+    auto main_ordered = [&](int j, const f32x16 (&s)[2], f32x16 (&sn)[2], const bf16x8 (&bias)[2]) {
+        const float nref = m == -INFINITY ? 0.0f : -m;
         const uint8_t* kst = lds + ((j + 1) & 1) * kKBytes;
         lds_khalf<D, false>(k0, kst, 0, lane);
         lds_khalf<D, false>(k1, kst, 1, lane);
         __builtin_amdgcn_sched_barrier(0);
         copy_k(j + 2, j & 1);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sn[kt][i] = 0.0f;
+        bias_products(sn, bias);
         // 2 * D/16 products of block j+1; the 32 exponentials of block j spread over them
         constexpr int kProducts = 2 * (D / 16);
         constexpr int kPerProduct = (32 + kProducts - 1) / kProducts;
@@ -173,8 +193,6 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
             for (int e = 0; e < kPerProduct; ++e) {
                 const int i = pi * kPerProduct + e;
                 if (i < 32) {
-                    if (masked) s[i >> 4][i & 15] = keep_or_neg_inf(s[i >> 4][i & 15], m32[i >> 4],
-                                                                    8 * ((i & 15) >> 2) + (i & 3));
                     const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i >> 4][i & 15], scale_log2, nref));
                     if (i & 1) acc1 += t;
                     else acc0 += t;
@@ -195,10 +213,10 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
     {
         lds_khalf<D, false>(k0, lds, 0, lane);
         lds_khalf<D, false>(k1, lds, 1, lane);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sa[kt][i] = 0.0f;
+        bf16x8 bias[2];
+        key_bias(edge_code(), bias);
+        bias_products(sa, bias);
+        next_coords();                                       // the coordinates run one block ahead
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
             sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0.b[st], qop.b[st], sa[0], 0, 0, 0);
@@ -206,14 +224,11 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
         }
     }
     auto step = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2]) {
-        const int code = edge_code();
+        bf16x8 bias[2];
+        key_bias(edge_code(), bias);                         // of block j+1
         // K(j+1) landed; every wave is done reading K(j) (its slot is refilled below)
         copies_landed_barrier();
-        // two straight-line versions of the main section: edge blocks mask their
-        // padding keys before the exponentials
-        float sum;
-        if (code == 0) sum = main_ordered(j, s, sn, false, ~0ull);
-        else sum = main_ordered(j, s, sn, true, edge.mask(code));
+        const float sum = main_ordered(j, s, sn, bias);
         finish(s, j, sum);
         next_coords();
     };
