@@ -8,6 +8,11 @@ synthetic seeded inputs already resident in HBM).
 Prints one JSON line. `value` is kept-block TFLOP per step (nnz * 4 * 64 * 64 * D,
 the MFMA work of the sparse forward) divided by the whole step time; per-kernel
 times come from HIP events recorded on the stream the kernels run on.
+
+`--workload wan720p | hunyuan720p | grat8192` instead prints per-call timings of that
+workload (medians with p10/p90): the 720p step with the FP8 Q/K forward, the
+HunyuanVideo dense call followed by ten calls on its frozen selection, or the
+8192x8192 image with the fixed structured mask.
 """
 from __future__ import annotations
 
@@ -89,6 +94,9 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.name != "wan480p":
+        measure_workload(args, w, dev)
+        return
     q, k, v = synth.make_qkv(w.grid, w.B, w.H, w.D, w.amp, w.sigma, w.seed, bf16=True)
     qd, kd, vd = (torch.from_numpy(x).to(dev).to(torch.bfloat16) for x in (q, k, v))
     bsa = BlockSparseAttention(w.grid, w.tile, w.B, w.H, w.D, device=dev)
@@ -178,6 +186,15 @@ def main():
                 "peak": dk["peak"], "unit": dk["unit"], "frac": round(dk["frac"], 4),
                 "traffic": dk["traffic"]}
 
+    spread = {s: _stats([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)])
+              for j, s in enumerate(stages)}
+    # the same stages with the infinity cache flushed before every step (K and V of
+    # this workload, 245 MB, would otherwise stay in the 256 MB cache between steps)
+    flushed = _stage_times([(s, fn) for s, fn in zip(stages, stage_fns(bsa, qd, kd, vd, qt, kt, vt, ot, o,
+                                                                       mass, csr, ws, mws))],
+                           args.steps, stream, flush=_flusher(dev))
+    flushed = {s: _stats(x) for s, x in flushed.items()}
+
     extras = next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, max(3, args.steps // 4))
 
     if args.calibrate_copy:
@@ -211,12 +228,220 @@ def main():
         "sparse_fwd_frac_of_bf16_peak": round(kernels["sparse_fwd"]["frac"], 4),
         "sparse_fwd_effective_tflops": round(eff_flop / per["sparse_fwd"] / 1e9, 2),
         "stage_ms": {s: round(x, 4) for s, x in per.items()},
+        "stage_ms_spread": spread,
+        "stage_ms_flushed": flushed,
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                     for n, d in kernels.items()},
         "roofline": roofline,
         "next_rows": extras,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out))
+
+
+def stage_fns(bsa, qd, kd, vd, qt, kt, vt, ot, o, mass, csr, ws, mws):
+    """The five stages of the headline step as separate callables."""
+    return [lambda: (bsa.tile_qk(qd, qt), bsa.tile_qk(kd, kt), bsa.tile_vt(vd, vt)),
+            lambda: bsa.block_mass(qt, kt, mass=mass, workspace=mws),
+            lambda: bsa.select(mass, 99, 100, csr=csr, workspace=ws),
+            lambda: bsa.forward(qt, kt, vt, csr, out=ot),
+            lambda: bsa.untile(ot, out=o)]
+
+
+def _stats(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4), "n": int(a.size)}
+
+
+def _flusher(dev):
+    """Rewrites a 512 MiB buffer (twice the infinity cache) so that nothing read
+    before it is still cached."""
+    import torch
+    buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    return lambda: buf.zero_()
+
+
+def _stage_times(stages, reps, stream, flush=None):
+    """Runs the (name, fn) stages in order `reps` times, each between HIP events on
+    `stream` (flush, when given, runs before each repetition, outside the events).
+    Returns name -> list of ms."""
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(reps)]
+    for r in range(reps):
+        if flush is not None:
+            flush()
+        evs[r][0].record(stream)
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            evs[r][i + 1].record(stream)
+    torch.cuda.synchronize()
+    return {name: [evs[r][i].elapsed_time(evs[r][i + 1]) for r in range(reps)] for i, (name, _) in enumerate(stages)}
+
+
+def device_inputs(w, step, dev, pe):
+    """Q, K, V [B, N, H, D] bf16 of call `step` drawn on the device: amp * pe + sigma *
+    N(0, 1) with the positional features of the workload and noise from torch's
+    generator seeded by (seed, step). Same recipe and distribution as the host
+    generator, used where drawing ~10^9 normals on the host would dominate the run."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * w.seed + step)
+    sigma = w.sigma_at(step)
+    base = (pe * w.amp).view(1, w.N, 1, w.D)
+    out = []
+    for _ in range(3):
+        x = torch.randn((w.B, w.N, w.H, w.D), generator=gen, device=dev, dtype=torch.float32)
+        x.mul_(sigma).add_(base)
+        out.append(x.to(torch.bfloat16))
+        del x
+    return out
+
+
+def _kernel_entry(times, flop=None, peak=None, nbytes=None):
+    e = _stats(times)
+    if flop is not None:
+        e["achieved_tflops"] = round(flop / e["median"] / 1e9, 2)
+        e["frac_of_peak"] = round(flop / e["median"] / 1e9 / peak, 4)
+        e["peak_tflops"] = peak
+    if nbytes is not None:
+        e["achieved_GBps"] = round(nbytes / e["median"] / 1e6, 1)
+        e["frac_of_hbm_peak"] = round(nbytes / e["median"] / 1e6 / HBM_PEAK, 4)
+    return e
+
+
+def measure_workload(args, w, dev):
+    """Per-call timings of the larger configurations (one JSON line): Wan2.1-14B 720p
+    (bf16 path and the FP8 Q/K forward on the bf16 selection), HunyuanVideo 720p (one
+    dense selection step, then ten calls on the frozen CSR) and the 8192x8192 image with
+    the fixed structured mask. Medians with p10/p90 over HIP-event timings."""
+    import torch
+    from block_sparse_attention_reorder_amd import synth
+    from block_sparse_attention_reorder_amd.pipeline import BlockSparseAttention
+
+    stream = torch.cuda.current_stream()
+    pe = torch.from_numpy(synth.positional_features(w.grid, w.D)).to(dev)
+    bsa = BlockSparseAttention(w.grid, w.tile, w.B, w.H, w.D, device=dev)
+    D, H, B = w.D, w.H, w.B
+    qd, kd, vd = device_inputs(w, 0, dev, pe)
+    qt, kt, vt, ot = (torch.empty(bsa.tiled_shape(), dtype=torch.bfloat16, device=dev) for _ in range(4))
+    o = torch.empty((B, bsa.N, H, D), dtype=torch.bfloat16, device=dev)
+    reps, warm = args.steps, args.warmup
+    tile_bytes = 3 * (B * bsa.N * H * D * 2 + B * H * bsa.npad * D * 2)
+    untile_bytes = B * H * bsa.npad * D * 2 + B * bsa.N * H * D * 2
+    kern = {}
+    extra = {}
+
+    def tile_all():
+        bsa.tile_qk(qd, qt), bsa.tile_qk(kd, kt), bsa.tile_vt(vd, vt)
+
+    if w.mask == "grat":
+        t_build = []
+        for _ in range(warm + reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            csr = bsa.structured()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_build.append(e0.elapsed_time(e1))
+        kern["structured_mask"] = _kernel_entry(t_build[warm:])
+        stages = [("tile_qkv", tile_all), ("sparse_fwd", lambda: bsa.forward(qt, kt, vt, csr, out=ot)),
+                  ("untile", lambda: bsa.untile(ot, out=o))]
+        _stage_times(stages, warm, stream)
+        t = _stage_times(stages, reps, stream)
+        nnz = int(csr.row_ptr[-1].item())
+        kept = nnz * 4.0 * 64 * 64 * D
+        kern["tile_qkv"] = _kernel_entry(t["tile_qkv"], nbytes=tile_bytes)
+        kern["sparse_fwd"] = _kernel_entry(t["sparse_fwd"], kept, PEAK["bf16"])
+        kern["untile"] = _kernel_entry(t["untile"], nbytes=untile_bytes)
+        call_ms = sum(kern[s]["median"] for s in ("tile_qkv", "sparse_fwd", "untile"))
+        value = kept / call_ms / 1e9
+        what = "tile Q, K, V -> sparse forward over the fixed structured mask -> untile O"
+    else:
+        mass = torch.empty((B, H, bsa.nb, bsa.nb), dtype=torch.float32, device=dev)
+        csr = bsa.new_csr()
+        ws = bsa.workspace()
+        mws = bsa.mass_workspace()
+        stages = list(zip(["tile_qkv", "block_mass", "select", "sparse_fwd", "untile"],
+                          stage_fns(bsa, qd, kd, vd, qt, kt, vt, ot, o, mass, csr, ws, mws)))
+        _stage_times(stages, warm, stream)
+        nreps = reps if w.reuse_steps == 0 else max(3, reps // 4)
+        t = _stage_times(stages, nreps, stream)
+        nnz = int(csr.row_ptr[-1].item())
+        kept = nnz * 4.0 * 64 * 64 * D
+        mass_flop = 2.0 * bsa.npad * bsa.npad * D * H * B
+        kern["tile_qkv"] = _kernel_entry(t["tile_qkv"], nbytes=tile_bytes)
+        kern["block_mass"] = _kernel_entry(t["block_mass"], mass_flop, PEAK["bf16"])
+        kern["select"] = _kernel_entry(t["select"])
+        kern["sparse_fwd"] = _kernel_entry(t["sparse_fwd"], kept, PEAK["bf16"])
+        kern["untile"] = _kernel_entry(t["untile"], nbytes=untile_bytes)
+        step_ms = sum(kern[s]["median"] for s in ("tile_qkv", "block_mass", "select", "sparse_fwd", "untile"))
+        value = kept / step_ms / 1e9
+        what = "tile Q, K, V -> mass pass -> 99 % selection -> sparse forward -> untile O"
+        if w.fp8:
+            q8, k8 = (torch.empty(bsa.tiled_shape(), dtype=torch.uint8, device=dev) for _ in range(2))
+            qs, ks = (torch.empty((B, H, bsa.nb), dtype=torch.float32, device=dev) for _ in range(2))
+            st8 = [("tile_qk_fp8", lambda: (bsa.tile_fp8(qd, q8, qs), bsa.tile_fp8(kd, k8, ks))),
+                   ("sparse_fwd_fp8", lambda: bsa.forward(q8, k8, vt, csr, q_scale=qs, k_scale=ks, out=ot))]
+            _stage_times(st8, warm, stream)
+            t8 = _stage_times(st8, reps, stream)
+            # QK^T at the fp8 rate and P*V at the bf16 rate: 4 FLOP units per pair take
+            # 2/fp8 + 2/bf16 time units
+            mixed = 4.0 / (2.0 / PEAK["fp8"] + 2.0 / PEAK["bf16"])
+            fp8_bytes = 2 * (B * bsa.N * H * D * 2 + B * H * bsa.npad * D) + 2 * B * H * bsa.nb * 4
+            kern["tile_qk_fp8"] = _kernel_entry(t8["tile_qk_fp8"], nbytes=fp8_bytes)
+            e = _kernel_entry(t8["sparse_fwd_fp8"], kept, mixed)
+            e["frac_of_fp8_peak"] = round(kept / e["median"] / 1e9 / PEAK["fp8"], 4)
+            e["peak_note"] = "mixed peak: QK^T at 5.0 PFLOP/s fp8, P*V at 2.5 PFLOP/s bf16"
+            kern["sparse_fwd_fp8"] = e
+        if w.reuse_steps:
+            # one dense selection call (above), then calls 1..reuse_steps with their own
+            # inputs on the frozen CSR
+            one_time = kern["block_mass"]["median"] + kern["select"]["median"]
+            calls = [kern["tile_qkv"]["median"] + kern["sparse_fwd"]["median"] + kern["untile"]["median"]]
+            fwd = []
+            st = [("tile_qkv", tile_all), ("sparse_fwd", lambda: bsa.forward(qt, kt, vt, csr, out=ot)),
+                  ("untile", lambda: bsa.untile(ot, out=o))]
+            for s in range(1, w.reuse_steps + 1):
+                del qd, kd, vd
+                qd, kd, vd = device_inputs(w, s, dev, pe)
+                _stage_times(st, 1, stream)
+                ts = _stage_times(st, 3, stream)
+                med = {k_: sorted(v_)[1] for k_, v_ in ts.items()}
+                fwd.append(med["sparse_fwd"])
+                calls.append(sum(med.values()))
+            extra["frozen_calls"] = {
+                "sparse_fwd_ms_per_call": [round(x, 4) for x in fwd],
+                "sparse_fwd_mean_ms": round(sum(fwd) / len(fwd), 4),
+                "sparse_fwd_mean_tflops": round(kept / (sum(fwd) / len(fwd)) / 1e9, 2),
+                "one_time_mass_and_select_ms": round(one_time, 4),
+                "call_ms_amortised_over_%d_calls" % len(calls): round((one_time + sum(calls)) / len(calls), 4),
+            }
+            value = kept / ((one_time + sum(calls)) / len(calls)) / 1e9
+            what = (f"call 0: tile -> mass pass -> 99 % selection -> sparse forward -> untile; calls "
+                    f"1..{w.reuse_steps}: tile -> sparse forward on the frozen CSR -> untile; value over the "
+                    f"amortised call")
+            step_ms = (one_time + sum(calls)) / len(calls)
+    out = {
+        "metric": f"kept-block TFLOP/s per call, {w.name}",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": warm,
+        "ms_per_step": round(kept / value / 1e9, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: positional features + N(0,1) noise drawn on the device (seeded), bf16",
+        "config": {"workload": f"{w.name}: {w.note}", "grid": list(w.grid), "tile": list(w.tile), "batch": B,
+                   "heads": H, "head_dim": D, "nb": bsa.nb, "kept_pairs": nnz,
+                   "density": round(nnz / (bsa.R * bsa.nb), 4), "call": what},
+        "kernels_ms": kern,
+    }
+    out.update(extra)
     print(json.dumps(out))
 
 
