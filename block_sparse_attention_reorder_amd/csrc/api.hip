@@ -210,6 +210,7 @@ int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_
     if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return FPSA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
     if ((long)B * H * geo.nb > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
+    if ((long)geo.nb * fpsa::kBlock * D * 2 > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;   // 32-bit tile offsets
     int fp8;
     if (qk_dtype == FPSA_BF16) {
         if (q_scale != nullptr || k_scale != nullptr) return FPSA_ERR_INVALID_ARG;
@@ -370,6 +371,7 @@ int32_t fpsa_sparse_attn_fwd_varlen(const void* q, const void* k, const void* v,
     if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return FPSA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
     if ((long)B * H * NB > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
+    if ((long)NB * fpsa::kBlock * D * 2 > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;       // 32-bit tile offsets
     // the blocks as one flat row of 64-token tiles: every slot is a query slot
     fpsa_grid flat = {1, 1, 64 * NB, 1, 1, 64};
     Geom geo;

@@ -7,7 +7,7 @@
 // gfx950 mapping. A workgroup of four waves owns one query block (64 rows) of one
 // (batch, head) and walks the block's CSR list in order. The K and V tiles of each
 // kept block are copied once per workgroup into LDS with direct global-to-LDS loads
-// (global_load_lds_dwordx4, each wave moving a quarter of each tile in contiguous
+// (buffer_load_dwordx4 ... lds, each wave moving a quarter of each tile in contiguous
 // kilobytes) into two-slot K and V rings, K two blocks and V one block ahead of
 // use; one barrier per block. Wave w takes query rows 32*(w & 1) .. +31 and key
 // rows 32*(w >> 1) .. +31 of every block (the layout conventions are described in
@@ -103,12 +103,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     // share of contiguous kilobytes, lane l carrying 16 bytes each. An entry with no
     // block copies block 0 (never read as data).
     const int lane16 = 16 * lane;
+    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbytes, (uint32_t)(g.nb * kKBytes));
+    const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbytes, (uint32_t)(g.nb * kVBytes));
     auto copy_k = [&](int info, int slot) {
-        copy_to_lds<kKChunks>(kbytes + (long)block_of(info) * kKBytes + kKChunks * w * 1024,
+        copy_to_lds<kKChunks>(krs, (uint32_t)(block_of(info) * kKBytes + kKChunks * w * 1024),
                                kring + slot * kKBytes + kKChunks * w * 1024, lane16);
     };
     auto copy_v = [&](int info, int slot) {
-        copy_to_lds<kVChunks>(vbytes + (long)block_of(info) * kVBytes + kVChunks * w * 1024,
+        copy_to_lds<kVChunks>(vrs, (uint32_t)(block_of(info) * kVBytes + kVChunks * w * 1024),
                                vring + slot * kVBytes + kVChunks * w * 1024, lane16);
     };
 
@@ -145,10 +147,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
         // copy i < kKChunks: kilobyte i of this wave's share of K(j+2); then V(j+1)
         auto copy_one = [&](int i) {
             if (i < kKChunks)
-                copy_kb_to_lds(kbytes + (long)block_of(inf2) * kKBytes + (kKChunks * w + i) * 1024,
+                copy_kb_to_lds(krs, (uint32_t)(block_of(inf2) * kKBytes + (kKChunks * w + i) * 1024),
                                kring + (j & 1) * kKBytes + (kKChunks * w + i) * 1024, lane16);
             else
-                copy_kb_to_lds(vbytes + (long)block_of(infn) * kVBytes + (kVChunks * w + i - kKChunks) * 1024,
+                copy_kb_to_lds(vrs, (uint32_t)(block_of(infn) * kVBytes + (kVChunks * w + i - kKChunks) * 1024),
                                vring + ((j + 1) & 1) * kVBytes + (kVChunks * w + i - kKChunks) * 1024, lane16);
         };
         constexpr int kCopies = kKChunks + kVChunks;

@@ -51,17 +51,32 @@ constexpr float kRescaleSlack = 8.0f;   // log2 units
 // produces it past this point (sched_barrier only constrains the machine scheduler).
 __device__ __attribute__((always_inline)) inline void pin(float& x) { asm volatile("" : "+v"(x)); }
 
-// Copy one kilobyte from global `src` to LDS `dst`, lane l carrying bytes
-// 16*l .. 16*l+15 (global_load_lds_dwordx4: the LDS address comes from M0, set from
-// the uniform `dst`). Completion is counted by vmcnt.
-__device__ __attribute__((always_inline)) inline void copy_kb_to_lds(const uint8_t* src, uint8_t* dst, int lane16) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + lane16),
-                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+// Direct global-to-LDS copies go through a buffer resource (base and size in SGPRs,
+// the raw buffer format of gfx9-family targets in dword 3) rather than global_load_lds:
+// the compiler counts the global form against lgkmcnt as well, so every LDS read issued
+// before such a copy would wait for all of them at its first use, while the buffer form
+// leaves one wait per read. Offsets are 32-bit: a resource spans one (batch, head)'s
+// tiles, which callers keep below 2^31 bytes.
+__device__ __attribute__((always_inline)) inline __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, 0x00020000);
+}
+// Copy one kilobyte at byte `off` (wave-uniform) of buffer `rs` to LDS `dst`, lane l
+// carrying bytes 16*l .. 16*l+15 (buffer_load_dwordx4 ... lds: the LDS address comes
+// from M0, set from the uniform `dst`). Completion is counted by vmcnt.
+__device__ __attribute__((always_inline)) inline void copy_kb_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                                                      uint8_t* dst, int lane16) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, lane16,
+                                             (int)__builtin_amdgcn_readfirstlane(off), 0, 0);
 }
 template <int KB>
-__device__ __attribute__((always_inline)) inline void copy_to_lds(const uint8_t* src, uint8_t* dst, int lane16) {
+__device__ __attribute__((always_inline)) inline void copy_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                                                   uint8_t* dst, int lane16) {
 #pragma unroll
-    for (int j = 0; j < KB; ++j) copy_kb_to_lds(src + j * 1024, dst + j * 1024, lane16);
+    for (int j = 0; j < KB; ++j) copy_kb_to_lds(rs, off + j * 1024, dst + j * 1024, lane16);
 }
 
 // K operand of one 32-key half: bf16 (D/16 steps of 8 values) or e4m3 (D/64 steps

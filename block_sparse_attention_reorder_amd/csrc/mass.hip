@@ -80,8 +80,9 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
 
     const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(k) + bh * npad * D * 2;
     const int lane16 = 16 * lane;
+    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbytes, (uint32_t)(npad * D * 2));
     auto copy_k = [&](int kb, int slot) {
-        copy_to_lds<kKChunks>(kbytes + (long)(kb < g.nb ? kb : 0) * kKBytes + kKChunks * w * 1024,
+        copy_to_lds<kKChunks>(krs, (uint32_t)((kb < g.nb ? kb : 0) * kKBytes + kKChunks * w * 1024),
                               lds + slot * kKBytes + kKChunks * w * 1024, lane16);
     };
 

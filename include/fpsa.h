@@ -244,6 +244,8 @@ int32_t fpsa_retained_mass(const float* mass, int64_t R, int32_t nb, const int32
  *   that normalise o (-inf for a query with none; 0 for padding), or NULL.
  * o_f32: NULL, or tiled rows float32 [B, H, Npad, D] receiving o before its BF16
  *   rounding (the backward's delta = dO.o is then free of that rounding).
+ * Requires B*H*nb < 2^31 and Npad*D*2 < 2^31 (one (batch, head)'s V tiles are
+ * addressed with 32-bit offsets; FPSA_ERR_UNSUPPORTED otherwise).
  */
 int32_t fpsa_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t qk_dtype,
                              const float* q_scale, const float* k_scale, const int32_t* row_ptr,
@@ -386,8 +388,8 @@ int32_t fpsa_cluster_blocks(const int32_t* crow_ptr, const int32_t* ccol_idx, co
 /*
  * Block-sparse forward over blocks whose real keys are counted instead of following
  * from a token grid: block kb of slice bh holds key_counts[bh*NB + kb] real keys in
- * its first slots (0..64). Otherwise as fpsa_sparse_attn_fwd with BF16 q, k (QK
- * layout) and v (VT layout) of B*H*NB blocks; every query slot gets an output (the
+ * its first slots (0..64). Otherwise as fpsa_sparse_attn_fwd (size limits with
+ * nb = NB included) with BF16 q, k (QK layout) and v (VT layout) of B*H*NB blocks; every query slot gets an output (the
  * caller scatters the real ones back); lse and o_f32 optional.
  */
 int32_t fpsa_sparse_attn_fwd_varlen(const void* q, const void* k, const void* v,

@@ -154,6 +154,12 @@ def test_sparse_attn_validation(L):
     assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 80, g, 0.125, FAKE, None, None, None) == fpsa.ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, -1.0, FAKE, None, None, None) == fpsa.ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 64, g, 0.125, None, None, None, None) == fpsa.ERR_INVALID_ARG
+    # one (batch, head)'s tiles must stay below 2^31 bytes (32-bit tile offsets):
+    # 131,072 blocks of 64 x 128 bf16 values are exactly 2^31 bytes
+    big = grid(1, 8, 8 * 131072, 1, 8, 8)
+    assert f(FAKE, FAKE, FAKE, fpsa.BF16, None, None, FAKE, FAKE, 1, 1, 128, big, 0.125, FAKE, None, None, None) == fpsa.ERR_UNSUPPORTED
+    fv = L.fpsa_sparse_attn_fwd_varlen
+    assert fv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 131072, 0.1, FAKE, None, None, None) == fpsa.ERR_UNSUPPORTED
 
 
 def test_pattern_mask_validation(L):
