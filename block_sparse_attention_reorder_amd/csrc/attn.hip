@@ -14,7 +14,8 @@
 // attn_common.h); the two key halves of a query row carry separate online-softmax
 // states that are merged once at the end through LDS. Workgroups are remapped so
 // that each XCD gets a contiguous range of rows (same heads), which keeps the
-// shared K/V tiles in that XCD's L2.
+// shared K/V tiles in that XCD's L2; on 2D grids the rows run in strips of 8 block
+// columns (strip_row), which keeps a structured mask's row and column blocks shared.
 #include "attn_common.h"
 #include "fpsa_internal.h"
 
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     uint8_t* const kring = lds;
     uint8_t* const vring = lds + 2 * kKBytes;
 
-    const long r = xcd_row(R);
+    const long r = strip_row(xcd_row(R), g);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int qh = w & 1, kh = w >> 1;

@@ -29,6 +29,32 @@ __device__ inline long xcd_row(long nwg) {
     return (i % 8) * (full / 8) + i / 8;
 }
 
+// Order of the query blocks of a 2D (image) grid: vertical strips of kStripW block
+// columns, row-major inside a strip, so the ~64 workgroups an XCD runs at a time cover
+// an 8 x 8 patch of blocks. Under a criss-cross mask (a group keeps its whole block row
+// and column) a patch shares each row block among 8 workgroups and each column block
+// among 8, where a row-major order shares row blocks among 64 and column blocks among
+// none. A bijection on each (batch, head)'s rows; identity for 3D grids and for grids
+// at most kStripW blocks wide.
+constexpr int kStripW = 8;
+__device__ inline long strip_row(long r, const Geom& g) {
+    if (g.nt != 1 || g.nw <= kStripW) return r;
+    const long bh = r / g.nb;
+    const int i = (int)(r - bh * g.nb);
+    const int ns = (g.nw + kStripW - 1) / kStripW, full = (ns - 1) * g.nh * kStripW;
+    int rb, cb;
+    if (i < full) {
+        const int st = i / (g.nh * kStripW), rem = i - st * g.nh * kStripW;
+        rb = rem / kStripW;
+        cb = kStripW * st + rem % kStripW;
+    } else {
+        const int wl = g.nw - kStripW * (ns - 1), rem = i - full;
+        rb = rem / wl;
+        cb = kStripW * (ns - 1) + rem % wl;
+    }
+    return bh * g.nb + (long)rb * g.nw + cb;
+}
+
 // Direct global-to-LDS copies are counted by vmcnt, and __syncthreads() alone only
 // waits for LDS instructions (lgkmcnt), so a barrier that hands copied tiles to the
 // other waves must first wait for this wave's copies. s_waitcnt immediate on

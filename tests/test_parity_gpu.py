@@ -322,6 +322,21 @@ def test_sparse_forward_matches_masked_oracle(grid, H, D, num, den):
         assert np.abs(lse[0, h, slot[qs]] - want).max() < 2e-3
 
 
+@pytest.mark.parametrize("grid,H,D", [((1, 40, 88), 2, 128), ((1, 36, 140), 1, 64), ((1, 24, 64), 2, 128)])
+def test_image_grid_forward_matches_masked_oracle(grid, H, D):
+    """2D grids of 8x8 groups: the forward visits query blocks in strips of 8 block
+    columns (ragged last strip and last row here; 8 columns exactly in the last case)."""
+    tile = (1, 8, 8)
+    q, k, v = inputs(grid, 1, H, D, amp=1.5, seed=19)
+    nb = O.num_blocks(grid, tile)
+    m = synth.random_mass_rows(H * nb, nb, seed=nb + 7 * H, tie_frac=0.1, zero_frac=0.2)
+    rp, ci = O.select_blocks(m, 9, 10)
+    bsa, ot, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci)
+    mx, mean = output_errors(o, out, tok)
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+
+
 def test_forward_skips_out_of_range_blocks():
     grid, tile, H, D = (5, 6, 7), (4, 4, 4), 1, 64
     q, k, v = inputs(grid, 1, H, D, seed=10)
