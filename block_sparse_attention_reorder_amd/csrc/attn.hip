@@ -157,6 +157,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
         constexpr int kCopies = kKChunks + kVChunks;
         if constexpr (D == 128 && !FP8)
             block_main_bf16_d128<kCopies>(kst, vst, kh, lane, q, k, v, acc, s, sn, c, nref, l, smax, copy_one);
+        else if constexpr (D == 128 && FP8)
+            block_main_fp8_d128<kCopies>(kst, vst, kh, lane, q, k, v, acc, s, sn, c, nref, l, smax, copy_one);
         else
             block_main_generic<D, FP8, kCopies>(kst, vst, kh, lane, q, k, v, acc, s, sn, c, nref, l, smax, copy_one);
 

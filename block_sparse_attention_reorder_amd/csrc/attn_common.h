@@ -353,6 +353,82 @@ __device__ __attribute__((always_inline)) inline void block_main_bf16_d128(
 #undef FPSA_SB
 }
 
+
+// Main section of a kept block for e4m3 Q/K, D = 128, in hand-chosen issue order:
+// the two fp8 QK^T products of the next block (64-key steps) and the eight bf16 P*V
+// products of this one, each followed by exponentials and other vector work, with
+// the copies (NC kilobytes) after the QK^T and first P*V products.
+template <int NC, class Copy>
+__device__ __attribute__((always_inline)) inline void block_main_fp8_d128(
+    const uint8_t* kst, const uint8_t* vst, int kh, int lane, const KHalf<128, true>& q,
+    KHalf<128, true>& k, bf16x8 (&v)[4][2], f32x16 (&acc)[4], const f32x16& s, f32x16& sn, float c,
+    float nref, float& l, float& smax, Copy&& copy_one) {
+    static_assert(NC <= 8, "copies fit the issue slots");
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float pf[16];
+    uint32_t pw[8];
+    float rs0 = 0.0f, rs1 = 0.0f;
+    float ma, mb, md, me;
+    auto FM = [&](int i) { pf[i] = __builtin_fmaf(s[i], c, nref); };
+    auto EX = [&](int i) { pf[i] = __builtin_amdgcn_exp2f(pf[i]); };
+    auto CV = [&](int i) {
+        bf16x2 pr;
+        pr[0] = (__bf16)pf[i];
+        pr[1] = (__bf16)pf[i + 1];
+        pw[i >> 1] = __builtin_bit_cast(uint32_t, pr);
+    };
+    auto DT = [&](int wi) {
+        const bf16x2 pr = __builtin_bit_cast(bf16x2, pw[wi]);
+        if (wi < 4) rs0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs0, false);
+        else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs1, false);
+    };
+    auto QK = [&](int i) {
+        if (i == 0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sn[e] = 0.0f;
+        }
+        sn = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k.f[i], q.f[i], sn, 0, 0, 0, 0, 0, 0);
+    };
+    auto PV = [&](int t, int cc) {
+        const i32x4 wv = {(int)pw[4 * cc], (int)pw[4 * cc + 1], (int)pw[4 * cc + 2], (int)pw[4 * cc + 3]};
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[t][cc], __builtin_bit_cast(bf16x8, wv), acc[t], 0, 0, 0);
+    };
+    auto CP = [&](int i) {
+        if (i < NC) copy_one(i);
+    };
+#define FPSA_SB __builtin_amdgcn_sched_barrier(0)
+    lds_khalf<128, true>(k, kst, kh, lane);
+    lds_vhalf<128>(v, vst, kh, lane);
+    FM(0); FM(1); FM(2); FM(3); EX(0); EX(1);
+    FPSA_SB;
+    QK(0); CP(0); CP(1); EX(2); FM(4); EX(3); FM(5); CV(0); FM(6);
+    FPSA_SB;
+    QK(1); CP(2); CP(3); EX(4); FM(7); EX(5); FM(8); CV(2); FM(9); EX(6); EX(7); CV(4); CV(6);
+    FPSA_SB;
+    PV(0, 0); CP(4); EX(8); FM(10); DT(0); DT(1);
+    FPSA_SB;
+    PV(1, 0); CP(5); EX(9); FM(11); DT(2); CV(8);
+    FPSA_SB;
+    PV(2, 0); CP(6); EX(10); FM(12); EX(11); FM(13); DT(3);
+    FPSA_SB;
+    PV(3, 0); CP(7); EX(12); FM(14); EX(13); FM(15); CV(10); DT(4);
+    FPSA_SB;
+    EX(14); EX(15); CV(12); CV(14); DT(5);
+    FPSA_SB;
+    PV(0, 1); DT(6); DT(7);
+    ma = fmaxf(fmaxf(sn[0], sn[1]), fmaxf(sn[2], sn[3]));
+    FPSA_SB;
+    PV(1, 1); mb = fmaxf(fmaxf(sn[4], sn[5]), fmaxf(sn[6], sn[7]));
+    md = fmaxf(fmaxf(sn[8], sn[9]), fmaxf(sn[10], sn[11]));
+    FPSA_SB;
+    PV(2, 1); me = fmaxf(fmaxf(sn[12], sn[13]), fmaxf(sn[14], sn[15]));
+    l += wave_add32(rs0 + rs1);
+    FPSA_SB;
+    PV(3, 1); smax = wave_max32(fmaxf(fmaxf(ma, mb), fmaxf(md, me)));
+    FPSA_SB;
+#undef FPSA_SB
+}
+
 // Merge the two key halves of each query row and store: wave (qh, 1) hands its
 // state to wave (qh, 0) through `xch` (LDS the caller no longer uses, 2 x (kDT*16+2)
 // x 64 floats); wave (qh, 0) rescales both to the larger reference, normalises and
