@@ -14,8 +14,11 @@
 //   k_bwd_dkdv  one workgroup per key block, walking the query blocks that keep it
 //               (the transposed CSR); dK and dV stay in registers;
 //   k_bwd_dq    one workgroup per query block, walking its kept key blocks.
-// Both walk their blocks through three LDS slots fed from two register staging sets:
-// a block's tiles are loaded two blocks ahead of their use.
+// k_bwd_dkdv walks its blocks through three LDS slots fed from two register staging
+// sets (a block's tiles are loaded two blocks ahead of their use); k_bwd_dq copies each
+// block's K and V tiles straight into one of two LDS slots an iteration ahead (copies
+// issued from inline asm, which the compiler does not wait for), which keeps it at 218
+// registers and so at two workgroups per CU.
 // Every operand comes from the QK tiled layout. Products whose reduction runs over
 // tokens (P^T dO, dS^T Q, dS K) need the tile transposed - channel per lane, tokens
 // along the operand - which the gfx950 transposing LDS read (ds_read_b64_tr_b16)
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
 // ---------------------------------------------------------------- dQ
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_bwd_dq(
+__global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, float c,
@@ -314,15 +317,14 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
     constexpr int kSlot = 2 * kTile;              // K tile, V tile
     constexpr int kDT = D / 32;
     static_assert(kDT * 16 * 64 * 4 <= kSlot, "reduction buffer fits a slot");
-    __shared__ __attribute__((aligned(16))) uint8_t sl0[kSlot];
-    __shared__ __attribute__((aligned(16))) uint8_t sl1[kSlot];
-    __shared__ __attribute__((aligned(16))) uint8_t sl2[kSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlot];   // two slots
 
     const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qh = w & 1, kh = w >> 1;
     const long row = xcd_row(gridDim.x);
     const long bh = row / g.nb;
+    const long npad = 64L * g.nb;
 
     KHalf<D, false> qf, gf;                        // B operands: query (lane % 32) of half qh
     load_khalf<D, false>(qf, q, row * 64, qh, lane);
@@ -347,26 +349,18 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
         if (jj >= n) return -1;
         return block_info(g, __builtin_amdgcn_readfirstlane(col_idx[e0 + jj]));
     };
-    // two register staging sets, as in the key-gradient kernel
-    constexpr int kCh = kTile / (256 * 16);
-    i32x4 rk[2][kCh], rv[2][kCh];
-    auto fetch = [&](int info, auto set) {
-        constexpr int P = decltype(set)::value;
-        const long base = (bh * g.nb + (info < 0 ? 0 : (info & kBlockIdMask))) * 64 * D;
-        const i32x4* ks = reinterpret_cast<const i32x4*>(k + base);
-        const i32x4* vs = reinterpret_cast<const i32x4*>(v + base);
+    // K and V tiles of a block copied straight into an LDS slot, this wave moving its
+    // quarter of each in whole kilobytes (a missing block copies block 0)
+    constexpr int kCh = kTile / 1024 / 4;
+    const int lane16 = 16 * lane;
+    const i32x4r krs = tile_rsrc_raw(k + bh * npad * D, (uint32_t)(npad * D * 2));
+    const i32x4r vrs = tile_rsrc_raw(v + bh * npad * D, (uint32_t)(npad * D * 2));
+    auto copy_block = [&](int info, uint8_t* dst) {
+        const uint32_t base = (uint32_t)((info < 0 ? 0 : (info & kBlockIdMask)) * kTile);
 #pragma unroll
-        for (int i = 0; i < kCh; ++i) {
-            rk[P][i] = ks[tid + 256 * i];
-            rv[P][i] = vs[tid + 256 * i];
-        }
-    };
-    auto stash = [&](auto set, uint8_t* dst) {
-        constexpr int P = decltype(set)::value;
-#pragma unroll
-        for (int i = 0; i < kCh; ++i) {
-            *reinterpret_cast<i32x4*>(dst + (tid + 256 * i) * 16) = rk[P][i];
-            *reinterpret_cast<i32x4*>(dst + kTile + (tid + 256 * i) * 16) = rv[P][i];
+        for (int ch = 0; ch < kCh; ++ch) {
+            copy_kb_asm(krs, base + (kCh * w + ch) * 1024, dst + (kCh * w + ch) * 1024, lane16);
+            copy_kb_asm(vrs, base + (kCh * w + ch) * 1024, dst + kTile + (kCh * w + ch) * 1024, lane16);
         }
     };
 
@@ -416,36 +410,27 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(
         }
     };
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    auto iter = [&](auto slot, auto set, int jj) {
-        constexpr int S = decltype(slot)::value;
-        uint8_t* cur = S == 0 ? sl0 : (S == 1 ? sl1 : sl2);
-        uint8_t* next = S == 0 ? sl1 : (S == 1 ? sl2 : sl0);
-        __syncthreads();
-        fetch(info_at(jj + 2), set);            // unconditional, as above
-        const int icur = info_at(jj);
-        if (icur >= 0) compute(cur, icur);
-        stash(std::integral_constant<int, 1 - decltype(set)::value>(), next);
-    };
+    // Two slots: block j sits in slot j % 2. Iteration j first waits for its own copy
+    // (issued an iteration earlier) and for every wave to leave iteration j - 1, then
+    // starts the copy of block j + 1 into the other slot and computes block j.
     if (n > 0) {
-        fetch(info_at(0), I0());
-        fetch(info_at(1), I1());
-        stash(I0(), sl0);
-        for (int jj = 0; jj < n; jj += 6) {
-            iter(std::integral_constant<int, 0>(), I0(), jj);
-            if (jj + 1 < n) iter(std::integral_constant<int, 1>(), I1(), jj + 1);
-            if (jj + 2 < n) iter(std::integral_constant<int, 2>(), I0(), jj + 2);
-            if (jj + 3 < n) iter(std::integral_constant<int, 0>(), I1(), jj + 3);
-            if (jj + 4 < n) iter(std::integral_constant<int, 1>(), I0(), jj + 4);
-            if (jj + 5 < n) iter(std::integral_constant<int, 2>(), I1(), jj + 5);
+        int icur = info_at(0);
+        copy_block(icur, lds);
+        for (int jj = 0; jj < n; ++jj) {
+            const int inext = info_at(jj + 1);
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (jj + 1 < n) copy_block(inext, lds + ((jj + 1) & 1) * kSlot);
+            if (icur >= 0) compute(lds + (jj & 1) * kSlot, icur);
+            icur = inext;
         }
     }
+    wait_vmcnt<0>();
     __syncthreads();
 
     // add the two key halves; element i of tile t: query 32*qh + 8*(i/4) + 4*hb +
     // i%4, channel 32*t + lane%32
-    float* xch = reinterpret_cast<float*>(qh == 0 ? sl0 : sl1);
+    float* xch = reinterpret_cast<float*>(lds + qh * kSlot);
     if (kh == 1) {
 #pragma unroll
         for (int t = 0; t < kDT; ++t)
