@@ -12,20 +12,20 @@
 //               forward's float32 copy) and lse in base 2 (+inf for padding or
 //               a query without keys, so its probabilities are exactly 0);
 //   k_bwd_dkdv  one workgroup per key block, walking the query blocks that keep it
-//               (the transposed CSR); dK and dV stay in registers;
+//               (the transposed CSR); dK and dV stay in registers, each wave holding
+//               half the channels of its 32 keys (P and dS are exchanged through LDS);
 //   k_bwd_dq    one workgroup per query block, walking its kept key blocks.
-// k_bwd_dkdv walks its blocks through three LDS slots fed from two register staging
-// sets (a block's tiles are loaded two blocks ahead of their use); k_bwd_dq copies each
-// block's K and V tiles straight into one of two LDS slots an iteration ahead (copies
-// issued from inline asm, which the compiler does not wait for), which keeps it at 218
-// registers and so at two workgroups per CU.
+// Both copy each block's tiles (Q and dO, or K and V) straight into one of two LDS
+// slots an iteration ahead, with copies issued from inline asm that the compiler does
+// not wait for; without register staging both fit 256 registers, so two workgroups
+// share a CU.
 // Every operand comes from the QK tiled layout. Products whose reduction runs over
 // tokens (P^T dO, dS^T Q, dS K) need the tile transposed - channel per lane, tokens
 // along the operand - which the gfx950 transposing LDS read (ds_read_b64_tr_b16)
 // delivers from the same LDS copy: within each 16-lane group, output lane i element
 // j is element i%4 of input lane 4j + i/4. Each wave owns a 32 x 32 (query, key)
 // sub-tile of every block pair; the two partial sums of each output half are added
-// through LDS at the end.
+// through LDS at the end (dQ) or exchanged before the products (dK, dV).
 #include <type_traits>
 
 #include "attn_common.h"
@@ -108,24 +108,31 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const OT* __restrict__ o,
 
 // ---------------------------------------------------------------- dK, dV
 
+// Two phases per query block. Phase 1, wave (kh, r): the S and dP products of its 32
+// keys against query half r, then P and dS for those 32 x 32 pairs, packed as the A
+// operands of the token-reduction products and written to an exchange buffer in LDS.
+// Phase 2, wave (kh, r): dV and dK of its 32 keys for channel half r, over all 64
+// queries, from the four P and dS operands of its key half. Each wave's accumulators
+// thus cover half the channels (64 registers instead of 128), which with the direct
+// copies into two slots keeps the kernel at two workgroups per CU.
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
+__global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, Geom g, float c,
     float scale, __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
     constexpr int kTile = 64 * D * 2;
-    constexpr int kSlot = 2 * kTile + 512;        // Q tile, dO tile, lse2[64], delta[64]
+    constexpr int kSlot = 2 * kTile;              // Q tile, dO tile
     constexpr int kDT = D / 32;
-    static_assert(2 * kDT * 16 * 64 * 4 <= kSlot, "reduction buffer fits a slot");
-    // three LDS slots
-    __shared__ __attribute__((aligned(16))) uint8_t sl0[kSlot];
-    __shared__ __attribute__((aligned(16))) uint8_t sl1[kSlot];
-    __shared__ __attribute__((aligned(16))) uint8_t sl2[kSlot];
+    constexpr int kHT = kDT / 2;                  // 32-channel tiles per channel half
+    static_assert(kHT >= 1, "two channel halves");
+    // two slots, then the exchange buffer [kh][r][ks][P, dS] of 1 KB operands
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlot + 16 * 1024];
+    uint8_t* const xbuf = lds + 2 * kSlot;
 
     const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kh = w & 1, qh = w >> 1;
+    const int kh = w & 1, r = w >> 1;             // phase 1: query half r; phase 2: channel half r
     const long col = xcd_row(gridDim.x);
     const long bh = col / g.nb;
     const int kb = (int)(col - bh * g.nb);
@@ -137,11 +144,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
     keep_resident<D>(kf);
     keep_resident<D>(vf);
     const bool kvalid = g.valid(kb, 32 * kh + (lane & 31));
-    const int trb = tr_base<D>(32 * qh, lane);
 
-    f32x16 accv[kDT], acck[kDT];
+    f32x16 accv[kHT], acck[kHT];
 #pragma unroll
-    for (int t = 0; t < kDT; ++t)
+    for (int t = 0; t < kHT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) accv[t][i] = acck[t][i] = 0.0f;
 
@@ -152,56 +158,50 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
         const int x = __builtin_amdgcn_readfirstlane(row_idx[e0 + jj]);
         return (x >= 0 && x < g.nb) ? x : -1;
     };
-    // Two register staging sets: the tiles of block j + 2 are loaded during iteration j
-    // and written to LDS at the end of iteration j + 1, so each load has two blocks of
-    // work to land. A missing block loads block 0.
-    constexpr int kCh = kTile / (256 * 16);       // 16-byte pieces per thread per tile
-    i32x4 rq[2][kCh], rg[2][kCh];
-    float rl[2] = {0.0f, 0.0f};
-    auto fetch = [&](int qbk, auto set) {
-        constexpr int P = decltype(set)::value;
-        const long base = (bh * g.nb + (qbk < 0 ? 0 : qbk)) * 64;
-        const i32x4* qs = reinterpret_cast<const i32x4*>(q + base * D);
-        const i32x4* gs = reinterpret_cast<const i32x4*>(dout + base * D);
+    // Q and dO tiles of a query block copied straight into a slot, this wave moving a
+    // quarter of each in whole kilobytes (a missing block copies block 0)
+    constexpr int kCh = kTile / 1024 / 4;
+    const int lane16 = 16 * lane;
+    const i32x4r qrs = tile_rsrc_raw(q + bh * npad * D, (uint32_t)(npad * D * 2));
+    const i32x4r grs = tile_rsrc_raw(dout + bh * npad * D, (uint32_t)(npad * D * 2));
+    auto copy_block = [&](int qbk, uint8_t* dst) {
+        const uint32_t base = (uint32_t)((qbk < 0 ? 0 : qbk) * kTile);
 #pragma unroll
-        for (int i = 0; i < kCh; ++i) {
-            rq[P][i] = qs[tid + 256 * i];
-            rg[P][i] = gs[tid + 256 * i];
+        for (int ch = 0; ch < kCh; ++ch) {
+            copy_kb_asm(qrs, base + (kCh * w + ch) * 1024, dst + (kCh * w + ch) * 1024, lane16);
+            copy_kb_asm(grs, base + (kCh * w + ch) * 1024, dst + kTile + (kCh * w + ch) * 1024, lane16);
         }
-        rl[P] = (tid < 64 ? lse2 : delta)[base + (tid & 63)];   // threads >= 128 load unused values
     };
-    auto stash = [&](auto set, uint8_t* dst) {
-        constexpr int P = decltype(set)::value;
-#pragma unroll
-        for (int i = 0; i < kCh; ++i) {
-            *reinterpret_cast<i32x4*>(dst + (tid + 256 * i) * 16) = rq[P][i];
-            *reinterpret_cast<i32x4*>(dst + kTile + (tid + 256 * i) * 16) = rg[P][i];
-        }
-        if (tid < 128) reinterpret_cast<float*>(dst + 2 * kTile)[tid] = rl[P];
+    // exchange operand (key half kh, query half qq, step ks, kind 0 = P / 1 = dS)
+    auto xop = [&](int qq, int ks, int kind) -> uint8_t* {
+        return xbuf + (((kh * 2 + qq) * 2 + ks) * 2 + kind) * 1024 + 16 * lane;
     };
 
-    auto compute = [&](const uint8_t* sq) {
-        const uint8_t* sg = sq + kTile;
-        const float* sl = reinterpret_cast<const float*>(sq + 2 * kTile);
-        // operand reads first (the S and dP products then issue back to back)
-        bf16x8 qa[D / 16], ga[D / 16];
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const int off = (qh * (D / 16) + st) * 1024 + 16 * lane;
-            qa[st] = *reinterpret_cast<const bf16x8*>(sq + off);
-            ga[st] = *reinterpret_cast<const bf16x8*>(sg + off);
-        }
-        // lse2 and delta of the rows this lane holds: queries 32*qh + 16*ks +
-        // 8*u + 4*hb + (0..3)
-        f32x4 L[2][2], G[2][2];
+    // lse2 and delta of the rows this lane holds in phase 1 (queries 32*r + 16*ks + 8*u +
+    // 4*hb + (0..3)), loaded one block ahead into registers: issued right after the
+    // barrier, before the copies, and first used an iteration later, after the next
+    // vmcnt(0), so no wait of the compiler's ever covers a copy in flight
+    f32x4 LG[2][2][2][2];                          // [set][L or G][ks][u]
+    auto load_lg = [&](int qbk, f32x4 (&L)[2][2], f32x4 (&G)[2][2]) {
+        const long qrow = (bh * g.nb + (qbk < 0 ? 0 : qbk)) * 64 + 32 * r + 4 * hb;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                L[ks][u] = *reinterpret_cast<const f32x4*>(sl + 32 * qh + 16 * ks + 8 * u + 4 * hb);
-                G[ks][u] = *reinterpret_cast<const f32x4*>(sl + 64 + 32 * qh + 16 * ks + 8 * u + 4 * hb);
+                L[ks][u] = *reinterpret_cast<const f32x4*>(lse2 + qrow + 16 * ks + 8 * u);
+                G[ks][u] = *reinterpret_cast<const f32x4*>(delta + qrow + 16 * ks + 8 * u);
             }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto phase1 = [&](const uint8_t* sq, const f32x4 (&L)[2][2], const f32x4 (&G)[2][2]) {
+        const uint8_t* sg = sq + kTile;
+        bf16x8 qa[D / 16], ga[D / 16];
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            const int off = (r * (D / 16) + st) * 1024 + 16 * lane;
+            qa[st] = *reinterpret_cast<const bf16x8*>(sq + off);
+            ga[st] = *reinterpret_cast<const bf16x8*>(sg + off);
+        }
         f32x16 s, dp;
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
@@ -210,99 +210,88 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[st], kf.b[st], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[st], vf.b[st], dp, 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // transposed operands of the two token-reduction products, read while the
-        // products above drain
-        bf16x8 gtr[2][kDT], qtr[2][kDT];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int t = 0; t < kDT; ++t) {
-                const int off = trb + t * 2048 + ks * 256;
-                gtr[ks][t] = tr_operand(sg, off);
-                qtr[ks][t] = tr_operand(sq, off);
-            }
-        __builtin_amdgcn_sched_barrier(0);
-        // element i: query 32*qh + 8*(i/4) + 4*hb + i%4, key 32*kh + lane%32
+        // element i: query 32*r + 8*(i/4) + 4*hb + i%4, key 32*kh + lane%32
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            float p[8], ds[8];
+            float pv[8], ds[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int i = 8 * ks + t;
                 const float lq = L[ks][t >> 2][t & 3];
                 const float gq = G[ks][t >> 2][t & 3];
                 const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq)) : 0.0f;
-                p[t] = pp;
+                pv[t] = pp;
                 ds[t] = pp * (dp[i] - gq);
             }
-            const bf16x8 pa = pack_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-            const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            *reinterpret_cast<bf16x8*>(xop(r, ks, 0)) = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+            *reinterpret_cast<bf16x8*>(xop(r, ks, 1)) = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        }
+    };
+    auto phase2 = [&](const uint8_t* sq) {
+        const uint8_t* sg = sq + kTile;
 #pragma unroll
-            for (int t = 0; t < kDT; ++t) {
-                accv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, gtr[ks][t], accv[t], 0, 0, 0);
-                acck[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, qtr[ks][t], acck[t], 0, 0, 0);
+        for (int qq = 0; qq < 2; ++qq) {
+            const int trb = tr_base<D>(32 * qq, lane);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 pa = *reinterpret_cast<const bf16x8*>(xop(qq, ks, 0));
+                const bf16x8 da = *reinterpret_cast<const bf16x8*>(xop(qq, ks, 1));
+#pragma unroll
+                for (int t = 0; t < kHT; ++t) {
+                    const int off = trb + (kHT * r + t) * 2048 + ks * 256;
+                    accv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, tr_operand(sg, off), accv[t], 0, 0, 0);
+                    acck[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, tr_operand(sq, off), acck[t], 0, 0, 0);
+                }
             }
         }
     };
 
-    // block j sits in LDS slot j % 3 and passes through staging set j % 2; iteration j
-    // computes it after the barrier, between loading block j + 2 and writing block
-    // j + 1 (loaded an iteration earlier) to its slot, which was last read in
-    // iteration j - 2
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    auto iter = [&](auto slot, auto set, int jj) {
-        constexpr int S = decltype(slot)::value;
-        uint8_t* cur = S == 0 ? sl0 : (S == 1 ? sl1 : sl2);
-        uint8_t* next = S == 0 ? sl1 : (S == 1 ? sl2 : sl0);
+    // Two slots: block j sits in slot j % 2; iteration j waits for its copy (issued an
+    // iteration earlier) and for every wave to leave iteration j - 1, starts the copy of
+    // block j + 1 into the other slot, then runs both phases with a barrier between them
+    // (the exchange buffer is rewritten only after the next iteration's barrier).
+    // iteration jj uses register set P = jj % 2 and slot jj % 2 (the loop is unrolled by
+    // two so both stay compile-time: a register copy would make the compiler wait for
+    // the loads, and with them for the copies in flight)
+    auto iter = [&](auto set, int jj, int qcur, int qnext) {
+        constexpr int P = decltype(set)::value;
+        wait_vmcnt<0>();
         __syncthreads();
-        // unconditional (a dummy block past the end) so that the waits before each
-        // stash count exactly one newer set in flight
-        fetch(qb_at(jj + 2), set);
-        if (qb_at(jj) >= 0) compute(cur);
-        stash(std::integral_constant<int, 1 - decltype(set)::value>(), next);
+        load_lg(qnext, LG[1 - P][0], LG[1 - P][1]);   // unconditional (block 0 past the end)
+        if (jj + 1 < n) copy_block(qnext, lds + (1 - P) * kSlot);
+        if (qcur >= 0) {                               // uniform
+            phase1(lds + P * kSlot, LG[P][0], LG[P][1]);
+            __syncthreads();
+            phase2(lds + P * kSlot);
+        }
     };
     if (n > 0) {
-        fetch(qb_at(0), I0());
-        fetch(qb_at(1), I1());
-        stash(I0(), sl0);
-        for (int jj = 0; jj < n; jj += 6) {
-            iter(std::integral_constant<int, 0>(), I0(), jj);
-            if (jj + 1 < n) iter(std::integral_constant<int, 1>(), I1(), jj + 1);
-            if (jj + 2 < n) iter(std::integral_constant<int, 2>(), I0(), jj + 2);
-            if (jj + 3 < n) iter(std::integral_constant<int, 0>(), I1(), jj + 3);
-            if (jj + 4 < n) iter(std::integral_constant<int, 1>(), I0(), jj + 4);
-            if (jj + 5 < n) iter(std::integral_constant<int, 2>(), I1(), jj + 5);
+        int qcur = qb_at(0);
+        load_lg(qcur, LG[0][0], LG[0][1]);
+        copy_block(qcur, lds);
+        for (int jj = 0; jj < n; jj += 2) {
+            const int q1 = qb_at(jj + 1);
+            iter(std::integral_constant<int, 0>(), jj, qcur, q1);
+            if (jj + 1 < n) {
+                const int q2 = qb_at(jj + 2);
+                iter(std::integral_constant<int, 1>(), jj + 1, q1, q2);
+                qcur = q2;
+            }
         }
     }
-    __syncthreads();
+    wait_vmcnt<0>();
 
-    // add the two query halves' partial sums; element i of tile t: key 32*kh +
-    // 8*(i/4) + 4*hb + i%4, channel 32*t + lane%32
-    float* xch = reinterpret_cast<float*>(kh == 0 ? sl0 : sl1);
-    if (qh == 1) {
+    // element i of tile t: key 32*kh + 8*(i/4) + 4*hb + i%4, channel 32*(kHT*r + t) + lane%32
+    const long row0 = bh * npad + 64L * kb + 32 * kh;
 #pragma unroll
-        for (int t = 0; t < kDT; ++t)
+    for (int t = 0; t < kHT; ++t)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                xch[((0 * kDT + t) * 16 + i) * 64 + lane] = accv[t][i];
-                xch[((1 * kDT + t) * 16 + i) * 64 + lane] = acck[t][i];
-            }
-    }
-    __syncthreads();
-    if (qh == 0) {
-        const long row0 = bh * npad + 64L * kb + 32 * kh;
-#pragma unroll
-        for (int t = 0; t < kDT; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const long r = row0 + 8 * (i >> 2) + 4 * hb + (i & 3);
-                const int ch = 32 * t + (lane & 31);
-                dv[r * D + ch] = (__bf16)(accv[t][i] + xch[((0 * kDT + t) * 16 + i) * 64 + lane]);
-                dk[r * D + ch] = (__bf16)(scale * (acck[t][i] + xch[((1 * kDT + t) * 16 + i) * 64 + lane]));
-            }
-    }
+        for (int i = 0; i < 16; ++i) {
+            const long rr = row0 + 8 * (i >> 2) + 4 * hb + (i & 3);
+            const int ch = 32 * (kHT * r + t) + (lane & 31);
+            dv[rr * D + ch] = (__bf16)accv[t][i];
+            dk[rr * D + ch] = (__bf16)(scale * acck[t][i]);
+        }
 }
 
 // ---------------------------------------------------------------- dQ
