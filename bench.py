@@ -195,7 +195,7 @@ def main():
                            args.steps, stream, flush=_flusher(dev))
     flushed = {s: _stats(x) for s, x in flushed.items()}
 
-    extras = next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, max(3, args.steps // 4))
+    extras = next_rows(bsa, w, qd, kd, qt, kt, vt, ot, mass, csr, stream, max(3, args.steps // 4))
 
     if args.calibrate_copy:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
@@ -458,7 +458,7 @@ def _timed(fn, stream, reps):
     return ev[0].elapsed_time(ev[1]) / reps
 
 
-def next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, reps):
+def next_rows(bsa, w, qd, kd, qt, kt, vt, ot, mass, csr, stream, reps):
     """Timings of the rows beyond the headline path on the same inputs, after the
     timed region: the retained-mass monitor over the step's masses and CSR, and
     fixed per-head patterns (mask build and the forward over them)."""
@@ -497,6 +497,17 @@ def next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, reps):
     t_bwd = _timed(lambda: bsa.backward(qt, kt, vq, o32, gt, lse, csr, csc, grads=grads, workspace=bws),
                    stream, reps)
     bflop = nnz * 10.0 * 64 * 64 * w.D          # five 64x64xD products per kept pair
+    # backward of the FP8 Q/K forward over the same CSR: Q and K as e4m3 code values in
+    # bf16 with the tile scales, lse and float32 output from the FP8 forward
+    q8, qs = bsa.tile_fp8(qd)
+    k8, ks = bsa.tile_fp8(kd)
+    lse8 = torch.empty_like(lse)
+    o32f = torch.empty_like(o32)
+    bsa.forward(q8, k8, vt, csr, q_scale=qs, k_scale=ks, out=ot, lse=lse8, out_f32=o32f)
+    qc, kc = bsa.dequantize(q8, None), bsa.dequantize(k8, None)
+    t_codes = _timed(lambda: (bsa.dequantize(q8, None, out=qc), bsa.dequantize(k8, None, out=kc)), stream, reps)
+    t_bwd8 = _timed(lambda: bsa.backward(qc, kc, vq, o32f, gt, lse8, csr, csc, grads=grads, workspace=bws,
+                                         q_scale=qs, k_scale=ks), stream, reps)
     sem = semantic_row(bsa, w, qt, stream, reps)
     return {
         "retained_mass": {"ms": round(t_mon, 4), "bound": "hbm",
@@ -514,7 +525,12 @@ def next_rows(bsa, w, qt, kt, vt, ot, mass, csr, stream, reps):
                      "tflops": round(bflop / t_bwd / 1e9, 2),
                      "frac_of_bf16_peak": round(bflop / t_bwd / 1e9 / PEAK["bf16"], 4),
                      "transpose_ms": round(t_tr, 4),
-                     "inputs": "Q, K from the step; V (QK layout) and dO random normal bf16"},
+                     "inputs": "Q, K from the step; V (QK layout) and dO random normal bf16",
+                     "fp8": {"ms": round(t_bwd8, 4), "code_tiles_ms": round(t_codes, 4),
+                             "tflops": round(bflop / t_bwd8 / 1e9, 2),
+                             "frac_of_bf16_peak": round(bflop / t_bwd8 / 1e9 / PEAK["bf16"], 4),
+                             "what": "backward of the FP8 Q/K forward: e4m3 code values of Q and K in bf16 "
+                                     "with the tile scales (straight-through quantizer)"}},
         "semantic_permutation": sem,
     }
 

@@ -99,6 +99,18 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
     return hip_status();
 }
 
+int32_t fpsa_dequantize_tiles(const void* src, const float* scale, int32_t B, int32_t H, int32_t D,
+                              const fpsa_grid* g, void* dst, void* stream) {
+    Geom geo;
+    if (!make_geom(g, &geo) || !dims_ok(B, H)) return FPSA_ERR_INVALID_ARG;
+    if (src == nullptr || dst == nullptr) return FPSA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
+    const long blocks = (long)B * H * geo.nb;
+    if (blocks > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
+    fpsa::launch_dequant_tiles(src, scale, dst, blocks, D, static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
 size_t fpsa_transpose_workspace_bytes(int64_t R, int32_t nb) {
     if (R <= 0 || nb <= 0 || R > (1L << 24)) return 0;
     return fpsa::transpose_workspace_bytes((long)R, nb);
@@ -246,7 +258,8 @@ int32_t fpsa_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int32
 int32_t fpsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                              int32_t o_dtype, const void* dout, const float* lse, const int32_t* row_ptr,
                              const int32_t* col_idx, const int32_t* col_ptr,
-                             const int32_t* row_idx, int32_t B, int32_t H, int32_t D,
+                             const int32_t* row_idx, const float* q_scale, const float* k_scale,
+                             int32_t B, int32_t H, int32_t D,
                              const fpsa_grid* g, float softmax_scale, void* dq, void* dk, void* dv,
                              void* workspace, size_t workspace_bytes, void* stream) {
     Geom geo;
@@ -260,10 +273,12 @@ int32_t fpsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const 
         return FPSA_ERR_INVALID_ARG;
     if (!(softmax_scale > 0.0f) || softmax_scale == INFINITY) return FPSA_ERR_INVALID_ARG;
     if (o_dtype != FPSA_BF16 && o_dtype != FPSA_F32) return FPSA_ERR_UNSUPPORTED;
+    if ((q_scale == nullptr) != (k_scale == nullptr)) return FPSA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
     if ((long)B * H * geo.nb > 0x7FFFFFFFL) return FPSA_ERR_UNSUPPORTED;
     if (workspace_bytes < fpsa::bwd_workspace_bytes(B, H, geo.nb)) return FPSA_ERR_CAPACITY;
-    fpsa::launch_sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, B, H, D,
+    fpsa::launch_sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, q_scale, k_scale,
+                                 B, H, D,
                                  geo, softmax_scale, o_dtype == FPSA_F32, dq, dk, dv, workspace,
                                  static_cast<hipStream_t>(stream));
     return hip_status();

@@ -147,7 +147,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
-    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, Geom g, float c,
+    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale, Geom g, float c,
     float scale, __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
     constexpr int kTile = 64 * D * 2;
     constexpr int kSlot = 2 * kTile;              // Q tile, dO tile
@@ -172,6 +173,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     keep_resident<D>(kf);
     keep_resident<D>(vf);
     const bool kvalid = g.valid(kb, 32 * kh + (lane & 31));
+    // e4m3 Q/K: q and k hold code values, the tile scales multiply the scores and, for
+    // dK = dS^T Q-hat, each query block's dS
+    const float sk = k_scale != nullptr ? k_scale[col] : 1.0f;
 
     f32x16 accv[kHT], acck[kHT];
 #pragma unroll
@@ -221,8 +225,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
             }
     };
 
-    auto phase1 = [&](const uint8_t* sq, const f32x4 (&L)[2][2], const f32x4 (&G)[2][2]) {
+    auto phase1 = [&](const uint8_t* sq, int qbk, const f32x4 (&L)[2][2], const f32x4 (&G)[2][2]) {
         const uint8_t* sg = sq + kTile;
+        const float tq = q_scale != nullptr ? q_scale[bh * g.nb + qbk] : 1.0f;   // uniform (scalar load)
+        const float cs = c * tq * sk;
         bf16x8 qa[D / 16], ga[D / 16];
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
@@ -247,9 +253,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
                 const int i = 8 * ks + t;
                 const float lq = L[ks][t >> 2][t & 3];
                 const float gq = G[ks][t >> 2][t & 3];
-                const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq)) : 0.0f;
+                const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lq)) : 0.0f;
                 pv[t] = pp;
-                ds[t] = pp * (dp[i] - gq);
+                ds[t] = pp * (dp[i] - gq) * tq;
             }
             *reinterpret_cast<bf16x8*>(xop(r, ks, 0)) = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
             *reinterpret_cast<bf16x8*>(xop(r, ks, 1)) = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         load_lg(qnext, LG[1 - P][0], LG[1 - P][1]);   // unconditional (block 0 past the end)
         if (jj + 1 < n) copy_block(qnext, lds + (1 - P) * kSlot);
         if (qcur >= 0) {                               // uniform
-            phase1(lds + P * kSlot, LG[P][0], LG[P][1]);
+            phase1(lds + P * kSlot, qcur, LG[P][0], LG[P][1]);
             __syncthreads();
             phase2(lds + P * kSlot);
         }
@@ -328,7 +334,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, float c,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale, Geom g, float c,
     float scale, __bf16* __restrict__ dq) {
     constexpr int kTile = 64 * D * 2;
     constexpr int kSlot = 2 * kTile;              // K tile, V tile
@@ -350,6 +357,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     keep_resident<D>(gf);
     const float lq = lse2[row * 64 + 32 * qh + (lane & 31)];
     const float gq = delta[row * 64 + 32 * qh + (lane & 31)];
+    // e4m3 Q/K: code values in q and k; the tile scales multiply the scores and, for
+    // dQ = dS K-hat, each key block's dS
+    const float tq = q_scale != nullptr ? q_scale[row] : 1.0f;
     const int trb = tr_base<D>(32 * kh, lane);
     EdgeSlots edge;
     edge.init(g, lane);
@@ -384,6 +394,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     auto compute = [&](const uint8_t* sk, int icur) {
         const uint8_t* sv = sk + kTile;
         const int code = icur >> kEdgeShift;
+        const float tk = k_scale != nullptr ? k_scale[bh * g.nb + (icur & kBlockIdMask)] : 1.0f;
+        const float cs = c * tq * tk;
         const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
         const uint32_t m32 = (uint32_t)(vm >> (32 * kh + 4 * hb));
         bf16x8 ka[D / 16], va[D / 16];
@@ -417,8 +429,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
             for (int t = 0; t < 8; ++t) {
                 const int i = 8 * ks + t;
                 const float x = keep_or_neg_inf(s[i], m32, 8 * (i >> 2) + (i & 3));
-                const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lq));
-                ds[t] = pp * (dp[i] - gq);
+                const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(x, cs, -lq));
+                ds[t] = pp * (dp[i] - gq) * tk;
             }
             const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
 #pragma unroll
@@ -474,8 +486,9 @@ size_t bwd_workspace_bytes(int B, int H, int nb) { return 2 * (size_t)B * H * nb
 template <int D>
 static void launch_bwd_d(const void* q, const void* k, const void* v, const void* o, const void* dout,
                          const float* lse, const int32_t* row_ptr, const int32_t* col_idx,
-                         const int32_t* col_ptr, const int32_t* row_idx, int B, int H, const Geom& g,
-                         float scale, int o_f32, void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
+                         const int32_t* col_ptr, const int32_t* row_idx, const float* q_scale,
+                         const float* k_scale, int B, int H, const Geom& g, float scale, int o_f32,
+                         void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
     const long rows = (long)B * H * g.nb;
     float* lse2 = static_cast<float*>(ws);
     float* delta = lse2 + rows * 64;
@@ -488,23 +501,24 @@ static void launch_bwd_d(const void* q, const void* k, const void* v, const void
         k_bwd_prep<D, float><<<(unsigned)rows, 256, 0, st>>>(static_cast<const float*>(o), bg, lse, g, lse2, delta);
     else
         k_bwd_prep<D, __bf16><<<(unsigned)rows, 256, 0, st>>>(static_cast<const __bf16*>(o), bg, lse, g, lse2, delta);
-    k_bwd_dkdv<D><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, col_ptr, row_idx, g, c, scale,
-                                                  static_cast<__bf16*>(dk), static_cast<__bf16*>(dv));
-    k_bwd_dq<D><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, g, c, scale,
-                                                static_cast<__bf16*>(dq));
+    k_bwd_dkdv<D><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, col_ptr, row_idx, q_scale,
+                                                  k_scale, g, c, scale, static_cast<__bf16*>(dk),
+                                                  static_cast<__bf16*>(dv));
+    k_bwd_dq<D><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, q_scale, k_scale,
+                                                g, c, scale, static_cast<__bf16*>(dq));
 }
 
 void launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,
-                            int B, int H, int D, const Geom& g, float scale, int o_f32, void* dq,
-                            void* dk, void* dv, void* ws, hipStream_t st) {
+                            const float* q_scale, const float* k_scale, int B, int H, int D, const Geom& g,
+                            float scale, int o_f32, void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
     if (D == 128)
-        launch_bwd_d<128>(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, B, H, g, scale, o_f32, dq,
-                          dk, dv, ws, st);
+        launch_bwd_d<128>(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, q_scale, k_scale, B, H, g,
+                          scale, o_f32, dq, dk, dv, ws, st);
     else
-        launch_bwd_d<64>(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, B, H, g, scale, o_f32, dq,
-                         dk, dv, ws, st);
+        launch_bwd_d<64>(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, q_scale, k_scale, B, H, g,
+                         scale, o_f32, dq, dk, dv, ws, st);
 }
 
 }  // namespace fpsa

@@ -11,6 +11,7 @@
 namespace fpsa {
 
 // layout: 0 rows, 1 VT, 2 QK (fpsa_layout values)
+void launch_dequant_tiles(const void* src, const float* scale, void* dst, long blocks, int D, hipStream_t st);
 void launch_tile_forward(const void* src, int src_dt, void* dst, int fp8, int layout, float* scale,
                          const Geom& g, long N, int B, int H, int D, hipStream_t st);
 void launch_tile_inverse(const void* src, void* dst, int dst_dt, const Geom& g, long N, int B,
@@ -68,8 +69,8 @@ size_t bwd_workspace_bytes(int B, int H, int nb);
 void launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, const float* lse, const int32_t* row_ptr,
                             const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,
-                            int B, int H, int D, const Geom& g, float scale, int o_f32, void* dq,
-                            void* dk, void* dv, void* ws, hipStream_t st);
+                            const float* q_scale, const float* k_scale, int B, int H, int D, const Geom& g,
+                            float scale, int o_f32, void* dq, void* dk, void* dv, void* ws, hipStream_t st);
 
 void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, const float* q_scale,
                         const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,

@@ -259,6 +259,53 @@ static void launch_inverse_map(const void* src, void* dst, int dst_dt, const Map
     }
 }
 
+// Value of an OCP e4m3fn code (finite codes only; the encoder above never writes the
+// NaN codes): sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormal step 2^-9.
+__device__ inline float decode_e4m3(uint32_t c) {
+    const uint32_t ex = (c >> 3) & 0xFu, man = c & 7u;
+    const float mag = ex == 0 ? ldexpf((float)man, -9) : ldexpf((float)(8u + man), (int)ex - 10);
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// Dequantized Q or K tiles: the e4m3 QK tile of a block times its scale, rounded to
+// bf16 (the float32 product, then nearest-even), or without a scale the code values
+// themselves (exact in bf16), written in the bf16 QK layout. Each
+// thread converts 16-byte chunks of 16 consecutive channels of one slot (two bf16
+// chunks out).
+template <int D>
+__global__ __launch_bounds__(256) void k_dequant_tiles(const uint8_t* __restrict__ src,
+                                                       const float* __restrict__ scale,
+                                                       __bf16* __restrict__ dst) {
+    const long blk = blockIdx.x;                         // (b*H + h)*nb + block
+    const float s = scale != nullptr ? scale[blk] : 1.0f;
+    const uint8_t* in = src + blk * 64 * D;
+    uint8_t* out = reinterpret_cast<uint8_t*>(dst + blk * 64 * D);
+    for (int oc = threadIdx.x; oc < 64 * D / 16; oc += 256) {
+        int e, d0;
+        chunk_source<D, 1, kQK>(oc, e, d0);
+        const i32x4 codes = *reinterpret_cast<const i32x4*>(in + 16 * oc);
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            bf16x8 o;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t c = ((uint32_t)codes[(8 * h8 + j) >> 2] >> (8 * ((8 * h8 + j) & 3))) & 0xFFu;
+                o[j] = (__bf16)(decode_e4m3(c) * s);
+            }
+            const int d = d0 + 8 * h8;
+            const int off = ((((e >> 5) * (D / 16) + (d >> 4)) * 2 + ((d >> 3) & 1)) * 32 + (e & 31)) * 8 + (d & 7);
+            *reinterpret_cast<bf16x8*>(out + 2 * off) = o;
+        }
+    }
+}
+
+void launch_dequant_tiles(const void* src, const float* scale, void* dst, long blocks, int D, hipStream_t st) {
+    const uint8_t* s = static_cast<const uint8_t*>(src);
+    __bf16* d = static_cast<__bf16*>(dst);
+    if (D == 128) k_dequant_tiles<128><<<(unsigned)blocks, 256, 0, st>>>(s, scale, d);
+    else k_dequant_tiles<64><<<(unsigned)blocks, 256, 0, st>>>(s, scale, d);
+}
+
 void launch_tile_forward(const void* src, int src_dt, void* dst, int fp8, int layout, float* scale,
                          const Geom& g, long N, int B, int H, int D, hipStream_t st) {
     launch_forward_map(src, src_dt, dst, fp8, layout, scale, GridMap{g}, N, B, H, D, st);

@@ -28,6 +28,7 @@ EXPORTED = [
     "fpsa_csr_transpose", "fpsa_transpose_workspace_bytes", "fpsa_sparse_attn_bwd",
     "fpsa_bwd_workspace_bytes", "fpsa_kmeans", "fpsa_cluster_layout", "fpsa_gather_tiles",
     "fpsa_scatter_tiles", "fpsa_cluster_mass", "fpsa_cluster_blocks", "fpsa_sparse_attn_fwd_varlen",
+    "fpsa_dequantize_tiles",
 ]
 
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.fpsa_select_workspace_bytes.argtypes = [i64, i32]
         L.fpsa_tile_reorder.restype = i32
         L.fpsa_tile_reorder.argtypes = [vp, i32, vp, i32, i32, vp, i32, i32, i32, gp, i32, vp]
+        L.fpsa_dequantize_tiles.restype = i32
+        L.fpsa_dequantize_tiles.argtypes = [vp, vp, i32, i32, i32, gp, vp, vp]
         L.fpsa_block_mass.restype = i32
         L.fpsa_block_mass.argtypes = [vp, vp, i32, i32, i32, gp, f32, vp, vp, vp, ctypes.c_size_t, vp]
         L.fpsa_mass_workspace_bytes.restype = ctypes.c_size_t
@@ -87,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.fpsa_transpose_workspace_bytes.restype = ctypes.c_size_t
         L.fpsa_transpose_workspace_bytes.argtypes = [i64, i32]
         L.fpsa_sparse_attn_bwd.restype = i32
-        L.fpsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, gp, f32,
+        L.fpsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, gp, f32,
                                            vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.fpsa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fpsa_bwd_workspace_bytes.argtypes = [i32, i32, gp]
@@ -172,6 +175,19 @@ def tile_reorder(src, dst, grid, tile, B, H, D, *, inverse=False, layout=LAYOUT_
     _check(s, "fpsa_tile_reorder")
 
 
+def dequantize_tiles(src, scale, grid, tile, B, H, D, dst, stream=None) -> None:
+    """fpsa_dequantize_tiles: e4m3 QK tiles (uint8) and their scales -> bf16 QK tiles
+    (scale None: the code values, the form the FP8 backward takes)."""
+    if src.dtype not in (torch.uint8, torch.float8_e4m3fn) or (scale is not None and scale.dtype != torch.float32):
+        raise ValueError("src e4m3 bytes, scale float32 or None (code values)")
+    if dst.dtype != torch.bfloat16:
+        raise ValueError("dst bf16")
+    g = Grid.of(grid, tile)
+    s = lib().fpsa_dequantize_tiles(_ptr(src), _ptr(scale), int(B), int(H), int(D), ctypes.byref(g),
+                                    _ptr(dst), _stream(stream))
+    _check(s, "fpsa_dequantize_tiles")
+
+
 def block_mass(q_tiled, k_tiled, grid, tile, B, H, D, softmax_scale, mass, workspace, lse=None,
                stream=None) -> None:
     if q_tiled.dtype != torch.bfloat16 or k_tiled.dtype != torch.bfloat16:
@@ -245,7 +261,7 @@ def csr_transpose(row_ptr, col_idx, B, H, nb, col_ptr, row_idx, workspace, strea
 
 
 def sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, grid, tile, B, H, D,
-                    softmax_scale, dq, dk, dv, workspace, stream=None) -> None:
+                    softmax_scale, dq, dk, dv, workspace, stream=None, q_scale=None, k_scale=None) -> None:
     for t in (q, k, v, dout, dq, dk, dv):
         if t.dtype != torch.bfloat16:
             raise ValueError("q, k, v, dout and the gradients are bf16")
@@ -254,8 +270,12 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, col_ptr, row_idx, g
     if lse.dtype != torch.float32:
         raise ValueError("lse float32")
     g = Grid.of(grid, tile)
+    for t in (q_scale, k_scale):
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("tile scales float32")
     s = lib().fpsa_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _DT[o.dtype], _ptr(dout), _ptr(lse), _ptr(row_ptr),
-                                   _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx), int(B), int(H), int(D),
+                                   _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx), _ptr(q_scale), _ptr(k_scale),
+                                   int(B), int(H), int(D),
                                    ctypes.byref(g), float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
                                    _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                                    _stream(stream))

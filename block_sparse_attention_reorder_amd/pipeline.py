@@ -81,6 +81,14 @@ class BlockSparseAttention:
                           stream=stream)
         return out, scale
 
+    def dequantize(self, x8, scale, out=None, stream=None):
+        """e4m3 QK tiles and their per-tile scales -> bf16 QK tiles of the dequantized
+        values; scale None gives the code values themselves (the operands of the FP8
+        forward's backward, which takes the scales separately)."""
+        out = torch.empty(self.tiled_shape(), dtype=torch.bfloat16, device=self.device) if out is None else out
+        fpsa.dequantize_tiles(x8, scale, self.grid, self.tile, self.B, self.H, self.D, out, stream=stream)
+        return out
+
     def untile(self, o_tiled, dtype=torch.bfloat16, out=None, stream=None):
         """tiled rows bf16 -> raster [B, N, H, D] of dtype (real tokens only)."""
         out = torch.empty((self.B, self.N, self.H, self.D), dtype=dtype, device=self.device) if out is None else out
@@ -172,7 +180,8 @@ class BlockSparseAttention:
                            stream=stream)
         return csc
 
-    def backward(self, qt, kt, vqk, ot, gt, lse, csr: Csr, csc: Csr, grads=None, workspace=None, stream=None):
+    def backward(self, qt, kt, vqk, ot, gt, lse, csr: Csr, csc: Csr, grads=None, workspace=None, stream=None,
+                 q_scale=None, k_scale=None):
         """Gradients (dq, dk, dv) in tiled rows bf16 from Q, K, V and dO in the QK
         layout, the forward's tiled output (bf16, or its float32 copy for a more
         accurate delta) and lse, the CSR and its transpose."""
@@ -184,7 +193,8 @@ class BlockSparseAttention:
             ws = torch.empty(fpsa.bwd_workspace_bytes(self.B, self.H, self.grid, self.tile), dtype=torch.uint8,
                              device=self.device)
         fpsa.sparse_attn_bwd(qt, kt, vqk, ot, gt, lse, csr.row_ptr, csr.col_idx, csc.row_ptr, csc.col_idx,
-                             self.grid, self.tile, self.B, self.H, self.D, self.scale, *grads, ws, stream=stream)
+                             self.grid, self.tile, self.B, self.H, self.D, self.scale, *grads, ws, stream=stream,
+                             q_scale=q_scale, k_scale=k_scale)
         return grads
 
     def run(self, q, k, v, thr_num=99, thr_den=100, out_dtype=torch.bfloat16):

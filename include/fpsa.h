@@ -128,6 +128,21 @@ int32_t fpsa_tile_reorder(const void* src, int32_t src_dtype, void* dst, int32_t
                           const fpsa_grid* g, int32_t inverse, void* stream);
 
 /*
+ * Dequantized e4m3 tiles, for the backward of the FP8 forward ([FPSAttention ...,
+ * Abstract]: training through the FP8 tiles; the quantizer passes gradients straight
+ * through, so the gradients are those of attention at the dequantized Q and K).
+ *
+ * src: tiled QK layout, e4m3 codes (as written by fpsa_tile_reorder with dst_dtype
+ * FPSA_FP8_E4M3); scale: its [B, H, nb] float32 tile scales, or NULL. dst: tiled QK
+ * layout, BF16, element = the float32 product code value * scale rounded to BF16
+ * (nearest even), or with a NULL scale the code value itself (exact in BF16; the
+ * form fpsa_sparse_attn_bwd takes for the FP8 backward). Deterministic; every element
+ * of every block is written.
+ */
+int32_t fpsa_dequantize_tiles(const void* src, const float* scale, int32_t B, int32_t H, int32_t D,
+                              const fpsa_grid* g, void* dst, void* stream);
+
+/*
  * Exact dense block attention mass (the one dense measurement step of [LoSA ...,
  * Abstract]).
  *
@@ -289,6 +304,14 @@ size_t fpsa_transpose_workspace_bytes(int64_t R, int32_t nb);
  * products in BF16 with float32 accumulation (p and ds are rounded to BF16 for the
  * matrix products). Padding rows and queries whose lse is -inf contribute nothing
  * and get zero gradients; so do key blocks no row keeps.
+ * q_scale, k_scale: both NULL (q and k are the attention inputs), or, for the
+ *   backward of the FP8 forward, the [B, H, nb] e4m3 tile scales, with q and k
+ *   holding the e4m3 code values as BF16 (fpsa_dequantize_tiles with a NULL scale;
+ *   e4m3 values are exact in BF16). The gradients are then those of attention at the
+ *   dequantized inputs q-hat = q * q_scale, k-hat = k * k_scale (the quantizer passes
+ *   gradients straight through): scores sq*sk*(q.k) exactly as the FP8 forward formed
+ *   them, and ds pre-multiplied by the tile scale before the dq and dk products.
+ *   Exactly one of the two NULL: FPSA_ERR_INVALID_ARG.
  * dq, dk, dv: tiled rows BF16 [B, H, Npad, D], fully written.
  * workspace_bytes >= fpsa_bwd_workspace_bytes(B, H, g) (two floats per query slot).
  * Deterministic: no atomics, fixed summation order.
@@ -296,7 +319,8 @@ size_t fpsa_transpose_workspace_bytes(int64_t R, int32_t nb);
 int32_t fpsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                              int32_t o_dtype, const void* dout, const float* lse, const int32_t* row_ptr,
                              const int32_t* col_idx, const int32_t* col_ptr,
-                             const int32_t* row_idx, int32_t B, int32_t H, int32_t D,
+                             const int32_t* row_idx, const float* q_scale, const float* k_scale,
+                             int32_t B, int32_t H, int32_t D,
                              const fpsa_grid* g, float softmax_scale, void* dq, void* dk, void* dv,
                              void* workspace, size_t workspace_bytes, void* stream);
 

@@ -80,6 +80,8 @@ def lib():
             L.orc_fp8_tile_quantize.argtypes = [_f32p] + [ctypes.c_int] * 4 + [_i32p, ctypes.c_int, _f32p, _f32p]
             L.orc_fp8_tile_codes.restype = None
             L.orc_fp8_tile_codes.argtypes = [_f32p] + [ctypes.c_int] * 4 + [_i32p, ctypes.c_int, _u8p, _f32p]
+            L.orc_round_bf16.restype = None
+            L.orc_round_bf16.argtypes = [_f32p, ctypes.c_int64, _f32p]
             L.orc_structured_mask.restype = ctypes.c_int64
             L.orc_structured_mask.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p]
             L.orc_retained_mass.restype = None
@@ -249,6 +251,21 @@ def fp8_tile_codes(x, grid, tile):
     scales = np.empty((B, H, nb), np.float32)
     lib().orc_fp8_tile_codes(x, B, N, H, D, blk, nb, codes, scales)
     return codes, scales
+
+
+def round_bf16(x):
+    """float32 array -> float32 array of its bf16 values (round to nearest even)."""
+    x = _c(x, np.float32)
+    out = np.empty_like(x)
+    lib().orc_round_bf16(x.reshape(-1), x.size, out.reshape(-1))
+    return out
+
+
+def fp8_dequantized_bf16(x, grid, tile):
+    """The dequantized e4m3 tile values (code value times tile scale, as float32)
+    rounded to bf16: the Q and K the backward of the FP8 forward reads."""
+    xhat, _ = fp8_tile_quantize(x, grid, tile)
+    return round_bf16(xhat)
 
 
 # --------------------------------------------------------------------------- structured mask

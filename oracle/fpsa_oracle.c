@@ -445,6 +445,29 @@ void orc_fp8_tile_codes(const float* x, int B, int N, int H, int D,
         }
 }
 
+/*
+ * bf16 value of a float32 under round-to-nearest-even: keep the upper 16 bits of the
+ * IEEE single encoding, rounding on the 16 dropped bits (above half up, below half
+ * down, exactly half to the even kept pattern). Infinities pass; NaN stays NaN. Used
+ * for the dequantized e4m3 tiles the FP8 backward reads (code value times tile scale,
+ * a float32 product, carried in bf16).
+ */
+void orc_round_bf16(const float* x, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t b;
+        memcpy(&b, &x[i], 4);
+        if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu) != 0) {
+            out[i] = x[i];                              /* NaN */
+            continue;
+        }
+        const uint32_t dropped = b & 0xFFFFu, kept = b >> 16;
+        uint32_t r = kept;
+        if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) r = kept + 1u;
+        const uint32_t o = r << 16;
+        memcpy(&out[i], &o, 4);
+    }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Retained mass of a frozen block set                                        */
 /* ------------------------------------------------------------------------- */

@@ -96,6 +96,16 @@ def test_tile_reorder_validation(L):
     assert call(inv=1, ddt=fpsa.FP8_E4M3) == fpsa.ERR_UNSUPPORTED
 
 
+def test_dequantize_tiles_validation(L):
+    f = L.fpsa_dequantize_tiles
+    g = grid()
+    assert f(None, FAKE, 1, 1, 64, g, FAKE, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, g, None, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 80, g, FAKE, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 0, 1, 64, g, FAKE, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 1, 1, 64, grid(4, 8, 8, 4, 4, 2), FAKE, None) == fpsa.ERR_INVALID_ARG
+
+
 def test_block_mass_validation(L):
     f = L.fpsa_block_mass
     ws = 2 * 4 * 64 * 4                                # one pair of query blocks of a 4-block grid
@@ -208,10 +218,11 @@ def test_sparse_attn_bwd_validation(L):
 
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, odt=fpsa.BF16, g_=FAKE, lse=FAKE, rp=FAKE, ci=FAKE, cp=FAKE, ri=FAKE,
-                 B=1, H=2, D=128, grid=g, sc=0.1, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, wsb=ws)
+                 qs=None, ks=None, B=1, H=2, D=128, grid=g, sc=0.1, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, wsb=ws)
         a.update(kw)
-        return f(a["q"], a["k"], a["v"], a["o"], a["odt"], a["g_"], a["lse"], a["rp"], a["ci"], a["cp"], a["ri"], a["B"], a["H"],
-                 a["D"], a["grid"], a["sc"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], None)
+        return f(a["q"], a["k"], a["v"], a["o"], a["odt"], a["g_"], a["lse"], a["rp"], a["ci"], a["cp"], a["ri"],
+                 a["qs"], a["ks"], a["B"], a["H"], a["D"], a["grid"], a["sc"], a["dq"], a["dk"], a["dv"], a["ws"],
+                 a["wsb"], None)
 
     for name in ("q", "k", "v", "o", "g_", "lse", "rp", "ci", "cp", "ri", "dq", "dk", "dv", "ws"):
         assert call(**{name: None}) == fpsa.ERR_INVALID_ARG, name
@@ -222,6 +233,9 @@ def test_sparse_attn_bwd_validation(L):
     assert call(D=96) == fpsa.ERR_UNSUPPORTED
     assert call(odt=fpsa.FP8_E4M3) == fpsa.ERR_UNSUPPORTED
     assert call(wsb=ws - 1) == fpsa.ERR_CAPACITY
+    # tile scales come in pairs (both for the FP8 backward, or neither)
+    assert call(qs=FAKE) == fpsa.ERR_INVALID_ARG
+    assert call(ks=FAKE) == fpsa.ERR_INVALID_ARG
 
 
 def test_kmeans_permutation_validation(L):

@@ -10,7 +10,7 @@ from block_sparse_attention_reorder_amd import fpsa, synth
 from block_sparse_attention_reorder_amd.pipeline import BlockSparseAttention, Csr
 from block_sparse_attention_reorder_amd.workloads import WORKLOADS
 
-from parity_util import csr_to_numpy, dev, inputs
+from parity_util import csr_to_numpy, dev, expected_tiled_rows, inputs, rows_to_qk
 
 pytestmark = pytest.mark.gpu
 
@@ -210,3 +210,60 @@ def test_backward_full_480p_sampled():
     # each stored element carries a bf16 rounding (2^-9 of itself) on top of terms
     # rounded by as much: the sums stay within 2^-8 of the sum of magnitudes
     assert worst_k <= 2.0 ** -8 and worst_v <= 2.0 ** -8
+
+
+# --------------------------------------------------------------------------- FP8
+
+@pytest.mark.parametrize("grid,H,D", [((5, 6, 7), 2, 128), ((9, 10, 13), 2, 64)])
+def test_dequantize_tiles_bitexact(grid, H, D):
+    tile = (4, 4, 4)
+    q = inputs(grid, 2, H, D, amp=2.0, seed=71)[0]
+    bsa = BlockSparseAttention(grid, tile, 2, H, D)
+    q8, qs = bsa.tile_fp8(dev(q, torch.bfloat16))
+    got = bsa.dequantize(q8, qs).view(torch.int16).cpu().numpy()
+    rows = expected_tiled_rows(O.fp8_dequantized_bf16(q, grid, tile), grid, tile)
+    want = rows_to_qk(torch.from_numpy(rows).to(torch.bfloat16).view(torch.int16).numpy(), bsa.nb, esize=2)
+    assert np.array_equal(got.reshape(want.shape), want)
+    # without a scale: the code values themselves, exact in bf16
+    codes, _ = O.fp8_tile_codes(q, grid, tile)
+    vals = np.vectorize(O.e4m3_decode)(codes).astype(np.float32)
+    got = bsa.dequantize(q8, None).view(torch.int16).cpu().numpy()
+    rows = expected_tiled_rows(vals, grid, tile)
+    want = rows_to_qk(torch.from_numpy(rows).to(torch.bfloat16).view(torch.int16).numpy(), bsa.nb, esize=2)
+    assert np.array_equal(got.reshape(want.shape), want)
+
+
+# The backward of the FP8 forward: the gradient of attention at the dequantized Q and K
+# (the quantizer passes gradients straight through). The kernels read the e4m3 code
+# values as bf16 (exact) with the tile scales, so their scores are the forward's and
+# the only new rounding is that of ds times the tile scale before the dq and dk
+# products, inside the bf16 bounds above.
+
+
+@pytest.mark.parametrize("grid,H,D", [((5, 6, 7), 2, 128), ((9, 10, 13), 2, 64), ((6, 9, 14), 1, 128)])
+def test_fp8_backward_matches_oracle(grid, H, D):
+    tile = (4, 4, 4)
+    q, k, v = inputs(grid, 1, H, D, amp=1.5, seed=73)
+    g = _dout(grid, 1, H, D, 74)
+    nb = O.num_blocks(grid, tile)
+    rp, ci = _csr_of_rows(H, nb, nb + 5 * H, 99, 100, empty=(0,))
+    bsa = BlockSparseAttention(grid, tile, 1, H, D)
+    q8, qs = bsa.tile_fp8(dev(q, torch.bfloat16))
+    k8, ks = bsa.tile_fp8(dev(k, torch.bfloat16))
+    vt = bsa.tile_vt(dev(v, torch.bfloat16))
+    vq = bsa.tile_qk(dev(v, torch.bfloat16))
+    gt = bsa.tile_qk(dev(g, torch.bfloat16))
+    csr = Csr(dev(rp, torch.int32), dev(ci if len(ci) else np.zeros(1, np.int32), torch.int32))
+    lse = torch.empty((1, H, bsa.npad), dtype=torch.float32, device="cuda")
+    o32 = torch.empty(bsa.tiled_shape(), dtype=torch.float32, device="cuda")
+    bsa.forward(q8, k8, vt, csr, q_scale=qs, k_scale=ks, lse=lse, out_f32=o32)
+    qc, kc = bsa.dequantize(q8, None), bsa.dequantize(k8, None)
+    csc = bsa.transpose(csr)
+    grads = bsa.backward(qc, kc, vq, o32, gt, lse, csr, csc, q_scale=qs, k_scale=ks)
+    dq, dk, dv = (bsa.untile(x, torch.float32).cpu().numpy() for x in grads)
+    xq, _ = O.fp8_tile_quantize(q, grid, tile)
+    xk, _ = O.fp8_tile_quantize(k, grid, tile)
+    wq, wk, wv, mq, mk, mv = O.masked_attention_bwd(xq, xk, v, g, grid, tile, bsa.scale, rp, ci, magnitudes=True)
+    _check(dq, wq, mq, "dq")
+    _check(dk, wk, mk, "dk")
+    _check(dv, wv, mv, "dv")

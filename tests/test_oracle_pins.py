@@ -742,3 +742,39 @@ def test_cluster_attention_all_and_single_cluster():
     sub = O.cluster_attention(q, k, v, qa, ka, 4, 5, 0.25, crow, np.array([3], np.int32), tokens=sel)
     for h in range(2):
         assert np.array_equal(sub[0, h], out[0, sel, h])
+
+
+def test_round_bf16_nearest_even():
+    """bf16 rounding by hand-worked halfway cases, and against torch's float32 -> bf16
+    cast (an independent implementation of the same IEEE rounding) on random and
+    extreme values."""
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -(1 + 2.0 ** -8),
+                  2.0 ** -130, np.inf, -np.inf, 0.0, 3.3895e38], np.float32)
+    want = np.array([1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -1.0], np.float32)
+    got = O.round_bf16(x)
+    assert np.array_equal(got[:4], want)
+    assert np.isposinf(got[5]) and np.isneginf(got[6]) and got[7] == 0.0
+    r = np.random.default_rng(3).standard_normal(200000).astype(np.float32)
+    r *= np.float32(10.0) ** np.random.default_rng(4).integers(-40, 38, r.size).astype(np.float32)
+    r = np.concatenate([r, x])
+    ref = torch.from_numpy(r).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.round_bf16(r), ref, equal_nan=True)
+
+
+def test_fp8_dequantized_bf16_values():
+    """The dequantized tiles the FP8 backward reads: a tile whose largest magnitude is
+    448 has scale 1, so its values are e4m3 values themselves, which bf16 holds exactly;
+    in general the result is the bf16 rounding of the quantizer's own output."""
+    grid, tile = (4, 4, 4), (4, 4, 4)
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 64, 1, 8)).astype(np.float32) * 100
+    x[0, 5, 0, 3] = 448.0
+    xhat, scales = O.fp8_tile_quantize(x, grid, tile)
+    assert scales[0, 0, 0] == 1.0
+    got = O.fp8_dequantized_bf16(x, grid, tile)
+    assert np.array_equal(got, xhat)
+    assert np.array_equal(got, np.array([O.e4m3_decode(O.e4m3_encode(v)) for v in x.ravel()],
+                                        np.float32).reshape(x.shape))
+    y = x * np.float32(0.37)
+    yhat, _ = O.fp8_tile_quantize(y, grid, tile)
+    assert np.array_equal(O.fp8_dequantized_bf16(y, grid, tile), O.round_bf16(yhat))
