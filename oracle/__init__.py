@@ -5,8 +5,8 @@ CPU-baseline leg import this package; the product path never does. It shares no
 code with the HIP library: geometry, masses, selection, masked attention, FP8
 quantization, the structured mask, the retained-mass monitor, the fixed
 diagonal / multi-diagonal / stripe patterns, the gradients of masked attention, the
-block-CSR transpose and the k-means semantic permutation (clusters, layout, cluster
-masses, cluster attention) are each written here from their definitions
+block-CSR transpose, the k-means semantic permutation (clusters, layout, cluster
+masses, cluster attention) and bf16 rounding are each written here from their definitions
 (``fpsa_oracle.c``), over raster-ordered tokens.
 
 Parity pins (tests/test_oracle_pins.py) tie each function to something other than
