@@ -5,19 +5,20 @@
 // [Sparse VideoGen2: Accelerate Video Generation with Sparse Attention via
 // Semantic-Aware Permutation, Abstract].
 //
-// k-means is Lloyd's algorithm in float64 with a fixed order of every operation:
-// distances summed over channels in order (no fused multiply-add: this file is
-// compiled with contraction off), ties to the lower cluster, member sums in eight
-// interleaved partials combined pairwise. The assignment is therefore the same on
-// every device and run.
+// k-means is Lloyd's algorithm in float64 with a fixed order of every operation: a
+// token goes to the centroid of least e = |c|^2 - 2 x.c (the squared distance less
+// |x|^2, common to every candidate), each of |c|^2 and x.c a chain of fused
+// multiply-adds over the channels in order; ties to the lower cluster; member sums in
+// eight interleaved partials combined pairwise. This file is compiled with
+// contraction off, so every fused operation is an explicit one. The assignment is
+// therefore the same on every device and run.
 //
-// Kernels: k_km_init (strided starting centroids), k_km_assign (nearest centroid; a
-// lane per token, token vectors and centroids staged through LDS; cluster sizes by
-// atomic counts), k_km_fill (member lists in token order, a wave per cluster with
-// ballots),
-// k_km_update (centroid = member mean), k_cluster_layout (slot map of the
-// cluster-contiguous blocks), k_cluster_mass (centroid-based cluster masses),
-// k_cblk_count / k_cblk_fill (block CSR of a cluster selection).
+// Kernels: k_km_init (strided starting centroids), k_km_assign (nearest centroid as
+// float64 matrix products; cluster sizes by atomic counts), k_km_fill (member lists in
+// token order, a wave per cluster with ballots), k_km_update (centroid = member
+// mean), k_cluster_layout (slot map of the cluster-contiguous blocks), k_cluster_mass
+// (centroid-based cluster masses), k_cblk_count / k_cblk_fill (block CSR of a cluster
+// selection).
 #include "fpsa_device.h"
 #include "fpsa_internal.h"
 
@@ -39,85 +40,169 @@ __global__ __launch_bounds__(128) void k_km_init(const T* __restrict__ x, int N,
     cent[(bh * C + c) * D + d] = (double)as_float(x[((b * N + t) * H + h) * D + d]);
 }
 
-// A lane per token of a 64-token tile; the tile's vectors sit in LDS (rows padded by
-// one float so that the 64 lanes read 64 different banks) and centroids pass through
-// LDS in chunks of kKmChunk clusters (every lane reads the same centroid value: a
-// broadcast). Within a chunk wave w takes a quarter of the clusters, four at a time so that
-// each converted token value serves four distances. Each wave keeps the first strict
-// minimum of its clusters (visited in increasing order), and the four candidates are
-// merged on (distance, cluster), which is the sequential scan's answer.
-constexpr int kKmChunk = 16;
+// Assignment as float64 matrix products. v_mfma_f64_16x16x4 forms each output as a
+// chain of four fused multiply-adds in k order on top of the accumulator, so a run of
+// them over channel groups 0..3, 4..7, ... is exactly the channel-order fused chain of
+// x.c. Tokens are the A rows (a wave holds two 16-token tiles as loaded and converts
+// each operand when it is used), centroids the B columns (16-centroid tiles staged
+// through LDS in operand order, double-buffered). Each lane keeps the first minimum of
+// e over its centroid column across the tiles, and the 16 columns then merge on
+// (e, cluster): the least e, ties to the lower cluster.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kKmWaves = 8;                     // waves x 32 tokens per workgroup
+constexpr int kKmTokens = kKmWaves * 32;
+
+// operand A of a 16-token tile, kept as loaded: lane l holds channels 4s + l/16 of its
+// token, s = 0 .. D/4-1, two bf16 channels (steps 2q and 2q+1) per word, or one float
+template <typename T, int D> struct TileA;
+template <int D> struct TileA<__bf16, D> {
+    uint32_t w[D / 8];
+    __device__ void load(const __bf16* row, int k) {
+#pragma unroll
+        for (int q = 0; q < D / 8; ++q) {       // channels 8q .. 8q+7
+            const uint4 u = reinterpret_cast<const uint4*>(row)[q];
+            const uint32_t w0 = (k >> 1) ? u.y : u.x, w1 = (k >> 1) ? u.w : u.z;
+            const uint32_t lo = (k & 1) ? (w0 >> 16) : (w0 & 0xffffu);   // channel 8q + k
+            const uint32_t hi = (k & 1) ? (w1 & 0xffff0000u) : (w1 << 16); // channel 8q + 4 + k
+            w[q] = lo | hi;
+        }
+    }
+    __device__ double get(int s) const {
+        return (double)__uint_as_float((s & 1) ? (w[s >> 1] & 0xffff0000u) : (w[s >> 1] << 16));
+    }
+    __device__ void keep() {                    // converted per use: no float64 copy held across tiles
+#pragma unroll
+        for (int q = 0; q < D / 8; ++q) asm volatile("" : "+v"(w[q]));
+    }
+};
+template <int D> struct TileA<float, D> {
+    float w[D / 4];
+    __device__ void load(const float* row, int k) {
+#pragma unroll
+        for (int q = 0; q < D / 4; ++q) {       // channels 4q .. 4q+3
+            const float4 u = reinterpret_cast<const float4*>(row)[q];
+            const float lo = (k & 1) ? u.y : u.x, hi = (k & 1) ? u.w : u.z;
+            w[q] = (k >> 1) ? hi : lo;
+        }
+    }
+    __device__ double get(int s) const { return (double)w[s]; }
+    __device__ void keep() {
+#pragma unroll
+        for (int q = 0; q < D / 4; ++q) asm volatile("" : "+v"(w[q]));
+    }
+};
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_km_assign(const T* __restrict__ x, int N, int H, int C,
-                                                   const double* __restrict__ cent,
-                                                   int32_t* __restrict__ assign, int32_t* __restrict__ count) {
-    constexpr int kRow = D + 1;
-    __shared__ float xs[64 * kRow];
-    __shared__ double cs[kKmChunk * D];
-    __shared__ double bestd[4][64];
-    __shared__ int bestc[4][64];
+__global__ __launch_bounds__(kKmWaves * 64) void k_km_assign(const T* __restrict__ x, int N, int H, int C,
+                                                           const double* __restrict__ cent,
+                                                           int32_t* __restrict__ assign,
+                                                           int32_t* __restrict__ count) {
+    constexpr int kSteps = D / 4;               // products per tile pair
+    constexpr int kTile = kSteps * 64;          // doubles per staged centroid tile
+    constexpr int kPer = 16 * D / (kKmWaves * 64);   // staged doubles per thread
+    extern __shared__ double km_lds[];          // two staged tiles, then C squared norms
+    double* tiles = km_lds;
+    double* cnorm = km_lds + 2 * kTile;
     const long bh = blockIdx.y;
     const long b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = blockIdx.x * 64 + lane;
-    for (int i = tid; i < 64 * D; i += 256) {
-        const int t = i / D, d = i - t * D;
-        const long nn = (long)blockIdx.x * 64 + t;
-        xs[t * kRow + d] = nn < N ? as_float(x[((b * N + nn) * H + h) * D + d]) : 0.0f;
-    }
-    const float* xrow = xs + lane * kRow;
-    const double* cb = cent + bh * C * D;
-    double bd = INFINITY;
-    int bc = C;
-    for (int c0 = 0; c0 < C; c0 += kKmChunk) {
-        __syncthreads();
-        const long lim = (long)(C - c0) * D;
-        for (int i = tid; i < kKmChunk * D; i += 256) cs[i] = i < lim ? cb[(long)c0 * D + i] : 0.0;
-        __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const double* cb = cent + bh * (long)C * D;
+    const int ntile = (C + 15) / 16;
+
+    // staging: element e = tid + 512 r of tile t is centroid 16t + e / D, channel e % D,
+    // stored at operand position (channel / 4) * 64 + (e / D) + 16 (channel % 4)
+    double stage[kPer];
+    auto fetch = [&](int t) {
 #pragma unroll
-        for (int g = 0; g < kKmChunk / 16; ++g) {
-            const int cc = (kKmChunk / 4) * w + 4 * g;  // chunk-local cluster of this group
-            if (c0 + cc >= C) break;
-            const double* p = cs + cc * D;
-            double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-#pragma unroll 8
-            for (int d = 0; d < D; ++d) {
-                const double xd = (double)xrow[d];
-                const double t0 = xd - p[d], t1 = xd - p[D + d], t2 = xd - p[2 * D + d], t3 = xd - p[3 * D + d];
-                s0 = s0 + t0 * t0;
-                s1 = s1 + t1 * t1;
-                s2 = s2 + t2 * t2;
-                s3 = s3 + t3 * t3;
-            }
-            const double sv[4] = {s0, s1, s2, s3};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = c0 + cc + u;
-                if (c < C && sv[u] < bd) {
-                    bd = sv[u];
-                    bc = c;
-                }
-            }
+        for (int r = 0; r < kPer; ++r) {
+            const int e = tid + kKmWaves * 64 * r;
+            const int c = 16 * t + e / D;
+            stage[r] = c < C ? cb[(long)c * D + (e % D)] : 0.0;
         }
+    };
+    auto put = [&](int t) {
+        double* dst = tiles + (t & 1) * kTile;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int e = tid + kKmWaves * 64 * r;
+            const int jj = e / D, d = e % D;
+            dst[(d >> 2) * 64 + jj + 16 * (d & 3)] = stage[r];
+        }
+    };
+    fetch(0);
+    for (int c = tid; c < C; c += kKmWaves * 64) {  // |c|^2: one sequential fused chain per centroid
+        const double* p = cb + (long)c * D;
+        double s = 0.0;
+        for (int d = 0; d < D; ++d) s = __builtin_fma(p[d], p[d], s);
+        cnorm[c] = s;
     }
-    bestd[w][lane] = bd;
-    bestc[w][lane] = bc;
+    // the wave's two token tiles
+    const long tok0 = (long)blockIdx.x * kKmTokens + wave * 32;
+    TileA<T, D> a0, a1;
+    {
+        const long t0 = min(tok0 + (lane & 15), (long)N - 1), t1 = min(tok0 + 16 + (lane & 15), (long)N - 1);
+        a0.load(x + ((b * N + t0) * H + h) * D, lane >> 4);   // past N: a real row, result unused
+        a1.load(x + ((b * N + t1) * H + h) * D, lane >> 4);
+    }
+    put(0);
     __syncthreads();
-    if (w == 0 && n < N) {
+
+    double bd0[4], bd1[4];
+    int bi0[4], bi1[4];
 #pragma unroll
-        for (int u = 1; u < 4; ++u) {
-            const double d2 = bestd[u][lane];
-            const int c2 = bestc[u][lane];
-            if (d2 < bd || (d2 == bd && c2 < bc)) {
-                bd = d2;
-                bc = c2;
+    for (int v = 0; v < 4; ++v) bi0[v] = bi1[v] = -1, bd0[v] = bd1[v] = 0.0;
+    for (int t = 0; t < ntile; ++t) {
+        if (t + 1 < ntile) fetch(t + 1);
+        const double* bt = tiles + (t & 1) * kTile;
+        a0.keep();
+        a1.keep();
+        f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            const double bv = bt[s * 64 + lane];
+            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.get(s), bv, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.get(s), bv, acc1, 0, 0, 0);
+        }
+        const int j = 16 * t + (lane & 15);     // this lane's centroid; rows l/16 + 4v
+        if (j < C) {
+            const double cn = cnorm[j];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const double e0 = cn - 2.0 * acc0[v], e1 = cn - 2.0 * acc1[v];
+                if (bi0[v] < 0 || e0 < bd0[v]) bd0[v] = e0, bi0[v] = j;
+                if (bi1[v] < 0 || e1 < bd1[v]) bd1[v] = e1, bi1[v] = j;
             }
         }
-        const int a = bc < C ? bc : 0;
-        assign[bh * N + n] = a;
-        atomicAdd(&count[bh * C + a], 1);            // sizes only: the order is irrelevant
+        if (t + 1 < ntile) put(t + 1);
+        __syncthreads();
+    }
+    // merge the 16 centroid columns of each row on (e, cluster)
+    auto merge = [&](double& bd, int& bi) {
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+            const double od = __shfl_xor(bd, m);
+            const int oi = __shfl_xor(bi, m);
+            if (oi >= 0 && (bi < 0 || od < bd || (od == bd && oi < bi))) bd = od, bi = oi;
+        }
+    };
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        merge(bd0[v], bi0[v]);
+        merge(bd1[v], bi1[v]);
+    }
+    // lane (g, u): u < 4 writes row g + 4u of tile 0, 4 <= u < 8 row g + 4(u-4) of tile 1
+    const int u = lane & 15, g = lane >> 4;
+    if (u < 8) {
+        const int v = u & 3;
+        int bi = bi0[0];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            if (v == w) bi = u < 4 ? bi0[w] : bi1[w];
+        const long n = tok0 + (u < 4 ? 0 : 16) + g + 4 * v;
+        if (n < N) {
+            assign[bh * N + n] = bi;
+            atomicAdd(&count[bh * C + bi], 1);          // sizes only: the order is irrelevant
+        }
     }
 }
 
@@ -193,13 +278,13 @@ static void kmeans_t(const T* x, int B, int N, int H, int D, int C, int iters, i
     const long rows = (long)B * H * C;
     dim3 gc(C, B * H);
     k_km_init<T><<<gc, 128, 0, st>>>(x, N, H, D, C, cent);
-    dim3 ga((N + 63) / 64, B * H);
+    dim3 ga((N + kKmTokens - 1) / kKmTokens, B * H);
     const unsigned wb = (unsigned)((rows + 3) / 4);
     const unsigned zb = (unsigned)min((rows + 255) / 256, 4096L);
     for (int it = 0; it < iters; ++it) {
         k_zero_i32<<<zb, 256, 0, st>>>(count, rows);
-        if (D == 128) k_km_assign<T, 128><<<ga, 256, 0, st>>>(x, N, H, C, cent, assign, count);
-        else k_km_assign<T, 64><<<ga, 256, 0, st>>>(x, N, H, C, cent, assign, count);
+        if (D == 128) k_km_assign<T, 128><<<ga, kKmWaves * 64, (size_t)(2 * 32 * 64 + C) * 8, st>>>(x, N, H, C, cent, assign, count);
+        else k_km_assign<T, 64><<<ga, kKmWaves * 64, (size_t)(2 * 16 * 64 + C) * 8, st>>>(x, N, H, C, cent, assign, count);
         launch_scan(count, rows, off, st);
         k_km_fill<<<wb, 256, 0, st>>>(assign, N, C, rows, off, members);
         if (D == 128) k_km_update<T, 128><<<gc, kKmParts * 128, 0, st>>>(x, N, H, C, off, members, cent);

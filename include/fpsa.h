@@ -340,17 +340,18 @@ size_t fpsa_bwd_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g);
  * FPSA_BF16 or FPSA_F32), in float64 with a fixed operation order (results are the
  * same on every run and device):
  *   start: centroid c = x of token floor(c N / C);
- *   iters times: assign each token to the centroid at the least squared distance
- *   (summed over channels in order, no fused multiply-add; ties to the lower
- *   cluster), then set each non-empty cluster's centroid to the mean of its members
- *   (member r, in token order, goes to partial sum r % 8, each partial summed in
- *   order, the partials combined as ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))); an empty
- *   cluster keeps its centroid.
+ *   iters times: assign each token to the centroid of least e = |c|^2 - 2 x.c (the
+ *   squared distance less |x|^2, common to every candidate; |c|^2 and x.c each a
+ *   chain of fused multiply-adds over the channels in order from zero; ties to the
+ *   lower cluster), then set each non-empty cluster's centroid to the mean of its
+ *   members (member r, in token order, goes to partial sum r % 8, each partial
+ *   summed in order, the partials combined as ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)));
+ *   an empty cluster keeps its centroid.
  * Outputs (device): assign [B, H, N]; centroids [B, H, C, D] float64; counts
  * [B, H, C]; member_off [B*H*C + 1] and members [B*H*N]: the tokens of cluster c of
  * slice bh, ascending, are members[member_off[bh*C + c] .. member_off[bh*C + c + 1]).
  * Requires D in {64, 128}, 1 <= C <= min(N, FPSA_MAX_SELECT_BLOCKS), 1 <= iters <=
- * 1000, B*H*N < 2^31.
+ * 1000, B*H*N < 2^31, and finite inputs.
  */
 int32_t fpsa_kmeans(const void* x, int32_t x_dtype, int32_t B, int32_t N, int32_t H, int32_t D,
                     int32_t C, int32_t iters, int32_t* assign, double* centroids, int32_t* counts,

@@ -758,20 +758,27 @@ int64_t orc_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int B,
  * VideoGen2: Accelerate Video Generation with Sparse Attention via Semantic-Aware
  * Permutation, Abstract]. Lloyd's k-means per (b, h) over the N vectors x[b, :, h, :]:
  *   start: centroid c = x of token floor(c N / C);
- *   iters times: assign every token to the nearest centroid (squared Euclidean
- *   distance summed over channels in order, ties to the lower cluster), then move
- *   every non-empty cluster's centroid to the mean of its members (eight interleaved
+ *   iters times: assign every token to the nearest centroid, then move every
+ *   non-empty cluster's centroid to the mean of its members (eight interleaved
  *   partial sums in token order, combined pairwise); an empty cluster keeps its
  *   centroid.
+ * "Nearest" compares e(x, c) = |c|^2 - 2 x.c, the squared Euclidean distance less
+ * |x|^2, which is the same for every candidate: |c|^2 and x.c are each a chain of
+ * fused multiply-adds over the channels in order, starting from zero, in float64;
+ * e = |c|^2 - 2 (x.c) (the doubling is exact); the least e wins, ties to the lower
+ * cluster. Inputs are finite.
  * assign [B, H, N], cent [B, H, C, D] float64, count [B, H, C]: the last assignment
  * and the centroids and sizes that follow from it.
  */
-static double sqdist(const float* x, int D, const double* c) {
+static double sqnorm(const double* c, int D) {
     double s = 0.0;
-    for (int d = 0; d < D; ++d) {
-        const double t = (double)x[d] - c[d];
-        s = s + t * t;
-    }
+    for (int d = 0; d < D; ++d) s = fma(c[d], c[d], s);
+    return s;
+}
+
+static double dot_xc(const float* x, int D, const double* c) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s = fma((double)x[d], c[d], s);
     return s;
 }
 
@@ -788,15 +795,17 @@ void orc_kmeans(const float* x, int B, int N, int H, int D, int C, int iters, in
                 const int64_t t = (int64_t)c * N / C;
                 for (int d = 0; d < D; ++d) cc[(int64_t)c * D + d] = (double)x[RIX(b, t, h, d)];
             }
+            double* cnorm = (double*)malloc((size_t)C * sizeof(double));
             for (int it = 0; it < iters; ++it) {
+                for (int c = 0; c < C; ++c) cnorm[c] = sqnorm(cc + (int64_t)c * D, D);
                 for (int n = 0; n < N; ++n) {
                     const float* xn = x + RIX(b, n, h, 0);
                     int best = 0;
-                    double bd = sqdist(xn, D, cc);
+                    double bd = cnorm[0] - 2.0 * dot_xc(xn, D, cc);
                     for (int c = 1; c < C; ++c) {
-                        const double dd = sqdist(xn, D, cc + (int64_t)c * D);
-                        if (dd < bd) {
-                            bd = dd;
+                        const double e = cnorm[c] - 2.0 * dot_xc(xn, D, cc + (int64_t)c * D);
+                        if (e < bd) {
+                            bd = e;
                             best = c;
                         }
                     }
@@ -825,6 +834,7 @@ void orc_kmeans(const float* x, int B, int N, int H, int D, int C, int iters, in
                 }
                 free(part);
             }
+            free(cnorm);
         }
 }
 

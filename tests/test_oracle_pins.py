@@ -664,6 +664,38 @@ def test_kmeans_lloyd_properties():
         assert np.array_equal(np.argmin(d, axis=1), a[0, h])
 
 
+def test_kmeans_assignment_is_the_exact_nearest_centroid():
+    # every assignment step against exact rational arithmetic: the squared distance
+    # sum_d (x_d - c_d)^2 to the centroids the step starts from (the starting tokens,
+    # or the centroids the oracle returns after one step fewer), least value, ties to
+    # the lower cluster; the oracle compares |c|^2 - 2 x.c in float64 instead
+    from fractions import Fraction as Fr
+    x = _rand_qkv(1, 40, 2, 8, 11)[0]
+    C = 5
+    N = x.shape[1]
+    for iters in range(1, 5):
+        asg, _, _ = O.kmeans(x, C, iters)
+        for h in range(2):
+            if iters == 1:
+                cent = [x[0, c * N // C, h].astype(np.float64) for c in range(C)]
+            else:
+                cent = O.kmeans(x, C, iters - 1)[1][0, h]
+            for n in range(N):
+                xn = [Fr(float(v)) for v in x[0, n, h]]
+                dist = [sum((a - Fr(float(cv))) ** 2 for a, cv in zip(xn, cent[c])) for c in range(C)]
+                assert asg[0, h, n] == min(range(C), key=lambda c: (dist[c], c))
+
+
+def test_kmeans_equidistant_token_goes_to_the_lower_cluster():
+    # token 2 sits exactly halfway between tokens 0 and 1, the starting centroids of
+    # clusters 0 and 1 (token floor(c N / C) for N = 3, C = 2): equal squared
+    # distances, so it joins cluster 0
+    x = np.array([[[2.0, 0.0], [0.0, 2.0], [1.0, 1.0]]], np.float32)[:, :, None, :]
+    asg, cent, cnt = O.kmeans(x, 2, 1)
+    assert asg[0, 0].tolist() == [0, 1, 0] and cnt[0, 0].tolist() == [2, 1]
+    assert cent[0, 0, 0].tolist() == [1.5, 0.5] and cent[0, 0, 1].tolist() == [0.0, 2.0]
+
+
 def test_cluster_layout_closed_forms():
     rng = np.random.default_rng(4)
     B, H, N, C = 1, 2, 500, 9

@@ -48,6 +48,27 @@ def test_kmeans_and_layout_bitexact(case, f32):
     assert np.array_equal(c.blk_count.cpu().numpy(), bc)
 
 
+@pytest.mark.parametrize("N,H,D,C,iters", [(33, 2, 64, 1, 3), (33, 1, 128, 33, 2), (700, 2, 64, 300, 3),
+                                           (1030, 1, 128, 129, 2)])
+def test_kmeans_extreme_cluster_counts(N, H, D, C, iters):
+    """One cluster; as many clusters as tokens (every token starts as its own
+    centroid); cluster counts that leave a partial last centroid tile; token counts
+    that leave a partial last workgroup."""
+    rng = np.random.default_rng(N + C)
+    x = (rng.standard_normal((1, N, H, D)) * 2.0).astype(np.float32)
+    xb = dev(x, torch.bfloat16)
+    xr = xb.float().cpu().numpy()                   # the bf16 values, exactly
+    i32 = dict(dtype=torch.int32, device="cuda")
+    a, cnt = torch.empty((1, H, N), **i32), torch.empty((1, H, C), **i32)
+    cent = torch.empty((1, H, C, D), dtype=torch.float64, device="cuda")
+    mo, mem = torch.empty(H * C + 1, **i32), torch.empty(H * N, **i32)
+    fpsa.kmeans(xb, 1, N, H, D, C, iters, a, cent, cnt, mo, mem)
+    ra, rc, rn = O.kmeans(xr, C, iters)
+    assert np.array_equal(a.cpu().numpy(), ra)
+    assert np.array_equal(cnt.cpu().numpy(), rn)
+    assert np.array_equal(cent.cpu().numpy(), rc)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_gather_and_scatter_by_slot_map(D):
     grid, H, C = (5, 6, 7), 2, 9
