@@ -284,11 +284,17 @@ int32_t fpsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const 
     return hip_status();
 }
 
+size_t fpsa_kmeans_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t C) {
+    if (B < 1 || H < 1 || N < 1 || C < 1) return 0;
+    return fpsa::kmeans_workspace_bytes(B, H, N, C);
+}
+
 int32_t fpsa_kmeans(const void* x, int32_t x_dtype, int32_t B, int32_t N, int32_t H, int32_t D,
                     int32_t C, int32_t iters, int32_t* assign, double* centroids, int32_t* counts,
-                    int32_t* member_off, int32_t* members, void* stream) {
+                    int32_t* member_off, int32_t* members, void* workspace, size_t workspace_bytes,
+                    void* stream) {
     if (x == nullptr || assign == nullptr || centroids == nullptr || counts == nullptr ||
-        member_off == nullptr || members == nullptr)
+        member_off == nullptr || members == nullptr || workspace == nullptr)
         return FPSA_ERR_INVALID_ARG;
     if (!dims_ok(B, H) || N < 1 || C < 1 || C > N || iters < 1 || iters > 1000)
         return FPSA_ERR_INVALID_ARG;
@@ -296,8 +302,9 @@ int32_t fpsa_kmeans(const void* x, int32_t x_dtype, int32_t B, int32_t N, int32_
     if (D != 64 && D != 128) return FPSA_ERR_UNSUPPORTED;
     if (C > FPSA_MAX_SELECT_BLOCKS) return FPSA_ERR_UNSUPPORTED;
     if ((int64_t)B * H * N > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    if (workspace_bytes < fpsa::kmeans_workspace_bytes(B, H, N, C)) return FPSA_ERR_CAPACITY;
     fpsa::launch_kmeans(x, x_dtype == FPSA_F32, B, N, H, D, C, iters, assign, centroids, counts, member_off,
-                        members, static_cast<hipStream_t>(stream));
+                        members, workspace, static_cast<hipStream_t>(stream));
     return hip_status();
 }
 

@@ -14,9 +14,9 @@
 // therefore the same on every device and run.
 //
 // Kernels: k_km_init (strided starting centroids), k_km_assign (nearest centroid as
-// float64 matrix products; cluster sizes by atomic counts), k_km_fill (member lists in
-// token order, a wave per cluster with ballots), k_km_update (centroid = member
-// mean), k_cluster_layout (slot map of the cluster-contiguous blocks), k_cluster_mass
+// float64 matrix products; cluster sizes per 256-token chunk), k_km_chunk_scan +
+// k_km_scatter (member lists in token order from the chunk counts), k_km_update
+// (centroid = member mean), k_cluster_layout (slot map of the cluster-contiguous blocks), k_cluster_mass
 // (centroid-based cluster masses), k_cblk_count / k_cblk_fill (block CSR of a cluster
 // selection).
 #include "fpsa_device.h"
@@ -96,7 +96,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kKmWaves * 64) void k_km_assign(const T* __restrict__ x, int N, int H, int C,
                                                            const double* __restrict__ cent,
                                                            int32_t* __restrict__ assign,
-                                                           int32_t* __restrict__ count) {
+                                                           int32_t* __restrict__ chunk_count) {
     constexpr int kSteps = D / 4;               // products per tile pair
     constexpr int kTile = kSteps * 64;          // doubles per staged centroid tile
     constexpr int kPer = 16 * D / (kKmWaves * 64);   // staged doubles per thread
@@ -190,7 +190,12 @@ __global__ __launch_bounds__(kKmWaves * 64) void k_km_assign(const T* __restrict
         merge(bd0[v], bi0[v]);
         merge(bd1[v], bi1[v]);
     }
-    // lane (g, u): u < 4 writes row g + 4u of tile 0, 4 <= u < 8 row g + 4(u-4) of tile 1
+    // lane (g, u): u < 4 writes row g + 4u of tile 0, 4 <= u < 8 row g + 4(u-4) of tile 1;
+    // the workgroup's cluster sizes (its 256 tokens are one chunk of the member
+    // scatter) are counted in LDS, where the staged tiles were
+    int* hist = reinterpret_cast<int*>(tiles);
+    for (int c = tid; c < C; c += kKmWaves * 64) hist[c] = 0;
+    __syncthreads();
     const int u = lane & 15, g = lane >> 4;
     if (u < 8) {
         const int v = u & 3;
@@ -201,103 +206,164 @@ __global__ __launch_bounds__(kKmWaves * 64) void k_km_assign(const T* __restrict
         const long n = tok0 + (u < 4 ? 0 : 16) + g + 4 * v;
         if (n < N) {
             assign[bh * N + n] = bi;
-            atomicAdd(&count[bh * C + bi], 1);          // sizes only: the order is irrelevant
+            atomicAdd(&hist[bi], 1);
         }
     }
+    __syncthreads();
+    int32_t* row = chunk_count + (bh * C) * (long)gridDim.x + blockIdx.x;   // [bh][c][chunk]
+    for (int c = tid; c < C; c += kKmWaves * 64) row[(long)c * gridDim.x] = hist[c];
 }
 
-__global__ __launch_bounds__(256) void k_zero_i32(int32_t* __restrict__ p, long n) {
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0;
-}
-
-// Members of cluster c of slice bh (row bh*C + c), written in token order with
-// ballots over the slice's assignment.
-__global__ __launch_bounds__(256) void k_km_fill(const int32_t* __restrict__ assign, int N, int C, long rows,
-                                                 const int32_t* __restrict__ off, int32_t* __restrict__ members) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long r = (long)blockIdx.x * 4 + w;
+// Per (slice, cluster): the chunk counts [bh][c][chunk] become exclusive prefix sums over
+// the chunks (a wave per row), and the total is the cluster's size.
+__global__ __launch_bounds__(256) void k_km_chunk_scan(int32_t* __restrict__ chunk_count, int nchunk, long rows,
+                                                       int32_t* __restrict__ count) {
+    const int lane = threadIdx.x & 63;
+    const long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= rows) return;
-    const long bh = r / C;
-    const int c = (int)(r - bh * C);
-    const int32_t* a = assign + bh * N;
-    int32_t* out = members + off[r];
-    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    int32_t* p = chunk_count + r * nchunk;
     int base = 0;
-    for (int n0 = 0; n0 < N; n0 += 64) {
-        const int n = n0 + lane;
-        const bool mine = n < N && a[n] == c;
-        const uint64_t m = __ballot(mine);
-        if (mine) out[base + __popcll(m & lt)] = n;
-        base += __popcll(m);
+    for (int k0 = 0; k0 < nchunk; k0 += 64) {
+        const int k = k0 + lane;
+        const int v = k < nchunk ? p[k] : 0;
+        int s = v;                              // inclusive prefix over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(s, o);
+            if (lane >= o) s += t;
+        }
+        if (k < nchunk) p[k] = base + s - v;
+        base += __shfl(s, 63);
     }
+    if (lane == 0) count[r] = base;
+}
+
+// Members in token order: token n of chunk k (the assignment's workgroups) goes to
+// member_off[bh*C + c] + (members of c in chunks before k) + (members of c before n in
+// chunk k).
+__global__ __launch_bounds__(kKmTokens) void k_km_scatter(const int32_t* __restrict__ assign, int N, int C,
+                                                          const int32_t* __restrict__ chunk_base,
+                                                          const int32_t* __restrict__ off,
+                                                          int32_t* __restrict__ members) {
+    __shared__ int cl[kKmTokens];
+    const long bh = blockIdx.y;
+    const int t = threadIdx.x;
+    const long n = (long)blockIdx.x * kKmTokens + t;
+    const int c = n < N ? assign[bh * N + n] : -1;
+    cl[t] = c;
+    __syncthreads();
+    if (c < 0) return;
+    int rank = 0;
+    for (int s = 0; s < t; ++s) rank += cl[s] == c;
+    members[off[bh * C + c] + chunk_base[(bh * C + c) * (long)gridDim.x + blockIdx.x] + rank] = (int32_t)n;
 }
 
 // Centroid = member mean. The r-th member of a cluster (token order) goes to partial
-// sum r % 8; thread (p, d) adds its partial's members in order (loads fetched 16 at a
-// time), and the eight partials combine as ((p0 + p1) + (p2 + p3)) + ((p4 + p5) +
-// (p6 + p7)). Eight independent chains per channel instead of one.
+// sum r % 8; thread (p, j) adds its partial's members in order for channels 2j and
+// 2j + 1 of a 64-channel slice (member indices of the next batch load while a batch's
+// values arrive), and the eight partials combine as ((p0 + p1) + (p2 + p3)) +
+// ((p4 + p5) + (p6 + p7)). Eight independent chains per channel instead of one.
 constexpr int kKmParts = 8;
+constexpr int kKmSlice = 64;                    // channels per workgroup
+
+__device__ inline void two_channels(const __bf16* p, float& a, float& b) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xffff0000u);
+}
+__device__ inline void two_channels(const float* p, float& a, float& b) {
+    const float2 w = *reinterpret_cast<const float2*>(p);
+    a = w.x;
+    b = w.y;
+}
 
 template <typename T, int D>
-__global__ __launch_bounds__(kKmParts * D) void k_km_update(const T* __restrict__ x, int N, int H, int C,
-                                                            const int32_t* __restrict__ off,
-                                                            const int32_t* __restrict__ members,
-                                                            double* __restrict__ cent) {
-    __shared__ double part[kKmParts][D];
-    const long bh = blockIdx.y;
+__global__ __launch_bounds__(kKmParts * kKmSlice / 2) void k_km_update(const T* __restrict__ x, int N, int H, int C,
+                                                                      const int32_t* __restrict__ off,
+                                                                      const int32_t* __restrict__ members,
+                                                                      double* __restrict__ cent) {
+    __shared__ double part[kKmParts][kKmSlice];
+    const long bh = blockIdx.z;
     const int c = blockIdx.x;
-    const int p = threadIdx.x / D, d = threadIdx.x - (threadIdx.x / D) * D;
+    const int p = threadIdx.x / (kKmSlice / 2), j = threadIdx.x % (kKmSlice / 2);
+    const int d = blockIdx.y * kKmSlice + 2 * j;  // this thread's first channel
     const long b = bh / H, h = bh % H;
     const int r0 = off[bh * C + c], r1 = off[bh * C + c + 1];
     if (r1 == r0) return;                        // an empty cluster keeps its centroid
-    double s = 0.0;
+    double s0 = 0.0, s1 = 0.0;
     constexpr int kBatch = 16;
+    int idx[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+        const int rr = r0 + p + kKmParts * i;
+        idx[i] = rr < r1 ? members[rr] : -1;
+    }
     for (int r = r0 + p; r < r1; r += kKmParts * kBatch) {
-        float v[kBatch];
+        float va[kBatch], vb[kBatch];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
-            const int rr = r + kKmParts * i;
-            v[i] = rr < r1 ? as_float(x[((b * N + members[rr]) * H + h) * D + d]) : 0.0f;
+            va[i] = vb[i] = 0.0f;
+            if (idx[i] >= 0) two_channels(x + ((b * N + idx[i]) * H + h) * D + d, va[i], vb[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int rr = r + kKmParts * (kBatch + i);
+            idx[i] = rr < r1 ? members[rr] : -1;
         }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            if (r + kKmParts * i < r1) s = s + (double)v[i];
+            if (r + kKmParts * i < r1) {
+                s0 = s0 + (double)va[i];
+                s1 = s1 + (double)vb[i];
+            }
     }
-    part[p][d] = s;
+    part[p][2 * j] = s0;
+    part[p][2 * j + 1] = s1;
     __syncthreads();
-    if (p == 0) {
-        const double s01 = part[0][d] + part[1][d], s23 = part[2][d] + part[3][d];
-        const double s45 = part[4][d] + part[5][d], s67 = part[6][d] + part[7][d];
-        cent[(bh * C + c) * D + d] = ((s01 + s23) + (s45 + s67)) / (double)(r1 - r0);
+    if (threadIdx.x < kKmSlice) {
+        const int dd = threadIdx.x;
+        const double s01 = part[0][dd] + part[1][dd], s23 = part[2][dd] + part[3][dd];
+        const double s45 = part[4][dd] + part[5][dd], s67 = part[6][dd] + part[7][dd];
+        cent[(bh * C + c) * D + blockIdx.y * kKmSlice + dd] = ((s01 + s23) + (s45 + s67)) / (double)(r1 - r0);
     }
+}
+
+size_t kmeans_workspace_bytes(int B, int H, int N, int C) {
+    return (size_t)B * H * C * ((N + kKmTokens - 1) / kKmTokens) * sizeof(int32_t);
 }
 
 template <typename T>
 static void kmeans_t(const T* x, int B, int N, int H, int D, int C, int iters, int32_t* assign, double* cent,
-                     int32_t* count, int32_t* off, int32_t* members, hipStream_t st) {
+                     int32_t* count, int32_t* off, int32_t* members, int32_t* chunk, hipStream_t st) {
     const long rows = (long)B * H * C;
     dim3 gc(C, B * H);
     k_km_init<T><<<gc, 128, 0, st>>>(x, N, H, D, C, cent);
-    dim3 ga((N + kKmTokens - 1) / kKmTokens, B * H);
+    const int nchunk = (N + kKmTokens - 1) / kKmTokens;
+    dim3 ga(nchunk, B * H);
     const unsigned wb = (unsigned)((rows + 3) / 4);
-    const unsigned zb = (unsigned)min((rows + 255) / 256, 4096L);
+    dim3 gu(C, D / kKmSlice, B * H);
     for (int it = 0; it < iters; ++it) {
-        k_zero_i32<<<zb, 256, 0, st>>>(count, rows);
-        if (D == 128) k_km_assign<T, 128><<<ga, kKmWaves * 64, (size_t)(2 * 32 * 64 + C) * 8, st>>>(x, N, H, C, cent, assign, count);
-        else k_km_assign<T, 64><<<ga, kKmWaves * 64, (size_t)(2 * 16 * 64 + C) * 8, st>>>(x, N, H, C, cent, assign, count);
+        if (D == 128)
+            k_km_assign<T, 128><<<ga, kKmWaves * 64, (size_t)(2 * 32 * 64 + C) * 8, st>>>(x, N, H, C, cent, assign,
+                                                                                          chunk);
+        else
+            k_km_assign<T, 64><<<ga, kKmWaves * 64, (size_t)(2 * 16 * 64 + C) * 8, st>>>(x, N, H, C, cent, assign,
+                                                                                         chunk);
+        k_km_chunk_scan<<<wb, 256, 0, st>>>(chunk, nchunk, rows, count);
         launch_scan(count, rows, off, st);
-        k_km_fill<<<wb, 256, 0, st>>>(assign, N, C, rows, off, members);
-        if (D == 128) k_km_update<T, 128><<<gc, kKmParts * 128, 0, st>>>(x, N, H, C, off, members, cent);
-        else k_km_update<T, 64><<<gc, kKmParts * 64, 0, st>>>(x, N, H, C, off, members, cent);
+        k_km_scatter<<<ga, kKmTokens, 0, st>>>(assign, N, C, chunk, off, members);
+        if (D == 128) k_km_update<T, 128><<<gu, kKmParts * kKmSlice / 2, 0, st>>>(x, N, H, C, off, members, cent);
+        else k_km_update<T, 64><<<gu, kKmParts * kKmSlice / 2, 0, st>>>(x, N, H, C, off, members, cent);
     }
 }
 
 void launch_kmeans(const void* x, int x_f32, int B, int N, int H, int D, int C, int iters, int32_t* assign,
-                   double* cent, int32_t* count, int32_t* off, int32_t* members, hipStream_t st) {
+                   double* cent, int32_t* count, int32_t* off, int32_t* members, void* ws, hipStream_t st) {
+    int32_t* chunk = static_cast<int32_t*>(ws);
     if (x_f32)
-        kmeans_t(static_cast<const float*>(x), B, N, H, D, C, iters, assign, cent, count, off, members, st);
+        kmeans_t(static_cast<const float*>(x), B, N, H, D, C, iters, assign, cent, count, off, members, chunk, st);
     else
-        kmeans_t(static_cast<const __bf16*>(x), B, N, H, D, C, iters, assign, cent, count, off, members, st);
+        kmeans_t(static_cast<const __bf16*>(x), B, N, H, D, C, iters, assign, cent, count, off, members, chunk, st);
 }
 
 // ---------------------------------------------------------------- layout

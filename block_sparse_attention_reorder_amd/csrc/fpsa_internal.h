@@ -49,8 +49,9 @@ void launch_retained_mass(const float* mass, long R, int nb, const int32_t* row_
 void launch_scan(const int32_t* count, long R, int32_t* out, hipStream_t st);
 
 // k-means semantic permutation (cluster.hip).
+size_t kmeans_workspace_bytes(int B, int H, int N, int C);
 void launch_kmeans(const void* x, int x_f32, int B, int N, int H, int D, int C, int iters, int32_t* assign,
-                   double* cent, int32_t* count, int32_t* off, int32_t* members, hipStream_t st);
+                   double* cent, int32_t* count, int32_t* off, int32_t* members, void* ws, hipStream_t st);
 void launch_cluster_layout(const int32_t* off, const int32_t* members, int B, int H, int C, int nblocks,
                            int32_t* slot_token, int32_t* blk_off, int32_t* blk_count, hipStream_t st);
 void launch_cluster_mass(const double* cq, const int32_t* nq, const double* ck, const int32_t* nk, int B, int H,

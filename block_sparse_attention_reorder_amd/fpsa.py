@@ -26,7 +26,8 @@ EXPORTED = [
     "fpsa_tile_reorder", "fpsa_block_mass", "fpsa_select_blocks", "fpsa_structured_mask",
     "fpsa_pattern_mask", "fpsa_retained_mass", "fpsa_sparse_attn_fwd",
     "fpsa_csr_transpose", "fpsa_transpose_workspace_bytes", "fpsa_sparse_attn_bwd",
-    "fpsa_bwd_workspace_bytes", "fpsa_kmeans", "fpsa_cluster_layout", "fpsa_gather_tiles",
+    "fpsa_bwd_workspace_bytes", "fpsa_kmeans", "fpsa_kmeans_workspace_bytes", "fpsa_cluster_layout",
+    "fpsa_gather_tiles",
     "fpsa_scatter_tiles", "fpsa_cluster_mass", "fpsa_cluster_blocks", "fpsa_sparse_attn_fwd_varlen",
     "fpsa_dequantize_tiles",
 ]
@@ -95,7 +96,9 @@ def lib() -> ctypes.CDLL:
         L.fpsa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fpsa_bwd_workspace_bytes.argtypes = [i32, i32, gp]
         L.fpsa_kmeans.restype = i32
-        L.fpsa_kmeans.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.fpsa_kmeans.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.fpsa_kmeans_workspace_bytes.restype = ctypes.c_size_t
+        L.fpsa_kmeans_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.fpsa_cluster_layout.restype = i32
         L.fpsa_cluster_layout.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         L.fpsa_gather_tiles.restype = i32
@@ -304,13 +307,18 @@ def _i32(*ts):
             raise ValueError("index arrays are int32")
 
 
-def kmeans(x, B, N, H, D, C, iters, assign, centroids, counts, member_off, members, stream=None) -> None:
+def kmeans_workspace_bytes(B, H, N, C) -> int:
+    return int(lib().fpsa_kmeans_workspace_bytes(int(B), int(H), int(N), int(C)))
+
+
+def kmeans(x, B, N, H, D, C, iters, assign, centroids, counts, member_off, members, workspace,
+           stream=None) -> None:
     _i32(assign, counts, member_off, members)
     if centroids.dtype != torch.float64:
         raise ValueError("centroids float64")
     s = lib().fpsa_kmeans(_ptr(x), _DT[x.dtype], int(B), int(N), int(H), int(D), int(C), int(iters),
                           _ptr(assign), _ptr(centroids), _ptr(counts), _ptr(member_off), _ptr(members),
-                          _stream(stream))
+                          _ptr(workspace), int(workspace.numel() * workspace.element_size()), _stream(stream))
     _check(s, "fpsa_kmeans")
 
 

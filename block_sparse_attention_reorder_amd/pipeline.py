@@ -247,7 +247,8 @@ class SemanticSparseAttention:
                      torch.empty((B, H, C), **i32), torch.empty(B * H * C + 1, **i32), torch.empty(B * H * N, **i32),
                      torch.empty((B, H, NB * 64), **i32), torch.empty((B, H, C + 1), **i32),
                      torch.empty((B, H, NB), **i32))
-        fpsa.kmeans(x, B, N, H, D, C, self.iters, c.assign, c.centroids, c.counts, c.member_off, c.members,
+        ws = torch.empty(max(fpsa.kmeans_workspace_bytes(B, H, N, C), 1), dtype=torch.uint8, device=dev)
+        fpsa.kmeans(x, B, N, H, D, C, self.iters, c.assign, c.centroids, c.counts, c.member_off, c.members, ws,
                     stream=stream)
         fpsa.cluster_layout(c.member_off, c.members, B, H, N, C, NB, c.slot_token, c.blk_off, c.blk_count,
                             stream=stream)

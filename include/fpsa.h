@@ -350,12 +350,18 @@ size_t fpsa_bwd_workspace_bytes(int32_t B, int32_t H, const fpsa_grid* g);
  * Outputs (device): assign [B, H, N]; centroids [B, H, C, D] float64; counts
  * [B, H, C]; member_off [B*H*C + 1] and members [B*H*N]: the tokens of cluster c of
  * slice bh, ascending, are members[member_off[bh*C + c] .. member_off[bh*C + c + 1]).
- * Requires D in {64, 128}, 1 <= C <= min(N, FPSA_MAX_SELECT_BLOCKS), 1 <= iters <=
- * 1000, B*H*N < 2^31, and finite inputs.
+ * workspace: device scratch of at least fpsa_kmeans_workspace_bytes(B, H, N, C) bytes
+ * (per-chunk cluster counts; FPSA_ERR_CAPACITY if smaller), contents on return
+ * unspecified. Requires D in {64, 128}, 1 <= C <= min(N, FPSA_MAX_SELECT_BLOCKS),
+ * 1 <= iters <= 1000, B*H*N < 2^31, and finite inputs.
  */
 int32_t fpsa_kmeans(const void* x, int32_t x_dtype, int32_t B, int32_t N, int32_t H, int32_t D,
                     int32_t C, int32_t iters, int32_t* assign, double* centroids, int32_t* counts,
-                    int32_t* member_off, int32_t* members, void* stream);
+                    int32_t* member_off, int32_t* members, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Device scratch bytes fpsa_kmeans needs (0 for invalid sizes). Host-only. */
+size_t fpsa_kmeans_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t C);
 
 /*
  * Cluster-contiguous block layout: cluster c of slice bh fills blocks

@@ -240,7 +240,10 @@ def test_sparse_attn_bwd_validation(L):
 
 def test_kmeans_permutation_validation(L):
     km = L.fpsa_kmeans
-    args = [FAKE, fpsa.BF16, 1, 500, 2, 128, 8, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    wsb = L.fpsa_kmeans_workspace_bytes(1, 2, 500, 8)
+    assert wsb == 2 * 8 * 2 * 4                                 # [bh][c][256-token chunk] counts
+    assert L.fpsa_kmeans_workspace_bytes(1, 2, 500, 0) == 0
+    args = [FAKE, fpsa.BF16, 1, 500, 2, 128, 8, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsb, None]
     def call(i, val, f=km, base=args):
         a = list(base)
         a[i] = val
@@ -253,6 +256,8 @@ def test_kmeans_permutation_validation(L):
     assert call(6, 501) == fpsa.ERR_INVALID_ARG                 # more clusters than tokens
     assert call(7, 0) == fpsa.ERR_INVALID_ARG
     assert call(12, None) == fpsa.ERR_INVALID_ARG
+    assert call(13, None) == fpsa.ERR_INVALID_ARG
+    assert call(14, wsb - 1) == fpsa.ERR_CAPACITY
     lay = [FAKE, FAKE, 1, 2, 500, 8, 8 + 8, FAKE, FAKE, FAKE, None]   # ceil(500/64) + 8 = 16 blocks
     assert call(6, 15, L.fpsa_cluster_layout, lay) == fpsa.ERR_CAPACITY
     assert call(0, None, L.fpsa_cluster_layout, lay) == fpsa.ERR_INVALID_ARG

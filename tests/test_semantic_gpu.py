@@ -62,7 +62,8 @@ def test_kmeans_extreme_cluster_counts(N, H, D, C, iters):
     a, cnt = torch.empty((1, H, N), **i32), torch.empty((1, H, C), **i32)
     cent = torch.empty((1, H, C, D), dtype=torch.float64, device="cuda")
     mo, mem = torch.empty(H * C + 1, **i32), torch.empty(H * N, **i32)
-    fpsa.kmeans(xb, 1, N, H, D, C, iters, a, cent, cnt, mo, mem)
+    ws = torch.empty(fpsa.kmeans_workspace_bytes(1, H, N, C), dtype=torch.uint8, device="cuda")
+    fpsa.kmeans(xb, 1, N, H, D, C, iters, a, cent, cnt, mo, mem, ws)
     ra, rc, rn = O.kmeans(xr, C, iters)
     assert np.array_equal(a.cpu().numpy(), ra)
     assert np.array_equal(cnt.cpu().numpy(), rn)
