@@ -26,7 +26,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"bf16": 2500.0, "fp8": 5000.0}          # dense MFMA, TFLOP/s
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "fp64": 78.6}   # dense MFMA, TFLOP/s
 HBM_PEAK = 8000.0                                # GB/s
 CSRC = os.path.join(ROOT, "block_sparse_attention_reorder_amd", "csrc")
 # sources each timed kernel is built from (its counters go stale when they change)
@@ -569,7 +569,12 @@ def semantic_row(bsa, w, qt, stream, reps):
             "density_of_padded_pairs": round(nnz / (w.B * w.H * ssa.NB * ssa.NB), 4),
             "padding_overhead": round(w.B * w.H * ssa.NB / max(real_pairs, 1.0), 4),
             "fwd_kept_tflops": round(flop / st["forward"] / 1e9, 2),
-            "fwd_frac_of_bf16_peak": round(flop / st["forward"] / 1e9 / PEAK["bf16"], 4)}
+            "fwd_frac_of_bf16_peak": round(flop / st["forward"] / 1e9 / PEAK["bf16"], 4),
+            # the assignment products (2 N C D FLOP per step, slice and tensor, float64
+            # MFMA) over the whole k-means time (layout and member lists included)
+            "kmeans_fp64_tflops": round(2 * 4 * 2.0 * bsa.N * 128 * w.D * w.B * w.H / st["kmeans_q_and_k"] / 1e9, 2),
+            "kmeans_frac_of_fp64_peak": round(2 * 4 * 2.0 * bsa.N * 128 * w.D * w.B * w.H / st["kmeans_q_and_k"]
+                                              / 1e9 / PEAK["fp64"], 4)}
 
 
 def cpu_baseline(w, q, k, v, bsa, nsample):
