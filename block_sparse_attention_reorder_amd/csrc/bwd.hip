@@ -71,22 +71,33 @@ __device__ inline int qk_off(int e, int d) {
     return 2 * (((((e >> 5) * (D / 16) + (d >> 4)) * 2 + ((d >> 3) & 1)) * 32 + (e & 31)) * 8 + (d & 7));
 }
 
-// Offset of this lane's 8-byte source for a transposing read of the QK tile that
-// gives each lane of a 16-lane group g one channel (16*(g%2) + lane%16 of a 32-channel
-// tile) and four consecutive tokens, starting at token t0 + 4*(g/2): input lane a
-// supplies token t0 + 4*(g/2) + a/4, channels 4*(a%4) .. +3. Tokens t0 + 8 .. follow
-// at +128 bytes, the next 16 tokens at +256, the next 32-channel tile at +2048.
+// LDS copies of the QK tiles are swizzled: within each kilobyte (two 512-byte groups of
+// 32 tokens x 8 channels), the odd group has its 8-token runs of 128 bytes swapped in
+// pairs (16-byte unit e of an odd group sits at unit e ^ 8). A copy lane l therefore
+// fetches source unit l ^ 8*(l >> 5) of its kilobyte, and a plain operand read by lane l
+// of unit l of a kilobyte reads position l ^ 8*(l >> 5) (swz_unit). The transposing reads
+// below touch four groups at once; without the swap the even and odd groups share their
+// banks (two-way conflicts), with it they fall on different halves of the banks.
+__device__ inline int swz_unit(int l) { return l ^ ((l >> 5) << 3); }
+
+// Offset of this lane's 8-byte source for a transposing read of the swizzled QK tile
+// that gives each lane of a 16-lane group g one channel (16*(g%2) + lane%16 of a
+// 32-channel tile) and four consecutive tokens, starting at token t0 + 4*(g/2): input
+// lane a supplies token t0 + 4*(g/2) + a/4, channels 4*(a%4) .. +3 (t0 a multiple of
+// 32). Tokens t0 + 8 .. follow at offset ^ 128 bytes, the next 16 tokens at +256, the
+// next 32-channel tile at +2048. Channels 8 .. 15 of a 16 (a%4 >= 2) sit in the odd
+// group, whose 8-token halves are swapped: +128 for those lanes.
 template <int D>
 __device__ inline int tr_base(int t0, int lane) {
     const int g = lane >> 4, a = lane & 15;
-    return qk_off<D>(t0 + 4 * (g >> 1) + (a >> 2), 16 * (g & 1) + 4 * (a & 3));
+    return qk_off<D>(t0 + 4 * (g >> 1) + (a >> 2), 16 * (g & 1) + 4 * (a & 3)) + 128 * ((a >> 1) & 1);
 }
 
 // Operand of 8 tokens in position order (t0..t0+3, then t0+8..t0+11 of the lane's
 // half) for one channel per lane.
 __device__ inline bf16x8 tr_operand(const uint8_t* tile, int off) {
     const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off));
-    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off + 128));
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + (off ^ 128)));
     const s16x8 z = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, z);
 }
@@ -193,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     // Q and dO tiles of a query block copied straight into a slot, this wave moving a
     // quarter of each in whole kilobytes (a missing block copies block 0)
     constexpr int kCh = kTile / 1024 / 4;
-    const int lane16 = 16 * lane;
+    const int lane16 = 16 * swz_unit(lane);       // swizzled source unit of this lane
     const i32x4r qrs = tile_rsrc_raw(q + bh * npad * D, (uint32_t)(npad * D * 2));
     const i32x4r grs = tile_rsrc_raw(dout + bh * npad * D, (uint32_t)(npad * D * 2));
     auto copy_block = [&](int qbk, uint8_t* dst) {
@@ -232,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         bf16x8 qa[D / 16], ga[D / 16];
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            const int off = (r * (D / 16) + st) * 1024 + 16 * lane;
+            const int off = (r * (D / 16) + st) * 1024 + 16 * swz_unit(lane);
             qa[st] = *reinterpret_cast<const bf16x8*>(sq + off);
             ga[st] = *reinterpret_cast<const bf16x8*>(sg + off);
         }
@@ -379,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     // K and V tiles of a block copied straight into an LDS slot, this wave moving its
     // quarter of each in whole kilobytes (a missing block copies block 0)
     constexpr int kCh = kTile / 1024 / 4;
-    const int lane16 = 16 * lane;
+    const int lane16 = 16 * swz_unit(lane);       // swizzled source unit of this lane
     const i32x4r krs = tile_rsrc_raw(k + bh * npad * D, (uint32_t)(npad * D * 2));
     const i32x4r vrs = tile_rsrc_raw(v + bh * npad * D, (uint32_t)(npad * D * 2));
     auto copy_block = [&](int info, uint8_t* dst) {
@@ -401,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
         bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            const int off = (kh * (D / 16) + st) * 1024 + 16 * lane;
+            const int off = (kh * (D / 16) + st) * 1024 + 16 * swz_unit(lane);
             ka[st] = *reinterpret_cast<const bf16x8*>(sk + off);
             va[st] = *reinterpret_cast<const bf16x8*>(sv + off);
         }
