@@ -101,14 +101,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     auto block_of = [](int info) { return info < 0 ? 0 : (info & kBlockIdMask); };
 
     // Copy the K (or V) tile of a block into ring slot `slot`: this wave moves its
-    // share of contiguous kilobytes, lane l carrying 16 bytes each. An entry with no
-    // block copies block 0 (never read as data).
+    // share of the tile's LDS kilobytes, lane l carrying 16 bytes each. LDS kilobyte c
+    // of a K tile holds, for bf16, the same kilobyte of the tile (lane l: bytes 16 l);
+    // for e4m3, half c % 2 of the 2 KB operand step c / 2 (lane l: bytes 32 l + 16 (c % 2)),
+    // the split layout the e4m3 operand reads expect. An entry with no block copies
+    // block 0 (never read as data).
     const int lane16 = 16 * lane;
+    const int klane = FP8 ? 32 * lane : 16 * lane;
+    auto ksrc = [](int c) -> uint32_t { return FP8 ? (c >> 1) * 2048 + 16 * (c & 1) : c * 1024; };
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbytes, (uint32_t)(g.nb * kKBytes));
     const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbytes, (uint32_t)(g.nb * kVBytes));
     auto copy_k = [&](int info, int slot) {
-        copy_to_lds<kKChunks>(krs, (uint32_t)(block_of(info) * kKBytes + kKChunks * w * 1024),
-                               kring + slot * kKBytes + kKChunks * w * 1024, lane16);
+#pragma unroll
+        for (int i = 0; i < kKChunks; ++i)
+            copy_kb_to_lds(krs, (uint32_t)(block_of(info) * kKBytes) + ksrc(kKChunks * w + i),
+                           kring + slot * kKBytes + (kKChunks * w + i) * 1024, klane);
     };
     auto copy_v = [&](int info, int slot) {
         copy_to_lds<kVChunks>(vrs, (uint32_t)(block_of(info) * kVBytes + kVChunks * w * 1024),
@@ -148,8 +155,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
         // copy i < kKChunks: kilobyte i of this wave's share of K(j+2); then V(j+1)
         auto copy_one = [&](int i) {
             if (i < kKChunks)
-                copy_kb_to_lds(krs, (uint32_t)(block_of(inf2) * kKBytes + (kKChunks * w + i) * 1024),
-                               kring + (j & 1) * kKBytes + (kKChunks * w + i) * 1024, lane16);
+                copy_kb_to_lds(krs, (uint32_t)(block_of(inf2) * kKBytes) + ksrc(kKChunks * w + i),
+                               kring + (j & 1) * kKBytes + (kKChunks * w + i) * 1024, klane);
             else
                 copy_kb_to_lds(vrs, (uint32_t)(block_of(infn) * kVBytes + (kVChunks * w + i - kKChunks) * 1024),
                                vring + ((j + 1) & 1) * kVBytes + (kVChunks * w + i - kKChunks) * 1024, lane16);

@@ -130,13 +130,20 @@ __device__ inline void load_khalf(KHalf<D, FP8>& k, const void* base, long row0,
     }
 }
 
-// LDS operand reads: the same lane-order kilobytes the global layouts hold.
+// LDS operand reads: bf16, the same lane-order kilobytes the global layout holds; e4m3,
+// each 2 KB step split by halves (the first 16 bytes of every lane's 32, in lane order,
+// then the second 16), so that both reads run over a contiguous kilobyte instead of
+// striding 32 bytes (which used half of the banks).
 template <int D, bool FP8>
 __device__ inline void lds_khalf(KHalf<D, FP8>& k, const uint8_t* st, int kh, int lane) {
     if constexpr (FP8) {
 #pragma unroll
-        for (int j = 0; j < D / 64; ++j)
-            k.f[j] = *reinterpret_cast<const i32x8*>(st + (kh * (D / 64) + j) * 2048 + 32 * lane);
+        for (int j = 0; j < D / 64; ++j) {
+            const uint8_t* p = st + (kh * (D / 64) + j) * 2048 + 16 * lane;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 1024);
+            k.f[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < D / 16; ++j)
