@@ -33,34 +33,6 @@
 
 namespace fpsa {
 
-// Direct global-to-LDS copy of one kilobyte (buffer_load_dwordx4 ... lds, lane l
-// carrying bytes 16*l .. +15 to M0 + 16*l) issued from inline asm, for loops that keep a
-// copy in flight while they read other LDS slots: the compiler does not see it and so adds no waits of its
-// own before LDS reads; the caller orders every read of a slot after the copy into it
-// has landed (vmcnt, then a barrier) and every copy into a slot after the last read of
-// it (a barrier). The asm has no register outputs besides the M0 save, and restores M0.
-typedef int i32x4r __attribute__((ext_vector_type(4)));
-__device__ __attribute__((always_inline)) inline i32x4r tile_rsrc_raw(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4r r;
-    r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)a);
-    r[1] = (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    r[2] = (int)bytes;
-    r[3] = 0x00020000;
-    return r;
-}
-__device__ __attribute__((always_inline)) inline void copy_kb_asm(i32x4r rs, uint32_t off, uint8_t* dst,
-                                                                   int lane16) {
-    const uint32_t la = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)dst);
-    const uint32_t so = __builtin_amdgcn_readfirstlane(off);
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "s"(la), "v"(lane16), "s"(rs), "s"(so)
-                 : "memory");
-}
-
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;

@@ -16,8 +16,11 @@
 // share every key tile: a workgroup of four waves owns both, wave w taking query
 // rows 32*(w & 1) .. +31 of block 2i + (w >> 1) against all 64 keys of each key
 // block. The K tile of each block is copied once per workgroup into a two-slot LDS
-// ring with direct global-to-LDS loads; every wave reads it in the lane order of the MFMA
-// operand (QK tiled layout). Scores use the transposed MFMA form of the sparse
+// ring with direct global-to-LDS loads issued from inline asm (so that the compiler
+// adds no wait for them before reads of the other slot), and each wave streams the
+// operands four steps ahead of their products: 168 registers, three workgroups per
+// CU. Every wave reads the tile in the lane order of the MFMA operand (QK tiled
+// layout). Scores use the transposed MFMA form of the sparse
 // forward (S^T = K * Q^T, v_mfma_f32_32x32x16_bf16), so a lane holds 32 of its
 // query's 64 block scores and the block sums are in-lane plus one swap of the wave
 // halves. The products of block j+1 are issued between the exponentials of block j
@@ -38,7 +41,7 @@ constexpr int kMassThreads = 256;
 constexpr float kMassSumLimit = 18446744073709551616.0f;   // 2^64
 
 template <int D>
-__global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __restrict__ q,
+__global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __restrict__ q,
                                                                 const __bf16* __restrict__ k,
                                                                 Geom g, long p_begin, long p_count,
                                                                 float scale_log2,
@@ -80,10 +83,15 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
 
     const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(k) + bh * npad * D * 2;
     const int lane16 = 16 * lane;
-    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbytes, (uint32_t)(npad * D * 2));
+    // copies from inline asm: the compiler adds no wait for them before the K reads of
+    // the other slot that follow them (every read of a slot comes after the vmcnt(0) and
+    // barrier that follow the copy into it)
+    const i32x4r krs = tile_rsrc_raw(kbytes, (uint32_t)(npad * D * 2));
     auto copy_k = [&](int kb, int slot) {
-        copy_to_lds<kKChunks>(krs, (uint32_t)((kb < g.nb ? kb : 0) * kKBytes + kKChunks * w * 1024),
-                              lds + slot * kKBytes + kKChunks * w * 1024, lane16);
+#pragma unroll
+        for (int i = 0; i < kKChunks; ++i)
+            copy_kb_asm(krs, (uint32_t)((kb < g.nb ? kb : 0) * kKBytes + (kKChunks * w + i) * 1024),
+                        lds + slot * kKBytes + (kKChunks * w + i) * 1024, lane16);
     };
 
     // Edge code of block kb (bit a: last, partial tile along a ragged axis), kept
@@ -175,8 +183,15 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
     auto main_ordered = [&](int j, const f32x16 (&s)[2], f32x16 (&sn)[2], const bf16x8 (&bias)[2]) {
         const float nref = m == -INFINITY ? 0.0f : -m;
         const uint8_t* kst = lds + ((j + 1) & 1) * kKBytes;
-        lds_khalf<D, false>(k0, kst, 0, lane);
-        lds_khalf<D, false>(k1, kst, 1, lane);
+        // the K(j+1) operands stream in four steps ahead of their products, which keeps
+        // the kernel within 168 registers (three workgroups per CU)
+        constexpr int kAheadSt = 4;
+        auto kread = [&](int st) {
+            k0.b[st] = *reinterpret_cast<const bf16x8*>(kst + st * 1024 + 16 * lane);
+            k1.b[st] = *reinterpret_cast<const bf16x8*>(kst + (D / 16 + st) * 1024 + 16 * lane);
+        };
+#pragma unroll
+        for (int st = 0; st < kAheadSt && st < D / 16; ++st) kread(st);
         __builtin_amdgcn_sched_barrier(0);
         copy_k(j + 2, j & 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -201,6 +216,7 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
             }
             pin(acc0);
             pin(acc1);
+            if (kt == 1 && st + kAheadSt < D / 16) kread(st + kAheadSt);
             __builtin_amdgcn_sched_barrier(0);
         }
         return wave_add32(acc0 + acc1);
@@ -237,6 +253,8 @@ __global__ __launch_bounds__(kMassThreads, 2) void k_block_mass(const __bf16* __
         step(j, sa, sb);
         if (j + 1 < nb) step(j + 1, sb, sa);
     }
+
+    wait_vmcnt<0>();                                         // drain the last (unused) copies
 
     // Row log-sum-exp (base 2) of each query; padding queries take +inf so that
     // they add 2^-inf = 0 to every mass.
