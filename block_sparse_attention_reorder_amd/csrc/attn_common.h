@@ -105,12 +105,14 @@ __device__ __attribute__((always_inline)) inline void copy_to_lds(__amdgpu_buffe
     for (int j = 0; j < KB; ++j) copy_kb_to_lds(rs, off + j * 1024, dst + j * 1024, lane16);
 }
 
-// Direct global-to-LDS copy of one kilobyte (buffer_load_dwordx4 ... lds, lane l
-// carrying bytes 16*l .. +15 to M0 + 16*l) issued from inline asm, for loops that keep a
-// copy in flight while they read other LDS slots: the compiler does not see it and so adds no waits of its
-// own before LDS reads; the caller orders every read of a slot after the copy into it
-// has landed (vmcnt, then a barrier) and every copy into a slot after the last read of
-// it (a barrier). The asm has no register outputs besides the M0 save, and restores M0.
+// Direct global-to-LDS copy of one kilobyte (buffer_load_dwordx4 ... lds: lane l carries
+// the 16 bytes at its own source offset `lane16` past `off` to M0 + 16*l) issued from
+// inline asm, for loops that keep a copy in flight while they read other LDS slots: the
+// compiler does not see it and so adds no waits of its own before LDS reads; the caller
+// orders every read of a slot after the copy into it has landed (vmcnt, then a barrier),
+// every copy into a slot after the last read of it (a barrier), and drains the copies
+// before the kernel ends. The asm has no register outputs besides the M0 save, and
+// restores M0.
 typedef int i32x4r __attribute__((ext_vector_type(4)));
 __device__ __attribute__((always_inline)) inline i32x4r tile_rsrc_raw(const void* base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);

@@ -260,68 +260,71 @@ __global__ __launch_bounds__(kKmTokens) void k_km_scatter(const int32_t* __restr
 
 // Centroid = member mean. The r-th member of a cluster (token order) goes to partial
 // sum r % 8; thread (p, j) adds its partial's members in order for channels 2j and
-// 2j + 1 of a 64-channel slice (member indices of the next batch load while a batch's
-// values arrive), and the eight partials combine as ((p0 + p1) + (p2 + p3)) +
-// ((p4 + p5) + (p6 + p7)). Eight independent chains per channel instead of one.
+// 2j + 1 of a 64-channel slice, and the eight partials combine as ((p0 + p1) + (p2 +
+// p3)) + ((p4 + p5) + (p6 + p7)). Eight independent chains per channel instead of one.
+// Members are taken in stages of 256: the stage's member indices sit in LDS (loaded
+// one stage ahead, one per thread), and each thread has its 32 values of the stage in
+// flight at once, so a large cluster costs one memory round trip per 256 members.
 constexpr int kKmParts = 8;
 constexpr int kKmSlice = 64;                    // channels per workgroup
+constexpr int kKmThreads = kKmParts * kKmSlice / 2;
+constexpr int kKmStage = kKmThreads;            // members per stage
+constexpr int kKmPer = kKmStage / kKmParts;     // values per thread per stage
 
-__device__ inline void two_channels(const __bf16* p, float& a, float& b) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+__device__ inline uint32_t two_raw(const __bf16* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ inline float2 two_raw(const float* p) { return *reinterpret_cast<const float2*>(p); }
+__device__ inline void two_channels(uint32_t w, float& a, float& b) {
     a = __uint_as_float(w << 16);
     b = __uint_as_float(w & 0xffff0000u);
 }
-__device__ inline void two_channels(const float* p, float& a, float& b) {
-    const float2 w = *reinterpret_cast<const float2*>(p);
+__device__ inline void two_channels(float2 w, float& a, float& b) {
     a = w.x;
     b = w.y;
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kKmParts * kKmSlice / 2) void k_km_update(const T* __restrict__ x, int N, int H, int C,
-                                                                      const int32_t* __restrict__ off,
-                                                                      const int32_t* __restrict__ members,
-                                                                      double* __restrict__ cent) {
+__global__ __launch_bounds__(kKmThreads) void k_km_update(const T* __restrict__ x, int N, int H, int C,
+                                                         const int32_t* __restrict__ off,
+                                                         const int32_t* __restrict__ members,
+                                                         double* __restrict__ cent) {
     __shared__ double part[kKmParts][kKmSlice];
+    __shared__ int32_t sidx[2][kKmStage];
     const long bh = blockIdx.z;
     const int c = blockIdx.x;
-    const int p = threadIdx.x / (kKmSlice / 2), j = threadIdx.x % (kKmSlice / 2);
+    const int tid = threadIdx.x;
+    const int p = tid / (kKmSlice / 2), j = tid % (kKmSlice / 2);
     const int d = blockIdx.y * kKmSlice + 2 * j;  // this thread's first channel
     const long b = bh / H, h = bh % H;
     const int r0 = off[bh * C + c], r1 = off[bh * C + c + 1];
-    if (r1 == r0) return;                        // an empty cluster keeps its centroid
+    if (r1 == r0) return;                        // an empty cluster keeps its centroid (uniform)
+    const T* xb = x + (b * N * H + h) * (long)D + d;   // token t at xb + t * H * D
     double s0 = 0.0, s1 = 0.0;
-    constexpr int kBatch = 16;
-    int idx[kBatch];
+    int nxt = r0 + tid < r1 ? members[r0 + tid] : 0;
+    for (int base = r0, st = 0; base < r1; base += kKmStage, st ^= 1) {
+        sidx[st][tid] = nxt;
+        __syncthreads();                         // indices of this stage visible; the other buffer free
+        const int cnt = min(kKmStage, r1 - base);
+        decltype(two_raw(xb)) raw[kKmPer];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-        const int rr = r0 + p + kKmParts * i;
-        idx[i] = rr < r1 ? members[rr] : -1;
-    }
-    for (int r = r0 + p; r < r1; r += kKmParts * kBatch) {
-        float va[kBatch], vb[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            va[i] = vb[i] = 0.0f;
-            if (idx[i] >= 0) two_channels(x + ((b * N + idx[i]) * H + h) * D + d, va[i], vb[i]);
+        for (int i = 0; i < kKmPer; ++i) {
+            const int q = p + kKmParts * i;      // member base + q of partial p
+            raw[i] = two_raw(xb + (long)sidx[st][q < cnt ? q : 0] * H * D);
         }
+        nxt = base + kKmStage + tid < r1 ? members[base + kKmStage + tid] : 0;
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
-            const int rr = r + kKmParts * (kBatch + i);
-            idx[i] = rr < r1 ? members[rr] : -1;
-        }
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-            if (r + kKmParts * i < r1) {
-                s0 = s0 + (double)va[i];
-                s1 = s1 + (double)vb[i];
+        for (int i = 0; i < kKmPer; ++i)
+            if (p + kKmParts * i < cnt) {
+                float va, vb;
+                two_channels(raw[i], va, vb);
+                s0 = s0 + (double)va;
+                s1 = s1 + (double)vb;
             }
     }
     part[p][2 * j] = s0;
     part[p][2 * j + 1] = s1;
     __syncthreads();
-    if (threadIdx.x < kKmSlice) {
-        const int dd = threadIdx.x;
+    if (tid < kKmSlice) {
+        const int dd = tid;
         const double s01 = part[0][dd] + part[1][dd], s23 = part[2][dd] + part[3][dd];
         const double s45 = part[4][dd] + part[5][dd], s67 = part[6][dd] + part[7][dd];
         cent[(bh * C + c) * D + blockIdx.y * kKmSlice + dd] = ((s01 + s23) + (s45 + s67)) / (double)(r1 - r0);
@@ -352,8 +355,8 @@ static void kmeans_t(const T* x, int B, int N, int H, int D, int C, int iters, i
         k_km_chunk_scan<<<wb, 256, 0, st>>>(chunk, nchunk, rows, count);
         launch_scan(count, rows, off, st);
         k_km_scatter<<<ga, kKmTokens, 0, st>>>(assign, N, C, chunk, off, members);
-        if (D == 128) k_km_update<T, 128><<<gu, kKmParts * kKmSlice / 2, 0, st>>>(x, N, H, C, off, members, cent);
-        else k_km_update<T, 64><<<gu, kKmParts * kKmSlice / 2, 0, st>>>(x, N, H, C, off, members, cent);
+        if (D == 128) k_km_update<T, 128><<<gu, kKmThreads, 0, st>>>(x, N, H, C, off, members, cent);
+        else k_km_update<T, 64><<<gu, kKmThreads, 0, st>>>(x, N, H, C, off, members, cent);
     }
 }
 
