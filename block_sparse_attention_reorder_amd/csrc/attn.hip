@@ -9,7 +9,9 @@
 // kept block are copied once per workgroup into LDS with direct global-to-LDS loads
 // (buffer_load_dwordx4 ... lds, each wave moving a quarter of each tile in contiguous
 // kilobytes) into two-slot K and V rings, K two blocks and V one block ahead of
-// use; one barrier per block. Wave w takes query rows 32*(w & 1) .. +31 and key
+// use; one barrier per block. The e4m3 variant issues its copies from inline asm and
+// reads the second half of its V operands later in the block, which fits it in 168
+// registers and three workgroups per CU (its K ring is half the size). Wave w takes query rows 32*(w & 1) .. +31 and key
 // rows 32*(w >> 1) .. +31 of every block (the layout conventions are described in
 // attn_common.h); the two key halves of a query row carry separate online-softmax
 // states that are merged once at the end through LDS. Workgroups are remapped so
@@ -26,7 +28,7 @@ constexpr int kAttnThreads = 256;
 // CNT: the real keys of each key block are its first kcount[(b*H + h)*nb + kb] slots
 // (blocks of a cluster-contiguous layout) instead of following from the token grid.
 template <int D, bool FP8, bool CNT>
-__global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
+__global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
     const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long R,
@@ -111,15 +113,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
     auto ksrc = [](int c) -> uint32_t { return FP8 ? (c >> 1) * 2048 + 16 * (c & 1) : c * 1024; };
     const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kbytes, (uint32_t)(g.nb * kKBytes));
     const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vbytes, (uint32_t)(g.nb * kVBytes));
+    const i32x4r krs_a = tile_rsrc_raw(kbytes, (uint32_t)(g.nb * kKBytes));
+    const i32x4r vrs_a = tile_rsrc_raw(vbytes, (uint32_t)(g.nb * kVBytes));
+    auto kcopy = [&](uint32_t off, uint8_t* dst) {
+        if constexpr (FP8) copy_kb_asm(krs_a, off, dst, klane);
+        else copy_kb_to_lds(krs, off, dst, klane);
+    };
+    auto vcopy = [&](uint32_t off, uint8_t* dst) {
+        if constexpr (FP8) copy_kb_asm(vrs_a, off, dst, lane16);
+        else copy_kb_to_lds(vrs, off, dst, lane16);
+    };
     auto copy_k = [&](int info, int slot) {
 #pragma unroll
         for (int i = 0; i < kKChunks; ++i)
-            copy_kb_to_lds(krs, (uint32_t)(block_of(info) * kKBytes) + ksrc(kKChunks * w + i),
-                           kring + slot * kKBytes + (kKChunks * w + i) * 1024, klane);
+            kcopy((uint32_t)(block_of(info) * kKBytes) + ksrc(kKChunks * w + i),
+                  kring + slot * kKBytes + (kKChunks * w + i) * 1024);
     };
     auto copy_v = [&](int info, int slot) {
-        copy_to_lds<kVChunks>(vrs, (uint32_t)(block_of(info) * kVBytes + kVChunks * w * 1024),
-                               vring + slot * kVBytes + kVChunks * w * 1024, lane16);
+#pragma unroll
+        for (int i = 0; i < kVChunks; ++i)
+            vcopy((uint32_t)(block_of(info) * kVBytes + (kVChunks * w + i) * 1024),
+                  vring + slot * kVBytes + (kVChunks * w + i) * 1024);
     };
 
     // Software pipeline across kept blocks. Iteration j holds the scores of block j
@@ -155,11 +169,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_sparse_attn(
         // copy i < kKChunks: kilobyte i of this wave's share of K(j+2); then V(j+1)
         auto copy_one = [&](int i) {
             if (i < kKChunks)
-                copy_kb_to_lds(krs, (uint32_t)(block_of(inf2) * kKBytes) + ksrc(kKChunks * w + i),
-                               kring + (j & 1) * kKBytes + (kKChunks * w + i) * 1024, klane);
+                kcopy((uint32_t)(block_of(inf2) * kKBytes) + ksrc(kKChunks * w + i),
+                      kring + (j & 1) * kKBytes + (kKChunks * w + i) * 1024);
             else
-                copy_kb_to_lds(vrs, (uint32_t)(block_of(infn) * kVBytes + (kVChunks * w + i - kKChunks) * 1024),
-                               vring + ((j + 1) & 1) * kVBytes + (kVChunks * w + i - kKChunks) * 1024, lane16);
+                vcopy((uint32_t)(block_of(infn) * kVBytes + (kVChunks * w + i - kKChunks) * 1024),
+                      vring + ((j + 1) & 1) * kVBytes + (kVChunks * w + i - kKChunks) * 1024);
         };
         constexpr int kCopies = kKChunks + kVChunks;
         if constexpr (D == 128 && !FP8)

@@ -434,21 +434,24 @@ __device__ __attribute__((always_inline)) inline void block_main_fp8_d128(
         if (i < NC) copy_one(i);
     };
 #define FPSA_SB __builtin_amdgcn_sched_barrier(0)
+    auto VR = [&](int t, int cc) {     // V operand, read a few products before its use
+        v[t][cc] = *reinterpret_cast<const bf16x8*>(vst + (t * 4 + 2 * kh + cc) * 1024 + 16 * lane);
+    };
     lds_khalf<128, true>(k, kst, kh, lane);
-    lds_vhalf<128>(v, vst, kh, lane);
+    VR(0, 0); VR(1, 0); VR(2, 0); VR(3, 0);
     FM(0); FM(1); FM(2); FM(3); EX(0); EX(1);
     FPSA_SB;
     QK(0); CP(0); CP(1); EX(2); FM(4); EX(3); FM(5); CV(0); FM(6);
     FPSA_SB;
     QK(1); CP(2); CP(3); EX(4); FM(7); EX(5); FM(8); CV(2); FM(9); EX(6); EX(7); CV(4); CV(6);
     FPSA_SB;
-    PV(0, 0); CP(4); EX(8); FM(10); DT(0); DT(1);
+    PV(0, 0); VR(0, 1); CP(4); EX(8); FM(10); DT(0); DT(1);
     FPSA_SB;
-    PV(1, 0); CP(5); EX(9); FM(11); DT(2); CV(8);
+    PV(1, 0); VR(1, 1); CP(5); EX(9); FM(11); DT(2); CV(8);
     FPSA_SB;
-    PV(2, 0); CP(6); EX(10); FM(12); EX(11); FM(13); DT(3);
+    PV(2, 0); VR(2, 1); CP(6); EX(10); FM(12); EX(11); FM(13); DT(3);
     FPSA_SB;
-    PV(3, 0); CP(7); EX(12); FM(14); EX(13); FM(15); CV(10); DT(4);
+    PV(3, 0); VR(3, 1); CP(7); EX(12); FM(14); EX(13); FM(15); CV(10); DT(4);
     FPSA_SB;
     EX(14); EX(15); CV(12); CV(14); DT(5);
     FPSA_SB;
