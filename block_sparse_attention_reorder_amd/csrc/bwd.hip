@@ -354,10 +354,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
 
     const int e0 = row_ptr[row], n = row_ptr[row + 1] - e0;
-    // index word (block and edge code) of entry jj, -1 when none
+    // index word (block and edge code) of entry jj, -1 when none; jj = 0, 1, 2, ... in
+    // order. The words of 64 entries are formed at once, a lane each (the edge code's
+    // divisions run once per 64 blocks), and the next 64 indices load a window ahead.
+    int cur = lane < n ? block_info(g, col_idx[e0 + lane]) : -1;
+    int raw = 64 + lane < n ? col_idx[e0 + 64 + lane] : -1;
+    int wbase = 0;
     auto info_at = [&](int jj) {
         if (jj >= n) return -1;
-        return block_info(g, __builtin_amdgcn_readfirstlane(col_idx[e0 + jj]));
+        if (jj - wbase == 64) {
+            wbase += 64;
+            cur = block_info(g, raw);
+            raw = wbase + 64 + lane < n ? col_idx[e0 + wbase + 64 + lane] : -1;
+        }
+        return __builtin_amdgcn_readlane(cur, jj - wbase);
     };
     // K and V tiles of a block copied straight into an LDS slot, this wave moving its
     // quarter of each in whole kilobytes (a missing block copies block 0)
