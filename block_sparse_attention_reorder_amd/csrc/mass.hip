@@ -18,7 +18,7 @@
 // block. The K tile of each block is copied once per workgroup into a two-slot LDS
 // ring with direct global-to-LDS loads issued from inline asm (so that the compiler
 // adds no wait for them before reads of the other slot), and each wave streams the
-// operands four steps ahead of their products: 168 registers, three workgroups per
+// operands two steps ahead of their products: 156 registers, three workgroups per
 // CU. Every wave reads the tile in the lane order of the MFMA operand (QK tiled
 // layout). Scores use the transposed MFMA form of the sparse
 // forward (S^T = K * Q^T, v_mfma_f32_32x32x16_bf16), so a lane holds 32 of its
@@ -183,9 +183,9 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
     auto main_ordered = [&](int j, const f32x16 (&s)[2], f32x16 (&sn)[2], const bf16x8 (&bias)[2]) {
         const float nref = m == -INFINITY ? 0.0f : -m;
         const uint8_t* kst = lds + ((j + 1) & 1) * kKBytes;
-        // the K(j+1) operands stream in four steps ahead of their products, which keeps
+        // the K(j+1) operands stream in two steps ahead of their products, which keeps
         // the kernel within 168 registers (three workgroups per CU)
-        constexpr int kAheadSt = 4;
+        constexpr int kAheadSt = 2;
         auto kread = [&](int st) {
             k0.b[st] = *reinterpret_cast<const bf16x8*>(kst + st * 1024 + 16 * lane);
             k1.b[st] = *reinterpret_cast<const bf16x8*>(kst + (D / 16 + st) * 1024 + 16 * lane);
