@@ -225,7 +225,9 @@ def test_retained_mass_matches_oracle(R, nb):
 # --------------------------------------------------------------------------- block masses
 
 MASS_CASES = [((4, 8, 8), 1, 64, 0.5), ((5, 6, 7), 2, 128, 1.0), ((9, 10, 13), 2, 64, 2.0),
-              ((8, 8, 8), 1, 128, 4.0), ((4, 12, 16), 2, 128, 3.0), ((6, 9, 14), 1, 128, 1.5)]
+              ((8, 8, 8), 1, 128, 4.0), ((4, 12, 16), 2, 128, 3.0), ((6, 9, 14), 1, 128, 1.5),
+              # odd block counts (15 and 9): the last workgroup of each head has one query block
+              ((4, 12, 20), 2, 128, 1.0), ((3, 9, 9), 1, 64, 2.0)]
 
 
 @pytest.mark.parametrize("grid,H,D,amp", MASS_CASES)
