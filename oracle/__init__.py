@@ -24,7 +24,13 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fpsa_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# FPSA_ORACLE_SANITIZE=1 selects a build with AddressSanitizer and UndefinedBehavior-
+# Sanitizer (the process must preload gcc's libasan and libubsan); the arithmetic is
+# the same source
+_SANITIZE = os.environ.get("FPSA_ORACLE_SANITIZE", "") not in ("", "0")
+_LIB_PATH = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=undefined"]
 _lock = threading.Lock()
 _lib = None
 
@@ -40,7 +46,8 @@ def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain -O2, OpenMP over independent rows)."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall",
+        opt = _SAN_FLAGS if _SANITIZE else ["-O2"]
+        subprocess.check_call(["gcc", *opt, "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -96,6 +103,10 @@ def lib():
             L.orc_csr_transpose.restype = ctypes.c_int64
             L.orc_kmeans.restype = None
             L.orc_kmeans.argtypes = [_f32p] + [ctypes.c_int] * 6 + [_i32p, _f64p, _i32p]
+            L.orc_kmeans_assign.restype = None
+            L.orc_kmeans_assign.argtypes = [_f32p] + [ctypes.c_int] * 5 + [_f64p, _i32p, _vp, _vp, _vp]
+            L.orc_kmeans_means.restype = None
+            L.orc_kmeans_means.argtypes = [_f32p] + [ctypes.c_int] * 5 + [_i32p, _f64p, _f64p, _i32p, _vp]
             L.orc_cluster_layout.restype = ctypes.c_int
             L.orc_cluster_layout.argtypes = [_i32p] + [ctypes.c_int] * 5 + [_i32p, _i32p, _i32p]
             L.orc_cluster_mass.restype = None
@@ -364,6 +375,51 @@ def kmeans(x, C, iters):
     count = np.zeros((B, H, C), np.int32)
     lib().orc_kmeans(x, B, N, H, D, int(C), int(iters), assign, cent, count)
     return assign, cent, count
+
+
+def kmeans_start(x, C):
+    """Starting centroids [B, H, C, D] float64: centroid c is token floor(c N / C)."""
+    x = _c(x, np.float32)
+    B, N, H, D = x.shape
+    idx = (np.arange(C, dtype=np.int64) * N) // C
+    return np.ascontiguousarray(np.transpose(x[:, idx, :, :], (0, 2, 1, 3)).astype(np.float64))
+
+
+def kmeans_assign(x, cent, other=None):
+    """Nearest centroid of every token (least squared distance, ties to the lower
+    cluster): assign [B, H, N]. With ``other`` (an assignment [B, H, N] to check),
+    also (excess, tol) [B, H, N]: how much farther other's centroid is than the
+    nearest, and the bound on evaluation error for the two distances; ``other`` is a
+    valid choice where excess <= tol."""
+    x = _c(x, np.float32)
+    cent = _c(cent, np.float64)
+    B, N, H, D = x.shape
+    C = cent.shape[2]
+    assign = np.zeros((B, H, N), np.int32)
+    if other is None:
+        lib().orc_kmeans_assign(x, B, N, H, D, C, cent, assign, None, None, None)
+        return assign
+    oth = _c(other, np.int32)
+    excess = np.zeros((B, H, N), np.float64)
+    tol = np.zeros((B, H, N), np.float64)
+    lib().orc_kmeans_assign(x, B, N, H, D, C, cent, assign, oth.ctypes.data, excess.ctypes.data,
+                            tol.ctypes.data)
+    return assign, excess, tol
+
+
+def kmeans_means(x, assign, cent_in):
+    """(cent [B, H, C, D] float64, count [B, H, C], abs_sum [B, H, C, D]): members'
+    means in token order (empty clusters keep cent_in) and the sums of |x| over the
+    members."""
+    x = _c(x, np.float32)
+    cent_in = _c(cent_in, np.float64)
+    B, N, H, D = x.shape
+    C = cent_in.shape[2]
+    cent = np.zeros_like(cent_in)
+    count = np.zeros((B, H, C), np.int32)
+    abs_sum = np.zeros_like(cent_in)
+    lib().orc_kmeans_means(x, B, N, H, D, C, _c(assign, np.int32), cent_in, cent, count, abs_sum.ctypes.data)
+    return cent, count, abs_sum
 
 
 def blocks_for(N, C):

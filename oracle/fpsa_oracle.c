@@ -282,7 +282,8 @@ void orc_masked_attention(const float* q, const float* k, const float* v,
                 int qb = qblocks ? qblocks[r] : r;
                 int64_t row = ((int64_t)b * H + h) * nb + qb;
                 char* allowed = (char*)calloc((size_t)nb, 1);
-                for (int32_t e = row_ptr[row]; e < row_ptr[row + 1]; ++e) allowed[col_idx[e]] = 1;
+                for (int32_t e = row_ptr[row]; e < row_ptr[row + 1]; ++e)
+                    if ((uint32_t)col_idx[e] < (uint32_t)nb) allowed[col_idx[e]] = 1;   /* others: nothing */
                 double* s = (double*)malloc(sizeof(double) * (size_t)N);
                 int64_t base = (((int64_t)b * H + h) * count + r) * 64;
                 for (int e = 0; e < 64; ++e) {
@@ -756,86 +757,146 @@ int64_t orc_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, int B,
  * cluster is contiguous, which both sharpens the cluster representation used to find
  * the critical tokens and packs those tokens densely for the kernel [Sparse
  * VideoGen2: Accelerate Video Generation with Sparse Attention via Semantic-Aware
- * Permutation, Abstract]. Lloyd's k-means per (b, h) over the N vectors x[b, :, h, :]:
+ * Permutation, Abstract]. Plain Lloyd k-means per (b, h) over the N vectors
+ * x[b, :, h, :], in float64:
  *   start: centroid c = x of token floor(c N / C);
- *   iters times: assign every token to the nearest centroid, then move every
- *   non-empty cluster's centroid to the mean of its members (eight interleaved
- *   partial sums in token order, combined pairwise); an empty cluster keeps its
- *   centroid.
- * "Nearest" compares e(x, c) = |c|^2 - 2 x.c, the squared Euclidean distance less
- * |x|^2, which is the same for every candidate: |c|^2 and x.c are each a chain of
- * fused multiply-adds over the channels in order, starting from zero, in float64;
- * e = |c|^2 - 2 (x.c) (the doubling is exact); the least e wins, ties to the lower
- * cluster. Inputs are finite.
- * assign [B, H, N], cent [B, H, C, D] float64, count [B, H, C]: the last assignment
- * and the centroids and sizes that follow from it.
+ *   iters times: assign every token to the centroid at the least squared Euclidean
+ *   distance sum_d (x_d - c_d)^2 (channels summed in order; ties to the lower
+ *   cluster), then move every non-empty cluster's centroid to the mean of its
+ *   members (summed in token order, divided by the count); an empty cluster keeps
+ *   its centroid.
+ * Inputs are finite.
  */
-static double sqnorm(const double* c, int D) {
+
+/* Squared Euclidean distance, summed over the channels in order. */
+static double sqdist(const float* x, const double* c, int D) {
     double s = 0.0;
-    for (int d = 0; d < D; ++d) s = fma(c[d], c[d], s);
+    for (int d = 0; d < D; ++d) {
+        const double t = (double)x[d] - c[d];
+        s += t * t;
+    }
     return s;
 }
 
-static double dot_xc(const float* x, int D, const double* c) {
-    double s = 0.0;
-    for (int d = 0; d < D; ++d) s = fma((double)x[d], c[d], s);
-    return s;
+/* Unit roundoff of float64 and the bound gamma_n = n u / (1 - n u) on the relative
+   error of an n-term float64 sum or dot product (Higham, Accuracy and Stability of
+   Numerical Algorithms, section 3.1). */
+static double gamma_n(double n) {
+    const double u = 0x1p-53;
+    return n * u / (1.0 - n * u);
 }
 
-void orc_kmeans(const float* x, int B, int N, int H, int D, int C, int iters, int32_t* assign,
-                double* cent, int32_t* count) {
-#pragma omp parallel for collapse(2) schedule(dynamic)
+/*
+ * One assignment step against given centroids cent [B, H, C, D]: assign [B, H, N]
+ * the nearest centroid (least sqdist, ties to the lower cluster).
+ * If `other` is given (another evaluation's assignment [B, H, N]), excess[n] =
+ * dist(other) - dist(best) as computed here, and tol[n] bounds how far an
+ * evaluation of the two distances may be from the exact ones: the sum, over both
+ * candidates, of this function's own error bound gamma_{D+2} * dist and that of the
+ * form |c|^2 - 2 x.c (each product chain within gamma_D of its absolute sum, plus
+ * one rounding of the difference). An assignment `other` is a valid nearest
+ * centroid choice when excess[n] <= tol[n] for every token.
+ */
+void orc_kmeans_assign(const float* x, int B, int N, int H, int D, int C, const double* cent,
+                       int32_t* assign, const int32_t* other, double* excess, double* tol) {
+#pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < H; ++h) {
             const int64_t bh = (int64_t)b * H + h;
-            double* cc = cent + bh * C * D;
-            int32_t* as = assign + bh * N;
+            const double* cc = cent + bh * C * D;
+            for (int n = 0; n < N; ++n) {
+                const float* xn = x + RIX(b, n, h, 0);
+                int best = 0;
+                double bd = sqdist(xn, cc, D);
+                for (int c = 1; c < C; ++c) {
+                    const double dd = sqdist(xn, cc + (int64_t)c * D, D);
+                    if (dd < bd) {
+                        bd = dd;
+                        best = c;
+                    }
+                }
+                assign[bh * N + n] = best;
+                if (other) {
+                    const int o = other[bh * N + n];
+                    const int pick[2] = {best, o};
+                    double t = 0.0;
+                    for (int i = 0; i < 2; ++i) {
+                        const double* ci = cc + (int64_t)pick[i] * D;
+                        double c2 = 0.0, xc = 0.0;
+                        for (int d = 0; d < D; ++d) {
+                            c2 += ci[d] * ci[d];
+                            xc += fabs((double)xn[d] * ci[d]);
+                        }
+                        const double di = sqdist(xn, ci, D);
+                        t += gamma_n(D + 2) * di + gamma_n(D + 1) * (c2 + 2.0 * xc) + 0x1p-52 * (c2 + 2.0 * xc);
+                    }
+                    excess[bh * N + n] = sqdist(xn, cc + (int64_t)o * D, D) - bd;
+                    tol[bh * N + n] = t;
+                }
+            }
+        }
+}
+
+/*
+ * One update step: for every cluster of every (b, h), count[c] = its members under
+ * assign [B, H, N], and cent_out[c] = the mean of their vectors (summed in token
+ * order, then divided by the count), or cent_in[c] when the cluster is empty.
+ * abs_sum [B, H, C, D] (optional) receives sum |x_d| over the members, from which a
+ * caller bounds the rounding of any order of the member sum (gamma_{count-1} of it).
+ */
+void orc_kmeans_means(const float* x, int B, int N, int H, int D, int C, const int32_t* assign,
+                      const double* cent_in, double* cent_out, int32_t* count, double* abs_sum) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const int64_t bh = (int64_t)b * H + h;
+            const int32_t* as = assign + bh * N;
+            double* co = cent_out + bh * C * D;
+            double* sum = (double*)calloc((size_t)C * D, sizeof(double));
+            double* sabs = (double*)calloc((size_t)C * D, sizeof(double));
             int32_t* cn = count + bh * C;
+            for (int c = 0; c < C; ++c) cn[c] = 0;
+            for (int n = 0; n < N; ++n) {
+                const int c = as[n];
+                cn[c]++;
+                for (int d = 0; d < D; ++d) {
+                    sum[(int64_t)c * D + d] += (double)x[RIX(b, n, h, d)];
+                    sabs[(int64_t)c * D + d] += fabs((double)x[RIX(b, n, h, d)]);
+                }
+            }
+            for (int c = 0; c < C; ++c)
+                for (int d = 0; d < D; ++d) {
+                    const int64_t i = (int64_t)c * D + d;
+                    co[i] = cn[c] ? sum[i] / (double)cn[c] : cent_in[bh * C * D + i];
+                    if (abs_sum) abs_sum[bh * C * D + i] = sabs[i];
+                }
+            free(sum);
+            free(sabs);
+        }
+}
+
+/*
+ * The whole clustering: assign [B, H, N], cent [B, H, C, D] float64 and count
+ * [B, H, C] after `iters` Lloyd steps from the strided start (the last assignment
+ * and the centroids and sizes that follow from it).
+ */
+void orc_kmeans(const float* x, int B, int N, int H, int D, int C, int iters, int32_t* assign,
+                double* cent, int32_t* count) {
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
             for (int c = 0; c < C; ++c) {
                 const int64_t t = (int64_t)c * N / C;
-                for (int d = 0; d < D; ++d) cc[(int64_t)c * D + d] = (double)x[RIX(b, t, h, d)];
+                for (int d = 0; d < D; ++d)
+                    cent[(((int64_t)b * H + h) * C + c) * D + d] = (double)x[RIX(b, t, h, d)];
             }
-            double* cnorm = (double*)malloc((size_t)C * sizeof(double));
-            for (int it = 0; it < iters; ++it) {
-                for (int c = 0; c < C; ++c) cnorm[c] = sqnorm(cc + (int64_t)c * D, D);
-                for (int n = 0; n < N; ++n) {
-                    const float* xn = x + RIX(b, n, h, 0);
-                    int best = 0;
-                    double bd = cnorm[0] - 2.0 * dot_xc(xn, D, cc);
-                    for (int c = 1; c < C; ++c) {
-                        const double e = cnorm[c] - 2.0 * dot_xc(xn, D, cc + (int64_t)c * D);
-                        if (e < bd) {
-                            bd = e;
-                            best = c;
-                        }
-                    }
-                    as[n] = best;
-                }
-                /* member sums: the r-th member of a cluster (token order) is added to
-                   partial sum r % 8, each partial in member order; the partials then
-                   combine as ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7)) */
-                double* part = (double*)calloc((size_t)C * 8 * D, sizeof(double));
-                for (int c = 0; c < C; ++c) cn[c] = 0;
-                for (int n = 0; n < N; ++n) {
-                    const int c = as[n];
-                    double* pc = part + ((int64_t)c * 8 + cn[c] % 8) * D;
-                    cn[c]++;
-                    for (int d = 0; d < D; ++d) pc[d] = pc[d] + (double)x[RIX(b, n, h, d)];
-                }
-                for (int c = 0; c < C; ++c) {
-                    if (cn[c] == 0) continue;
-                    const double* pc = part + (int64_t)c * 8 * D;
-                    for (int d = 0; d < D; ++d) {
-                        const double s01 = pc[d] + pc[D + d], s23 = pc[2 * D + d] + pc[3 * D + d];
-                        const double s45 = pc[4 * D + d] + pc[5 * D + d], s67 = pc[6 * D + d] + pc[7 * D + d];
-                        const double sum = (s01 + s23) + (s45 + s67);
-                        cc[(int64_t)c * D + d] = sum / (double)cn[c];
-                    }
-                }
-                free(part);
-            }
-            free(cnorm);
-        }
+    const size_t ncent = (size_t)B * H * C * D;
+    double* prev = (double*)malloc(ncent * sizeof(double));
+    for (int it = 0; it < iters; ++it) {
+        memcpy(prev, cent, ncent * sizeof(double));
+        orc_kmeans_assign(x, B, N, H, D, C, prev, assign, NULL, NULL, NULL);
+        orc_kmeans_means(x, B, N, H, D, C, assign, prev, cent, count, NULL);
+    }
+    free(prev);
 }
 
 /*

@@ -274,6 +274,23 @@ def test_single_kept_block_is_attention_within_that_block():
     assert np.all(out[0, 0, 2] == 0)                   # empty row: zero output
 
 
+def test_out_of_range_blocks_contribute_nothing():
+    # the ABI defines CSR entries outside [0, nb) as contributing nothing: with such
+    # entries mixed in (negative, nb, far past nb) each row equals library attention
+    # over the keys of its in-range blocks, and a row of only bad entries is zero
+    grid, tile = (4, 8, 8), (4, 4, 4)
+    q, k, v = _rand_qkv(1, 256, 1, 16, 29)
+    blk, _ = O.token_blocks(grid, tile)
+    rp = np.array([0, 4, 6, 8, 9], np.int32)
+    ci = np.array([2, -1, 3, 4, 0, 1 << 30, -7, 99, 3], np.int32)
+    out, tok = O.masked_attention(q, k, v, grid, tile, 0.4, rp, ci)
+    for qb, kbs in [(0, [2, 3]), (1, [0]), (3, [3])]:
+        qs, ks = np.where(blk == qb)[0], np.where(np.isin(blk, kbs))[0]
+        ref = _torch_sdpa(q[:, qs], k[:, ks], v[:, ks], 0.4)
+        assert np.abs(out[0, 0, qb] - ref[0, :, 0]).max() < 1e-12
+    assert np.all(out[0, 0, 2] == 0)
+
+
 def test_masked_attention_constant_values_give_constant_output():
     grid, tile = (5, 6, 7), (4, 4, 4)
     q, k, v = _rand_qkv(1, 210, 1, 8, 10)
@@ -668,14 +685,17 @@ def test_kmeans_assignment_is_the_exact_nearest_centroid():
     # every assignment step against exact rational arithmetic: the squared distance
     # sum_d (x_d - c_d)^2 to the centroids the step starts from (the starting tokens,
     # or the centroids the oracle returns after one step fewer), least value, ties to
-    # the lower cluster; the oracle compares |c|^2 - 2 x.c in float64 instead
+    # the lower cluster; the oracle sums the float64 squares of the differences
+    _exact_nearest_steps(_rand_qkv(1, 40, 2, 8, 11)[0], 5, 4)
+    _exact_nearest_steps(_rand_qkv(1, 150, 1, 16, 12)[0] * np.float32(0.25), 9, 3)
+
+
+def _exact_nearest_steps(x, C, steps):
     from fractions import Fraction as Fr
-    x = _rand_qkv(1, 40, 2, 8, 11)[0]
-    C = 5
     N = x.shape[1]
-    for iters in range(1, 5):
+    for iters in range(1, steps + 1):
         asg, _, _ = O.kmeans(x, C, iters)
-        for h in range(2):
+        for h in range(x.shape[2]):
             if iters == 1:
                 cent = [x[0, c * N // C, h].astype(np.float64) for c in range(C)]
             else:
@@ -684,6 +704,65 @@ def test_kmeans_assignment_is_the_exact_nearest_centroid():
                 xn = [Fr(float(v)) for v in x[0, n, h]]
                 dist = [sum((a - Fr(float(cv))) ** 2 for a, cv in zip(xn, cent[c])) for c in range(C)]
                 assert asg[0, h, n] == min(range(C), key=lambda c: (dist[c], c))
+
+
+def test_kmeans_assign_step_excess_and_tolerance():
+    # the checking form of one assignment step: against exact rational distances, the
+    # excess of another choice is its distance less the nearest one's (up to float64
+    # rounding of the two sums), zero when the choices agree, and the tolerance is a
+    # small positive bound that a clearly farther centroid exceeds
+    from fractions import Fraction as Fr
+    x = _rand_qkv(1, 60, 2, 8, 21)[0]
+    cent = O.kmeans(x, 6, 2)[1]
+    a = O.kmeans_assign(x, cent)
+    assert np.array_equal(a, O.kmeans(x, 6, 3)[0])           # the step the clustering takes
+    _, ex0, tol0 = O.kmeans_assign(x, cent, other=a)
+    assert np.all(ex0 == 0) and np.all(tol0 > 0) and np.all(tol0 < 1e-11)
+    far = (a + 3) % 6
+    _, ex, tol = O.kmeans_assign(x, cent, other=far)
+    for h in range(2):
+        for n in range(0, 60, 7):
+            xn = [Fr(float(v)) for v in x[0, n, h]]
+            d = [sum((u - Fr(float(cv))) ** 2 for u, cv in zip(xn, cent[0, h, c])) for c in range(6)]
+            want = float(d[far[0, h, n]] - d[a[0, h, n]])
+            assert abs(ex[0, h, n] - want) <= 1e-13 * (1 + abs(want))
+    assert np.all(ex > tol)
+    # an exact tie: token 2 halfway between the two starting centroids; either choice is valid
+    xt = np.array([[[2.0, 0.0], [0.0, 2.0], [1.0, 1.0]]], np.float32)[:, :, None, :]
+    c0 = O.kmeans_start(xt, 2)
+    assert O.kmeans_assign(xt, c0)[0, 0].tolist() == [0, 1, 0]
+    _, ext, tolt = O.kmeans_assign(xt, c0, other=np.array([[[0, 1, 1]]], np.int32))
+    assert ext[0, 0, 2] == 0 and np.all(ext <= tolt)
+
+
+def test_kmeans_means_against_exact_means():
+    # members' means against exact rational means (one rounding of the exact value
+    # apart at most a few ulps of float64 summation), the absolute sums exactly, and an
+    # empty cluster keeping its given centroid
+    from fractions import Fraction as Fr
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((1, 90, 1, 5)).astype(np.float32)
+    a = rng.integers(0, 4, size=(1, 1, 90)).astype(np.int32)       # cluster 4 stays empty
+    cin = rng.standard_normal((1, 1, 5, 5))
+    cent, cnt, sabs = O.kmeans_means(x, a, cin)
+    assert cnt[0, 0].tolist() == [int((a == c).sum()) for c in range(5)]
+    assert np.array_equal(cent[0, 0, 4], cin[0, 0, 4])
+    for c in range(4):
+        mem = np.where(a[0, 0] == c)[0]
+        for d in range(5):
+            ex = sum(Fr(float(x[0, n, 0, d])) for n in mem) / len(mem)
+            assert abs(cent[0, 0, c, d] - float(ex)) <= 8 * len(mem) * 2.0 ** -53 * float(sabs[0, 0, c, d]) / len(mem)
+            assert sabs[0, 0, c, d] == float(sum(abs(Fr(float(x[0, n, 0, d]))) for n in mem))
+
+
+def test_kmeans_is_start_then_alternating_steps():
+    x = _rand_qkv(1, 80, 2, 8, 23)[0]
+    cent = O.kmeans_start(x, 7)
+    for it in range(1, 5):
+        a = O.kmeans_assign(x, cent)
+        cent, cnt, _ = O.kmeans_means(x, a, cent)
+        ra, rc, rn = O.kmeans(x, 7, it)
+        assert np.array_equal(a, ra) and np.array_equal(cent, rc) and np.array_equal(cnt, rn)
 
 
 def test_kmeans_equidistant_token_goes_to_the_lower_cluster():
