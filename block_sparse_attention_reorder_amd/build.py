@@ -35,29 +35,40 @@ NO_NAN_SOURCES = {"attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
                   "cluster.hip": ["-ffp-contract=off"]}
 
 
-def _compile(src: str, build_dir: str) -> str:
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the C ABI's host layer
+# (argument validation, workspace carving, launch set-up); device code is unchanged.
+# Each sanitizer flag applies to the host compilation only.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, build_dir: str, extra=()) -> str:
     obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, *NO_NAN_SOURCES.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *NO_NAN_SOURCES.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    build_dir = os.path.join(HERE, "_build")
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    """Build libfpsa.so; with sanitize=True build a host-sanitized copy instead
+    (_build/san/libfpsa.so, loaded with the compiler's ASan runtime preloaded)."""
+    build_dir = os.path.join(HERE, "_build", "san" if sanitize else "")
     os.makedirs(build_dir, exist_ok=True)
+    extra = SANITIZE_FLAGS if sanitize else []
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, build_dir, extra), SOURCES))
+    out = os.path.join(build_dir, "libfpsa.so") if sanitize else LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -303,7 +303,17 @@ void launch_block_mass(const void* q, const void* k, int B, int H, int D, const 
     const float sl2 = scale * kLog2e;
     const __bf16* qb = static_cast<const __bf16*>(q);
     const __bf16* kb = static_cast<const __bf16*>(k);
-    const long chunk = (long)(ws_bytes / mass_workspace_bytes_min(g.nb));   // >= 1, checked by the caller
+    long chunk = (long)(ws_bytes / mass_workspace_bytes_min(g.nb));   // >= 1, checked by the caller
+    if (chunk < P) {
+        // a workspace smaller than the whole grid: launch whole waves of workgroups
+        // (three per compute unit), so that no launch but the last ends on a partial wave
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
+            const long wave = 3L * cus;
+            if (chunk >= wave) chunk -= chunk % wave;
+        }
+    }
     for (long p0 = 0; p0 < P; p0 += chunk) {
         const long n = P - p0 < chunk ? P - p0 : chunk;
         if (D == 128)

@@ -13,7 +13,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfpsa.so")
+# FPSA_LIB names another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("FPSA_LIB") or os.path.join(HERE, "libfpsa.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_HIP = 0, 1, 2, 3, 4
 F32, BF16, FP8_E4M3 = 0, 1, 2

@@ -96,12 +96,18 @@ class BlockSparseAttention:
         return out
 
     # ------------------------------------------------------------------ selection
-    def mass_workspace(self, max_bytes=None):
+    # Default bound on the mass pass's scratch: the per-query-block log-sum-exps of the
+    # query blocks in flight (nb * 64 * 4 bytes each). The whole grid's would be 28.7 GB
+    # at the HunyuanVideo shape; 2 GiB holds two waves of workgroups there, and the pass
+    # runs in several launches of whole waves.
+    MASS_WORKSPACE_CAP = 2 << 30
+
+    def mass_workspace(self, max_bytes=MASS_WORKSPACE_CAP):
         """Scratch for the mass pass: enough for one launch, or at most max_bytes
-        (then the pass runs in several launches)."""
+        (then the pass runs in several launches); max_bytes=None takes the whole grid."""
         n = fpsa.mass_workspace_bytes(self.B, self.H, self.grid, self.tile)
         if max_bytes is not None:
-            n = min(n, int(max_bytes))
+            n = max(min(n, int(max_bytes)), 2 * self.nb * 64 * 4)
         return torch.empty(n, dtype=torch.uint8, device=self.device)
 
     def block_mass(self, qt, kt, mass=None, lse=None, want_lse=False, workspace=None, stream=None):

@@ -239,7 +239,12 @@ int32_t fpsa_retained_mass(const float* mass, int64_t R, int32_t nb, const int32
                            const int32_t* col_idx, float* retained, void* stream);
 
 /*
- * Block-sparse attention forward with an online softmax over the kept blocks.
+ * Block-sparse attention forward with an online softmax over the kept blocks: the
+ * FlashAttention-style kernel that visits only the frozen key/value blocks of each
+ * query block ([LoSA ..., Abstract]: the kept block set of each head and query
+ * block is reused for the remaining steps; [FPSAttention ..., Abstract]: the kernel
+ * builds on FlashAttention, and one 3D tile is both the sparsity block and the FP8
+ * quantization group, so a tile's scale factors out of its scores).
  *
  * q, k: tiled QK layout, BF16 when qk_dtype = FPSA_BF16, or FP8_E4M3 bytes with
  *   q_scale / k_scale [B, H, nb] float32, positive (as produced by

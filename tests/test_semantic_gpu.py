@@ -24,24 +24,73 @@ def _inputs(grid, H, D, seed, amp=1.5):
     return synth.make_qkv(grid, 1, H, D, amp, 1.0, seed, bf16=True)
 
 
+U64 = 2.0 ** -53
+
+
+def _gamma(n):
+    n = np.asarray(n, np.float64)
+    return n * U64 / (1.0 - n * U64)
+
+
+def _gpu_kmeans(xd, N, H, D, C, iters):
+    i32 = dict(dtype=torch.int32, device="cuda")
+    a, cnt = torch.empty((1, H, N), **i32), torch.empty((1, H, C), **i32)
+    cent = torch.empty((1, H, C, D), dtype=torch.float64, device="cuda")
+    mo, mem = torch.empty(H * C + 1, **i32), torch.empty(H * N, **i32)
+    ws = torch.empty(fpsa.kmeans_workspace_bytes(1, H, N, C), dtype=torch.uint8, device="cuda")
+    fpsa.kmeans(xd, 1, N, H, D, C, iters, a, cent, cnt, mo, mem, ws)
+    return (a.cpu().numpy(), cent.cpu().numpy(), cnt.cpu().numpy(), mo.cpu().numpy(), mem.cpu().numpy())
+
+
+def _check_kmeans(x, xd, C, iters):
+    """The GPU's k-means against plain Lloyd in the oracle.
+
+    Step by step (the GPU run for s steps against the GPU run for s - 1): every
+    token's cluster is a nearest centroid of the previous centroids, exactly, except
+    where two candidates lie within the certified float64 evaluation bound of each
+    other (excess <= tol, either choice valid); counts and member lists are exact for
+    that assignment; each centroid is the mean of its members within the rounding
+    bound of any summation order, 2 gamma_n sum|x| / n plus a few ulps (the GPU sums
+    members in eight interleaved partials, the oracle in token order).
+    End to end: the assignment after the last step equals the oracle's own run."""
+    N, H, D = x.shape[1], x.shape[2], x.shape[3]
+    prev = O.kmeans_start(x, C)
+    ulps = 0
+    for s in range(1, iters + 1):
+        a, cent, cnt, mo, mem = _gpu_kmeans(xd, N, H, D, C, s)
+        _, excess, tol = O.kmeans_assign(x, prev, other=a)
+        assert np.all(excess <= tol), (s, float((excess - tol).max()))
+        ulps += int(np.sum(excess > 0))
+        want, wcnt, abs_sum = O.kmeans_means(x, a, prev)
+        assert np.array_equal(cnt, wcnt)
+        n = np.maximum(wcnt, 1)[..., None].astype(np.float64)
+        bound = 2 * _gamma(n) * abs_sum / n + 4 * U64 * np.abs(want)
+        assert np.all(np.abs(cent - want) <= bound), (s, float((np.abs(cent - want) - bound).max()))
+        for h in range(H):
+            for k in range(C):
+                r = h * C + k
+                assert np.array_equal(mem[mo[r]:mo[r + 1]], np.where(a[0, h] == k)[0])
+        prev = cent
+    ra, rc, rn = O.kmeans(x, C, iters)
+    assert np.array_equal(a, ra), int(np.sum(a != ra))
+    assert np.array_equal(cnt, rn)
+    n = np.maximum(rn, 1)[..., None].astype(np.float64)
+    print(f"k-means C={C} iters={iters}: {ulps} near-tie choices; centroids max |gpu - oracle| "
+          f"{float(np.abs(cent - rc).max()):.2e}")
+    return a, cent, cnt
+
+
 @pytest.mark.parametrize("case", CASES)
 @pytest.mark.parametrize("f32", [False, True])
-def test_kmeans_and_layout_bitexact(case, f32):
+def test_kmeans_and_layout(case, f32):
     grid, H, D, Cq, _, iters = case
     q, _, _ = _inputs(grid, H, D, 61)
     N = q.shape[1]
     ssa = SemanticSparseAttention(N, 1, H, D, Cq, Cq, iters=iters)
-    c = ssa.cluster(dev(q, torch.float32 if f32 else torch.bfloat16), Cq)
-    a, cent, cnt = O.kmeans(q, Cq, iters)
+    qd = dev(q, torch.float32 if f32 else torch.bfloat16)
+    a, _, _ = _check_kmeans(q, qd, Cq, iters)
+    c = ssa.cluster(qd, Cq)
     assert np.array_equal(c.assign.cpu().numpy(), a)
-    assert np.array_equal(c.counts.cpu().numpy(), cnt)
-    assert np.array_equal(c.centroids.cpu().numpy(), cent)          # bit for bit in float64
-    mo = c.member_off.cpu().numpy()
-    mem = c.members.cpu().numpy()
-    for h in range(H):
-        for k in range(Cq):
-            r = h * Cq + k
-            assert np.array_equal(mem[mo[r]:mo[r + 1]], np.where(a[0, h] == k)[0])
     st, off, bc = O.cluster_layout(a, Cq, ssa.NB)
     assert np.array_equal(c.slot_token.cpu().numpy(), st)
     assert np.array_equal(c.blk_off.cpu().numpy(), off)
@@ -58,16 +107,7 @@ def test_kmeans_extreme_cluster_counts(N, H, D, C, iters):
     x = (rng.standard_normal((1, N, H, D)) * 2.0).astype(np.float32)
     xb = dev(x, torch.bfloat16)
     xr = xb.float().cpu().numpy()                   # the bf16 values, exactly
-    i32 = dict(dtype=torch.int32, device="cuda")
-    a, cnt = torch.empty((1, H, N), **i32), torch.empty((1, H, C), **i32)
-    cent = torch.empty((1, H, C, D), dtype=torch.float64, device="cuda")
-    mo, mem = torch.empty(H * C + 1, **i32), torch.empty(H * N, **i32)
-    ws = torch.empty(fpsa.kmeans_workspace_bytes(1, H, N, C), dtype=torch.uint8, device="cuda")
-    fpsa.kmeans(xb, 1, N, H, D, C, iters, a, cent, cnt, mo, mem, ws)
-    ra, rc, rn = O.kmeans(xr, C, iters)
-    assert np.array_equal(a.cpu().numpy(), ra)
-    assert np.array_equal(cnt.cpu().numpy(), rn)
-    assert np.array_equal(cent.cpu().numpy(), rc)
+    _check_kmeans(xr, xb, C, iters)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -172,19 +212,19 @@ def test_semantic_attention_end_to_end(case):
     crp_g, cci_g = csr_to_numpy(res["ccsr"].row_ptr, res["ccsr"].col_idx)
     same = _rows_equal(crp_g, cci_g, crp, cci)
     _certify(same, est.reshape(-1, Ck), ssa)
-    ref = O.cluster_attention(q, k, v, qa, ka, Cq, Ck, ssa.scale, crp, cci)
-    errs = []
-    for h in range(H):
-        ok = same[h * Cq + qa[0, h]]                    # queries whose cluster row matched
-        errs.append(np.abs(o[0, ok, h].astype(np.float64) - ref[0, ok, h]).ravel())
-    e = np.concatenate(errs)
+    # every query against attention under the GPU's own clusters and cluster selection
+    # (the selection the forward consumed; its parity with the oracle's is checked above)
+    ref = O.cluster_attention(q, k, v, res["qc"].assign.cpu().numpy(), res["kc"].assign.cpu().numpy(), Cq, Ck,
+                              ssa.scale, crp_g, cci_g)
+    e = np.abs(o.astype(np.float64) - ref).ravel()
     assert e.max() <= BF16_MAX_ABS and e.mean() <= BF16_MEAN_ABS, (e.max(), e.mean())
 
 
 def test_semantic_full_480p_sampled():
-    """The 480p shape with 128 query and 128 key clusters: every cluster of heads 0 and
-    11 bit-exact against the oracle's k-means, their cluster masses within an ulp, and
-    outputs of sampled query tokens against attention under the oracle's selection."""
+    """The 480p shape with 128 query and 128 key clusters: the assignments of heads 0
+    and 11 equal the oracle's k-means, their cluster masses (from the GPU's and the
+    oracle's centroids) within an ulp, and outputs of sampled query tokens against
+    attention under the oracle's selection."""
     w = WORKLOADS["wan480p"]
     q, k, v = synth.make_qkv(w.grid, w.B, w.H, w.D, w.amp, w.sigma, w.seed, bf16=True)
     N = q.shape[1]
@@ -206,7 +246,9 @@ def test_semantic_full_480p_sampled():
         same = _rows_equal(sub_rp, sub_ci, crp, cci)
         _certify(same, est.reshape(-1, ssa.Ck), ssa)
         toks = np.sort(rng.choice(N, size=48, replace=False)).astype(np.int32)
-        toks = toks[same[qa[0, 0, toks]]]
-        ref = O.cluster_attention(qh, kh, vh, qa, ka, ssa.Cq, ssa.Ck, ssa.scale, crp, cci, tokens=toks)
+        # outputs against attention under the GPU's own clusters and selection of this head
+        qa_g = res["qc"].assign.cpu().numpy()[:, h:h + 1]
+        ka_g = res["kc"].assign.cpu().numpy()[:, h:h + 1]
+        ref = O.cluster_attention(qh, kh, vh, qa_g, ka_g, ssa.Cq, ssa.Ck, ssa.scale, sub_rp, sub_ci, tokens=toks)
         e = np.abs(o[0, toks, h].astype(np.float64) - ref[0, 0])
         assert e.max() <= BF16_MAX_ABS and e.mean() <= BF16_MEAN_ABS, (h, e.max(), e.mean())
