@@ -162,6 +162,24 @@ int32_t fpsa_select_blocks(const float* mass, int64_t R, int32_t nb, uint32_t th
     return hip_status();
 }
 
+int32_t fpsa_select_blocks_noalloc(const float* mass, int64_t R, int32_t nb, uint32_t thr_num,
+                                   uint32_t thr_den, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, void* stream) {
+    if (mass == nullptr || row_ptr == nullptr || col_idx == nullptr) return FPSA_ERR_INVALID_ARG;
+    if (R <= 0 || R > (1L << 24) || nb <= 0) return FPSA_ERR_INVALID_ARG;
+    if (nb > FPSA_MAX_SELECT_BLOCKS) return FPSA_ERR_UNSUPPORTED;
+    if (thr_den < 1 || thr_den > 1000 || thr_num > thr_den) return FPSA_ERR_INVALID_ARG;
+    if ((int64_t)R * nb > 0x7FFFFFFFLL) return FPSA_ERR_UNSUPPORTED;
+    if (col_capacity < (int64_t)R * nb) return FPSA_ERR_CAPACITY;
+    if (R > FPSA_SELECT_NOALLOC_MAX_ROWS) return FPSA_ERR_CAPACITY;   // beyond the static scratch
+    static_assert(FPSA_SELECT_NOALLOC_MAX_ROWS == fpsa::kSelectNoAllocMaxRows, "one limit");
+    void* ws = nullptr;
+    if (fpsa::select_scratch(&ws) != hipSuccess) return FPSA_ERR_HIP;
+    fpsa::launch_select(mass, (long)R, nb, thr_num, thr_den, row_ptr, col_idx, ws,
+                        static_cast<hipStream_t>(stream));
+    return hip_status();
+}
+
 int32_t fpsa_structured_mask(const fpsa_grid* g, int32_t copies, int32_t* row_ptr,
                              int32_t* col_idx, int64_t col_capacity, void* workspace,
                              size_t workspace_bytes, void* stream) {

@@ -36,6 +36,11 @@ void launch_block_mass(const void* q, const void* k, int B, int H, int D, const 
 // Workspace layout for selection: per row a kept count (int32) and the cut key
 // (uint64) with the number of tied keys kept (int32).
 size_t select_workspace_bytes(long R);
+// Rows the no-allocation selection entry point accepts; its file-scope device scratch
+// holds select_workspace_bytes(kSelectNoAllocMaxRows) bytes on every GPU it runs on.
+constexpr long kSelectNoAllocMaxRows = 1L << 20;
+// The address of that scratch on the current device (looked up once per device).
+hipError_t select_scratch(void** out);
 void launch_select(const float* mass, long R, int nb, uint32_t num, uint32_t den, int32_t* row_ptr,
                    int32_t* col_idx, void* ws, hipStream_t st);
 void launch_structured(const Geom& g, int copies, int32_t* row_ptr, int32_t* col_idx, void* ws,

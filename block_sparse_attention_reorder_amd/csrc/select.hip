@@ -13,6 +13,8 @@
 // threshold; it is found bit by bit (41 wave-wide sums) instead of by sorting,
 // which gives the same set as sort + prefix sum + cut. One wavefront per row; the
 // ascending output order falls out of ballot prefix counts over index order.
+#include <mutex>
+
 #include "fpsa_device.h"
 #include "fpsa_internal.h"
 
@@ -168,6 +170,37 @@ size_t select_workspace_bytes(long R) {
     // count int32 [R] | ties int32 [R] | cut uint64 [R], each 256-byte aligned
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     return up((size_t)R * 4) * 2 + up((size_t)R * 8);
+}
+
+// Scratch of the no-allocation entry point (fpsa_select_blocks_noalloc): per row a
+// kept count, a tie count and a cut key, 16 bytes, for up to kSelectNoAllocMaxRows
+// rows (16 MiB). One copy lives on every GPU the library runs on, until the process
+// ends. In host code `scratch` only names the symbol: kernels receive the device
+// address that hipGetSymbolAddress returns for the current device, kept per device.
+constexpr size_t kSelectScratchBytes = (size_t)kSelectNoAllocMaxRows * 16;
+static __device__ __align__(256) uint8_t scratch[kSelectScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t select_scratch(void** out) {
+    static_assert(kSelectScratchBytes >= 16 * (size_t)kSelectNoAllocMaxRows, "16 bytes per row");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 static void carve(void* ws, long R, int32_t** count, int32_t** ties, uint64_t** cut) {

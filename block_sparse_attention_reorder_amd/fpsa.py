@@ -30,8 +30,9 @@ EXPORTED = [
     "fpsa_bwd_workspace_bytes", "fpsa_kmeans", "fpsa_kmeans_workspace_bytes", "fpsa_cluster_layout",
     "fpsa_gather_tiles",
     "fpsa_scatter_tiles", "fpsa_cluster_mass", "fpsa_cluster_blocks", "fpsa_sparse_attn_fwd_varlen",
-    "fpsa_dequantize_tiles",
+    "fpsa_dequantize_tiles", "fpsa_select_blocks_noalloc",
 ]
+SELECT_NOALLOC_MAX_ROWS = 1 << 20
 
 
 class FpsaError(RuntimeError):
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.fpsa_mass_workspace_bytes.argtypes = [i32, i32, gp]
         L.fpsa_select_blocks.restype = i32
         L.fpsa_select_blocks.argtypes = [vp, i64, i32, u32, u32, vp, vp, i64, vp, ctypes.c_size_t, vp]
+        L.fpsa_select_blocks_noalloc.restype = i32
+        L.fpsa_select_blocks_noalloc.argtypes = [vp, i64, i32, u32, u32, vp, vp, i64, vp]
         L.fpsa_structured_mask.restype = i32
         L.fpsa_structured_mask.argtypes = [gp, i32, vp, vp, i64, vp, ctypes.c_size_t, vp]
         L.fpsa_sparse_attn_fwd.restype = i32
@@ -212,6 +215,15 @@ def select_blocks(mass, R, nb, thr_num, thr_den, row_ptr, col_idx, workspace, st
                                  _ptr(col_idx), int(col_idx.numel()), _ptr(workspace),
                                  int(workspace.numel() * workspace.element_size()), _stream(stream))
     _check(s, "fpsa_select_blocks")
+
+
+def select_blocks_noalloc(mass, R, nb, thr_num, thr_den, row_ptr, col_idx, stream=None) -> None:
+    """fpsa_select_blocks on the library's static device scratch (no workspace)."""
+    if mass.dtype != torch.float32 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("mass float32, row_ptr/col_idx int32")
+    s = lib().fpsa_select_blocks_noalloc(_ptr(mass), int(R), int(nb), int(thr_num), int(thr_den), _ptr(row_ptr),
+                                         _ptr(col_idx), int(col_idx.numel()), _stream(stream))
+    _check(s, "fpsa_select_blocks_noalloc")
 
 
 def structured_mask(grid, tile, copies, row_ptr, col_idx, workspace, stream=None) -> None:

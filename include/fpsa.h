@@ -188,6 +188,24 @@ int32_t fpsa_select_blocks(const float* mass, int64_t R, int32_t nb, uint32_t th
                            void* stream);
 
 /*
+ * fpsa_select_blocks without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same arguments, rule, output and errors as fpsa_select_blocks;
+ * the scratch is a static device array of the library (16 bytes per row, 16 MiB,
+ * one copy per GPU, held until the process ends; nothing is allocated). R above
+ * FPSA_SELECT_NOALLOC_MAX_ROWS returns FPSA_ERR_CAPACITY. The scratch of the current
+ * device is used, so `stream` must belong to the current device. Every word of the
+ * scratch that a call reads is first written by that call, so nothing needs
+ * clearing between calls; but all calls on one GPU share the one scratch, so calls
+ * that overlap in time on one GPU (concurrent streams, or threads) race and must be
+ * serialised by the caller.
+ */
+#define FPSA_SELECT_NOALLOC_MAX_ROWS (1L << 20)
+int32_t fpsa_select_blocks_noalloc(const float* mass, int64_t R, int32_t nb, uint32_t thr_num,
+                                   uint32_t thr_den, int32_t* row_ptr, int32_t* col_idx,
+                                   int64_t col_capacity, void* stream);
+
+/*
  * Structured group-shared mask ([Grouping First, Attending Smartly ..., Abstract]).
  *
  * Only for 2D grids (t = 1, tile_t = 1): the blocks form an nh x nw grid of token

@@ -142,6 +142,19 @@ def test_select_blocks_validation(L):
     assert f(FAKE, 10, 8, 99, 100, None, FAKE, 80, FAKE, ws, None) == fpsa.ERR_INVALID_ARG
 
 
+def test_select_blocks_noalloc_validation(L):
+    f = L.fpsa_select_blocks_noalloc
+    assert f(None, 10, 8, 99, 100, FAKE, FAKE, 80, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 0, 8, 99, 100, FAKE, FAKE, 80, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 8, 101, 100, FAKE, FAKE, 80, None) == fpsa.ERR_INVALID_ARG
+    assert f(FAKE, 10, 8, 99, 100, FAKE, FAKE, 79, None) == fpsa.ERR_CAPACITY
+    assert f(FAKE, 10, 4097, 99, 100, FAKE, FAKE, 10 * 4097, None) == fpsa.ERR_UNSUPPORTED
+    assert f(FAKE, 10, 8, 99, 100, FAKE, None, 80, None) == fpsa.ERR_INVALID_ARG
+    # rows beyond the static scratch: a clear capacity error, nothing launched
+    R = fpsa.SELECT_NOALLOC_MAX_ROWS + 1
+    assert f(FAKE, R, 8, 99, 100, FAKE, FAKE, R * 8, None) == fpsa.ERR_CAPACITY
+
+
 def test_structured_mask_validation(L):
     f = L.fpsa_structured_mask
     g2 = grid(1, 64, 64, 1, 8, 8)
