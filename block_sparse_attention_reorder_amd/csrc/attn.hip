@@ -4,20 +4,34 @@
 // indices of the retained-mass selection [LoSA: Near-Lossless Sparse Attention for
 // Training-Free Video Diffusion Acceleration, Abstract].
 //
-// gfx950 mapping. A workgroup of four waves owns one query block (64 rows) of one
-// (batch, head) and walks the block's CSR list in order. The K and V tiles of each
-// kept block are copied once per workgroup into LDS with direct global-to-LDS loads
-// (buffer_load_dwordx4 ... lds, each wave moving a quarter of each tile in contiguous
-// kilobytes) into two-slot K and V rings, K two blocks and V one block ahead of
-// use; one barrier per block. The e4m3 variant issues its copies from inline asm and
-// reads the second half of its V operands later in the block, which fits it in 168
-// registers and three workgroups per CU (its K ring is half the size). Wave w takes query rows 32*(w & 1) .. +31 and key
-// rows 32*(w >> 1) .. +31 of every block (the layout conventions are described in
+// Two gfx950 kernels.
+//
+// k_sparse_attn_pair (bf16, D = 128, blocks from the token grid, nb <= 4096; the main
+// path): a workgroup of four waves owns two neighbouring query blocks and walks the
+// union of their kept lists in ascending block order, so every K/V tile copied into
+// LDS serves 128 queries (half the copy bytes and barriers per product of a
+// one-block workgroup). Each wave takes 32 query rows of one of the two blocks
+// against all 64 keys of every union block; blocks its own query block does not keep,
+// and padding keys, are excluded by a -inf bias tile that starts the QK^T chain. See
+// the comment above the kernel.
+//
+// k_sparse_attn (e4m3 Q/K, D = 64, and blocks with counted keys): a workgroup of
+// four waves owns one query block (64 rows) of one (batch, head) and walks the
+// block's CSR list in order. The K and V tiles of each kept block are copied once per
+// workgroup into LDS with direct global-to-LDS loads (buffer_load_dwordx4 ... lds,
+// each wave moving a quarter of each tile in contiguous kilobytes) into two-slot K
+// and V rings, K two blocks and V one block ahead of use; one barrier per block. The
+// e4m3 variant issues its copies from inline asm and reads the second half of its V
+// operands later in the block, which fits it in 168 registers and three workgroups
+// per CU (its K ring is half the size). Wave w takes query rows 32*(w & 1) .. +31 and
+// key rows 32*(w >> 1) .. +31 of every block (the layout conventions are described in
 // attn_common.h); the two key halves of a query row carry separate online-softmax
-// states that are merged once at the end through LDS. Workgroups are remapped so
-// that each XCD gets a contiguous range of rows (same heads), which keeps the
-// shared K/V tiles in that XCD's L2; on 2D grids the rows run in strips of 8 block
-// columns (strip_row), which keeps a structured mask's row and column blocks shared.
+// states that are merged once at the end through LDS.
+//
+// Both remap workgroups so that each XCD gets a contiguous range of rows (same
+// heads), which keeps the shared K/V tiles in that XCD's L2; on 2D grids the rows run
+// in strips of 8 block columns (strip_row), which keeps a structured mask's row and
+// column blocks shared.
 #include "attn_common.h"
 #include "fpsa_internal.h"
 
@@ -215,6 +229,365 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
     merge_and_store<D>(reinterpret_cast<float*>(lds), qh, kh, lane, acc, m, l, true, g, qb, qblk0, o, lse, o32);
 }
 
+// ---------------------------------------------------------------------------------
+// Paired form (bf16, D = 128, token-grid blocks, nb <= 4096). One workgroup owns two
+// neighbouring query blocks of one (batch, head) and walks the union of their kept
+// lists, so each K/V tile copied into LDS serves 128 queries instead of 64: half the
+// copy bytes and barriers per product. Wave w takes the 32 query rows 32*(w & 1) ..
+// of query block w >> 1 against all 64 keys of every union block. The union is
+// walked in ascending block order from two 4096-bit membership bitmaps built in LDS
+// (a repeated entry counts once; entries outside [0, nb) are ignored). A union block
+// the wave's own query block does not keep contributes nothing: its scores are -inf.
+//
+// Key masking costs no vector instruction: every QK^T chain starts from a bias tile
+// read from a small LDS table instead of from zero, 0 for a real key and -inf for a
+// padding key of an edge block (or for every key of a block the wave does not keep).
+// The table holds, per edge code (and the "nothing" code), the 2 x 16 accumulator
+// values of each lane half; the tile for block u+2 is read at the end of block u's
+// section into the registers that hold its scores two sections later.
+constexpr int kPairThreads = 256;
+constexpr int kMaxBitmapWords = 4096 / 32;               // 32-bit words of one row's bitmap
+constexpr int kBiasCodes = 9;                            // edge codes 0..7, then "nothing kept"
+
+__device__ inline float max16_lane(const f32x16& x) {
+    const float a = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    const float b = fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]));
+    const float d = fmaxf(fmaxf(x[8], x[9]), fmaxf(x[10], x[11]));
+    const float e = fmaxf(fmaxf(x[12], x[13]), fmaxf(x[14], x[15]));
+    return fmaxf(fmaxf(a, b), fmaxf(d, e));
+}
+
+// Bias tiles of code `bc` for this lane: element i of tile kt is key 32 kt + 8 (i / 4)
+// + 4 half + i % 4 of the block.
+__device__ __attribute__((always_inline)) inline void load_bias(f32x16 (&t)[2], const float* table, int bc,
+                                                                 int half) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(table + ((bc * 2 + half) * 2 + kt) * 16 + 4 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[kt][4 * j + e] = v[e];
+        }
+}
+
+// Main section of union block u for this wave: the QK^T of block u+1 (two 32-key
+// halves, 16 products, starting from its bias tile in sn) and the exponentials and
+// P*V of block u (16 products), in a fixed issue order. K(u+1) and V(u) operands are
+// read from LDS four products ahead of use; the NC copies into LDS (inline asm, so
+// that no read waits for them) go one after each of the first NC products. The 96
+// vector steps of the softmax (per pair of scores: two scale-and-shift FMAs, two
+// exponentials, one bf16 pack, one dot into the row sum) run as a stream, three per
+// product after twelve up front. At the end, s receives the bias tile of block u+2.
+template <int NC, class Copy>
+__device__ __attribute__((always_inline)) inline void pair_main(
+    const uint8_t* kst, const uint8_t* vst, int lane, int half, const KHalf<128, false>& q, f32x16 (&acc)[4],
+    f32x16 (&s)[2], f32x16 (&sn)[2], float c, float nref, float& l, float& smax, const float* bias_table,
+    int bias_next, Copy&& copy_one) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    bf16x8 kk[8];
+    bf16x8 vv[8];
+    float pf[2][16];
+    uint32_t pw[2][8];
+    float rs[2] = {0.0f, 0.0f};
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+    // K operand of product n (0..15: half n / 8, step n % 8)
+    auto KR = [&](int n) { kk[n & 7] = *reinterpret_cast<const bf16x8*>(kst + n * 1024 + 16 * lane); };
+    // V operand of P*V product n (0..15: half kt = n / 8, cc = (n / 4) % 2, t = n % 4)
+    auto VR = [&](int n) {
+        const int kt = n >> 3, cc = (n >> 2) & 1, t = n & 3;
+        vv[n & 7] = *reinterpret_cast<const bf16x8*>(vst + (t * 4 + 2 * kt + cc) * 1024 + 16 * lane);
+    };
+    auto QK = [&](int n) {
+        const int kt = n >> 3, st = n & 7;
+        sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n & 7], q.b[st], sn[kt], 0, 0, 0);
+    };
+    auto PV = [&](int n) {
+        const int kt = n >> 3, cc = (n >> 2) & 1, t = n & 3;
+        const i32x4 wv = {(int)pw[kt][4 * cc], (int)pw[kt][4 * cc + 1], (int)pw[kt][4 * cc + 2],
+                          (int)pw[kt][4 * cc + 3]};
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[n & 7], __builtin_bit_cast(bf16x8, wv), acc[t], 0, 0, 0);
+    };
+    // vector step k of the softmax stream (k = 0..95)
+    auto VS = [&](int k) {
+        const int pr = k / 6, op = k % 6, kt = pr >> 3, i = 2 * (pr & 7);
+        if (op == 0) pf[kt][i] = __builtin_fmaf(s[kt][i], c, nref);
+        else if (op == 1) pf[kt][i + 1] = __builtin_fmaf(s[kt][i + 1], c, nref);
+        else if (op == 2) pf[kt][i] = __builtin_amdgcn_exp2f(pf[kt][i]);
+        else if (op == 3) pf[kt][i + 1] = __builtin_amdgcn_exp2f(pf[kt][i + 1]);
+        else if (op == 4) {
+            bf16x2 b;
+            b[0] = (__bf16)pf[kt][i];
+            b[1] = (__bf16)pf[kt][i + 1];
+            pw[kt][i >> 1] = __builtin_bit_cast(uint32_t, b);
+        } else {
+            rs[kt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[kt][i >> 1]), ones, rs[kt], false);
+        }
+    };
+    auto MX = [&](int kt, int gi) {   // partial maximum of the next block's scores 4 gi .. 4 gi + 3 of half kt
+        const float x = fmaxf(fmaxf(sn[kt][4 * gi], sn[kt][4 * gi + 1]), fmaxf(sn[kt][4 * gi + 2], sn[kt][4 * gi + 3]));
+        if (kt == 0) mx0 = fmaxf(mx0, x);
+        else mx1 = fmaxf(mx1, x);
+    };
+#define FPSA_SB __builtin_amdgcn_sched_barrier(0)
+    KR(0); KR(1); KR(2); KR(3);
+#pragma unroll
+    for (int k = 0; k < 12; ++k) VS(k);
+    FPSA_SB;
+#pragma unroll
+    for (int n = 0; n < 32; ++n) {
+        if (n < 16) QK(n);
+        else PV(n - 16);
+        if (n < NC) copy_one(n);
+        // operand reads four products ahead: K of products 4..15, then V of 0..15
+        if (n + 4 < 16) KR(n + 4);
+        else if (n + 4 - 16 < 16) VR(n + 4 - 16);
+#pragma unroll
+        for (int k = 12 + 3 * n; k < 15 + 3 * n; ++k)
+            if (k < 96) VS(k);
+        if (n >= 20 && n < 24) MX(0, n - 20);
+        if (n >= 24 && n < 28) MX(1, n - 24);
+        if (n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
+        if (n == 30) l += wave_add32(rs[0] + rs[1]);
+        if (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
+        FPSA_SB;
+    }
+#undef FPSA_SB
+}
+
+// Lazy rescale at the entry of a union block: when the block's maximum (bias included,
+// so padding keys and blocks the wave does not keep are excluded) exceeds the running
+// reference by more than the slack, move the reference and rescale the state. Returns
+// -m (0 before any key).
+__device__ __attribute__((always_inline)) inline float pair_enter(float smax, float c, f32x16 (&acc)[4], float& m,
+                                                                  float& l) {
+    const float mloc = smax * c;
+    const bool grow = mloc > m + kRescaleSlack;
+    if (__ballot(grow)) {
+        const float mnew = grow ? mloc : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+        l *= alpha;
+        m = mnew;
+    }
+    return m == -INFINITY ? 0.0f : -m;
+}
+
+__global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
+    const __bf16* __restrict__ qv, const __bf16* __restrict__ kv, const __bf16* __restrict__ vt,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long P, float scale_log2,
+    __bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o32) {
+    constexpr int D = 128;
+    constexpr int kKBytes = kBlock * D * 2, kVBytes = kBlock * D * 2;
+    constexpr int kChunks = kKBytes / 1024 / 4;           // kilobytes per wave per tile
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kKBytes + kVBytes)];
+    __shared__ uint32_t bits[2][kMaxBitmapWords];
+    __shared__ __attribute__((aligned(16))) float bias_table[kBiasCodes * 2 * 2 * 16];
+    uint8_t* const kring = lds;
+    uint8_t* const vring = lds + 2 * kKBytes;
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qsel = w >> 1, qh = w & 1;
+    const int half = lane >> 5;
+    const long p = xcd_row(P);
+    const int ph = (g.nb + 1) >> 1;
+    const long bh = p / ph;
+    const int v0 = 2 * (int)(p - bh * ph);
+    const bool hasrow = v0 + qsel < g.nb;                 // uniform per wave
+    const long r = strip_row(bh * g.nb + (hasrow ? v0 + qsel : v0), g);
+    const int qb = (int)(r - bh * g.nb);
+    const long npad = (long)g.nb * kBlock;
+    const long qblk0 = bh * npad + (long)qb * kBlock;
+
+    KHalf<D, false> q;
+    if (hasrow) {
+        load_khalf<D, false>(q, qv, qblk0, qh, lane);
+    } else {
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q.b[j][e] = (__bf16)0.0f;
+    }
+    const float cq = scale_log2;
+
+    // bias table: entry ((code * 2 + half) * 2 + kt) * 16 + i is 0 when key 32 kt + 8 (i / 4)
+    // + 4 half + i % 4 of a block with edge code `code` is real, else -inf (code 8: none)
+    for (int x = threadIdx.x; x < kBiasCodes * 64; x += kPairThreads) {
+        const int code = x >> 6, i = x & 15, kt = (x >> 4) & 1, hf = (x >> 5) & 1;
+        const int key = 32 * kt + 8 * (i >> 2) + 4 * hf + (i & 3);
+        const int plane = g.th * g.tw;
+        const int et = key / plane, eh = (key - et * plane) / g.tw, ew = key - et * plane - eh * g.tw;
+        const int ok = (et < g.T - (g.nt - 1) * g.tt ? 1 : 0) | (eh < g.Hg - (g.nh - 1) * g.th ? 2 : 0) |
+                       (ew < g.Wg - (g.nw - 1) * g.tw ? 4 : 0);
+        const bool real = code < 8 && ((ok | ~code) & 7) == 7;
+        bias_table[((code * 2 + hf) * 2 + kt) * 16 + i] = real ? 0.0f : -INFINITY;
+    }
+    // membership bitmaps of the two kept lists
+    const int nwords = (g.nb + 63) >> 6;
+    for (int i = threadIdx.x; i < 2 * kMaxBitmapWords; i += kPairThreads) (&bits[0][0])[i] = 0u;
+    __syncthreads();
+    if (hasrow) {
+        const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
+        for (int e = e0 + 64 * qh + lane; e < e1; e += 128) {
+            const int x = col_idx[e];
+            if ((unsigned)x < (unsigned)g.nb) atomicOr(&bits[qsel][x >> 5], 1u << (x & 31));
+        }
+    }
+    __syncthreads();
+    // number of union entries: lane l counts word l of the two bitmaps
+    int n_union;
+    {
+        int cnt = 0;
+        if (lane < 2 * nwords) cnt = __builtin_popcount(bits[0][lane] | bits[1][lane]);
+        if (lane + 64 < 2 * nwords) cnt += __builtin_popcount(bits[0][lane + 64] | bits[1][lane + 64]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+        n_union = __builtin_amdgcn_readfirstlane(cnt);
+    }
+
+    // Union entries in ascending order: the index word (block | edge code << kEdgeShift)
+    // and whether this wave's query block keeps it; -1 past the end. The bitmap words
+    // are read once per 64 blocks.
+    int gw = -1, winfo = -1;
+    uint64_t rem = 0, own = 0;
+    auto word = [&](int sel, int i) {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(bits[sel][2 * i]);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(bits[sel][2 * i + 1]);
+        return ((uint64_t)hi << 32) | lo;
+    };
+    auto gen = [&](int& info, bool& mine) {
+        while (rem == 0) {
+            if (gw + 1 >= nwords) {
+                info = -1;
+                mine = false;
+                return;
+            }
+            ++gw;
+            const uint64_t a = word(0, gw), b = word(1, gw);
+            rem = a | b;
+            own = qsel ? b : a;
+            winfo = block_info(g, 64 * gw + lane);
+        }
+        const int bit = __builtin_ctzll(rem);
+        rem &= rem - 1;
+        info = __builtin_amdgcn_readlane(winfo, bit);
+        mine = (own >> bit) & 1ull;
+    };
+    auto block_of = [](int info) { return info < 0 ? 0 : (info & kBlockIdMask); };
+    auto bias_code = [](int info, bool mine) { return (info < 0 || !mine) ? 8 : (info >> kEdgeShift); };
+
+    const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(kv) + bh * npad * D * 2;
+    const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(vt) + bh * npad * D * 2;
+    const i32x4r krs = tile_rsrc_raw(kbytes, (uint32_t)(g.nb * kKBytes));
+    const i32x4r vrs = tile_rsrc_raw(vbytes, (uint32_t)(g.nb * kVBytes));
+    const int lane16 = 16 * lane;
+    auto copy_tile = [&](const i32x4r& rs, int info, uint8_t* ring, int tile_bytes, int i) {
+        copy_kb_asm(rs, (uint32_t)(block_of(info) * tile_bytes + (kChunks * w + i) * 1024),
+                    ring + (kChunks * w + i) * 1024, lane16);
+    };
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+    float m = -INFINITY, l = 0.0f;
+
+    int inf, infn;
+    bool mine, minen;
+    gen(inf, mine);
+    gen(infn, minen);
+    float smax = -INFINITY;
+    // iteration parity selects the ring slots: K(u+1) is read from slot (u+1)&1 while
+    // K(u+2) is copied into slot u&1; V(u) from slot u&1 while V(u+1) goes to (u+1)&1
+    auto step = [&](int par, f32x16 (&s)[2], f32x16 (&sn)[2]) {
+        int inf2;
+        bool mine2;
+        gen(inf2, mine2);
+        const float nref = pair_enter(smax, cq, acc, m, l);
+        copies_landed_barrier();                          // K(u+1), V(u) landed; slots of u-1 free
+        const uint8_t* kst = kring + (par ^ 1) * kKBytes;
+        const uint8_t* vst = vring + par * kVBytes;
+        auto copy_one = [&](int i) {
+            if (i < kChunks) copy_tile(krs, inf2, kring + par * kKBytes, kKBytes, i);
+            else copy_tile(vrs, infn, vring + (par ^ 1) * kVBytes, kVBytes, i - kChunks);
+        };
+        pair_main<2 * kChunks>(kst, vst, lane, half, q, acc, s, sn, cq, nref, l, smax, bias_table,
+                               bias_code(inf2, mine2), copy_one);
+        inf = infn;
+        mine = minen;
+        infn = inf2;
+        minen = mine2;
+    };
+
+    f32x16 s0[2], s1[2];
+    if (n_union > 0) {
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            copy_tile(krs, inf, kring, kKBytes, i);
+            copy_tile(vrs, inf, vring, kVBytes, i);
+            copy_tile(krs, infn, kring + kKBytes, kKBytes, i);
+        }
+        copies_landed_barrier();                          // K(0), V(0), K(1) landed
+        load_bias(s0, bias_table, bias_code(inf, mine), half);
+        load_bias(s1, bias_table, bias_code(infn, minen), half);
+        {
+            KHalf<D, false> k0, k1;
+            lds_khalf<D, false>(k0, kring, 0, lane);
+            lds_khalf<D, false>(k1, kring, 1, lane);
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                s0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0.b[st], q.b[st], s0[0], 0, 0, 0);
+                s0[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1.b[st], q.b[st], s0[1], 0, 0, 0);
+            }
+        }
+        smax = wave_max32(fmaxf(max16_lane(s0[0]), max16_lane(s0[1])));
+        for (int j = 0; j < n_union; j += 2) {
+            step(0, s0, s1);
+            if (j + 1 < n_union) step(1, s1, s0);
+        }
+    }
+    wait_vmcnt<0>();                                      // drain the last copies
+
+    if (!hasrow) return;
+    const int col = lane & 31;
+    const int qslot = 32 * qh + col;
+    const bool qvalid = g.valid(qb, qslot);
+    const float inv = (qvalid && l > 0.0f) ? 1.0f / l : 0.0f;
+    __bf16* orow = o + (qblk0 + qslot) * D;
+    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            bf16x4 v4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(acc[t][4 * g4 + j] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g4 + 4 * half) = v4;
+        }
+    if (o32 != nullptr) {
+        float* frow = o32 + (qblk0 + qslot) * D;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 v4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v4[j] = acc[t][4 * g4 + j] * inv;
+                *reinterpret_cast<f32x4*>(frow + 32 * t + 8 * g4 + 4 * half) = v4;
+            }
+    }
+    if (lse != nullptr && half == 0) {
+        float val = 0.0f;
+        if (qvalid) val = l > 0.0f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+        lse[qblk0 + qslot] = val;
+    }
+}
+
 void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, const float* q_scale,
                         const float* k_scale, const int32_t* row_ptr, const int32_t* col_idx,
                         int B, int H, int D, const Geom& g, float scale, void* o, float* lse, float* o32,
@@ -224,6 +597,12 @@ void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, co
     const __bf16* vt = static_cast<const __bf16*>(v);
     __bf16* out = static_cast<__bf16*>(o);
     dim3 grid((unsigned)R), block(kAttnThreads);
+    if (D == 128 && !fp8 && kcount == nullptr && g.nb <= 4096) {
+        const long P = (long)B * H * ((g.nb + 1) / 2);
+        k_sparse_attn_pair<<<(unsigned)P, kPairThreads, 0, st>>>(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                                                                 vt, row_ptr, col_idx, g, P, sl2, out, lse, o32);
+        return;
+    }
     if (D == 128) {
         if (fp8) k_sparse_attn<128, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
         else if (kcount) k_sparse_attn<128, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, kcount);

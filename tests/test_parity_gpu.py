@@ -356,6 +356,43 @@ def test_forward_skips_out_of_range_blocks():
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
 
 
+@pytest.mark.parametrize("grid,H", [((4, 12, 20), 2), ((3, 9, 9), 1), ((1, 24, 40), 2)])
+def test_forward_odd_block_counts_repeats_and_unsorted_rows(grid, H):
+    """bf16, D = 128 (two query blocks per workgroup over the union of their rows): odd
+    block counts (the last workgroup of a head holds one query block), rows listed in
+    shuffled order with repeated and out-of-range entries. Output bit-identical to the
+    same rows sorted and cleaned, and within the bf16 bounds of the oracle."""
+    D = 128
+    tile = (4, 4, 4) if grid[0] > 1 else (1, 8, 8)
+    q, k, v = inputs(grid, 1, H, D, amp=1.5, seed=27)
+    nb = O.num_blocks(grid, tile)
+    assert nb % 2 == 1
+    m = synth.random_mass_rows(H * nb, nb, seed=nb + 11, tie_frac=0.1, zero_frac=0.2)
+    m[H * nb - 1] = 0.0                                  # the lone last query block keeps nothing
+    rp, ci = O.select_blocks(m, 9, 10)
+    rng = np.random.default_rng(3)
+    rows, rows_bad = [], []
+    for r in range(H * nb):
+        row = ci[rp[r]:rp[r + 1]].tolist()
+        rows.append(row)
+        bad = row + row[: len(row) // 3] + [nb, -2, 1 << 20][: r % 3]
+        rng.shuffle(bad)
+        rows_bad.append(bad)
+    rp_bad = np.concatenate([[0], np.cumsum([len(x) for x in rows_bad])]).astype(np.int32)
+    ci_bad = np.array([x for row in rows_bad for x in row], np.int32)
+    bsa, ot, o, lse = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    _, ot_bad, o_bad, lse_bad = _run_forward(q, k, v, grid, tile, H, D, rp_bad, ci_bad)
+    assert torch.equal(ot.view(torch.int16), ot_bad.view(torch.int16))
+    assert np.array_equal(lse, lse_bad)
+    out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp_bad, ci_bad)
+    mx, mean = output_errors(o_bad, out, tok)
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    _, slot = O.token_blocks(grid, tile)
+    blk, _ = O.token_blocks(grid, tile)
+    last = np.where(blk == nb - 1)[0]
+    assert np.all(o_bad[0, last, H - 1, :] == 0) and np.all(np.isneginf(lse_bad[0, H - 1, slot[last]]))
+
+
 @pytest.mark.parametrize("grid,H,D", [((5, 6, 7), 2, 128), ((9, 10, 13), 1, 128), ((4, 8, 8), 2, 64)])
 def test_fp8_forward(grid, H, D):
     """FP8 Q/K: parity with the oracle's simulation of the same per-tile e4m3
