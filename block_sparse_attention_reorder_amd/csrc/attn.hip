@@ -32,6 +32,8 @@
 // heads), which keeps the shared K/V tiles in that XCD's L2; on 2D grids the rows run
 // in strips of 8 block columns (strip_row), which keeps a structured mask's row and
 // column blocks shared.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "fpsa_internal.h"
 
@@ -245,6 +247,16 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
 // The table holds, per edge code (and the "nothing" code), the 2 x 16 accumulator
 // values of each lane half; the tile for block u+2 is read at the end of block u's
 // section into the registers that hold its scores two sections later.
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so that every
+// index into a section's register arrays is a constant whatever the unroller decides.
+template <int B, int E, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 constexpr int kPairThreads = 256;
 constexpr int kMaxBitmapWords = 4096 / 32;               // 32-bit words of one row's bitmap
 constexpr int kBiasCodes = 9;                            // edge codes 0..7, then "nothing kept"
@@ -331,27 +343,24 @@ __device__ __attribute__((always_inline)) inline void pair_main(
     };
 #define FPSA_SB __builtin_amdgcn_sched_barrier(0)
     KR(0); KR(1); KR(2); KR(3);
-#pragma unroll
-    for (int k = 0; k < 12; ++k) VS(k);
+    static_for<0, 12>([&](auto kc) { VS(decltype(kc)::value); });
     FPSA_SB;
-#pragma unroll
-    for (int n = 0; n < 32; ++n) {
-        if (n < 16) QK(n);
+    static_for<0, 32>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        if constexpr (n < 16) QK(n);
         else PV(n - 16);
-        if (n < NC) copy_one(n);
+        if constexpr (n < NC) copy_one(n);
         // operand reads four products ahead: K of products 4..15, then V of 0..15
-        if (n + 4 < 16) KR(n + 4);
-        else if (n + 4 - 16 < 16) VR(n + 4 - 16);
-#pragma unroll
-        for (int k = 12 + 3 * n; k < 15 + 3 * n; ++k)
-            if (k < 96) VS(k);
-        if (n >= 20 && n < 24) MX(0, n - 20);
-        if (n >= 24 && n < 28) MX(1, n - 24);
-        if (n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
-        if (n == 30) l += wave_add32(rs[0] + rs[1]);
-        if (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
+        if constexpr (n + 4 < 16) KR(n + 4);
+        else if constexpr (n + 4 - 16 < 16) VR(n + 4 - 16);
+        static_for<12 + 3 * n, (15 + 3 * n < 96 ? 15 + 3 * n : 96)>([&](auto kc) { VS(decltype(kc)::value); });
+        if constexpr (n >= 20 && n < 24) MX(0, n - 20);
+        if constexpr (n >= 24 && n < 28) MX(1, n - 24);
+        if constexpr (n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
+        if constexpr (n == 30) l += wave_add32(rs[0] + rs[1]);
+        if constexpr (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
         FPSA_SB;
-    }
+    });
 #undef FPSA_SB
 }
 
