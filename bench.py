@@ -442,7 +442,20 @@ def measure_workload(args, w, dev):
         "kernels_ms": kern,
     }
     out.update(extra)
+    if args.cpu_sample > 0 and not args.kernels_only:
+        # the oracle on head 0 of the same (device-drawn) inputs, copied to the host;
+        # the sample is sized for 10-30 s of host work at this workload's token count
+        sample = min(args.cpu_sample, CPU_SAMPLE_BLOCKS.get(w.name, args.cpu_sample))
+        if w.reuse_steps:
+            qd, kd, vd = device_inputs(w, 0, dev, pe)
+        q0, k0, v0 = (x[:, :, :1, :].float().cpu().numpy() for x in (qd, kd, vd))
+        out["cpu_baseline"] = cpu_baseline(w, q0, k0, v0, bsa, sample, structured=w.mask == "grat")
     print(json.dumps(out))
+
+
+# Query blocks of head 0 the CPU baseline samples per workload (the mass pass costs
+# O(N) per query block; the structured mask's rows keep about 131 blocks each).
+CPU_SAMPLE_BLOCKS = {"wan720p": 256, "hunyuan720p": 160, "grat8192": 512, "tiny": 4}
 
 
 def _timed(fn, stream, reps):
@@ -577,9 +590,10 @@ def semantic_row(bsa, w, qt, stream, reps):
                                               / 1e9 / PEAK["fp64"], 4)}
 
 
-def cpu_baseline(w, q, k, v, bsa, nsample):
+def cpu_baseline(w, q, k, v, bsa, nsample, structured=False):
     """The oracle, as it stands, on a bounded sample: mass pass, selection and masked
-    attention for `nsample` query blocks of head 0 (first, last and seeded others).
+    attention for `nsample` query blocks of head 0 (first, last and seeded others); on
+    the structured-mask workload the fixed mask's rows replace mass pass and selection.
     Reported in the same unit as `value`: kept-block FLOP of the sampled rows over the
     oracle's time for those rows."""
     import numpy as np
@@ -588,14 +602,22 @@ def cpu_baseline(w, q, k, v, bsa, nsample):
 
     rng = np.random.default_rng(12345)
     nb = bsa.nb
+    nsample = min(nsample, nb)
     picks = sorted(set([0, nb - 1] + rng.choice(nb, size=max(0, nsample - 2), replace=False).tolist()))[:nsample]
     q0, k0, v0 = (np.ascontiguousarray(x[:, :, :1, :]) for x in (q, k, v))
     t0 = time.perf_counter()
-    m = O.block_mass(q0, k0, w.grid, w.tile, bsa.scale, qblocks=picks)
-    t1 = time.perf_counter()
-    rows = m.reshape(len(picks), nb).astype(np.float32)
-    rp_s, ci_s = O.select_blocks(rows)
-    t2 = time.perf_counter()
+    if structured:
+        nh, nw = -(-w.grid[1] // w.tile[1]), -(-w.grid[2] // w.tile[2])
+        rp_all, ci_all = O.structured_mask(nh, nw, 1)
+        rp_s = np.concatenate([[0], np.cumsum([rp_all[b + 1] - rp_all[b] for b in picks])]).astype(np.int32)
+        ci_s = np.concatenate([ci_all[rp_all[b]:rp_all[b + 1]] for b in picks]).astype(np.int32)
+        t1 = t2 = time.perf_counter()
+    else:
+        m = O.block_mass(q0, k0, w.grid, w.tile, bsa.scale, qblocks=picks)
+        t1 = time.perf_counter()
+        rows = m.reshape(len(picks), nb).astype(np.float32)
+        rp_s, ci_s = O.select_blocks(rows)
+        t2 = time.perf_counter()
     # expand the sampled rows into a CSR over all rows of head 0 (others empty)
     rp = np.zeros(nb + 1, np.int32)
     counts = np.zeros(nb, np.int64)
@@ -611,8 +633,9 @@ def cpu_baseline(w, q, k, v, bsa, nsample):
     return {"value": round(flop / (t3 - t0) / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{len(picks)} query blocks of head 0 of {w.name} (first, last, seeded others): "
-                      f"float64 mass pass {t1 - t0:.2f} s, selection {t2 - t1:.3f} s, masked attention "
-                      f"{t3 - t2:.2f} s; {kept} kept pairs",
+                      + (f"fixed structured mask rows, masked attention {t3 - t2:.2f} s" if structured else
+                         f"float64 mass pass {t1 - t0:.2f} s, selection {t2 - t1:.3f} s, masked attention "
+                         f"{t3 - t2:.2f} s") + f"; {kept} kept pairs",
             "seconds": round(t3 - t0, 3)}
 
 

@@ -6,17 +6,17 @@
 //
 // Two gfx950 kernels.
 //
-// k_sparse_attn_pair (bf16, D = 128, blocks from the token grid, nb <= 4096; the main
-// path): a workgroup of four waves owns two neighbouring query blocks and walks the
-// union of their kept lists in ascending block order, so every K/V tile copied into
-// LDS serves 128 queries (half the copy bytes and barriers per product of a
-// one-block workgroup). Each wave takes 32 query rows of one of the two blocks
-// against all 64 keys of every union block; blocks its own query block does not keep,
-// and padding keys, are excluded by a -inf bias tile that starts the QK^T chain. See
-// the comment above the kernel.
+// k_sparse_attn_pair (bf16 or e4m3 Q/K, D = 128, blocks from the token grid, at most
+// 4096 blocks; the main path): a workgroup of four waves owns two neighbouring query
+// blocks and walks the union of their kept lists in ascending block order, so every
+// K/V tile copied into LDS serves 128 queries (half the copy bytes and barriers per
+// product of a one-block workgroup). Each wave takes 32 query rows of one of the two
+// blocks against all 64 keys of every union block; blocks its own query block does
+// not keep, and padding keys, are excluded by a -inf bias tile that starts the QK^T
+// chain. See the comment above the kernel.
 //
-// k_sparse_attn (e4m3 Q/K, D = 64, and blocks with counted keys): a workgroup of
-// four waves owns one query block (64 rows) of one (batch, head) and walks the
+// k_sparse_attn (D = 64, blocks with counted keys, grids over 4096 blocks): a
+// workgroup of four waves owns one query block (64 rows) of one (batch, head) and walks the
 // block's CSR list in order. The K and V tiles of each kept block are copied once per
 // workgroup into LDS with direct global-to-LDS loads (buffer_load_dwordx4 ... lds,
 // each wave moving a quarter of each tile in contiguous kilobytes) into two-slot K
@@ -291,28 +291,46 @@ __device__ __attribute__((always_inline)) inline void load_bias(f32x16 (&t)[2], 
 // vector steps of the softmax (per pair of scores: two scale-and-shift FMAs, two
 // exponentials, one bf16 pack, one dot into the row sum) run as a stream, three per
 // product after twelve up front. At the end, s receives the bias tile of block u+2.
-template <int NC, class Copy>
+template <bool FP8, int NC, class Copy>
 __device__ __attribute__((always_inline)) inline void pair_main(
-    const uint8_t* kst, const uint8_t* vst, int lane, int half, const KHalf<128, false>& q, f32x16 (&acc)[4],
+    const uint8_t* kst, const uint8_t* vst, int lane, int half, const KHalf<128, FP8>& q, f32x16 (&acc)[4],
     f32x16 (&s)[2], f32x16 (&sn)[2], float c, float nref, float& l, float& smax, const float* bias_table,
     int bias_next, Copy&& copy_one) {
+    // products of the next block's QK^T: 16 bf16 32x32x16, or 4 e4m3 32x32x64
+    constexpr int kQK = FP8 ? 4 : 16;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     bf16x8 kk[8];
+    i32x8 kf[4];
     bf16x8 vv[8];
     float pf[2][16];
     uint32_t pw[2][8];
     float rs[2] = {0.0f, 0.0f};
     float mx0 = -INFINITY, mx1 = -INFINITY;
-    // K operand of product n (0..15: half n / 8, step n % 8)
-    auto KR = [&](int n) { kk[n & 7] = *reinterpret_cast<const bf16x8*>(kst + n * 1024 + 16 * lane); };
+    // K operand of product n: bf16, half n / 8 and step n % 8, one kilobyte; e4m3, half
+    // n / 2 and step n % 2, the two halves of a 2 KB step split in LDS
+    auto KR = [&](int n) {
+        if constexpr (FP8) {
+            const uint8_t* p = kst + n * 2048 + 16 * lane;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 1024);
+            kf[n & 3] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            kk[n & 7] = *reinterpret_cast<const bf16x8*>(kst + n * 1024 + 16 * lane);
+        }
+    };
     // V operand of P*V product n (0..15: half kt = n / 8, cc = (n / 4) % 2, t = n % 4)
     auto VR = [&](int n) {
         const int kt = n >> 3, cc = (n >> 2) & 1, t = n & 3;
         vv[n & 7] = *reinterpret_cast<const bf16x8*>(vst + (t * 4 + 2 * kt + cc) * 1024 + 16 * lane);
     };
     auto QK = [&](int n) {
-        const int kt = n >> 3, st = n & 7;
-        sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n & 7], q.b[st], sn[kt], 0, 0, 0);
+        if constexpr (FP8) {
+            const int kt = n >> 1, st = n & 1;
+            sn[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[n & 3], q.f[st], sn[kt], 0, 0, 0, 0, 0, 0);
+        } else {
+            const int kt = n >> 3, st = n & 7;
+            sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n & 7], q.b[st], sn[kt], 0, 0, 0);
+        }
     };
     auto PV = [&](int n) {
         const int kt = n >> 3, cc = (n >> 2) & 1, t = n & 3;
@@ -342,25 +360,48 @@ __device__ __attribute__((always_inline)) inline void pair_main(
         else mx1 = fmaxf(mx1, x);
     };
 #define FPSA_SB __builtin_amdgcn_sched_barrier(0)
-    KR(0); KR(1); KR(2); KR(3);
-    static_for<0, 12>([&](auto kc) { VS(decltype(kc)::value); });
-    FPSA_SB;
-    static_for<0, 32>([&](auto nc) {
-        constexpr int n = decltype(nc)::value;
-        if constexpr (n < 16) QK(n);
-        else PV(n - 16);
-        if constexpr (n < NC) copy_one(n);
-        // operand reads four products ahead: K of products 4..15, then V of 0..15
-        if constexpr (n + 4 < 16) KR(n + 4);
-        else if constexpr (n + 4 - 16 < 16) VR(n + 4 - 16);
-        static_for<12 + 3 * n, (15 + 3 * n < 96 ? 15 + 3 * n : 96)>([&](auto kc) { VS(decltype(kc)::value); });
-        if constexpr (n >= 20 && n < 24) MX(0, n - 20);
-        if constexpr (n >= 24 && n < 28) MX(1, n - 24);
-        if constexpr (n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
-        if constexpr (n == 30) l += wave_add32(rs[0] + rs[1]);
-        if constexpr (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
+    if constexpr (FP8) {
+        // 20 products: the 4 QK^T first (their K operands read up front), then the 16
+        // P*V, V read four products ahead; 32 vector steps up front and 4 per product
+        // finish the softmax stream before the last P*V product that needs it
+        static_for<0, 4>([&](auto kc) { KR(decltype(kc)::value); });
+        static_for<0, 32>([&](auto kc) { VS(decltype(kc)::value); });
         FPSA_SB;
-    });
+        static_for<0, 20>([&](auto nc) {
+            constexpr int n = decltype(nc)::value;
+            if constexpr (n < kQK) QK(n);
+            else PV(n - kQK);
+            if constexpr (n < NC) copy_one(n);
+            if constexpr (n < 16) VR(n);
+            static_for<32 + 4 * n, (36 + 4 * n < 96 ? 36 + 4 * n : 96)>([&](auto kc) { VS(decltype(kc)::value); });
+            if constexpr (n >= 8 && n < 12) MX(0, n - 8);
+            if constexpr (n >= 12 && n < 16) MX(1, n - 12);
+            if constexpr (n == 16) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
+            if constexpr (n == 17) l += wave_add32(rs[0] + rs[1]);
+            if constexpr (n == 19) smax = wave_max32(fmaxf(mx0, mx1));
+            FPSA_SB;
+        });
+    } else {
+        KR(0); KR(1); KR(2); KR(3);
+        static_for<0, 12>([&](auto kc) { VS(decltype(kc)::value); });
+        FPSA_SB;
+        static_for<0, 32>([&](auto nc) {
+            constexpr int n = decltype(nc)::value;
+            if constexpr (n < kQK) QK(n);
+            else PV(n - kQK);
+            if constexpr (n < NC) copy_one(n);
+            // operand reads four products ahead: K of products 4..15, then V of 0..15
+            if constexpr (n + 4 < 16) KR(n + 4);
+            else if constexpr (n + 4 - 16 < 16) VR(n + 4 - 16);
+            static_for<12 + 3 * n, (15 + 3 * n < 96 ? 15 + 3 * n : 96)>([&](auto kc) { VS(decltype(kc)::value); });
+            if constexpr (n >= 20 && n < 24) MX(0, n - 20);
+            if constexpr (n >= 24 && n < 28) MX(1, n - 24);
+            if constexpr (n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
+            if constexpr (n == 30) l += wave_add32(rs[0] + rs[1]);
+            if constexpr (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
+            FPSA_SB;
+        });
+    }
 #undef FPSA_SB
 }
 
@@ -385,13 +426,16 @@ __device__ __attribute__((always_inline)) inline float pair_enter(float smax, fl
     return m == -INFINITY ? 0.0f : -m;
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
-    const __bf16* __restrict__ qv, const __bf16* __restrict__ kv, const __bf16* __restrict__ vt,
+    const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long P, float scale_log2,
     __bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o32) {
     constexpr int D = 128;
-    constexpr int kKBytes = kBlock * D * 2, kVBytes = kBlock * D * 2;
-    constexpr int kChunks = kKBytes / 1024 / 4;           // kilobytes per wave per tile
+    constexpr int kKBytes = kBlock * D * (FP8 ? 1 : 2), kVBytes = kBlock * D * 2;
+    constexpr int kKChunks = kKBytes / 1024 / 4;          // kilobytes per wave per tile
+    constexpr int kVChunks = kVBytes / 1024 / 4;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kKBytes + kVBytes)];
     __shared__ uint32_t bits[2][kMaxBitmapWords];
     __shared__ __attribute__((aligned(16))) float bias_table[kBiasCodes * 2 * 2 * 16];
@@ -412,16 +456,24 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     const long npad = (long)g.nb * kBlock;
     const long qblk0 = bh * npad + (long)qb * kBlock;
 
-    KHalf<D, false> q;
+    KHalf<D, FP8> q;
     if (hasrow) {
-        load_khalf<D, false>(q, qv, qblk0, qh, lane);
+        load_khalf<D, FP8>(q, qv, qblk0, qh, lane);
+    } else if constexpr (FP8) {
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q.f[j][e] = 0;
     } else {
 #pragma unroll
         for (int j = 0; j < D / 16; ++j)
 #pragma unroll
             for (int e = 0; e < 8; ++e) q.b[j][e] = (__bf16)0.0f;
     }
-    const float cq = scale_log2;
+    // base-2 softmax scale, times this query block's e4m3 tile scale; a block's own
+    // key tile scale multiplies it per block
+    const float cq = FP8 ? scale_log2 * (hasrow ? q_scale[r] : 1.0f) : scale_log2;
+    const float* ksc_row = FP8 ? k_scale + bh * g.nb : nullptr;
 
     // bias table: entry ((code * 2 + half) * 2 + kt) * 16 + i is 0 when key 32 kt + 8 (i / 4)
     // + 4 half + i % 4 of a block with edge code `code` is real, else -inf (code 8: none)
@@ -489,15 +541,24 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     auto block_of = [](int info) { return info < 0 ? 0 : (info & kBlockIdMask); };
     auto bias_code = [](int info, bool mine) { return (info < 0 || !mine) ? 8 : (info >> kEdgeShift); };
 
-    const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(kv) + bh * npad * D * 2;
+    const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(kv) + bh * npad * D * (FP8 ? 1 : 2);
     const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(vt) + bh * npad * D * 2;
     const i32x4r krs = tile_rsrc_raw(kbytes, (uint32_t)(g.nb * kKBytes));
     const i32x4r vrs = tile_rsrc_raw(vbytes, (uint32_t)(g.nb * kVBytes));
     const int lane16 = 16 * lane;
-    auto copy_tile = [&](const i32x4r& rs, int info, uint8_t* ring, int tile_bytes, int i) {
-        copy_kb_asm(rs, (uint32_t)(block_of(info) * tile_bytes + (kChunks * w + i) * 1024),
-                    ring + (kChunks * w + i) * 1024, lane16);
+    // kilobyte c of a tile in LDS: for V and bf16 K the same kilobyte of the tile (lane
+    // l: bytes 16 l); for e4m3 K, half c % 2 of the 2 KB operand step c / 2 (lane l: bytes
+    // 32 l + 16 (c % 2)), the split layout the e4m3 operand reads expect
+    auto copy_k = [&](int info, uint8_t* ring, int i) {
+        const int c = kKChunks * w + i;
+        const uint32_t src = FP8 ? (c >> 1) * 2048 + 16 * (c & 1) : c * 1024;
+        copy_kb_asm(krs, (uint32_t)(block_of(info) * kKBytes) + src, ring + c * 1024, FP8 ? 32 * lane : lane16);
     };
+    auto copy_v = [&](int info, uint8_t* ring, int i) {
+        const int c = kVChunks * w + i;
+        copy_kb_asm(vrs, (uint32_t)(block_of(info) * kVBytes + c * 1024), ring + c * 1024, lane16);
+    };
+    auto kscale = [&](int info) { return FP8 ? ksc_row[block_of(info)] : 1.0f; };
 
     f32x16 acc[4];
 #pragma unroll
@@ -510,6 +571,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     bool mine, minen;
     gen(inf, mine);
     gen(infn, minen);
+    float ksc = kscale(inf), kscn = kscale(infn);
     float smax = -INFINITY;
     // iteration parity selects the ring slots: K(u+1) is read from slot (u+1)&1 while
     // K(u+2) is copied into slot u&1; V(u) from slot u&1 while V(u+1) goes to (u+1)&1
@@ -517,41 +579,54 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
         int inf2;
         bool mine2;
         gen(inf2, mine2);
-        const float nref = pair_enter(smax, cq, acc, m, l);
+        const float ksc2 = kscale(inf2);
+        const float c = cq * ksc;
+        const float nref = pair_enter(smax, c, acc, m, l);
         copies_landed_barrier();                          // K(u+1), V(u) landed; slots of u-1 free
         const uint8_t* kst = kring + (par ^ 1) * kKBytes;
         const uint8_t* vst = vring + par * kVBytes;
         auto copy_one = [&](int i) {
-            if (i < kChunks) copy_tile(krs, inf2, kring + par * kKBytes, kKBytes, i);
-            else copy_tile(vrs, infn, vring + (par ^ 1) * kVBytes, kVBytes, i - kChunks);
+            if (i < kKChunks) copy_k(inf2, kring + par * kKBytes, i);
+            else copy_v(infn, vring + (par ^ 1) * kVBytes, i - kKChunks);
         };
-        pair_main<2 * kChunks>(kst, vst, lane, half, q, acc, s, sn, cq, nref, l, smax, bias_table,
-                               bias_code(inf2, mine2), copy_one);
+        pair_main<FP8, kKChunks + kVChunks>(kst, vst, lane, half, q, acc, s, sn, c, nref, l, smax, bias_table,
+                                             bias_code(inf2, mine2), copy_one);
         inf = infn;
         mine = minen;
         infn = inf2;
         minen = mine2;
+        ksc = kscn;
+        kscn = ksc2;
     };
 
     f32x16 s0[2], s1[2];
     if (n_union > 0) {
 #pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            copy_tile(krs, inf, kring, kKBytes, i);
-            copy_tile(vrs, inf, vring, kVBytes, i);
-            copy_tile(krs, infn, kring + kKBytes, kKBytes, i);
+        for (int i = 0; i < kKChunks; ++i) {
+            copy_k(inf, kring, i);
+            copy_k(infn, kring + kKBytes, i);
         }
+#pragma unroll
+        for (int i = 0; i < kVChunks; ++i) copy_v(inf, vring, i);
         copies_landed_barrier();                          // K(0), V(0), K(1) landed
         load_bias(s0, bias_table, bias_code(inf, mine), half);
         load_bias(s1, bias_table, bias_code(infn, minen), half);
         {
-            KHalf<D, false> k0, k1;
-            lds_khalf<D, false>(k0, kring, 0, lane);
-            lds_khalf<D, false>(k1, kring, 1, lane);
+            KHalf<D, FP8> k0, k1;
+            lds_khalf<D, FP8>(k0, kring, 0, lane);
+            lds_khalf<D, FP8>(k1, kring, 1, lane);
+            if constexpr (FP8) {
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                s0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0.b[st], q.b[st], s0[0], 0, 0, 0);
-                s0[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1.b[st], q.b[st], s0[1], 0, 0, 0);
+                for (int st = 0; st < D / 64; ++st) {
+                    s0[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0.f[st], q.f[st], s0[0], 0, 0, 0, 0, 0, 0);
+                    s0[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k1.f[st], q.f[st], s0[1], 0, 0, 0, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int st = 0; st < D / 16; ++st) {
+                    s0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0.b[st], q.b[st], s0[0], 0, 0, 0);
+                    s0[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1.b[st], q.b[st], s0[1], 0, 0, 0);
+                }
             }
         }
         smax = wave_max32(fmaxf(max16_lane(s0[0]), max16_lane(s0[1])));
@@ -606,10 +681,14 @@ void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, co
     const __bf16* vt = static_cast<const __bf16*>(v);
     __bf16* out = static_cast<__bf16*>(o);
     dim3 grid((unsigned)R), block(kAttnThreads);
-    if (D == 128 && !fp8 && kcount == nullptr && g.nb <= 4096) {
+    if (D == 128 && kcount == nullptr && g.nb <= kMaxBitmapWords * 32) {
         const long P = (long)B * H * ((g.nb + 1) / 2);
-        k_sparse_attn_pair<<<(unsigned)P, kPairThreads, 0, st>>>(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                                                                 vt, row_ptr, col_idx, g, P, sl2, out, lse, o32);
+        if (fp8)
+            k_sparse_attn_pair<true><<<(unsigned)P, kPairThreads, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx,
+                                                                           g, P, sl2, out, lse, o32);
+        else
+            k_sparse_attn_pair<false><<<(unsigned)P, kPairThreads, 0, st>>>(q, k, vt, nullptr, nullptr, row_ptr, col_idx,
+                                                                            g, P, sl2, out, lse, o32);
         return;
     }
     if (D == 128) {
