@@ -270,18 +270,19 @@ int32_t fpsa_retained_mass(const float* mass, int64_t R, int32_t nb, const int32
  * v: tiled VT, BF16.
  * row_ptr / col_idx: CSR with R = B*H*nb rows; key-block indices outside [0, nb)
  *   contribute nothing (they are treated as blocks without real keys). A row should
- *   list each block once (the selection and mask calls never repeat one): for bf16
- *   Q/K with D = 128 on grids of at most FPSA_MAX_SELECT_BLOCKS blocks a repeated
- *   block counts once, on the other paths once per listing.
+ *   list each block once (the selection and mask calls never repeat one): with
+ *   D = 128 on video grids (t > 1) of at most FPSA_MAX_SELECT_BLOCKS blocks a
+ *   repeated block counts once, on the other paths once per listing.
  * For each real query i of block qb of row r: o_i = sum_j p_ij v_j over the real
  *   keys j of the kept blocks, p the softmax of softmax_scale * q_i . k_j over
  *   exactly those keys (FP8: the scores use the decoded values, q8 * k8 * q_scale *
  *   k_scale). Queries with no kept key, and padding rows, get o = 0. The kept blocks
- *   are visited in ascending block order (bf16, D = 128, nb <= FPSA_MAX_SELECT_BLOCKS:
- *   two neighbouring query blocks share one pass over the union of their rows) or
- *   in CSR order (other paths); the order changes only rounding. Probabilities are
- *   rounded to BF16 for the P*V product, which accumulates in float32, and the
- *   softmax denominator is the sum of those rounded probabilities.
+ *   are visited in ascending block order (D = 128 on video grids (t > 1) of at most
+ *   FPSA_MAX_SELECT_BLOCKS blocks: two neighbouring query blocks share one pass over
+ *   the union of their rows) or in CSR order (other paths); the order changes only
+ *   rounding. Probabilities are rounded to BF16 for the P*V product, which
+ *   accumulates in float32, and the softmax denominator is the sum of those rounded
+ *   probabilities.
  * o: tiled rows BF16 [B, H, Npad, D]. lse: [B, H, Npad] float32 natural-log
  *   log-sum-exp over the visited keys, taken from the same rounded probabilities
  *   that normalise o (-inf for a query with none; 0 for padding), or NULL.

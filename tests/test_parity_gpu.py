@@ -356,14 +356,13 @@ def test_forward_skips_out_of_range_blocks():
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
 
 
-@pytest.mark.parametrize("grid,H", [((4, 12, 20), 2), ((3, 9, 9), 1), ((1, 24, 40), 2)])
+@pytest.mark.parametrize("grid,H", [((4, 12, 20), 2), ((3, 9, 9), 1), ((9, 4, 12), 2)])
 def test_forward_odd_block_counts_repeats_and_unsorted_rows(grid, H):
-    """bf16, D = 128 (two query blocks per workgroup over the union of their rows): odd
+    """bf16, D = 128, video grids (two query blocks per workgroup over the union of their rows): odd
     block counts (the last workgroup of a head holds one query block), rows listed in
     shuffled order with repeated and out-of-range entries. Output bit-identical to the
     same rows sorted and cleaned, and within the bf16 bounds of the oracle."""
-    D = 128
-    tile = (4, 4, 4) if grid[0] > 1 else (1, 8, 8)
+    D, tile = 128, (4, 4, 4)
     q, k, v = inputs(grid, 1, H, D, amp=1.5, seed=27)
     nb = O.num_blocks(grid, tile)
     assert nb % 2 == 1
