@@ -105,16 +105,27 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
             return block_info(g, x);
         }
     };
+    // e4m3: `cursc` holds the key tile scales of the same 64 entries, gathered at each
+    // window switch (a scale read per block inside the loop would be a scalar load,
+    // which shares the LDS reads' wait counter and returns out of order, turning every
+    // operand wait into a full drain)
     int cur = info_of(lane < n ? col_idx[e0 + lane] : -1);
     int raw = 64 + lane < n ? col_idx[e0 + 64 + lane] : -1;
     int base = 0;
+    auto gather_scales = [&]() { return FP8 ? ksc_row[cur < 0 ? 0 : (cur & kBlockIdMask)] : 1.0f; };
+    float cursc = gather_scales();
     auto info_at = [&](int jj) {          // jj = 0, 1, 2, ... in order
         if (jj - base == 64) {
             base += 64;
             cur = info_of(raw);
+            cursc = gather_scales();
             raw = base + 64 + lane < n ? col_idx[e0 + base + 64 + lane] : -1;
         }
         return __builtin_amdgcn_readlane(cur, jj - base);
+    };
+    // scale of entry jj, right after info_at(jj)
+    auto scale_at = [&](int jj) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cursc), jj - base));
     };
     auto block_of = [](int info) { return info < 0 ? 0 : (info & kBlockIdMask); };
 
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
     float smax = -INFINITY;       // unmasked maximum of the current block's scores
     auto step = [&](int j, f32x16& s, f32x16& sn) {
         const int inf2 = info_at(j + 2);
-        const float ksc2 = FP8 ? ksc_row[block_of(inf2)] : 1.0f;
+        const float ksc2 = FP8 ? scale_at(j + 2) : 1.0f;
         const float c = FP8 ? cq * ksc : cq;
         const int code = inf >> kEdgeShift;           // 0: interior block; < 0: no block
         uint64_t vm;
@@ -208,11 +219,9 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
     f32x16 s0, s1;
     if (n > 0) {
         inf = info_at(0);
+        if constexpr (FP8) ksc = scale_at(0);
         infn = info_at(1);
-        if constexpr (FP8) {
-            ksc = ksc_row[block_of(inf)];
-            kscn = ksc_row[block_of(infn)];
-        }
+        if constexpr (FP8) kscn = scale_at(1);
         copy_k(inf, 0);
         copy_v(inf, 0);
         copy_k(infn, 1);
@@ -439,6 +448,10 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (kKBytes + kVBytes)];
     __shared__ uint32_t bits[2][kMaxBitmapWords];
     __shared__ __attribute__((aligned(16))) float bias_table[kBiasCodes * 2 * 2 * 16];
+    // e4m3: the key tile scales of this (batch, head), staged once; a scale read from
+    // memory inside the loop would be a scalar load, which shares the LDS reads' wait
+    // counter and returns out of order, so every operand wait would become a full drain
+    __shared__ float ksc_lds[FP8 ? kMaxBitmapWords * 32 : 1];
     uint8_t* const kring = lds;
     uint8_t* const vring = lds + 2 * kKBytes;
 
@@ -490,6 +503,8 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     // membership bitmaps of the two kept lists
     const int nwords = (g.nb + 63) >> 6;
     for (int i = threadIdx.x; i < 2 * kMaxBitmapWords; i += kPairThreads) (&bits[0][0])[i] = 0u;
+    if constexpr (FP8)
+        for (int i = threadIdx.x; i < g.nb; i += kPairThreads) ksc_lds[i] = ksc_row[i];
     __syncthreads();
     if (hasrow) {
         const int e0 = row_ptr[r], e1 = row_ptr[r + 1];
@@ -558,7 +573,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
         const int c = kVChunks * w + i;
         copy_kb_asm(vrs, (uint32_t)(block_of(info) * kVBytes + c * 1024), ring + c * 1024, lane16);
     };
-    auto kscale = [&](int info) { return FP8 ? ksc_row[block_of(info)] : 1.0f; };
+    auto kscale = [&](int info) { return FP8 ? ksc_lds[block_of(info)] : 1.0f; };
 
     f32x16 acc[4];
 #pragma unroll

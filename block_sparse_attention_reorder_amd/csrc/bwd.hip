@@ -196,8 +196,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     // 4*hb + (0..3)), loaded one block ahead into registers: issued right after the
     // barrier, before the copies, and first used an iteration later, after the next
     // vmcnt(0), so no wait of the compiler's ever covers a copy in flight
+    // (e4m3: also the query tile's scale, as a vector load: its index is moved into a
+    // vector register, since a scalar load shares the LDS reads' wait counter and
+    // returns out of order, which would turn every operand wait into a full drain)
     f32x4 LG[2][2][2][2];                          // [set][L or G][ks][u]
-    auto load_lg = [&](int qbk, f32x4 (&L)[2][2], f32x4 (&G)[2][2]) {
+    float TQ[2];                                   // [set]
+    auto load_lg = [&](int qbk, f32x4 (&L)[2][2], f32x4 (&G)[2][2], float& T) {
         const long qrow = (bh * g.nb + (qbk < 0 ? 0 : qbk)) * 64 + 32 * r + 4 * hb;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -206,11 +210,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
                 L[ks][u] = *reinterpret_cast<const f32x4*>(lse2 + qrow + 16 * ks + 8 * u);
                 G[ks][u] = *reinterpret_cast<const f32x4*>(delta + qrow + 16 * ks + 8 * u);
             }
+        T = 1.0f;
+        if (q_scale != nullptr) {
+            long idx = bh * g.nb + (qbk < 0 ? 0 : qbk);
+            asm volatile("" : "+v"(idx));
+            T = q_scale[idx];
+        }
     };
 
-    auto phase1 = [&](const uint8_t* sq, int qbk, const f32x4 (&L)[2][2], const f32x4 (&G)[2][2]) {
+    auto phase1 = [&](const uint8_t* sq, const f32x4 (&L)[2][2], const f32x4 (&G)[2][2], float tq) {
         const uint8_t* sg = sq + kTile;
-        const float tq = q_scale != nullptr ? q_scale[bh * g.nb + qbk] : 1.0f;   // uniform (scalar load)
         const float cs = c * tq * sk;
         bf16x8 qa[D / 16], ga[D / 16];
 #pragma unroll
@@ -274,17 +283,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         constexpr int P = decltype(set)::value;
         wait_vmcnt<0>();
         __syncthreads();
-        load_lg(qnext, LG[1 - P][0], LG[1 - P][1]);   // unconditional (block 0 past the end)
+        load_lg(qnext, LG[1 - P][0], LG[1 - P][1], TQ[1 - P]);   // unconditional (block 0 past the end)
         if (jj + 1 < n) copy_block(qnext, lds + (1 - P) * kSlot);
         if (qcur >= 0) {                               // uniform
-            phase1(lds + P * kSlot, qcur, LG[P][0], LG[P][1]);
+            phase1(lds + P * kSlot, LG[P][0], LG[P][1], TQ[P]);
             __syncthreads();
             phase2(lds + P * kSlot);
         }
     };
     if (n > 0) {
         int qcur = qb_at(0);
-        load_lg(qcur, LG[0][0], LG[0][1]);
+        load_lg(qcur, LG[0][0], LG[0][1], TQ[0]);
         copy_block(qcur, lds);
         for (int jj = 0; jj < n; jj += 2) {
             const int q1 = qb_at(jj + 1);
@@ -357,17 +366,31 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     // index word (block and edge code) of entry jj, -1 when none; jj = 0, 1, 2, ... in
     // order. The words of 64 entries are formed at once, a lane each (the edge code's
     // divisions run once per 64 blocks), and the next 64 indices load a window ahead.
+    // e4m3: `cursc` holds the key tile scales of the same 64 entries, gathered at each
+    // window switch (a scale read per block in the loop would be a scalar load, which
+    // shares the LDS reads' wait counter and returns out of order, turning every
+    // operand wait into a full drain)
     int cur = lane < n ? block_info(g, col_idx[e0 + lane]) : -1;
     int raw = 64 + lane < n ? col_idx[e0 + 64 + lane] : -1;
     int wbase = 0;
+    auto gather_scales = [&]() {
+        return k_scale != nullptr ? k_scale[bh * g.nb + (cur < 0 ? 0 : (cur & kBlockIdMask))] : 1.0f;
+    };
+    float cursc = gather_scales();
     auto info_at = [&](int jj) {
         if (jj >= n) return -1;
         if (jj - wbase == 64) {
             wbase += 64;
             cur = block_info(g, raw);
+            cursc = gather_scales();
             raw = wbase + 64 + lane < n ? col_idx[e0 + wbase + 64 + lane] : -1;
         }
         return __builtin_amdgcn_readlane(cur, jj - wbase);
+    };
+    // scale of entry jj, right after info_at(jj) (1 past the end)
+    auto scale_at = [&](int jj) {
+        return jj >= n ? 1.0f
+                       : __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cursc), jj - wbase));
     };
     // K and V tiles of a block copied straight into an LDS slot, this wave moving its
     // quarter of each in whole kilobytes (a missing block copies block 0)
@@ -384,10 +407,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
         }
     };
 
-    auto compute = [&](const uint8_t* sk, int icur) {
+    auto compute = [&](const uint8_t* sk, int icur, float tk) {
         const uint8_t* sv = sk + kTile;
         const int code = icur >> kEdgeShift;
-        const float tk = k_scale != nullptr ? k_scale[bh * g.nb + (icur & kBlockIdMask)] : 1.0f;
         const float cs = c * tq * tk;
         const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
         const uint32_t m32 = (uint32_t)(vm >> (32 * kh + 4 * hb));
@@ -437,14 +459,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     // starts the copy of block j + 1 into the other slot and computes block j.
     if (n > 0) {
         int icur = info_at(0);
+        float tcur = scale_at(0);
         copy_block(icur, lds);
         for (int jj = 0; jj < n; ++jj) {
             const int inext = info_at(jj + 1);
+            const float tnext = scale_at(jj + 1);
             wait_vmcnt<0>();
             __syncthreads();
             if (jj + 1 < n) copy_block(inext, lds + ((jj + 1) & 1) * kSlot);
-            if (icur >= 0) compute(lds + (jj & 1) * kSlot, icur);
+            if (icur >= 0) compute(lds + (jj & 1) * kSlot, icur, tcur);
             icur = inext;
+            tcur = tnext;
         }
     }
     wait_vmcnt<0>();
