@@ -32,6 +32,7 @@ CSRC = os.path.join(ROOT, "block_sparse_attention_reorder_amd", "csrc")
 # sources each timed kernel is built from (its counters go stale when they change)
 KERNEL_SOURCES = {
     "sparse_fwd": ["attn.hip", "attn_common.h", "fpsa_device.h"],
+    "sparse_fwd_fp8": ["attn.hip", "attn_common.h", "fpsa_device.h"],
     "block_mass": ["mass.hip", "attn_common.h", "fpsa_device.h"],
     "tile_qkv": ["reorder.hip", "fpsa_device.h"],
     "untile": ["reorder.hip", "fpsa_device.h"],
@@ -48,19 +49,41 @@ def source_hash(kernel):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE,
-    each scaled by the same counter on a plain copy of known size), or None when the
-    kernel's sources changed since the counters were taken."""
+def measured_traffic(kernel, workload="wan480p"):
+    """HBM bytes per call of `kernel` at `workload` from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a plain copy of known
+    size; a call is one launch except for a mass pass in a bounded workspace), or None
+    when there is no such run or the kernel's sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get("kernels", {}).get(kernel)
+    e = t.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
     if not e or e.get("source_sha256") != source_hash(kernel):
         return None
-    return int(e["hbm_bytes_per_launch"])
+    return int(e["hbm_bytes_per_call"])
+
+
+def algorithmic_bytes(kernel, B, H, D, npad, nb, R, nnz):
+    """Bytes a call must move at least: each operand tile read once, each output
+    written once (the CSR read once for the forward)."""
+    t = B * H * npad * D
+    csr = 4 * (R + 1) + 4 * nnz
+    if kernel == "sparse_fwd":                      # Q, K, V read, O written, bf16
+        return 4 * t * 2 + csr
+    if kernel == "sparse_fwd_fp8":                  # e4m3 Q, K and their tile scales; bf16 V, O
+        return 2 * t + 2 * t * 2 + 2 * B * H * nb * 4 + csr
+    if kernel == "block_mass":                      # Q, K read, float32 masses written
+        return 2 * t * 2 + B * H * nb * nb * 4
+    raise KeyError(kernel)
+
+
+def traffic_fields(kernel, workload, B, H, D, npad, nb, R, nnz):
+    meas = measured_traffic(kernel, workload)
+    alg = algorithmic_bytes(kernel, B, H, D, npad, nb, R, nnz)
+    return {"hbm_bytes_measured": meas, "algorithmic_bytes": alg,
+            "traffic_ratio": None if meas is None else round(meas / alg, 2)}
 
 
 def parse():
@@ -180,11 +203,13 @@ def main():
         kk["frac"] = kk["achieved"] / kk["peak"]
     for name, kk in kernels.items():
         kk["traffic"] = measured_traffic(name)
+        if name in ("sparse_fwd", "block_mass"):
+            kk.update(traffic_fields(name, w.name, B, H, D, bsa.npad, bsa.nb, bsa.R, nnz))
     dominant = max(kernels, key=lambda n: kernels[n]["ms"])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": round(dk["achieved"], 2),
                 "peak": dk["peak"], "unit": dk["unit"], "frac": round(dk["frac"], 4),
-                "traffic": dk["traffic"]}
+                "traffic": dk["traffic"], "traffic_vs_algorithmic": dk.get("traffic_ratio")}
 
     spread = {s: _stats([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)])
               for j, s in enumerate(stages)}
@@ -423,6 +448,9 @@ def measure_workload(args, w, dev):
                     f"1..{w.reuse_steps}: tile -> sparse forward on the frozen CSR -> untile; value over the "
                     f"amortised call")
             step_ms = (one_time + sum(calls)) / len(calls)
+    for name in ("block_mass", "sparse_fwd", "sparse_fwd_fp8"):
+        if name in kern:
+            kern[name].update(traffic_fields(name, w.name, B, H, D, bsa.npad, bsa.nb, bsa.R, nnz))
     out = {
         "metric": f"kept-block TFLOP/s per call, {w.name}",
         "value": round(value, 2),
@@ -455,7 +483,7 @@ def measure_workload(args, w, dev):
 
 # Query blocks of head 0 the CPU baseline samples per workload (the mass pass costs
 # O(N) per query block; the structured mask's rows keep about 131 blocks each).
-CPU_SAMPLE_BLOCKS = {"wan720p": 256, "hunyuan720p": 160, "grat8192": 512, "tiny": 4}
+CPU_SAMPLE_BLOCKS = {"wan720p": 256, "hunyuan720p": 160, "grat8192": 2048, "tiny": 4}
 
 
 def _timed(fn, stream, reps):

@@ -28,10 +28,12 @@
 // attn_common.h); the two key halves of a query row carry separate online-softmax
 // states that are merged once at the end through LDS.
 //
-// Both remap workgroups so that each XCD gets a contiguous range of rows (same
-// heads), which keeps the shared K/V tiles in that XCD's L2; on 2D grids the rows run
-// in strips of 8 block columns (strip_row), which keeps a structured mask's row and
-// column blocks shared.
+// On video grids both remap workgroups so that each XCD gets a contiguous range of
+// rows (same heads), which keeps the shared K/V tiles in that XCD's L2. On 2D grids the
+// rows run in strips of 8 block columns (strip_row), which keeps a structured mask's
+// row and column blocks shared, and the eight XCDs take consecutive 64-row patches of
+// one head at a time (xcd_chunk_row), so that head's K and V stay in the infinity
+// cache.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -62,7 +64,10 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
     uint8_t* const kring = lds;
     uint8_t* const vring = lds + 2 * kKBytes;
 
-    const long r = strip_row(xcd_row(R), g);
+    // 2D grids: the strip order's 8 x 8 patches, one per XCD, all eight from one head at
+    // a time (its K and V fit the infinity cache: 8.6 % faster at 8192 x 8192 than one
+    // range of heads per XCD); video grids keep one contiguous range per XCD
+    const long r = strip_row(strip_grid(g) ? xcd_chunk_row(R) : xcd_row(R), g);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int qh = w & 1, kh = w >> 1;

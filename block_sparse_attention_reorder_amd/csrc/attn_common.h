@@ -29,6 +29,20 @@ __device__ inline long xcd_row(long nwg) {
     return (i % 8) * (full / 8) + i / 8;
 }
 
+// blockIdx.x -> work item for grids whose concurrent workgroups should all serve one
+// (batch, head): each XCD still takes 64 consecutive items (what its 32 CUs run at
+// once at two workgroups per CU), but the eight XCDs take the eight consecutive
+// chunks of 64 in turn, so the whole chip works through the items in order and one
+// head's K and V, rather than eight heads', compete for the 256 MB infinity cache.
+// A bijection on [0, nwg); the last nwg % 512 items keep their own index.
+__device__ inline long xcd_chunk_row(long nwg) {
+    const long i = blockIdx.x;
+    const long full = nwg - nwg % 512;
+    if (i >= full) return i;
+    const long x = i % 8, s = i / 8;
+    return (s / 64) * 512 + x * 64 + (s % 64);
+}
+
 // Order of the query blocks of a 2D (image) grid: vertical strips of kStripW block
 // columns, row-major inside a strip, so the ~64 workgroups an XCD runs at a time cover
 // an 8 x 8 patch of blocks. Under a criss-cross mask (a group keeps its whole block row
@@ -37,8 +51,9 @@ __device__ inline long xcd_row(long nwg) {
 // none. A bijection on each (batch, head)'s rows; identity for 3D grids and for grids
 // at most kStripW blocks wide.
 constexpr int kStripW = 8;
+__device__ inline bool strip_grid(const Geom& g) { return g.nt == 1 && g.nw > kStripW; }
 __device__ inline long strip_row(long r, const Geom& g) {
-    if (g.nt != 1 || g.nw <= kStripW) return r;
+    if (!strip_grid(g)) return r;
     const long bh = r / g.nb;
     const int i = (int)(r - bh * g.nb);
     const int ns = (g.nw + kStripW - 1) / kStripW, full = (ns - 1) * g.nh * kStripW;
