@@ -74,6 +74,21 @@ __device__ inline bf16x8 tr_operand(const uint8_t* tile, int off) {
     return __builtin_bit_cast(bf16x8, z);
 }
 
+// Compile-time loop: f(std::integral_constant<int, i>) for i = B .. E-1.
+template <int B, int E, class F>
+__device__ __attribute__((always_inline)) inline void bwd_static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>());
+        bwd_static_for<B + 1, E>(f);
+    }
+}
+
+// The value lane I of this lane's 16-lane row holds (DPP row broadcast).
+template <int I>
+__device__ inline float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + I, 0xF, 0xF, true));
+}
+
 // Fragments loaded once and reused for every block: an empty asm that rewrites each
 // register keeps the compiler from re-issuing the global loads inside the loop.
 template <int D>
@@ -192,24 +207,21 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         return xbuf + (((kh * 2 + qq) * 2 + ks) * 2 + kind) * 1024 + 16 * lane;
     };
 
-    // lse2 and delta of the rows this lane holds in phase 1 (queries 32*r + 16*ks + 8*u +
-    // 4*hb + (0..3)), loaded one block ahead into registers: issued right after the
-    // barrier, before the copies, and first used an iteration later, after the next
-    // vmcnt(0), so no wait of the compiler's ever covers a copy in flight
-    // (e4m3: also the query tile's scale, as a vector load: its index is moved into a
-    // vector register, since a scalar load shares the LDS reads' wait counter and
-    // returns out of order, which would turn every operand wait into a full drain)
-    f32x4 LG[2][2][2][2];                          // [set][L or G][ks][u]
+    // lse2 and delta of the 32 queries of this wave's phase-1 half, one per lane: lane
+    // 16 g + n (g the 16-lane row) holds query 32*r + 8*(n/4) + 4*(g/2) + n%4, which is
+    // exactly the query of phase-1 element i = n for the lanes of row g, so element i
+    // takes it from lane i of its own row (a DPP row broadcast). Loaded one block ahead:
+    // issued right after the barrier, before the copies, and first used an iteration
+    // later, after the next vmcnt(0), so no wait of the compiler's ever covers a copy in
+    // flight. (e4m3: also the query tile's scale, as a vector load: its index is moved
+    // into a vector register, since a scalar load shares the LDS reads' wait counter and
+    // returns out of order, which would turn every operand wait into a full drain.)
+    float LG[2][2];                                // [set][L or G]
     float TQ[2];                                   // [set]
-    auto load_lg = [&](int qbk, f32x4 (&L)[2][2], f32x4 (&G)[2][2], float& T) {
-        const long qrow = (bh * g.nb + (qbk < 0 ? 0 : qbk)) * 64 + 32 * r + 4 * hb;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                L[ks][u] = *reinterpret_cast<const f32x4*>(lse2 + qrow + 16 * ks + 8 * u);
-                G[ks][u] = *reinterpret_cast<const f32x4*>(delta + qrow + 16 * ks + 8 * u);
-            }
+    auto load_lg = [&](int qbk, float (&X)[2], float& T) {
+        const long qrow = (bh * g.nb + (qbk < 0 ? 0 : qbk)) * 64 + 32 * r + 8 * ((lane & 15) >> 2) + 4 * hb + (lane & 3);
+        X[0] = lse2[qrow];
+        X[1] = delta[qrow];
         T = 1.0f;
         if (q_scale != nullptr) {
             long idx = bh * g.nb + (qbk < 0 ? 0 : qbk);
@@ -218,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         }
     };
 
-    auto phase1 = [&](const uint8_t* sq, const f32x4 (&L)[2][2], const f32x4 (&G)[2][2], float tq) {
+    auto phase1 = [&](const uint8_t* sq, const float (&X)[2], float tq) {
         const uint8_t* sg = sq + kTile;
         const float cs = c * tq * sk;
         bf16x8 qa[D / 16], ga[D / 16];
@@ -237,20 +249,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[st], vf.b[st], dp, 0, 0, 0);
         }
         // element i: query 32*r + 8*(i/4) + 4*hb + i%4, key 32*kh + lane%32
+        float pv[16], ds[16];
+        bwd_static_for<0, 16>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const float lq = row_bcast<i>(X[0]);
+            const float gq = row_bcast<i>(X[1]);
+            const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lq)) : 0.0f;
+            pv[i] = pp;
+            ds[i] = pp * (dp[i] - gq) * tq;
+        });
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            float pv[8], ds[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int i = 8 * ks + t;
-                const float lq = L[ks][t >> 2][t & 3];
-                const float gq = G[ks][t >> 2][t & 3];
-                const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lq)) : 0.0f;
-                pv[t] = pp;
-                ds[t] = pp * (dp[i] - gq) * tq;
-            }
-            *reinterpret_cast<bf16x8*>(xop(r, ks, 0)) = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-            *reinterpret_cast<bf16x8*>(xop(r, ks, 1)) = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+            const int b = 8 * ks;
+            *reinterpret_cast<bf16x8*>(xop(r, ks, 0)) =
+                pack_bf16x8(pv[b], pv[b + 1], pv[b + 2], pv[b + 3], pv[b + 4], pv[b + 5], pv[b + 6], pv[b + 7]);
+            *reinterpret_cast<bf16x8*>(xop(r, ks, 1)) =
+                pack_bf16x8(ds[b], ds[b + 1], ds[b + 2], ds[b + 3], ds[b + 4], ds[b + 5], ds[b + 6], ds[b + 7]);
         }
     };
     auto phase2 = [&](const uint8_t* sq) {
@@ -283,17 +297,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
         constexpr int P = decltype(set)::value;
         wait_vmcnt<0>();
         __syncthreads();
-        load_lg(qnext, LG[1 - P][0], LG[1 - P][1], TQ[1 - P]);   // unconditional (block 0 past the end)
+        load_lg(qnext, LG[1 - P], TQ[1 - P]);         // unconditional (block 0 past the end)
         if (jj + 1 < n) copy_block(qnext, lds + (1 - P) * kSlot);
         if (qcur >= 0) {                               // uniform
-            phase1(lds + P * kSlot, LG[P][0], LG[P][1], TQ[P]);
+            phase1(lds + P * kSlot, LG[P], TQ[P]);
             __syncthreads();
             phase2(lds + P * kSlot);
         }
     };
     if (n > 0) {
         int qcur = qb_at(0);
-        load_lg(qcur, LG[0][0], LG[0][1], TQ[0]);
+        load_lg(qcur, LG[0], TQ[0]);
         copy_block(qcur, lds);
         for (int jj = 0; jj < n; jj += 2) {
             const int q1 = qb_at(jj + 1);
