@@ -95,6 +95,9 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=624,
                    help="query blocks of head 0 the oracle runs for the CPU baseline (0: skip)")
     p.add_argument("--kernels-only", action="store_true", help="skip the CPU baseline")
+    p.add_argument("--gemm-reference", action="store_true",
+                   help="only time a library bf16 GEMM (torch.matmul, 8192^3 and 16384^3): the matrix-core "
+                        "rate this box delivers to a plain GEMM, as a reference for the kernels' rates")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after timing, run one plain 256 MiB device copy (reference for counter runs)")
     return p.parse_args()
@@ -117,6 +120,9 @@ def main():
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.gemm_reference:
+        gemm_reference(dev, args.steps)
+        return
     if w.name != "wan480p":
         measure_workload(args, w, dev)
         return
@@ -322,6 +328,29 @@ def device_inputs(w, step, dev, pe):
         out.append(x.to(torch.bfloat16))
         del x
     return out
+
+
+def gemm_reference(dev, reps):
+    """Library bf16 GEMM (hipBLASLt through torch.matmul) on this machine, one JSON line per size."""
+    import torch
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+        b = torch.randn(n, n, device=dev).to(torch.bfloat16).t().contiguous()
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * n ** 3 / ms / 1e9
+        print(json.dumps({"gemm": f"bf16 {n}x{n}x{n}, torch.matmul", "ms": round(ms, 4), "tflops": round(tf, 1),
+                          "frac_of_bf16_peak": round(tf / PEAK["bf16"], 4)}), flush=True)
+        del a, b, c
 
 
 def _kernel_entry(times, flop=None, peak=None, nbytes=None):
