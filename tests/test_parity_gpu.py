@@ -415,6 +415,26 @@ def test_fp8_forward(grid, H, D):
     assert mx <= quant + BF16_MAX_ABS, (mx, quant)
 
 
+@pytest.mark.parametrize("grid,tile,D", [((1, 96, 104), (1, 8, 8), 128), ((16, 20, 24), (4, 4, 4), 64)])
+def test_fp8_forward_one_block_kernel_long_rows(grid, tile, D):
+    """FP8 Q/K through the one-query-block kernel (a 2D grid at D = 128, a video grid at
+    D = 64) with rows of more than 64 kept blocks, so that the key tile scales come from
+    several 64-entry windows: parity with the oracle's simulation of the same per-tile
+    e4m3 quantization at the bf16 tolerances."""
+    H = 1
+    q, k, v = inputs(grid, 1, H, D, amp=1.0, seed=31)
+    nb = O.num_blocks(grid, tile)
+    m = np.random.default_rng(32).random((H * nb, nb)).astype(np.float32)   # flat rows: long kept lists
+    rp, ci = O.select_blocks(m / m.sum(axis=1, keepdims=True), 99, 100)
+    assert np.diff(rp).min() > 64, np.diff(rp).min()
+    bsa, _, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=True)
+    qh, _ = O.fp8_tile_quantize(q, grid, tile)
+    kh, _ = O.fp8_tile_quantize(k, grid, tile)
+    out_s, tok_s = O.masked_attention(qh, kh, v, grid, tile, bsa.scale, rp, ci)
+    mx_s, mean_s = output_errors(o, out_s, tok_s)
+    assert mx_s <= BF16_MAX_ABS and mean_s <= BF16_MEAN_ABS, (mx_s, mean_s)
+
+
 @pytest.mark.parametrize("grid", [(8, 12, 16), (12, 16, 20)])
 def test_fp8_forward_unquantized_bar(grid):
     """FP8 Q/K on inputs made as for the 720p workload (amplitude 1, noise 1, head size
