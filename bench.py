@@ -211,6 +211,8 @@ def main():
         kk["traffic"] = measured_traffic(name)
         if name in ("sparse_fwd", "block_mass"):
             kk.update(traffic_fields(name, w.name, B, H, D, bsa.npad, bsa.nb, bsa.R, nnz))
+        elif kk["traffic"] is not None:                # HBM-bound: counter bytes over the timed call
+            kk["achieved_GBps_measured"] = round(kk["traffic"] / kk["ms"] / 1e6, 1)
     dominant = max(kernels, key=lambda n: kernels[n]["ms"])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": round(dk["achieved"], 2),
@@ -480,6 +482,15 @@ def measure_workload(args, w, dev):
     for name in ("block_mass", "sparse_fwd", "sparse_fwd_fp8"):
         if name in kern:
             kern[name].update(traffic_fields(name, w.name, B, H, D, bsa.npad, bsa.nb, bsa.R, nnz))
+    for name in ("tile_qkv", "select", "untile"):       # HBM-bound: counter bytes over the timed call
+        if name in kern:
+            tb = measured_traffic(name, w.name)
+            kern[name]["hbm_bytes_measured"] = tb
+            kern[name]["measured_GBps"] = None if tb is None else round(tb / kern[name]["median"] / 1e6, 1)
+    eff_flop = 4.0 * bsa.N * bsa.N * D * H * B          # dense-equivalent over real tokens
+    for name in ("sparse_fwd", "sparse_fwd_fp8"):
+        if name in kern:
+            kern[name]["effective_tflops"] = round(eff_flop / kern[name]["median"] / 1e9, 2)
     out = {
         "metric": f"kept-block TFLOP/s per call, {w.name}",
         "value": round(value, 2),
