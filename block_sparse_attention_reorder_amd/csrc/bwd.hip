@@ -348,6 +348,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     constexpr int kDT = D / 32;
     static_assert(kDT * 16 * 64 * 4 <= kSlot, "reduction buffer fits a slot");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlot];   // two slots
+    // bias tiles: entry ((code * 2 + kh) * 2 + hb) * 16 + i is 0 when key 32 kh + 8 (i / 4)
+    // + 4 hb + i % 4 of a block with edge code `code` is real, else -inf; used as the
+    // C operand that starts the score products, so padding keys get p = 0 without any
+    // per-score masking
+    __shared__ __attribute__((aligned(16))) float sbias[8 * 2 * 2 * 16];
 
     const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,8 +372,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     // dQ = dS K-hat, each key block's dS
     const float tq = q_scale != nullptr ? q_scale[row] : 1.0f;
     const int trb = tr_base<D>(32 * kh, lane);
-    EdgeSlots edge;
-    edge.init(g, lane);
+    for (int x = tid; x < 8 * 64; x += 256) {
+        const int code = x >> 6, kx = (x >> 5) & 1, hx = (x >> 4) & 1, i = x & 15;
+        const int key = 32 * kx + 8 * (i >> 2) + 4 * hx + (i & 3);
+        const int plane = g.th * g.tw;
+        const int et = key / plane, eh = (key - et * plane) / g.tw, ew = key - et * plane - eh * g.tw;
+        const int ok = (et < g.T - (g.nt - 1) * g.tt ? 1 : 0) | (eh < g.Hg - (g.nh - 1) * g.th ? 2 : 0) |
+                       (ew < g.Wg - (g.nw - 1) * g.tw ? 4 : 0);
+        sbias[x] = ((ok | ~code) & 7) == 7 ? 0.0f : -INFINITY;
+    }
+    // (the first iteration's barrier precedes every read of the table)
 
     f32x16 acc[kDT];
 #pragma unroll
@@ -425,8 +438,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
         const uint8_t* sv = sk + kTile;
         const int code = icur >> kEdgeShift;
         const float cs = c * tq * tk;
-        const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
-        const uint32_t m32 = (uint32_t)(vm >> (32 * kh + 4 * hb));
         bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
@@ -436,8 +447,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x16 s, dp;
+        {
+            const float* bt = sbias + ((code * 2 + kh) * 2 + hb) * 16;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(bt + 4 * j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[4 * j + e] = v[e];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp[i] = 0.0f;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf.b[st], s, 0, 0, 0);
@@ -457,8 +477,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int i = 8 * ks + t;
-                const float x = keep_or_neg_inf(s[i], m32, 8 * (i >> 2) + (i & 3));
-                const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(x, cs, -lq));
+                const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lq));
                 ds[t] = pp * (dp[i] - gq) * tk;
             }
             const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
