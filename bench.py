@@ -96,8 +96,8 @@ def parse():
                    help="query blocks of head 0 the oracle runs for the CPU baseline (0: skip)")
     p.add_argument("--kernels-only", action="store_true", help="skip the CPU baseline")
     p.add_argument("--gemm-reference", action="store_true",
-                   help="only time a library bf16 GEMM (torch.matmul, 8192^3 and 16384^3): the matrix-core "
-                        "rate this box delivers to a plain GEMM, as a reference for the kernels' rates")
+                   help="only time a library bf16 GEMM (torch.matmul, 8192^3 and 16384^3) and the library's dense "
+                        "flash attention at the 480p shape: references for the kernels' rates")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after timing, run one plain 256 MiB device copy (reference for counter runs)")
     return p.parse_args()
@@ -333,7 +333,8 @@ def device_inputs(w, step, dev, pe):
 
 
 def gemm_reference(dev, reps):
-    """Library bf16 GEMM (hipBLASLt through torch.matmul) on this machine, one JSON line per size."""
+    """Library bf16 GEMM (hipBLASLt through torch.matmul) and dense flash attention on this machine,
+    one JSON line each."""
     import torch
     for n in (8192, 16384):
         a = torch.randn(n, n, device=dev).to(torch.bfloat16)
@@ -353,6 +354,30 @@ def gemm_reference(dev, reps):
         print(json.dumps({"gemm": f"bf16 {n}x{n}x{n}, torch.matmul", "ms": round(ms, 4), "tflops": round(tf, 1),
                           "frac_of_bf16_peak": round(tf / PEAK["bf16"], 4)}), flush=True)
         del a, b, c
+    # the library's dense FlashAttention at the 480p attention shape (12 heads, 32,760
+    # tokens, head size 128, bf16), flash backend only (no fallback to other paths)
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    B, H, N, D = 1, 12, 32760, 128
+    q, k, v = (torch.randn(B, H, N, D, device=dev).to(torch.bfloat16) for _ in range(3))
+    try:
+        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+            fn = lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 4.0 * N * N * D * H * B / ms / 1e9
+        print(json.dumps({"attention": f"dense bf16 B={B} H={H} N={N} D={D}, torch scaled_dot_product_attention "
+                                       f"(flash backend)", "ms": round(ms, 4), "tflops": round(tf, 1),
+                          "frac_of_bf16_peak": round(tf / PEAK["bf16"], 4)}), flush=True)
+    except RuntimeError as err:
+        print(json.dumps({"attention": "flash backend unavailable", "error": str(err)[:200]}), flush=True)
 
 
 def _kernel_entry(times, flop=None, peak=None, nbytes=None):
