@@ -415,6 +415,28 @@ def test_fp8_forward(grid, H, D):
     assert mx <= quant + BF16_MAX_ABS, (mx, quant)
 
 
+def test_paired_forward_at_the_block_limit():
+    """bf16, D = 128 on a ragged video grid with exactly 4096 blocks (the most the paired
+    kernel's membership bitmaps hold): rows of about 48 random blocks, every row keeping the
+    last block, so the union walk reads the last bitmap words. Sampled query blocks (the
+    first and last pairs, edge tiles, seeded others) within the bf16 bounds of the oracle."""
+    grid, tile, H, D = (63, 63, 64), (4, 4, 4), 1, 128
+    nb = O.num_blocks(grid, tile)
+    assert nb == 4096
+    q, k, v = inputs(grid, 1, H, D, amp=1.0, seed=41)
+    rng = np.random.default_rng(42)
+    rows = [np.unique(np.concatenate([rng.choice(nb - 1, size=47, replace=False), [nb - 1]])) for _ in range(nb)]
+    rp = np.zeros(nb + 1, np.int32)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    ci = np.concatenate(rows).astype(np.int32)
+    bsa, _, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    blocks = sorted({0, 1, 2, 3, nb - 2, nb - 1, 255, 3840, 4000} | set(rng.choice(nb, size=6, replace=False).tolist()))
+    out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci, qblocks=np.array(blocks, np.int32))
+    mx, mean = output_errors(o, out, tok)
+    print(f"4096 blocks: sampled max|err| {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+
+
 @pytest.mark.parametrize("grid,tile,D", [((1, 96, 104), (1, 8, 8), 128), ((16, 20, 24), (4, 4, 4), 64)])
 def test_fp8_forward_one_block_kernel_long_rows(grid, tile, D):
     """FP8 Q/K through the one-query-block kernel (a 2D grid at D = 128, a video grid at
