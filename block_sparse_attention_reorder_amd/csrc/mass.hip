@@ -53,6 +53,7 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
     static_assert(kKBytes % 4096 == 0, "copies split into whole kilobytes");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kKBytes];
     __shared__ float lse_q[2][64];
+    __shared__ __attribute__((aligned(16))) float kbias[8 * 2 * 2 * 16];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -68,8 +69,16 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
     const long qblk0 = bh * npad + (long)qb * kBlock;
     // workspace [pair slot][sel][nb][64]: block log-sum-exp of each query
     float* wrow = ws + ((p - p_begin) * 2 + sel) * (long)g.nb * kBlock;
-    EdgeSlots edge;
-    edge.init(g, lane);
+    for (int x = threadIdx.x; x < 8 * 64; x += kMassThreads) {
+        const int code = x >> 6, hf = (x >> 5) & 1, kt = (x >> 4) & 1, i = x & 15;
+        const int key = 32 * kt + 8 * (i >> 2) + 4 * hf + (i & 3);
+        const int plane = g.th * g.tw;
+        const int et = key / plane, eh = (key - et * plane) / g.tw, ew = key - et * plane - eh * g.tw;
+        const int ok = (et < g.T - (g.nt - 1) * g.tt ? 1 : 0) | (eh < g.Hg - (g.nh - 1) * g.th ? 2 : 0) |
+                       (ew < g.Wg - (g.nw - 1) * g.tw ? 4 : 0);
+        kbias[x] = ((ok | ~code) & 7) == 7 ? 0.0f : -0x1p100f;
+    }
+    // (read only after the prologue's barrier)
 
     KHalf<D, false> qop;
     if (hasrow) {
@@ -146,32 +155,20 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
         if (hasrow && half == 0) wrow[(long)kb * kBlock + 32 * qh + col] = m + __builtin_amdgcn_logf(sum);
     };
 
-    // Padding keys of an edge block are excluded inside the products: one extra product
-    // per key tile adds bias(key) * 1 to every query's score, with bias = -2^100 for a
-    // padding key and 0 for a real one (A holds the bias in k slot 0 of the key's row,
-    // B a one in k slot 0 of every query column; all other slots are 0). A real key's
-    // score gains exactly +0, so it is bit-identical to the unbiased product; a padding
-    // key's score becomes -2^100 and its term 2^(t - m) underflows to 0.
-    bf16x8 one_k0;
+    // Padding keys of an edge block are excluded by the C operand that starts the score
+    // products: a tile of 0 (real key) or -2^100 (padding key) from a table per edge code,
+    // so a real key's score is bit-identical to the unbiased product and a padding key's
+    // term 2^(t - m) underflows to 0. Entry ((code * 2 + half) * 2 + kt) * 16 + i is for
+    // key 32 kt + 8 (i / 4) + 4 half + i % 4.
+    auto load_block_bias = [&](int code, f32x16 (&sn)[2]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) one_k0[e] = (__bf16)0.0f;
-    if (half == 0) one_k0[0] = (__bf16)1.0f;
-    auto key_bias = [&](int code, bf16x8 (&bias)[2]) {
-        const uint64_t vm = code == 0 ? ~0ull : edge.mask(code);
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(kbias + ((code * 2 + half) * 2 + kt) * 16 + 4 * j4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bias[kt][e] = (__bf16)0.0f;
-            const bool real = (vm >> (32 * kt + col)) & 1ull;
-            if (half == 0 && !real) bias[kt][0] = (__bf16)-0x1p100f;
-        }
-    };
-    auto bias_products = [&](f32x16 (&sn)[2], const bf16x8 (&bias)[2]) {
-        f32x16 z;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = 0.0f;
-        sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias[0], one_k0, z, 0, 0, 0);
-        sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias[1], one_k0, z, 0, 0, 0);
+                for (int e = 0; e < 4; ++e) sn[kt][4 * j4 + e] = v4[e];
+            }
     };
 
     // Main section of block j (scores s) with the products of block j+1 (into sn, with
@@ -180,7 +177,7 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
     // might write the same bytes has to wait for it), then each product of block j+1 is
     // followed by exponentials of block j. Returns the sum of block j's terms against
     // the current reference.
-    auto main_ordered = [&](int j, const f32x16 (&s)[2], f32x16 (&sn)[2], const bf16x8 (&bias)[2]) {
+    auto main_ordered = [&](int j, const f32x16 (&s)[2], f32x16 (&sn)[2], int code_next) {
         const float nref = m == -INFINITY ? 0.0f : -m;
         const uint8_t* kst = lds + ((j + 1) & 1) * kKBytes;
         // the K(j+1) operands stream in two steps ahead of their products, which keeps
@@ -195,7 +192,7 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
         __builtin_amdgcn_sched_barrier(0);
         copy_k(j + 2, j & 1);
         __builtin_amdgcn_sched_barrier(0);
-        bias_products(sn, bias);
+        load_block_bias(code_next, sn);
         // 2 * D/16 products of block j+1; the 32 exponentials of block j spread over them
         constexpr int kProducts = 2 * (D / 16);
         constexpr int kPerProduct = (32 + kProducts - 1) / kProducts;
@@ -230,9 +227,7 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
     {
         lds_khalf<D, false>(k0, lds, 0, lane);
         lds_khalf<D, false>(k1, lds, 1, lane);
-        bf16x8 bias[2];
-        key_bias(edge_code(), bias);
-        bias_products(sa, bias);
+        load_block_bias(edge_code(), sa);
         next_coords();                                       // the coordinates run one block ahead
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
@@ -241,11 +236,10 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
         }
     }
     auto step = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2]) {
-        bf16x8 bias[2];
-        key_bias(edge_code(), bias);                         // of block j+1
+        const int code_next = edge_code();                   // of block j+1
         // K(j+1) landed; every wave is done reading K(j) (its slot is refilled below)
         copies_landed_barrier();
-        const float sum = main_ordered(j, s, sn, bias);
+        const float sum = main_ordered(j, s, sn, code_next);
         finish(s, j, sum);
         next_coords();
     };
