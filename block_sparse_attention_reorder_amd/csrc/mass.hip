@@ -18,8 +18,9 @@
 // block. The K tile of each block is copied once per workgroup into a two-slot LDS
 // ring with direct global-to-LDS loads issued from inline asm (so that the compiler
 // adds no wait for them before reads of the other slot), and each wave streams the
-// operands two steps ahead of their products: 156 registers, three workgroups per
-// CU. Every wave reads the tile in the lane order of the MFMA operand (QK tiled
+// operands one step ahead of their products: 126 registers, four workgroups per
+// CU. Padding keys of edge blocks get -2^100 from the bias tile that starts each score
+// product. Every wave reads the tile in the lane order of the MFMA operand (QK tiled
 // layout). Scores use the transposed MFMA form of the sparse
 // forward (S^T = K * Q^T, v_mfma_f32_32x32x16_bf16), so a lane holds 32 of its
 // query's 64 block scores and the block sums are in-lane plus one swap of the wave
@@ -41,7 +42,7 @@ constexpr int kMassThreads = 256;
 constexpr float kMassSumLimit = 18446744073709551616.0f;   // 2^64
 
 template <int D>
-__global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __restrict__ q,
+__global__ __launch_bounds__(kMassThreads, 4) void k_block_mass(const __bf16* __restrict__ q,
                                                                 const __bf16* __restrict__ k,
                                                                 Geom g, long p_begin, long p_count,
                                                                 float scale_log2,
@@ -180,9 +181,9 @@ __global__ __launch_bounds__(kMassThreads, 3) void k_block_mass(const __bf16* __
     auto main_ordered = [&](int j, const f32x16 (&s)[2], f32x16 (&sn)[2], int code_next) {
         const float nref = m == -INFINITY ? 0.0f : -m;
         const uint8_t* kst = lds + ((j + 1) & 1) * kKBytes;
-        // the K(j+1) operands stream in two steps ahead of their products, which keeps
-        // the kernel within 168 registers (three workgroups per CU)
-        constexpr int kAheadSt = 2;
+        // the K(j+1) operands stream in one step ahead of their products, which keeps
+        // the kernel within 128 registers (four workgroups per CU)
+        constexpr int kAheadSt = 1;
         auto kread = [&](int st) {
             k0.b[st] = *reinterpret_cast<const bf16x8*>(kst + st * 1024 + 16 * lane);
             k1.b[st] = *reinterpret_cast<const bf16x8*>(kst + (D / 16 + st) * 1024 + 16 * lane);
@@ -300,11 +301,11 @@ void launch_block_mass(const void* q, const void* k, int B, int H, int D, const 
     long chunk = (long)(ws_bytes / mass_workspace_bytes_min(g.nb));   // >= 1, checked by the caller
     if (chunk < P) {
         // a workspace smaller than the whole grid: launch whole waves of workgroups
-        // (three per compute unit), so that no launch but the last ends on a partial wave
+        // (four per compute unit), so that no launch but the last ends on a partial wave
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
-            const long wave = 3L * cus;
+            const long wave = 4L * cus;
             if (chunk >= wave) chunk -= chunk % wave;
         }
     }
