@@ -13,7 +13,9 @@
 // product of a one-block workgroup). Each wave takes 32 query rows of one of the two
 // blocks against all 64 keys of every union block; blocks its own query block does
 // not keep, and padding keys, are excluded by a -inf bias tile that starts the QK^T
-// chain. See the comment above the kernel.
+// chain. The bf16 call without lse takes queries pre-scaled to base-2 units (rounded to
+// bf16 once) and shifted scores, with no scale-and-shift step per score. See the
+// comment above the kernel.
 //
 // k_sparse_attn (D = 64, blocks with counted keys, 2D grids, grids over 4096 blocks):
 // a workgroup of four waves owns one query block (64 rows) of one (batch, head) and walks the
@@ -256,11 +258,20 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
 // the wave's own query block does not keep contributes nothing: its scores are -inf.
 //
 // Key masking costs no vector instruction: every QK^T chain starts from a bias tile
-// read from a small LDS table instead of from zero, 0 for a real key and -inf for a
-// padding key of an edge block (or for every key of a block the wave does not keep).
-// The table holds, per edge code (and the "nothing" code), the 2 x 16 accumulator
-// values of each lane half; the tile for block u+2 is read at the end of block u's
-// section into the registers that hold its scores two sections later.
+// instead of from zero, 0 for a real key and -inf for a padding key of an edge block
+// (or for every key of a block the wave does not keep). A small LDS table holds, per
+// edge code (and the "nothing" code), the 2 x 16 accumulator values of each lane half.
+//
+// Two forms for bf16. The inference form (SHIFT; the call without lse) multiplies the
+// queries by scale * log2(e) once and rounds them to bf16, so the products give base-2
+// scores; its C tiles also carry -r, the running reference of the online softmax, so
+// the scores come out shifted and go straight into the exponentials (no scale-and-shift
+// instruction per score). Those tiles stay in registers and are re-read from the table
+// only when the edge code changes between union blocks (a run of block columns shares
+// it) and moved with r when the reference grows. The form that also returns lse (for a
+// backward pass, which recomputes exact scores against it) and the e4m3 form keep the
+// float32 scale-and-shift per score and read each block's tile at the end of block
+// u-1's section into the registers that hold its scores one section later.
 // Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so that every
 // index into a section's register arrays is a constant whatever the unroller decides.
 template <int B, int E, class F>
@@ -298,18 +309,22 @@ __device__ __attribute__((always_inline)) inline void load_bias(f32x16 (&t)[2], 
 }
 
 // Main section of union block u for this wave: the QK^T of block u+1 (two 32-key
-// halves, 16 products, starting from its bias tile in sn) and the exponentials and
-// P*V of block u (16 products), in a fixed issue order. K(u+1) and V(u) operands are
-// read from LDS four products ahead of use; the NC copies into LDS (inline asm, so
-// that no read waits for them) go one after each of the first NC products. The 96
-// vector steps of the softmax (per pair of scores: two scale-and-shift FMAs, two
-// exponentials, one bf16 pack, one dot into the row sum) run as a stream, three per
-// product after twelve up front. At the end, s receives the bias tile of block u+2.
-template <bool FP8, int NC, class Copy>
+// halves) and the exponentials and P*V of block u (16 products), in a fixed issue
+// order. Each QK^T chain starts from a tile of the block's bias: with SHIFT the tile
+// ct[kt], which also carries -r and so shifts the scores to the reference r; otherwise
+// the tile already in sn (read at the end of the previous section). K(u+1) and V(u)
+// operands are read from LDS four products ahead of use; the NC copies into LDS
+// (inline asm, so that no read waits for them) go one after each of the first NC
+// products. The vector steps of the softmax (per pair of scores: two exponentials,
+// one bf16 pack, one dot into the row sum, and without SHIFT first two scale-and-shift
+// FMAs; with SHIFT the scores already sit in base-2 units relative to r) run as a
+// stream after a few up front. Without SHIFT, s receives the bias tile of block u+2 at
+// the end.
+template <bool FP8, bool SHIFT, int NC, class Copy>
 __device__ __attribute__((always_inline)) inline void pair_main(
     const uint8_t* kst, const uint8_t* vst, int lane, int half, const KHalf<128, FP8>& q, f32x16 (&acc)[4],
-    f32x16 (&s)[2], f32x16 (&sn)[2], float c, float nref, float& l, float& smax, const float* bias_table,
-    int bias_next, Copy&& copy_one) {
+    f32x16 (&s)[2], f32x16 (&sn)[2], const f32x16 (&ct)[2], float c, float nref, float& l, float& smax,
+    const float* bias_table, int bias_next, Copy&& copy_one) {
     // products of the next block's QK^T: 16 bf16 32x32x16, or 4 e4m3 32x32x64
     constexpr int kQK = FP8 ? 4 : 16;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -343,7 +358,7 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             sn[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[n & 3], q.f[st], sn[kt], 0, 0, 0, 0, 0, 0);
         } else {
             const int kt = n >> 3, st = n & 7;
-            sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n & 7], q.b[st], sn[kt], 0, 0, 0);
+            sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n & 7], q.b[st], (SHIFT && st == 0) ? ct[kt] : sn[kt], 0, 0, 0);
         }
     };
     auto PV = [&](int n) {
@@ -355,8 +370,8 @@ __device__ __attribute__((always_inline)) inline void pair_main(
     // vector step k of the softmax stream (k = 0..95)
     auto VS = [&](int k) {
         const int pr = k / 6, op = k % 6, kt = pr >> 3, i = 2 * (pr & 7);
-        if (op == 0) pf[kt][i] = __builtin_fmaf(s[kt][i], c, nref);
-        else if (op == 1) pf[kt][i + 1] = __builtin_fmaf(s[kt][i + 1], c, nref);
+        if (op == 0) pf[kt][i] = SHIFT ? s[kt][i] : __builtin_fmaf(s[kt][i], c, nref);
+        else if (op == 1) pf[kt][i + 1] = SHIFT ? s[kt][i + 1] : __builtin_fmaf(s[kt][i + 1], c, nref);
         else if (op == 2) pf[kt][i] = __builtin_amdgcn_exp2f(pf[kt][i]);
         else if (op == 3) pf[kt][i + 1] = __builtin_amdgcn_exp2f(pf[kt][i + 1]);
         else if (op == 4) {
@@ -410,7 +425,7 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             static_for<12 + 3 * n, (15 + 3 * n < 96 ? 15 + 3 * n : 96)>([&](auto kc) { VS(decltype(kc)::value); });
             if constexpr (n >= 20 && n < 24) MX(0, n - 20);
             if constexpr (n >= 24 && n < 28) MX(1, n - 24);
-            if constexpr (n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
+            if constexpr (!SHIFT && n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
             if constexpr (n == 30) l += wave_add32(rs[0] + rs[1]);
             if constexpr (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
             FPSA_SB;
@@ -440,7 +455,35 @@ __device__ __attribute__((always_inline)) inline float pair_enter(float smax, fl
     return m == -INFINITY ? 0.0f : -m;
 }
 
-template <bool FP8>
+// The same for scores that arrive in base-2 units already shifted by the reference r (r = m, or 0 before any key): smax and the scores s of the block are
+// relative to r. Moving the reference shifts s and the C tiles ct (which carry -r) with
+// it.
+__device__ __attribute__((always_inline)) inline void pair_enter_shifted(float smax, f32x16 (&acc)[4],
+                                                                         f32x16 (&s)[2], f32x16 (&ct)[2], float& m,
+                                                                         float& l) {
+    const bool grow = smax > (m == -INFINITY ? -INFINITY : kRescaleSlack);
+    if (__ballot(grow)) {
+        const float r = m == -INFINITY ? 0.0f : m;
+        const float mnew = r + smax;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;   // 0 when m = -inf
+        const float d = grow ? smax : 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+        l *= alpha;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[kt][i] -= d;
+                ct[kt][i] -= d;
+            }
+        if (grow) m = mnew;
+    }
+}
+
+template <bool FP8, bool SHIFT>
 __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
@@ -492,6 +535,16 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     // key tile scale multiplies it per block
     const float cq = FP8 ? scale_log2 * (hasrow ? q_scale[r] : 1.0f) : scale_log2;
     const float* ksc_row = FP8 ? k_scale + bh * g.nb : nullptr;
+    // SHIFT (bf16 only): the base-2 softmax scale goes into the query operand (one more
+    // rounding to bf16, at most 2^-8 relative per element), so that the products give
+    // base-2 scores and the exponentials need no scale-and-shift step
+    static_assert(!(FP8 && SHIFT), "e4m3 scores are scaled per key block");
+    if constexpr (SHIFT) {
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q.b[j][e] = (__bf16)((float)q.b[j][e] * scale_log2);
+    }
 
     // bias table: entry ((code * 2 + half) * 2 + kt) * 16 + i is 0 when key 32 kt + 8 (i / 4)
     // + 4 half + i % 4 of a block with edge code `code` is real, else -inf (code 8: none)
@@ -586,6 +639,12 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
     float m = -INFINITY, l = 0.0f;
+    // SHIFT: C tiles of the QK^T chains, the bias tile of edge code `ccode` plus -r, r
+    // the reference the scores are shifted by (m once a key has been seen, 0 before).
+    // Neighbouring union blocks mostly share their code (a run of block columns), so
+    // the tiles are re-read from the table only when the code changes.
+    f32x16 ct[2];
+    int ccode = -1;
 
     int inf, infn;
     bool mine, minen;
@@ -601,7 +660,19 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
         gen(inf2, mine2);
         const float ksc2 = kscale(inf2);
         const float c = cq * ksc;
-        const float nref = pair_enter(smax, c, acc, m, l);
+        float nref = 0.0f;
+        if constexpr (SHIFT) pair_enter_shifted(smax, acc, s, ct, m, l);
+        else nref = pair_enter(smax, c, acc, m, l);
+        const int code1 = bias_code(infn, minen);
+        if (SHIFT && code1 != ccode) {
+            ccode = code1;
+            load_bias(ct, bias_table, code1, half);
+            const float nr = m == -INFINITY ? 0.0f : -m;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) ct[kt][i] += nr;
+        }
         copies_landed_barrier();                          // K(u+1), V(u) landed; slots of u-1 free
         const uint8_t* kst = kring + (par ^ 1) * kKBytes;
         const uint8_t* vst = vring + par * kVBytes;
@@ -609,7 +680,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
             if (i < kKChunks) copy_k(inf2, kring + par * kKBytes, i);
             else copy_v(infn, vring + (par ^ 1) * kVBytes, i - kKChunks);
         };
-        pair_main<FP8, kKChunks + kVChunks>(kst, vst, lane, half, q, acc, s, sn, c, nref, l, smax, bias_table,
+        pair_main<FP8, SHIFT, kKChunks + kVChunks>(kst, vst, lane, half, q, acc, s, sn, ct, c, nref, l, smax, bias_table,
                                              bias_code(inf2, mine2), copy_one);
         inf = infn;
         mine = minen;
@@ -629,8 +700,15 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
 #pragma unroll
         for (int i = 0; i < kVChunks; ++i) copy_v(inf, vring, i);
         copies_landed_barrier();                          // K(0), V(0), K(1) landed
-        load_bias(s0, bias_table, bias_code(inf, mine), half);
-        load_bias(s1, bias_table, bias_code(infn, minen), half);
+        if constexpr (!SHIFT) {
+            load_bias(s0, bias_table, bias_code(inf, mine), half);
+            load_bias(s1, bias_table, bias_code(infn, minen), half);
+        } else {
+            ccode = bias_code(inf, mine);
+            load_bias(ct, bias_table, ccode, half);        // r = 0 so far
+            s0[0] = ct[0];
+            s0[1] = ct[1];
+        }
         {
             KHalf<D, FP8> k0, k1;
             lds_khalf<D, FP8>(k0, kring, 0, lane);
@@ -708,12 +786,18 @@ void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, co
     // list: those take the one-block kernel.
     if (D == 128 && kcount == nullptr && g.nb <= kMaxBitmapWords * 32 && g.T > 1) {
         const long P = (long)B * H * ((g.nb + 1) / 2);
+        // bf16 without lse (inference) pre-scales the queries; with lse, whose consumer
+        // (the backward) recomputes exact scores against it, the scores are scaled in
+        // float32
         if (fp8)
-            k_sparse_attn_pair<true><<<(unsigned)P, kPairThreads, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx,
-                                                                           g, P, sl2, out, lse, o32);
+            k_sparse_attn_pair<true, false><<<(unsigned)P, kPairThreads, 0, st>>>(
+                q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, P, sl2, out, lse, o32);
+        else if (lse == nullptr)
+            k_sparse_attn_pair<false, true><<<(unsigned)P, kPairThreads, 0, st>>>(
+                q, k, vt, nullptr, nullptr, row_ptr, col_idx, g, P, sl2, out, lse, o32);
         else
-            k_sparse_attn_pair<false><<<(unsigned)P, kPairThreads, 0, st>>>(q, k, vt, nullptr, nullptr, row_ptr, col_idx,
-                                                                            g, P, sl2, out, lse, o32);
+            k_sparse_attn_pair<false, false><<<(unsigned)P, kPairThreads, 0, st>>>(
+                q, k, vt, nullptr, nullptr, row_ptr, col_idx, g, P, sl2, out, lse, o32);
         return;
     }
     if (D == 128) {

@@ -260,6 +260,9 @@ def test_block_mass_matches_oracle(grid, H, D, amp):
 # --------------------------------------------------------------------------- attention
 
 def _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=False):
+    """The forward without lse (the inference call: bf16 on the paired kernel takes
+    pre-scaled queries there) and again with lse (scores scaled in float32). Returns
+    (bsa, tiled output, raster output, lse, raster output of the call with lse)."""
     bsa = BlockSparseAttention(grid, tile, 1, H, D)
     vt = bsa.tile_vt(dev(v, torch.bfloat16))
     csr = Csr(dev(rp, torch.int32), dev(ci if len(ci) else np.zeros(1, np.int32), torch.int32))
@@ -267,11 +270,14 @@ def _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=False):
     if fp8:
         qt, qs = bsa.tile_fp8(dev(q, torch.bfloat16))
         kt, ks = bsa.tile_fp8(dev(k, torch.bfloat16))
-        ot = bsa.forward(qt, kt, vt, csr, q_scale=qs, k_scale=ks, lse=lse)
+        kw = dict(q_scale=qs, k_scale=ks)
     else:
         qt, kt = bsa.tile_qk(dev(q, torch.bfloat16)), bsa.tile_qk(dev(k, torch.bfloat16))
-        ot = bsa.forward(qt, kt, vt, csr, lse=lse)
-    return bsa, ot, bsa.untile(ot, torch.float32).cpu().numpy(), lse.cpu().numpy()
+        kw = {}
+    ot = bsa.forward(qt, kt, vt, csr, **kw)
+    ol = bsa.forward(qt, kt, vt, csr, lse=lse, **kw)
+    raster = lambda t: bsa.untile(t, torch.float32).cpu().numpy()
+    return bsa, ot, raster(ot), lse.cpu().numpy(), raster(ol)
 
 
 @pytest.mark.parametrize("grid,H,D", RAGGED)
@@ -282,10 +288,11 @@ def test_all_blocks_forward_equals_dense_attention(grid, H, D):
     R = H * nb
     rp = np.arange(0, R * nb + 1, nb, dtype=np.int32)
     ci = np.tile(np.arange(nb, dtype=np.int32), R)
-    bsa, ot, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    bsa, ot, o, _, o_l = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
     dense = O.dense_attention(q, k, v, bsa.scale)
-    err = np.abs(o.astype(np.float64) - dense)
-    assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS, (err.max(), err.mean())
+    for x in (o, o_l):
+        err = np.abs(x.astype(np.float64) - dense)
+        assert err.max() <= BF16_MAX_ABS and err.mean() <= BF16_MEAN_ABS, (err.max(), err.mean())
     # padding rows of the tiled output are zero
     _, slot = O.token_blocks(grid, tile)
     pad = np.setdiff1d(np.arange(bsa.npad), slot)
@@ -301,13 +308,14 @@ def test_sparse_forward_matches_masked_oracle(grid, H, D, num, den):
     m = synth.random_mass_rows(H * nb, nb, seed=nb + H, tie_frac=0.1, zero_frac=0.2)
     m[0] = 0.0                                      # one query block with no kept key
     rp, ci = O.select_blocks(m, num, den)
-    bsa, ot, o, lse = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    bsa, ot, o, lse, o_l = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
     out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci)
-    mx, mean = output_errors(o, out, tok)
-    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    for x in (o, o_l):
+        mx, mean = output_errors(x, out, tok)
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
     # the empty row: zero output, lse = -inf
     t0 = tok[0, 0, 0][tok[0, 0, 0] >= 0]
-    assert np.all(o[0, t0, 0, :] == 0)
+    assert np.all(o[0, t0, 0, :] == 0) and np.all(o_l[0, t0, 0, :] == 0)
     _, slot = O.token_blocks(grid, tile)
     assert np.all(np.isneginf(lse[0, 0, slot[t0]]))
     # lse of the other rows against a float64 library logsumexp over allowed keys; the
@@ -333,7 +341,7 @@ def test_image_grid_forward_matches_masked_oracle(grid, H, D):
     nb = O.num_blocks(grid, tile)
     m = synth.random_mass_rows(H * nb, nb, seed=nb + 7 * H, tie_frac=0.1, zero_frac=0.2)
     rp, ci = O.select_blocks(m, 9, 10)
-    bsa, ot, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    bsa, ot, o, _, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
     out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci)
     mx, mean = output_errors(o, out, tok)
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
@@ -347,8 +355,8 @@ def test_forward_skips_out_of_range_blocks():
     ci_bad = np.array([1, 99, 5, -1, 2, 7, nb], np.int32)
     ci_ok = np.array([1, 5, 2, 7], np.int32)
     rp_ok = np.array([0, 2, 2, 2, 4, 4, 4, 4, 4][: nb + 1], np.int32)
-    bsa, _, o_bad, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci_bad)
-    _, _, o_ok, _ = _run_forward(q, k, v, grid, tile, H, D, rp_ok, ci_ok)
+    bsa, _, o_bad, _, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci_bad)
+    _, _, o_ok, _, _ = _run_forward(q, k, v, grid, tile, H, D, rp_ok, ci_ok)
     assert np.array_equal(o_bad, o_ok)
     # and against the oracle under the same CSR, out-of-range entries included
     out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci_bad)
@@ -379,13 +387,14 @@ def test_forward_odd_block_counts_repeats_and_unsorted_rows(grid, H):
         rows_bad.append(bad)
     rp_bad = np.concatenate([[0], np.cumsum([len(x) for x in rows_bad])]).astype(np.int32)
     ci_bad = np.array([x for row in rows_bad for x in row], np.int32)
-    bsa, ot, o, lse = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
-    _, ot_bad, o_bad, lse_bad = _run_forward(q, k, v, grid, tile, H, D, rp_bad, ci_bad)
+    bsa, ot, o, lse, o_l = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    _, ot_bad, o_bad, lse_bad, o_l_bad = _run_forward(q, k, v, grid, tile, H, D, rp_bad, ci_bad)
     assert torch.equal(ot.view(torch.int16), ot_bad.view(torch.int16))
-    assert np.array_equal(lse, lse_bad)
+    assert np.array_equal(o_l, o_l_bad) and np.array_equal(lse, lse_bad)
     out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp_bad, ci_bad)
-    mx, mean = output_errors(o_bad, out, tok)
-    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    for x in (o_bad, o_l_bad):
+        mx, mean = output_errors(x, out, tok)
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
     _, slot = O.token_blocks(grid, tile)
     blk, _ = O.token_blocks(grid, tile)
     last = np.where(blk == nb - 1)[0]
@@ -403,7 +412,7 @@ def test_fp8_forward(grid, H, D):
     nb = O.num_blocks(grid, tile)
     m = synth.random_mass_rows(H * nb, nb, seed=5)
     rp, ci = O.select_blocks(m, 9, 10)
-    bsa, _, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=True)
+    bsa, _, o, _, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=True)
     qh, _ = O.fp8_tile_quantize(q, grid, tile)
     kh, _ = O.fp8_tile_quantize(k, grid, tile)
     out_s, tok_s = O.masked_attention(qh, kh, v, grid, tile, bsa.scale, rp, ci)
@@ -429,12 +438,13 @@ def test_paired_forward_at_the_block_limit():
     rp = np.zeros(nb + 1, np.int32)
     rp[1:] = np.cumsum([len(r) for r in rows])
     ci = np.concatenate(rows).astype(np.int32)
-    bsa, _, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
+    bsa, _, o, _, o_l = _run_forward(q, k, v, grid, tile, H, D, rp, ci)
     blocks = sorted({0, 1, 2, 3, nb - 2, nb - 1, 255, 3840, 4000} | set(rng.choice(nb, size=6, replace=False).tolist()))
     out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci, qblocks=np.array(blocks, np.int32))
-    mx, mean = output_errors(o, out, tok)
-    print(f"4096 blocks: sampled max|err| {mx:.3e} mean {mean:.3e}")
-    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    for x in (o, o_l):
+        mx, mean = output_errors(x, out, tok)
+        print(f"4096 blocks: sampled max|err| {mx:.3e} mean {mean:.3e}")
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
 
 
 @pytest.mark.parametrize("grid,tile,D", [((1, 96, 104), (1, 8, 8), 128), ((16, 20, 24), (4, 4, 4), 64)])
@@ -449,7 +459,7 @@ def test_fp8_forward_one_block_kernel_long_rows(grid, tile, D):
     m = np.random.default_rng(32).random((H * nb, nb)).astype(np.float32)   # flat rows: long kept lists
     rp, ci = O.select_blocks(m / m.sum(axis=1, keepdims=True), 99, 100)
     assert np.diff(rp).min() > 64, np.diff(rp).min()
-    bsa, _, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=True)
+    bsa, _, o, _, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=True)
     qh, _ = O.fp8_tile_quantize(q, grid, tile)
     kh, _ = O.fp8_tile_quantize(k, grid, tile)
     out_s, tok_s = O.masked_attention(qh, kh, v, grid, tile, bsa.scale, rp, ci)
@@ -467,7 +477,7 @@ def test_fp8_forward_unquantized_bar(grid):
     q, k, v = inputs(grid, 1, H, D, amp=1.0, sigma=1.0, seed=0)
     scale = 1.0 / math.sqrt(D)
     rp, ci = O.select_blocks(O.block_mass(q, k, grid, tile, scale).astype(np.float32))
-    bsa, _, o, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=True)
+    bsa, _, o, _, _ = _run_forward(q, k, v, grid, tile, H, D, rp, ci, fp8=True)
     out, tok = O.masked_attention(q, k, v, grid, tile, bsa.scale, rp, ci)
     mx, mean = output_errors(o, out, tok)
     qh, _ = O.fp8_tile_quantize(q, grid, tile)
@@ -566,7 +576,9 @@ def test_outputs_stay_inside_their_buffers(grid, H, D):
     csr = Csr(g((bsa.R + 1,), torch.int32), g((bsa.R * bsa.nb,), torch.int32))
     bsa.select(mass, csr=csr)
     lse = g((1, H, bsa.npad), torch.float32)
-    ot = bsa.forward(qt, kt, vt, csr, out=g(bsa.tiled_shape(), torch.bfloat16), lse=lse)
+    bsa.forward(qt, kt, vt, csr, out=g(bsa.tiled_shape(), torch.bfloat16), lse=lse,
+                out_f32=g(bsa.tiled_shape(), torch.float32))
+    ot = bsa.forward(qt, kt, vt, csr, out=g(bsa.tiled_shape(), torch.bfloat16))
     o = bsa.untile(ot, torch.float32, out=g((1, bsa.N, H, D), torch.float32))
     q8, qs = bsa.tile_fp8(qd, out=g(bsa.tiled_shape(), torch.uint8), scale=g((1, H, bsa.nb), torch.float32))
     torch.cuda.synchronize()
