@@ -19,7 +19,8 @@
 //
 // k_sparse_attn (D = 64, blocks with counted keys, 2D grids, grids over 4096 blocks):
 // a workgroup of four waves owns one query block (64 rows) of one (batch, head) and walks the
-// block's CSR list in order. The K and V tiles of each kept block are copied once per
+// block's CSR list in order (bf16, D = 128, no lse: pre-scaled queries, as in the paired
+// kernel). The K and V tiles of each kept block are copied once per
 // workgroup into LDS with direct global-to-LDS loads (buffer_load_dwordx4 ... lds,
 // each wave moving a quarter of each tile in contiguous kilobytes) into two-slot K
 // and V rings, K two blocks and V one block ahead of use; one barrier per block. The
@@ -47,7 +48,9 @@ constexpr int kAttnThreads = 256;
 
 // CNT: the real keys of each key block are its first kcount[(b*H + h)*nb + kb] slots
 // (blocks of a cluster-contiguous layout) instead of following from the token grid.
-template <int D, bool FP8, bool CNT>
+// SHIFT (bf16, D = 128, the call without lse): queries pre-scaled to base-2 units and
+// score chains that start from -r, as in the paired kernel.
+template <int D, bool FP8, bool CNT, bool SHIFT = false>
 __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
     const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
@@ -85,6 +88,16 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
     KHalf<D, FP8> q;
     load_khalf<D, FP8>(q, qv, qblk0, qh, lane);
     const float cq = FP8 ? scale_log2 * q_scale[r] : scale_log2;
+    static_assert(!SHIFT || (D == 128 && !FP8), "pre-scaled queries: bf16, D = 128");
+    if constexpr (SHIFT) {
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q.b[j][e] = (__bf16)((float)q.b[j][e] * scale_log2);
+    }
+    f32x16 mt;                                        // SHIFT: -r in every element
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt[i] = 0.0f;
 
     f32x16 acc[kDT];
 #pragma unroll
@@ -194,7 +207,9 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
             vm = code == 0 ? ~0ull : ((inf < 0 || code >= kBlock) ? 0ull : (~0ull >> code));
         else
             vm = code == 0 ? ~0ull : (inf < 0 ? 0ull : edge.mask(code));
-        const float nref = softmax_enter<kDT>(s, code == 0, vm, smax, c, kh, half, acc, m, l);
+        float nref = 0.0f;
+        if constexpr (SHIFT) softmax_enter_shifted<kDT>(s, code == 0, vm, smax, kh, half, acc, mt, m, l);
+        else nref = softmax_enter<kDT>(s, code == 0, vm, smax, c, kh, half, acc, m, l);
 
         // K(j+1) and V(j) landed; every wave is done with iteration j-1's reads
         copies_landed_barrier();
@@ -211,7 +226,8 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
         };
         constexpr int kCopies = kKChunks + kVChunks;
         if constexpr (D == 128 && !FP8)
-            block_main_bf16_d128<kCopies>(kst, vst, kh, lane, q, k, v, acc, s, sn, c, nref, l, smax, copy_one);
+            block_main_bf16_d128<kCopies, SHIFT>(kst, vst, kh, lane, q, k, v, acc, s, sn, mt, c, nref, l, smax,
+                                                 copy_one);
         else if constexpr (D == 128 && FP8)
             block_main_fp8_d128<kCopies>(kst, vst, kh, lane, q, k, v, acc, s, sn, c, nref, l, smax, copy_one);
         else
@@ -802,7 +818,9 @@ void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, co
     }
     if (D == 128) {
         if (fp8) k_sparse_attn<128, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
+        else if (kcount && lse == nullptr) k_sparse_attn<128, false, true, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, kcount);
         else if (kcount) k_sparse_attn<128, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, kcount);
+        else if (lse == nullptr) k_sparse_attn<128, false, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
         else k_sparse_attn<128, false, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
     } else {
         if (fp8) k_sparse_attn<64, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);

@@ -265,6 +265,40 @@ __device__ __attribute__((always_inline)) inline float softmax_enter(
     return m == -INFINITY ? 0.0f : -m;
 }
 
+// The same for scores that arrive in base-2 units already shifted by the reference r
+// (r = m, or 0 before any key; the tile mt holds -r and starts the score products):
+// smax and s are relative to r, and moving the reference shifts s and mt with it.
+template <int kDT>
+__device__ __attribute__((always_inline)) inline void softmax_enter_shifted(
+    f32x16& s, bool all_keys, uint64_t vm, float smax, int kh, int half, f32x16 (&acc)[kDT], f32x16& mt,
+    float& m, float& l) {
+    float mx = smax;
+    if (!all_keys) {
+        const uint32_t m32 = (uint32_t)(vm >> (32 * kh + 4 * half));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = keep_or_neg_inf(s[i], m32, 8 * (i >> 2) + (i & 3));
+        mx = max16(s);
+    }
+    const bool grow = mx > (m == -INFINITY ? -INFINITY : kRescaleSlack);
+    if (__ballot(grow)) {
+        const float r = m == -INFINITY ? 0.0f : m;
+        const float mnew = r + mx;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;   // 0 when m = -inf
+        const float d = grow ? mx : 0.0f;
+#pragma unroll
+        for (int t = 0; t < kDT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[t][i] *= alpha;
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] -= d;
+        if (grow) m = mnew;
+        const float nr = m == -INFINITY ? 0.0f : -m;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt[i] = nr;
+    }
+}
+
 // Main section of a kept block in its plain form (any D, bf16 or e4m3 scores):
 // read K of the next block and V of this one from LDS, then start the copies (after
 // the reads, for the reason given below), issue the next block's QK^T, then this
@@ -316,19 +350,21 @@ __device__ __attribute__((always_inline)) inline void block_main_generic(
 // of stalling the wave. The QK^T chain of the next block comes first, then P*V of
 // this block,
 // whose first half needs the first eight probabilities and whose second half the
-// rest; the next block's score maximum is taken under the last products.
-template <int NC, class Copy>
+// rest; the next block's score maximum is taken under the last products. SHIFT: the
+// queries carry the base-2 scale and the score chain starts from mt (-r), so the scores
+// need no scale-and-shift step before their exponentials.
+template <int NC, bool SHIFT, class Copy>
 __device__ __attribute__((always_inline)) inline void block_main_bf16_d128(
     const uint8_t* kst, const uint8_t* vst, int kh, int lane, const KHalf<128, false>& q,
-    KHalf<128, false>& k, bf16x8 (&v)[4][2], f32x16 (&acc)[4], const f32x16& s, f32x16& sn, float c,
-    float nref, float& l, float& smax, Copy&& copy_one) {
+    KHalf<128, false>& k, bf16x8 (&v)[4][2], f32x16 (&acc)[4], const f32x16& s, f32x16& sn, const f32x16& mt,
+    float c, float nref, float& l, float& smax, Copy&& copy_one) {
     static_assert(NC <= 8, "one copy per QK^T product");
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float pf[16];
     uint32_t pw[8];
     float rs0 = 0.0f, rs1 = 0.0f;
     float ma, mb, md, me;
-    auto FM = [&](int i) { pf[i] = __builtin_fmaf(s[i], c, nref); };
+    auto FM = [&](int i) { pf[i] = SHIFT ? s[i] : __builtin_fmaf(s[i], c, nref); };
     auto EX = [&](int i) { pf[i] = __builtin_amdgcn_exp2f(pf[i]); };
     auto CV = [&](int i) {
         bf16x2 pr;
@@ -342,11 +378,11 @@ __device__ __attribute__((always_inline)) inline void block_main_bf16_d128(
         else rs1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs1, false);
     };
     auto QK = [&](int i) {
-        if (i == 0) {
+        if (i == 0 && !SHIFT) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) sn[e] = 0.0f;
         }
-        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.b[i], q.b[i], sn, 0, 0, 0);
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.b[i], q.b[i], (SHIFT && i == 0) ? mt : sn, 0, 0, 0);
     };
     auto PV = [&](int t, int cc) {
         const i32x4 wv = {(int)pw[4 * cc], (int)pw[4 * cc + 1], (int)pw[4 * cc + 2], (int)pw[4 * cc + 3]};

@@ -282,11 +282,10 @@ int32_t fpsa_retained_mass(const float* mass, int64_t R, int32_t nb, const int32
  *   the union of their rows) or in CSR order (other paths); the order changes only
  *   rounding. Probabilities are rounded to BF16 for the P*V product, which
  *   accumulates in float32, and the softmax denominator is the sum of those rounded
- *   probabilities. Scores: BF16 Q/K with D = 128 on video grids (t > 1) of at most
- *   FPSA_MAX_SELECT_BLOCKS blocks and lse == NULL (the inference call) take q times
- *   softmax_scale * log2(e) rounded to BF16 once (at most 2^-8 relative per element,
- *   as a library attention that pre-scales q in the input precision); every other
- *   call scales the float32 score product instead.
+ *   probabilities. Scores: BF16 Q/K with D = 128 and lse == NULL (the inference call)
+ *   take q times softmax_scale * log2(e) rounded to BF16 once (at most 2^-8 relative per
+ *   element, as a library attention that pre-scales q in the input precision); every
+ *   other call (D = 64, FP8, or lse requested) scales the float32 score product.
  * o: tiled rows BF16 [B, H, Npad, D]. lse: [B, H, Npad] float32 natural-log
  *   log-sum-exp over the visited keys, taken from the same rounded probabilities
  *   that normalise o (-inf for a query with none; 0 for padding), or NULL.
