@@ -141,7 +141,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const OT* __restrict__ o,
 // queries, from the four P and dS operands of its key half. Each wave's accumulators
 // thus cover half the channels (64 registers instead of 128), which with the direct
 // copies into two slots keeps the kernel at two workgroups per CU.
-template <int D>
+// SCALED: e4m3 Q/K (tile scales multiply the scores and dS); without it the scales
+// are 1 and their multiplications are left out.
+template <int D, bool SCALED>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
             const float gq = row_bcast<i>(X[1]);
             const float pp = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lq)) : 0.0f;
             pv[i] = pp;
-            ds[i] = pp * (dp[i] - gq) * tq;
+            ds[i] = SCALED ? pp * (dp[i] - gq) * tq : pp * (dp[i] - gq);
         });
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(
 
 // ---------------------------------------------------------------- dQ
 
-template <int D>
+template <int D, bool SCALED>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -478,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
             for (int t = 0; t < 8; ++t) {
                 const int i = 8 * ks + t;
                 const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lq));
-                ds[t] = pp * (dp[i] - gq) * tk;
+                ds[t] = SCALED ? pp * (dp[i] - gq) * tk : pp * (dp[i] - gq);
             }
             const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
 #pragma unroll
@@ -552,11 +554,20 @@ static void launch_bwd_d(const void* q, const void* k, const void* v, const void
         k_bwd_prep<D, float><<<(unsigned)rows, 256, 0, st>>>(static_cast<const float*>(o), bg, lse, g, lse2, delta);
     else
         k_bwd_prep<D, __bf16><<<(unsigned)rows, 256, 0, st>>>(static_cast<const __bf16*>(o), bg, lse, g, lse2, delta);
-    k_bwd_dkdv<D><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, col_ptr, row_idx, q_scale,
-                                                  k_scale, g, c, scale, static_cast<__bf16*>(dk),
-                                                  static_cast<__bf16*>(dv));
-    k_bwd_dq<D><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, q_scale, k_scale,
-                                                g, c, scale, static_cast<__bf16*>(dq));
+    // the host checks that q_scale and k_scale are both given or both NULL
+    if (q_scale != nullptr) {
+        k_bwd_dkdv<D, true><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, col_ptr, row_idx, q_scale,
+                                                            k_scale, g, c, scale, static_cast<__bf16*>(dk),
+                                                            static_cast<__bf16*>(dv));
+        k_bwd_dq<D, true><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, q_scale,
+                                                          k_scale, g, c, scale, static_cast<__bf16*>(dq));
+    } else {
+        k_bwd_dkdv<D, false><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, col_ptr, row_idx, nullptr,
+                                                             nullptr, g, c, scale, static_cast<__bf16*>(dk),
+                                                             static_cast<__bf16*>(dv));
+        k_bwd_dq<D, false><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, nullptr,
+                                                           nullptr, g, c, scale, static_cast<__bf16*>(dq));
+    }
 }
 
 void launch_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
