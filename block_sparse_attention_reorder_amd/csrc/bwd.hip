@@ -14,7 +14,9 @@
 //   k_bwd_dkdv  one workgroup per key block, walking the query blocks that keep it
 //               (the transposed CSR); dK and dV stay in registers, each wave holding
 //               half the channels of its 32 keys (P and dS are exchanged through LDS);
-//   k_bwd_dq    one workgroup per query block, walking its kept key blocks.
+//   k_bwd_dq    one workgroup per query block, walking its kept key blocks; for bf16,
+//               D = 128 on video grids (k_bwd_dq_pair) one workgroup per two
+//               neighbouring query blocks, walking the union of their rows.
 // Both copy each block's tiles (Q and dO, or K and V) straight into one of two LDS
 // slots an iteration ahead, with copies issued from inline asm that the compiler does
 // not wait for; without register staging both fit 256 registers, so two workgroups
@@ -532,6 +534,227 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
     }
 }
 
+// ---------------------------------------------------------------- dQ, paired form
+
+// bf16, D = 128, video grids (t > 1) of at most 4096 blocks: a workgroup owns two
+// neighbouring query blocks of one (batch, head) and walks the union of their kept
+// lists in ascending block order, as the paired forward does, so each K/V tile copied
+// into LDS serves 128 queries instead of 64 (half the copy bytes and barriers per
+// product). Wave w takes the 32 queries 32*(w & 1) .. of query block w >> 1 against
+// both 32-key halves of every union block its own block keeps, one half after the
+// other (scores, dP, dS and the dQ products of a half before the next), and skips the
+// blocks its block does not keep; each wave then holds its queries' whole sum, so no
+// partial sums are added at the end. The lists become membership bitmaps in LDS
+// (entries outside [0, nb) dropped, repeats collapsing, as in the transpose the dK/dV
+// pass walks).
+constexpr int kDqMaxWords = 4096 / 32;                    // 32-bit words of one row's bitmap
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_bwd_dq_pair(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long P, float c,
+    float scale, __bf16* __restrict__ dq) {
+    static_assert(D == 128, "paired dQ: D = 128");
+    constexpr int kTile = 64 * D * 2;
+    constexpr int kSlot = 2 * kTile;              // K tile, V tile
+    constexpr int kDT = D / 32;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kSlot];   // two slots
+    // bias tiles as in k_bwd_dq: entry ((code * 2 + kh) * 2 + hb) * 16 + i is 0 when key
+    // 32 kh + 8 (i / 4) + 4 hb + i % 4 of a block with edge code `code` is real, else -inf
+    __shared__ __attribute__((aligned(16))) float sbias[8 * 2 * 2 * 16];
+    __shared__ uint32_t bits[2][kDqMaxWords];
+
+    const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qsel = w >> 1, qh = w & 1;
+    const long p = xcd_row(P);
+    const int ph = (g.nb + 1) >> 1;
+    const long bh = p / ph;
+    const int v0 = 2 * (int)(p - bh * ph);
+    const bool hasrow = v0 + qsel < g.nb;         // uniform per wave
+    const long row = bh * g.nb + (hasrow ? v0 + qsel : v0);
+    const long npad = 64L * g.nb;
+
+    KHalf<D, false> qf, gf;                        // B operands: query (lane % 32) of half qh
+    load_khalf<D, false>(qf, q, row * 64, qh, lane);
+    load_khalf<D, false>(gf, dout, row * 64, qh, lane);
+    keep_resident<D>(qf);
+    keep_resident<D>(gf);
+    const float lq = lse2[row * 64 + 32 * qh + (lane & 31)];
+    const float gq = delta[row * 64 + 32 * qh + (lane & 31)];
+    for (int x = tid; x < 8 * 64; x += 256) {
+        const int code = x >> 6, kx = (x >> 5) & 1, hx = (x >> 4) & 1, i = x & 15;
+        const int key = 32 * kx + 8 * (i >> 2) + 4 * hx + (i & 3);
+        const int plane = g.th * g.tw;
+        const int et = key / plane, eh = (key - et * plane) / g.tw, ew = key - et * plane - eh * g.tw;
+        const int ok = (et < g.T - (g.nt - 1) * g.tt ? 1 : 0) | (eh < g.Hg - (g.nh - 1) * g.th ? 2 : 0) |
+                       (ew < g.Wg - (g.nw - 1) * g.tw ? 4 : 0);
+        sbias[x] = ((ok | ~code) & 7) == 7 ? 0.0f : -INFINITY;
+    }
+    for (int i = tid; i < 2 * kDqMaxWords; i += 256) (&bits[0][0])[i] = 0u;
+    __syncthreads();
+    if (hasrow) {
+        const int e0 = row_ptr[row], e1 = row_ptr[row + 1];
+        for (int e = e0 + 64 * qh + lane; e < e1; e += 128) {
+            const int x = col_idx[e];
+            if ((unsigned)x < (unsigned)g.nb) atomicOr(&bits[qsel][x >> 5], 1u << (x & 31));
+        }
+    }
+    __syncthreads();
+    // number of union entries: lane l counts 32-bit words l and l + 64 of both bitmaps
+    const int nwords = (g.nb + 63) >> 6;
+    int n_union;
+    {
+        int cnt = 0;
+        if (lane < 2 * nwords) cnt = __builtin_popcount(bits[0][lane] | bits[1][lane]);
+        if (lane + 64 < 2 * nwords) cnt += __builtin_popcount(bits[0][lane + 64] | bits[1][lane + 64]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+        n_union = __builtin_amdgcn_readfirstlane(cnt);
+    }
+    // union entries in ascending order: the index word (block | edge code << kEdgeShift)
+    // and whether this wave's query block keeps it; -1 past the end
+    int gw = -1, winfo = -1;
+    uint64_t rem = 0, own = 0;
+    auto word = [&](int sel, int i) {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane(bits[sel][2 * i]);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane(bits[sel][2 * i + 1]);
+        return ((uint64_t)hi << 32) | lo;
+    };
+    auto gen = [&](int& info, bool& mine) {
+        while (rem == 0) {
+            if (gw + 1 >= nwords) {
+                info = -1;
+                mine = false;
+                return;
+            }
+            ++gw;
+            const uint64_t a = word(0, gw), b = word(1, gw);
+            rem = a | b;
+            own = qsel ? b : a;
+            winfo = block_info(g, 64 * gw + lane);
+        }
+        const int bit = __builtin_ctzll(rem);
+        rem &= rem - 1;
+        info = __builtin_amdgcn_readlane(winfo, bit);
+        mine = (own >> bit) & 1ull;
+    };
+
+    f32x16 acc[kDT];
+#pragma unroll
+    for (int t = 0; t < kDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+
+    constexpr int kCh = kTile / 1024 / 4;
+    const int lane16 = 16 * swz_unit(lane);       // swizzled source unit of this lane
+    const i32x4r krs = tile_rsrc_raw(k + bh * npad * D, (uint32_t)(npad * D * 2));
+    const i32x4r vrs = tile_rsrc_raw(v + bh * npad * D, (uint32_t)(npad * D * 2));
+    auto copy_block = [&](int info, uint8_t* dst) {
+        const uint32_t base = (uint32_t)((info < 0 ? 0 : (info & kBlockIdMask)) * kTile);
+#pragma unroll
+        for (int ch = 0; ch < kCh; ++ch) {
+            copy_kb_asm(krs, base + (kCh * w + ch) * 1024, dst + (kCh * w + ch) * 1024, lane16);
+            copy_kb_asm(vrs, base + (kCh * w + ch) * 1024, dst + kTile + (kCh * w + ch) * 1024, lane16);
+        }
+    };
+
+    // key half kh of a kept block: scores and dP (starting from the block's bias tile),
+    // then dS, then the dQ products over the half's 32 keys
+    auto compute_half = [&](const uint8_t* sk, int code, auto khc) {
+        constexpr int kh = decltype(khc)::value;
+        const uint8_t* sv = sk + kTile;
+        bf16x8 ka[D / 16], va[D / 16];
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            const int off = (kh * (D / 16) + st) * 1024 + 16 * swz_unit(lane);
+            ka[st] = *reinterpret_cast<const bf16x8*>(sk + off);
+            va[st] = *reinterpret_cast<const bf16x8*>(sv + off);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 s, dp;
+        {
+            const float* bt = sbias + ((code * 2 + kh) * 2 + hb) * 16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(bt + 4 * j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[4 * j + e] = b4[e];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp[i] = 0.0f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st], qf.b[st], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st], gf.b[st], dp, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int trb = tr_base<D>(32 * kh, lane);
+        bf16x8 ktr[2][kDT];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int t = 0; t < kDT; ++t) ktr[ks][t] = tr_operand(sk, trb + t * 2048 + ks * 256);
+        __builtin_amdgcn_sched_barrier(0);
+        // element i: key 32*kh + 8*(i/4) + 4*hb + i%4, query 32*qh + lane%32
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            float ds[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int i = 8 * ks + t;
+                const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq));
+                ds[t] = pp * (dp[i] - gq);
+            }
+            const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+#pragma unroll
+            for (int t = 0; t < kDT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, ktr[ks][t], acc[t], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Two slots: union block j sits in slot j % 2. Iteration j waits for its own copy
+    // (issued an iteration earlier) and for every wave to leave iteration j - 1, then
+    // starts the copy of block j + 1 into the other slot and computes block j if this
+    // wave's query block keeps it.
+    if (n_union > 0) {
+        int icur;
+        bool mcur;
+        gen(icur, mcur);
+        copy_block(icur, lds);
+        for (int jj = 0; jj < n_union; ++jj) {
+            int inext;
+            bool mnext;
+            gen(inext, mnext);
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (jj + 1 < n_union) copy_block(inext, lds + ((jj + 1) & 1) * kSlot);
+            if (mcur && hasrow) {                      // uniform per wave
+                const uint8_t* sk = lds + (jj & 1) * kSlot;
+                const int code = icur >> kEdgeShift;
+                compute_half(sk, code, std::integral_constant<int, 0>());
+                compute_half(sk, code, std::integral_constant<int, 1>());
+            }
+            icur = inext;
+            mcur = mnext;
+        }
+    }
+    wait_vmcnt<0>();
+    if (!hasrow) return;
+    // element i of tile t: query 32*qh + 8*(i/4) + 4*hb + i%4, channel 32*t + lane%32
+    const long row0 = row * 64 + 32 * qh;
+#pragma unroll
+    for (int t = 0; t < kDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const long r = row0 + 8 * (i >> 2) + 4 * hb + (i & 3);
+            dq[r * D + 32 * t + (lane & 31)] = (__bf16)(scale * acc[t][i]);
+        }
+}
+
 // ---------------------------------------------------------------- host
 
 size_t bwd_workspace_bytes(int B, int H, int nb) { return 2 * (size_t)B * H * nb * 64 * sizeof(float); }
@@ -565,6 +788,14 @@ static void launch_bwd_d(const void* q, const void* k, const void* v, const void
         k_bwd_dkdv<D, false><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, col_ptr, row_idx, nullptr,
                                                              nullptr, g, c, scale, static_cast<__bf16*>(dk),
                                                              static_cast<__bf16*>(dv));
+        if constexpr (D == 128) {
+            if (g.T > 1 && g.nb <= kDqMaxWords * 32) {
+                const long P = (long)B * H * ((g.nb + 1) / 2);
+                k_bwd_dq_pair<D><<<(unsigned)P, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, g, P, c,
+                                                               scale, static_cast<__bf16*>(dq));
+                return;
+            }
+        }
         k_bwd_dq<D, false><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, nullptr,
                                                            nullptr, g, c, scale, static_cast<__bf16*>(dq));
     }

@@ -328,7 +328,12 @@ size_t fpsa_transpose_workspace_bytes(int64_t R, int32_t nb);
  *   layout too, not VT). o: the forward's output in tiled rows, BF16 (o_dtype =
  *   FPSA_BF16) or its float32 copy o_f32 (o_dtype = FPSA_F32, more accurate delta).
  *   lse: the forward's lse [B, H, Npad] (natural log). row_ptr / col_idx: the forward's CSR;
- *   col_ptr / row_idx: its transpose (fpsa_csr_transpose).
+ *   col_ptr / row_idx: its transpose (fpsa_csr_transpose). Entries outside [0, nb)
+ *   contribute nothing. A row should list each block once; a repeated block counts once
+ *   in dk and dv (the transpose collapses repeats) and, for BF16 with D = 128 on video
+ *   grids (t > 1) of at most FPSA_MAX_SELECT_BLOCKS blocks, in dq (whose pass walks the
+ *   union of two rows' membership bitmaps, as the forward does there); in dq on the
+ *   other paths once per listing.
  * With p_ij = exp(softmax_scale q_i.k_j - lse_i) over the kept keys j of query i
  * and delta_i = dO_i.o_i:
  *   dv_j = sum_i p_ij dO_i,  ds_ij = p_ij (dO_i.v_j - delta_i),

@@ -139,6 +139,41 @@ def test_backward_all_blocks_equals_dense_gradients():
     _check(dv, wv, mv, "dv")
 
 
+def test_backward_odd_block_count_and_untidy_rows():
+    """D = 128 on a video grid of 15 blocks (the last two-block workgroup of the dQ pass
+    holds one query block; the last query block keeps nothing). Rows shuffled, with
+    repeated and out-of-range entries: every gradient bit-identical to that of the same
+    rows sorted and cleaned (repeats count once and out-of-range entries drop out, in
+    the forward, the transpose and both gradient passes), and within the bounds of the
+    oracle under the cleaned rows."""
+    grid, tile, H, D = (4, 12, 20), (4, 4, 4), 2, 128
+    q, k, v = inputs(grid, 1, H, D, amp=1.5, seed=57)
+    g = _dout(grid, 1, H, D, 58)
+    nb = O.num_blocks(grid, tile)
+    assert nb % 2 == 1
+    rp, ci = _csr_of_rows(H, nb, 11, 9, 10, empty=(H * nb - 1,))
+    rng = np.random.default_rng(5)
+    rows_bad = []
+    for r in range(H * nb):
+        row = ci[rp[r]:rp[r + 1]].tolist()
+        bad = row + row[: len(row) // 3] + [nb, -1, 1 << 20][: r % 3]
+        rng.shuffle(bad)
+        rows_bad.append(bad)
+    rp_bad = np.concatenate([[0], np.cumsum([len(x) for x in rows_bad])]).astype(np.int32)
+    ci_bad = np.array([x for row in rows_bad for x in row], np.int32)
+    bsa, raster, tiled = _gpu_grads(q, k, v, g, grid, tile, H, D, rp, ci)
+    _, _, tiled_bad = _gpu_grads(q, k, v, g, grid, tile, H, D, rp_bad, ci_bad)
+    for a, b in zip(tiled, tiled_bad):
+        assert np.array_equal(a, b)
+    wq, wk, wv, mq, mk, mv = O.masked_attention_bwd(q, k, v, g, grid, tile, bsa.scale, rp, ci, magnitudes=True)
+    dq, dk, dv = raster
+    _check(dq, wq, mq, "dq")
+    _check(dk, wk, mk, "dk")
+    _check(dv, wv, mv, "dv")
+    blk, _ = O.token_blocks(grid, tile)
+    assert np.all(dq[0, blk == nb - 1, H - 1] == 0)
+
+
 def test_backward_repeat_is_bitwise_identical():
     grid, tile, H, D = (9, 10, 13), (4, 4, 4), 2, 128
     q, k, v = inputs(grid, 1, H, D, seed=55)
