@@ -14,7 +14,7 @@
 //   k_bwd_dkdv  one workgroup per key block, walking the query blocks that keep it
 //               (the transposed CSR); dK and dV stay in registers, each wave holding
 //               half the channels of its 32 keys (P and dS are exchanged through LDS);
-//   k_bwd_dq    one workgroup per query block, walking its kept key blocks; for bf16,
+//   k_bwd_dq    one workgroup per query block, walking its kept key blocks; for
 //               D = 128 on video grids (k_bwd_dq_pair) one workgroup per two
 //               neighbouring query blocks, walking the union of their rows.
 // Both copy each block's tiles (Q and dO, or K and V) straight into one of two LDS
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
 
 // ---------------------------------------------------------------- dQ, paired form
 
-// bf16, D = 128, video grids (t > 1) of at most 4096 blocks: a workgroup owns two
+// D = 128, video grids (t > 1) of at most 4096 blocks: a workgroup owns two
 // neighbouring query blocks of one (batch, head) and walks the union of their kept
 // lists in ascending block order, as the paired forward does, so each K/V tile copied
 // into LDS serves 128 queries instead of 64 (half the copy bytes and barriers per
@@ -546,14 +546,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(
 // blocks its block does not keep; each wave then holds its queries' whole sum, so no
 // partial sums are added at the end. The lists become membership bitmaps in LDS
 // (entries outside [0, nb) dropped, repeats collapsing, as in the transpose the dK/dV
-// pass walks).
+// pass walks). SCALED (e4m3 Q/K): the key tile scales of each 64-block window of the
+// bitmaps arrive with one vector load, a lane each, and are picked per block.
 constexpr int kDqMaxWords = 4096 / 32;                    // 32-bit words of one row's bitmap
 
-template <int D>
+template <int D, bool SCALED>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq_pair(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long P, float c,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale, Geom g, long P, float c,
     float scale, __bf16* __restrict__ dq) {
     static_assert(D == 128, "paired dQ: D = 128");
     constexpr int kTile = 64 * D * 2;
@@ -583,6 +585,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_pair(
     keep_resident<D>(gf);
     const float lq = lse2[row * 64 + 32 * qh + (lane & 31)];
     const float gq = delta[row * 64 + 32 * qh + (lane & 31)];
+    const float tq = SCALED ? q_scale[row] : 1.0f;       // e4m3: this query block's tile scale
+    const float* ksc_row = SCALED ? k_scale + bh * g.nb : nullptr;
     for (int x = tid; x < 8 * 64; x += 256) {
         const int code = x >> 6, kx = (x >> 5) & 1, hx = (x >> 4) & 1, i = x & 15;
         const int key = 32 * kx + 8 * (i >> 2) + 4 * hx + (i & 3);
@@ -616,17 +620,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_pair(
     // union entries in ascending order: the index word (block | edge code << kEdgeShift)
     // and whether this wave's query block keeps it; -1 past the end
     int gw = -1, winfo = -1;
+    float wsc = 1.0f;
     uint64_t rem = 0, own = 0;
     auto word = [&](int sel, int i) {
         const uint32_t lo = __builtin_amdgcn_readfirstlane(bits[sel][2 * i]);
         const uint32_t hi = __builtin_amdgcn_readfirstlane(bits[sel][2 * i + 1]);
         return ((uint64_t)hi << 32) | lo;
     };
-    auto gen = [&](int& info, bool& mine) {
+    auto gen = [&](int& info, bool& mine, float& tk) {
         while (rem == 0) {
             if (gw + 1 >= nwords) {
                 info = -1;
                 mine = false;
+                tk = 1.0f;
                 return;
             }
             ++gw;
@@ -634,11 +640,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_pair(
             rem = a | b;
             own = qsel ? b : a;
             winfo = block_info(g, 64 * gw + lane);
+            if constexpr (SCALED) wsc = 64 * gw + lane < g.nb ? ksc_row[64 * gw + lane] : 1.0f;
         }
         const int bit = __builtin_ctzll(rem);
         rem &= rem - 1;
         info = __builtin_amdgcn_readlane(winfo, bit);
         mine = (own >> bit) & 1ull;
+        tk = SCALED ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsc), bit)) : 1.0f;
     };
 
     f32x16 acc[kDT];
@@ -662,8 +670,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_pair(
 
     // key half kh of a kept block: scores and dP (starting from the block's bias tile),
     // then dS, then the dQ products over the half's 32 keys
-    auto compute_half = [&](const uint8_t* sk, int code, auto khc) {
+    auto compute_half = [&](const uint8_t* sk, int code, float tk, auto khc) {
         constexpr int kh = decltype(khc)::value;
+        const float cs = SCALED ? c * tq * tk : c;
         const uint8_t* sv = sk + kTile;
         bf16x8 ka[D / 16], va[D / 16];
 #pragma unroll
@@ -705,8 +714,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_pair(
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int i = 8 * ks + t;
-                const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lq));
-                ds[t] = pp * (dp[i] - gq);
+                const float pp = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lq));
+                ds[t] = SCALED ? pp * (dp[i] - gq) * tk : pp * (dp[i] - gq);
             }
             const bf16x8 da = pack_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
 #pragma unroll
@@ -723,23 +732,26 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_pair(
     if (n_union > 0) {
         int icur;
         bool mcur;
-        gen(icur, mcur);
+        float tcur;
+        gen(icur, mcur, tcur);
         copy_block(icur, lds);
         for (int jj = 0; jj < n_union; ++jj) {
             int inext;
             bool mnext;
-            gen(inext, mnext);
+            float tnext;
+            gen(inext, mnext, tnext);
             wait_vmcnt<0>();
             __syncthreads();
             if (jj + 1 < n_union) copy_block(inext, lds + ((jj + 1) & 1) * kSlot);
             if (mcur && hasrow) {                      // uniform per wave
                 const uint8_t* sk = lds + (jj & 1) * kSlot;
                 const int code = icur >> kEdgeShift;
-                compute_half(sk, code, std::integral_constant<int, 0>());
-                compute_half(sk, code, std::integral_constant<int, 1>());
+                compute_half(sk, code, tcur, std::integral_constant<int, 0>());
+                compute_half(sk, code, tcur, std::integral_constant<int, 1>());
             }
             icur = inext;
             mcur = mnext;
+            tcur = tnext;
         }
     }
     wait_vmcnt<0>();
@@ -782,6 +794,15 @@ static void launch_bwd_d(const void* q, const void* k, const void* v, const void
         k_bwd_dkdv<D, true><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, col_ptr, row_idx, q_scale,
                                                             k_scale, g, c, scale, static_cast<__bf16*>(dk),
                                                             static_cast<__bf16*>(dv));
+        if constexpr (D == 128) {
+            if (g.T > 1 && g.nb <= kDqMaxWords * 32) {
+                const long P = (long)B * H * ((g.nb + 1) / 2);
+                k_bwd_dq_pair<D, true><<<(unsigned)P, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx,
+                                                                     q_scale, k_scale, g, P, c, scale,
+                                                                     static_cast<__bf16*>(dq));
+                return;
+            }
+        }
         k_bwd_dq<D, true><<<(unsigned)rows, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, q_scale,
                                                           k_scale, g, c, scale, static_cast<__bf16*>(dq));
     } else {
@@ -791,8 +812,9 @@ static void launch_bwd_d(const void* q, const void* k, const void* v, const void
         if constexpr (D == 128) {
             if (g.T > 1 && g.nb <= kDqMaxWords * 32) {
                 const long P = (long)B * H * ((g.nb + 1) / 2);
-                k_bwd_dq_pair<D><<<(unsigned)P, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx, g, P, c,
-                                                               scale, static_cast<__bf16*>(dq));
+                k_bwd_dq_pair<D, false><<<(unsigned)P, 256, 0, st>>>(bq, bk, bv, bg, lse2, delta, row_ptr, col_idx,
+                                                                      nullptr, nullptr, g, P, c, scale,
+                                                                      static_cast<__bf16*>(dq));
                 return;
             }
         }
