@@ -104,6 +104,8 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
     for (int t = 0; t < kDT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+    // m: the query's running reference (the same in both lane halves); l: this lane's share
+    // of the row sum (its keys of each block), the two halves added once at the end
     float m = -INFINITY, l = 0.0f;
 
     const int e0 = __builtin_amdgcn_readfirstlane(row_ptr[r]);
@@ -260,6 +262,7 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
 
     // The last iteration's copies target the memory the merge uses: drain them.
     copies_landed_barrier();
+    l = wave_add32(l);                                // the two lane halves of each query
     merge_and_store<D>(reinterpret_cast<float*>(lds), qh, kh, lane, acc, m, l, true, g, qb, qblk0, o, lse, o32);
 }
 
@@ -399,10 +402,12 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             rs[kt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[kt][i >> 1]), ones, rs[kt], false);
         }
     };
-    auto MX = [&](int kt, int gi) {   // partial maximum of the next block's scores 4 gi .. 4 gi + 3 of half kt
-        const float x = fmaxf(fmaxf(sn[kt][4 * gi], sn[kt][4 * gi + 1]), fmaxf(sn[kt][4 * gi + 2], sn[kt][4 * gi + 3]));
-        if (kt == 0) mx0 = fmaxf(mx0, x);
-        else mx1 = fmaxf(mx1, x);
+    // running maximum over the next block's scores 4 gi .. 4 gi + 3 of half kt (a chain of
+    // three-input maxima)
+    auto MX = [&](int kt, int gi) {
+        float& mx = kt == 0 ? mx0 : mx1;
+        mx = fmaxf(fmaxf(mx, sn[kt][4 * gi]), sn[kt][4 * gi + 1]);
+        mx = fmaxf(fmaxf(mx, sn[kt][4 * gi + 2]), sn[kt][4 * gi + 3]);
     };
 #define FPSA_SB __builtin_amdgcn_sched_barrier(0)
     if constexpr (FP8) {
@@ -422,7 +427,7 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             if constexpr (n >= 8 && n < 12) MX(0, n - 8);
             if constexpr (n >= 12 && n < 16) MX(1, n - 12);
             if constexpr (n == 16) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
-            if constexpr (n == 17) l += wave_add32(rs[0] + rs[1]);
+            if constexpr (n == 17) l += rs[0] + rs[1];
             if constexpr (n == 19) smax = wave_max32(fmaxf(mx0, mx1));
             FPSA_SB;
         });
@@ -442,7 +447,7 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             if constexpr (n >= 20 && n < 24) MX(0, n - 20);
             if constexpr (n >= 24 && n < 28) MX(1, n - 24);
             if constexpr (!SHIFT && n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
-            if constexpr (n == 30) l += wave_add32(rs[0] + rs[1]);
+            if constexpr (n == 30) l += rs[0] + rs[1];
             if constexpr (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
             FPSA_SB;
         });
@@ -654,6 +659,8 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+    // m: the query's running reference (the same in both lane halves); l: this lane's share
+    // of the row sum (its keys of each block), the two halves added once at the end
     float m = -INFINITY, l = 0.0f;
     // SHIFT: C tiles of the QK^T chains, the bias tile of edge code `ccode` plus -r, r
     // the reference the scores are shifted by (m once a key has been seen, 0 before).
@@ -750,6 +757,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
         }
     }
     wait_vmcnt<0>();                                      // drain the last copies
+    l = wave_add32(l);                                    // the two lane halves of each query
 
     if (!hasrow) return;
     const int col = lane & 31;

@@ -336,7 +336,7 @@ __device__ __attribute__((always_inline)) inline void block_main_generic(
 #pragma unroll
         for (int t = 0; t < kDT; ++t)
             acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[t][cc], pb[cc], acc[t], 0, 0, 0);
-    l += wave_add32(rs0 + rs1);
+    l += rs0 + rs1;
     smax = max16(sn);
 }
 
@@ -434,7 +434,7 @@ __device__ __attribute__((always_inline)) inline void block_main_bf16_d128(
     md = fmaxf(fmaxf(sn[8], sn[9]), fmaxf(sn[10], sn[11]));
     FPSA_SB;
     PV(2, 1); me = fmaxf(fmaxf(sn[12], sn[13]), fmaxf(sn[14], sn[15]));
-    l += wave_add32(rs0 + rs1);
+    l += rs0 + rs1;
     FPSA_SB;
     PV(3, 1); smax = wave_max32(fmaxf(fmaxf(ma, mb), fmaxf(md, me)));
     FPSA_SB;
@@ -513,7 +513,7 @@ __device__ __attribute__((always_inline)) inline void block_main_fp8_d128(
     md = fmaxf(fmaxf(sn[8], sn[9]), fmaxf(sn[10], sn[11]));
     FPSA_SB;
     PV(2, 1); me = fmaxf(fmaxf(sn[12], sn[13]), fmaxf(sn[14], sn[15]));
-    l += wave_add32(rs0 + rs1);
+    l += rs0 + rs1;
     FPSA_SB;
     PV(3, 1); smax = wave_max32(fmaxf(fmaxf(ma, mb), fmaxf(md, me)));
     FPSA_SB;
