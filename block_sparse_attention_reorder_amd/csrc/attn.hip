@@ -377,7 +377,8 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             sn[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[n & 3], q.f[st], sn[kt], 0, 0, 0, 0, 0, 0);
         } else {
             const int kt = n >> 3, st = n & 7;
-            sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n & 7], q.b[st], (SHIFT && st == 0) ? ct[kt] : sn[kt], 0, 0, 0);
+            sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[n & 7], q.b[st], (SHIFT && st == 0) ? ct[kt] : sn[kt],
+                                                             0, 0, 0);
         }
     };
     auto PV = [&](int n) {
@@ -446,7 +447,8 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             static_for<12 + 3 * n, (15 + 3 * n < 96 ? 15 + 3 * n : 96)>([&](auto kc) { VS(decltype(kc)::value); });
             if constexpr (n >= 20 && n < 24) MX(0, n - 20);
             if constexpr (n >= 24 && n < 28) MX(1, n - 24);
-            if constexpr (!SHIFT && n == 28) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
+            // every score of block u is consumed: s takes block u+2's bias tile
+            if constexpr (!SHIFT && n == 28) load_bias(s, bias_table, bias_next, half);
             if constexpr (n == 30) l += rs[0] + rs[1];
             if constexpr (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
             FPSA_SB;
@@ -476,9 +478,9 @@ __device__ __attribute__((always_inline)) inline float pair_enter(float smax, fl
     return m == -INFINITY ? 0.0f : -m;
 }
 
-// The same for scores that arrive in base-2 units already shifted by the reference r (r = m, or 0 before any key): smax and the scores s of the block are
-// relative to r. Moving the reference shifts s and the C tiles ct (which carry -r) with
-// it.
+// The same for scores that arrive in base-2 units already shifted by the reference r
+// (r = m, or 0 before any key): smax and the scores s of the block are relative to r.
+// Moving the reference shifts s and the C tiles ct (which carry -r) with it.
 __device__ __attribute__((always_inline)) inline void pair_enter_shifted(float smax, f32x16 (&acc)[4],
                                                                          f32x16 (&s)[2], f32x16 (&ct)[2], float& m,
                                                                          float& l) {
@@ -825,15 +827,33 @@ void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, co
         return;
     }
     if (D == 128) {
-        if (fp8) k_sparse_attn<128, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
-        else if (kcount && lse == nullptr) k_sparse_attn<128, false, true, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, kcount);
-        else if (kcount) k_sparse_attn<128, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, kcount);
-        else if (lse == nullptr) k_sparse_attn<128, false, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
-        else k_sparse_attn<128, false, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
+        // bf16 without lse (inference) takes pre-scaled queries, as in the paired kernel
+        const bool shift = !fp8 && lse == nullptr;
+        if (fp8)
+            k_sparse_attn<128, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R,
+                                                                    sl2, out, lse, o32, nullptr);
+        else if (kcount && shift)
+            k_sparse_attn<128, false, true, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx,
+                                                                          g, R, sl2, out, lse, o32, kcount);
+        else if (kcount)
+            k_sparse_attn<128, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R,
+                                                                    sl2, out, lse, o32, kcount);
+        else if (shift)
+            k_sparse_attn<128, false, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx,
+                                                                           g, R, sl2, out, lse, o32, nullptr);
+        else
+            k_sparse_attn<128, false, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R,
+                                                                     sl2, out, lse, o32, nullptr);
     } else {
-        if (fp8) k_sparse_attn<64, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
-        else if (kcount) k_sparse_attn<64, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, kcount);
-        else k_sparse_attn<64, false, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R, sl2, out, lse, o32, nullptr);
+        if (fp8)
+            k_sparse_attn<64, true, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R,
+                                                                   sl2, out, lse, o32, nullptr);
+        else if (kcount)
+            k_sparse_attn<64, false, true><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R,
+                                                                   sl2, out, lse, o32, kcount);
+        else
+            k_sparse_attn<64, false, false><<<grid, block, 0, st>>>(q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, R,
+                                                                    sl2, out, lse, o32, nullptr);
     }
 }
 
