@@ -6,8 +6,8 @@
 //
 // Two gfx950 kernels.
 //
-// k_sparse_attn_pair (bf16 or e4m3 Q/K, D = 128, blocks of a video grid (T > 1), at most
-// 4096 blocks; the main path): a workgroup of four waves owns two neighbouring query
+// k_sparse_attn_pair (bf16 or e4m3 Q/K, D = 128, blocks of a video grid (T > 1) or bf16
+// blocks with counted keys, at most 4096 blocks; the main path): a workgroup of four waves owns two neighbouring query
 // blocks and walks the union of their kept lists in ascending block order, so every
 // K/V tile copied into LDS serves 128 queries (half the copy bytes and barriers per
 // product of a one-block workgroup). Each wave takes 32 query rows of one of the two
@@ -17,7 +17,7 @@
 // bf16 once) and shifted scores, with no scale-and-shift step per score. See the
 // comment above the kernel.
 //
-// k_sparse_attn (D = 64, blocks with counted keys, 2D grids, grids over 4096 blocks):
+// k_sparse_attn (D = 64, 2D grids, grids over 4096 blocks):
 // a workgroup of four waves owns one query block (64 rows) of one (batch, head) and walks the
 // block's CSR list in order (bf16, D = 128, no lse: pre-scaled queries, as in the paired
 // kernel). The K and V tiles of each kept block are copied once per
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
 }
 
 // ---------------------------------------------------------------------------------
-// Paired form (bf16, D = 128, token-grid blocks, nb <= 4096). One workgroup owns two
+// Paired form (D = 128, token-grid or counted blocks, nb <= 4096). One workgroup owns two
 // neighbouring query blocks of one (batch, head) and walks the union of their kept
 // lists, so each K/V tile copied into LDS serves 128 queries instead of 64: half the
 // copy bytes and barriers per product. Wave w takes the 32 query rows 32*(w & 1) ..
@@ -279,7 +279,10 @@ __global__ __launch_bounds__(kAttnThreads, FP8 ? 3 : 2) void k_sparse_attn(
 // Key masking costs no vector instruction: every QK^T chain starts from a bias tile
 // instead of from zero, 0 for a real key and -inf for a padding key of an edge block
 // (or for every key of a block the wave does not keep). A small LDS table holds, per
-// edge code (and the "nothing" code), the 2 x 16 accumulator values of each lane half.
+// edge code (and the "nothing" code), the 2 x 16 accumulator values of each lane half;
+// for counted blocks (the real keys of key block kb are its first kcount[kb] slots) the
+// code is the number of padding keys and the table holds the 17 prefix patterns of a
+// 16-element tile.
 //
 // Two forms for bf16. The inference form (SHIFT; the call without lse) multiplies the
 // queries by scale * log2(e) once and rounds them to bf16, so the products give base-2
@@ -314,17 +317,33 @@ __device__ inline float max16_lane(const f32x16& x) {
 }
 
 // Bias tiles of code `bc` for this lane: element i of tile kt is key 32 kt + 8 (i / 4)
-// + 4 half + i % 4 of the block.
+// + 4 half + i % 4 of the block. Grid blocks (CNT false): the table holds both tiles per
+// edge code. Counted blocks (CNT): `bc` is the number of padding keys at the block's end
+// (64 - real keys; 64 for a block the wave does not keep). A tile's keys increase with i,
+// so its real keys are a prefix of v elements, and row v of a table of the 17 prefix
+// patterns (v zeros, then -inf) is the tile.
+template <bool CNT>
 __device__ __attribute__((always_inline)) inline void load_bias(f32x16 (&t)[2], const float* table, int bc,
                                                                  int half) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+        const float* row;
+        if constexpr (CNT) {
+            // real keys of this tile: those below c' = (64 - bc) - 32 kt - 4 half among
+            // 0..3, 8..11, 16..19, 24..27 (arithmetic shift and mask also hold for c' < 0)
+            const int cp = kBlock - bc - 32 * kt - 4 * half;
+            const int v = min(max(4 * (cp >> 3) + min(cp & 7, 4), 0), 16);
+            row = table + 16 * v;
+        } else {
+            row = table + ((bc * 2 + half) * 2 + kt) * 16;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(table + ((bc * 2 + half) * 2 + kt) * 16 + 4 * j);
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(row + 4 * j);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) t[kt][4 * j + e] = v[e];
+            for (int e = 0; e < 4; ++e) t[kt][4 * j + e] = v4[e];
         }
+    }
 }
 
 // Main section of union block u for this wave: the QK^T of block u+1 (two 32-key
@@ -339,7 +358,7 @@ __device__ __attribute__((always_inline)) inline void load_bias(f32x16 (&t)[2], 
 // FMAs; with SHIFT the scores already sit in base-2 units relative to r) run as a
 // stream after a few up front. Without SHIFT, s receives the bias tile of block u+2 at
 // the end.
-template <bool FP8, bool SHIFT, int NC, class Copy>
+template <bool FP8, bool SHIFT, bool CNT, int NC, class Copy>
 __device__ __attribute__((always_inline)) inline void pair_main(
     const uint8_t* kst, const uint8_t* vst, int lane, int half, const KHalf<128, FP8>& q, f32x16 (&acc)[4],
     f32x16 (&s)[2], f32x16 (&sn)[2], const f32x16 (&ct)[2], float c, float nref, float& l, float& smax,
@@ -427,7 +446,7 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             static_for<32 + 4 * n, (36 + 4 * n < 96 ? 36 + 4 * n : 96)>([&](auto kc) { VS(decltype(kc)::value); });
             if constexpr (n >= 8 && n < 12) MX(0, n - 8);
             if constexpr (n >= 12 && n < 16) MX(1, n - 12);
-            if constexpr (n == 16) load_bias(s, bias_table, bias_next, half);   // every score of block u is consumed
+            if constexpr (n == 16) load_bias<CNT>(s, bias_table, bias_next, half);   // every score of block u is consumed
             if constexpr (n == 17) l += rs[0] + rs[1];
             if constexpr (n == 19) smax = wave_max32(fmaxf(mx0, mx1));
             FPSA_SB;
@@ -448,7 +467,7 @@ __device__ __attribute__((always_inline)) inline void pair_main(
             if constexpr (n >= 20 && n < 24) MX(0, n - 20);
             if constexpr (n >= 24 && n < 28) MX(1, n - 24);
             // every score of block u is consumed: s takes block u+2's bias tile
-            if constexpr (!SHIFT && n == 28) load_bias(s, bias_table, bias_next, half);
+            if constexpr (!SHIFT && n == 28) load_bias<CNT>(s, bias_table, bias_next, half);
             if constexpr (n == 30) l += rs[0] + rs[1];
             if constexpr (n == 31) smax = wave_max32(fmaxf(mx0, mx1));
             FPSA_SB;
@@ -506,12 +525,12 @@ __device__ __attribute__((always_inline)) inline void pair_enter_shifted(float s
     }
 }
 
-template <bool FP8, bool SHIFT>
+template <bool FP8, bool SHIFT, bool CNT>
 __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     const void* __restrict__ qv, const void* __restrict__ kv, const __bf16* __restrict__ vt,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, Geom g, long P, float scale_log2,
-    __bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o32) {
+    __bf16* __restrict__ o, float* __restrict__ lse, float* __restrict__ o32, const int32_t* __restrict__ kcount) {
     constexpr int D = 128;
     constexpr int kKBytes = kBlock * D * (FP8 ? 1 : 2), kVBytes = kBlock * D * 2;
     constexpr int kKChunks = kKBytes / 1024 / 4;          // kilobytes per wave per tile
@@ -523,6 +542,9 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     // memory inside the loop would be a scalar load, which shares the LDS reads' wait
     // counter and returns out of order, so every operand wait would become a full drain
     __shared__ float ksc_lds[FP8 ? kMaxBitmapWords * 32 : 1];
+    // counted blocks: each key block's code (64 - real keys), staged once for the same reason
+    __shared__ uint8_t kcode_lds[CNT ? kMaxBitmapWords * 32 : 1];
+    static_assert(!(FP8 && CNT), "counted blocks are bf16");
     uint8_t* const kring = lds;
     uint8_t* const vring = lds + 2 * kKBytes;
 
@@ -570,8 +592,15 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
     }
 
     // bias table: entry ((code * 2 + half) * 2 + kt) * 16 + i is 0 when key 32 kt + 8 (i / 4)
-    // + 4 half + i % 4 of a block with edge code `code` is real, else -inf (code 8: none)
-    for (int x = threadIdx.x; x < kBiasCodes * 64; x += kPairThreads) {
+    // + 4 half + i % 4 of a block with edge code `code` is real, else -inf (code 8: none);
+    // counted blocks: entry 16 v + i is 0 for i < v, else -inf
+    if constexpr (CNT) {
+        for (int x = threadIdx.x; x < 17 * 16; x += kPairThreads)
+            bias_table[x] = (x & 15) < (x >> 4) ? 0.0f : -INFINITY;
+        for (int i = threadIdx.x; i < g.nb; i += kPairThreads)
+            kcode_lds[i] = (uint8_t)(kBlock - min(max(kcount[bh * g.nb + i], 0), kBlock));
+    }
+    for (int x = threadIdx.x; !CNT && x < kBiasCodes * 64; x += kPairThreads) {
         const int code = x >> 6, i = x & 15, kt = (x >> 4) & 1, hf = (x >> 5) & 1;
         const int key = 32 * kt + 8 * (i >> 2) + 4 * hf + (i & 3);
         const int plane = g.th * g.tw;
@@ -627,7 +656,9 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
             const uint64_t a = word(0, gw), b = word(1, gw);
             rem = a | b;
             own = qsel ? b : a;
-            winfo = block_info(g, 64 * gw + lane);
+            const int kb = 64 * gw + lane;
+            if constexpr (CNT) winfo = kb < g.nb ? kb | ((int)kcode_lds[kb] << kEdgeShift) : -1;
+            else winfo = block_info(g, kb);
         }
         const int bit = __builtin_ctzll(rem);
         rem &= rem - 1;
@@ -635,7 +666,9 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
         mine = (own >> bit) & 1ull;
     };
     auto block_of = [](int info) { return info < 0 ? 0 : (info & kBlockIdMask); };
-    auto bias_code = [](int info, bool mine) { return (info < 0 || !mine) ? 8 : (info >> kEdgeShift); };
+    // the code of a block the wave does not keep: every key masked
+    constexpr int kNone = CNT ? kBlock : kBiasCodes - 1;
+    auto bias_code = [](int info, bool mine) { return (info < 0 || !mine) ? kNone : (info >> kEdgeShift); };
 
     const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(kv) + bh * npad * D * (FP8 ? 1 : 2);
     const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(vt) + bh * npad * D * 2;
@@ -691,7 +724,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
         const int code1 = bias_code(infn, minen);
         if (SHIFT && code1 != ccode) {
             ccode = code1;
-            load_bias(ct, bias_table, code1, half);
+            load_bias<CNT>(ct, bias_table, code1, half);
             const float nr = m == -INFINITY ? 0.0f : -m;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -705,7 +738,7 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
             if (i < kKChunks) copy_k(inf2, kring + par * kKBytes, i);
             else copy_v(infn, vring + (par ^ 1) * kVBytes, i - kKChunks);
         };
-        pair_main<FP8, SHIFT, kKChunks + kVChunks>(kst, vst, lane, half, q, acc, s, sn, ct, c, nref, l, smax, bias_table,
+        pair_main<FP8, SHIFT, CNT, kKChunks + kVChunks>(kst, vst, lane, half, q, acc, s, sn, ct, c, nref, l, smax, bias_table,
                                              bias_code(inf2, mine2), copy_one);
         inf = infn;
         mine = minen;
@@ -726,11 +759,11 @@ __global__ __launch_bounds__(kPairThreads, 2) void k_sparse_attn_pair(
         for (int i = 0; i < kVChunks; ++i) copy_v(inf, vring, i);
         copies_landed_barrier();                          // K(0), V(0), K(1) landed
         if constexpr (!SHIFT) {
-            load_bias(s0, bias_table, bias_code(inf, mine), half);
-            load_bias(s1, bias_table, bias_code(infn, minen), half);
+            load_bias<CNT>(s0, bias_table, bias_code(inf, mine), half);
+            load_bias<CNT>(s1, bias_table, bias_code(infn, minen), half);
         } else {
             ccode = bias_code(inf, mine);
-            load_bias(ct, bias_table, ccode, half);        // r = 0 so far
+            load_bias<CNT>(ct, bias_table, ccode, half);   // r = 0 so far
             s0[0] = ct[0];
             s0[1] = ct[1];
         }
@@ -806,24 +839,33 @@ void launch_sparse_attn(const void* q, const void* k, const void* v, int fp8, co
     __bf16* out = static_cast<__bf16*>(o);
     dim3 grid((unsigned)R), block(kAttnThreads);
     // Paired query blocks pay off when neighbouring query blocks keep nearly the same key
-    // blocks, as measured selections on video grids do (the union adds 1.4 % at 480p). On
-    // 2D grids the workloads are group-structured masks, whose neighbouring groups share
-    // only their row (or column) of groups, so a pair's union is about 1.5 times either
-    // list: those take the one-block kernel.
-    if (D == 128 && kcount == nullptr && g.nb <= kMaxBitmapWords * 32 && g.T > 1) {
+    // blocks, as measured selections on video grids do (the union adds 1.4 % at 480p), and
+    // as the blocks of one query cluster do in a cluster-contiguous layout (counted keys:
+    // they keep the same key clusters; 1.5 % at 480p with 128 clusters). On 2D grids the
+    // workloads are group-structured masks, whose neighbouring groups share only their
+    // row (or column) of groups, so a pair's union is about 1.5 times either list: those
+    // take the one-block kernel.
+    if (D == 128 && g.nb <= kMaxBitmapWords * 32 && (kcount != nullptr ? !fp8 : g.T > 1)) {
         const long P = (long)B * H * ((g.nb + 1) / 2);
+        const unsigned n = (unsigned)P;
         // bf16 without lse (inference) pre-scales the queries; with lse, whose consumer
         // (the backward) recomputes exact scores against it, the scores are scaled in
         // float32
         if (fp8)
-            k_sparse_attn_pair<true, false><<<(unsigned)P, kPairThreads, 0, st>>>(
-                q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, P, sl2, out, lse, o32);
+            k_sparse_attn_pair<true, false, false><<<n, kPairThreads, 0, st>>>(
+                q, k, vt, q_scale, k_scale, row_ptr, col_idx, g, P, sl2, out, lse, o32, nullptr);
+        else if (kcount != nullptr && lse == nullptr)
+            k_sparse_attn_pair<false, true, true><<<n, kPairThreads, 0, st>>>(
+                q, k, vt, nullptr, nullptr, row_ptr, col_idx, g, P, sl2, out, lse, o32, kcount);
+        else if (kcount != nullptr)
+            k_sparse_attn_pair<false, false, true><<<n, kPairThreads, 0, st>>>(
+                q, k, vt, nullptr, nullptr, row_ptr, col_idx, g, P, sl2, out, lse, o32, kcount);
         else if (lse == nullptr)
-            k_sparse_attn_pair<false, true><<<(unsigned)P, kPairThreads, 0, st>>>(
-                q, k, vt, nullptr, nullptr, row_ptr, col_idx, g, P, sl2, out, lse, o32);
+            k_sparse_attn_pair<false, true, false><<<n, kPairThreads, 0, st>>>(
+                q, k, vt, nullptr, nullptr, row_ptr, col_idx, g, P, sl2, out, lse, o32, nullptr);
         else
-            k_sparse_attn_pair<false, false><<<(unsigned)P, kPairThreads, 0, st>>>(
-                q, k, vt, nullptr, nullptr, row_ptr, col_idx, g, P, sl2, out, lse, o32);
+            k_sparse_attn_pair<false, false, false><<<n, kPairThreads, 0, st>>>(
+                q, k, vt, nullptr, nullptr, row_ptr, col_idx, g, P, sl2, out, lse, o32, nullptr);
         return;
     }
     if (D == 128) {

@@ -456,9 +456,14 @@ int32_t fpsa_cluster_blocks(const int32_t* crow_ptr, const int32_t* ccol_idx, co
 /*
  * Block-sparse forward over blocks whose real keys are counted instead of following
  * from a token grid: block kb of slice bh holds key_counts[bh*NB + kb] real keys in
- * its first slots (0..64). Otherwise as fpsa_sparse_attn_fwd (size limits with
- * nb = NB included) with BF16 q, k (QK layout) and v (VT layout) of B*H*NB blocks; every query slot gets an output (the
- * caller scatters the real ones back); lse and o_f32 optional.
+ * its first slots (values outside 0..64 are clamped to it). Otherwise as
+ * fpsa_sparse_attn_fwd (size limits with nb = NB included) with BF16 q, k (QK layout)
+ * and v (VT layout) of B*H*NB blocks; every query slot gets an output (the caller
+ * scatters the real ones back); lse and o_f32 optional. With D = 128 and NB <=
+ * FPSA_MAX_SELECT_BLOCKS, two neighbouring query blocks share one pass over the union
+ * of their rows in ascending block order (the blocks of one query cluster keep the
+ * same key clusters), and a repeated block counts once; with D = 64 or a larger NB the
+ * rows are walked in CSR order, once per listing.
  */
 int32_t fpsa_sparse_attn_fwd_varlen(const void* q, const void* k, const void* v,
                                     const int32_t* key_counts, const int32_t* row_ptr,

@@ -252,3 +252,117 @@ def test_semantic_full_480p_sampled():
         ref = O.cluster_attention(qh, kh, vh, qa_g, ka_g, ssa.Cq, ssa.Ck, ssa.scale, sub_rp, sub_ci, tokens=toks)
         e = np.abs(o[0, toks, h].astype(np.float64) - ref[0, 0])
         assert e.max() <= BF16_MAX_ABS and e.mean() <= BF16_MEAN_ABS, (h, e.max(), e.mean())
+
+
+@pytest.mark.parametrize("NB,H,D,seed", [(37, 2, 128, 1), (40, 1, 128, 2), (23, 2, 64, 3)])
+def test_varlen_forward_counted_blocks(NB, H, D, seed):
+    """The forward over counted blocks on its own: key blocks with 0 .. 64 real keys
+    (every prefix pattern of a 16-key tile occurs), runs of query blocks with the same
+    row (as one query cluster gives) and neighbours with different rows, empty rows,
+    repeated and out-of-range entries, and an odd block count (the last workgroup of
+    a slice holds one query block). Each block is taken as one cluster, so the outputs
+    are the oracle's attention under that cluster selection; lse against a float64
+    library logsumexp over the allowed keys. Both calls: without lse (pre-scaled
+    queries for D = 128) and with lse and float32 output."""
+    rng = np.random.default_rng(seed)
+    choices = np.array([0, 1, 3, 4, 5, 8, 12, 17, 24, 27, 28, 29, 31, 32, 33, 36, 40, 47, 59, 60, 63, 64])
+    kcnt = np.where(rng.random((H, NB)) < 0.5, 64, rng.choice(choices, (H, NB))).astype(np.int32)
+    qcnt = np.where(rng.random((H, NB)) < 0.6, 64, rng.choice(choices, (H, NB))).astype(np.int32)
+    N = int(max(kcnt.sum(1).max(), qcnt.sum(1).max()))
+    x = [rng.standard_normal((1, N, H, D)).astype(np.float32) for _ in range(3)]
+    x[0] *= 1.5
+    q, k, v = (torch.from_numpy(a).to(torch.bfloat16).float().numpy() for a in x)
+    # slot maps: each block's first count slots hold distinct tokens; tokens left over
+    # belong to an extra cluster NB that no row lists
+    kslot = np.full((H, NB * 64), -1, np.int64)
+    qslot = np.full((H, NB * 64), -1, np.int64)
+    kassign = np.full((1, H, N), NB, np.int32)
+    qassign = np.full((1, H, N), NB, np.int32)
+    for h in range(H):
+        for slot, cnt, assign in ((kslot, kcnt, kassign), (qslot, qcnt, qassign)):
+            perm = rng.permutation(N)
+            t = 0
+            for b in range(NB):
+                toks = perm[t:t + cnt[h, b]]
+                slot[h, b * 64:b * 64 + len(toks)] = toks
+                assign[0, h, toks] = b
+                t += cnt[h, b]
+    # rows: runs of 1..4 query blocks share one list; a few empty rows; some rows with
+    # out-of-range entries (-2, NB + 3) and, for D = 128, a repeated entry
+    rows = []
+    for h in range(H):
+        b = 0
+        while b < NB:
+            run = int(rng.integers(1, 5))
+            lst = rng.permutation(NB)[: int(rng.integers(0, NB + 1))]
+            if rng.random() < 0.1:
+                lst = lst[:0]
+            for _ in range(min(run, NB - b)):
+                r = list(lst)
+                if len(r) and rng.random() < 0.3:
+                    # D = 64 walks rows in CSR order, where a repeat counts per listing
+                    r = r + ([r[0]] if D == 128 else []) + [-2, NB + 3]
+                    rng.shuffle(r)
+                rows.append(np.array(r, np.int32))
+                b += 1
+    rp = np.zeros(H * NB + 1, np.int32)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    ci = np.concatenate(rows).astype(np.int32) if rp[-1] else np.zeros(1, np.int32)
+    # the oracle's cluster rows: the same lists plus an empty row for cluster NB
+    orows = []
+    for h in range(H):
+        orows += rows[h * NB:(h + 1) * NB] + [np.zeros(0, np.int32)]
+    orp = np.zeros(H * (NB + 1) + 1, np.int32)
+    orp[1:] = np.cumsum([len(r) for r in orows])
+    oci = np.concatenate(orows).astype(np.int32) if orp[-1] else np.zeros(0, np.int32)
+    scale = 1.0 / np.sqrt(D)
+    ref = O.cluster_attention(q, k, v, qassign, kassign, NB + 1, NB + 1, scale, orp, oci)
+
+    def tiled(a, slot):
+        out = np.zeros((1, H, NB * 64, D), np.float32)
+        for h in range(H):
+            real = slot[h] >= 0
+            out[0, h, real] = a[0, slot[h][real], h]
+        return out
+    qt = dev(rows_to_qk(tiled(q, qslot), NB), torch.bfloat16)
+    kt = dev(rows_to_qk(tiled(k, kslot), NB), torch.bfloat16)
+    vt = dev(rows_to_vt(tiled(v, kslot), NB), torch.bfloat16)
+    kc, rpd, cid = dev(kcnt, torch.int32), dev(rp, torch.int32), dev(ci, torch.int32)
+    o1 = torch.empty((1, H, NB * 64, D), dtype=torch.bfloat16, device="cuda")
+    o2, o32 = torch.empty_like(o1), torch.empty((1, H, NB * 64, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, H, NB * 64), dtype=torch.float32, device="cuda")
+    fpsa.sparse_attn_fwd_varlen(qt, kt, vt, kc, rpd, cid, 1, H, D, NB, scale, o1)
+    fpsa.sparse_attn_fwd_varlen(qt, kt, vt, kc, rpd, cid, 1, H, D, NB, scale, o2, lse=lse, o_f32=o32)
+    o1, o2, o32, lse = (t.float().cpu().numpy() for t in (o1, o2, o32, lse))
+    for h in range(H):
+        real = qslot[h] >= 0
+        want = ref[0, qslot[h][real], h]
+        for got in (o1, o2, o32):
+            e = np.abs(got[0, h, real].astype(np.float64) - want)
+            assert e.max() <= BF16_MAX_ABS and e.mean() <= BF16_MEAN_ABS, (h, e.max(), e.mean())
+        # lse: each real query against the allowed keys of its block's row
+        for qb in range(NB):
+            r = h * NB + qb
+            kept = np.unique(ci[rp[r]:rp[r + 1]])
+            kept = kept[(kept >= 0) & (kept < NB)]
+            keys = np.concatenate([kslot[h, b * 64:b * 64 + kcnt[h, b]] for b in kept]) if len(kept) else []
+            qs = qslot[h, qb * 64:qb * 64 + qcnt[h, qb]]
+            if len(qs) == 0:
+                continue
+            got = lse[0, h, qb * 64:qb * 64 + len(qs)]
+            if len(keys) == 0:
+                assert np.all(np.isneginf(got)) and np.all(o1[0, h, qb * 64:(qb + 1) * 64] == 0)
+                continue
+            s = q[0, qs, h].astype(np.float64) @ k[0, keys, h].astype(np.float64).T * scale
+            want_l = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy()
+            assert np.abs(got - want_l).max() < 2e-3, (h, qb)
+    # a repeated entry and out-of-range entries change nothing: the same rows cleaned
+    if D == 128:
+        clean = [np.unique(r[(r >= 0) & (r < NB)]) for r in rows]
+        crp = np.zeros(H * NB + 1, np.int32)
+        crp[1:] = np.cumsum([len(r) for r in clean])
+        cci = np.concatenate(clean).astype(np.int32) if crp[-1] else np.zeros(1, np.int32)
+        o3 = torch.empty((1, H, NB * 64, D), dtype=torch.bfloat16, device="cuda")
+        fpsa.sparse_attn_fwd_varlen(qt, kt, vt, kc, dev(crp, torch.int32), dev(cci, torch.int32), 1, H, D, NB,
+                                    scale, o3)
+        assert np.array_equal(o3.float().cpu().numpy(), o1)
