@@ -10,9 +10,11 @@
 // reproducible. The kept set is the top of the ranking up to the cut key v*:
 // every key above v*, plus the lowest-indexed keys equal to v* that are still
 // needed. v* is the largest key value v for which the keys >= v already reach the
-// threshold; it is found bit by bit (41 wave-wide sums) instead of by sorting,
-// which gives the same set as sort + prefix sum + cut. One wavefront per row; the
-// ascending output order falls out of ballot prefix counts over index order.
+// threshold; it is found one 8-bit digit at a time, most significant first (six
+// passes over the row, each summing the keys per digit value in LDS), instead of
+// by sorting, which gives the same set as sort + prefix sum + cut. One wavefront
+// per row; the ascending output order falls out of ballot prefix counts over
+// index order.
 #include <mutex>
 
 #include "fpsa_device.h"
@@ -22,10 +24,16 @@ namespace fpsa {
 
 constexpr int kSelWaves = 4;               // rows per workgroup (one wave each)
 constexpr size_t kSelLdsBytes = 64 * 1024; // keys of all rows of a workgroup live in LDS
+constexpr int kDigitBits = 8;              // the cut key is found 8 bits at a time
+constexpr int kDigits = 1 << kDigitBits;   // digit values, 4 per lane
 
-// Rows (waves) per workgroup of the counting kernel so that their keys fit in LDS.
+// LDS bytes of one row of the counting kernel: its keys and its per-digit sums.
+static size_t select_row_lds(int nb) { return (size_t)nb * 8 + kDigits * 8; }
+
+// Rows (waves) per workgroup of the counting kernel so that their keys fit in LDS
+// (nb <= 4096: one row takes at most 34 KB).
 static int select_waves(int nb) {
-    int w = (int)(kSelLdsBytes / ((size_t)nb * 8));
+    int w = (int)(kSelLdsBytes / select_row_lds(nb));
     return w < 1 ? 1 : (w > kSelWaves ? kSelWaves : w);
 }
 
@@ -36,13 +44,32 @@ __device__ inline uint64_t mass_key(float m) {
     return (uint64_t)(double)(m * 1099511627776.0f);
 }
 
+// Makes each lane's LDS writes visible to the other lanes of its wave before the
+// accesses that follow (without it the compiler may, for example, hand a lane its
+// own earlier store instead of reading what other lanes added since).
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 __device__ inline uint64_t lanemask_lt() {
     int lane = threadIdx.x & 63;
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
 // Per row: kept count, cut key and how many keys equal to the cut key are kept.
-// Dynamic LDS: (blockDim.x / 64) * nb keys.
+// Dynamic LDS: (blockDim.x / 64) rows of nb keys, then as many rows of 256 digit sums.
+//
+// The cut v* is the largest v with den * (sum of keys >= v) >= num * S. Keys are
+// below 2^41, so v* has six 8-bit digits (bits 47..40, the top one 0 or 1, down to
+// 7..0). With the digits above `shift + 8` fixed at `prefix`, `above` is the sum of
+// the keys whose top digits exceed the prefix; the next digit is the largest d for
+// which den * (above + sum of the keys that carry the prefix and a digit >= d)
+// reaches the target. The condition holds at d = 0 (it held for the prefix) and
+// weakens as d grows, so d is the number of digits where it holds, minus one. After
+// the last digit, prefix = v* and above = the sum of the keys above v*. Every step
+// is exact integer arithmetic, so v* is the same value a bit-by-bit search finds.
 __global__ __launch_bounds__(64 * kSelWaves) void k_select_count(const float* __restrict__ mass,
                                                                  long R, int nb, uint32_t num,
                                                                  uint32_t den,
@@ -56,6 +83,8 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_count(const float* __
     if (r >= R) return;
     const float* row = mass + r * nb;
     uint64_t* kk = keys + (size_t)w * nb;
+    // this wave's digit sums; lane l owns digits 4l .. 4l+3
+    unsigned long long* dsum = reinterpret_cast<unsigned long long*>(keys + (size_t)waves * nb + (size_t)w * kDigits);
     uint64_t part = 0;
     for (int i = lane; i < nb; i += 64) {
         uint64_t key = mass_key(row[i]);
@@ -68,28 +97,49 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_count(const float* __
     int nties = 0;
     if (S > 0 && num > 0) {
         const uint64_t target = (uint64_t)num * S;     // <= 1000 * 2^52
-        uint64_t v = 0;
-        for (int bit = 40; bit >= 0; --bit) {
-            uint64_t cand = v | (1ull << bit);
-            uint64_t c = 0;
+        uint64_t prefix = 0, above = 0;
+        for (int shift = 40; shift >= 0; shift -= kDigitBits) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dsum[4 * lane + j] = 0;
+            wave_lds_sync();
             for (int i = lane; i < nb; i += 64) {
-                uint64_t key = kk[i];
-                c += key >= cand ? key : 0;
+                const uint64_t key = kk[i];
+                if ((key >> (shift + kDigitBits)) == prefix) atomicAdd(&dsum[(key >> shift) & (kDigits - 1)], (unsigned long long)key);
             }
-            c = wave_sum_u64(c);
-            if ((uint64_t)den * c >= target) v = cand;
+            wave_lds_sync();
+            uint64_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = dsum[4 * lane + j];
+            // suffix sum over lanes: this lane's four digits and every higher lane's
+            uint64_t suf = h[0] + h[1] + h[2] + h[3];
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint64_t t = __shfl_down((unsigned long long)suf, o);
+                if (lane + o < 64) suf += t;
+            }
+            // sv[j]: sum of the prefix's keys whose digit is >= 4 lane + j
+            uint64_t sv[4];
+            sv[0] = suf;
+#pragma unroll
+            for (int j = 1; j < 4; ++j) sv[j] = sv[j - 1] - h[j - 1];
+            int holds = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) holds += __popcll(__ballot((uint64_t)den * (above + sv[j]) >= target));
+            const int d = holds - 1;                     // >= 0, uniform
+            // keys of the prefix with a digit above d join `above`
+            if (d + 1 < kDigits) {
+                const int j1 = (d + 1) & 3;
+                const uint64_t pick = j1 == 0 ? sv[0] : j1 == 1 ? sv[1] : j1 == 2 ? sv[2] : sv[3];
+                above += __shfl((unsigned long long)pick, (d + 1) >> 2);
+            }
+            prefix = (prefix << kDigitBits) | (uint64_t)d;
         }
-        // v >= 1 here: all positive keys sum to S and den >= num.
-        uint64_t cgt = 0;
+        const uint64_t v = prefix;                       // >= 1: all positive keys sum to S, den >= num
         int ngt = 0;
-        for (int i = lane; i < nb; i += 64) {
-            uint64_t key = kk[i];
-            if (key > v) { cgt += key; ngt++; }
-        }
-        cgt = wave_sum_u64(cgt);
+        for (int i = lane; i < nb; i += 64) ngt += kk[i] > v ? 1 : 0;
         for (int o = 32; o >= 1; o >>= 1) ngt += __shfl_xor(ngt, o);
-        // den*cgt < target by maximality of v; the tied keys needed, each worth v:
-        const uint64_t need = target - (uint64_t)den * cgt;
+        // den * above < target by maximality of v; the tied keys needed, each worth v:
+        const uint64_t need = target - (uint64_t)den * above;
         const uint64_t per = (uint64_t)den * v;
         nties = (int)((need + per - 1) / per);
         kept = ngt + nties;
@@ -218,7 +268,7 @@ void launch_select(const float* mass, long R, int nb, uint32_t num, uint32_t den
     carve(ws, R, &count, &ties, &cut);
     const int cw = select_waves(nb);
     unsigned cblocks = (unsigned)((R + cw - 1) / cw);
-    k_select_count<<<cblocks, 64 * cw, (size_t)cw * nb * 8, st>>>(mass, R, nb, num, den, count, cut,
+    k_select_count<<<cblocks, 64 * cw, (size_t)cw * select_row_lds(nb), st>>>(mass, R, nb, num, den, count, cut,
                                                                   ties);
     unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
     k_scan_counts<<<1, 1024, 0, st>>>(count, R, row_ptr);
