@@ -23,19 +23,8 @@
 namespace fpsa {
 
 constexpr int kSelWaves = 4;               // rows per workgroup (one wave each)
-constexpr size_t kSelLdsBytes = 64 * 1024; // keys of all rows of a workgroup live in LDS
 constexpr int kDigitBits = 8;              // the cut key is found 8 bits at a time
 constexpr int kDigits = 1 << kDigitBits;   // digit values, 4 per lane
-
-// LDS bytes of one row of the counting kernel: its keys and its per-digit sums.
-static size_t select_row_lds(int nb) { return (size_t)nb * 8 + kDigits * 8; }
-
-// Rows (waves) per workgroup of the counting kernel so that their keys fit in LDS
-// (nb <= 4096: one row takes at most 34 KB).
-static int select_waves(int nb) {
-    int w = (int)(kSelLdsBytes / select_row_lds(nb));
-    return w < 1 ? 1 : (w > kSelWaves ? kSelWaves : w);
-}
 
 __device__ inline uint64_t mass_key(float m) {
     if (!(m > 0.0f)) return 0;             // zero, negative, NaN
@@ -53,91 +42,143 @@ __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Lane shift of a float64 by DPP (both halves moved; lanes with no source, or in rows
+// the row mask leaves out, get +0.0).
+template <int CTRL, int ROWS>
+__device__ inline double dpp_f64(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive sum over lanes 0..l of x (every partial sum an integer below 2^53, so
+// exact): shifts by 1, 2, 4, 8 within each row of 16 lanes, then row 0's total into
+// rows 1 and 3 and the first two rows' total into rows 2 and 3.
+__device__ inline double wave_prefix_sum_exact(double x) {
+    x += dpp_f64<0x111, 0xF>(x);     // row_shr:1
+    x += dpp_f64<0x112, 0xF>(x);     // row_shr:2
+    x += dpp_f64<0x114, 0xF>(x);     // row_shr:4
+    x += dpp_f64<0x118, 0xF>(x);     // row_shr:8
+    x += dpp_f64<0x142, 0xA>(x);     // row_bcast:15
+    x += dpp_f64<0x143, 0xC>(x);     // row_bcast:31
+    return x;
+}
+
+// Maximum over lanes 0..l of x >= 0 (the same lane pattern as the prefix sum).
+__device__ inline double wave_prefix_max(double x) {
+    x = fmax(x, dpp_f64<0x111, 0xF>(x));
+    x = fmax(x, dpp_f64<0x112, 0xF>(x));
+    x = fmax(x, dpp_f64<0x114, 0xF>(x));
+    x = fmax(x, dpp_f64<0x118, 0xF>(x));
+    x = fmax(x, dpp_f64<0x142, 0xA>(x));
+    x = fmax(x, dpp_f64<0x143, 0xC>(x));
+    return x;
+}
+
+__device__ inline double lane_f64(double x, int l) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __device__ inline uint64_t lanemask_lt() {
     int lane = threadIdx.x & 63;
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
 // Per row: kept count, cut key and how many keys equal to the cut key are kept.
-// Dynamic LDS: (blockDim.x / 64) rows of nb keys, then as many rows of 256 digit sums.
 //
-// The cut v* is the largest v with den * (sum of keys >= v) >= num * S. Keys are
-// below 2^41, so v* has six 8-bit digits (bits 47..40, the top one 0 or 1, down to
-// 7..0). With the digits above `shift + 8` fixed at `prefix`, `above` is the sum of
-// the keys whose top digits exceed the prefix; the next digit is the largest d for
-// which den * (above + sum of the keys that carry the prefix and a digit >= d)
-// reaches the target. The condition holds at d = 0 (it held for the prefix) and
-// weakens as d grows, so d is the number of digits where it holds, minus one. After
-// the last digit, prefix = v* and above = the sum of the keys above v*. Every step
-// is exact integer arithmetic, so v* is the same value a bit-by-bit search finds.
+// The cut v* is the largest v with den * (sum of keys >= v) >= num * S. No key has a
+// bit above the row's highest set bit `top`, so v* is found in digits of up to 8 bits
+// from bit `top` down to bit 0 (bits hi .. lo per pass; a window aligned to the
+// largest key spreads the first pass's keys over many digit values). With the bits
+// above hi fixed at `prefix`, `above` is the sum of the keys whose bits above hi
+// exceed the prefix; the next digit is the largest d for which den * (above + sum of
+// the keys that carry the prefix and a digit >= d) reaches the target. The condition
+// holds at d = 0 (it held for the prefix; above is 0 in the first pass, and den >=
+// num) and weakens as d grows, so d is the number of digit values where it holds,
+// minus one (values the window cannot hold count as empty and fail, den * above
+// being below the target). After the last digit, prefix = v* and above = the sum of
+// the keys above v*. Every step is exact integer arithmetic (sums of keys stay below
+// 2^53 and are carried exactly in float64 through the lane scans), so v* is the
+// value a bit-by-bit search finds.
+//
+// One wave per row; lane l holds keys l, l + 64, ... in registers (KPL per lane,
+// nb <= 64 KPL). Per digit pass the matching keys are added into 256 digit sums in
+// LDS (this wave's own 2 KB); lane l reads the four sums of digits 4 (63 - l) ..
+// 4 (63 - l) + 3, so a prefix sum over lanes is a suffix sum over digits.
+template <int KPL>
 __global__ __launch_bounds__(64 * kSelWaves) void k_select_count(const float* __restrict__ mass,
                                                                  long R, int nb, uint32_t num,
                                                                  uint32_t den,
                                                                  int32_t* __restrict__ count,
                                                                  uint64_t* __restrict__ cut,
                                                                  int32_t* __restrict__ ties) {
-    extern __shared__ uint64_t keys[];
-    const int waves = blockDim.x >> 6;
+    __shared__ unsigned long long dsum_all[kSelWaves][kDigits];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long r = (long)blockIdx.x * waves + w;
+    const long r = (long)blockIdx.x * kSelWaves + w;
     if (r >= R) return;
     const float* row = mass + r * nb;
-    uint64_t* kk = keys + (size_t)w * nb;
-    // this wave's digit sums; lane l owns digits 4l .. 4l+3
-    unsigned long long* dsum = reinterpret_cast<unsigned long long*>(keys + (size_t)waves * nb + (size_t)w * kDigits);
-    uint64_t part = 0;
-    for (int i = lane; i < nb; i += 64) {
-        uint64_t key = mass_key(row[i]);
-        kk[i] = key;
-        part += key;
+    unsigned long long* dsum = dsum_all[w];
+    float mv[KPL];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) mv[j] = lane + 64 * j < nb ? row[lane + 64 * j] : 0.0f;
+    uint64_t key[KPL];
+    double part = 0.0, kmax = 0.0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        key[j] = mass_key(mv[j]);
+        part += (double)key[j];                          // < 2^47: exact
+        kmax = fmax(kmax, (double)key[j]);
     }
-    const uint64_t S = wave_sum_u64(part);
+    const double S = lane_f64(wave_prefix_sum_exact(part), 63);
     int kept = 0;
     uint64_t vstar = 0;
     int nties = 0;
-    if (S > 0 && num > 0) {
-        const uint64_t target = (uint64_t)num * S;     // <= 1000 * 2^52
+    if (S > 0.0 && num > 0) {
+        const uint64_t target = (uint64_t)num * (uint64_t)S;     // <= 1000 * 2^52
+        const int g = 63 - lane;                                  // this lane's digit group
+        const uint64_t kmx = (uint64_t)lane_f64(wave_prefix_max(kmax), 63);   // >= 1
         uint64_t prefix = 0, above = 0;
-        for (int shift = 40; shift >= 0; shift -= kDigitBits) {
+        for (int hi = 63 - __builtin_clzll(kmx); hi >= 0;) {
+            const int lo = hi >= kDigitBits - 1 ? hi - (kDigitBits - 1) : 0;
+            const int width = hi - lo + 1;
+            const uint64_t dmask = (1ull << width) - 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dsum[4 * lane + j] = 0;
+            for (int j = 0; j < 4; ++j) dsum[4 * g + j] = 0;
             wave_lds_sync();
-            for (int i = lane; i < nb; i += 64) {
-                const uint64_t key = kk[i];
-                if ((key >> (shift + kDigitBits)) == prefix) atomicAdd(&dsum[(key >> shift) & (kDigits - 1)], (unsigned long long)key);
-            }
+#pragma unroll
+            for (int j = 0; j < KPL; ++j)
+                if ((key[j] >> (hi + 1)) == prefix && key[j] != 0)
+                    atomicAdd(&dsum[(key[j] >> lo) & dmask], (unsigned long long)key[j]);
             wave_lds_sync();
-            uint64_t h[4];
+            double h[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) h[j] = dsum[4 * lane + j];
-            // suffix sum over lanes: this lane's four digits and every higher lane's
-            uint64_t suf = h[0] + h[1] + h[2] + h[3];
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint64_t t = __shfl_down((unsigned long long)suf, o);
-                if (lane + o < 64) suf += t;
-            }
-            // sv[j]: sum of the prefix's keys whose digit is >= 4 lane + j
-            uint64_t sv[4];
-            sv[0] = suf;
+            for (int j = 0; j < 4; ++j) h[j] = (double)dsum[4 * g + j];
+            // sum of the prefix's keys with a digit >= 4 g, then >= 4 g + j
+            double sv[4];
+            sv[0] = wave_prefix_sum_exact(h[0] + h[1] + h[2] + h[3]);
 #pragma unroll
             for (int j = 1; j < 4; ++j) sv[j] = sv[j - 1] - h[j - 1];
             int holds = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) holds += __popcll(__ballot((uint64_t)den * (above + sv[j]) >= target));
+            for (int j = 0; j < 4; ++j) holds += __popcll(__ballot((uint64_t)den * (above + (uint64_t)sv[j]) >= target));
             const int d = holds - 1;                     // >= 0, uniform
             // keys of the prefix with a digit above d join `above`
             if (d + 1 < kDigits) {
                 const int j1 = (d + 1) & 3;
-                const uint64_t pick = j1 == 0 ? sv[0] : j1 == 1 ? sv[1] : j1 == 2 ? sv[2] : sv[3];
-                above += __shfl((unsigned long long)pick, (d + 1) >> 2);
+                const double pick = j1 == 0 ? sv[0] : j1 == 1 ? sv[1] : j1 == 2 ? sv[2] : sv[3];
+                above += (uint64_t)lane_f64(pick, 63 - ((d + 1) >> 2));
             }
-            prefix = (prefix << kDigitBits) | (uint64_t)d;
+            prefix = (prefix << width) | (uint64_t)d;
+            hi = lo - 1;
         }
         const uint64_t v = prefix;                       // >= 1: all positive keys sum to S, den >= num
         int ngt = 0;
-        for (int i = lane; i < nb; i += 64) ngt += kk[i] > v ? 1 : 0;
-        for (int o = 32; o >= 1; o >>= 1) ngt += __shfl_xor(ngt, o);
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) ngt += __popcll(__ballot(key[j] > v));
         // den * above < target by maximality of v; the tied keys needed, each worth v:
         const uint64_t need = target - (uint64_t)den * above;
         const uint64_t per = (uint64_t)den * v;
@@ -152,37 +193,46 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select_count(const float* __
     }
 }
 
-// Exclusive scan of per-row counts into row_ptr[R + 1] with a single workgroup.
+// Exclusive scan of per-row counts into row_ptr[R + 1] with a single workgroup, in
+// tiles of 4096 counts: each thread loads its four at once, the workgroup scans the
+// tile's thread sums, and the running total carries to the next tile.
 __global__ __launch_bounds__(1024) void k_scan_counts(const int32_t* __restrict__ count, long R,
                                                       int32_t* __restrict__ row_ptr) {
     __shared__ int32_t wsum[16];
-    const int tid = threadIdx.x;
-    const long per = (R + 1023) / 1024;
-    const long lo = min((long)tid * per, R), hi = min(lo + per, R);
-    int32_t local = 0;
-    for (long i = lo; i < hi; ++i) local += count[i];
-    // inclusive scan of `local` across the workgroup
-    int lane = tid & 63, w = tid >> 6;
-    int32_t x = local;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int32_t carry = 0;
+    for (long base = 0; base < R; base += 4096) {
+        const long i0 = base + 4 * (long)tid;
+        int32_t c[4];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
+        for (int j = 0; j < 4; ++j) c[j] = i0 + j < R ? count[i0 + j] : 0;
+        const int32_t local = c[0] + c[1] + c[2] + c[3];
+        // inclusive scan of `local` across the wave, then across the 16 waves
+        int32_t x = local;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) wsum[w] = x;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int32_t t = wsum[i];
+            before += i < w ? t : 0;
+            total += t;
+        }
+        int32_t run = carry + before + x - local;        // exclusive prefix of this thread's four
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (i0 + j < R) row_ptr[i0 + j] = run;
+            run += c[j];
+        }
+        carry += total;
+        __syncthreads();                                 // wsum is rewritten by the next tile
     }
-    if (lane == 63) wsum[w] = x;
-    __syncthreads();
-    int32_t before = 0;
-    for (int i = 0; i < w; ++i) before += wsum[i];
-    int32_t run = before + x - local;            // exclusive prefix of this thread's chunk
-    for (long i = lo; i < hi; ++i) {
-        row_ptr[i] = run;
-        run += count[i];
-    }
-    if (tid == 1023) {
-        int32_t total = 0;
-        for (int i = 0; i < 16; ++i) total += wsum[i];
-        row_ptr[R] = total;
-    }
+    if (tid == 0) row_ptr[R] = carry;
 }
 
 // Write kept indices of each row in ascending order.
@@ -266,11 +316,12 @@ void launch_select(const float* mass, long R, int nb, uint32_t num, uint32_t den
     int32_t *count, *ties;
     uint64_t* cut;
     carve(ws, R, &count, &ties, &cut);
-    const int cw = select_waves(nb);
-    unsigned cblocks = (unsigned)((R + cw - 1) / cw);
-    k_select_count<<<cblocks, 64 * cw, (size_t)cw * select_row_lds(nb), st>>>(mass, R, nb, num, den, count, cut,
-                                                                  ties);
     unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
+    // keys of a row in registers: 16 per lane up to 1024 blocks, else 64 (nb <= 4096)
+    if (nb <= 64 * 16)
+        k_select_count<16><<<blocks, 64 * kSelWaves, 0, st>>>(mass, R, nb, num, den, count, cut, ties);
+    else
+        k_select_count<64><<<blocks, 64 * kSelWaves, 0, st>>>(mass, R, nb, num, den, count, cut, ties);
     k_scan_counts<<<1, 1024, 0, st>>>(count, R, row_ptr);
     k_select_fill<<<blocks, 64 * kSelWaves, 0, st>>>(mass, R, nb, cut, ties, row_ptr, col_idx);
 }

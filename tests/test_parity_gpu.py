@@ -118,7 +118,7 @@ def _gpu_select(mass_np, num, den):
 
 
 @pytest.mark.parametrize("R,nb", [(5, 1), (40, 3), (64, 64), (64, 65), (300, 200), (500, 624),
-                                  (40, 2160), (12, 4096)])
+                                  (9, 1024), (9, 1025), (40, 2160), (12, 4096)])
 @pytest.mark.parametrize("num,den", [(99, 100), (1, 2), (9, 10), (1000, 1000), (0, 7)])
 def test_select_bitexact_on_seeded_masses(R, nb, num, den):
     m = synth.random_mass_rows(R, nb, seed=R * 31 + nb, tie_frac=0.2, zero_frac=0.1)
