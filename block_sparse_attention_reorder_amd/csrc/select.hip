@@ -15,6 +15,7 @@
 // by sorting, which gives the same set as sort + prefix sum + cut. One wavefront
 // per row; the ascending output order falls out of ballot prefix counts over
 // index order.
+#include <algorithm>
 #include <mutex>
 
 #include "fpsa_device.h"
@@ -443,36 +444,55 @@ void launch_pattern(int nb, int B, int H, const int32_t* patterns, int32_t* row_
 // frozen indices rest on the support staying put across steps [LoSA: Near-Lossless
 // Sparse Attention for Training-Free Video Diffusion Acceleration, Abstract]; this
 // measures how much of the new mass they cover. One wave per row: the row's indices
-// are marked in an LDS bitmap (duplicates collapse), then the dense mass row is read
-// once, coalesced, and the marked entries are summed in float64 (lane-strided
-// partial sums, then a fixed butterfly: deterministic).
+// are marked in an LDS byte map (duplicates collapse; plain byte stores of 1, so
+// neighbouring indices in one word do not serialise as atomic ORs would), then the
+// dense mass row is read once, coalesced, and the marked entries are summed in float64
+// (lane-strided partial sums, then a fixed butterfly: deterministic). Each lane issues
+// its first KPL index loads and its KPL mass loads (nb <= 64 KPL) before it waits.
 
+template <int KPL>
 __global__ __launch_bounds__(64 * kSelWaves) void k_retained_mass(const float* __restrict__ mass,
                                                                   long R, int nb,
                                                                   const int32_t* __restrict__ row_ptr,
                                                                   const int32_t* __restrict__ col_idx,
                                                                   float* __restrict__ out) {
-    extern __shared__ uint32_t marks[];    // kSelWaves bitmaps of ceil(nb / 32) words
+    extern __shared__ uint32_t marks[];    // kSelWaves byte maps of ceil(nb / 4) words
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int words = (nb + 31) >> 5;
-    uint32_t* my = marks + w * words;
+    const int words = (nb + 3) >> 2;
+    uint32_t* myw = marks + w * words;
+    uint8_t* my = reinterpret_cast<uint8_t*>(myw);
     const long r = (long)blockIdx.x * kSelWaves + w;
     const bool live = r < R;
-    for (int i = lane; i < words; i += 64) my[i] = 0;
+    for (int i = lane; i < words; i += 64) myw[i] = 0;
+    float mv[KPL];
+    if (live) {
+        const float* row = mass + r * nb;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) mv[j] = lane + 64 * j < nb ? row[lane + 64 * j] : 0.0f;
+    }
     __syncthreads();
     if (live) {
-        const int32_t e1 = row_ptr[r + 1];
-        for (int32_t e = row_ptr[r] + lane; e < e1; e += 64) {
+        const int32_t e0 = row_ptr[r], e1 = row_ptr[r + 1];
+        int32_t kbs[KPL];
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) kbs[j] = e0 + lane + 64 * j < e1 ? col_idx[e0 + lane + 64 * j] : -1;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j)
+            if ((unsigned)kbs[j] < (unsigned)nb) my[kbs[j]] = 1;
+        // rows listing more than 64 KPL entries (repeats)
+        for (int32_t e = e0 + lane + 64 * KPL; e < e1; e += 64) {
             const int kb = col_idx[e];
-            if ((unsigned)kb < (unsigned)nb) atomicOr(&my[kb >> 5], 1u << (kb & 31));
+            if ((unsigned)kb < (unsigned)nb) my[kb] = 1;
         }
     }
     __syncthreads();
     if (!live) return;
-    const float* row = mass + r * nb;
     double s = 0.0;
-    for (int kb = lane; kb < nb; kb += 64)
-        if ((my[kb >> 5] >> (kb & 31)) & 1u) s += (double)row[kb];
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int kb = lane + 64 * j;
+        if (kb < nb && my[kb]) s += (double)mv[j];
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
     if (lane == 0) out[r] = (float)s;
@@ -481,8 +501,11 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_retained_mass(const float* _
 void launch_retained_mass(const float* mass, long R, int nb, const int32_t* row_ptr,
                           const int32_t* col_idx, float* out, hipStream_t st) {
     unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
-    size_t lds = (size_t)kSelWaves * ((nb + 31) / 32) * 4;
-    k_retained_mass<<<blocks, 64 * kSelWaves, lds, st>>>(mass, R, nb, row_ptr, col_idx, out);
+    size_t lds = (size_t)kSelWaves * ((nb + 3) / 4) * 4;
+    if (nb <= 64 * 16)
+        k_retained_mass<16><<<blocks, 64 * kSelWaves, lds, st>>>(mass, R, nb, row_ptr, col_idx, out);
+    else
+        k_retained_mass<64><<<blocks, 64 * kSelWaves, lds, st>>>(mass, R, nb, row_ptr, col_idx, out);
 }
 
 // ---------------------------------------------------------------- CSR transpose
@@ -491,24 +514,35 @@ void launch_retained_mass(const float* mass, long R, int nb, const int32_t* row_
 // the column view the key-gradient pass walks. The rows are first marked in a bitmap
 // (one bit per (row, kb); repeats collapse, out-of-range indices are dropped), then a
 // wave per column counts and writes its query blocks in index order from ballots, so
-// the result is deterministic.
+// the result is deterministic. A row's bitmap is formed in LDS as a byte map (plain
+// byte stores: neighbouring indices would serialise as atomic ORs into one word) and
+// written out as whole words from ballots.
 
-__global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, long n) {
-    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0u;
-}
-
+// Dynamic LDS: (blockDim.x / 64) byte maps of nb rounded up to 4 bytes.
 __global__ __launch_bounds__(64 * kSelWaves) void k_csr_bitmap(const int32_t* __restrict__ row_ptr,
                                                                const int32_t* __restrict__ col_idx,
                                                                long R, int nb, int words,
                                                                uint32_t* __restrict__ bits) {
+    extern __shared__ uint32_t maps[];
+    const int waves = blockDim.x >> 6;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long r = (long)blockIdx.x * kSelWaves + w;
+    const long r = (long)blockIdx.x * waves + w;
     if (r >= R) return;
-    uint32_t* row = bits + r * words;
+    const int mwords = (nb + 3) >> 2;
+    uint32_t* mw = maps + (size_t)w * mwords;
+    uint8_t* mb = reinterpret_cast<uint8_t*>(mw);
+    for (int i = lane; i < mwords; i += 64) mw[i] = 0;
+    wave_lds_sync();
     const int32_t e1 = row_ptr[r + 1];
     for (int32_t e = row_ptr[r] + lane; e < e1; e += 64) {
         const int kb = col_idx[e];
-        if ((unsigned)kb < (unsigned)nb) atomicOr(&row[kb >> 5], 1u << (kb & 31));
+        if ((unsigned)kb < (unsigned)nb) mb[kb] = 1;
+    }
+    wave_lds_sync();
+    uint32_t* row = bits + r * words;
+    for (int c = 0; c < nb; c += 64) {
+        const uint64_t m = __ballot(c + lane < nb && mb[c + lane] != 0);
+        if (lane < 2 && (c >> 5) + lane < words) row[(c >> 5) + lane] = (uint32_t)(m >> (32 * lane));
     }
 }
 
@@ -569,11 +603,12 @@ void launch_csr_transpose(const int32_t* row_ptr, const int32_t* col_idx, long R
     const int words = (nb + 31) / 32;
     uint32_t* bits = static_cast<uint32_t*>(ws);
     int32_t* count = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + up((size_t)R * words * 4));
-    const long nbits = R * words;
-    const unsigned fill_blocks = (unsigned)min((nbits + 255) / 256, 65536L);
-    k_fill_zero<<<fill_blocks, 256, 0, st>>>(bits, nbits);
+    // every word of every row's bitmap is written by k_csr_bitmap (no clearing pass)
+    const size_t map_bytes = (size_t)((nb + 3) / 4) * 4;           // <= 46,344 (R >= nb, R nb < 2^31)
+    const int mw = (int)std::max<size_t>(1, std::min<size_t>(kSelWaves, 65536 / map_bytes));
+    k_csr_bitmap<<<(unsigned)((R + mw - 1) / mw), 64 * mw, mw * map_bytes, st>>>(row_ptr, col_idx, R, nb, words,
+                                                                                bits);
     const unsigned blocks = (unsigned)((R + kSelWaves - 1) / kSelWaves);
-    k_csr_bitmap<<<blocks, 64 * kSelWaves, 0, st>>>(row_ptr, col_idx, R, nb, words, bits);
     k_col_count<<<blocks, 64 * kSelWaves, 0, st>>>(bits, nb, words, R, count);
     k_scan_counts<<<1, 1024, 0, st>>>(count, R, col_ptr);
     k_col_fill<<<blocks, 64 * kSelWaves, 0, st>>>(bits, nb, words, R, col_ptr, row_idx);

@@ -222,6 +222,24 @@ def test_retained_mass_matches_oracle(R, nb):
     assert np.all(got == 0)
 
 
+@pytest.mark.parametrize("nb,n", [(200, 1500), (1100, 4500)])
+def test_retained_mass_rows_longer_than_a_register_window(nb, n):
+    """Rows listing more entries (with repeats) than the kernel's per-lane register window
+    (16 per lane up to 1,024 blocks, else 64): the rest are taken by its tail loop."""
+    R = 3
+    m = synth.random_mass_rows(R, nb, seed=nb + n, tie_frac=0.2, zero_frac=0.1)
+    rng = np.random.default_rng(n)
+    rows = [rng.integers(-3, nb + 3, size=n).astype(np.int32), np.zeros(0, np.int32),
+            rng.integers(0, nb, size=n // 3).astype(np.int32)]
+    rp = np.zeros(R + 1, np.int32)
+    rp[1:] = np.cumsum([len(x) for x in rows])
+    ci = np.concatenate(rows)
+    got = _gpu_retained(m, rp, ci)
+    want = O.retained_mass(m, rp, ci).astype(np.float32)
+    assert np.all(np.abs(got - want) <= np.spacing(want)), np.abs(got - want).max()
+    assert got[1] == 0
+
+
 # --------------------------------------------------------------------------- block masses
 
 MASS_CASES = [((4, 8, 8), 1, 64, 0.5), ((5, 6, 7), 2, 128, 1.0), ((9, 10, 13), 2, 64, 2.0),
