@@ -10,9 +10,10 @@
 // reproducible. The kept set is the top of the ranking up to the cut key v*:
 // every key above v*, plus the lowest-indexed keys equal to v* that are still
 // needed. v* is the largest key value v for which the keys >= v already reach the
-// threshold; it is found one 8-bit digit at a time, most significant first (six
-// passes over the row, each summing the keys per digit value in LDS), instead of
-// by sorting, which gives the same set as sort + prefix sum + cut. One wavefront
+// threshold; it is found one digit of up to 8 bits at a time, from the row's
+// largest key down (at most six passes over the row's keys, held in registers, each
+// summing the keys per digit value in LDS), instead of by sorting, which gives the
+// same set as sort + prefix sum + cut. One wavefront
 // per row; the ascending output order falls out of ballot prefix counts over
 // index order.
 #include <algorithm>
